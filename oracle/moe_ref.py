@@ -1,0 +1,179 @@
+"""Plain float64 reference of the routed MoE expert FFN (test infrastructure).
+
+Only the test suite, the package smoke check and the benchmark's CPU-baseline
+leg may use this module.
+
+Sources (page title, then section):
+
+* [NKI] "Gated DeltaNet (+ FP8 MoE) -- AWS Neuron (NKI) kernels for
+  Trainium2", section "FP8 MoE decode kernel (moe_fused_w8_35b)": the fused
+  path is gate/up GEMM -> SwiGLU -> down GEMM -> affinity scale -> expert-sum,
+  on official E4M3FN weights with per 128x128 block scales ("maps each 128x128
+  block exactly", Validation paragraph); the router is softmax -> top-8 ->
+  normalise and the shared expert is added after the routed sum (Serving
+  contract paragraph); the result is [B, H] fp32 (Interface paragraph).
+* [NEMO] "nemo_automodel.components.models.qwen3_5.layers", ``_silu_mul``:
+  the SwiGLU product is silu(gate) * up; ``Qwen3_5FusedMLP``: a dense SwiGLU
+  MLP projects, applies silu(gate)*up and projects back.
+* [SPARK] "spark_model/layers/nemotron_moe.rs", module documentation
+  ("Forward: ... weighted_sum ... sum routed+shared") and the sorted prefill
+  path (sort by expert, grouped GEMM, unpermute-reduce).
+* [AITER] "Add gfx950 Q256 fused MXFP4 prefill pipeline" (ROCm/aiter
+  PR #5988), description: tokens sorted by expert with an inverse route map,
+  an FP32 route reduction, and one always-on shared expert.
+
+Readings where the pages are silent (each one is listed in the design doc):
+
+* selection is taken on the fp32 logits (softmax is strictly increasing, so the
+  chosen set is the same as on the probabilities), ties go to the lower expert
+  index, and -0.0 equals +0.0;
+* slot j of a token holds its j-th expert in that order;
+* "normalise" divides each selected probability by the sum of the k selected
+  probabilities;
+* within one expert's segment of the sorted map, routes keep ascending flat
+  route index r = t*k + j (stable order); offsets are not padded;
+* the output is overwritten, fp32-or-better, summed over routes then the shared
+  expert (affinity exactly 1).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+BLOCK = 128
+E4M3FN_MAX = 448.0
+
+
+# --------------------------------------------------------------------------
+# E4M3FN decoding and block dequantisation  ([NKI] weight format paragraph)
+# --------------------------------------------------------------------------
+def _e4m3fn_value(code: int) -> float:
+    """Value of one E4M3FN byte: 1 sign bit, 4 exponent bits (bias 7), 3 mantissa
+    bits, no infinities, and only S.1111.111 reserved for NaN."""
+    s = (code >> 7) & 1
+    e = (code >> 3) & 0xF
+    m = code & 0x7
+    if e == 0xF and m == 0x7:
+        return float("nan")
+    if e == 0:                       # subnormal: 0.m * 2^(1-7)
+        mag = (m / 8.0) * 2.0 ** (1 - 7)
+    else:                            # normal: 1.m * 2^(e-7)
+        mag = (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    return -mag if s else mag
+
+
+def e4m3fn_table() -> np.ndarray:
+    """The value of every one of the 256 codes, float64 (NaN for 0x7F, 0xFF)."""
+    return np.array([_e4m3fn_value(c) for c in range(256)], dtype=np.float64)
+
+
+_TABLE = e4m3fn_table()
+
+
+def e4m3fn_decode(codes) -> np.ndarray:
+    """Decode an array of E4M3FN bytes to float64."""
+    return _TABLE[np.asarray(codes, dtype=np.uint8)]
+
+
+def dequantize_blocks(codes, scales, block: int = BLOCK) -> np.ndarray:
+    """W[r, c] = decode(codes[r, c]) * scales[r // 128, c // 128] (float64).
+
+    ``codes`` is [..., R, C] uint8, ``scales`` [..., R/128, C/128] float32."""
+    vals = e4m3fn_decode(codes)
+    s = np.asarray(scales, dtype=np.float64)
+    s = np.repeat(np.repeat(s, block, axis=-2), block, axis=-1)
+    assert s.shape == vals.shape, (s.shape, vals.shape)
+    return vals * s
+
+
+# --------------------------------------------------------------------------
+# Routing: softmax -> top-k -> normalise  ([NKI] Serving contract)
+# --------------------------------------------------------------------------
+def route_softmax_topk(logits, k: int):
+    """ids int32 [T, k] and renormalised affinities float64 [T, k]."""
+    l32 = np.asarray(logits, dtype=np.float32)
+    T, E = l32.shape
+    assert 1 <= k <= E
+    l = l32.astype(np.float64)
+    # softmax over all E experts
+    p = np.exp(l - l.max(axis=1, keepdims=True))
+    p = p / p.sum(axis=1, keepdims=True)
+    # top-k: order by (logit descending, expert index ascending) and keep k
+    idx = np.broadcast_to(np.arange(E), (T, E))
+    order = np.lexsort((idx, -l), axis=1)
+    ids = order[:, :k].astype(np.int32)
+    # normalise the k selected probabilities to sum to one
+    sel = np.take_along_axis(p, ids.astype(np.int64), axis=1)
+    aff = sel / sel.sum(axis=1, keepdims=True)
+    return ids, aff
+
+
+# --------------------------------------------------------------------------
+# Sort by expert  ([SPARK] sorted prefill path; [AITER] inverse route map)
+# --------------------------------------------------------------------------
+def sort_by_expert(ids, E: int):
+    """counts[E], offsets[E+1], sorted_route[R], inv_route[R] (all int32).
+
+    Route r = t*k + j.  Expert e's segment is sorted_route[offsets[e]:offsets[e+1]]
+    and holds, in ascending r, every route whose id is e; inv_route[r] is the
+    position of route r in sorted_route."""
+    flat = np.asarray(ids, dtype=np.int64).reshape(-1)
+    R = flat.size
+    assert flat.size == 0 or (flat.min() >= 0 and flat.max() < E)
+    counts = np.bincount(flat, minlength=E).astype(np.int64)
+    offsets = np.zeros(E + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(counts)
+    sorted_route = np.argsort(flat, kind="stable")
+    inv_route = np.empty(R, dtype=np.int64)
+    inv_route[sorted_route] = np.arange(R)
+    return (counts.astype(np.int32), offsets.astype(np.int32),
+            sorted_route.astype(np.int32), inv_route.astype(np.int32))
+
+
+# --------------------------------------------------------------------------
+# Expert FFN  ([NKI] fused path; [NEMO] _silu_mul / fused dense MLP)
+# --------------------------------------------------------------------------
+def swiglu(g, u):
+    """silu(g) * u with silu(g) = g * sigmoid(g) = g / (1 + exp(-g))."""
+    with np.errstate(over="ignore"):
+        return g / (1.0 + np.exp(-g)) * u
+
+
+def expert_mlp(xrows, w13, w13_scale, w2, w2_scale):
+    """One expert on rows of x (float64 [M, H]) -> float64 [M, H].
+
+    w13 [2I, H] (gate rows first, then up rows), w2 [H, I], both block-scaled."""
+    W13 = dequantize_blocks(w13, w13_scale)
+    I = W13.shape[0] // 2
+    g = xrows @ W13[:I].T
+    u = xrows @ W13[I:].T
+    a = swiglu(g, u)
+    W2 = dequantize_blocks(w2, w2_scale)
+    return a @ W2.T
+
+
+def moe_ffn(x, w13, w13_scale, w2, w2_scale, ids, aff, shared=None):
+    """out[t] = sum_j aff[t, j] * MLP_{ids[t, j]}(x[t]) (+ shared MLP(x[t])).
+
+    x is [T, H] (bf16 values given as float32/float64), ids [T, k], aff [T, k].
+    The routed terms are added expert by expert in ascending expert index, then
+    the shared expert with affinity exactly 1."""
+    x = np.asarray(x, dtype=np.float64)
+    ids = np.asarray(ids, dtype=np.int64)
+    aff = np.asarray(aff, dtype=np.float64)
+    T, H = x.shape
+    out = np.zeros((T, H), dtype=np.float64)
+    for e in np.unique(ids):
+        t_idx, j_idx = np.nonzero(ids == e)
+        y = expert_mlp(x[t_idx], w13[e], w13_scale[e], w2[e], w2_scale[e])
+        np.add.at(out, t_idx, aff[t_idx, j_idx][:, None] * y)
+    if shared is not None:
+        out += expert_mlp(x, shared["w13"], shared["w13_scale"],
+                          shared["w2"], shared["w2_scale"])
+    return out
+
+
+def moe_forward(x, logits, k, w13, w13_scale, w2, w2_scale, shared=None):
+    """Route then run the expert FFN: returns (ids, aff, out)."""
+    ids, aff = route_softmax_topk(logits, k)
+    out = moe_ffn(x, w13, w13_scale, w2, w2_scale, ids, aff, shared)
+    return ids, aff, out

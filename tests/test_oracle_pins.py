@@ -1,0 +1,331 @@
+"""Pins for the CPU oracle: each checks it against something other than itself.
+
+* torch's own float8_e4m3fn conversion (an independent library routine),
+* hand-derived closed forms stored under tests/golden/ with their citations,
+* brute-force enumeration on tiny inputs,
+* dense SwiGLU MLPs written with torch CPU fp64 library calls,
+* invariants the method must satisfy (zero affinities, token permutation,
+  linearity, sort-map structure).
+"""
+import itertools
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle
+from block_scaled_fp8_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden_lines(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return [ln.strip() for ln in f if ln.strip() and not ln.startswith("#")]
+
+
+# ----------------------------------------------------------------- E4M3FN
+def test_e4m3fn_all_codes_match_torch_cast():
+    codes = torch.arange(256, dtype=torch.int64).to(torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = oracle.e4m3fn_decode(codes.numpy())
+    nan = np.isnan(ref)
+    assert list(np.nonzero(nan)[0]) == [0x7F, 0xFF]
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    # signs of zero agree too
+    assert np.signbit(got[0x80]) and not np.signbit(got[0x00])
+
+
+def test_e4m3fn_spot_values():
+    for ln in _golden_lines("e4m3fn_spot_values.txt"):
+        code_s, val_s = ln.split()
+        code, val = int(code_s, 16), float(val_s)
+        got = oracle.e4m3fn_decode(np.array([code], np.uint8))[0]
+        if math.isnan(val):
+            assert math.isnan(got), hex(code)
+        else:
+            assert got == val and np.signbit(got) == np.signbit(val), (hex(code), got, val)
+
+
+def test_e4m3fn_structure():
+    t = oracle.e4m3fn_table()
+    assert np.isfinite(t).sum() == 254
+    pos = t[:0x7F]
+    assert np.all(np.diff(pos) > 0)                      # 0x00..0x7E strictly increasing
+    assert np.array_equal(t[0x80:0xFF], -t[0x00:0x7F])   # sign bit mirrors
+    assert t[0x7E] == oracle.E4M3FN_MAX == 448.0
+    # every finite value is exactly representable in bf16
+    fin = t[np.isfinite(t)]
+    rt = torch.tensor(fin, dtype=torch.float64).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(rt, fin)
+
+
+def test_dequant_block_indexing():
+    rng = np.random.default_rng(0)
+    R, C = 384, 256
+    scales = (2.0 ** rng.integers(-6, 6, size=(R // 128, C // 128))).astype(np.float32)
+    codes = np.full((R, C), 0x38, np.uint8)              # every code is 1.0
+    got = oracle.dequantize_blocks(codes, scales)
+    assert np.array_equal(got, np.kron(scales.astype(np.float64), np.ones((128, 128))))
+    codes[5, 200] = 0x40                                  # one element is 2.0
+    got = oracle.dequantize_blocks(codes, scales)
+    assert got[5, 200] == 2.0 * scales[0, 1]
+
+
+def test_quantiser_round_trip_bound():
+    g = torch.Generator().manual_seed(3)
+    w = torch.randn((2, 256, 384), generator=g) * 0.02
+    w[1, :128, :128] = 0.0                                # an all-zero block
+    codes, scales = synth.quantize_blocks(w)
+    deq = oracle.dequantize_blocks(codes.numpy(), scales.numpy())
+    wn = w.double().numpy()
+    s = np.repeat(np.repeat(scales.double().numpy(), 128, -2), 128, -1)
+    v = np.abs(wn) / np.where(s > 0, s, 1)
+    # half an E4M3 spacing at the magnitude of w/s (2^-10 below the normal range)
+    ulp = np.where(v >= 2.0 ** -6, 2.0 ** (np.floor(np.log2(np.maximum(v, 1e-300))) - 3), 2.0 ** -9)
+    assert np.all(np.abs(deq - wn) <= 0.5 * ulp * s * (1 + 1e-6) + 1e-30)
+    assert np.all(deq[1, :128, :128] == 0.0)
+    # the largest magnitude of each block lands on code +-448
+    blk = np.abs(codes.numpy().reshape(2, 2, 128, 3, 128).astype(np.int64) & 0x7F)
+    assert np.all((blk.max(axis=(2, 4)) == 0x7E) | (scales.numpy() == 0))
+
+
+# ----------------------------------------------------------------- routing
+def _brute_topk(row, k):
+    """The unique ordered k-subset whose members all precede the others in
+    (logit descending, index ascending); found by enumeration."""
+    E = len(row)
+
+    def before(a, b):
+        return row[a] > row[b] or (row[a] == row[b] and a < b)
+
+    found = []
+    for sub in itertools.combinations(range(E), k):
+        rest = [e for e in range(E) if e not in sub]
+        if all(before(a, b) for a in sub for b in rest):
+            found.append(sub)
+    assert len(found) == 1
+    sub = list(found[0])
+    # order inside the subset
+    out = []
+    while sub:
+        best = sub[0]
+        for e in sub[1:]:
+            if before(e, best):
+                best = e
+        out.append(best)
+        sub.remove(best)
+    return out
+
+
+def test_topk_brute_force_with_ties():
+    rng = np.random.default_rng(1)
+    vals = np.array([-1.0, -0.0, 0.0, 0.5, 1.0, 2.5], dtype=np.float32)
+    for _ in range(300):
+        E = int(rng.integers(1, 9))
+        k = int(rng.integers(1, min(E, 3) + 1))
+        T = 3
+        logits = rng.choice(vals, size=(T, E)).astype(np.float32)
+        ids, aff = oracle.route_softmax_topk(logits, k)
+        for t in range(T):
+            assert list(ids[t]) == _brute_topk(list(logits[t]), k), (logits[t], k)
+
+
+def test_route_golden_rows():
+    for ln in _golden_lines("route_closed_form.txt"):
+        k_s, l_s, i_s, a_s = [p.strip() for p in ln.split("|")]
+        logits = np.array([[float(v) for v in l_s.split()]], dtype=np.float32)
+        ids, aff = oracle.route_softmax_topk(logits, int(k_s))
+        assert list(ids[0]) == [int(v) for v in i_s.split()]
+        np.testing.assert_allclose(aff[0], [float(v) for v in a_s.split()], rtol=1e-14, atol=0)
+
+
+def test_affinities_closed_forms():
+    rng = np.random.default_rng(2)
+    logits = rng.standard_normal((16, 12)).astype(np.float32)
+    ids, aff = oracle.route_softmax_topk(logits, 4)
+    np.testing.assert_allclose(aff.sum(axis=1), 1.0, rtol=0, atol=1e-14)
+    # renormalised softmax == softmax over the selected logits alone
+    sel = np.take_along_axis(logits.astype(np.float64), ids.astype(np.int64), axis=1)
+    np.testing.assert_allclose(aff, scipy.special.softmax(sel, axis=1), rtol=1e-13)
+    # k = E: the full softmax, in rank order
+    ids_all, aff_all = oracle.route_softmax_topk(logits, 12)
+    full = scipy.special.softmax(logits.astype(np.float64), axis=1)
+    np.testing.assert_allclose(aff_all, np.take_along_axis(full, ids_all.astype(np.int64), 1),
+                               rtol=1e-13)
+    # slots are in descending logit order
+    assert np.all(np.diff(np.take_along_axis(logits, ids_all.astype(np.int64), 1), axis=1) <= 0)
+
+
+# ----------------------------------------------------------------- sort
+def _brute_sort(flat, E):
+    sorted_route = [r for e in range(E) for r in range(len(flat)) if flat[r] == e]
+    counts = [sum(1 for v in flat if v == e) for e in range(E)]
+    offsets = [0]
+    for c in counts:
+        offsets.append(offsets[-1] + c)
+    inv = [0] * len(flat)
+    for p, r in enumerate(sorted_route):
+        inv[r] = p
+    return counts, offsets, sorted_route, inv
+
+
+@pytest.mark.parametrize("T,k,E", [(1, 1, 1), (5, 2, 4), (13, 3, 7), (0, 2, 3), (40, 4, 9)])
+def test_sort_brute_force(T, k, E):
+    rng = np.random.default_rng(T * 100 + E)
+    ids = rng.integers(0, E, size=(T, k)).astype(np.int32)
+    got = oracle.sort_by_expert(ids, E)
+    exp = _brute_sort(list(ids.reshape(-1)), E)
+    for g, e in zip(got, exp):
+        assert list(g) == list(e)
+
+
+def test_sort_invariants_large():
+    rng = np.random.default_rng(7)
+    T, k, E = 4096, 8, 256
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    ids, _ = oracle.route_softmax_topk(logits, k)
+    counts, offsets, sr, inv = oracle.sort_by_expert(ids, E)
+    flat = ids.reshape(-1)
+    assert counts.sum() == T * k and offsets[0] == 0 and offsets[-1] == T * k
+    assert np.all(np.diff(offsets) == counts)
+    assert np.array_equal(np.sort(sr), np.arange(T * k))
+    assert np.array_equal(inv[sr], np.arange(T * k))
+    assert np.all(np.diff(flat[sr]) >= 0)
+    for e in range(E):
+        seg = sr[offsets[e]:offsets[e + 1]]
+        assert np.all(flat[seg] == e) and np.all(np.diff(seg) > 0)
+
+
+# ----------------------------------------------------------------- FFN
+def _torch_deq(codes, scales):
+    c = torch.as_tensor(codes).view(torch.float8_e4m3fn).to(torch.float64)
+    s = torch.as_tensor(scales).to(torch.float64)
+    return c * s.repeat_interleave(128, -2).repeat_interleave(128, -1)
+
+
+def _torch_mlp(x, w13, w13s, w2, w2s):
+    """Dense SwiGLU MLP, torch CPU fp64: down(silu(gate x) * up x)."""
+    W13 = _torch_deq(w13, w13s)
+    I = W13.shape[0] // 2
+    W1, W3 = W13[:I], W13[I:]
+    W2 = _torch_deq(w2, w2s)
+    xx = torch.as_tensor(x, dtype=torch.float64)
+    return (torch.nn.functional.silu(xx @ W1.T) * (xx @ W3.T)) @ W2.T
+
+
+def _small_case(E=4, T=6, H=256, I=128, seed=0, shared=False):
+    cfg = synth.MoeConfig("t", T=T, H=H, I=I, E=E, k=1, shared=shared)
+    c = synth.make_case(cfg, seed)
+    np_w = {n: c[n].numpy() for n in ("w13", "w13_scale", "w2", "w2_scale")}
+    sh = None
+    if shared:
+        sh = {n: c["shared"][n].numpy() for n in ("w13", "w13_scale", "w2", "w2_scale")}
+    x = c["x"].float().numpy()
+    return c, x, np_w, sh
+
+
+def test_ffn_single_expert_is_dense_swiglu_mlp():
+    c, x, w, _ = _small_case(E=1, T=7, H=384, I=256, seed=4)
+    ids = np.zeros((7, 1), np.int32)
+    aff = np.ones((7, 1))
+    got = oracle.moe_ffn(x, w["w13"], w["w13_scale"], w["w2"], w["w2_scale"], ids, aff)
+    ref = _torch_mlp(x, c["w13"][0], c["w13_scale"][0], c["w2"][0], c["w2_scale"][0]).numpy()
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+
+
+def test_ffn_all_experts_is_softmax_mixture():
+    E, T = 4, 5
+    c, x, w, _ = _small_case(E=E, T=T, seed=5)
+    logits = c["logits"].numpy()
+    ids, aff = oracle.route_softmax_topk(logits, E)
+    got = oracle.moe_ffn(x, w["w13"], w["w13_scale"], w["w2"], w["w2_scale"], ids, aff)
+    p = torch.softmax(torch.as_tensor(logits, dtype=torch.float64), dim=1)
+    ref = sum(p[:, e:e + 1] * _torch_mlp(x, c["w13"][e], c["w13_scale"][e], c["w2"][e],
+                                         c["w2_scale"][e]) for e in range(E)).numpy()
+    np.testing.assert_allclose(got, ref, rtol=1e-11, atol=1e-12 * np.abs(ref).max())
+
+
+def test_ffn_golden_closed_form():
+    H, I = 256, 128
+    w13 = np.zeros((2, 2 * I, H), np.uint8)
+    w13[0, :I] = 0x38
+    w13[0, I:] = 0x40
+    w13[1] = 0xB8
+    w13s = np.ones((2, 2, 2), np.float32)
+    w13s[0] = [[0.5, 0.125], [0.25, 4.0]]
+    w2 = np.zeros((2, H, I), np.uint8)
+    w2[0] = 0x30
+    w2[1] = 0x38
+    w2s = np.ones((2, 2, 1), np.float32)
+    w2s[0] = [[2.0], [0.5]]
+    x = np.zeros((2, H), np.float32)
+    x[0, 3] = 1.0
+    x[1, 200] = -2.0
+    logits = np.array([[3.0, 1.0], [2.0, -1.0]], np.float32)
+    ids, aff, out = oracle.moe_forward(x, logits, 1, w13, w13s, w2, w2s)
+    assert ids.tolist() == [[0], [0]] and aff.tolist() == [[1.0], [1.0]]
+    for ln in _golden_lines("ffn_closed_form.txt"):
+        t_s, lo_s, hi_s = [p.strip() for p in ln.split("|")]
+        t = int(t_s)
+        np.testing.assert_allclose(out[t, :128], float(lo_s), rtol=1e-14)
+        np.testing.assert_allclose(out[t, 128:], float(hi_s), rtol=1e-14)
+
+
+def test_ffn_zero_affinities_and_shared_expert():
+    c, x, w, sh = _small_case(E=4, T=6, seed=6, shared=True)
+    ids = synth.random_ids(6, 2, 4, 6).numpy()
+    zero = np.zeros((6, 2))
+    out = oracle.moe_ffn(x, w["w13"], w["w13_scale"], w["w2"], w["w2_scale"], ids, zero)
+    assert np.all(out == 0.0)
+    out_sh = oracle.moe_ffn(x, w["w13"], w["w13_scale"], w["w2"], w["w2_scale"], ids, zero, sh)
+    ref = _torch_mlp(x, c["shared"]["w13"], c["shared"]["w13_scale"], c["shared"]["w2"],
+                     c["shared"]["w2_scale"]).numpy()
+    np.testing.assert_allclose(out_sh, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+    # shared expert adds exactly its own MLP on top of the routed sum
+    aff = synth.random_affinities(6, 2, 6).numpy()
+    r = oracle.moe_ffn(x, w["w13"], w["w13_scale"], w["w2"], w["w2_scale"], ids, aff)
+    rs = oracle.moe_ffn(x, w["w13"], w["w13_scale"], w["w2"], w["w2_scale"], ids, aff, sh)
+    np.testing.assert_allclose(rs - r, ref, rtol=1e-10, atol=1e-12 * np.abs(ref).max())
+
+
+def test_ffn_token_permutation_and_linearity():
+    c, x, w, _ = _small_case(E=8, T=9, seed=8)
+    logits = c["logits"].numpy()
+    ids, aff, out = oracle.moe_forward(x, logits, 2, w["w13"], w["w13_scale"], w["w2"],
+                                       w["w2_scale"])
+    perm = np.random.default_rng(8).permutation(9)
+    ids_p, aff_p, out_p = oracle.moe_forward(x[perm], logits[perm], 2, w["w13"],
+                                             w["w13_scale"], w["w2"], w["w2_scale"])
+    assert np.array_equal(ids_p, ids[perm])
+    assert np.array_equal(aff_p, aff[perm])
+    assert np.array_equal(out_p, out[perm])
+    out2 = oracle.moe_ffn(x, w["w13"], w["w13_scale"], w["w2"], w["w2_scale"], ids, 2 * aff)
+    assert np.array_equal(out2, 2 * out)
+    # each route contributes aff * MLP_e(x): compare one token against torch
+    t = 4
+    ref = sum(aff[t, j] * _torch_mlp(x[t:t + 1], c["w13"][ids[t, j]], c["w13_scale"][ids[t, j]],
+                                     c["w2"][ids[t, j]], c["w2_scale"][ids[t, j]]).numpy()[0]
+              for j in range(2))
+    np.testing.assert_allclose(out[t], ref, rtol=1e-11, atol=1e-12 * np.abs(ref).max())
+
+
+def test_ffn_block_scale_is_local():
+    """Doubling one down-projection block scale changes the output by exactly that
+    block's contribution (powers of two keep it exact)."""
+    c, x, w, _ = _small_case(E=1, T=3, H=256, I=256, seed=9)
+    ids = np.zeros((3, 1), np.int32)
+    aff = np.ones((3, 1))
+    base = oracle.moe_ffn(x, w["w13"], w["w13_scale"], w["w2"], w["w2_scale"], ids, aff)
+    s2 = w["w2_scale"].copy()
+    s2[0, 1, 0] *= 2.0          # rows 128..255 of W2, K block 0
+    bumped = oracle.moe_ffn(x, w["w13"], w["w13_scale"], w["w2"], s2, ids, aff)
+    assert np.array_equal(bumped[:, :128], base[:, :128])
+    only = np.zeros_like(s2)
+    only[0, 1, 0] = w["w2_scale"][0, 1, 0]
+    block = oracle.moe_ffn(x, w["w13"], w["w13_scale"], w["w2"], only, ids, aff)
+    np.testing.assert_allclose(bumped - base, block, rtol=1e-12, atol=1e-12 * np.abs(base).max())
