@@ -1,0 +1,243 @@
+#!/usr/bin/env python3
+"""Throughput of the fused block-scaled FP8 (W8A16) routed-MoE expert FFN on one MI355X.
+
+A step is one pass of the whole hot path over one batch: softmax top-k routing,
+sort by expert, gate/up GEMM + SwiGLU, down GEMM, affinity-weighted fp32 expert
+sum.  The default workload is the decode batch (T=64 tokens, hidden 2048,
+expert intermediate 512, 256 experts, top-8).  Inputs are resident in HBM before
+timing starts; successive steps cycle through several independent weight sets
+(like successive MoE layers), so the 256 MB last-level cache cannot serve the
+weights from one step to the next.
+
+Prints ONE JSON line.  Only --gpus 1 is supported.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "fused FP8 MoE tokens/s + %HBM BW (decode T=64) / %MFMA peak (prefill T=8192)"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def expert_bytes(H, I):
+    """FP8 weight bytes + fp32 scale bytes of one expert (gate/up and down)."""
+    return 3 * H * I + 4 * (2 * I // 128) * (H // 128) + 4 * (H // 128) * (I // 128)
+
+
+def kernel_bytes(name, cfg, n_active, with_shared):
+    """Algorithmic HBM bytes one launch of a kernel must move."""
+    T, H, I, k = cfg.T, cfg.H, cfg.I, cfg.k
+    R = T * k
+    nseg = n_active + (1 if with_shared else 0)
+    rows = R + (T if with_shared else 0)
+    w13 = 2 * I * H + 4 * (2 * I // 128) * (H // 128)
+    w2 = H * I + 4 * (H // 128) * (I // 128)
+    if name.endswith("gateup_swiglu"):
+        return nseg * w13 + 2 * T * H + 2 * rows * I
+    if name.endswith("down"):
+        return nseg * w2 + 2 * rows * I + 4 * rows * H
+    if name == "combine":
+        return 4 * rows * H + 8 * R + 4 * T * H
+    if name == "route_topk_softmax":
+        return 4 * T * cfg.E + 8 * R
+    return None
+
+
+def step_bytes(cfg, n_active, with_shared):
+    """Algorithmic bytes of one whole step: active experts' weights, x, out,
+    ids + affinities, router logits."""
+    T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
+    nseg = n_active + (1 if with_shared else 0)
+    return nseg * expert_bytes(H, I) + 2 * T * H + 4 * T * H + 8 * T * k + 4 * T * E
+
+
+def step_flops(cfg, with_shared):
+    return 6.0 * cfg.H * cfg.I * (cfg.T * cfg.k + (cfg.T if with_shared else 0))
+
+
+def cpu_baseline(case, cfg, max_tokens):
+    """The oracle (numpy float64) on a bounded sample of the same workload."""
+    import numpy as np
+    import torch
+
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    n = min(cfg.T, max_tokens)
+    x = case["x"][:n].float().cpu().numpy()
+    logits = case["logits"][:n].cpu().numpy()
+    t0 = time.perf_counter()
+    ids, aff = oracle.route_softmax_topk(logits, cfg.k)
+    oracle.sort_by_expert(ids, cfg.E)
+    t1 = time.perf_counter()
+    # host copies of the experts the sample uses (not timed)
+    uniq = np.unique(ids)
+    sel = torch.as_tensor(uniq, dtype=torch.long, device=case["w13"].device)
+    w13 = case["w13"].index_select(0, sel).cpu().numpy()
+    w13s = case["w13_scale"].index_select(0, sel).cpu().numpy()
+    w2 = case["w2"].index_select(0, sel).cpu().numpy()
+    w2s = case["w2_scale"].index_select(0, sel).cpu().numpy()
+    sh = None
+    if case.get("shared") is not None:
+        sh = {kk: v.cpu().numpy() for kk, v in case["shared"].items()}
+    remap = np.searchsorted(uniq, ids)
+    t2 = time.perf_counter()
+    oracle.moe_ffn(x, w13, w13s, w2, w2s, remap, aff, sh)
+    t3 = time.perf_counter()
+    secs = (t1 - t0) + (t3 - t2)
+    return {"value": round(n / secs, 2), "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{n} of {cfg.T} tokens of {cfg.name}: route + sort + expert FFN in numpy "
+                      f"float64 ({len(uniq)} experts dequantised); host copy of weights not timed",
+            "seconds": round(secs, 3)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="decode64")
+    ap.add_argument("--weight-sets", type=int, default=4)
+    ap.add_argument("--variant", default="auto", choices=["auto", "decode", "prefill"])
+    ap.add_argument("--cpu-tokens", type=int, default=64)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB, 5 times (PMC byte-counter "
+                         "calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE={world}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from block_scaled_fp8_amd import binding, synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        a = torch.ones(n, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_launch": n, "launches": 5}), flush=True)
+        return
+    binding.load_library()
+    cfg = synth.CONFIGS[args.workload]
+    L = max(1, args.weight_sets)
+    log(f"workload {cfg.name}: T={cfg.T} H={cfg.H} I={cfg.I} E={cfg.E} k={cfg.k} "
+        f"shared={cfg.shared}, {L} weight sets")
+
+    x, logits = synth.make_activations(cfg, args.seed, dev)
+    wsets = [synth.make_weights(cfg, args.seed + 100 * i, dev) for i in range(L)]
+    steps = [binding.MoeStep(x, logits, cfg.k, w["w13"], w["w13_scale"], w["w2"], w["w2_scale"],
+                             shared=w["shared"], variant=args.variant) for w in wsets]
+    torch.cuda.synchronize()
+
+    # routing facts for the algorithmic byte counts (outside the timed region)
+    ids, _ = binding.route(logits, cfg.k)
+    counts = torch.bincount(ids.reshape(-1).long(), minlength=cfg.E)
+    n_active = int((counts > 0).sum().item())
+    log(f"active experts {n_active}, max routes/expert {int(counts.max().item())}")
+
+    for i in range(args.warmup):
+        steps[i % L]()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        steps[i % L]()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / K
+    log(f"timed {K} steps: {ms_per_step * 1e3:.1f} us/step")
+
+    # the same region again with per-kernel HIP events on the launch stream
+    binding.profile_enable(True)
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    for i in range(K):
+        steps[i % L]()
+    torch.cuda.synchronize()
+    t3 = time.perf_counter()
+    binding.profile_enable(False)
+    prof = binding.profile_collect()
+    ms_profiled = (t3 - t2) * 1e3 / K
+    kernels = {n: {"launches": c, "avg_us": round(ms * 1e3, 3)} for n, (c, ms) in prof.items()}
+    for n, v in sorted(kernels.items(), key=lambda kv: -kv[1]["launches"] * kv[1]["avg_us"]):
+        log(f"  {n:24s} {v['launches']:6d} x {v['avg_us']:9.2f} us")
+
+    dom = max(prof.items(), key=lambda kv: kv[1][0] * kv[1][1])[0]
+    dom_bytes = kernel_bytes(dom, cfg, n_active, cfg.shared)
+    dom_ms = prof[dom][1]
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9 if dom_bytes else None
+    roofline = {"bound": "hbm", "kernel": dom,
+                "achieved": round(achieved, 1) if achieved else None,
+                "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4) if achieved else None,
+                "traffic": None,
+                "bytes_per_launch": dom_bytes, "avg_us": round(dom_ms * 1e3, 3)}
+
+    sb = step_bytes(cfg, n_active, cfg.shared)
+    sf = step_flops(cfg, cfg.shared)
+    tokens_per_s = cfg.T / (ms_per_step * 1e-3)
+    result = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "T": cfg.T, "hidden": cfg.H, "moe_inter": cfg.I,
+                   "experts": cfg.E, "top_k": cfg.k, "shared_expert": cfg.shared,
+                   "weights": "E4M3FN, fp32 128x128 block scales", "weight_sets": L,
+                   "variant": args.variant, "active_experts": n_active},
+        "roofline": roofline,
+        "step": {"algorithmic_bytes": sb, "GB_per_s": round(sb / (ms_per_step * 1e-3) / 1e9, 1),
+                 "hbm_frac": round(sb / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                 "TFLOP_per_s": round(sf / (ms_per_step * 1e-3) / 1e12, 2),
+                 "ms_per_step_profiled": round(ms_profiled, 5)},
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        case = dict(x=x, logits=logits, **wsets[0])
+        result["cpu_baseline"] = cpu_baseline(case, cfg, args.cpu_tokens)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

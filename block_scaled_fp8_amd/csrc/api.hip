@@ -1,0 +1,358 @@
+// C ABI of the block-scaled FP8 routed MoE expert FFN (see include/moe_w8a16.h).
+//
+// Host-side contract checks follow "spark_model/layers/nemotron_moe.rs" (the
+// layer constructor validates top_k against 1..=E and the expert count
+// against a maximum, failing with a message) and the AITER PR page (tensor
+// contracts validated in the launcher, caller-provided outputs, scratch kept
+// below the dispatch, unsupported geometry rejected).  Nothing here allocates,
+// synchronises or reads device memory back.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "common.hpp"
+#include "plan.hpp"
+
+namespace moe {
+
+static thread_local char g_err[512] = "";
+
+void set_error(const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+}
+
+int check_launch(const char* what) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) {
+        set_error("%s: launch failed: %s", what, hipGetErrorString(e));
+        return MOE_EHIP;
+    }
+    return MOE_OK;
+}
+
+// Workspace carve-up for moe_fused_w8a16 (256-byte aligned pieces).
+struct FusedLayout {
+    size_t counts, offsets, sorted_route, inv_route, seg_n, seg_expert, seg_row0, seg_rows,
+        seg_tile0, sort_scratch, abuf, ybuf, total;
+};
+
+static FusedLayout fused_layout(int T, int H, int I, int E, int k, int has_shared) {
+    FusedLayout L;
+    const size_t R = (size_t)T * k;
+    const size_t rows = R + (has_shared ? (size_t)T : 0);
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = o;
+        o += halign(bytes);
+        return at;
+    };
+    L.counts = take(sizeof(int32_t) * E);
+    L.offsets = take(sizeof(int32_t) * (E + 1));
+    L.sorted_route = take(sizeof(int32_t) * R);
+    L.inv_route = take(sizeof(int32_t) * R);
+    L.seg_n = take(sizeof(int32_t));
+    L.seg_expert = take(sizeof(int32_t) * (E + 1));
+    L.seg_row0 = take(sizeof(int32_t) * (E + 1));
+    L.seg_rows = take(sizeof(int32_t) * (E + 1));
+    L.seg_tile0 = take(sizeof(int32_t) * (E + 2));
+    L.sort_scratch = take(sort_scratch_bytes((int)R, E));
+    L.abuf = take(sizeof(uint16_t) * rows * I);
+    L.ybuf = take(sizeof(float) * rows * H);
+    L.total = o;
+    return L;
+}
+
+static int check_route_args(int T, int E, int k) {
+    if (T < 0) {
+        set_error("T must be >= 0 (got %d)", T);
+        return MOE_EINVAL;
+    }
+    if (E < 1 || E > MOE_MAX_EXPERTS) {
+        set_error("E must be in 1..%d (got %d)", MOE_MAX_EXPERTS, E);
+        return MOE_EINVAL;
+    }
+    if (k < 1 || k > E || k > MOE_MAX_TOPK) {
+        set_error("k must be in 1..min(E, %d) (got k=%d, E=%d)", MOE_MAX_TOPK, k, E);
+        return MOE_EINVAL;
+    }
+    if ((long long)T * k > (1LL << 30)) {
+        set_error("T*k too large (%lld)", (long long)T * k);
+        return MOE_EINVAL;
+    }
+    return MOE_OK;
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+const char* moe_last_error(void) { return g_err; }
+
+int moe_route(const float* logits, int T, int E, int k, int32_t* ids, float* aff,
+              int32_t* status, void* stream) {
+    g_err[0] = 0;
+    if (int rc = check_route_args(T, E, k)) return rc;
+    if (T == 0) return MOE_OK;
+    if (!logits || !ids || !aff) {
+        set_error("moe_route: logits, ids and aff must be non-NULL");
+        return MOE_EINVAL;
+    }
+    return launch_route(logits, T, E, k, ids, aff, status, (hipStream_t)stream);
+}
+
+size_t moe_sort_workspace_bytes(int T, int k, int E) {
+    if (T < 0 || k < 1 || E < 1) return 0;
+    return sort_scratch_bytes(T * k, E);
+}
+
+int moe_sort(const int32_t* ids, int T, int k, int E, int32_t* counts, int32_t* offsets,
+             int32_t* sorted_route, int32_t* inv_route, int32_t* status, void* ws,
+             size_t ws_bytes, void* stream) {
+    g_err[0] = 0;
+    if (int rc = check_route_args(T, E, k)) return rc;
+    if (!counts || !offsets) {
+        set_error("moe_sort: counts and offsets must be non-NULL");
+        return MOE_EINVAL;
+    }
+    if (T > 0 && (!ids || !sorted_route || !inv_route)) {
+        set_error("moe_sort: ids, sorted_route and inv_route must be non-NULL");
+        return MOE_EINVAL;
+    }
+    const size_t need = sort_scratch_bytes(T * k, E);
+    if (need && (!ws || ws_bytes < need)) {
+        set_error("moe_sort: workspace of %zu bytes needed (got %zu)", need, ws_bytes);
+        return MOE_EINVAL;
+    }
+    Plan p{};
+    p.counts = counts;
+    p.offsets = offsets;
+    p.sorted_route = sorted_route;
+    p.inv_route = inv_route;
+    if (T == 0) {
+        // empty input: zero counts and offsets
+        if (int rc = launch_fill_i32(counts, 0, E, (hipStream_t)stream)) return rc;
+        return launch_fill_i32(offsets, 0, E + 1, (hipStream_t)stream);
+    }
+    return launch_sort(ids, T, k, E, p, 0, 1, status, ws, (hipStream_t)stream);
+}
+
+size_t moe_fused_workspace_bytes(int T, int H, int I, int E, int k, int has_shared,
+                                 int variant) {
+    (void)variant;
+    if (T < 0 || H < 1 || I < 1 || E < 1 || k < 1) return 0;
+    return fused_layout(T, H, I, E, k, has_shared ? 1 : 0).total;
+}
+
+int moe_fused_w8a16(const void* x, const uint8_t* w13, const float* w13_scale,
+                    const uint8_t* w2, const float* w2_scale, const int32_t* ids,
+                    const float* aff, int T, int H, int I, int E, int k,
+                    const moe_expert_w8* shared, float* out, int32_t* status, void* ws,
+                    size_t ws_bytes, int variant, void* stream) {
+    g_err[0] = 0;
+    if (int rc = check_route_args(T, E, k)) return rc;
+    if (H < 128 || I < 128 || H % 128 || I % 128) {
+        set_error("H and I must be positive multiples of 128 (got H=%d, I=%d)", H, I);
+        return MOE_EUNSUPPORTED;
+    }
+    if ((long long)H * I * 3 > (1LL << 40)) {
+        set_error("expert too large (H=%d, I=%d)", H, I);
+        return MOE_EUNSUPPORTED;
+    }
+    if (variant < MOE_VARIANT_AUTO || variant > MOE_VARIANT_PREFILL) {
+        set_error("unknown variant %d", variant);
+        return MOE_EINVAL;
+    }
+    if (T == 0) return MOE_OK;
+    if (!x || !w13 || !w13_scale || !w2 || !w2_scale || !ids || !aff || !out) {
+        set_error("moe_fused_w8a16: x, weights, scales, ids, aff and out must be non-NULL");
+        return MOE_EINVAL;
+    }
+    if (shared && (!shared->w13 || !shared->w13_scale || !shared->w2 || !shared->w2_scale)) {
+        set_error("moe_fused_w8a16: shared expert descriptor has a NULL member");
+        return MOE_EINVAL;
+    }
+    if ((const void*)out == x) {
+        set_error("moe_fused_w8a16: out must not alias x");
+        return MOE_EINVAL;
+    }
+    const int has_shared = shared ? 1 : 0;
+    const FusedLayout L = fused_layout(T, H, I, E, k, has_shared);
+    if (!ws || ws_bytes < L.total) {
+        set_error("moe_fused_w8a16: workspace of %zu bytes needed (got %zu)", L.total, ws_bytes);
+        return MOE_EINVAL;
+    }
+    if (variant == MOE_VARIANT_AUTO)
+        variant = MOE_VARIANT_DECODE;
+
+    char* base = static_cast<char*>(ws);
+    Plan p;
+    p.counts = reinterpret_cast<int32_t*>(base + L.counts);
+    p.offsets = reinterpret_cast<int32_t*>(base + L.offsets);
+    p.sorted_route = reinterpret_cast<int32_t*>(base + L.sorted_route);
+    p.inv_route = reinterpret_cast<int32_t*>(base + L.inv_route);
+    p.seg_n = reinterpret_cast<int32_t*>(base + L.seg_n);
+    p.seg_expert = reinterpret_cast<int32_t*>(base + L.seg_expert);
+    p.seg_row0 = reinterpret_cast<int32_t*>(base + L.seg_row0);
+    p.seg_rows = reinterpret_cast<int32_t*>(base + L.seg_rows);
+    p.seg_tile0 = reinterpret_cast<int32_t*>(base + L.seg_tile0);
+    uint16_t* abuf = reinterpret_cast<uint16_t*>(base + L.abuf);
+    float* ybuf = reinterpret_cast<float*>(base + L.ybuf);
+    hipStream_t s = (hipStream_t)stream;
+
+    SharedW sh{nullptr, nullptr, nullptr, nullptr};
+    if (shared) sh = SharedW{shared->w13, shared->w13_scale, shared->w2, shared->w2_scale};
+
+    const int tile_m = variant == MOE_VARIANT_PREFILL ? prefill_tile_m() : 1;
+    if (int rc = launch_sort(ids, T, k, E, p, has_shared, tile_m, status, base + L.sort_scratch, s))
+        return rc;
+    const uint16_t* xb = static_cast<const uint16_t*>(x);
+    int rc;
+    if (variant == MOE_VARIANT_DECODE)
+        rc = launch_decode_ffn(xb, w13, w13_scale, w2, w2_scale, sh, p, T, H, I, E, k, abuf, ybuf, s);
+    else
+        rc = launch_prefill_ffn(xb, w13, w13_scale, w2, w2_scale, sh, p, T, H, I, E, k, abuf, ybuf,
+                                s);
+    if (rc) return rc;
+    return launch_combine(ybuf, p.inv_route, aff, T, H, k, has_shared, out, s);
+}
+
+int moe_decode_e4m3fn(const uint8_t* codes, uint16_t* out, int64_t n, void* stream) {
+    g_err[0] = 0;
+    if (n < 0) {
+        set_error("moe_decode_e4m3fn: n must be >= 0");
+        return MOE_EINVAL;
+    }
+    if (n == 0) return MOE_OK;
+    if (!codes || !out) {
+        set_error("moe_decode_e4m3fn: codes and out must be non-NULL");
+        return MOE_EINVAL;
+    }
+    return launch_decode_e4m3fn(codes, out, n, (hipStream_t)stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- profiling
+#include <mutex>
+#include <string>
+#include <vector>
+
+namespace moe {
+namespace {
+struct ProfRecord {
+    const char* name;
+    hipEvent_t start, stop;
+};
+struct ProfStat {
+    std::string name;
+    int64_t launches = 0;
+    double total_ms = 0.0;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<hipEvent_t> g_prof_pool;
+std::vector<ProfRecord> g_prof_open;   // begun, not yet ended (per call, at most one)
+std::vector<ProfRecord> g_prof_done;
+std::vector<ProfStat> g_prof_stats;
+constexpr size_t kMaxPending = 1 << 16;
+
+hipEvent_t prof_event() {
+    if (!g_prof_pool.empty()) {
+        hipEvent_t e = g_prof_pool.back();
+        g_prof_pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+}  // namespace
+
+void prof_begin(const char* name, hipStream_t stream) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    if (!g_prof_on || g_prof_done.size() >= kMaxPending) return;
+    hipEvent_t a = prof_event(), b = prof_event();
+    if (!a || !b) return;
+    if (hipEventRecord(a, stream) != hipSuccess) {
+        g_prof_pool.push_back(a);
+        g_prof_pool.push_back(b);
+        return;
+    }
+    g_prof_open.push_back(ProfRecord{name, a, b});
+}
+
+void prof_end(hipStream_t stream) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    if (g_prof_open.empty()) return;
+    ProfRecord r = g_prof_open.back();
+    g_prof_open.pop_back();
+    if (hipEventRecord(r.stop, stream) != hipSuccess) {
+        g_prof_pool.push_back(r.start);
+        g_prof_pool.push_back(r.stop);
+        return;
+    }
+    g_prof_done.push_back(r);
+}
+
+}  // namespace moe
+
+extern "C" {
+
+int moe_profile_enable(int on) {
+    std::lock_guard<std::mutex> lk(moe::g_prof_mu);
+    if (on) moe::g_prof_stats.clear();
+    moe::g_prof_on = on != 0;
+    return MOE_OK;
+}
+
+int moe_profile_collect(void) {
+    std::lock_guard<std::mutex> lk(moe::g_prof_mu);
+    int rc = MOE_OK;
+    for (const auto& r : moe::g_prof_done) {
+        float ms = 0.f;
+        if (hipEventSynchronize(r.stop) != hipSuccess ||
+            hipEventElapsedTime(&ms, r.start, r.stop) != hipSuccess) {
+            moe::set_error("moe_profile_collect: event query failed");
+            rc = MOE_EHIP;
+        } else {
+            moe::ProfStat* st = nullptr;
+            for (auto& s : moe::g_prof_stats)
+                if (s.name == r.name) st = &s;
+            if (!st) {
+                moe::g_prof_stats.push_back(moe::ProfStat{r.name, 0, 0.0});
+                st = &moe::g_prof_stats.back();
+            }
+            st->launches += 1;
+            st->total_ms += ms;
+        }
+        moe::g_prof_pool.push_back(r.start);
+        moe::g_prof_pool.push_back(r.stop);
+    }
+    moe::g_prof_done.clear();
+    return rc;
+}
+
+int moe_profile_count(void) {
+    std::lock_guard<std::mutex> lk(moe::g_prof_mu);
+    return (int)moe::g_prof_stats.size();
+}
+
+int moe_profile_stat(int i, char* name, int name_len, int64_t* launches, double* total_ms) {
+    std::lock_guard<std::mutex> lk(moe::g_prof_mu);
+    if (i < 0 || i >= (int)moe::g_prof_stats.size() || !name || name_len < 1 || !launches ||
+        !total_ms) {
+        moe::set_error("moe_profile_stat: bad index or NULL output");
+        return MOE_EINVAL;
+    }
+    const auto& s = moe::g_prof_stats[i];
+    snprintf(name, (size_t)name_len, "%s", s.name.c_str());
+    *launches = s.launches;
+    *total_ms = s.total_ms;
+    return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,103 @@
+// Device helpers shared by the MoE kernels (gfx950 / CDNA4, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe_w8a16.h"
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define MOE_WAVE 64
+
+namespace moe {
+
+// ---------------------------------------------------------------- FP8 decode
+// Two E4M3FN bytes (byte 0/1 of `w` when hi == false, 2/3 when true) to two
+// bf16 values with the gfx950 scaled converter at scale 1.0.  Every finite
+// E4M3FN value (4 significant bits, |v| in [2^-9, 448]) is a bf16 value, so
+// this is exact.
+__device__ __forceinline__ bf16x2 fp8x2_to_bf16x2(uint32_t w, bool hi) {
+    return hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)
+              : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+}
+
+// 8 FP8 bytes (two dwords, little-endian byte order) -> 8 bf16, element i = byte i.
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
+    bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+    bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+    bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+    bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+    bf16x8 r;
+    r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+    r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+    return r;
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+// ---------------------------------------------------------------- bf16 <-> f32
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+    return __uint_as_float(((uint32_t)b) << 16);
+}
+
+// Round to nearest even (inputs here are finite).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    uint32_t r = u + 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(r >> 16);
+}
+
+// ---------------------------------------------------------------- SwiGLU
+// silu(g) * u with silu(g) = g / (1 + exp(-g)).
+__device__ __forceinline__ float swiglu(float g, float u) {
+    return g / (1.0f + __expf(-g)) * u;
+}
+
+// ---------------------------------------------------------------- wave helpers
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (MOE_WAVE - 1); }
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+    const int l = lane_id();
+    return l == 0 ? 0ull : (~0ull >> (64 - l));
+}
+
+__device__ __forceinline__ int wave_sum_i32(int v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, MOE_WAVE);
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum_f32(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, MOE_WAVE);
+    return v;
+}
+
+// Inclusive scan over the wave (lane order).
+__device__ __forceinline__ int wave_incl_scan_i32(int v) {
+    const int l = lane_id();
+#pragma unroll
+    for (int o = 1; o < MOE_WAVE; o <<= 1) {
+        int n = __shfl_up(v, o, MOE_WAVE);
+        if (l >= o) v += n;
+    }
+    return v;
+}
+
+__device__ __forceinline__ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+}  // namespace moe
+
+// Host-side helpers (defined in api.hip).
+namespace moe {
+void set_error(const char* fmt, ...);
+int check_launch(const char* what);
+inline size_t halign(size_t v, size_t a = 256) { return (v + a - 1) / a * a; }
+}  // namespace moe

@@ -1,0 +1,326 @@
+// Decode variant of the expert FFN: weight-bandwidth-bound streaming kernels.
+//
+// Source: "Gated DeltaNet (+ FP8 MoE) -- AWS Neuron (NKI) kernels for
+// Trainium2", section "FP8 MoE decode kernel (moe_fused_w8_35b)": gate/up GEMM
+// -> SwiGLU -> down GEMM -> affinity scale -> expert-sum, E4M3FN weights with
+// 128x128 block scales decoded to BF16 tile by tile; at decode the expert
+// weights dominate the bytes moved.
+//
+// Design (gfx950): one workgroup per (segment, N tile) with segments = active
+// experts (plus the shared expert), so each active expert's weights are read
+// from HBM once.  The 4 waves of a workgroup split the contraction dimension;
+// each wave streams 16-byte FP8 fragments directly in the register layout of
+// v_mfma_f32_16x16x32_bf16 (lane l: weight row l%16, 16 consecutive K bytes
+// at 16*(l/16) inside each 64-wide K chunk), converts them exactly to bf16
+// and multiplies against the token rows (M = 16 per MFMA tile).  The same K
+// permutation is used for the token operand, so the dot products are exact
+// sums over K.  Each 128-wide K block accumulates into a fresh fp32 partial
+// that is multiplied by the block's fp32 scale before joining the total, so
+// the scale is never rounded into bf16.
+#include "common.hpp"
+#include "plan.hpp"
+
+namespace moe {
+
+enum { MODE_GATEUP = 0, MODE_DOWN = 1 };
+
+constexpr int DEC_THREADS = 256;
+constexpr int DEC_WAVES = 4;
+constexpr int DEC_NTILE = 4;   // 16-row weight tiles per workgroup
+constexpr int DEC_DEPTH = 4;   // 64-K chunks in flight per wave
+
+// MODE_GATEUP: rows = 32 gate rows + the 32 matching up rows, K = H,
+//              A = x rows of the segment's tokens, out = bf16 SwiGLU into abuf.
+// MODE_DOWN:   rows = 64 rows of W2, K = I, A = abuf rows, out = fp32 ybuf.
+template <int MODE, int MT>
+__global__ __launch_bounds__(DEC_THREADS) void decode_ffn_kernel(
+    const uint16_t* __restrict__ x, const uint8_t* __restrict__ w13,
+    const float* __restrict__ w13s, const uint8_t* __restrict__ w2,
+    const float* __restrict__ w2s, SharedW shared, Plan plan, int T, int H, int I, int k,
+    uint16_t* __restrict__ abuf, float* __restrict__ ybuf) {
+    constexpr int MROWS = 16 * MT;
+    const int K = MODE == MODE_GATEUP ? H : I;
+    const int ntile_per_seg = MODE == MODE_GATEUP ? I / 32 : H / 64;
+    const int seg = blockIdx.x / ntile_per_seg;
+    const int nt = blockIdx.x % ntile_per_seg;
+    if (seg >= plan.seg_n[0]) return;
+    const int e = plan.seg_expert[seg];
+    const int row0 = plan.seg_row0[seg];
+    const int rows = plan.seg_rows[seg];
+
+    const uint8_t* W;
+    const float* S;
+    if (MODE == MODE_GATEUP) {
+        W = e >= 0 ? w13 + (size_t)e * 2 * I * H : shared.w13;
+        S = e >= 0 ? w13s + (size_t)e * (2 * I / 128) * (H / 128) : shared.w13_scale;
+    } else {
+        W = e >= 0 ? w2 + (size_t)e * H * I : shared.w2;
+        S = e >= 0 ? w2s + (size_t)e * (H / 128) * (I / 128) : shared.w2_scale;
+    }
+    const int kblocks = K / 128;
+
+    const int lane = lane_id(), wave = threadIdx.x / MOE_WAVE;
+    const int ln = lane & 15, lg = lane >> 4;
+
+    // weight rows of the 4 tiles
+    int brow[DEC_NTILE];
+#pragma unroll
+    for (int j = 0; j < DEC_NTILE; ++j) {
+        if (MODE == MODE_GATEUP)
+            brow[j] = (j < 2 ? 0 : I) + nt * 32 + (j & 1) * 16;
+        else
+            brow[j] = nt * 64 + j * 16;
+    }
+    const uint8_t* bptr[DEC_NTILE];
+#pragma unroll
+    for (int j = 0; j < DEC_NTILE; ++j) bptr[j] = W + (size_t)(brow[j] + ln) * K + lg * 16;
+
+    // this wave's 64-K chunks
+    const int nchunk = K / 64;
+    const int per = (nchunk + DEC_WAVES - 1) / DEC_WAVES;
+    const int cb = min(nchunk, wave * per), ce = min(nchunk, cb + per);
+
+    __shared__ float red[DEC_WAVES][MT][DEC_NTILE][4][MOE_WAVE];
+    __shared__ int tok_s[MROWS];
+
+    const size_t R = (size_t)T * k;
+    for (int mp = 0; mp < rows; mp += MROWS) {
+        // token (or abuf row) of each of the MROWS rows of this pass
+        __syncthreads();
+        if (threadIdx.x < MROWS) {
+            const int m = mp + threadIdx.x;
+            int src = -1;
+            if (m < rows) {
+                const int p = row0 + m;
+                if (MODE == MODE_GATEUP)
+                    src = e >= 0 ? plan.sorted_route[p] / k : p - (int)R;
+                else
+                    src = p;
+            }
+            tok_s[threadIdx.x] = src;
+        }
+        __syncthreads();
+        const uint16_t* aptr[MT];
+        bool avalid[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const int src = tok_s[mt * 16 + ln];
+            avalid[mt] = src >= 0;
+            const int s = src >= 0 ? src : 0;
+            aptr[mt] = (MODE == MODE_GATEUP ? x + (size_t)s * H : abuf + (size_t)s * I) + lg * 16;
+        }
+
+        f32x4 acc[MT][DEC_NTILE], part[MT][DEC_NTILE];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int j = 0; j < DEC_NTILE; ++j) {
+                acc[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+                part[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+
+        u32x4 bq[DEC_DEPTH][DEC_NTILE];
+        u32x4 aq[DEC_DEPTH][MT][2];
+        auto issue = [&](int d, int c) {
+#pragma unroll
+            for (int j = 0; j < DEC_NTILE; ++j)
+                bq[d][j] = *reinterpret_cast<const u32x4*>(bptr[j] + (size_t)c * 64);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const u32x4* ap = reinterpret_cast<const u32x4*>(aptr[mt] + (size_t)c * 64);
+                aq[d][mt][0] = ap[0];
+                aq[d][mt][1] = ap[1];
+            }
+        };
+#pragma unroll
+        for (int d = 0; d < DEC_DEPTH; ++d)
+            if (cb + d < ce) issue(d, cb + d);
+
+        for (int c0 = cb; c0 < ce; c0 += DEC_DEPTH) {
+#pragma unroll
+            for (int d = 0; d < DEC_DEPTH; ++d) {
+                const int c = c0 + d;
+                if (c < ce) {
+#pragma unroll
+                    for (int s = 0; s < 2; ++s) {
+                        bf16x8 bfrag[DEC_NTILE];
+#pragma unroll
+                        for (int j = 0; j < DEC_NTILE; ++j)
+                            bfrag[j] = s == 0 ? fp8x8_to_bf16x8(bq[d][j][0], bq[d][j][1])
+                                              : fp8x8_to_bf16x8(bq[d][j][2], bq[d][j][3]);
+#pragma unroll
+                        for (int mt = 0; mt < MT; ++mt) {
+                            u32x4 av = aq[d][mt][s];
+                            if (!avalid[mt]) av = u32x4{0u, 0u, 0u, 0u};
+                            const bf16x8 afrag = as_bf16x8(av);
+#pragma unroll
+                            for (int j = 0; j < DEC_NTILE; ++j)
+                                part[mt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                    afrag, bfrag[j], part[mt][j], 0, 0, 0);
+                        }
+                    }
+                    if (c + DEC_DEPTH < ce) issue(d, c + DEC_DEPTH);
+                    if ((c & 1) == 1 || c == ce - 1) {
+                        const int kb = c >> 1;
+#pragma unroll
+                        for (int j = 0; j < DEC_NTILE; ++j) {
+                            const float sc = S[(size_t)(brow[j] / 128) * kblocks + kb];
+#pragma unroll
+                            for (int mt = 0; mt < MT; ++mt) {
+                                acc[mt][j] += sc * part[mt][j];
+                                part[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+                            }
+                        }
+                    }
+                }
+            }
+        }
+
+        // cross-wave reduction of the K split
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int j = 0; j < DEC_NTILE; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) red[wave][mt][j][i][lane] = acc[mt][j][i];
+        __syncthreads();
+
+        if (MODE == MODE_GATEUP) {
+            // items: (mt, pair p) with gate tile p and up tile 2 + p
+            for (int item = wave; item < MT * 2; item += DEC_WAVES) {
+                const int mt = item >> 1, p = item & 1;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float g = 0.f, u = 0.f;
+#pragma unroll
+                    for (int v = 0; v < DEC_WAVES; ++v) {
+                        g += red[v][mt][p][i][lane];
+                        u += red[v][mt][2 + p][i][lane];
+                    }
+                    const int m = mp + mt * 16 + lg * 4 + i;
+                    if (m < rows) {
+                        const int col = nt * 32 + p * 16 + ln;
+                        abuf[(size_t)(row0 + m) * I + col] = f32_to_bf16_bits(swiglu(g, u));
+                    }
+                }
+            }
+        } else {
+            for (int item = wave; item < MT * DEC_NTILE; item += DEC_WAVES) {
+                const int mt = item / DEC_NTILE, j = item % DEC_NTILE;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float y = 0.f;
+#pragma unroll
+                    for (int v = 0; v < DEC_WAVES; ++v) y += red[v][mt][j][i][lane];
+                    const int m = mp + mt * 16 + lg * 4 + i;
+                    if (m < rows) ybuf[(size_t)(row0 + m) * H + brow[j] + ln] = y;
+                }
+            }
+        }
+    }
+}
+
+// out[t] = sum_j aff[t,j] * y[inv_route[t*k+j]]  (+ y[R + t] for the shared
+// expert), in slot order, fp32.  Source: AITER PR page (FP32 route
+// reduction); NKI page (affinity scale -> expert-sum, shared expert added
+// after the routed sum).
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ ybuf,
+                                                      const int32_t* __restrict__ inv_route,
+                                                      const float* __restrict__ aff, int T, int H,
+                                                      int k, int has_shared,
+                                                      float* __restrict__ out) {
+    const int t = blockIdx.y;
+    const int h = (blockIdx.x * 256 + threadIdx.x) * 4;
+    if (h >= H) return;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < k; ++j) {
+        const int p = inv_route[(size_t)t * k + j];
+        if (p >= 0) {
+            const float a = aff[(size_t)t * k + j];
+            const f32x4 y = *reinterpret_cast<const f32x4*>(ybuf + (size_t)p * H + h);
+            acc += a * y;
+        }
+    }
+    if (has_shared) {
+        const size_t R = (size_t)T * k;
+        acc += *reinterpret_cast<const f32x4*>(ybuf + (R + t) * H + h);
+    }
+    *reinterpret_cast<f32x4*>(out + (size_t)t * H + h) = acc;
+}
+
+template <int MODE>
+static int launch_decode_mode(int MT, int nseg_max, const uint16_t* x, const uint8_t* w13,
+                              const float* w13s, const uint8_t* w2, const float* w2s,
+                              const SharedW& sh, const Plan& plan, int T, int H, int I, int k,
+                              uint16_t* abuf, float* ybuf, hipStream_t stream) {
+    const int ntile = MODE == MODE_GATEUP ? I / 32 : H / 64;
+    const dim3 grid((unsigned)nseg_max * ntile), block(DEC_THREADS);
+    prof_begin(MODE == MODE_GATEUP ? "decode_gateup_swiglu" : "decode_down", stream);
+    if (MT == 1)
+        decode_ffn_kernel<MODE, 1><<<grid, block, 0, stream>>>(x, w13, w13s, w2, w2s, sh, plan, T,
+                                                               H, I, k, abuf, ybuf);
+    else
+        decode_ffn_kernel<MODE, 2><<<grid, block, 0, stream>>>(x, w13, w13s, w2, w2s, sh, plan, T,
+                                                               H, I, k, abuf, ybuf);
+    prof_end(stream);
+    return check_launch(MODE == MODE_GATEUP ? "decode_ffn_kernel<gateup>" : "decode_ffn_kernel<down>");
+}
+
+int launch_decode_ffn(const uint16_t* x, const uint8_t* w13, const float* w13s, const uint8_t* w2,
+                      const float* w2s, const SharedW& sh, const Plan& plan, int T, int H, int I,
+                      int E, int k, uint16_t* abuf, float* ybuf, hipStream_t stream) {
+    const int has_shared = sh.w13 != nullptr;
+    const int nseg_max = E + has_shared;
+    const int MT = ((long)T * k <= 4L * E) ? 1 : 2;
+    if (int rc = launch_decode_mode<MODE_GATEUP>(MT, nseg_max, x, w13, w13s, w2, w2s, sh, plan, T,
+                                                 H, I, k, abuf, ybuf, stream))
+        return rc;
+    return launch_decode_mode<MODE_DOWN>(MT, nseg_max, x, w13, w13s, w2, w2s, sh, plan, T, H, I,
+                                         k, abuf, ybuf, stream);
+}
+
+int launch_combine(const float* ybuf, const int32_t* inv_route, const float* aff, int T, int H,
+                   int k, int has_shared, float* out, hipStream_t stream) {
+    const dim3 grid((H / 4 + 255) / 256, T), block(256);
+    prof_begin("combine", stream);
+    combine_kernel<<<grid, block, 0, stream>>>(ybuf, inv_route, aff, T, H, k, has_shared, out);
+    prof_end(stream);
+    return check_launch("combine_kernel");
+}
+
+// n E4M3FN bytes -> bf16 bit patterns, with the FFN kernels' converter.
+__global__ __launch_bounds__(256) void decode_e4m3fn_kernel(const uint8_t* __restrict__ codes,
+                                                            uint16_t* __restrict__ out, int64_t n) {
+    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 2;
+    if (i >= n) return;
+    const uint32_t w = (uint32_t)codes[i] | (i + 1 < n ? (uint32_t)codes[i + 1] << 8 : 0u);
+    // split the converted pair as one 32-bit word (element 0 in the low half)
+    const uint32_t v = __builtin_bit_cast(uint32_t, fp8x2_to_bf16x2(w, false));
+    out[i] = (uint16_t)(v & 0xFFFFu);
+    if (i + 1 < n) out[i + 1] = (uint16_t)(v >> 16);
+}
+
+int launch_decode_e4m3fn(const uint8_t* codes, uint16_t* out, int64_t n, hipStream_t stream) {
+    const int64_t blocks = (n + 511) / 512;
+    prof_begin("decode_e4m3fn", stream);
+    decode_e4m3fn_kernel<<<(unsigned)blocks, 256, 0, stream>>>(codes, out, n);
+    prof_end(stream);
+    return check_launch("decode_e4m3fn_kernel");
+}
+
+__global__ __launch_bounds__(256) void fill_i32_kernel(int32_t* __restrict__ p, int32_t v,
+                                                       int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = v;
+}
+
+// A fill kernel rather than hipMemsetAsync, so callers may capture it in a graph.
+int launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t stream) {
+    if (n <= 0) return MOE_OK;
+    prof_begin("fill_i32", stream);
+    fill_i32_kernel<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(p, v, n);
+    prof_end(stream);
+    return check_launch("fill_i32_kernel");
+}
+
+}  // namespace moe

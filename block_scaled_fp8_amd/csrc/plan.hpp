@@ -1,0 +1,57 @@
+// The routing plan: sort maps plus the segment list consumed by the FFN kernels.
+//
+// A segment is a run of rows of the sorted route space that share one weight
+// set: an active routed expert (rows offsets[e] .. offsets[e+1]-1) or the
+// shared expert (rows R .. R+T-1 with R = T*k, token t at row R + t).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+struct Plan {
+    int32_t* counts;        // [E]
+    int32_t* offsets;       // [E+1]
+    int32_t* sorted_route;  // [R]
+    int32_t* inv_route;     // [R]
+    int32_t* seg_n;         // [1]   number of segments
+    int32_t* seg_expert;    // [E+1] expert id, -1 = shared expert
+    int32_t* seg_row0;      // [E+1] first row in sorted space
+    int32_t* seg_rows;      // [E+1] rows in the segment
+    int32_t* seg_tile0;     // [E+2] prefix of ceil(rows / tile_m)
+};
+
+// One expert's weights outside the routed arrays (the shared expert).
+struct SharedW {
+    const uint8_t* w13;
+    const float* w13_scale;
+    const uint8_t* w2;
+    const float* w2_scale;
+};
+
+// Sort entry used by moe_sort and moe_fused_w8a16 (sort.hip).  `plan.seg_*`
+// may be null when no segment list is wanted.
+size_t sort_scratch_bytes(int R, int E);
+int launch_sort(const int32_t* ids, int T, int k, int E, const Plan& plan, int has_shared,
+                int tile_m, int32_t* status, void* scratch, hipStream_t stream);
+
+// Kernel launchers (route.hip, ffn_decode.hip, ffn_prefill.hip, misc).
+int launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* aff,
+                 int32_t* status, hipStream_t stream);
+int launch_decode_ffn(const uint16_t* x, const uint8_t* w13, const float* w13s, const uint8_t* w2,
+                      const float* w2s, const SharedW& sh, const Plan& plan, int T, int H, int I,
+                      int E, int k, uint16_t* abuf, float* ybuf, hipStream_t stream);
+int launch_prefill_ffn(const uint16_t* x, const uint8_t* w13, const float* w13s, const uint8_t* w2,
+                       const float* w2s, const SharedW& sh, const Plan& plan, int T, int H, int I,
+                       int E, int k, uint16_t* abuf, float* ybuf, hipStream_t stream);
+int prefill_tile_m();
+int launch_combine(const float* ybuf, const int32_t* inv_route, const float* aff, int T, int H,
+                   int k, int has_shared, float* out, hipStream_t stream);
+int launch_decode_e4m3fn(const uint8_t* codes, uint16_t* out, int64_t n, hipStream_t stream);
+int launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t stream);
+
+// Optional per-kernel timing events around each launch (api.hip).
+void prof_begin(const char* name, hipStream_t stream);
+void prof_end(hipStream_t stream);
+
+}  // namespace moe

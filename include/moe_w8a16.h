@@ -1,0 +1,183 @@
+/*
+ * moe_w8a16.h -- C ABI of the block-scaled FP8 (W8A16) routed MoE expert FFN
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes (sources are the pages' titles and sections):
+ *
+ *  - "Gated DeltaNet (+ FP8 MoE) -- AWS Neuron (NKI) kernels for Trainium2",
+ *    section "FP8 MoE decode kernel (moe_fused_w8_35b)": the routed experts
+ *    run gate/up GEMM -> SwiGLU -> down GEMM -> affinity scale -> expert-sum on
+ *    E4M3FN weights with one scale per 128x128 block, decoded to BF16 tile by
+ *    tile; the router is softmax -> top-k -> normalise; a shared expert is
+ *    added after the routed sum; the result is [tokens, hidden] fp32.
+ *  - "spark_model/layers/nemotron_moe.rs", module documentation: expert
+ *    dispatch stays on the device, with no device-to-host synchronisation; the
+ *    layer constructor rejects a top-k outside 1..E.
+ *  - "Add gfx950 Q256 fused MXFP4 prefill pipeline" (ROCm/aiter PR #5988):
+ *    tokens sorted by expert with an inverse route map, a grouped producer
+ *    for gate/up + SiLU + down, an FP32 route reduction, one shared expert,
+ *    caller-provided output buffers and graph replay.
+ *
+ * Conventions shared by every entry point
+ *  - Every pointer argument is a DEVICE pointer owned by the caller, except
+ *    the `shared` descriptor struct itself, which is read on the host during
+ *    the call (its members are device pointers).  Nothing is allocated,
+ *    freed, synchronised or read back by the library: every call only
+ *    enqueues kernels on `stream` (a hipStream_t; NULL = the null stream) and
+ *    returns, so calls can be captured into a HIP graph.
+ *  - Arrays are dense and row-major (last index contiguous).
+ *  - Route r of token t, slot j, is r = t*k + j.
+ *  - Return value: MOE_OK, or a negative moe_status; on failure nothing has
+ *    been enqueued and moe_last_error() describes the reason.
+ *  - Data faults found on the device (an expert id outside [0, E), a
+ *    non-finite router logit) do not stop the kernels: they OR a bit into
+ *    `*status` when `status` is not NULL (the caller zeroes it), and the
+ *    faulty route is dropped from the sort and from the sum.
+ *  - Calls on different streams must use different workspaces.
+ */
+#ifndef MOE_W8A16_H
+#define MOE_W8A16_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_EINVAL = -1,        /* bad argument: NULL pointer, size or workspace */
+    MOE_EUNSUPPORTED = -2,  /* valid but unsupported geometry (e.g. H % 128) */
+    MOE_EHIP = -3           /* the HIP runtime refused a launch */
+} moe_status;
+
+enum {
+    MOE_STATUS_BAD_EXPERT_ID = 1,   /* an id outside [0, E) was dropped */
+    MOE_STATUS_NONFINITE_LOGIT = 2  /* a router logit was NaN or +-inf */
+};
+
+enum {
+    MOE_MAX_EXPERTS = 1024,  /* E */
+    MOE_MAX_TOPK = 16        /* k */
+};
+
+enum {
+    MOE_VARIANT_AUTO = 0,     /* decode when T*k/E <= 32 routes per expert, else prefill */
+    MOE_VARIANT_DECODE = 1,   /* weight-streaming kernels, one workgroup per (expert, N tile) */
+    MOE_VARIANT_PREFILL = 2   /* grouped bf16-MFMA GEMM over 128-row tiles of sorted routes */
+};
+
+/* Message describing the most recent failure on the calling thread ("" if none). */
+const char* moe_last_error(void);
+
+/*
+ * moe_route -- router: softmax over E experts, top-k, renormalised affinities.
+ * Source: NKI page above, section "FP8 MoE decode kernel", Serving contract
+ * ("softmax -> top-8 -> norm").
+ *   logits  [T, E] fp32                (in)
+ *   ids     [T, k] int32               (out) slot j = the j-th largest logit;
+ *                                       equal logits go to the lower expert
+ *                                       index and -0.0 equals +0.0
+ *   aff     [T, k] fp32                (out) p_j / sum of the k selected p
+ *   status  int32 or NULL              (in/out) MOE_STATUS_NONFINITE_LOGIT
+ * Requires 1 <= k <= min(E, MOE_MAX_TOPK), E <= MOE_MAX_EXPERTS, T >= 0.
+ * T == 0 is a successful no-op.
+ */
+int moe_route(const float* logits, int T, int E, int k,
+              int32_t* ids, float* aff, int32_t* status, void* stream);
+
+/*
+ * moe_sort -- per-expert histogram, exclusive scan, stable sorted route map
+ * and its inverse.  Sources: nemotron_moe.rs page (sort by expert before the
+ * grouped GEMM, unpermute-reduce after); AITER PR page (sorting and inverse
+ * route map).
+ *   ids          [T*k] int32   (in)
+ *   counts       [E]   int32   (out) routes per expert
+ *   offsets      [E+1] int32   (out) exclusive scan of counts; offsets[E] =
+ *                               number of valid routes (no padding)
+ *   sorted_route [T*k] int32   (out) expert-major, ascending r inside an
+ *                               expert; entries past offsets[E] are -1
+ *   inv_route    [T*k] int32   (out) position of route r in sorted_route,
+ *                               -1 for a dropped route
+ *   status       int32 or NULL (in/out) MOE_STATUS_BAD_EXPERT_ID
+ *   ws, ws_bytes: device scratch of at least moe_sort_workspace_bytes(T,k,E).
+ */
+size_t moe_sort_workspace_bytes(int T, int k, int E);
+int moe_sort(const int32_t* ids, int T, int k, int E,
+             int32_t* counts, int32_t* offsets,
+             int32_t* sorted_route, int32_t* inv_route,
+             int32_t* status, void* ws, size_t ws_bytes, void* stream);
+
+/* One expert's block-scaled FP8 weights (same H and I as the routed experts). */
+typedef struct {
+    const uint8_t* w13;        /* [2I, H] E4M3FN: rows 0..I-1 gate, I..2I-1 up */
+    const float* w13_scale;    /* [2I/128, H/128] fp32 */
+    const uint8_t* w2;         /* [H, I] E4M3FN */
+    const float* w2_scale;     /* [H/128, I/128] fp32 */
+} moe_expert_w8;
+
+/*
+ * moe_fused_w8a16 -- sort + routed expert FFN + affinity-weighted fp32 sum
+ * (+ optional always-on shared expert with affinity 1.0).
+ * Sources: NKI page, section "FP8 MoE decode kernel" (fused path, weight
+ * format, fp32 [B, H] result, shared expert added after the routed sum);
+ * AITER PR page (sorted routes, fp32 route reduction, one shared expert).
+ *   x          [T, H] bf16 (raw 16-bit patterns)                   (in)
+ *   w13        [E, 2I, H] E4M3FN bytes, w13_scale [E, 2I/128, H/128] fp32
+ *   w2         [E, H, I]  E4M3FN bytes, w2_scale  [E, H/128, I/128]  fp32
+ *              weight value = E4M3FN(code) * scale of its 128x128 block
+ *   ids, aff   [T, k] int32 / fp32 (e.g. from moe_route)            (in)
+ *   shared     host pointer to a moe_expert_w8, or NULL for none    (in)
+ *   out        [T, H] fp32, overwritten (must not alias x)          (out)
+ *   status     int32 or NULL                                        (in/out)
+ *   ws         device scratch of moe_fused_workspace_bytes(...) bytes
+ *   variant    MOE_VARIANT_*
+ * H and I must be multiples of 128 (else MOE_EUNSUPPORTED); T >= 0; T == 0
+ * is a no-op.  The expert FFN computes in bf16 x bf16 products with fp32
+ * accumulation; each 128-wide K block's partial sum is multiplied by its
+ * fp32 block scale; the SwiGLU output is rounded to bf16 before the down GEMM.
+ */
+size_t moe_fused_workspace_bytes(int T, int H, int I, int E, int k,
+                                 int has_shared, int variant);
+int moe_fused_w8a16(const void* x,
+                    const uint8_t* w13, const float* w13_scale,
+                    const uint8_t* w2, const float* w2_scale,
+                    const int32_t* ids, const float* aff,
+                    int T, int H, int I, int E, int k,
+                    const moe_expert_w8* shared, float* out,
+                    int32_t* status, void* ws, size_t ws_bytes,
+                    int variant, void* stream);
+
+/*
+ * moe_decode_e4m3fn -- decode n E4M3FN bytes to bf16 bit patterns with the
+ * same on-chip conversion the FFN kernels use (scale 1, exact: every finite
+ * E4M3FN value is a bf16 value).  Exposed so the decode step can be checked
+ * on its own.  Source: NKI page, file table ("decode official E4M3FN").
+ *   codes [n] uint8 (in), out [n] uint16 (out); n >= 0.
+ */
+int moe_decode_e4m3fn(const uint8_t* codes, uint16_t* out, int64_t n, void* stream);
+
+/*
+ * Per-kernel timing, for measurement only (not from the pages).  While
+ * enabled, every kernel the library launches is bracketed by two HIP timing
+ * events recorded on that kernel's own stream.  moe_profile_collect() waits
+ * on the host for the recorded events and folds their elapsed times into
+ * per-kernel statistics, so it must not be called under graph capture, and
+ * profiling must be off while a graph is being captured.
+ *   moe_profile_enable(1) clears the statistics and starts recording;
+ *   moe_profile_enable(0) stops recording (statistics are kept).
+ *   moe_profile_stat(i, ...) reports kernel i < moe_profile_count(): its name
+ *   (NUL-terminated, truncated to name_len), launches and total milliseconds.
+ * All return MOE_OK or a negative moe_status (MOE_EHIP if an event call
+ * fails, MOE_EINVAL for a bad index or NULL output).
+ */
+int moe_profile_enable(int on);
+int moe_profile_collect(void);
+int moe_profile_count(void);
+int moe_profile_stat(int i, char* name, int name_len, int64_t* launches, double* total_ms);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_W8A16_H */

@@ -1,0 +1,64 @@
+"""Helpers for GPU-vs-oracle parity tests (inputs on the GPU, oracle on the CPU)."""
+import numpy as np
+import torch
+
+import oracle
+from block_scaled_fp8_amd import synth
+
+OUT_TOL = 2e-2          # max |gpu - oracle| <= OUT_TOL * RMS(oracle output)
+AFF_RTOL = 2e-6         # fp32 exp/sum/divide against float64
+
+
+def gpu_case(name_or_cfg, seed=0):
+    cfg = synth.CONFIGS[name_or_cfg] if isinstance(name_or_cfg, str) else name_or_cfg
+    dev = "cuda"
+    # tiny geometries are drawn on the CPU; the large ones on the GPU
+    gen_dev = "cpu" if cfg.E * 3 * cfg.H * cfg.I < (64 << 20) else dev
+    case = synth.make_case(cfg, seed, gen_dev)
+    for n in ("x", "logits", "w13", "w13_scale", "w2", "w2_scale"):
+        case[n] = case[n].to(dev)
+    if case["shared"] is not None:
+        case["shared"] = {n: t.to(dev) for n, t in case["shared"].items()}
+    return case
+
+
+def np_(t):
+    return t.detach().cpu().numpy()
+
+
+def oracle_rows(case, ids, aff, rows, with_shared=True):
+    """Oracle output for the given token rows, copying only the experts they use."""
+    rows = np.asarray(rows)
+    sub_ids = np.asarray(ids)[rows]
+    uniq = np.unique(sub_ids)
+    sel = torch.as_tensor(uniq, dtype=torch.long, device=case["w13"].device)
+    w13 = np_(case["w13"].index_select(0, sel))
+    w13s = np_(case["w13_scale"].index_select(0, sel))
+    w2 = np_(case["w2"].index_select(0, sel))
+    w2s = np_(case["w2_scale"].index_select(0, sel))
+    remap = np.searchsorted(uniq, sub_ids)
+    sh = None
+    if with_shared and case.get("shared") is not None:
+        sh = {n: np_(t) for n, t in case["shared"].items()}
+    x = np_(case["x"].float())[rows]
+    return oracle.moe_ffn(x, w13, w13s, w2, w2s, remap, np.asarray(aff)[rows], sh)
+
+
+def assert_out_close(got, ref, tol=OUT_TOL, what=""):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite GPU output"
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    err = float(np.max(np.abs(got - ref))) if got.size else 0.0
+    print(f"[parity] {what}: max|d|={err:.4g} rms={rms:.4g} ratio={err / max(rms, 1e-300):.4g}",
+          flush=True)
+    assert err <= tol * rms, f"{what}: max|gpu-oracle| = {err:.4g} > {tol} * RMS {rms:.4g}"
+
+
+def sample_rows(T, n, seed=0):
+    if T <= n:
+        return np.arange(T)
+    rng = np.random.default_rng(seed)
+    pick = set(rng.choice(T, size=n - 2, replace=False).tolist()) | {0, T - 1}
+    return np.array(sorted(pick))

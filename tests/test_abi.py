@@ -1,0 +1,113 @@
+"""Host-side checks of the C ABI: the library loads, exports every function the
+header declares, and rejects bad arguments before touching the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_scaled_fp8_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_w8a16.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(moe_[a-z0-9_]+)\s*\(",
+                       src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for n in ("moe_route", "moe_sort", "moe_fused_w8a16", "moe_last_error",
+              "moe_sort_workspace_bytes", "moe_fused_workspace_bytes", "moe_decode_e4m3fn"):
+        assert n in names
+    assert set(names) == set(binding.EXPORTED)
+
+
+def test_library_loads_and_exports_every_symbol():
+    lib = binding.load_library()
+    for n in _declared_functions():
+        assert hasattr(lib, n), n
+    assert lib.moe_last_error() == b""
+
+
+def _null():
+    return ctypes.c_void_p(0)
+
+
+def test_route_argument_checks():
+    lib = binding.load_library()
+    fake = ctypes.c_void_p(0x1000)
+    # k > E, k > MAX_K, E > MAX_E, T < 0 are rejected without a launch
+    assert lib.moe_route(fake, 4, 8, 9, fake, fake, None, None) == binding.MOE_EINVAL
+    assert b"k must be" in lib.moe_last_error()
+    assert lib.moe_route(fake, 4, 64, 17, fake, fake, None, None) == binding.MOE_EINVAL
+    assert lib.moe_route(fake, 4, 2000, 2, fake, fake, None, None) == binding.MOE_EINVAL
+    assert lib.moe_route(fake, -1, 8, 2, fake, fake, None, None) == binding.MOE_EINVAL
+    assert lib.moe_route(fake, 4, 8, 0, fake, fake, None, None) == binding.MOE_EINVAL
+    # NULL outputs
+    assert lib.moe_route(fake, 4, 8, 2, None, fake, None, None) == binding.MOE_EINVAL
+    # T == 0 is a no-op that never touches the device
+    assert lib.moe_route(None, 0, 8, 2, None, None, None, None) == binding.MOE_OK
+    assert lib.moe_last_error() == b""
+
+
+def test_sort_argument_checks():
+    lib = binding.load_library()
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.moe_sort(fake, 4, 3, 2, fake, fake, fake, fake, None, None, 0, None) == binding.MOE_EINVAL
+    assert lib.moe_sort(fake, 4, 2, 8, None, fake, fake, fake, None, None, 0, None) == binding.MOE_EINVAL
+    # the large-R path needs scratch: too small a workspace is rejected
+    T, k, E = 8192, 8, 256
+    need = lib.moe_sort_workspace_bytes(T, k, E)
+    assert need >= E * 4
+    assert lib.moe_sort(fake, T, k, E, fake, fake, fake, fake, None, fake, need - 1, None) == binding.MOE_EINVAL
+    assert b"workspace" in lib.moe_last_error()
+    assert lib.moe_sort_workspace_bytes(64, 8, 256) == 0   # single-workgroup path needs none
+
+
+def test_fused_argument_checks():
+    lib = binding.load_library()
+    f = ctypes.c_void_p(0x1000)
+    o = ctypes.c_void_p(0x3000)
+    ws = lib.moe_fused_workspace_bytes(64, 2048, 512, 256, 8, 0, 0)
+    assert ws > 64 * 8 * (512 * 2 + 2048 * 4)
+    args = lambda T, H, I, E, k, ws_bytes, variant=0, out=o: (  # noqa: E731
+        f, f, f, f, f, f, f, T, H, I, E, k, None, out, None, f, ws_bytes, variant, None)
+    assert lib.moe_fused_w8a16(*args(64, 2000, 512, 256, 8, ws)) == binding.MOE_EUNSUPPORTED
+    assert lib.moe_fused_w8a16(*args(64, 2048, 500, 256, 8, ws)) == binding.MOE_EUNSUPPORTED
+    assert b"multiples of 128" in lib.moe_last_error()
+    assert lib.moe_fused_w8a16(*args(64, 2048, 512, 256, 8, ws - 1)) == binding.MOE_EINVAL
+    assert b"workspace" in lib.moe_last_error()
+    assert lib.moe_fused_w8a16(*args(64, 2048, 512, 256, 8, ws, 7)) == binding.MOE_EINVAL
+    assert lib.moe_fused_w8a16(*args(64, 2048, 512, 256, 300, ws)) == binding.MOE_EINVAL
+    # out aliasing x
+    assert lib.moe_fused_w8a16(*args(64, 2048, 512, 256, 8, ws, 0, f)) == binding.MOE_EINVAL
+    assert b"alias" in lib.moe_last_error()
+    # shared descriptor with a NULL member
+    bad = binding.ExpertW8(0x1000, 0, 0x1000, 0x1000)
+    a = list(args(64, 2048, 512, 256, 8, ws + 10**9))
+    a[12] = ctypes.pointer(bad)
+    a[13] = ctypes.c_void_p(0x2000)
+    lib.moe_fused_w8a16.argtypes[12] = ctypes.POINTER(binding.ExpertW8)
+    assert lib.moe_fused_w8a16(*a) == binding.MOE_EINVAL
+    assert b"shared" in lib.moe_last_error()
+    # T == 0 is a no-op
+    assert lib.moe_fused_w8a16(*args(0, 2048, 512, 256, 8, 0)) == binding.MOE_OK
+
+
+def test_workspace_grows_with_shared_expert():
+    lib = binding.load_library()
+    a = lib.moe_fused_workspace_bytes(512, 2048, 512, 256, 8, 0, 0)
+    b = lib.moe_fused_workspace_bytes(512, 2048, 512, 256, 8, 1, 0)
+    assert b > a
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        binding.route(torch.zeros((4, 8), dtype=torch.float32), 2)

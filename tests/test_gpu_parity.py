@@ -1,0 +1,305 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Routing ids and the sort maps must be bit-exact; affinities agree to fp32
+rounding; expert-FFN outputs satisfy max|gpu - oracle| <= 2e-2 * RMS(oracle).
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_scaled_fp8_amd import binding, synth
+
+from _parity import (AFF_RTOL, assert_out_close, gpu_case, np_, oracle_rows, sample_rows)
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+FFN_SAMPLE = {"tiny": 4, "decode64": 64, "decode512": 64, "prefill8k_skew": 24,
+              "prefill16k_wide": 6}
+
+
+def setup_module(module):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    binding.load_library()
+
+
+_cases = {}
+
+
+def _case(name):
+    if name not in _cases:
+        _cases.clear()
+        torch.cuda.empty_cache()
+        _cases[name] = gpu_case(name, seed=1)
+    return _cases[name]
+
+
+# ------------------------------------------------------------------ decode step
+def test_e4m3fn_decode_is_exact():
+    codes = torch.arange(256, dtype=torch.int64).to(torch.uint8).cuda()
+    got = binding.decode_e4m3fn(codes).float().cpu().numpy().astype(np.float64)
+    ref = oracle.e4m3fn_table()
+    fin = np.isfinite(ref)
+    assert np.array_equal(got[fin], ref[fin])
+    assert np.array_equal(np.signbit(got[fin]), np.signbit(ref[fin]))
+    assert np.all(np.isnan(got[~fin]))
+    # an odd length exercises the tail
+    got7 = binding.decode_e4m3fn(codes[:7]).float().cpu().numpy()
+    assert np.array_equal(got7, ref[:7])
+
+
+# ------------------------------------------------------------------ routing
+@pytest.mark.parametrize("name", synth.CONFIG_ORDER)
+def test_route_parity(name):
+    c = _case(name)
+    cfg = c["cfg"]
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ids, aff = binding.route(c["logits"], cfg.k, status)
+    torch.cuda.synchronize()
+    ref_ids, ref_aff = oracle.route_softmax_topk(np_(c["logits"]), cfg.k)
+    assert np.array_equal(np_(ids), ref_ids)
+    np.testing.assert_allclose(np_(aff), ref_aff, rtol=AFF_RTOL, atol=0)
+    assert int(status.item()) == 0
+
+
+def _golden_route_rows():
+    rows = []
+    with open(os.path.join(GOLDEN, "route_closed_form.txt")) as f:
+        for ln in f:
+            if ln.strip() and not ln.startswith("#"):
+                k_s, l_s, i_s, a_s = [p.strip() for p in ln.split("|")]
+                rows.append((int(k_s), [float(v) for v in l_s.split()],
+                             [int(v) for v in i_s.split()], [float(v) for v in a_s.split()]))
+    return rows
+
+
+def test_route_golden_rows_and_ties():
+    for k, logits, ids_exp, aff_exp in _golden_route_rows():
+        lg = torch.tensor([logits], dtype=torch.float32, device="cuda")
+        ids, aff = binding.route(lg, k)
+        assert np_(ids)[0].tolist() == ids_exp
+        np.testing.assert_allclose(np_(aff)[0], aff_exp, rtol=AFF_RTOL)
+
+
+@pytest.mark.parametrize("T,E,k", [(1, 1, 1), (3, 100, 5), (7, 64, 16), (5, 1024, 16),
+                                   (9, 513, 11), (130, 65, 3)])
+def test_route_shapes_and_ties(T, E, k):
+    rng = np.random.default_rng(T * 1000 + E)
+    vals = np.array([-1.5, -0.0, 0.0, 0.25, 1.0], dtype=np.float32)
+    logits = rng.choice(vals, size=(T, E)).astype(np.float32)       # many ties
+    logits[0] = rng.standard_normal(E).astype(np.float32)
+    lg = torch.from_numpy(logits).cuda()
+    ids, aff = binding.route(lg, k)
+    ref_ids, ref_aff = oracle.route_softmax_topk(logits, k)
+    assert np.array_equal(np_(ids), ref_ids)
+    np.testing.assert_allclose(np_(aff), ref_aff, rtol=AFF_RTOL)
+
+
+def test_route_flags_nonfinite_logits():
+    lg = torch.randn((4, 16), device="cuda")
+    lg[2, 5] = float("nan")
+    lg[3, 0] = float("inf")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    binding.route(lg, 2, status)
+    torch.cuda.synchronize()
+    assert int(status.item()) & binding.MOE_STATUS_NONFINITE_LOGIT
+
+
+# ------------------------------------------------------------------ sort
+def _check_sort(ids_np, E, got):
+    ref = oracle.sort_by_expert(ids_np, E)
+    for g, r, n in zip(got, ref, ("counts", "offsets", "sorted_route", "inv_route")):
+        assert np.array_equal(np_(g), r), n
+
+
+@pytest.mark.parametrize("name", synth.CONFIG_ORDER)
+def test_sort_parity(name):
+    c = _case(name)
+    cfg = c["cfg"]
+    ref_ids, _ = oracle.route_softmax_topk(np_(c["logits"]), cfg.k)
+    ids = torch.from_numpy(ref_ids).cuda()
+    _check_sort(ref_ids, cfg.E, binding.sort(ids, cfg.E))
+
+
+@pytest.mark.parametrize("T,k,E", [(1, 1, 1), (1, 8, 256), (37, 3, 7), (2048, 8, 256),
+                                   (2049, 8, 256), (4096, 4, 1024), (5000, 10, 512),
+                                   (16384, 1, 3)])
+def test_sort_random_ids(T, k, E):
+    ids_np = synth.random_ids(T, k, E, seed=T + k, distinct=False).numpy()
+    _check_sort(ids_np, E, binding.sort(torch.from_numpy(ids_np).cuda(), E))
+
+
+def test_sort_all_routes_one_expert():
+    T, k, E = 3000, 8, 64
+    ids_np = np.zeros((T, k), np.int32)
+    _check_sort(ids_np, E, binding.sort(torch.from_numpy(ids_np).cuda(), E))
+
+
+@pytest.mark.parametrize("T", [5, 6000])
+def test_sort_drops_bad_ids(T):
+    k, E = 4, 16
+    ids_np = synth.random_ids(T, k, E, seed=3, distinct=False).numpy()
+    ids_np[1, 2] = E
+    ids_np[T - 1, 0] = -3
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    counts, offsets, sr, inv = binding.sort(torch.from_numpy(ids_np).cuda(), E, status)
+    torch.cuda.synchronize()
+    assert int(status.item()) & binding.MOE_STATUS_BAD_EXPERT_ID
+    flat = ids_np.reshape(-1)
+    good = (flat >= 0) & (flat < E)
+    ref_c, ref_o, ref_sr, _ = oracle.sort_by_expert(np.where(good, flat, 0)[good], E)
+    assert np.array_equal(np_(counts), ref_c)
+    assert np.array_equal(np_(offsets), ref_o)
+    routes = np.nonzero(good)[0]
+    n = int(good.sum())
+    assert np.array_equal(np_(sr)[:n], routes[ref_sr])
+    assert np.all(np_(sr)[n:] == -1)
+    inv_np = np_(inv)
+    assert np.all(inv_np[~good] == -1)
+    assert np.array_equal(np_(sr)[inv_np[good]], routes)
+
+
+# ------------------------------------------------------------------ fused FFN
+def _fused(c, ids, aff, variant="auto", shared=True, **kw):
+    return binding.fused_w8a16(c["x"], c["w13"], c["w13_scale"], c["w2"], c["w2_scale"], ids,
+                               aff, shared=c["shared"] if shared else None, variant=variant, **kw)
+
+
+@pytest.mark.parametrize("variant", ["decode"])
+@pytest.mark.parametrize("name", synth.CONFIG_ORDER)
+def test_fused_parity(name, variant):
+    """End to end on the GPU (route -> sort -> FFN), oracle from the logits."""
+    c = _case(name)
+    cfg = c["cfg"]
+    ids, aff = binding.route(c["logits"], cfg.k)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = _fused(c, ids, aff, variant=variant, status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    ref_ids, ref_aff = oracle.route_softmax_topk(np_(c["logits"]), cfg.k)
+    assert np.array_equal(np_(ids), ref_ids)
+    rows = sample_rows(cfg.T, FFN_SAMPLE[name], seed=2)
+    ref = oracle_rows(c, ref_ids, ref_aff, rows)
+    assert_out_close(np_(out)[rows], ref, what=f"{name}/{variant}")
+
+
+@pytest.mark.parametrize("variant", ["decode"])
+@pytest.mark.parametrize("T", [1, 15, 16, 17, 37])
+def test_fused_token_boundaries(T, variant):
+    cfg = synth.MoeConfig("b", T=T, H=256, I=256, E=16, k=4)
+    c = gpu_case(cfg, seed=T)
+    ids, aff = binding.route(c["logits"], cfg.k)
+    out = _fused(c, ids, aff, variant=variant)
+    ref_ids, ref_aff = oracle.route_softmax_topk(np_(c["logits"]), cfg.k)
+    ref = oracle_rows(c, ref_ids, ref_aff, np.arange(T))
+    assert_out_close(np_(out), ref, what=f"T={T}/{variant}")
+
+
+@pytest.mark.parametrize("variant", ["decode"])
+def test_fused_hot_expert_and_shared(variant):
+    """Every token routed to the same experts (one long segment) + a shared expert."""
+    cfg = synth.MoeConfig("hot", T=70, H=384, I=256, E=8, k=2, shared=True)
+    c = gpu_case(cfg, seed=5)
+    ids_np = np.tile(np.array([[3, 6]], np.int32), (cfg.T, 1))
+    aff_np = synth.random_affinities(cfg.T, 2, seed=5).numpy()
+    out = _fused(c, torch.from_numpy(ids_np).cuda(), torch.from_numpy(aff_np).cuda(),
+                 variant=variant)
+    ref = oracle_rows(c, ids_np, aff_np, np.arange(cfg.T))
+    assert_out_close(np_(out), ref, what=f"hot+shared/{variant}")
+
+
+@pytest.mark.parametrize("variant", ["decode"])
+def test_fused_zero_affinities(variant):
+    cfg = synth.MoeConfig("z", T=9, H=256, I=128, E=8, k=3, shared=True)
+    c = gpu_case(cfg, seed=6)
+    ids, _ = binding.route(c["logits"], cfg.k)
+    zero = torch.zeros((cfg.T, cfg.k), dtype=torch.float32, device="cuda")
+    out = _fused(c, ids, zero, variant=variant, shared=False)
+    assert torch.all(out == 0)
+    out_sh = _fused(c, ids, zero, variant=variant, shared=True)
+    ref = oracle_rows(c, np_(ids), np.zeros((cfg.T, cfg.k)), np.arange(cfg.T))
+    assert_out_close(np_(out_sh), ref, what=f"zero-aff+shared/{variant}")
+
+
+@pytest.mark.parametrize("variant", ["decode"])
+def test_fused_single_expert_dense(variant):
+    cfg = synth.MoeConfig("d", T=33, H=512, I=384, E=1, k=1)
+    c = gpu_case(cfg, seed=7)
+    ids = torch.zeros((cfg.T, 1), dtype=torch.int32, device="cuda")
+    aff = torch.ones((cfg.T, 1), dtype=torch.float32, device="cuda")
+    out = _fused(c, ids, aff, variant=variant)
+    ref = oracle_rows(c, np.zeros((cfg.T, 1), np.int64), np.ones((cfg.T, 1)), np.arange(cfg.T))
+    assert_out_close(np_(out), ref, what=f"E=1/{variant}")
+
+
+def test_fused_bad_ids_are_dropped():
+    cfg = synth.MoeConfig("bad", T=6, H=256, I=128, E=8, k=2)
+    c = gpu_case(cfg, seed=8)
+    ids_np = synth.random_ids(cfg.T, 2, 8, seed=8).numpy()
+    aff_np = synth.random_affinities(cfg.T, 2, seed=8).numpy()
+    ids_np[2, 1] = 99
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = _fused(c, torch.from_numpy(ids_np).cuda(), torch.from_numpy(aff_np).cuda(),
+                 status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) & binding.MOE_STATUS_BAD_EXPERT_ID
+    aff_ref = aff_np.copy()
+    aff_ref[2, 1] = 0.0
+    ids_ref = ids_np.copy()
+    ids_ref[2, 1] = 0
+    ref = oracle_rows(c, ids_ref, aff_ref, np.arange(cfg.T))
+    assert_out_close(np_(out), ref, what="bad ids dropped")
+
+
+def test_fused_is_deterministic():
+    c = _case("decode512")
+    ids, aff = binding.route(c["logits"], c["cfg"].k)
+    a = _fused(c, ids, aff)
+    b = _fused(c, ids, aff)
+    assert torch.equal(a, b)
+
+
+def test_graph_replay_with_changing_routes():
+    """Capture route + fused once; replay with new logits and zero routing
+    weights and compare every replay with the eager result."""
+    cfg = synth.MoeConfig("g", T=48, H=512, I=256, E=32, k=4)
+    c = gpu_case(cfg, seed=9)
+    logits = c["logits"].clone()
+    ws = torch.empty(binding.fused_workspace_bytes(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k),
+                     dtype=torch.uint8, device="cuda")
+    out = torch.empty((cfg.T, cfg.H), dtype=torch.float32, device="cuda")
+    scale_aff = torch.ones(1, device="cuda")
+
+    def step():
+        ids, aff = binding.route(logits, cfg.k)
+        binding.fused_w8a16(c["x"], c["w13"], c["w13_scale"], c["w2"], c["w2_scale"], ids,
+                            aff * scale_aff, out=out, ws=ws)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        logits.copy_(torch.randn(logits.shape, device="cuda", generator=torch.Generator(
+            "cuda").manual_seed(100 + rep)))
+        scale_aff.fill_(0.0 if rep == 2 else 1.0)
+        g.replay()
+        torch.cuda.synchronize()
+        got = out.clone()
+        step()
+        torch.cuda.synchronize()
+        assert torch.equal(got, out), f"replay {rep} differs from eager"
+        if rep == 2:
+            assert torch.all(got == 0)
+        else:
+            ref_ids, ref_aff = oracle.route_softmax_topk(np_(logits), cfg.k)
+            ref = oracle_rows(c, ref_ids, ref_aff, np.arange(cfg.T))
+            assert_out_close(np_(got), ref, what=f"graph replay {rep}")
