@@ -45,6 +45,8 @@ def kernel_bytes(name, cfg, n_active, with_shared):
     rows = R + (T if with_shared else 0)
     w13 = 2 * I * H + 4 * (2 * I // 128) * (H // 128)
     w2 = H * I + 4 * (H // 128) * (I // 128)
+    if name == "decode_fused_expert":
+        return nseg * (w13 + w2) + 2 * T * H + 4 * rows * H
     if name.endswith("gateup_swiglu"):
         return nseg * w13 + 2 * T * H + 2 * rows * I
     if name.endswith("down"):
@@ -116,6 +118,8 @@ def main():
     ap.add_argument("--workload", default="decode64")
     ap.add_argument("--weight-sets", type=int, default=4)
     ap.add_argument("--variant", default="auto", choices=["auto", "decode", "prefill"])
+    ap.add_argument("--layout", default="tiled", choices=["rowmajor", "tiled"],
+                    help="weight layout; tiled = packed once at load time (offline prep)")
     ap.add_argument("--cpu-tokens", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
@@ -155,8 +159,21 @@ def main():
 
     x, logits = synth.make_activations(cfg, args.seed, dev)
     wsets = [synth.make_weights(cfg, args.seed + 100 * i, dev) for i in range(L)]
+    if args.layout == "tiled":
+        # offline weight preparation, once per weight set (not part of a step)
+        packed = []
+        for w in wsets:
+            p = dict(w, w13=binding.pack_w8(w["w13"]), w2=binding.pack_w8(w["w2"]))
+            if w["shared"] is not None:
+                p["shared"] = dict(w["shared"], w13=binding.pack_w8(w["shared"]["w13"]),
+                                   w2=binding.pack_w8(w["shared"]["w2"]))
+            packed.append(p)
+        run_sets = packed
+    else:
+        run_sets = wsets
     steps = [binding.MoeStep(x, logits, cfg.k, w["w13"], w["w13_scale"], w["w2"], w["w2_scale"],
-                             shared=w["shared"], variant=args.variant) for w in wsets]
+                             shared=w["shared"], variant=args.variant, layout=args.layout)
+             for w in run_sets]
     torch.cuda.synchronize()
 
     # routing facts for the algorithmic byte counts (outside the timed region)
@@ -224,7 +241,8 @@ def main():
         "config": {"workload": cfg.name, "T": cfg.T, "hidden": cfg.H, "moe_inter": cfg.I,
                    "experts": cfg.E, "top_k": cfg.k, "shared_expert": cfg.shared,
                    "weights": "E4M3FN, fp32 128x128 block scales", "weight_sets": L,
-                   "variant": args.variant, "active_experts": n_active},
+                   "variant": args.variant, "weight_layout": args.layout,
+                   "active_experts": n_active},
         "roofline": roofline,
         "step": {"algorithmic_bytes": sb, "GB_per_s": round(sb / (ms_per_step * 1e-3) / 1e9, 1),
                  "hbm_frac": round(sb / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),

@@ -21,10 +21,11 @@ MOE_STATUS_NONFINITE_LOGIT = 2
 MOE_MAX_EXPERTS = 1024
 MOE_MAX_TOPK = 16
 VARIANTS = {"auto": 0, "decode": 1, "prefill": 2}
+LAYOUTS = {"rowmajor": 0, "tiled": 1}
 
 EXPORTED = (
     "moe_last_error", "moe_route", "moe_sort_workspace_bytes", "moe_sort",
-    "moe_fused_workspace_bytes", "moe_fused_w8a16", "moe_decode_e4m3fn",
+    "moe_fused_workspace_bytes", "moe_fused_w8a16", "moe_decode_e4m3fn", "moe_pack_w8",
     "moe_profile_enable", "moe_profile_collect", "moe_profile_count", "moe_profile_stat",
 )
 
@@ -70,7 +71,9 @@ def load_library():
     lib.moe_fused_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
     lib.moe_fused_w8a16.restype = i32
     lib.moe_fused_w8a16.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
-                                    ctypes.POINTER(ExpertW8), vp, vp, vp, sz, i32, vp]
+                                    ctypes.POINTER(ExpertW8), vp, vp, vp, sz, i32, i32, vp]
+    lib.moe_pack_w8.restype = i32
+    lib.moe_pack_w8.argtypes = [vp, vp, i64, i32, i32, vp]
     lib.moe_decode_e4m3fn.restype = i32
     lib.moe_decode_e4m3fn.argtypes = [vp, vp, i64, vp]
     lib.moe_profile_enable.restype = i32
@@ -159,8 +162,24 @@ def fused_workspace_bytes(T, H, I, E, k, has_shared=False, variant="auto") -> in
     return int(load_library().moe_fused_workspace_bytes(T, H, I, E, k, int(bool(has_shared)), v))
 
 
+def _layout(layout):
+    return LAYOUTS[layout] if isinstance(layout, str) else int(layout)
+
+
+def pack_w8(w: torch.Tensor) -> torch.Tensor:
+    """Row-major FP8 weights [..., rows, cols] uint8 -> the tile-coalesced layout
+    (same shape and bytes, reordered on the GPU)."""
+    lib = load_library()
+    _need(w, "w", torch.uint8)
+    rows, cols = w.shape[-2], w.shape[-1]
+    n = w.numel() // max(1, rows * cols)
+    out = torch.empty_like(w)
+    _check(lib.moe_pack_w8(_ptr(w), _ptr(out), n, rows, cols, _stream(w.device)))
+    return out
+
+
 def fused_w8a16(x, w13, w13_scale, w2, w2_scale, ids, aff, shared=None, out=None, ws=None,
-                status=None, variant="auto"):
+                status=None, variant="auto", layout="rowmajor"):
     """Routed expert FFN with block-scaled FP8 weights -> out [T, H] fp32.
 
     x bf16 [T, H]; w13 uint8 [E, 2I, H]; w13_scale fp32 [E, 2I/128, H/128];
@@ -204,7 +223,8 @@ def fused_w8a16(x, w13, w13_scale, w2, w2_scale, ids, aff, shared=None, out=None
         _need(status, "status", torch.int32, dev)
     _check(lib.moe_fused_w8a16(_ptr(x), _ptr(w13), _ptr(w13_scale), _ptr(w2), _ptr(w2_scale),
                                _ptr(ids), _ptr(aff), T, H, I, E, k, sh_ptr, _ptr(out),
-                               _ptr(status), _ptr(ws), ws.numel(), v, _stream(dev)))
+                               _ptr(status), _ptr(ws), ws.numel(), _layout(layout), v,
+                               _stream(dev)))
     return out
 
 
@@ -217,10 +237,12 @@ def decode_e4m3fn(codes: torch.Tensor) -> torch.Tensor:
     return out
 
 
-def forward(x, logits, k, w13, w13_scale, w2, w2_scale, shared=None, variant="auto"):
+def forward(x, logits, k, w13, w13_scale, w2, w2_scale, shared=None, variant="auto",
+            layout="rowmajor"):
     """Whole hot path: route, then the fused sort + expert FFN."""
     ids, aff = route(logits, k)
-    out = fused_w8a16(x, w13, w13_scale, w2, w2_scale, ids, aff, shared=shared, variant=variant)
+    out = fused_w8a16(x, w13, w13_scale, w2, w2_scale, ids, aff, shared=shared, variant=variant,
+                      layout=layout)
     return ids, aff, out
 
 
@@ -248,7 +270,7 @@ class MoeStep:
     stream of the tensors' device."""
 
     def __init__(self, x, logits, k, w13, w13_scale, w2, w2_scale, shared=None,
-                 variant="auto"):
+                 variant="auto", layout="rowmajor"):
         lib = load_library()
         dev = x.device
         T, H = x.shape
@@ -263,7 +285,7 @@ class MoeStep:
                               dtype=torch.uint8, device=dev)
         ids, aff = route(logits, k)
         fused_w8a16(x, w13, w13_scale, w2, w2_scale, ids, aff, shared=shared, out=self.out,
-                    ws=self.ws, variant=variant)
+                    ws=self.ws, variant=variant, layout=layout)
         self._keep = (x, logits, w13, w13_scale, w2, w2_scale, shared)
         self._sh = None
         if shared is not None:
@@ -276,7 +298,8 @@ class MoeStep:
                             _ptr(self.aff), None)
         self._fused_args = (_ptr(x), _ptr(w13), _ptr(w13_scale), _ptr(w2), _ptr(w2_scale),
                             _ptr(self.ids), _ptr(self.aff), T, H, I, E, k, self._sh,
-                            _ptr(self.out), None, _ptr(self.ws), self.ws.numel(), v)
+                            _ptr(self.out), None, _ptr(self.ws), self.ws.numel(),
+                            _layout(layout), v)
         self._lib = lib
         self._dev = dev
 

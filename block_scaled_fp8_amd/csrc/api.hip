@@ -59,7 +59,7 @@ static FusedLayout fused_layout(int T, int H, int I, int E, int k, int has_share
     L.seg_tile0 = take(sizeof(int32_t) * (E + 2));
     L.sort_scratch = take(sort_scratch_bytes((int)R, E));
     L.abuf = take(sizeof(uint16_t) * rows * I);
-    L.ybuf = take(sizeof(float) * rows * H);
+    L.ybuf = take(sizeof(float) * (rows + 1) * H);  // + one trash row for padded stores
     L.total = o;
     return L;
 }
@@ -151,7 +151,7 @@ int moe_fused_w8a16(const void* x, const uint8_t* w13, const float* w13_scale,
                     const uint8_t* w2, const float* w2_scale, const int32_t* ids,
                     const float* aff, int T, int H, int I, int E, int k,
                     const moe_expert_w8* shared, float* out, int32_t* status, void* ws,
-                    size_t ws_bytes, int variant, void* stream) {
+                    size_t ws_bytes, int weight_layout, int variant, void* stream) {
     g_err[0] = 0;
     if (int rc = check_route_args(T, E, k)) return rc;
     if (H < 128 || I < 128 || H % 128 || I % 128) {
@@ -161,6 +161,10 @@ int moe_fused_w8a16(const void* x, const uint8_t* w13, const float* w13_scale,
     if ((long long)H * I * 3 > (1LL << 40)) {
         set_error("expert too large (H=%d, I=%d)", H, I);
         return MOE_EUNSUPPORTED;
+    }
+    if (weight_layout != MOE_LAYOUT_ROWMAJOR && weight_layout != MOE_LAYOUT_TILED) {
+        set_error("unknown weight layout %d", weight_layout);
+        return MOE_EINVAL;
     }
     if (variant < MOE_VARIANT_AUTO || variant > MOE_VARIANT_PREFILL) {
         set_error("unknown variant %d", variant);
@@ -212,12 +216,36 @@ int moe_fused_w8a16(const void* x, const uint8_t* w13, const float* w13_scale,
     const uint16_t* xb = static_cast<const uint16_t*>(x);
     int rc;
     if (variant == MOE_VARIANT_DECODE)
-        rc = launch_decode_ffn(xb, w13, w13_scale, w2, w2_scale, sh, p, T, H, I, E, k, abuf, ybuf, s);
+        rc = launch_decode_ffn(weight_layout, xb, w13, w13_scale, w2, w2_scale, sh, p, T, H, I, E,
+                               k, abuf, ybuf, s);
     else
-        rc = launch_prefill_ffn(xb, w13, w13_scale, w2, w2_scale, sh, p, T, H, I, E, k, abuf, ybuf,
-                                s);
+        rc = launch_prefill_ffn(weight_layout, xb, w13, w13_scale, w2, w2_scale, sh, p, T, H, I,
+                                E, k, abuf, ybuf, s);
     if (rc) return rc;
     return launch_combine(ybuf, p.inv_route, aff, T, H, k, has_shared, out, s);
+}
+
+int moe_pack_w8(const uint8_t* src, uint8_t* dst, int64_t n_mats, int rows, int cols,
+                void* stream) {
+    g_err[0] = 0;
+    if (n_mats < 0 || rows < 0 || cols < 0 || rows % 16 || cols % 64) {
+        set_error("moe_pack_w8: need n_mats, rows, cols >= 0, rows %% 16 == 0, cols %% 64 == 0 "
+                  "(got %lld, %d, %d)", (long long)n_mats, rows, cols);
+        return MOE_EINVAL;
+    }
+    if (n_mats == 0 || rows == 0 || cols == 0) return MOE_OK;
+    if (!src || !dst) {
+        set_error("moe_pack_w8: src and dst must be non-NULL");
+        return MOE_EINVAL;
+    }
+    const size_t bytes = (size_t)n_mats * rows * cols;
+    const char* a = reinterpret_cast<const char*>(src);
+    const char* b = reinterpret_cast<const char*>(dst);
+    if (a < b + bytes && b < a + bytes) {
+        set_error("moe_pack_w8: src and dst overlap");
+        return MOE_EINVAL;
+    }
+    return launch_pack_w8(src, dst, n_mats, rows, cols, (hipStream_t)stream);
 }
 
 int moe_decode_e4m3fn(const uint8_t* codes, uint16_t* out, int64_t n, void* stream) {

@@ -42,6 +42,24 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {
     return __builtin_bit_cast(bf16x8, v);
 }
 
+// ---------------------------------------------------------------- weight layouts
+// A weight matrix [rows, K] of FP8 bytes (rows % 16 == 0, K % 64 == 0) is
+// consumed in 16-row tiles and 64-wide K chunks; lane l of a wave takes the 16
+// bytes of row 16*t + l%16, columns 64*c + 16*(l/16) .. +15.
+//  - row-major: those 16 bytes sit at row * K + column;
+//  - tiled:     tile t, chunk c is one contiguous kilobyte, lane l at byte 16*l,
+//               so a wave's load of one chunk is a single 1 KB burst.
+enum { LAYOUT_ROWMAJOR = MOE_LAYOUT_ROWMAJOR, LAYOUT_TILED = MOE_LAYOUT_TILED };
+
+template <int LAYOUT>
+__device__ __forceinline__ const uint8_t* tile_lane_ptr(const uint8_t* W, int row0, int K, int lane) {
+    if (LAYOUT == LAYOUT_TILED) return W + (size_t)(row0 >> 4) * 16 * K + lane * 16;
+    return W + (size_t)(row0 + (lane & 15)) * K + (lane >> 4) * 16;
+}
+
+template <int LAYOUT>
+__device__ __forceinline__ constexpr int chunk_stride() { return LAYOUT == LAYOUT_TILED ? 1024 : 64; }
+
 // ---------------------------------------------------------------- bf16 <-> f32
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
     return __uint_as_float(((uint32_t)b) << 16);
@@ -62,6 +80,13 @@ __device__ __forceinline__ float swiglu(float g, float u) {
 
 // ---------------------------------------------------------------- wave helpers
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (MOE_WAVE - 1); }
+
+// Wave index inside the workgroup, marked wave-uniform so that values derived
+// from it (tile rows, scale addresses) live in SGPRs and scale reads become
+// scalar loads that never wait on the vector-memory counter.
+__device__ __forceinline__ int wave_id() {
+    return __builtin_amdgcn_readfirstlane(threadIdx.x / MOE_WAVE);
+}
 
 __device__ __forceinline__ uint64_t lanemask_lt() {
     const int l = lane_id();

@@ -17,6 +17,8 @@
 // sums over K.  Each 128-wide K block accumulates into a fresh fp32 partial
 // that is multiplied by the block's fp32 scale before joining the total, so
 // the scale is never rounded into bf16.
+#include <algorithm>
+
 #include "common.hpp"
 #include "plan.hpp"
 
@@ -32,11 +34,13 @@ constexpr int DEC_DEPTH = 4;   // 64-K chunks in flight per wave
 // MODE_GATEUP: rows = 32 gate rows + the 32 matching up rows, K = H,
 //              A = x rows of the segment's tokens, out = bf16 SwiGLU into abuf.
 // MODE_DOWN:   rows = 64 rows of W2, K = I, A = abuf rows, out = fp32 ybuf.
-template <int MODE, int MT>
+template <int MODE, int MT, int LAYOUT>
 __global__ __launch_bounds__(DEC_THREADS) void decode_ffn_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ w13,
     const float* __restrict__ w13s, const uint8_t* __restrict__ w2,
-    const float* __restrict__ w2s, SharedW shared, Plan plan, int T, int H, int I, int k,
+    const float* __restrict__ w2s, const uint8_t* __restrict__ sh_w13,
+    const float* __restrict__ sh_w13s, const uint8_t* __restrict__ sh_w2,
+    const float* __restrict__ sh_w2s, Plan plan, int T, int H, int I, int k,
     uint16_t* __restrict__ abuf, float* __restrict__ ybuf) {
     constexpr int MROWS = 16 * MT;
     const int K = MODE == MODE_GATEUP ? H : I;
@@ -51,15 +55,15 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_ffn_kernel(
     const uint8_t* W;
     const float* S;
     if (MODE == MODE_GATEUP) {
-        W = e >= 0 ? w13 + (size_t)e * 2 * I * H : shared.w13;
-        S = e >= 0 ? w13s + (size_t)e * (2 * I / 128) * (H / 128) : shared.w13_scale;
+        W = e >= 0 ? w13 + (size_t)e * 2 * I * H : sh_w13;
+        S = e >= 0 ? w13s + (size_t)e * (2 * I / 128) * (H / 128) : sh_w13s;
     } else {
-        W = e >= 0 ? w2 + (size_t)e * H * I : shared.w2;
-        S = e >= 0 ? w2s + (size_t)e * (H / 128) * (I / 128) : shared.w2_scale;
+        W = e >= 0 ? w2 + (size_t)e * H * I : sh_w2;
+        S = e >= 0 ? w2s + (size_t)e * (H / 128) * (I / 128) : sh_w2s;
     }
     const int kblocks = K / 128;
 
-    const int lane = lane_id(), wave = threadIdx.x / MOE_WAVE;
+    const int lane = lane_id(), wave = wave_id();
     const int ln = lane & 15, lg = lane >> 4;
 
     // weight rows of the 4 tiles
@@ -73,7 +77,7 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_ffn_kernel(
     }
     const uint8_t* bptr[DEC_NTILE];
 #pragma unroll
-    for (int j = 0; j < DEC_NTILE; ++j) bptr[j] = W + (size_t)(brow[j] + ln) * K + lg * 16;
+    for (int j = 0; j < DEC_NTILE; ++j) bptr[j] = tile_lane_ptr<LAYOUT>(W, brow[j], K, lane);
 
     // this wave's 64-K chunks
     const int nchunk = K / 64;
@@ -124,7 +128,7 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_ffn_kernel(
         auto issue = [&](int d, int c) {
 #pragma unroll
             for (int j = 0; j < DEC_NTILE; ++j)
-                bq[d][j] = *reinterpret_cast<const u32x4*>(bptr[j] + (size_t)c * 64);
+                bq[d][j] = *reinterpret_cast<const u32x4*>(bptr[j] + (size_t)c * chunk_stride<LAYOUT>());
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
                 const u32x4* ap = reinterpret_cast<const u32x4*>(aptr[mt] + (size_t)c * 64);
@@ -164,7 +168,9 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_ffn_kernel(
                         const int kb = c >> 1;
 #pragma unroll
                         for (int j = 0; j < DEC_NTILE; ++j) {
-                            const float sc = S[(size_t)(brow[j] / 128) * kblocks + kb];
+                            // uniform index -> scalar load (no wait on in-flight weight loads)
+                        const int sidx = __builtin_amdgcn_readfirstlane((brow[j] >> 7) * kblocks + kb);
+                        const float sc = S[sidx];
 #pragma unroll
                             for (int mt = 0; mt < MT; ++mt) {
                                 acc[mt][j] += sc * part[mt][j];
@@ -248,34 +254,63 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     *reinterpret_cast<f32x4*>(out + (size_t)t * H + h) = acc;
 }
 
-template <int MODE>
-static int launch_decode_mode(int MT, int nseg_max, const uint16_t* x, const uint8_t* w13,
-                              const float* w13s, const uint8_t* w2, const float* w2s,
-                              const SharedW& sh, const Plan& plan, int T, int H, int I, int k,
-                              uint16_t* abuf, float* ybuf, hipStream_t stream) {
+template <int MODE, int LAYOUT>
+static int launch_decode_mode_l(int MT, int nseg_max, const uint16_t* x, const uint8_t* w13,
+                                const float* w13s, const uint8_t* w2, const float* w2s,
+                                const SharedW& sh, const Plan& plan, int T, int H, int I, int k,
+                                uint16_t* abuf, float* ybuf, hipStream_t stream) {
     const int ntile = MODE == MODE_GATEUP ? I / 32 : H / 64;
     const dim3 grid((unsigned)nseg_max * ntile), block(DEC_THREADS);
     prof_begin(MODE == MODE_GATEUP ? "decode_gateup_swiglu" : "decode_down", stream);
     if (MT == 1)
-        decode_ffn_kernel<MODE, 1><<<grid, block, 0, stream>>>(x, w13, w13s, w2, w2s, sh, plan, T,
-                                                               H, I, k, abuf, ybuf);
+        decode_ffn_kernel<MODE, 1, LAYOUT><<<grid, block, 0, stream>>>(
+            x, w13, w13s, w2, w2s, sh.w13, sh.w13_scale, sh.w2, sh.w2_scale, plan, T, H, I, k, abuf,
+            ybuf);
     else
-        decode_ffn_kernel<MODE, 2><<<grid, block, 0, stream>>>(x, w13, w13s, w2, w2s, sh, plan, T,
-                                                               H, I, k, abuf, ybuf);
+        decode_ffn_kernel<MODE, 2, LAYOUT><<<grid, block, 0, stream>>>(
+            x, w13, w13s, w2, w2s, sh.w13, sh.w13_scale, sh.w2, sh.w2_scale, plan, T, H, I, k, abuf,
+            ybuf);
     prof_end(stream);
     return check_launch(MODE == MODE_GATEUP ? "decode_ffn_kernel<gateup>" : "decode_ffn_kernel<down>");
 }
 
-int launch_decode_ffn(const uint16_t* x, const uint8_t* w13, const float* w13s, const uint8_t* w2,
-                      const float* w2s, const SharedW& sh, const Plan& plan, int T, int H, int I,
-                      int E, int k, uint16_t* abuf, float* ybuf, hipStream_t stream) {
+template <int MODE>
+static int launch_decode_mode(int layout, int MT, int nseg_max, const uint16_t* x,
+                              const uint8_t* w13, const float* w13s, const uint8_t* w2,
+                              const float* w2s, const SharedW& sh, const Plan& plan, int T, int H,
+                              int I, int k, uint16_t* abuf, float* ybuf, hipStream_t stream) {
+    if (layout == LAYOUT_TILED)
+        return launch_decode_mode_l<MODE, LAYOUT_TILED>(MT, nseg_max, x, w13, w13s, w2, w2s, sh,
+                                                        plan, T, H, I, k, abuf, ybuf, stream);
+    return launch_decode_mode_l<MODE, LAYOUT_ROWMAJOR>(MT, nseg_max, x, w13, w13s, w2, w2s, sh,
+                                                       plan, T, H, I, k, abuf, ybuf, stream);
+}
+
+int launch_decode_fused(int layout, int MT, const uint16_t* x, const uint8_t* w13,
+                        const float* w13s, const uint8_t* w2, const float* w2s, const SharedW& sh,
+                        const Plan& plan, int T, int H, int I, int E, int k, float* ybuf,
+                        hipStream_t stream);
+
+// At most min(E, T*k) routed experts are active.  When that fills most of the
+// chip, one workgroup per active expert (ffn_decode_fused.hip) streams every
+// weight byte once with no inter-workgroup dependency; with few active
+// experts the work is split into (expert, N tile) workgroups over two kernels
+// so that all CUs still stream.
+int launch_decode_ffn(int layout, const uint16_t* x, const uint8_t* w13, const float* w13s,
+                      const uint8_t* w2, const float* w2s, const SharedW& sh, const Plan& plan,
+                      int T, int H, int I, int E, int k, uint16_t* abuf, float* ybuf,
+                      hipStream_t stream) {
     const int has_shared = sh.w13 != nullptr;
     const int nseg_max = E + has_shared;
     const int MT = ((long)T * k <= 4L * E) ? 1 : 2;
-    if (int rc = launch_decode_mode<MODE_GATEUP>(MT, nseg_max, x, w13, w13s, w2, w2s, sh, plan, T,
+    const long max_active = std::min<long>(E, (long)T * k) + has_shared;
+    if (max_active >= 128)
+        return launch_decode_fused(layout, MT, x, w13, w13s, w2, w2s, sh, plan, T, H, I, E, k,
+                                   ybuf, stream);
+    if (int rc = launch_decode_mode<MODE_GATEUP>(layout, MT, nseg_max, x, w13, w13s, w2, w2s, sh, plan, T,
                                                  H, I, k, abuf, ybuf, stream))
         return rc;
-    return launch_decode_mode<MODE_DOWN>(MT, nseg_max, x, w13, w13s, w2, w2s, sh, plan, T, H, I,
+    return launch_decode_mode<MODE_DOWN>(layout, MT, nseg_max, x, w13, w13s, w2, w2s, sh, plan, T, H, I,
                                          k, abuf, ybuf, stream);
 }
 

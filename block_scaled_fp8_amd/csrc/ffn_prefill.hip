@@ -6,7 +6,7 @@ namespace moe {
 
 int prefill_tile_m() { return 128; }
 
-int launch_prefill_ffn(const uint16_t*, const uint8_t*, const float*, const uint8_t*,
+int launch_prefill_ffn(int, const uint16_t*, const uint8_t*, const float*, const uint8_t*,
                        const float*, const SharedW&, const Plan&, int, int, int, int, int,
                        uint16_t*, float*, hipStream_t) {
     set_error("moe_fused_w8a16: the prefill variant is not available in this build");

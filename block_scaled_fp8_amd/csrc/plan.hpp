@@ -38,12 +38,16 @@ int launch_sort(const int32_t* ids, int T, int k, int E, const Plan& plan, int h
 // Kernel launchers (route.hip, ffn_decode.hip, ffn_prefill.hip, misc).
 int launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* aff,
                  int32_t* status, hipStream_t stream);
-int launch_decode_ffn(const uint16_t* x, const uint8_t* w13, const float* w13s, const uint8_t* w2,
-                      const float* w2s, const SharedW& sh, const Plan& plan, int T, int H, int I,
-                      int E, int k, uint16_t* abuf, float* ybuf, hipStream_t stream);
-int launch_prefill_ffn(const uint16_t* x, const uint8_t* w13, const float* w13s, const uint8_t* w2,
-                       const float* w2s, const SharedW& sh, const Plan& plan, int T, int H, int I,
-                       int E, int k, uint16_t* abuf, float* ybuf, hipStream_t stream);
+int launch_decode_ffn(int layout, const uint16_t* x, const uint8_t* w13, const float* w13s,
+                      const uint8_t* w2, const float* w2s, const SharedW& sh, const Plan& plan,
+                      int T, int H, int I, int E, int k, uint16_t* abuf, float* ybuf,
+                      hipStream_t stream);
+int launch_prefill_ffn(int layout, const uint16_t* x, const uint8_t* w13, const float* w13s,
+                       const uint8_t* w2, const float* w2s, const SharedW& sh, const Plan& plan,
+                       int T, int H, int I, int E, int k, uint16_t* abuf, float* ybuf,
+                       hipStream_t stream);
+int launch_pack_w8(const uint8_t* src, uint8_t* dst, int64_t n_mats, int rows, int cols,
+                   hipStream_t stream);
 int prefill_tile_m();
 int launch_combine(const float* ybuf, const int32_t* inv_route, const float* aff, int T, int H,
                    int k, int has_shared, float* out, hipStream_t stream);

@@ -5,11 +5,9 @@
 // contract: the router is softmax -> top-8 -> norm.
 //
 // One wave64 per token; lane l holds experts l, l+64, ... (NPL per lane).
-// Selection runs k wave-wide arg-max passes over 64-bit keys
-//     key = (order-preserving bits of the fp32 logit) << 32 | ~expert
-// so a larger logit wins and, between equal logits, the lower expert index
-// wins.  -0.0 is canonicalised to +0.0 first (they tie); NaN maps to the
-// lowest key.  Softmax is strictly increasing, so choosing on logits picks
+// Selection runs k wave-wide arg-max passes: a larger logit wins and, between
+// equal logits, the lower expert index wins.  -0.0 is canonicalised to +0.0
+// first (they tie); NaN ranks below every other value.  Softmax is strictly increasing, so choosing on logits picks
 // the same experts as choosing on probabilities, without exp() rounding
 // ever reordering them.  The renormalised affinity of slot j is
 //     p_j / sum_sel p = exp(l_j - M) / sum_sel exp(l - M),
@@ -19,30 +17,55 @@
 
 namespace moe {
 
-__device__ __forceinline__ uint64_t route_key(float v, int e) {
-    uint32_t b = __float_as_uint(v == 0.0f ? 0.0f : v);
-    uint32_t o = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-    if (v != v) o = 0u;
-    return ((uint64_t)o << 32) | (uint64_t)(~(uint32_t)e);
+// Order-preserving unsigned image of a float: larger float -> larger value;
+// -0.0 maps like +0.0 and NaN to 0 (below -inf).
+__device__ __forceinline__ uint32_t ordered_bits(float v) {
+    const uint32_t b = __float_as_uint(v == 0.0f ? 0.0f : v);
+    const uint32_t o = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+    return v != v ? 0u : o;
 }
 
-__device__ __forceinline__ float key_logit(uint64_t key) {
-    uint32_t o = (uint32_t)(key >> 32);
-    uint32_t b = (o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o;
-    return __uint_as_float(b);
+__device__ __forceinline__ float from_ordered(uint32_t o) {
+    return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        uint32_t lo = __shfl_xor((uint32_t)v, o, MOE_WAVE);
-        uint32_t hi = __shfl_xor((uint32_t)(v >> 32), o, MOE_WAVE);
-        uint64_t w = ((uint64_t)hi << 32) | lo;
-        v = w > v ? w : v;
+// DPP controls (gfx9): quad_perm(1,0,3,2), quad_perm(2,3,0,1), row_ror:4, row_ror:8.
+#define MOE_DPP_QP_1032 0xB1
+#define MOE_DPP_QP_2301 0x4E
+#define MOE_DPP_ROR4 0x124
+#define MOE_DPP_ROR8 0x128
+
+__device__ __forceinline__ uint32_t dpp_max(uint32_t v, int ctrl) {
+    uint32_t o = 0;
+    switch (ctrl) {  // the control must be a literal
+        case MOE_DPP_QP_1032: o = __builtin_amdgcn_update_dpp(0, (int)v, MOE_DPP_QP_1032, 0xF, 0xF, false); break;
+        case MOE_DPP_QP_2301: o = __builtin_amdgcn_update_dpp(0, (int)v, MOE_DPP_QP_2301, 0xF, 0xF, false); break;
+        case MOE_DPP_ROR4: o = __builtin_amdgcn_update_dpp(0, (int)v, MOE_DPP_ROR4, 0xF, 0xF, false); break;
+        default: o = __builtin_amdgcn_update_dpp(0, (int)v, MOE_DPP_ROR8, 0xF, 0xF, false); break;
     }
-    return v;
+    return o > v ? o : v;
 }
 
+// Wave-wide maximum, returned as a wave-uniform value: a butterfly inside each
+// 16-lane row (DPP), then the four row maxima read as scalars.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = dpp_max(v, MOE_DPP_QP_1032);
+    v = dpp_max(v, MOE_DPP_QP_2301);
+    v = dpp_max(v, MOE_DPP_ROR4);
+    v = dpp_max(v, MOE_DPP_ROR8);
+    const uint32_t r0 = __builtin_amdgcn_readlane((int)v, 0);
+    const uint32_t r1 = __builtin_amdgcn_readlane((int)v, 16);
+    const uint32_t r2 = __builtin_amdgcn_readlane((int)v, 32);
+    const uint32_t r3 = __builtin_amdgcn_readlane((int)v, 48);
+    const uint32_t a = r0 > r1 ? r0 : r1, b = r2 > r3 ? r2 : r3;
+    return a > b ? a : b;
+}
+
+// Each of the k passes takes the wave-wide maximum of the ordered logit bits,
+// then the lowest expert index holding that maximum (one ballot per register
+// slot: slot i holds experts 64*i + lane, so the first slot with a hit and its
+// lowest lane give the lowest index).  The chosen entry leaves the candidate
+// set; padding entries are never candidates.
 template <int NPL>
 __global__ __launch_bounds__(256) void route_topk_softmax_kernel(
     const float* __restrict__ logits, int T, int E, int k,
@@ -52,38 +75,44 @@ __global__ __launch_bounds__(256) void route_topk_softmax_kernel(
     if (t >= T) return;
     const float* row = logits + (size_t)t * E;
 
-    uint64_t key[NPL];
+    uint32_t o[NPL];
+    bool cand[NPL];
     bool bad = false;
 #pragma unroll
     for (int i = 0; i < NPL; ++i) {
         const int e = lane + MOE_WAVE * i;
-        if (e < E) {
-            const float v = row[e];
-            bad |= !__builtin_isfinite(v);
-            key[i] = route_key(v, e);
-        } else {
-            key[i] = 0ull;  // padding: below every real key
-        }
+        cand[i] = e < E;
+        const float v = cand[i] ? row[e] : 0.0f;
+        bad |= cand[i] && !__builtin_isfinite(v);
+        o[i] = cand[i] ? ordered_bits(v) : 0u;
     }
     if (status && __ballot(bad) != 0ull && lane == 0) atomicOr(status, MOE_STATUS_NONFINITE_LOGIT);
 
-    float my_logit = 0.0f;
+    uint32_t my_o = 0, top_o = 0;
     int my_id = 0;
     for (int j = 0; j < k; ++j) {
-        uint64_t best = key[0];
-#pragma unroll
-        for (int i = 1; i < NPL; ++i) best = key[i] > best ? key[i] : best;
-        best = wave_max_u64(best);
+        uint32_t best = 0;
 #pragma unroll
         for (int i = 0; i < NPL; ++i)
-            if (key[i] == best) key[i] = 0ull;  // keys are unique (index in low bits)
+            if (cand[i] && o[i] > best) best = o[i];
+        const uint32_t gmax = wave_max_u32(best);
+        int sel = -1;
+#pragma unroll
+        for (int i = 0; i < NPL; ++i) {
+            const uint64_t hit = __ballot(cand[i] && o[i] == gmax);
+            if (sel < 0 && hit != 0ull) sel = __builtin_ctzll(hit) + MOE_WAVE * i;
+        }
+#pragma unroll
+        for (int i = 0; i < NPL; ++i)
+            if (lane + MOE_WAVE * i == sel) cand[i] = false;
+        if (j == 0) top_o = gmax;
         if (lane == j) {
-            my_id = (int)(~(uint32_t)best);
-            my_logit = key_logit(best);
+            my_id = sel;
+            my_o = gmax;
         }
     }
-    const float M = __shfl(my_logit, 0, MOE_WAVE);
-    const float w = lane < k ? expf(my_logit - M) : 0.0f;
+    const float M = from_ordered(top_o);
+    const float w = lane < k ? expf(from_ordered(my_o) - M) : 0.0f;
     const float s = wave_sum_f32(w);
     if (lane < k) {
         ids[(size_t)t * k + lane] = my_id;

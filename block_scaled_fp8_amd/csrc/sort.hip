@@ -10,8 +10,8 @@
 // Determinism: LDS atomics only ever build histograms (their result does not
 // depend on arrival order).  Ranks inside an expert never come from atomic
 // return values: each wave walks its contiguous range of routes in order, 64
-// at a time, and ranks equal ids inside a step with ballot matching, on top of
-// per-(block, wave, expert) bases from exclusive scans.  So route r sits at
+// at a time, and ranks equal ids inside a step by comparing against every
+// lane's id, on top of per-(block, wave, expert) bases from exclusive scans.  So route r sits at
 //     offsets[e] + #{ r' < r : ids[r'] == e },
 // the stable expert-major order.
 #include "common.hpp"
@@ -19,7 +19,7 @@
 
 namespace moe {
 
-constexpr int SORT_SMALL_THREADS = 512;       // single-workgroup path
+constexpr int SORT_SMALL_THREADS = 1024;      // single-workgroup path
 constexpr int SORT_SMALL_MAX_ROUTES = 16384;
 constexpr int SORT_CHUNK = 4096;              // routes per workgroup, multi-workgroup path
 constexpr int SORT_THREADS = 256;
@@ -72,28 +72,32 @@ __device__ bool count_range(const int32_t* __restrict__ ids, int r0, int r1, int
     return bad;
 }
 
-// One wave places routes [r_begin, r_end) in order.  wcnt[e] is the position
-// of this wave's next route of expert e (LDS, touched by this wave only).
+// One wave places routes [r_begin, r_end) in order, 64 at a time.  wcnt[e] is
+// the position of this wave's next route of expert e (LDS, touched by this
+// wave only).  Inside a step, the rank of a lane among the lanes holding the
+// same id is counted against every lane's id read as a scalar (readlane), so
+// the step costs a fixed, short sequence of ALU instructions.
 __device__ void wave_place(const int32_t* __restrict__ ids, int r_begin, int r_end, int E, int* wcnt,
                            int32_t* __restrict__ sorted_route, int32_t* __restrict__ inv_route) {
     const int lane = lane_id();
     for (int r0 = r_begin; r0 < r_end; r0 += MOE_WAVE) {
         const int r = r0 + lane;
         const bool in = r < r_end;
-        const int id = in ? ids[r] : -1;
-        const bool valid = in && id >= 0 && id < E;
-        uint64_t remaining = __ballot(valid);
-        int pos = -1;
-        while (remaining) {
-            const int leader = __builtin_ctzll(remaining);
-            const int lid = __shfl(id, leader, MOE_WAVE);
-            const bool mine = valid && id == lid;
-            const uint64_t m = __ballot(mine);
-            if (mine) pos = wcnt[lid] + __popcll(m & lanemask_lt());
-            // every lane of the group has read the base before the leader bumps it
-            if (lane == leader) wcnt[lid] += __popcll(m);
-            remaining &= ~m;
+        const int raw = in ? ids[r] : -1;
+        const bool valid = in && raw >= 0 && raw < E;
+        const int id = valid ? raw : -1;
+        int rank = 0, cnt = 0;
+#pragma unroll
+        for (int l = 0; l < MOE_WAVE; ++l) {
+            const int other = __builtin_amdgcn_readlane(id, l);
+            const int same = (other == id) ? 1 : 0;
+            rank += (l < lane) ? same : 0;
+            cnt += same;
         }
+        int pos = -1;
+        if (valid) pos = wcnt[id] + rank;
+        // every lane has read its base before the group's first lane bumps it
+        if (valid && rank == 0) wcnt[id] += cnt;
         if (in) {
             if (valid) {
                 sorted_route[pos] = r;

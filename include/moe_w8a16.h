@@ -68,6 +68,11 @@ enum {
     MOE_VARIANT_PREFILL = 2   /* grouped bf16-MFMA GEMM over 128-row tiles of sorted routes */
 };
 
+enum {
+    MOE_LAYOUT_ROWMAJOR = 0,  /* FP8 weights as [rows, K], K contiguous */
+    MOE_LAYOUT_TILED = 1      /* tile-coalesced, see moe_pack_w8 */
+};
+
 /* Message describing the most recent failure on the calling thread ("" if none). */
 const char* moe_last_error(void);
 
@@ -109,6 +114,21 @@ int moe_sort(const int32_t* ids, int T, int k, int E,
              int32_t* sorted_route, int32_t* inv_route,
              int32_t* status, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * moe_pack_w8 -- offline weight preparation: reorder FP8 weight bytes into the
+ * tile-coalesced layout the decode kernels stream.  Source: NKI page, file
+ * table (moe_w8.py: offline weight prep that packs coalesced operands).
+ * For each of n_mats matrices W[rows, cols] (row-major, rows % 16 == 0,
+ * cols % 64 == 0) the packed matrix P holds, for tile t < rows/16, chunk
+ * c < cols/64, lane l < 64 and byte b < 16,
+ *     P[((t * (cols/64) + c) * 64 + l) * 16 + b] = W[16t + l%16][64c + 16(l/16) + b],
+ * so one wave's 16-byte-per-lane load of a tile chunk is one contiguous 1 KB.
+ * The byte count and the block scales are unchanged.  src and dst are device
+ * pointers of n_mats*rows*cols bytes each and must not overlap.
+ */
+int moe_pack_w8(const uint8_t* src, uint8_t* dst, int64_t n_mats, int rows, int cols,
+                void* stream);
+
 /* One expert's block-scaled FP8 weights (same H and I as the routed experts). */
 typedef struct {
     const uint8_t* w13;        /* [2I, H] E4M3FN: rows 0..I-1 gate, I..2I-1 up */
@@ -132,6 +152,8 @@ typedef struct {
  *   out        [T, H] fp32, overwritten (must not alias x)          (out)
  *   status     int32 or NULL                                        (in/out)
  *   ws         device scratch of moe_fused_workspace_bytes(...) bytes
+ *   weight_layout  MOE_LAYOUT_ROWMAJOR or MOE_LAYOUT_TILED (moe_pack_w8
+ *              output); applies to w13, w2 and the shared expert alike
  *   variant    MOE_VARIANT_*
  * H and I must be multiples of 128 (else MOE_EUNSUPPORTED); T >= 0; T == 0
  * is a no-op.  The expert FFN computes in bf16 x bf16 products with fp32
@@ -147,7 +169,7 @@ int moe_fused_w8a16(const void* x,
                     int T, int H, int I, int E, int k,
                     const moe_expert_w8* shared, float* out,
                     int32_t* status, void* ws, size_t ws_bytes,
-                    int variant, void* stream);
+                    int weight_layout, int variant, void* stream);
 
 /*
  * moe_decode_e4m3fn -- decode n E4M3FN bytes to bf16 bit patterns with the

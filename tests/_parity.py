@@ -62,3 +62,28 @@ def sample_rows(T, n, seed=0):
     rng = np.random.default_rng(seed)
     pick = set(rng.choice(T, size=n - 2, replace=False).tolist()) | {0, T - 1}
     return np.array(sorted(pick))
+
+
+def pack_reference(w):
+    """numpy statement of the tile-coalesced layout: out[((t*(C/64)+c)*64+l)*16+b] =
+    w[16t + l%16, 64c + 16(l//16) + b] for each matrix."""
+    w = np.asarray(w)
+    *lead, R, C = w.shape
+    v = w.reshape(*lead, R // 16, 16, C // 64, 4, 16)          # [.., t, l%16, c, l//16, b]
+    v = np.moveaxis(v, -2, -4)                                    # [.., t, l//16, l%16, c, b]
+    v = np.moveaxis(v, -2, -4)                                    # [.., t, c, l//16, l%16, b]
+    return np.ascontiguousarray(v).reshape(w.shape)
+
+
+def tiled_case(case):
+    """A copy of a GPU case whose expert weights are packed for the tiled layout."""
+    from block_scaled_fp8_amd import binding
+    out = dict(case)
+    out["w13"] = binding.pack_w8(case["w13"])
+    out["w2"] = binding.pack_w8(case["w2"])
+    if case.get("shared") is not None:
+        sh = dict(case["shared"])
+        sh["w13"] = binding.pack_w8(sh["w13"])
+        sh["w2"] = binding.pack_w8(sh["w2"])
+        out["shared"] = sh
+    return out

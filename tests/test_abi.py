@@ -23,7 +23,8 @@ def _declared_functions():
 def test_header_declares_the_boundary():
     names = _declared_functions()
     for n in ("moe_route", "moe_sort", "moe_fused_w8a16", "moe_last_error",
-              "moe_sort_workspace_bytes", "moe_fused_workspace_bytes", "moe_decode_e4m3fn"):
+              "moe_sort_workspace_bytes", "moe_fused_workspace_bytes", "moe_decode_e4m3fn",
+              "moe_pack_w8"):
         assert n in names
     assert set(names) == set(binding.EXPORTED)
 
@@ -76,14 +77,16 @@ def test_fused_argument_checks():
     o = ctypes.c_void_p(0x3000)
     ws = lib.moe_fused_workspace_bytes(64, 2048, 512, 256, 8, 0, 0)
     assert ws > 64 * 8 * (512 * 2 + 2048 * 4)
-    args = lambda T, H, I, E, k, ws_bytes, variant=0, out=o: (  # noqa: E731
-        f, f, f, f, f, f, f, T, H, I, E, k, None, out, None, f, ws_bytes, variant, None)
+    args = lambda T, H, I, E, k, ws_bytes, variant=0, out=o, layout=0: (  # noqa: E731
+        f, f, f, f, f, f, f, T, H, I, E, k, None, out, None, f, ws_bytes, layout, variant, None)
     assert lib.moe_fused_w8a16(*args(64, 2000, 512, 256, 8, ws)) == binding.MOE_EUNSUPPORTED
     assert lib.moe_fused_w8a16(*args(64, 2048, 500, 256, 8, ws)) == binding.MOE_EUNSUPPORTED
     assert b"multiples of 128" in lib.moe_last_error()
     assert lib.moe_fused_w8a16(*args(64, 2048, 512, 256, 8, ws - 1)) == binding.MOE_EINVAL
     assert b"workspace" in lib.moe_last_error()
     assert lib.moe_fused_w8a16(*args(64, 2048, 512, 256, 8, ws, 7)) == binding.MOE_EINVAL
+    assert lib.moe_fused_w8a16(*args(64, 2048, 512, 256, 8, ws, 0, o, 5)) == binding.MOE_EINVAL
+    assert b"layout" in lib.moe_last_error()
     assert lib.moe_fused_w8a16(*args(64, 2048, 512, 256, 300, ws)) == binding.MOE_EINVAL
     # out aliasing x
     assert lib.moe_fused_w8a16(*args(64, 2048, 512, 256, 8, ws, 0, f)) == binding.MOE_EINVAL
@@ -111,3 +114,14 @@ def test_binding_refuses_cpu_tensors():
     import torch
     with pytest.raises(ValueError):
         binding.route(torch.zeros((4, 8), dtype=torch.float32), 2)
+
+
+def test_pack_argument_checks():
+    lib = binding.load_library()
+    f = ctypes.c_void_p(0x1000)
+    g = ctypes.c_void_p(0x1000 + 8 * 256 * 512)
+    assert lib.moe_pack_w8(f, g, 8, 250, 512, None) == binding.MOE_EINVAL   # rows % 16
+    assert lib.moe_pack_w8(f, g, 8, 256, 100, None) == binding.MOE_EINVAL   # cols % 64
+    assert lib.moe_pack_w8(f, ctypes.c_void_p(0x1000 + 64), 8, 256, 512, None) == binding.MOE_EINVAL
+    assert b"overlap" in lib.moe_last_error()
+    assert lib.moe_pack_w8(None, None, 0, 256, 512, None) == binding.MOE_OK

@@ -12,7 +12,8 @@ import torch
 import oracle
 from block_scaled_fp8_amd import binding, synth
 
-from _parity import (AFF_RTOL, assert_out_close, gpu_case, np_, oracle_rows, sample_rows)
+from _parity import (AFF_RTOL, assert_out_close, gpu_case, np_, oracle_rows, pack_reference,
+                     sample_rows, tiled_case)
 
 pytestmark = pytest.mark.gpu
 
@@ -163,77 +164,104 @@ def test_sort_drops_bad_ids(T):
     assert np.array_equal(np_(sr)[inv_np[good]], routes)
 
 
+# ------------------------------------------------------------------ weight packing
+@pytest.mark.parametrize("shape", [(1, 16, 64), (3, 256, 128), (8, 1024, 2048), (2, 2048, 512)])
+def test_pack_w8_matches_reference(shape):
+    g = torch.Generator().manual_seed(sum(shape))
+    w = torch.randint(0, 256, shape, generator=g, dtype=torch.int64).to(torch.uint8)
+    got = binding.pack_w8(w.cuda())
+    assert np.array_equal(np_(got), pack_reference(w.numpy()))
+
+
 # ------------------------------------------------------------------ fused FFN
-def _fused(c, ids, aff, variant="auto", shared=True, **kw):
-    return binding.fused_w8a16(c["x"], c["w13"], c["w13_scale"], c["w2"], c["w2_scale"], ids,
-                               aff, shared=c["shared"] if shared else None, variant=variant, **kw)
+LAYOUTS = ["rowmajor", "tiled"]
+_tiled = {"src": None, "packed": None}   # holds its source case, so identity stays valid
 
 
+def _fused(c, ids, aff, variant="auto", shared=True, layout="rowmajor", **kw):
+    if layout == "tiled":
+        if _tiled["src"] is not c:
+            _tiled["src"], _tiled["packed"] = None, None
+            _tiled["packed"] = tiled_case(c)
+            _tiled["src"] = c
+        g = _tiled["packed"]
+    else:
+        g = c
+    return binding.fused_w8a16(g["x"], g["w13"], g["w13_scale"], g["w2"], g["w2_scale"], ids,
+                               aff, shared=g["shared"] if shared else None, variant=variant,
+                               layout=layout, **kw)
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("variant", ["decode"])
 @pytest.mark.parametrize("name", synth.CONFIG_ORDER)
-def test_fused_parity(name, variant):
+def test_fused_parity(name, variant, layout):
     """End to end on the GPU (route -> sort -> FFN), oracle from the logits."""
     c = _case(name)
     cfg = c["cfg"]
     ids, aff = binding.route(c["logits"], cfg.k)
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
-    out = _fused(c, ids, aff, variant=variant, status=status)
+    out = _fused(c, ids, aff, variant=variant, status=status, layout=layout)
     torch.cuda.synchronize()
     assert int(status.item()) == 0
     ref_ids, ref_aff = oracle.route_softmax_topk(np_(c["logits"]), cfg.k)
     assert np.array_equal(np_(ids), ref_ids)
     rows = sample_rows(cfg.T, FFN_SAMPLE[name], seed=2)
     ref = oracle_rows(c, ref_ids, ref_aff, rows)
-    assert_out_close(np_(out)[rows], ref, what=f"{name}/{variant}")
+    assert_out_close(np_(out)[rows], ref, what=f"{name}/{variant}/{layout}")
 
 
+@pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("variant", ["decode"])
 @pytest.mark.parametrize("T", [1, 15, 16, 17, 37])
-def test_fused_token_boundaries(T, variant):
+def test_fused_token_boundaries(T, variant, layout):
     cfg = synth.MoeConfig("b", T=T, H=256, I=256, E=16, k=4)
     c = gpu_case(cfg, seed=T)
     ids, aff = binding.route(c["logits"], cfg.k)
-    out = _fused(c, ids, aff, variant=variant)
+    out = _fused(c, ids, aff, variant=variant, layout=layout)
     ref_ids, ref_aff = oracle.route_softmax_topk(np_(c["logits"]), cfg.k)
     ref = oracle_rows(c, ref_ids, ref_aff, np.arange(T))
-    assert_out_close(np_(out), ref, what=f"T={T}/{variant}")
+    assert_out_close(np_(out), ref, what=f"T={T}/{variant}/{layout}")
 
 
+@pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("variant", ["decode"])
-def test_fused_hot_expert_and_shared(variant):
+def test_fused_hot_expert_and_shared(variant, layout):
     """Every token routed to the same experts (one long segment) + a shared expert."""
     cfg = synth.MoeConfig("hot", T=70, H=384, I=256, E=8, k=2, shared=True)
     c = gpu_case(cfg, seed=5)
     ids_np = np.tile(np.array([[3, 6]], np.int32), (cfg.T, 1))
     aff_np = synth.random_affinities(cfg.T, 2, seed=5).numpy()
     out = _fused(c, torch.from_numpy(ids_np).cuda(), torch.from_numpy(aff_np).cuda(),
-                 variant=variant)
+                 variant=variant, layout=layout)
     ref = oracle_rows(c, ids_np, aff_np, np.arange(cfg.T))
-    assert_out_close(np_(out), ref, what=f"hot+shared/{variant}")
+    assert_out_close(np_(out), ref, what=f"hot+shared/{variant}/{layout}")
 
 
+@pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("variant", ["decode"])
-def test_fused_zero_affinities(variant):
+def test_fused_zero_affinities(variant, layout):
     cfg = synth.MoeConfig("z", T=9, H=256, I=128, E=8, k=3, shared=True)
     c = gpu_case(cfg, seed=6)
     ids, _ = binding.route(c["logits"], cfg.k)
     zero = torch.zeros((cfg.T, cfg.k), dtype=torch.float32, device="cuda")
-    out = _fused(c, ids, zero, variant=variant, shared=False)
+    out = _fused(c, ids, zero, variant=variant, shared=False, layout=layout)
     assert torch.all(out == 0)
-    out_sh = _fused(c, ids, zero, variant=variant, shared=True)
+    out_sh = _fused(c, ids, zero, variant=variant, shared=True, layout=layout)
     ref = oracle_rows(c, np_(ids), np.zeros((cfg.T, cfg.k)), np.arange(cfg.T))
-    assert_out_close(np_(out_sh), ref, what=f"zero-aff+shared/{variant}")
+    assert_out_close(np_(out_sh), ref, what=f"zero-aff+shared/{variant}/{layout}")
 
 
+@pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("variant", ["decode"])
-def test_fused_single_expert_dense(variant):
+def test_fused_single_expert_dense(variant, layout):
     cfg = synth.MoeConfig("d", T=33, H=512, I=384, E=1, k=1)
     c = gpu_case(cfg, seed=7)
     ids = torch.zeros((cfg.T, 1), dtype=torch.int32, device="cuda")
     aff = torch.ones((cfg.T, 1), dtype=torch.float32, device="cuda")
-    out = _fused(c, ids, aff, variant=variant)
+    out = _fused(c, ids, aff, variant=variant, layout=layout)
     ref = oracle_rows(c, np.zeros((cfg.T, 1), np.int64), np.ones((cfg.T, 1)), np.arange(cfg.T))
-    assert_out_close(np_(out), ref, what=f"E=1/{variant}")
+    assert_out_close(np_(out), ref, what=f"E=1/{variant}/{layout}")
 
 
 def test_fused_bad_ids_are_dropped():
