@@ -110,6 +110,87 @@ def cpu_baseline(case, cfg, max_tokens):
             "seconds": round(secs, 3)}
 
 
+def measure(cfg, L, steps, warmup, variant, layout, seed, dev):
+    """Time `steps` passes of the whole hot path (route + fused sort/FFN/combine),
+    cycling over L weight sets; then the same region again with per-kernel
+    HIP events on the launch stream."""
+    import torch
+
+    from block_scaled_fp8_amd import binding, synth
+    log(f"workload {cfg.name}: T={cfg.T} H={cfg.H} I={cfg.I} E={cfg.E} k={cfg.k} "
+        f"shared={cfg.shared}, {L} weight sets, variant={variant}, layout={layout}")
+    x, logits = synth.make_activations(cfg, seed, dev)
+    wsets = [synth.make_weights(cfg, seed + 100 * i, dev) for i in range(L)]
+    if layout == "tiled":
+        # offline weight preparation, once per weight set (not part of a step)
+        run_sets = []
+        for w in wsets:
+            p = dict(w, w13=binding.pack_w8(w["w13"]), w2=binding.pack_w8(w["w2"]))
+            if w["shared"] is not None:
+                p["shared"] = dict(w["shared"], w13=binding.pack_w8(w["shared"]["w13"]),
+                                   w2=binding.pack_w8(w["shared"]["w2"]))
+            run_sets.append(p)
+    else:
+        run_sets = wsets
+    runs = [binding.MoeStep(x, logits, cfg.k, w["w13"], w["w13_scale"], w["w2"], w["w2_scale"],
+                            shared=w["shared"], variant=variant, layout=layout)
+            for w in run_sets]
+    torch.cuda.synchronize()
+    ids, _ = binding.route(logits, cfg.k)
+    counts = torch.bincount(ids.reshape(-1).long(), minlength=cfg.E)
+    n_active = int((counts > 0).sum().item())
+    log(f"active experts {n_active}, max routes/expert {int(counts.max().item())}")
+    for i in range(warmup):
+        runs[i % L]()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        runs[i % L]()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / steps
+    log(f"timed {steps} steps: {ms_per_step * 1e3:.1f} us/step")
+    binding.profile_enable(True)
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    for i in range(steps):
+        runs[i % L]()
+    torch.cuda.synchronize()
+    t3 = time.perf_counter()
+    binding.profile_enable(False)
+    prof = binding.profile_collect()
+    for n, (c, ms) in sorted(prof.items(), key=lambda kv: -kv[1][0] * kv[1][1]):
+        log(f"  {n:24s} {c:6d} x {ms * 1e3:9.2f} us")
+    return dict(n_active=n_active, ms_per_step=ms_per_step, ms_profiled=(t3 - t2) * 1e3 / steps,
+                prof=prof, x=x, logits=logits, wsets=wsets, L=L, runs=runs)
+
+
+def prefill_summary(cfg, m):
+    """MFMA roofline of the prefill workload (secondary object of the JSON line)."""
+    R = cfg.T * cfg.k + (cfg.T if cfg.shared else 0)
+    flops_gateup = 2.0 * R * 2 * cfg.I * cfg.H
+    flops_down = 2.0 * R * cfg.H * cfg.I
+    tot = flops_gateup + flops_down
+    prof = m["prof"]
+    out = {"workload": cfg.name, "T": cfg.T, "hidden": cfg.H, "moe_inter": cfg.I,
+           "experts": cfg.E, "top_k": cfg.k, "shared_expert": cfg.shared,
+           "active_experts": m["n_active"],
+           "ms_per_step": round(m["ms_per_step"], 5),
+           "tokens_per_s": round(cfg.T / (m["ms_per_step"] * 1e-3), 1),
+           "TFLOP_per_s": round(tot / (m["ms_per_step"] * 1e-3) / 1e12, 1),
+           "mfma_frac_step": round(tot / (m["ms_per_step"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+           "kernels": {n: {"launches": c, "avg_us": round(ms * 1e3, 3)} for n, (c, ms) in prof.items()}}
+    if "prefill_gateup_swiglu" in prof:
+        us = prof["prefill_gateup_swiglu"][1] * 1e3
+        ach = flops_gateup / (us * 1e-6) / 1e12
+        out["roofline"] = {"bound": "mfma", "kernel": "prefill_gateup_swiglu",
+                           "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS,
+                           "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4),
+                           "traffic": None, "flops_per_launch": flops_gateup,
+                           "avg_us": round(us, 3)}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -122,6 +203,9 @@ def main():
                     help="weight layout; tiled = packed once at load time (offline prep)")
     ap.add_argument("--cpu-tokens", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prefill-workload", default="prefill8k_skew",
+                    help="secondary MFMA-bound workload reported in the 'prefill' object ('' = skip)")
+    ap.add_argument("--prefill-steps", type=int, default=20)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB, 5 times (PMC byte-counter "
@@ -153,64 +237,11 @@ def main():
         return
     binding.load_library()
     cfg = synth.CONFIGS[args.workload]
-    L = max(1, args.weight_sets)
-    log(f"workload {cfg.name}: T={cfg.T} H={cfg.H} I={cfg.I} E={cfg.E} k={cfg.k} "
-        f"shared={cfg.shared}, {L} weight sets")
-
-    x, logits = synth.make_activations(cfg, args.seed, dev)
-    wsets = [synth.make_weights(cfg, args.seed + 100 * i, dev) for i in range(L)]
-    if args.layout == "tiled":
-        # offline weight preparation, once per weight set (not part of a step)
-        packed = []
-        for w in wsets:
-            p = dict(w, w13=binding.pack_w8(w["w13"]), w2=binding.pack_w8(w["w2"]))
-            if w["shared"] is not None:
-                p["shared"] = dict(w["shared"], w13=binding.pack_w8(w["shared"]["w13"]),
-                                   w2=binding.pack_w8(w["shared"]["w2"]))
-            packed.append(p)
-        run_sets = packed
-    else:
-        run_sets = wsets
-    steps = [binding.MoeStep(x, logits, cfg.k, w["w13"], w["w13_scale"], w["w2"], w["w2_scale"],
-                             shared=w["shared"], variant=args.variant, layout=args.layout)
-             for w in run_sets]
-    torch.cuda.synchronize()
-
-    # routing facts for the algorithmic byte counts (outside the timed region)
-    ids, _ = binding.route(logits, cfg.k)
-    counts = torch.bincount(ids.reshape(-1).long(), minlength=cfg.E)
-    n_active = int((counts > 0).sum().item())
-    log(f"active experts {n_active}, max routes/expert {int(counts.max().item())}")
-
-    for i in range(args.warmup):
-        steps[i % L]()
-    torch.cuda.synchronize()
-
-    K = args.steps
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(K):
-        steps[i % L]()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / K
-    log(f"timed {K} steps: {ms_per_step * 1e3:.1f} us/step")
-
-    # the same region again with per-kernel HIP events on the launch stream
-    binding.profile_enable(True)
-    torch.cuda.synchronize()
-    t2 = time.perf_counter()
-    for i in range(K):
-        steps[i % L]()
-    torch.cuda.synchronize()
-    t3 = time.perf_counter()
-    binding.profile_enable(False)
-    prof = binding.profile_collect()
-    ms_profiled = (t3 - t2) * 1e3 / K
+    m = measure(cfg, max(1, args.weight_sets), args.steps, args.warmup, args.variant, args.layout,
+                args.seed, dev)
+    n_active, ms_per_step, ms_profiled, prof = m["n_active"], m["ms_per_step"], m["ms_profiled"], m["prof"]
+    x, logits, wsets, L = m["x"], m["logits"], m["wsets"], m["L"]
     kernels = {n: {"launches": c, "avg_us": round(ms * 1e3, 3)} for n, (c, ms) in prof.items()}
-    for n, v in sorted(kernels.items(), key=lambda kv: -kv[1]["launches"] * kv[1]["avg_us"]):
-        log(f"  {n:24s} {v['launches']:6d} x {v['avg_us']:9.2f} us")
-
     dom = max(prof.items(), key=lambda kv: kv[1][0] * kv[1][1])[0]
     dom_bytes = kernel_bytes(dom, cfg, n_active, cfg.shared)
     dom_ms = prof[dom][1]
@@ -230,7 +261,7 @@ def main():
         "value": round(tokens_per_s, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": K,
+        "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
@@ -250,6 +281,14 @@ def main():
                  "ms_per_step_profiled": round(ms_profiled, 5)},
         "kernels": kernels,
     }
+    if args.prefill_workload:
+        pcfg = synth.CONFIGS[args.prefill_workload]
+        del m
+        torch.cuda.empty_cache()
+        pm = measure(pcfg, 2, args.prefill_steps, 3, "auto", args.layout, args.seed, dev)
+        result["prefill"] = prefill_summary(pcfg, pm)
+        del pm
+        torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         case = dict(x=x, logits=logits, **wsets[0])

@@ -190,7 +190,8 @@ int moe_fused_w8a16(const void* x, const uint8_t* w13, const float* w13_scale,
         return MOE_EINVAL;
     }
     if (variant == MOE_VARIANT_AUTO)
-        variant = MOE_VARIANT_DECODE;
+        variant = ((long long)T * k <= 32LL * E || !prefill_supported(H, I)) ? MOE_VARIANT_DECODE
+                                                                             : MOE_VARIANT_PREFILL;
 
     char* base = static_cast<char*>(ws);
     Plan p;
@@ -216,13 +217,13 @@ int moe_fused_w8a16(const void* x, const uint8_t* w13, const float* w13_scale,
     const uint16_t* xb = static_cast<const uint16_t*>(x);
     int rc;
     if (variant == MOE_VARIANT_DECODE)
-        rc = launch_decode_ffn(weight_layout, xb, w13, w13_scale, w2, w2_scale, sh, p, T, H, I, E,
-                               k, abuf, ybuf, s);
+        rc = launch_decode_ffn(weight_layout, xb, w13, w13_scale, w2, w2_scale, sh, p, aff, T, H, I,
+                               E, k, abuf, ybuf, s);
     else
-        rc = launch_prefill_ffn(weight_layout, xb, w13, w13_scale, w2, w2_scale, sh, p, T, H, I,
-                                E, k, abuf, ybuf, s);
+        rc = launch_prefill_ffn(weight_layout, xb, w13, w13_scale, w2, w2_scale, sh, p, aff, T, H,
+                                I, E, k, abuf, ybuf, s);
     if (rc) return rc;
-    return launch_combine(ybuf, p.inv_route, aff, T, H, k, has_shared, out, s);
+    return launch_combine(ybuf, p.inv_route, T, H, k, has_shared, out, s);
 }
 
 int moe_pack_w8(const uint8_t* src, uint8_t* dst, int64_t n_mats, int rows, int cols,

@@ -40,8 +40,8 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_ffn_kernel(
     const float* __restrict__ w13s, const uint8_t* __restrict__ w2,
     const float* __restrict__ w2s, const uint8_t* __restrict__ sh_w13,
     const float* __restrict__ sh_w13s, const uint8_t* __restrict__ sh_w2,
-    const float* __restrict__ sh_w2s, Plan plan, int T, int H, int I, int k,
-    uint16_t* __restrict__ abuf, float* __restrict__ ybuf) {
+    const float* __restrict__ sh_w2s, Plan plan, const float* __restrict__ aff, int T, int H,
+    int I, int k, uint16_t* __restrict__ abuf, float* __restrict__ ybuf) {
     constexpr int MROWS = 16 * MT;
     const int K = MODE == MODE_GATEUP ? H : I;
     const int ntile_per_seg = MODE == MODE_GATEUP ? I / 32 : H / 64;
@@ -219,33 +219,34 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_ffn_kernel(
 #pragma unroll
                     for (int v = 0; v < DEC_WAVES; ++v) y += red[v][mt][j][i][lane];
                     const int m = mp + mt * 16 + lg * 4 + i;
-                    if (m < rows) ybuf[(size_t)(row0 + m) * H + brow[j] + ln] = y;
+                    if (m < rows) {
+                        const int p = row0 + m;
+                        const int r = e >= 0 ? plan.sorted_route[p] : p;
+                        const float a = e >= 0 ? aff[r] : 1.0f;
+                        ybuf[(size_t)r * H + brow[j] + ln] = y * a;
+                    }
                 }
             }
         }
     }
 }
 
-// out[t] = sum_j aff[t,j] * y[inv_route[t*k+j]]  (+ y[R + t] for the shared
-// expert), in slot order, fp32.  Source: AITER PR page (FP32 route
-// reduction); NKI page (affinity scale -> expert-sum, shared expert added
-// after the routed sum).
+// out[t] = sum_j y[t*k + j] over the valid routes (inv_route >= 0), in slot
+// order, + y[R + t] for the shared expert; fp32.  The producers have already
+// multiplied each row by its affinity.  Source: AITER PR page (FP32 route
+// reduction); NKI page (affinity scale -> expert-sum, shared expert added after
+// the routed sum).
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ ybuf,
                                                       const int32_t* __restrict__ inv_route,
-                                                      const float* __restrict__ aff, int T, int H,
-                                                      int k, int has_shared,
+                                                      int T, int H, int k, int has_shared,
                                                       float* __restrict__ out) {
     const int t = blockIdx.y;
     const int h = (blockIdx.x * 256 + threadIdx.x) * 4;
     if (h >= H) return;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int j = 0; j < k; ++j) {
-        const int p = inv_route[(size_t)t * k + j];
-        if (p >= 0) {
-            const float a = aff[(size_t)t * k + j];
-            const f32x4 y = *reinterpret_cast<const f32x4*>(ybuf + (size_t)p * H + h);
-            acc += a * y;
-        }
+        const size_t r = (size_t)t * k + j;
+        if (inv_route[r] >= 0) acc += *reinterpret_cast<const f32x4*>(ybuf + r * H + h);
     }
     if (has_shared) {
         const size_t R = (size_t)T * k;
@@ -257,19 +258,20 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 template <int MODE, int LAYOUT>
 static int launch_decode_mode_l(int MT, int nseg_max, const uint16_t* x, const uint8_t* w13,
                                 const float* w13s, const uint8_t* w2, const float* w2s,
-                                const SharedW& sh, const Plan& plan, int T, int H, int I, int k,
-                                uint16_t* abuf, float* ybuf, hipStream_t stream) {
+                                const SharedW& sh, const Plan& plan, const float* aff, int T,
+                                int H, int I, int k, uint16_t* abuf, float* ybuf,
+                                hipStream_t stream) {
     const int ntile = MODE == MODE_GATEUP ? I / 32 : H / 64;
     const dim3 grid((unsigned)nseg_max * ntile), block(DEC_THREADS);
     prof_begin(MODE == MODE_GATEUP ? "decode_gateup_swiglu" : "decode_down", stream);
     if (MT == 1)
         decode_ffn_kernel<MODE, 1, LAYOUT><<<grid, block, 0, stream>>>(
-            x, w13, w13s, w2, w2s, sh.w13, sh.w13_scale, sh.w2, sh.w2_scale, plan, T, H, I, k, abuf,
-            ybuf);
+            x, w13, w13s, w2, w2s, sh.w13, sh.w13_scale, sh.w2, sh.w2_scale, plan, aff, T, H, I, k,
+            abuf, ybuf);
     else
         decode_ffn_kernel<MODE, 2, LAYOUT><<<grid, block, 0, stream>>>(
-            x, w13, w13s, w2, w2s, sh.w13, sh.w13_scale, sh.w2, sh.w2_scale, plan, T, H, I, k, abuf,
-            ybuf);
+            x, w13, w13s, w2, w2s, sh.w13, sh.w13_scale, sh.w2, sh.w2_scale, plan, aff, T, H, I, k,
+            abuf, ybuf);
     prof_end(stream);
     return check_launch(MODE == MODE_GATEUP ? "decode_ffn_kernel<gateup>" : "decode_ffn_kernel<down>");
 }
@@ -277,19 +279,20 @@ static int launch_decode_mode_l(int MT, int nseg_max, const uint16_t* x, const u
 template <int MODE>
 static int launch_decode_mode(int layout, int MT, int nseg_max, const uint16_t* x,
                               const uint8_t* w13, const float* w13s, const uint8_t* w2,
-                              const float* w2s, const SharedW& sh, const Plan& plan, int T, int H,
-                              int I, int k, uint16_t* abuf, float* ybuf, hipStream_t stream) {
+                              const float* w2s, const SharedW& sh, const Plan& plan,
+                              const float* aff, int T, int H, int I, int k, uint16_t* abuf,
+                              float* ybuf, hipStream_t stream) {
     if (layout == LAYOUT_TILED)
         return launch_decode_mode_l<MODE, LAYOUT_TILED>(MT, nseg_max, x, w13, w13s, w2, w2s, sh,
-                                                        plan, T, H, I, k, abuf, ybuf, stream);
+                                                        plan, aff, T, H, I, k, abuf, ybuf, stream);
     return launch_decode_mode_l<MODE, LAYOUT_ROWMAJOR>(MT, nseg_max, x, w13, w13s, w2, w2s, sh,
-                                                       plan, T, H, I, k, abuf, ybuf, stream);
+                                                       plan, aff, T, H, I, k, abuf, ybuf, stream);
 }
 
 int launch_decode_fused(int layout, int MT, const uint16_t* x, const uint8_t* w13,
                         const float* w13s, const uint8_t* w2, const float* w2s, const SharedW& sh,
-                        const Plan& plan, int T, int H, int I, int E, int k, float* ybuf,
-                        hipStream_t stream);
+                        const Plan& plan, const float* aff, int T, int H, int I, int E, int k,
+                        float* ybuf, hipStream_t stream);
 
 // At most min(E, T*k) routed experts are active.  When that fills most of the
 // chip, one workgroup per active expert (ffn_decode_fused.hip) streams every
@@ -298,27 +301,27 @@ int launch_decode_fused(int layout, int MT, const uint16_t* x, const uint8_t* w1
 // so that all CUs still stream.
 int launch_decode_ffn(int layout, const uint16_t* x, const uint8_t* w13, const float* w13s,
                       const uint8_t* w2, const float* w2s, const SharedW& sh, const Plan& plan,
-                      int T, int H, int I, int E, int k, uint16_t* abuf, float* ybuf,
-                      hipStream_t stream) {
+                      const float* aff, int T, int H, int I, int E, int k, uint16_t* abuf,
+                      float* ybuf, hipStream_t stream) {
     const int has_shared = sh.w13 != nullptr;
     const int nseg_max = E + has_shared;
     const int MT = ((long)T * k <= 4L * E) ? 1 : 2;
     const long max_active = std::min<long>(E, (long)T * k) + has_shared;
     if (max_active >= 128)
-        return launch_decode_fused(layout, MT, x, w13, w13s, w2, w2s, sh, plan, T, H, I, E, k,
-                                   ybuf, stream);
-    if (int rc = launch_decode_mode<MODE_GATEUP>(layout, MT, nseg_max, x, w13, w13s, w2, w2s, sh, plan, T,
-                                                 H, I, k, abuf, ybuf, stream))
+        return launch_decode_fused(layout, MT, x, w13, w13s, w2, w2s, sh, plan, aff, T, H, I, E,
+                                   k, ybuf, stream);
+    if (int rc = launch_decode_mode<MODE_GATEUP>(layout, MT, nseg_max, x, w13, w13s, w2, w2s, sh,
+                                                 plan, aff, T, H, I, k, abuf, ybuf, stream))
         return rc;
-    return launch_decode_mode<MODE_DOWN>(layout, MT, nseg_max, x, w13, w13s, w2, w2s, sh, plan, T, H, I,
-                                         k, abuf, ybuf, stream);
+    return launch_decode_mode<MODE_DOWN>(layout, MT, nseg_max, x, w13, w13s, w2, w2s, sh, plan,
+                                         aff, T, H, I, k, abuf, ybuf, stream);
 }
 
-int launch_combine(const float* ybuf, const int32_t* inv_route, const float* aff, int T, int H,
-                   int k, int has_shared, float* out, hipStream_t stream) {
+int launch_combine(const float* ybuf, const int32_t* inv_route, int T, int H, int k,
+                   int has_shared, float* out, hipStream_t stream) {
     const dim3 grid((H / 4 + 255) / 256, T), block(256);
     prof_begin("combine", stream);
-    combine_kernel<<<grid, block, 0, stream>>>(ybuf, inv_route, aff, T, H, k, has_shared, out);
+    combine_kernel<<<grid, block, 0, stream>>>(ybuf, inv_route, T, H, k, has_shared, out);
     prof_end(stream);
     return check_launch("combine_kernel");
 }

@@ -56,8 +56,8 @@ __global__ __launch_bounds__(DF_THREADS) void decode_fused_kernel(
     const float* __restrict__ w13s, const uint8_t* __restrict__ w2,
     const float* __restrict__ w2s, const uint8_t* __restrict__ sh_w13,
     const float* __restrict__ sh_w13s, const uint8_t* __restrict__ sh_w2,
-    const float* __restrict__ sh_w2s, Plan plan, int T, int H, int I, int k,
-    float* __restrict__ ybuf, float* __restrict__ ytrash) {
+    const float* __restrict__ sh_w2s, Plan plan, const float* __restrict__ aff, int T, int H,
+    int I, int k, float* __restrict__ ybuf, float* __restrict__ ytrash) {
     static_assert(DEPTH == 1 || DEPTH == 2, "chunks per 128-wide scale block");
     constexpr int MROWS = 16 * MT, NT = DF_NT, HALF = DF_HALF;
     constexpr int CS = chunk_stride<LAYOUT>();
@@ -92,6 +92,7 @@ __global__ __launch_bounds__(DF_THREADS) void decode_fused_kernel(
         bool xvalid[MT];
         const uint16_t* ap[MT];
         float* yrow[MT][4];  // y destination of this lane's output rows (trash row if padded)
+        float yaff[MT][4];   // affinity of each of those routes
         u32x4 bq[DEPTH][NT];
         u32x4 aq[DEPTH][MT][2];
         f32x4 acc[MT][NT];
@@ -224,8 +225,9 @@ __global__ __launch_bounds__(DF_THREADS) void decode_fused_kernel(
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         float* dst = real ? yrow[mt][i] + g * NT * 16 + ln : ytrash + ln;
+                        const float sc = seff0 * yaff[mt][i];
 #pragma unroll
-                        for (int j = 0; j < NT; ++j) dst[j * 16] = acc[mt][j][i] * seff0;
+                        for (int j = 0; j < NT; ++j) dst[j * 16] = acc[mt][j][i] * sc;
                     }
                 reset();
                 pc = 0;
@@ -252,7 +254,14 @@ __global__ __launch_bounds__(DF_THREADS) void decode_fused_kernel(
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int mi = mp + mt * 16 + lg * 4 + i;
-                yrow[mt][i] = mi < rows ? ybuf + (size_t)(row0 + mi) * H : ytrash;
+                int r = -1;
+                float a = 0.0f;
+                if (mi < rows) {
+                    r = e >= 0 ? plan.sorted_route[row0 + mi] : row0 + mi;
+                    a = e >= 0 ? aff[r] : 1.0f;
+                }
+                yrow[mt][i] = r >= 0 ? ybuf + (size_t)r * H : ytrash;
+                yaff[mt][i] = a;
             }
         }
 #pragma unroll
@@ -290,8 +299,8 @@ __global__ __launch_bounds__(DF_THREADS) void decode_fused_kernel(
 template <int LAYOUT>
 static int launch_decode_fused_l(int MT, const uint16_t* x, const uint8_t* w13, const float* w13s,
                                  const uint8_t* w2, const float* w2s, const SharedW& sh,
-                                 const Plan& plan, int T, int H, int I, int E, int k, float* ybuf,
-                                 hipStream_t stream) {
+                                 const Plan& plan, const float* aff, int T, int H, int I, int E,
+                                 int k, float* ybuf, hipStream_t stream) {
     const int nseg_max = E + (sh.w13 ? 1 : 0);
     const size_t lds = sizeof(uint16_t) * (size_t)(16 * MT) * (I + 8);
     // the trash row sits right after the last real row of y
@@ -299,12 +308,12 @@ static int launch_decode_fused_l(int MT, const uint16_t* x, const uint8_t* w13, 
     prof_begin("decode_fused_expert", stream);
     if (MT == 1)
         decode_fused_kernel<1, 2, LAYOUT><<<nseg_max, DF_THREADS, lds, stream>>>(
-            x, w13, w13s, w2, w2s, sh.w13, sh.w13_scale, sh.w2, sh.w2_scale, plan, T, H, I, k, ybuf,
-            ytrash);
+            x, w13, w13s, w2, w2s, sh.w13, sh.w13_scale, sh.w2, sh.w2_scale, plan, aff, T, H, I, k,
+            ybuf, ytrash);
     else
         decode_fused_kernel<2, 2, LAYOUT><<<nseg_max, DF_THREADS, lds, stream>>>(
-            x, w13, w13s, w2, w2s, sh.w13, sh.w13_scale, sh.w2, sh.w2_scale, plan, T, H, I, k, ybuf,
-            ytrash);
+            x, w13, w13s, w2, w2s, sh.w13, sh.w13_scale, sh.w2, sh.w2_scale, plan, aff, T, H, I, k,
+            ybuf, ytrash);
     prof_end(stream);
     return check_launch("decode_fused_kernel");
 }
@@ -313,13 +322,13 @@ static int launch_decode_fused_l(int MT, const uint16_t* x, const uint8_t* w13, 
 // number of active segments exit at once.
 int launch_decode_fused(int layout, int MT, const uint16_t* x, const uint8_t* w13,
                         const float* w13s, const uint8_t* w2, const float* w2s, const SharedW& sh,
-                        const Plan& plan, int T, int H, int I, int E, int k, float* ybuf,
-                        hipStream_t stream) {
+                        const Plan& plan, const float* aff, int T, int H, int I, int E, int k,
+                        float* ybuf, hipStream_t stream) {
     if (layout == LAYOUT_TILED)
-        return launch_decode_fused_l<LAYOUT_TILED>(MT, x, w13, w13s, w2, w2s, sh, plan, T, H, I,
-                                                   E, k, ybuf, stream);
-    return launch_decode_fused_l<LAYOUT_ROWMAJOR>(MT, x, w13, w13s, w2, w2s, sh, plan, T, H, I, E,
-                                                  k, ybuf, stream);
+        return launch_decode_fused_l<LAYOUT_TILED>(MT, x, w13, w13s, w2, w2s, sh, plan, aff, T, H,
+                                                   I, E, k, ybuf, stream);
+    return launch_decode_fused_l<LAYOUT_ROWMAJOR>(MT, x, w13, w13s, w2, w2s, sh, plan, aff, T, H,
+                                                  I, E, k, ybuf, stream);
 }
 
 }  // namespace moe

@@ -1,16 +1,368 @@
-// Prefill variant of the expert FFN (grouped bf16-MFMA GEMM); not built yet.
+// Prefill variant of the expert FFN: grouped bf16-MFMA GEMMs over 128-row
+// tiles of the expert-sorted routes.
+//
+// Sources: "Add gfx950 Q256 fused MXFP4 prefill pipeline" (ROCm/aiter
+// PR #5988): a prefill producer over expert-sorted tokens does the gate/up
+// projection, SiLU and down projection, then an FP32 route reduction sums the
+// routed contributions (one always-on shared expert included);
+// "spark_model/layers/nemotron_moe.rs": the sorted prefill path runs one
+// grouped GEMM per projection over tokens sorted by expert and unpermutes with
+// a reduction.  The weights stay block-scaled E4M3FN ("Gated DeltaNet (+ FP8
+// MoE) -- AWS Neuron (NKI) kernels for Trainium2", FP8 MoE decode kernel
+// section) and are decoded to bf16 on chip.
+//
+// gfx950 design.  Kernel 1 (gate/up): each workgroup computes a 128-row x
+// (256 gate + 256 up) tile of one segment, applies SwiGLU in registers and
+// writes bf16 activations (abuf, sorted row order).  Kernel 2 (down): each
+// workgroup computes a 128-row x 512-column tile of y = a W2^T, multiplies it
+// by the route's affinity and writes fp32 rows at the route's own index
+// r = t*k + j, so the final combine streams k contiguous rows per token.
+//
+//  * Workgroup tile 128 rows x 512 columns (gate/up: 256 gate + the matching
+//    256 up columns), 8 waves (2 x 4), each a 64 x 128 tile of
+//    v_mfma_f32_32x32x16_bf16 (2 x 4 MFMA tiles, 128 fp32 accumulators).
+//  * Operands are staged through LDS with 16-byte direct-to-LDS loads
+//    (global_load_lds_dwordx4: a wave instruction fills one contiguous 1 KB),
+//    three stages of 64-wide K (144 KB), one barrier per K step; loads run
+//    two steps ahead of the MFMAs.
+//  * Activation tiles: 8 rows x 128 bytes per wave instruction, the 16-byte
+//    pieces of each row XOR-swizzled by (row % 8) to spread LDS banks.
+//    Weight tiles: one 16-row x 64-byte chunk per instruction, stored in lane
+//    order (the tile-coalesced layout is this chunk order in memory).
+//  * FP8 is converted exactly to bf16 after the LDS read; the fp32 block scale
+//    of each 128-wide K block is applied by rescaling the accumulators when the
+//    block starts (running scale), never by rounding it into bf16.
+//  * Work list: the sort builds per-segment tile prefixes; the grid covers the
+//    worst case and idle workgroups exit.  Workgroup ids are remapped so that
+//    consecutive tiles (same expert, neighbouring rows) land on the same XCD
+//    and share its L2.
 #include "common.hpp"
 #include "plan.hpp"
 
 namespace moe {
 
-int prefill_tile_m() { return 128; }
+constexpr int PF_BK = 64;  // K per stage
 
-int launch_prefill_ffn(int, const uint16_t*, const uint8_t*, const float*, const uint8_t*,
-                       const float*, const SharedW&, const Plan&, int, int, int, int, int,
-                       uint16_t*, float*, hipStream_t) {
-    set_error("moe_fused_w8a16: the prefill variant is not available in this build");
-    return MOE_EUNSUPPORTED;
+// Workgroup tile BM rows x BN columns, WM x WN waves of 64 x 128 each (2 x 4
+// MFMA tiles of 32 x 32), STAGES LDS stages of 64-wide K.
+template <int BM_, int BN_, int WM_, int WN_, int STAGES_>
+struct PfCfg {
+    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+    static constexpr int THREADS = WM * WN * MOE_WAVE;
+    static constexpr int WAVES = WM * WN;
+    static constexpr int STAGES = STAGES_;
+    static constexpr int A_BYTES = BM * PF_BK * 2;  // bf16
+    static constexpr int B_BYTES = BN * PF_BK;      // fp8
+    static constexpr int STAGE = A_BYTES + B_BYTES;
+    static constexpr int A_INSTR = A_BYTES / 1024 / WAVES;  // 1 KB loads per wave per stage
+    static constexpr int B_INSTR = B_BYTES / 1024 / WAVES;
+    static constexpr int MT = BM / WM / 32;
+    static constexpr int NT = BN / WN / 32;
+    static_assert(BM / WM == 64 && BN / WN == 128, "wave tile is 64 x 128");
+    static_assert(BM == 128, "tile prefixes are built for 128-row tiles");
+    static_assert(A_INSTR >= 1 && B_INSTR >= 1, "every wave issues loads");
+};
+using PfWide = PfCfg<128, 512, 2, 4, 3>;    // 8 waves, 144 KB LDS
+using PfNarrow = PfCfg<128, 256, 2, 2, 3>;  // 4 waves, 96 KB LDS (smaller widths)
+constexpr int PF_BM = 128;
+
+int prefill_tile_m() { return PF_BM; }
+
+// Widths the grouped GEMMs tile exactly (K % 128 holds for every valid call).
+int prefill_supported(int H, int I) { return H % 256 == 0 && (2 * I) % 256 == 0; }
+
+enum { PF_GATEUP = 0, PF_DOWN = 1 };
+
+__device__ __forceinline__ void lds_load16(const void* g, uint32_t lds_byte_addr_uniform, void* lds_base) {
+    __builtin_amdgcn_global_load_lds(g, reinterpret_cast<char*>(lds_base) + lds_byte_addr_uniform, 16,
+                                     0, 0);
+}
+
+// s_waitcnt vmcnt(n) (n < 16), leaving the other counters unconstrained.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 16, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+
+template <int MODE, int LAYOUT, class C>
+__global__ __launch_bounds__(C::THREADS, 1) void prefill_gemm_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ abuf_in,
+    const uint8_t* __restrict__ wexp, const float* __restrict__ sexp,
+    const uint8_t* __restrict__ wsh, const float* __restrict__ ssh, Plan plan,
+    const float* __restrict__ aff, int T, int H, int I, int k, int nblk, int xcd_chunk,
+    uint16_t* __restrict__ abuf_out, float* __restrict__ ybuf) {
+    constexpr int BM = C::BM, BN = C::BN;
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    __shared__ int row_tok[BM];     // activation row source (token or abuf row)
+    __shared__ int row_dst[BM];     // output row (abuf row / route index), -1 if padding
+    __shared__ float row_aff[BM];
+
+    // ---- which tile: XCD-aware remap of the workgroup id, then segment search
+    const int bid = blockIdx.x;
+    const int lin = xcd_chunk > 0 ? (bid & 7) * xcd_chunk + (bid >> 3) : bid;
+    const int tile = lin / nblk, nb = lin - tile * nblk;
+    const int nseg = plan.seg_n[0];
+    if (tile >= plan.seg_tile0[nseg]) return;
+    int lo = 0, hi = nseg - 1;  // last segment with seg_tile0 <= tile
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (plan.seg_tile0[mid] <= tile) lo = mid; else hi = mid - 1;
+    }
+    const int seg = lo;
+    const int e = plan.seg_expert[seg];
+    const int srow0 = plan.seg_row0[seg];
+    const int srows = plan.seg_rows[seg];
+    const int m0 = (tile - plan.seg_tile0[seg]) * BM;  // first row inside the segment
+
+    const int K = MODE == PF_GATEUP ? H : I;
+    const int Nrows = MODE == PF_GATEUP ? 2 * I : H;     // rows of the weight matrix
+    const uint8_t* W = e >= 0 ? wexp + (size_t)e * Nrows * K : wsh;
+    const float* S = e >= 0 ? sexp + (size_t)e * (Nrows / 128) * (K / 128) : ssh;
+    const int R = T * k;
+
+    const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
+    if (tid < BM) {
+        const int m = m0 + tid;
+        int src = 0, dst = -1;
+        float a = 0.0f;
+        if (m < srows) {
+            const int p = srow0 + m;
+            if (MODE == PF_GATEUP) {
+                src = e >= 0 ? plan.sorted_route[p] / k : p - R;
+                dst = p;
+            } else {
+                src = p;
+                const int r = e >= 0 ? plan.sorted_route[p] : p;
+                dst = r;
+                a = e >= 0 ? aff[r] : 1.0f;
+            }
+        }
+        row_tok[tid] = src;
+        row_dst[tid] = dst;
+        row_aff[tid] = a;
+    }
+    __syncthreads();
+
+    // ---- per-lane global sources of the staged tiles
+    // activations: instruction q of wave w fills rows (w*A_INSTR + q)*8 .. +8, 128 B each
+    const int ar_sub = lane >> 3, apiece = lane & 7;
+    const uint16_t* asrc[C::A_INSTR];
+#pragma unroll
+    for (int q = 0; q < C::A_INSTR; ++q) {
+        const int row = (wave * C::A_INSTR + q) * 8 + ar_sub;
+        const int sw = apiece ^ (row & 7);  // swizzled piece this lane fetches
+        const uint16_t* base = MODE == PF_GATEUP ? x + (size_t)row_tok[row] * H
+                                                 : abuf_in + (size_t)row_tok[row] * I;
+        asrc[q] = base + sw * 8;
+    }
+    // weights: instruction q of wave w fills 16-row tile w*B_INSTR + q
+    constexpr int HALF_T = BN / 2 / 16;  // gate tiles in a gate/up tile (MODE 0)
+    const uint8_t* bsrc[C::B_INSTR];
+#pragma unroll
+    for (int q = 0; q < C::B_INSTR; ++q) {
+        const int t16 = wave * C::B_INSTR + q;
+        int wrow;
+        if (MODE == PF_GATEUP)
+            wrow = (t16 < HALF_T ? 0 : I) + nb * (BN / 2) + (t16 % HALF_T) * 16;
+        else
+            wrow = nb * BN + t16 * 16;
+        bsrc[q] = tile_lane_ptr<LAYOUT>(W, wrow, K, lane);
+    }
+    constexpr int CS = chunk_stride<LAYOUT>();
+
+    auto issue_stage = [&](int st, int kc) {
+        const uint32_t sbase = st * C::STAGE;
+#pragma unroll
+        for (int q = 0; q < C::A_INSTR; ++q)
+            lds_load16(asrc[q] + kc * PF_BK, sbase + (wave * C::A_INSTR + q) * 1024, smem);
+#pragma unroll
+        for (int q = 0; q < C::B_INSTR; ++q)
+            lds_load16(bsrc[q] + (size_t)kc * CS, sbase + C::A_BYTES + (wave * C::B_INSTR + q) * 1024,
+                       smem);
+    };
+
+    // ---- wave tile: rows wm*64 .. +64, columns wn*128 .. +128 of the WG tile
+    const int wm = wave / C::WN;
+    const int wn = wave % C::WN;
+    const int ln = lane & 31, lg = lane >> 5;
+    // LDS byte offsets of this lane's operand pieces inside a stage
+    uint32_t a_off[C::MT][4];
+#pragma unroll
+    for (int mt = 0; mt < C::MT; ++mt) {
+        const int row = wm * 64 + mt * 32 + ln;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) a_off[mt][s] = row * 128 + (((4 * lg + s) ^ (row & 7)) * 16);
+    }
+    // weight LDS tiles of each 32-column MFMA tile (MODE 0: nt 0,1 gate, 2,3 the matching up)
+    uint32_t b_off[C::NT][2];
+#pragma unroll
+    for (int nt = 0; nt < C::NT; ++nt) {
+        int t16;
+        if (MODE == PF_GATEUP)
+            t16 = (nt < 2 ? 0 : HALF_T) + wn * 4 + (nt & 1) * 2;
+        else
+            t16 = wn * 8 + nt * 2;
+        const int tt = t16 + (ln >> 4), r = ln & 15;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) b_off[nt][h] = C::A_BYTES + tt * 1024 + ((2 * lg + h) * 16 + r) * 16;
+    }
+    // scale rows of this wave's columns (each group lies in one 128-row scale block)
+    int srow[2];
+    if (MODE == PF_GATEUP) {
+        srow[0] = __builtin_amdgcn_readfirstlane((nb * (BN / 2) + wn * 64) >> 7);
+        srow[1] = __builtin_amdgcn_readfirstlane((I + nb * (BN / 2) + wn * 64) >> 7);
+    } else {
+        srow[0] = srow[1] = __builtin_amdgcn_readfirstlane((nb * BN + wn * 128) >> 7);
+    }
+    const int kblocks = K >> 7;
+
+    f32x16 acc[C::MT][C::NT];
+#pragma unroll
+    for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < C::NT; ++nt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[mt][nt][i] = 0.0f;
+    float seff[2] = {0.0f, 0.0f};
+
+    const int nk = K / PF_BK;  // >= 2 since K % 128 == 0
+#pragma unroll
+    for (int st = 0; st < C::STAGES - 1; ++st)
+        if (st < nk) issue_stage(st, st);
+    constexpr int PER_STAGE = C::A_INSTR + C::B_INSTR;
+    for (int kc = 0; kc < nk; ++kc) {
+        // stage kc is complete once at most the younger stages' loads are pending
+        if (kc + C::STAGES - 2 < nk) wait_vmcnt<(C::STAGES - 2) * PER_STAGE>();
+        else wait_vmcnt<0>();
+        __syncthreads();  // every wave: stage kc landed, stage kc-1 fully consumed
+        if (kc + C::STAGES - 1 < nk) issue_stage((kc + C::STAGES - 1) % C::STAGES, kc + C::STAGES - 1);
+        if ((kc & 1) == 0) {  // new 128-wide K block: rescale to its scales
+            const int kb = kc >> 1;
+#pragma unroll
+            for (int g = 0; g < 2; ++g) {
+                if (MODE == PF_DOWN && g == 1) break;
+                const float sn = S[srow[g] * kblocks + kb];
+                if (sn != 0.0f) {
+                    if (seff[g] != 0.0f) {
+                        const float rr = seff[g] * __builtin_amdgcn_rcpf(sn);
+#pragma unroll
+                        for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+                            for (int nt = 0; nt < C::NT; ++nt)
+                                if (MODE == PF_DOWN || (nt >> 1) == g)
+#pragma unroll
+                                    for (int i = 0; i < 16; ++i) acc[mt][nt][i] *= rr;
+                    }
+                    seff[g] = sn;
+                }
+            }
+            if (MODE == PF_DOWN) seff[1] = seff[0];
+        }
+        const char* st = smem + (kc % C::STAGES) * C::STAGE;
+        u32x4 bw[C::NT][2];
+#pragma unroll
+        for (int nt = 0; nt < C::NT; ++nt)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) bw[nt][h] = *reinterpret_cast<const u32x4*>(st + b_off[nt][h]);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            bf16x8 af[C::MT];
+#pragma unroll
+            for (int mt = 0; mt < C::MT; ++mt)
+                af[mt] = as_bf16x8(*reinterpret_cast<const u32x4*>(st + a_off[mt][s]));
+#pragma unroll
+            for (int nt = 0; nt < C::NT; ++nt) {
+                const u32x4& v = bw[nt][s >> 1];
+                const bf16x8 bf = (s & 1) == 0 ? fp8x8_to_bf16x8(v[0], v[1]) : fp8x8_to_bf16x8(v[2], v[3]);
+#pragma unroll
+                for (int mt = 0; mt < C::MT; ++mt)
+                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mt], bf, acc[mt][nt], 0, 0, 0);
+            }
+        }
+    }
+
+    // ---- epilogue. 32x32 accumulator layout: lane l holds column l%32 and,
+    //      for register i, row 8*(i/4) + 4*(l/32) + i%4.
+#pragma unroll
+    for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int row = wm * 64 + mt * 32 + 8 * (i >> 2) + 4 * lg + (i & 3);
+            const int dst = row_dst[row];
+            if (dst < 0) continue;
+            if (MODE == PF_GATEUP) {
+                uint16_t* orow = abuf_out + (size_t)dst * I + nb * (BN / 2) + wn * 64 + ln;
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt)
+                    orow[nt * 32] = f32_to_bf16_bits(
+                        swiglu(acc[mt][nt][i] * seff[0], acc[mt][nt + 2][i] * seff[1]));
+            } else {
+                const float a = row_aff[row];
+                float* orow = ybuf + (size_t)dst * H + nb * BN + wn * 128 + ln;
+#pragma unroll
+                for (int nt = 0; nt < C::NT; ++nt) orow[nt * 32] = acc[mt][nt][i] * seff[0] * a;
+            }
+        }
+}
+
+template <int MODE, int LAYOUT, class C>
+static int launch_pf(const uint16_t* x, const uint16_t* abuf_in, const uint8_t* wexp,
+                     const float* sexp, const uint8_t* wsh, const float* ssh, const Plan& plan,
+                     const float* aff, int T, int H, int I, int E, int k, int has_shared,
+                     uint16_t* abuf_out, float* ybuf, hipStream_t stream) {
+    const int nblk = MODE == PF_GATEUP ? 2 * I / C::BN : H / C::BN;
+    const long R = (long)T * k;
+    const long max_tiles = (R + C::BM - 1) / C::BM + E + (has_shared ? (T + C::BM - 1) / C::BM : 0);
+    long grid = max_tiles * nblk;
+    int xcd_chunk = 0;
+    if (grid % 8 != 0) grid += 8 - grid % 8;  // whole XCD rounds
+    xcd_chunk = (int)(grid / 8);
+    if (grid > 0x7FFFFFFFL) {
+        set_error("prefill: too many tiles");
+        return MOE_EUNSUPPORTED;
+    }
+    const size_t lds = (size_t)C::STAGES * C::STAGE;
+    prof_begin(MODE == PF_GATEUP ? "prefill_gateup_swiglu" : "prefill_down", stream);
+    prefill_gemm_kernel<MODE, LAYOUT, C><<<(unsigned)grid, C::THREADS, lds, stream>>>(
+        x, abuf_in, wexp, sexp, wsh, ssh, plan, aff, T, H, I, k, nblk, xcd_chunk, abuf_out, ybuf);
+    prof_end(stream);
+    return check_launch(MODE == PF_GATEUP ? "prefill_gemm_kernel<gateup>" : "prefill_gemm_kernel<down>");
+}
+
+template <int LAYOUT, class C>
+static int launch_prefill_c(const uint16_t* x, const uint8_t* w13, const float* w13s,
+                            const uint8_t* w2, const float* w2s, const SharedW& sh,
+                            const Plan& plan, const float* aff, int T, int H, int I, int E, int k,
+                            uint16_t* abuf, float* ybuf, hipStream_t stream) {
+    const int hs = sh.w13 != nullptr;
+    int rc = launch_pf<PF_GATEUP, LAYOUT, C>(x, nullptr, w13, w13s, sh.w13, sh.w13_scale, plan,
+                                             aff, T, H, I, E, k, hs, abuf, ybuf, stream);
+    if (rc == MOE_OK)
+        rc = launch_pf<PF_DOWN, LAYOUT, C>(x, abuf, w2, w2s, sh.w2, sh.w2_scale, plan, aff, T, H,
+                                           I, E, k, hs, abuf, ybuf, stream);
+    return rc;
+}
+
+int launch_prefill_ffn(int layout, const uint16_t* x, const uint8_t* w13, const float* w13s,
+                       const uint8_t* w2, const float* w2s, const SharedW& sh, const Plan& plan,
+                       const float* aff, int T, int H, int I, int E, int k, uint16_t* abuf,
+                       float* ybuf, hipStream_t stream) {
+    if (!prefill_supported(H, I)) {
+        set_error("prefill variant needs H %% 256 == 0 (got H=%d, I=%d)", H, I);
+        return MOE_EUNSUPPORTED;
+    }
+    const bool wide = H % 512 == 0 && (2 * I) % 512 == 0;
+    if (layout == LAYOUT_TILED)
+        return wide ? launch_prefill_c<LAYOUT_TILED, PfWide>(x, w13, w13s, w2, w2s, sh, plan, aff,
+                                                             T, H, I, E, k, abuf, ybuf, stream)
+                    : launch_prefill_c<LAYOUT_TILED, PfNarrow>(x, w13, w13s, w2, w2s, sh, plan,
+                                                               aff, T, H, I, E, k, abuf, ybuf,
+                                                               stream);
+    return wide ? launch_prefill_c<LAYOUT_ROWMAJOR, PfWide>(x, w13, w13s, w2, w2s, sh, plan, aff, T,
+                                                            H, I, E, k, abuf, ybuf, stream)
+                : launch_prefill_c<LAYOUT_ROWMAJOR, PfNarrow>(x, w13, w13s, w2, w2s, sh, plan, aff,
+                                                              T, H, I, E, k, abuf, ybuf, stream);
 }
 
 }  // namespace moe

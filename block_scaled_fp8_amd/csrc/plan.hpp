@@ -38,19 +38,23 @@ int launch_sort(const int32_t* ids, int T, int k, int E, const Plan& plan, int h
 // Kernel launchers (route.hip, ffn_decode.hip, ffn_prefill.hip, misc).
 int launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* aff,
                  int32_t* status, hipStream_t stream);
+// Both FFN variants write, for every valid route r = t*k + j, the row
+// y[r] = aff[r] * MLP_e(x_t) (fp32, H wide) and, for the shared expert, y[R + t];
+// the combine then sums k contiguous rows per token.
 int launch_decode_ffn(int layout, const uint16_t* x, const uint8_t* w13, const float* w13s,
                       const uint8_t* w2, const float* w2s, const SharedW& sh, const Plan& plan,
-                      int T, int H, int I, int E, int k, uint16_t* abuf, float* ybuf,
-                      hipStream_t stream);
+                      const float* aff, int T, int H, int I, int E, int k, uint16_t* abuf,
+                      float* ybuf, hipStream_t stream);
 int launch_prefill_ffn(int layout, const uint16_t* x, const uint8_t* w13, const float* w13s,
                        const uint8_t* w2, const float* w2s, const SharedW& sh, const Plan& plan,
-                       int T, int H, int I, int E, int k, uint16_t* abuf, float* ybuf,
-                       hipStream_t stream);
+                       const float* aff, int T, int H, int I, int E, int k, uint16_t* abuf,
+                       float* ybuf, hipStream_t stream);
 int launch_pack_w8(const uint8_t* src, uint8_t* dst, int64_t n_mats, int rows, int cols,
                    hipStream_t stream);
 int prefill_tile_m();
-int launch_combine(const float* ybuf, const int32_t* inv_route, const float* aff, int T, int H,
-                   int k, int has_shared, float* out, hipStream_t stream);
+int prefill_supported(int H, int I);
+int launch_combine(const float* ybuf, const int32_t* inv_route, int T, int H, int k,
+                   int has_shared, float* out, hipStream_t stream);
 int launch_decode_e4m3fn(const uint8_t* codes, uint16_t* out, int64_t n, hipStream_t stream);
 int launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t stream);
 

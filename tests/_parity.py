@@ -1,4 +1,6 @@
 """Helpers for GPU-vs-oracle parity tests (inputs on the GPU, oracle on the CPU)."""
+import os
+
 import numpy as np
 import torch
 
@@ -51,8 +53,12 @@ def assert_out_close(got, ref, tol=OUT_TOL, what=""):
     assert np.all(np.isfinite(got)), f"{what}: non-finite GPU output"
     rms = float(np.sqrt(np.mean(ref ** 2)))
     err = float(np.max(np.abs(got - ref))) if got.size else 0.0
-    print(f"[parity] {what}: max|d|={err:.4g} rms={rms:.4g} ratio={err / max(rms, 1e-300):.4g}",
-          flush=True)
+    line = f"[parity] {what}: max|d|={err:.4g} rms={rms:.4g} ratio={err / max(rms, 1e-300):.4g}"
+    print(line, flush=True)
+    log = os.environ.get("MOE_PARITY_LOG")
+    if log:
+        with open(log, "a") as f:
+            f.write(line + "\n")
     assert err <= tol * rms, f"{what}: max|gpu-oracle| = {err:.4g} > {tol} * RMS {rms:.4g}"
 
 

@@ -175,6 +175,7 @@ def test_pack_w8_matches_reference(shape):
 
 # ------------------------------------------------------------------ fused FFN
 LAYOUTS = ["rowmajor", "tiled"]
+VARIANTS = ["decode", "prefill"]
 _tiled = {"src": None, "packed": None}   # holds its source case, so identity stays valid
 
 
@@ -193,7 +194,7 @@ def _fused(c, ids, aff, variant="auto", shared=True, layout="rowmajor", **kw):
 
 
 @pytest.mark.parametrize("layout", LAYOUTS)
-@pytest.mark.parametrize("variant", ["decode"])
+@pytest.mark.parametrize("variant", VARIANTS)
 @pytest.mark.parametrize("name", synth.CONFIG_ORDER)
 def test_fused_parity(name, variant, layout):
     """End to end on the GPU (route -> sort -> FFN), oracle from the logits."""
@@ -212,7 +213,7 @@ def test_fused_parity(name, variant, layout):
 
 
 @pytest.mark.parametrize("layout", LAYOUTS)
-@pytest.mark.parametrize("variant", ["decode"])
+@pytest.mark.parametrize("variant", VARIANTS)
 @pytest.mark.parametrize("T", [1, 15, 16, 17, 37])
 def test_fused_token_boundaries(T, variant, layout):
     cfg = synth.MoeConfig("b", T=T, H=256, I=256, E=16, k=4)
@@ -225,10 +226,10 @@ def test_fused_token_boundaries(T, variant, layout):
 
 
 @pytest.mark.parametrize("layout", LAYOUTS)
-@pytest.mark.parametrize("variant", ["decode"])
+@pytest.mark.parametrize("variant", VARIANTS)
 def test_fused_hot_expert_and_shared(variant, layout):
     """Every token routed to the same experts (one long segment) + a shared expert."""
-    cfg = synth.MoeConfig("hot", T=70, H=384, I=256, E=8, k=2, shared=True)
+    cfg = synth.MoeConfig("hot", T=300, H=512, I=256, E=8, k=2, shared=True)
     c = gpu_case(cfg, seed=5)
     ids_np = np.tile(np.array([[3, 6]], np.int32), (cfg.T, 1))
     aff_np = synth.random_affinities(cfg.T, 2, seed=5).numpy()
@@ -239,7 +240,7 @@ def test_fused_hot_expert_and_shared(variant, layout):
 
 
 @pytest.mark.parametrize("layout", LAYOUTS)
-@pytest.mark.parametrize("variant", ["decode"])
+@pytest.mark.parametrize("variant", VARIANTS)
 def test_fused_zero_affinities(variant, layout):
     cfg = synth.MoeConfig("z", T=9, H=256, I=128, E=8, k=3, shared=True)
     c = gpu_case(cfg, seed=6)
@@ -253,7 +254,7 @@ def test_fused_zero_affinities(variant, layout):
 
 
 @pytest.mark.parametrize("layout", LAYOUTS)
-@pytest.mark.parametrize("variant", ["decode"])
+@pytest.mark.parametrize("variant", VARIANTS)
 def test_fused_single_expert_dense(variant, layout):
     cfg = synth.MoeConfig("d", T=33, H=512, I=384, E=1, k=1)
     c = gpu_case(cfg, seed=7)
@@ -283,12 +284,24 @@ def test_fused_bad_ids_are_dropped():
     assert_out_close(np_(out), ref, what="bad ids dropped")
 
 
-def test_fused_is_deterministic():
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_fused_is_deterministic(variant):
     c = _case("decode512")
     ids, aff = binding.route(c["logits"], c["cfg"].k)
-    a = _fused(c, ids, aff)
-    b = _fused(c, ids, aff)
+    a = _fused(c, ids, aff, variant=variant)
+    b = _fused(c, ids, aff, variant=variant)
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_variants_agree(layout):
+    """Decode and prefill kernels compute the same sums (different tilings)."""
+    c = _case("decode512")
+    ids, aff = binding.route(c["logits"], c["cfg"].k)
+    d = np_(_fused(c, ids, aff, variant="decode", layout=layout)).astype(np.float64)
+    p = np_(_fused(c, ids, aff, variant="prefill", layout=layout)).astype(np.float64)
+    rms = np.sqrt(np.mean(d ** 2))
+    assert np.max(np.abs(d - p)) <= 2e-2 * rms
 
 
 def test_graph_replay_with_changing_routes():
