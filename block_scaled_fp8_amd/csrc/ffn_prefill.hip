@@ -12,21 +12,26 @@
 // section) and are decoded to bf16 on chip.
 //
 // gfx950 design.  Kernel 1 (gate/up): each workgroup computes a 128-row x
-// (256 gate + 256 up) tile of one segment, applies SwiGLU in registers and
+// (128 gate + 128 up) tile of one segment, applies SwiGLU in registers and
 // writes bf16 activations (abuf, sorted row order).  Kernel 2 (down): each
-// workgroup computes a 128-row x 512-column tile of y = a W2^T, multiplies it
+// workgroup computes a 128-row x 256-column tile of y = a W2^T, multiplies it
 // by the route's affinity and writes fp32 rows at the route's own index
 // r = t*k + j, so the final combine streams k contiguous rows per token.
 //
-//  * Workgroup tile 128 rows x 512 columns (gate/up: 256 gate + the matching
-//    256 up columns), 8 waves (2 x 4), each a 64 x 128 tile of
+//  * Workgroup tile 128 rows x 256 columns (gate/up: 128 gate + the matching
+//    128 up columns), 4 waves (2 x 2), each a 64 x 128 tile of
 //    v_mfma_f32_32x32x16_bf16 (2 x 4 MFMA tiles, 128 fp32 accumulators).
+//    Two workgroups share a CU (64 KB of stages each, 2 waves per SIMD), so
+//    one workgroup's prologue, epilogue and barrier waits overlap the other's
+//    MFMAs; measured, this beats one 8-wave 128 x 512 workgroup per CU.
 //  * Operands are staged through LDS with 16-byte direct-to-LDS loads
 //    (global_load_lds_dwordx4: a wave instruction fills one contiguous 1 KB),
-//    three stages of 64-wide K (144 KB), one barrier per K step; loads run
-//    two steps ahead of the MFMAs.
+//    two stages of 64-wide K, one barrier per K step; the next step's loads
+//    are in flight while a step is multiplied, and the LDS reads of the next
+//    half step overlap the MFMAs of the current one.
 //  * Activation tiles: 8 rows x 128 bytes per wave instruction, the 16-byte
-//    pieces of each row XOR-swizzled by (row % 8) to spread LDS banks.
+//    pieces of each row XOR-swizzled by (row / 2) % 8, so that the 16 rows read
+//    by one 16-lane phase of ds_read_b128 cover all 64 LDS banks.
 //    Weight tiles: one 16-row x 64-byte chunk per instruction, stored in lane
 //    order (the tile-coalesced layout is this chunk order in memory).
 //  * FP8 is converted exactly to bf16 after the LDS read; the fp32 block scale
@@ -44,9 +49,11 @@ namespace moe {
 constexpr int PF_BK = 64;  // K per stage
 
 // Workgroup tile BM rows x BN columns, WM x WN waves of 64 x 128 each (2 x 4
-// MFMA tiles of 32 x 32), STAGES LDS stages of 64-wide K.
-template <int BM_, int BN_, int WM_, int WN_, int STAGES_>
+// MFMA tiles of 32 x 32), STAGES LDS stages of 64-wide K, OCC workgroups per
+// CU (the register budget follows from it).
+template <int BM_, int BN_, int WM_, int WN_, int STAGES_, int OCC_>
 struct PfCfg {
+    static constexpr int OCC = OCC_;
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
     static constexpr int THREADS = WM * WN * MOE_WAVE;
     static constexpr int WAVES = WM * WN;
@@ -62,31 +69,55 @@ struct PfCfg {
     static_assert(BM == 128, "tile prefixes are built for 128-row tiles");
     static_assert(A_INSTR >= 1 && B_INSTR >= 1, "every wave issues loads");
 };
-using PfWide = PfCfg<128, 512, 2, 4, 3>;    // 8 waves, 144 KB LDS
-using PfNarrow = PfCfg<128, 256, 2, 2, 3>;  // 4 waves, 96 KB LDS (smaller widths)
+// 4 waves and 64 KB of stages: two workgroups share a CU, so one's prologue,
+// epilogue and barrier waits overlap the other's MFMAs.
+using PfTile = PfCfg<128, 256, 2, 2, 2, 2>;
 constexpr int PF_BM = 128;
 
 int prefill_tile_m() { return PF_BM; }
 
-// Widths the grouped GEMMs tile exactly (K % 128 holds for every valid call).
-int prefill_supported(int H, int I) { return H % 256 == 0 && (2 * I) % 256 == 0; }
+// Widths the grouped GEMMs tile exactly (K % 128 holds for every valid call);
+// the per-tile scale table (2 rows of K / 128 floats, padded to 64) must fit
+// in LDS beside the stages, which holds for K <= 65536.
+int prefill_supported(int H, int I) {
+    return H % 256 == 0 && (2 * I) % 256 == 0 && H <= 65536 && I <= 65536;
+}
 
 enum { PF_GATEUP = 0, PF_DOWN = 1 };
+
+// silu(g) * u with the hardware reciprocal (about 1 ulp) in place of an IEEE
+// divide; exp(-g) overflowing to +inf gives the correct limit 0.
+__device__ __forceinline__ float swiglu_fast(float g, float u) {
+    return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+}
 
 __device__ __forceinline__ void lds_load16(const void* g, uint32_t lds_byte_addr_uniform, void* lds_base) {
     __builtin_amdgcn_global_load_lds(g, reinterpret_cast<char*>(lds_base) + lds_byte_addr_uniform, 16,
                                      0, 0);
 }
 
-// s_waitcnt vmcnt(n) (n < 16), leaving the other counters unconstrained.
+// s_waitcnt vmcnt(n) (n < 64), leaving the other counters unconstrained.  The
+// gfx9 encoding splits vmcnt into bits 3:0 and 15:14; expcnt is bits 6:4 and
+// lgkmcnt bits 11:8.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 16, "vmcnt field");
-    __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+    static_assert(N >= 0 && N < 64, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// Workgroup barrier for the K loop.  A __syncthreads() fence would also wait
+// for every direct-to-LDS load in flight (they write LDS), which drains the
+// prefetch pipeline; here the caller has already waited (vmcnt) for the loads
+// other waves will read, and this wave's own LDS reads are waited for before
+// the barrier so that a buffer can be refilled after it.  The asm statement
+// also keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void barrier_after_lds_reads() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt unconstrained
+    asm volatile("s_barrier" ::: "memory");
 }
 
 template <int MODE, int LAYOUT, class C>
-__global__ __launch_bounds__(C::THREADS, 1) void prefill_gemm_kernel(
+__global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ abuf_in,
     const uint8_t* __restrict__ wexp, const float* __restrict__ sexp,
     const uint8_t* __restrict__ wsh, const float* __restrict__ ssh, Plan plan,
@@ -151,14 +182,16 @@ __global__ __launch_bounds__(C::THREADS, 1) void prefill_gemm_kernel(
 #pragma unroll
     for (int q = 0; q < C::A_INSTR; ++q) {
         const int row = (wave * C::A_INSTR + q) * 8 + ar_sub;
-        const int sw = apiece ^ (row & 7);  // swizzled piece this lane fetches
+        const int sw = apiece ^ ((row >> 1) & 7);  // swizzled piece this lane fetches
         const uint16_t* base = MODE == PF_GATEUP ? x + (size_t)row_tok[row] * H
                                                  : abuf_in + (size_t)row_tok[row] * I;
         asrc[q] = base + sw * 8;
     }
     // weights: instruction q of wave w fills 16-row tile w*B_INSTR + q
     constexpr int HALF_T = BN / 2 / 16;  // gate tiles in a gate/up tile (MODE 0)
-    const uint8_t* bsrc[C::B_INSTR];
+    // (a wave-uniform tile base plus one per-lane offset, so the loads address
+    //  through a scalar base; the lane's 16 bytes follow tile_lane_ptr)
+    const uint8_t* bbase[C::B_INSTR];
 #pragma unroll
     for (int q = 0; q < C::B_INSTR; ++q) {
         const int t16 = wave * C::B_INSTR + q;
@@ -167,8 +200,9 @@ __global__ __launch_bounds__(C::THREADS, 1) void prefill_gemm_kernel(
             wrow = (t16 < HALF_T ? 0 : I) + nb * (BN / 2) + (t16 % HALF_T) * 16;
         else
             wrow = nb * BN + t16 * 16;
-        bsrc[q] = tile_lane_ptr<LAYOUT>(W, wrow, K, lane);
+        bbase[q] = W + (size_t)wrow * K;  // the tiled layout keeps whole 16-row tiles in place
     }
+    const uint32_t blane = LAYOUT == LAYOUT_TILED ? lane * 16 : (lane & 15) * K + (lane >> 4) * 16;
     constexpr int CS = chunk_stride<LAYOUT>();
 
     auto issue_stage = [&](int st, int kc) {
@@ -178,7 +212,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void prefill_gemm_kernel(
             lds_load16(asrc[q] + kc * PF_BK, sbase + (wave * C::A_INSTR + q) * 1024, smem);
 #pragma unroll
         for (int q = 0; q < C::B_INSTR; ++q)
-            lds_load16(bsrc[q] + (size_t)kc * CS, sbase + C::A_BYTES + (wave * C::B_INSTR + q) * 1024,
+            lds_load16(bbase[q] + (size_t)kc * CS + blane, sbase + C::A_BYTES + (wave * C::B_INSTR + q) * 1024,
                        smem);
     };
 
@@ -192,7 +226,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void prefill_gemm_kernel(
     for (int mt = 0; mt < C::MT; ++mt) {
         const int row = wm * 64 + mt * 32 + ln;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) a_off[mt][s] = row * 128 + (((4 * lg + s) ^ (row & 7)) * 16);
+        for (int s = 0; s < 4; ++s) a_off[mt][s] = row * 128 + (((4 * lg + s) ^ ((row >> 1) & 7)) * 16);
     }
     // weight LDS tiles of each 32-column MFMA tile (MODE 0: nt 0,1 gate, 2,3 the matching up)
     uint32_t b_off[C::NT][2];
@@ -207,15 +241,37 @@ __global__ __launch_bounds__(C::THREADS, 1) void prefill_gemm_kernel(
 #pragma unroll
         for (int h = 0; h < 2; ++h) b_off[nt][h] = C::A_BYTES + tt * 1024 + ((2 * lg + h) * 16 + r) * 16;
     }
-    // scale rows of this wave's columns (each group lies in one 128-row scale block)
-    int srow[2];
-    if (MODE == PF_GATEUP) {
-        srow[0] = __builtin_amdgcn_readfirstlane((nb * (BN / 2) + wn * 64) >> 7);
-        srow[1] = __builtin_amdgcn_readfirstlane((I + nb * (BN / 2) + wn * 64) >> 7);
-    } else {
-        srow[0] = srow[1] = __builtin_amdgcn_readfirstlane((nb * BN + wn * 128) >> 7);
-    }
+    // ---- block scales of the workgroup's columns, staged once in LDS by
+    //      direct-to-LDS loads issued before the first operand stages (so the
+    //      first stage wait covers them).  Table row j < NR/2 (MODE 0: gate;
+    //      MODE 1: all NR rows) holds the 128-row scale block (col0 >> 7) + j
+    //      over all K blocks, MODE 0 rows NR/2.. the matching up blocks; rows
+    //      are padded to 64 floats and the padding repeats the last block.
+    constexpr int NR = BN / 128;
     const int kblocks = K >> 7;
+    const int kbp = (kblocks + 63) & ~63;
+    float* sc_tab = reinterpret_cast<float*>(smem + C::STAGES * C::STAGE);
+    {
+        const int nchunk = kbp >> 6;
+        for (int it = wave; it < NR * nchunk; it += C::WAVES) {
+            const int j = it / nchunk, c = it - j * nchunk;
+            int sr;
+            if (MODE == PF_GATEUP)
+                sr = j < NR / 2 ? ((nb * (BN / 2)) >> 7) + j : ((I + nb * (BN / 2)) >> 7) + j - NR / 2;
+            else
+                sr = ((nb * BN) >> 7) + j;
+            const int kb = min(c * 64 + lane, kblocks - 1);
+            __builtin_amdgcn_global_load_lds(S + (size_t)sr * kblocks + kb, sc_tab + j * kbp + c * 64, 4, 0, 0);
+        }
+    }
+    // this wave's table rows: g = 0 its gate (or only) columns, g = 1 its up columns
+    int sj[2];
+    if (MODE == PF_GATEUP) {
+        sj[0] = (wn * 64) >> 7;
+        sj[1] = NR / 2 + sj[0];
+    } else {
+        sj[0] = sj[1] = (wn * 128) >> 7;
+    }
 
     f32x16 acc[C::MT][C::NT];
 #pragma unroll
@@ -226,60 +282,106 @@ __global__ __launch_bounds__(C::THREADS, 1) void prefill_gemm_kernel(
             for (int i = 0; i < 16; ++i) acc[mt][nt][i] = 0.0f;
     float seff[2] = {0.0f, 0.0f};
 
-    const int nk = K / PF_BK;  // >= 2 since K % 128 == 0
-#pragma unroll
-    for (int st = 0; st < C::STAGES - 1; ++st)
-        if (st < nk) issue_stage(st, st);
+    // ---- K loop, software-pipelined by half steps.  Half p of a 64-wide step
+    //      covers sub-steps 2p, 2p+1 (16 K each): A pieces 2p, 2p+1 and 16-byte
+    //      weight piece p.  The LDS reads of the next half are in flight while
+    //      the MFMAs of the current half run; the LDS stages hold step kc
+    //      (being read) and the following ones (landing), and the buffer of
+    //      step kc is refilled with step kc+STAGES once every wave has read
+    //      it.  The body
+    //      covers the two steps of one 128-wide K block and is branch-free
+    //      around the LDS reads, so their waits stay partial.
+    const int nk = K / PF_BK;  // even and >= 2 since K % 128 == 0
     constexpr int PER_STAGE = C::A_INSTR + C::B_INSTR;
-    for (int kc = 0; kc < nk; ++kc) {
-        // stage kc is complete once at most the younger stages' loads are pending
-        if (kc + C::STAGES - 2 < nk) wait_vmcnt<(C::STAGES - 2) * PER_STAGE>();
+    u32x4 ah[2][C::MT][2], bh[2][C::NT];
+    auto read_half = [&](int stage, int p, u32x4 (&a)[C::MT][2], u32x4 (&b)[C::NT]) {
+        const char* st = smem + stage * C::STAGE;
+#pragma unroll
+        for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) a[mt][j] = *reinterpret_cast<const u32x4*>(st + a_off[mt][2 * p + j]);
+#pragma unroll
+        for (int nt = 0; nt < C::NT; ++nt) b[nt] = *reinterpret_cast<const u32x4*>(st + b_off[nt][p]);
+    };
+    // Sub-step j of a half.  rescale: the half opens a new K block, and each
+    // accumulator is multiplied by its group's factor right before its first
+    // MFMA of the block.
+    auto mma_sub = [&](const u32x4 (&a)[C::MT][2], const u32x4 (&b)[C::NT], int j, bool rescale,
+                       const float (&rr)[2]) {
+#pragma unroll
+        for (int nt = 0; nt < C::NT; ++nt) {
+            const bf16x8 bf = j == 0 ? fp8x8_to_bf16x8(b[nt][0], b[nt][1]) : fp8x8_to_bf16x8(b[nt][2], b[nt][3]);
+            const float f = MODE == PF_GATEUP ? rr[nt >> 1] : rr[0];
+#pragma unroll
+            for (int mt = 0; mt < C::MT; ++mt) {
+                if (rescale)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) acc[mt][nt][i] *= f;
+                acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[mt][j]), bf, acc[mt][nt], 0, 0, 0);
+            }
+        }
+    };
+    // step kc + 1 landed (with three stages step kc + 2 may still be in
+    // flight); the barrier also orders every wave's reads of buffer kc before
+    // its refill
+    auto next_step = [&](int kc) {
+        if (C::STAGES >= 3 && kc + 2 < nk) wait_vmcnt<(C::STAGES >= 3 ? PER_STAGE : 0)>();
         else wait_vmcnt<0>();
-        __syncthreads();  // every wave: stage kc landed, stage kc-1 fully consumed
-        if (kc + C::STAGES - 1 < nk) issue_stage((kc + C::STAGES - 1) % C::STAGES, kc + C::STAGES - 1);
-        if ((kc & 1) == 0) {  // new 128-wide K block: rescale to its scales
-            const int kb = kc >> 1;
+        barrier_after_lds_reads();
+        if (kc + C::STAGES < nk) issue_stage(kc % C::STAGES, kc + C::STAGES);
+        // past the last step this reads a stale buffer whose values are unused
+        read_half((kc + 1) % C::STAGES, 0, ah[0], bh[0]);
+    };
+
 #pragma unroll
-            for (int g = 0; g < 2; ++g) {
-                if (MODE == PF_DOWN && g == 1) break;
-                const float sn = S[srow[g] * kblocks + kb];
-                if (sn != 0.0f) {
-                    if (seff[g] != 0.0f) {
-                        const float rr = seff[g] * __builtin_amdgcn_rcpf(sn);
+    for (int st = 0; st < C::STAGES; ++st)
+        if (st < nk) issue_stage(st, st);
+    if (nk >= C::STAGES) wait_vmcnt<(C::STAGES - 1) * PER_STAGE>();
+    else wait_vmcnt<PER_STAGE>();  // nk == 2: stages 0 and 1 issued
+    barrier_after_lds_reads();     // stage 0 and the scale table landed in every wave
+    float snext[2] = {sc_tab[sj[0] * kbp], sc_tab[sj[1] * kbp]};
+    read_half(0, 0, ah[0], bh[0]);
+    const float one[2] = {1.0f, 1.0f};
+    for (int kb = 0; kb < kblocks; ++kb) {
+        const int kc = 2 * kb;
+        // running scale: a zero scale (all-zero block) keeps the current one
+        float rr[2];
 #pragma unroll
-                        for (int mt = 0; mt < C::MT; ++mt)
-#pragma unroll
-                            for (int nt = 0; nt < C::NT; ++nt)
-                                if (MODE == PF_DOWN || (nt >> 1) == g)
-#pragma unroll
-                                    for (int i = 0; i < 16; ++i) acc[mt][nt][i] *= rr;
-                    }
-                    seff[g] = sn;
-                }
-            }
-            if (MODE == PF_DOWN) seff[1] = seff[0];
+        for (int g = 0; g < 2; ++g) {
+            const float sn = snext[g];
+            const bool take = sn != 0.0f;
+            rr[g] = take && seff[g] != 0.0f ? seff[g] * __builtin_amdgcn_rcpf(sn) : 1.0f;
+            seff[g] = take ? sn : seff[g];
         }
-        const char* st = smem + (kc % C::STAGES) * C::STAGE;
-        u32x4 bw[C::NT][2];
-#pragma unroll
-        for (int nt = 0; nt < C::NT; ++nt)
-#pragma unroll
-            for (int h = 0; h < 2; ++h) bw[nt][h] = *reinterpret_cast<const u32x4*>(st + b_off[nt][h]);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            bf16x8 af[C::MT];
-#pragma unroll
-            for (int mt = 0; mt < C::MT; ++mt)
-                af[mt] = as_bf16x8(*reinterpret_cast<const u32x4*>(st + a_off[mt][s]));
-#pragma unroll
-            for (int nt = 0; nt < C::NT; ++nt) {
-                const u32x4& v = bw[nt][s >> 1];
-                const bf16x8 bf = (s & 1) == 0 ? fp8x8_to_bf16x8(v[0], v[1]) : fp8x8_to_bf16x8(v[2], v[3]);
-#pragma unroll
-                for (int mt = 0; mt < C::MT; ++mt)
-                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mt], bf, acc[mt][nt], 0, 0, 0);
-            }
-        }
+        const int kn = kb + 1 < kblocks ? kb + 1 : kb;
+        snext[0] = sc_tab[sj[0] * kbp + kn];
+        snext[1] = sc_tab[sj[1] * kbp + kn];
+
+        // the reads of the second half go out after the first sub-step's MFMAs,
+        // whose operands were read a whole half earlier
+        mma_sub(ah[0], bh[0], 0, true, rr);
+        __builtin_amdgcn_sched_barrier(0);
+        read_half(kc % C::STAGES, 1, ah[1], bh[1]);
+        __builtin_amdgcn_sched_barrier(0);
+        mma_sub(ah[0], bh[0], 1, false, one);
+        __builtin_amdgcn_sched_barrier(0);
+        next_step(kc);
+        __builtin_amdgcn_sched_barrier(0);
+        mma_sub(ah[1], bh[1], 0, false, one);
+        mma_sub(ah[1], bh[1], 1, false, one);
+        __builtin_amdgcn_sched_barrier(0);
+
+        mma_sub(ah[0], bh[0], 0, false, one);
+        __builtin_amdgcn_sched_barrier(0);
+        read_half((kc + 1) % C::STAGES, 1, ah[1], bh[1]);
+        __builtin_amdgcn_sched_barrier(0);
+        mma_sub(ah[0], bh[0], 1, false, one);
+        __builtin_amdgcn_sched_barrier(0);
+        next_step(kc + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        mma_sub(ah[1], bh[1], 0, false, one);
+        mma_sub(ah[1], bh[1], 1, false, one);
+        __builtin_amdgcn_sched_barrier(0);
     }
 
     // ---- epilogue. 32x32 accumulator layout: lane l holds column l%32 and,
@@ -296,7 +398,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void prefill_gemm_kernel(
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt)
                     orow[nt * 32] = f32_to_bf16_bits(
-                        swiglu(acc[mt][nt][i] * seff[0], acc[mt][nt + 2][i] * seff[1]));
+                        swiglu_fast(acc[mt][nt][i] * seff[0], acc[mt][nt + 2][i] * seff[1]));
             } else {
                 const float a = row_aff[row];
                 float* orow = ybuf + (size_t)dst * H + nb * BN + wn * 128 + ln;
@@ -305,6 +407,9 @@ __global__ __launch_bounds__(C::THREADS, 1) void prefill_gemm_kernel(
             }
         }
 }
+
+template <int MODE>
+static inline int K_of(int H, int I) { return MODE == PF_GATEUP ? H : I; }
 
 template <int MODE, int LAYOUT, class C>
 static int launch_pf(const uint16_t* x, const uint16_t* abuf_in, const uint8_t* wexp,
@@ -322,7 +427,8 @@ static int launch_pf(const uint16_t* x, const uint16_t* abuf_in, const uint8_t* 
         set_error("prefill: too many tiles");
         return MOE_EUNSUPPORTED;
     }
-    const size_t lds = (size_t)C::STAGES * C::STAGE;
+    const size_t kbp = ((size_t)K_of<MODE>(H, I) / 128 + 63) / 64 * 64;
+    const size_t lds = (size_t)C::STAGES * C::STAGE + (size_t)(C::BN / 128) * kbp * 4;
     prof_begin(MODE == PF_GATEUP ? "prefill_gateup_swiglu" : "prefill_down", stream);
     prefill_gemm_kernel<MODE, LAYOUT, C><<<(unsigned)grid, C::THREADS, lds, stream>>>(
         x, abuf_in, wexp, sexp, wsh, ssh, plan, aff, T, H, I, k, nblk, xcd_chunk, abuf_out, ybuf);
@@ -349,20 +455,14 @@ int launch_prefill_ffn(int layout, const uint16_t* x, const uint8_t* w13, const 
                        const float* aff, int T, int H, int I, int E, int k, uint16_t* abuf,
                        float* ybuf, hipStream_t stream) {
     if (!prefill_supported(H, I)) {
-        set_error("prefill variant needs H %% 256 == 0 (got H=%d, I=%d)", H, I);
+        set_error("prefill variant needs H %% 256 == 0, 2I %% 256 == 0 and H, I <= 65536 (got H=%d, I=%d)", H, I);
         return MOE_EUNSUPPORTED;
     }
-    const bool wide = H % 512 == 0 && (2 * I) % 512 == 0;
     if (layout == LAYOUT_TILED)
-        return wide ? launch_prefill_c<LAYOUT_TILED, PfWide>(x, w13, w13s, w2, w2s, sh, plan, aff,
-                                                             T, H, I, E, k, abuf, ybuf, stream)
-                    : launch_prefill_c<LAYOUT_TILED, PfNarrow>(x, w13, w13s, w2, w2s, sh, plan,
-                                                               aff, T, H, I, E, k, abuf, ybuf,
-                                                               stream);
-    return wide ? launch_prefill_c<LAYOUT_ROWMAJOR, PfWide>(x, w13, w13s, w2, w2s, sh, plan, aff, T,
-                                                            H, I, E, k, abuf, ybuf, stream)
-                : launch_prefill_c<LAYOUT_ROWMAJOR, PfNarrow>(x, w13, w13s, w2, w2s, sh, plan, aff,
-                                                              T, H, I, E, k, abuf, ybuf, stream);
+        return launch_prefill_c<LAYOUT_TILED, PfTile>(x, w13, w13s, w2, w2s, sh, plan, aff, T, H, I,
+                                                      E, k, abuf, ybuf, stream);
+    return launch_prefill_c<LAYOUT_ROWMAJOR, PfTile>(x, w13, w13s, w2, w2s, sh, plan, aff, T, H, I,
+                                                     E, k, abuf, ybuf, stream);
 }
 
 }  // namespace moe
