@@ -165,6 +165,34 @@ def measure(cfg, L, steps, warmup, variant, layout, seed, dev):
                 prof=prof, x=x, logits=logits, wsets=wsets, L=L, runs=runs)
 
 
+def profiled_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload` from the committed rocprofv3
+    summary profiles/<kernel>__<workload>.md (FETCH_SIZE and WRITE_SIZE passes,
+    scaled by a plain copy's reading), or None when there is no summary or the
+    kernel's sources changed since the counters were taken."""
+    import hashlib
+    import re
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                        f"{kernel}__{workload}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    got = {k: v.strip() for k, v in re.findall(r"^(traffic_bytes_per_launch|source_files|source_sha256):(.*)$",
+                                                 text, re.M)}
+    if len(got) != 3:
+        return None
+    h = hashlib.sha256()
+    root = os.path.dirname(os.path.abspath(__file__))
+    for f in got["source_files"].split():
+        fp = os.path.join(root, f)
+        if not os.path.exists(fp):
+            return None
+        h.update(open(fp, "rb").read())
+    if h.hexdigest()[:16] != got["source_sha256"]:
+        return None
+    return int(got["traffic_bytes_per_launch"])
+
+
 def prefill_summary(cfg, m):
     """MFMA roofline of the prefill workload (secondary object of the JSON line)."""
     R = cfg.T * cfg.k + (cfg.T if cfg.shared else 0)
@@ -186,7 +214,9 @@ def prefill_summary(cfg, m):
         out["roofline"] = {"bound": "mfma", "kernel": "prefill_gateup_swiglu",
                            "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS,
                            "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4),
-                           "traffic": None, "flops_per_launch": flops_gateup,
+                           "traffic": profiled_traffic("prefill_gateup_swiglu", cfg.name),
+                           "traffic_unit": "bytes per launch",
+                           "flops_per_launch": flops_gateup,
                            "avg_us": round(us, 3)}
     return out
 
@@ -250,7 +280,8 @@ def main():
                 "achieved": round(achieved, 1) if achieved else None,
                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4) if achieved else None,
-                "traffic": None,
+                "traffic": profiled_traffic(dom, cfg.name),
+                "traffic_unit": "bytes per launch",
                 "bytes_per_launch": dom_bytes, "avg_us": round(dom_ms * 1e3, 3)}
 
     sb = step_bytes(cfg, n_active, cfg.shared)
