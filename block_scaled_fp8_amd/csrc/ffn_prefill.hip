@@ -38,9 +38,9 @@
 //    of each 128-wide K block is applied by rescaling the accumulators when the
 //    block starts (running scale), never by rounding it into bf16.
 //  * Work list: the sort builds per-segment tile prefixes; the grid covers the
-//    worst case and idle workgroups exit.  Workgroup ids are remapped so that
-//    consecutive tiles (same expert, neighbouring rows) land on the same XCD
-//    and share its L2.
+//    worst case and idle workgroups exit.  The real work list is split evenly
+//    over the 8 XCDs, each taking a contiguous range, so consecutive tiles
+//    (same expert, neighbouring rows) share one L2 and no XCD idles.
 #include "common.hpp"
 #include "plan.hpp"
 
@@ -121,7 +121,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ abuf_in,
     const uint8_t* __restrict__ wexp, const float* __restrict__ sexp,
     const uint8_t* __restrict__ wsh, const float* __restrict__ ssh, Plan plan,
-    const float* __restrict__ aff, int T, int H, int I, int k, int nblk, int xcd_chunk,
+    const float* __restrict__ aff, int T, int H, int I, int k, int nblk, int xcd_split,
     uint16_t* __restrict__ abuf_out, float* __restrict__ ybuf) {
     constexpr int BM = C::BM, BN = C::BN;
     extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -129,12 +129,22 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
     __shared__ int row_dst[BM];     // output row (abuf row / route index), -1 if padding
     __shared__ float row_aff[BM];
 
-    // ---- which tile: XCD-aware remap of the workgroup id, then segment search
+    // ---- which tile.  Workgroups are dealt round-robin over the 8 XCDs
+    //      (id % 8); the real work list (tiles x column blocks, known only on
+    //      the device) is split into 8 contiguous ranges, one per XCD, so that
+    //      every XCD gets an equal share and neighbouring tiles of an expert
+    //      share one L2.  The grid covers the worst case; the rest exit.
     const int bid = blockIdx.x;
-    const int lin = xcd_chunk > 0 ? (bid & 7) * xcd_chunk + (bid >> 3) : bid;
-    const int tile = lin / nblk, nb = lin - tile * nblk;
     const int nseg = plan.seg_n[0];
-    if (tile >= plan.seg_tile0[nseg]) return;
+    const int total = plan.seg_tile0[nseg] * nblk;
+    int lin = bid;
+    if (xcd_split) {
+        const int chunk = (total + 7) >> 3;
+        if ((bid >> 3) >= chunk) return;
+        lin = (bid & 7) * chunk + (bid >> 3);
+    }
+    if (lin >= total) return;
+    const int tile = lin / nblk, nb = lin - tile * nblk;
     int lo = 0, hi = nseg - 1;  // last segment with seg_tile0 <= tile
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
@@ -420,9 +430,8 @@ static int launch_pf(const uint16_t* x, const uint16_t* abuf_in, const uint8_t* 
     const long R = (long)T * k;
     const long max_tiles = (R + C::BM - 1) / C::BM + E + (has_shared ? (T + C::BM - 1) / C::BM : 0);
     long grid = max_tiles * nblk;
-    int xcd_chunk = 0;
-    if (grid % 8 != 0) grid += 8 - grid % 8;  // whole XCD rounds
-    xcd_chunk = (int)(grid / 8);
+    if (grid % 8 != 0) grid += 8 - grid % 8;  // 8 * ceil(total / 8) <= grid for any total <= grid
+    const int xcd_split = 1;
     if (grid > 0x7FFFFFFFL) {
         set_error("prefill: too many tiles");
         return MOE_EUNSUPPORTED;
@@ -431,7 +440,7 @@ static int launch_pf(const uint16_t* x, const uint16_t* abuf_in, const uint8_t* 
     const size_t lds = (size_t)C::STAGES * C::STAGE + (size_t)(C::BN / 128) * kbp * 4;
     prof_begin(MODE == PF_GATEUP ? "prefill_gateup_swiglu" : "prefill_down", stream);
     prefill_gemm_kernel<MODE, LAYOUT, C><<<(unsigned)grid, C::THREADS, lds, stream>>>(
-        x, abuf_in, wexp, sexp, wsh, ssh, plan, aff, T, H, I, k, nblk, xcd_chunk, abuf_out, ybuf);
+        x, abuf_in, wexp, sexp, wsh, ssh, plan, aff, T, H, I, k, nblk, xcd_split, abuf_out, ybuf);
     prof_end(stream);
     return check_launch(MODE == PF_GATEUP ? "prefill_gemm_kernel<gateup>" : "prefill_gemm_kernel<down>");
 }
