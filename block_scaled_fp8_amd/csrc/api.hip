@@ -211,19 +211,25 @@ int moe_fused_w8a16(const void* x, const uint8_t* w13, const float* w13_scale,
     SharedW sh{nullptr, nullptr, nullptr, nullptr};
     if (shared) sh = SharedW{shared->w13, shared->w13_scale, shared->w2, shared->w2_scale};
 
-    const int tile_m = variant == MOE_VARIANT_PREFILL ? prefill_tile_m() : 1;
-    if (int rc = launch_sort(ids, T, k, E, p, has_shared, tile_m, status, base + L.sort_scratch, s))
-        return rc;
     const uint16_t* xb = static_cast<const uint16_t*>(x);
     int rc;
-    if (variant == MOE_VARIANT_DECODE)
-        rc = launch_decode_ffn(weight_layout, xb, w13, w13_scale, w2, w2_scale, sh, p, aff, T, H, I,
-                               E, k, abuf, ybuf, s);
-    else
-        rc = launch_prefill_ffn(weight_layout, xb, w13, w13_scale, w2, w2_scale, sh, p, aff, T, H,
-                                I, E, k, abuf, ybuf, s);
+    if (variant == MOE_VARIANT_DECODE && decode_fused_fits(T, k, E, I, has_shared, true)) {
+        // small decode batch: each expert's workgroup finds its own routes
+        rc = launch_decode_fused_self(weight_layout, decode_mt(T, k, E), xb, w13, w13_scale, w2,
+                                      w2_scale, sh, ids, aff, T, H, I, E, k, ybuf, s);
+    } else {
+        const int tile_m = variant == MOE_VARIANT_PREFILL ? prefill_tile_m() : 1;
+        if ((rc = launch_sort(ids, T, k, E, p, has_shared, tile_m, status, base + L.sort_scratch, s)))
+            return rc;
+        if (variant == MOE_VARIANT_DECODE)
+            rc = launch_decode_ffn(weight_layout, xb, w13, w13_scale, w2, w2_scale, sh, p, aff, T,
+                                   H, I, E, k, abuf, ybuf, s);
+        else
+            rc = launch_prefill_ffn(weight_layout, xb, w13, w13_scale, w2, w2_scale, sh, p, aff, T,
+                                    H, I, E, k, abuf, ybuf, s);
+    }
     if (rc) return rc;
-    return launch_combine(ybuf, p.inv_route, T, H, k, has_shared, out, s);
+    return launch_combine(ybuf, ids, T, H, k, E, has_shared, status, out, s);
 }
 
 int moe_pack_w8(const uint8_t* src, uint8_t* dst, int64_t n_mats, int rows, int cols,

@@ -237,17 +237,24 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_ffn_kernel(
 // reduction); NKI page (affinity scale -> expert-sum, shared expert added after
 // the routed sum).
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ ybuf,
-                                                      const int32_t* __restrict__ inv_route,
-                                                      int T, int H, int k, int has_shared,
+                                                      const int32_t* __restrict__ ids,
+                                                      int T, int H, int k, int E, int has_shared,
+                                                      int32_t* __restrict__ status,
                                                       float* __restrict__ out) {
     const int t = blockIdx.y;
     const int h = (blockIdx.x * 256 + threadIdx.x) * 4;
     if (h >= H) return;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    bool bad = false;
     for (int j = 0; j < k; ++j) {
         const size_t r = (size_t)t * k + j;
-        if (inv_route[r] >= 0) acc += *reinterpret_cast<const f32x4*>(ybuf + r * H + h);
+        const int id = ids[r];
+        if (id >= 0 && id < E)  // a route with an invalid id has no row (dropped)
+            acc += *reinterpret_cast<const f32x4*>(ybuf + r * H + h);
+        else
+            bad = true;
     }
+    if (bad && status && h == 0) atomicOr(status, MOE_STATUS_BAD_EXPERT_ID);
     if (has_shared) {
         const size_t R = (size_t)T * k;
         acc += *reinterpret_cast<const f32x4*>(ybuf + (R + t) * H + h);
@@ -299,15 +306,26 @@ int launch_decode_fused(int layout, int MT, const uint16_t* x, const uint8_t* w1
 // weight byte once with no inter-workgroup dependency; with few active
 // experts the work is split into (expert, N tile) workgroups over two kernels
 // so that all CUs still stream.
+int decode_mt(int T, int k, int E) { return ((long)T * k <= 4L * E) ? 1 : 2; }
+
+// The fused one-workgroup-per-expert kernel pays off once most CUs get an
+// expert, and needs its activations (and, self-routed, the route list) in LDS.
+bool decode_fused_fits(int T, int k, int E, int I, int has_shared, bool self_routed) {
+    const long R = (long)T * k;
+    const long max_active = std::min<long>(E, R) + has_shared;
+    if (max_active < 128) return false;
+    if (self_routed && R > decode_self_routed_max_routes()) return false;
+    return decode_fused_lds_bytes(decode_mt(T, k, E), I, self_routed ? (int)R : 0) <= 64 * 1024;
+}
+
 int launch_decode_ffn(int layout, const uint16_t* x, const uint8_t* w13, const float* w13s,
                       const uint8_t* w2, const float* w2s, const SharedW& sh, const Plan& plan,
                       const float* aff, int T, int H, int I, int E, int k, uint16_t* abuf,
                       float* ybuf, hipStream_t stream) {
     const int has_shared = sh.w13 != nullptr;
     const int nseg_max = E + has_shared;
-    const int MT = ((long)T * k <= 4L * E) ? 1 : 2;
-    const long max_active = std::min<long>(E, (long)T * k) + has_shared;
-    if (max_active >= 128)
+    const int MT = decode_mt(T, k, E);
+    if (decode_fused_fits(T, k, E, I, has_shared, false))
         return launch_decode_fused(layout, MT, x, w13, w13s, w2, w2s, sh, plan, aff, T, H, I, E,
                                    k, ybuf, stream);
     if (int rc = launch_decode_mode<MODE_GATEUP>(layout, MT, nseg_max, x, w13, w13s, w2, w2s, sh,
@@ -317,11 +335,11 @@ int launch_decode_ffn(int layout, const uint16_t* x, const uint8_t* w13, const f
                                          aff, T, H, I, k, abuf, ybuf, stream);
 }
 
-int launch_combine(const float* ybuf, const int32_t* inv_route, int T, int H, int k,
-                   int has_shared, float* out, hipStream_t stream) {
+int launch_combine(const float* ybuf, const int32_t* ids, int T, int H, int k, int E,
+                   int has_shared, int32_t* status, float* out, hipStream_t stream) {
     const dim3 grid((H / 4 + 255) / 256, T), block(256);
     prof_begin("combine", stream);
-    combine_kernel<<<grid, block, 0, stream>>>(ybuf, inv_route, T, H, k, has_shared, out);
+    combine_kernel<<<grid, block, 0, stream>>>(ybuf, ids, T, H, k, E, has_shared, status, out);
     prof_end(stream);
     return check_launch("combine_kernel");
 }

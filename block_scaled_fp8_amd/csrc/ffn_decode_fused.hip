@@ -50,35 +50,92 @@ constexpr int DF_NT = 4;  // weight tiles (16 rows each) per wave pass
 // never drains mid-stream.
 constexpr int DF_HALF = DF_NT / 2;
 
-template <int MT, int DEPTH, int LAYOUT>
+// Self-routed mode (decode batches of at most DF_SELF_MAX_ROUTES routes): the
+// workgroup of expert e finds its own routes by scanning the ids (wave ballots,
+// ascending route order, the same order as the stable sort), so the step needs
+// no separate sort launch.  Workgroup E is the shared expert.
+constexpr int DF_SELF_MAX_ROUTES = 4096;
+constexpr int DF_SELF_IDS_PER_THREAD = DF_SELF_MAX_ROUTES / DF_THREADS;
+
+size_t decode_fused_lds_bytes(int MT, int I, int self_routes) {
+    return sizeof(uint16_t) * (size_t)(16 * MT) * (I + 8) + sizeof(int32_t) * (size_t)self_routes;
+}
+
+template <int MT, int DEPTH, int LAYOUT, bool SELF>
 __global__ __launch_bounds__(DF_THREADS) void decode_fused_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ w13,
     const float* __restrict__ w13s, const uint8_t* __restrict__ w2,
     const float* __restrict__ w2s, const uint8_t* __restrict__ sh_w13,
     const float* __restrict__ sh_w13s, const uint8_t* __restrict__ sh_w2,
-    const float* __restrict__ sh_w2s, Plan plan, const float* __restrict__ aff, int T, int H,
-    int I, int k, float* __restrict__ ybuf, float* __restrict__ ytrash) {
+    const float* __restrict__ sh_w2s, Plan plan, const int32_t* __restrict__ ids, int E,
+    const float* __restrict__ aff, int T, int H, int I, int k, float* __restrict__ ybuf,
+    float* __restrict__ ytrash) {
     static_assert(DEPTH == 1 || DEPTH == 2, "chunks per 128-wide scale block");
     constexpr int MROWS = 16 * MT, NT = DF_NT, HALF = DF_HALF;
     constexpr int CS = chunk_stride<LAYOUT>();
-    // the segment fields are loaded together (arrays hold E+1 >= gridDim.x
-    // entries), so one memory latency passes before the weights are known
-    const int seg = blockIdx.x;
-    const int nseg = plan.seg_n[0];
-    const int e = plan.seg_expert[seg];
-    const int row0 = plan.seg_row0[seg];
-    const int rows = plan.seg_rows[seg];
-    if (seg >= nseg) return;
+    extern __shared__ uint16_t a_lds[];  // [MROWS][I + 8] bf16 SwiGLU activations
+    const int astride = I + 8;  // +16 bytes per row: conflict-free 16-byte column reads
+    const int lane = lane_id(), wave = wave_id();
+    const int R = T * k;
+    int e, row0, rows;
+    int32_t* rlist = reinterpret_cast<int32_t*>(a_lds + (size_t)MROWS * astride);  // SELF: routes of e
+    if (SELF) {
+        const int b = blockIdx.x;
+        if (b > E || (b == E && sh_w13 == nullptr)) return;
+        e = b < E ? b : -1;
+        row0 = 0;
+        rows = T;
+        if (e >= 0) {
+            __shared__ int wcnt[DF_WAVES];
+            int idv[DF_SELF_IDS_PER_THREAD];
+#pragma unroll
+            for (int c = 0; c < DF_SELF_IDS_PER_THREAD; ++c) {
+                const int r = c * DF_THREADS + (int)threadIdx.x;
+                idv[c] = r < R ? ids[r] : -1;
+            }
+            int base = 0;
+#pragma unroll
+            for (int c = 0; c < DF_SELF_IDS_PER_THREAD; ++c) {
+                if (c * DF_THREADS >= R) break;  // uniform
+                const bool hit = idv[c] == e;
+                const uint64_t m = __ballot(hit);
+                if (lane == 0) wcnt[wave] = (int)__popcll(m);
+                __syncthreads();
+                int woff = 0, tot = 0;
+#pragma unroll
+                for (int w = 0; w < DF_WAVES; ++w) {
+                    const int cw = wcnt[w];
+                    woff += w < wave ? cw : 0;
+                    tot += cw;
+                }
+                if (hit) rlist[base + woff + (int)__popcll(m & lanemask_lt())] = c * DF_THREADS + (int)threadIdx.x;
+                base += tot;
+                __syncthreads();  // wcnt is rewritten next round; rlist complete after the last
+            }
+            rows = base;
+            if (rows == 0) return;  // the same value in every thread
+        }
+    } else {
+        // the segment fields are loaded together (arrays hold E+1 >= gridDim.x
+        // entries), so one memory latency passes before the weights are known
+        const int seg = blockIdx.x;
+        const int nseg = plan.seg_n[0];
+        e = plan.seg_expert[seg];
+        row0 = plan.seg_row0[seg];
+        rows = plan.seg_rows[seg];
+        if (seg >= nseg) return;
+    }
+    // route index of the m-th row of this workgroup (shared expert: R + token)
+    auto route_of = [&](int m) -> int {
+        if (e < 0) return (SELF ? R : row0) + m;
+        return SELF ? rlist[m] : plan.sorted_route[row0 + m];
+    };
     const uint8_t* W13 = e >= 0 ? w13 + (size_t)e * 2 * I * H : sh_w13;
     const float* S13 = e >= 0 ? w13s + (size_t)e * (2 * I / 128) * (H / 128) : sh_w13s;
     const uint8_t* W2 = e >= 0 ? w2 + (size_t)e * H * I : sh_w2;
     const float* S2 = e >= 0 ? w2s + (size_t)e * (H / 128) * (I / 128) : sh_w2s;
 
-    extern __shared__ uint16_t a_lds[];  // [MROWS][I + 8] bf16 SwiGLU activations
-    const int astride = I + 8;  // +16 bytes per row: conflict-free 16-byte column reads
-    const int lane = lane_id(), wave = wave_id();
     const int ln = lane & 15, lg = lane >> 4;
-    const int R = T * k;
 
     const int nch1 = H >> 6, nch2 = I >> 6;  // chunks per group, both even
     const int kb1 = H >> 7, kb2 = I >> 7;    // scale blocks along K
@@ -247,7 +304,7 @@ __global__ __launch_bounds__(DF_THREADS) void decode_fused_kernel(
         for (int mt = 0; mt < MT; ++mt) {
             const int m = mp + mt * 16 + ln;
             int t = -1;
-            if (m < rows) t = e >= 0 ? plan.sorted_route[row0 + m] / k : row0 + m - R;
+            if (m < rows) t = e >= 0 ? route_of(m) / k : route_of(m) - R;
             xvalid[mt] = t >= 0;
             xp[mt] = x + (size_t)(t >= 0 ? t : 0) * H + lg * 16;
             ap[mt] = a_lds + (mt * 16 + ln) * astride + lg * 16;
@@ -257,7 +314,7 @@ __global__ __launch_bounds__(DF_THREADS) void decode_fused_kernel(
                 int r = -1;
                 float a = 0.0f;
                 if (mi < rows) {
-                    r = e >= 0 ? plan.sorted_route[row0 + mi] : row0 + mi;
+                    r = route_of(mi);
                     a = e >= 0 ? aff[r] : 1.0f;
                 }
                 yrow[mt][i] = r >= 0 ? ybuf + (size_t)r * H : ytrash;
@@ -296,24 +353,24 @@ __global__ __launch_bounds__(DF_THREADS) void decode_fused_kernel(
     }
 }
 
-template <int LAYOUT>
+template <int LAYOUT, bool SELF>
 static int launch_decode_fused_l(int MT, const uint16_t* x, const uint8_t* w13, const float* w13s,
                                  const uint8_t* w2, const float* w2s, const SharedW& sh,
-                                 const Plan& plan, const float* aff, int T, int H, int I, int E,
-                                 int k, float* ybuf, hipStream_t stream) {
+                                 const Plan& plan, const int32_t* ids, const float* aff, int T,
+                                 int H, int I, int E, int k, float* ybuf, hipStream_t stream) {
     const int nseg_max = E + (sh.w13 ? 1 : 0);
-    const size_t lds = sizeof(uint16_t) * (size_t)(16 * MT) * (I + 8);
+    const size_t lds = decode_fused_lds_bytes(MT, I, SELF ? T * k : 0);
     // the trash row sits right after the last real row of y
     float* ytrash = ybuf + ((size_t)T * k + (sh.w13 ? (size_t)T : 0)) * H;
     prof_begin("decode_fused_expert", stream);
     if (MT == 1)
-        decode_fused_kernel<1, 2, LAYOUT><<<nseg_max, DF_THREADS, lds, stream>>>(
-            x, w13, w13s, w2, w2s, sh.w13, sh.w13_scale, sh.w2, sh.w2_scale, plan, aff, T, H, I, k,
-            ybuf, ytrash);
+        decode_fused_kernel<1, 2, LAYOUT, SELF><<<nseg_max, DF_THREADS, lds, stream>>>(
+            x, w13, w13s, w2, w2s, sh.w13, sh.w13_scale, sh.w2, sh.w2_scale, plan, ids, E, aff, T,
+            H, I, k, ybuf, ytrash);
     else
-        decode_fused_kernel<2, 2, LAYOUT><<<nseg_max, DF_THREADS, lds, stream>>>(
-            x, w13, w13s, w2, w2s, sh.w13, sh.w13_scale, sh.w2, sh.w2_scale, plan, aff, T, H, I, k,
-            ybuf, ytrash);
+        decode_fused_kernel<2, 2, LAYOUT, SELF><<<nseg_max, DF_THREADS, lds, stream>>>(
+            x, w13, w13s, w2, w2s, sh.w13, sh.w13_scale, sh.w2, sh.w2_scale, plan, ids, E, aff, T,
+            H, I, k, ybuf, ytrash);
     prof_end(stream);
     return check_launch("decode_fused_kernel");
 }
@@ -325,10 +382,25 @@ int launch_decode_fused(int layout, int MT, const uint16_t* x, const uint8_t* w1
                         const Plan& plan, const float* aff, int T, int H, int I, int E, int k,
                         float* ybuf, hipStream_t stream) {
     if (layout == LAYOUT_TILED)
-        return launch_decode_fused_l<LAYOUT_TILED>(MT, x, w13, w13s, w2, w2s, sh, plan, aff, T, H,
-                                                   I, E, k, ybuf, stream);
-    return launch_decode_fused_l<LAYOUT_ROWMAJOR>(MT, x, w13, w13s, w2, w2s, sh, plan, aff, T, H,
-                                                  I, E, k, ybuf, stream);
+        return launch_decode_fused_l<LAYOUT_TILED, false>(MT, x, w13, w13s, w2, w2s, sh, plan,
+                                                          nullptr, aff, T, H, I, E, k, ybuf, stream);
+    return launch_decode_fused_l<LAYOUT_ROWMAJOR, false>(MT, x, w13, w13s, w2, w2s, sh, plan,
+                                                         nullptr, aff, T, H, I, E, k, ybuf, stream);
 }
+
+// The self-routed form: no sort beforehand; workgroup e scans the ids.
+int launch_decode_fused_self(int layout, int MT, const uint16_t* x, const uint8_t* w13,
+                             const float* w13s, const uint8_t* w2, const float* w2s,
+                             const SharedW& sh, const int32_t* ids, const float* aff, int T,
+                             int H, int I, int E, int k, float* ybuf, hipStream_t stream) {
+    const Plan none{};
+    if (layout == LAYOUT_TILED)
+        return launch_decode_fused_l<LAYOUT_TILED, true>(MT, x, w13, w13s, w2, w2s, sh, none, ids,
+                                                         aff, T, H, I, E, k, ybuf, stream);
+    return launch_decode_fused_l<LAYOUT_ROWMAJOR, true>(MT, x, w13, w13s, w2, w2s, sh, none, ids,
+                                                        aff, T, H, I, E, k, ybuf, stream);
+}
+
+int decode_self_routed_max_routes() { return DF_SELF_MAX_ROUTES; }
 
 }  // namespace moe

@@ -53,8 +53,21 @@ int launch_pack_w8(const uint8_t* src, uint8_t* dst, int64_t n_mats, int rows, i
                    hipStream_t stream);
 int prefill_tile_m();
 int prefill_supported(int H, int I);
-int launch_combine(const float* ybuf, const int32_t* inv_route, int T, int H, int k,
-                   int has_shared, float* out, hipStream_t stream);
+// Sums, per token, the k route rows whose id is valid (plus the shared row);
+// ids outside [0, E) set MOE_STATUS_BAD_EXPERT_ID in *status (if not NULL).
+int launch_combine(const float* ybuf, const int32_t* ids, int T, int H, int k, int E,
+                   int has_shared, int32_t* status, float* out, hipStream_t stream);
+// Decode variant helpers: the M tile, whether the fused one-workgroup-per-
+// expert kernel applies, and its self-routed form (no sort: each workgroup
+// scans the ids for its expert; at most decode_self_routed_max_routes() routes).
+int decode_mt(int T, int k, int E);
+bool decode_fused_fits(int T, int k, int E, int I, int has_shared, bool self_routed);
+size_t decode_fused_lds_bytes(int MT, int I, int self_routes);
+int decode_self_routed_max_routes();
+int launch_decode_fused_self(int layout, int MT, const uint16_t* x, const uint8_t* w13,
+                             const float* w13s, const uint8_t* w2, const float* w2s,
+                             const SharedW& sh, const int32_t* ids, const float* aff, int T,
+                             int H, int I, int E, int k, float* ybuf, hipStream_t stream);
 int launch_decode_e4m3fn(const uint8_t* codes, uint16_t* out, int64_t n, hipStream_t stream);
 int launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t stream);
 
