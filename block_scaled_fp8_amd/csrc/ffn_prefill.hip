@@ -145,12 +145,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
     }
     if (lin >= total) return;
     const int tile = lin / nblk, nb = lin - tile * nblk;
-    int lo = 0, hi = nseg - 1;  // last segment with seg_tile0 <= tile
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (plan.seg_tile0[mid] <= tile) lo = mid; else hi = mid - 1;
-    }
-    const int seg = lo;
+    const int seg = plan.tile_seg[tile];
     const int e = plan.seg_expert[seg];
     const int srow0 = plan.seg_row0[seg];
     const int srows = plan.seg_rows[seg];

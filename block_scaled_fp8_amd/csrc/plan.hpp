@@ -19,6 +19,7 @@ struct Plan {
     int32_t* seg_row0;      // [E+1] first row in sorted space
     int32_t* seg_rows;      // [E+1] rows in the segment
     int32_t* seg_tile0;     // [E+2] prefix of ceil(rows / tile_m)
+    int32_t* tile_seg;      // [seg_tile0[nseg]] segment of each tile, or null (not built)
 };
 
 // One expert's weights outside the routed arrays (the shared expert).

@@ -140,6 +140,14 @@ __device__ void build_segments(const int* cnt, const int* off, int E, int R, int
         plan.seg_tile0[nseg] = ntiles;
         plan.seg_n[0] = nseg;
     }
+    if (plan.tile_seg) {  // direct tile -> segment map (tiles[] holds the exclusive starts)
+        constexpr int NW = NT / MOE_WAVE;
+        const int w = tid / MOE_WAVE, lane = lane_id();
+        for (int s = w; s < nseg; s += NW) {
+            const int t1 = s + 1 < nseg ? tiles[s + 1] : ntiles;
+            for (int t = tiles[s] + lane; t < t1; t += MOE_WAVE) plan.tile_seg[t] = s;
+        }
+    }
 }
 
 // ------------------------------------------------------------------ small R
