@@ -236,6 +236,12 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_ffn_kernel(
 // multiplied each row by its affinity.  Source: AITER PR page (FP32 route
 // reduction); NKI page (affinity scale -> expert-sum, shared expert added after
 // the routed sum).
+// Sum of the k route rows of a token (slot order) plus its shared-expert row.
+// All loads are issued before any is used: the ids only select (a row of an
+// invalid route was never written and may hold anything, so it is masked, not
+// multiplied), which keeps one memory round trip per thread.  ybuf is read
+// once, so its loads bypass the caches' retention (non-temporal).
+template <int KMAX>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ ybuf,
                                                       const int32_t* __restrict__ ids,
                                                       int T, int H, int k, int E, int has_shared,
@@ -244,22 +250,35 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     const int t = blockIdx.y;
     const int h = (blockIdx.x * 256 + threadIdx.x) * 4;
     if (h >= H) return;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    bool bad = false;
-    for (int j = 0; j < k; ++j) {
-        const size_t r = (size_t)t * k + j;
-        const int id = ids[r];
-        if (id >= 0 && id < E)  // a route with an invalid id has no row (dropped)
-            acc += *reinterpret_cast<const f32x4*>(ybuf + r * H + h);
-        else
-            bad = true;
+    f32x4 v[KMAX];
+    int id[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+        if (j < k) {
+            const size_t r = (size_t)t * k + j;
+            id[j] = ids[r];
+            v[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(ybuf + r * H + h));
+        }
     }
-    if (bad && status && h == 0) atomicOr(status, MOE_STATUS_BAD_EXPERT_ID);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     if (has_shared) {
         const size_t R = (size_t)T * k;
-        acc += *reinterpret_cast<const f32x4*>(ybuf + (R + t) * H + h);
+        acc = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(ybuf + (R + t) * H + h));
     }
-    *reinterpret_cast<f32x4*>(out + (size_t)t * H + h) = acc;
+    f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+    bool bad = false;
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+        if (j < k) {
+            const bool ok = id[j] >= 0 && id[j] < E;  // an invalid id's route is dropped
+            bad |= !ok;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) sum[c] += ok ? v[j][c] : 0.0f;
+        }
+    }
+    if (bad && status && h == 0) atomicOr(status, MOE_STATUS_BAD_EXPERT_ID);
+    // routed sum in slot order first, then the shared expert
+    *reinterpret_cast<f32x4*>(out + (size_t)t * H + h) = sum + acc;
 }
 
 template <int MODE, int LAYOUT>
@@ -339,7 +358,11 @@ int launch_combine(const float* ybuf, const int32_t* ids, int T, int H, int k, i
                    int has_shared, int32_t* status, float* out, hipStream_t stream) {
     const dim3 grid((H / 4 + 255) / 256, T), block(256);
     prof_begin("combine", stream);
-    combine_kernel<<<grid, block, 0, stream>>>(ybuf, ids, T, H, k, E, has_shared, status, out);
+    if (k <= 8)
+        combine_kernel<8><<<grid, block, 0, stream>>>(ybuf, ids, T, H, k, E, has_shared, status, out);
+    else
+        combine_kernel<MOE_MAX_TOPK><<<grid, block, 0, stream>>>(ybuf, ids, T, H, k, E, has_shared,
+                                                                 status, out);
     prof_end(stream);
     return check_launch("combine_kernel");
 }
