@@ -21,7 +21,7 @@ namespace moe {
 
 constexpr int SORT_SMALL_THREADS = 1024;      // single-workgroup path
 constexpr int SORT_SMALL_MAX_ROUTES = 16384;
-constexpr int SORT_CHUNK = 4096;              // routes per workgroup, multi-workgroup path
+constexpr int SORT_CHUNK = 2048;              // routes per workgroup, multi-workgroup path
 constexpr int SORT_THREADS = 256;
 
 // Exclusive scan of arr[0..n) held in LDS, in place; returns the total.
@@ -230,23 +230,55 @@ __global__ __launch_bounds__(1024) void sort_scan_kernel(int T, int k, int E, in
     __shared__ int flags[MOE_MAX_EXPERTS + 2];
     __shared__ int tiles[MOE_MAX_EXPERTS + 2];
     __shared__ int tmp[NT / MOE_WAVE + 1];
-    const int R = T * k, tid = threadIdx.x;
-    for (int e = tid; e < E; e += NT) {
-        int run = 0;
-        int32_t* h = ghist + (size_t)e * nb;
-        for (int b = 0; b < nb; ++b) {
-            const int c = h[b];
-            h[b] = run;
-            run += c;
-        }
-        cnt[e] = run;
-        off[e] = run;
-    }
+    const int R = T * k, tid = threadIdx.x, lane = lane_id(), w = tid / MOE_WAVE;
+    constexpr int NW = NT / MOE_WAVE;
+    // one flat exclusive scan over the expert-major table (entry e*nb + b), in
+    // rounds of NT*V entries: thread tid takes V consecutive entries, all of
+    // them loaded before any is used (one memory round trip per round);
+    // per-expert totals come from LDS atomics (order-independent sums)
+    constexpr int V = 8;
+    for (int e = tid; e < E; e += NT) cnt[e] = 0;
     __syncthreads();
-    const int total = lds_excl_scan<NT>(off, E, tmp);
+    const int n = E * nb;
+    int carry = 0;  // the same in every thread
+    for (int base = 0; base < n; base += NT * V) {
+        const int i0 = base + tid * V;
+        int v[V];
+        int local = 0;
+#pragma unroll
+        for (int q = 0; q < V; ++q) {
+            v[q] = i0 + q < n ? ghist[i0 + q] : 0;
+            local += v[q];
+        }
+#pragma unroll
+        for (int q = 0; q < V; ++q)
+            if (v[q] != 0) atomicAdd(&cnt[(i0 + q) / nb], v[q]);
+        const int incl = wave_incl_scan_i32(local);
+        if (lane == MOE_WAVE - 1) tmp[w] = incl;
+        __syncthreads();
+        if (tid < MOE_WAVE) {
+            const int x = tid < NW ? tmp[tid] : 0;
+            const int sc = wave_incl_scan_i32(x);
+            if (tid < NW) tmp[tid] = sc - x;
+            if (tid == NW - 1) tmp[NW] = sc;
+        }
+        __syncthreads();
+        int run = carry + tmp[w] + incl - local;
+#pragma unroll
+        for (int q = 0; q < V; ++q) {
+            const int i = i0 + q;
+            if (i < n) {
+                ghist[i] = run;
+                if (i % nb == 0) off[i / nb] = run;  // expert e starts at its block 0
+            }
+            run += v[q];
+        }
+        carry += tmp[NW];
+        __syncthreads();  // tmp is rewritten by the next round
+    }
+    const int total = carry;
+    __syncthreads();
     for (int e = tid; e < E; e += NT) {
-        int32_t* h = ghist + (size_t)e * nb;
-        for (int b = 0; b < nb; ++b) h[b] += off[e];
         plan.counts[e] = cnt[e];
         plan.offsets[e] = off[e];
     }
