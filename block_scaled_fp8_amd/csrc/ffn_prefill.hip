@@ -462,6 +462,11 @@ int launch_prefill_ffn(int layout, const uint16_t* x, const uint8_t* w13, const 
         set_error("prefill variant needs H %% 256 == 0, 2I %% 256 == 0 and H, I <= 65536 (got H=%d, I=%d)", H, I);
         return MOE_EUNSUPPORTED;
     }
+    if (!plan.seg_n || !plan.seg_expert || !plan.seg_row0 || !plan.seg_rows || !plan.seg_tile0 ||
+        !plan.tile_seg || !plan.sorted_route) {
+        set_error("prefill variant needs the segment list and the tile map of the sort");
+        return MOE_EINVAL;
+    }
     if (layout == LAYOUT_TILED)
         return launch_prefill_c<LAYOUT_TILED, PfTile>(x, w13, w13s, w2, w2s, sh, plan, aff, T, H, I,
                                                       E, k, abuf, ybuf, stream);
