@@ -407,8 +407,11 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
             } else {
                 const float a = row_aff[row];
                 float* orow = ybuf + (size_t)dst * H + nb * BN + wn * 128 + ln;
+                // each contribution row is read once, by the combine: streaming
+                // (non-temporal) stores keep it from occupying the caches
 #pragma unroll
-                for (int nt = 0; nt < C::NT; ++nt) orow[nt * 32] = acc[mt][nt][i] * seff[0] * a;
+                for (int nt = 0; nt < C::NT; ++nt)
+                    __builtin_nontemporal_store(acc[mt][nt][i] * seff[0] * a, orow + nt * 32);
             }
         }
 }
