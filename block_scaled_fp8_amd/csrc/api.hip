@@ -233,7 +233,8 @@ int moe_fused_w8a16(const void* x, const uint8_t* w13, const float* w13_scale,
                                     H, I, E, k, abuf, ybuf, s);
     }
     if (rc) return rc;
-    return launch_combine(ybuf, ids, T, H, k, E, has_shared, status, out, s);
+    return launch_combine(ybuf, ids, variant == MOE_VARIANT_PREFILL ? p.inv_route : nullptr, T, H,
+                          k, E, has_shared, status, out, s);
 }
 
 int moe_pack_w8(const uint8_t* src, uint8_t* dst, int64_t n_mats, int rows, int cols,

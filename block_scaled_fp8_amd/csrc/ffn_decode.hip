@@ -241,9 +241,12 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_ffn_kernel(
 // invalid route was never written and may hold anything, so it is masked, not
 // multiplied), which keeps one memory round trip per thread.  ybuf is read
 // once, so its loads bypass the caches' retention (non-temporal).
-template <int KMAX>
+// GATHER: route r's row sits at inv_route[r] (the prefill producers write at
+// the sorted position); otherwise at r itself.
+template <int KMAX, bool GATHER>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ ybuf,
                                                       const int32_t* __restrict__ ids,
+                                                      const int32_t* __restrict__ inv_route,
                                                       int T, int H, int k, int E, int has_shared,
                                                       int32_t* __restrict__ status,
                                                       float* __restrict__ out) {
@@ -257,7 +260,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
         if (j < k) {
             const size_t r = (size_t)t * k + j;
             id[j] = ids[r];
-            v[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(ybuf + r * H + h));
+            const int p = GATHER ? inv_route[r] : (int)r;
+            const size_t row = p >= 0 ? (size_t)p : 0;  // a dropped route: any row, masked below
+            v[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(ybuf + row * H + h));
         }
     }
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -354,15 +359,25 @@ int launch_decode_ffn(int layout, const uint16_t* x, const uint8_t* w13, const f
                                          aff, T, H, I, k, abuf, ybuf, stream);
 }
 
-int launch_combine(const float* ybuf, const int32_t* ids, int T, int H, int k, int E,
-                   int has_shared, int32_t* status, float* out, hipStream_t stream) {
+int launch_combine(const float* ybuf, const int32_t* ids, const int32_t* inv_route, int T, int H,
+                   int k, int E, int has_shared, int32_t* status, float* out, hipStream_t stream) {
     const dim3 grid((H / 4 + 255) / 256, T), block(256);
     prof_begin("combine", stream);
-    if (k <= 8)
-        combine_kernel<8><<<grid, block, 0, stream>>>(ybuf, ids, T, H, k, E, has_shared, status, out);
-    else
-        combine_kernel<MOE_MAX_TOPK><<<grid, block, 0, stream>>>(ybuf, ids, T, H, k, E, has_shared,
-                                                                 status, out);
+    if (inv_route) {
+        if (k <= 8)
+            combine_kernel<8, true><<<grid, block, 0, stream>>>(ybuf, ids, inv_route, T, H, k, E,
+                                                                has_shared, status, out);
+        else
+            combine_kernel<MOE_MAX_TOPK, true><<<grid, block, 0, stream>>>(
+                ybuf, ids, inv_route, T, H, k, E, has_shared, status, out);
+    } else {
+        if (k <= 8)
+            combine_kernel<8, false><<<grid, block, 0, stream>>>(ybuf, ids, inv_route, T, H, k, E,
+                                                                 has_shared, status, out);
+        else
+            combine_kernel<MOE_MAX_TOPK, false><<<grid, block, 0, stream>>>(
+                ybuf, ids, inv_route, T, H, k, E, has_shared, status, out);
+    }
     prof_end(stream);
     return check_launch("combine_kernel");
 }

@@ -15,8 +15,9 @@
 // (128 gate + 128 up) tile of one segment, applies SwiGLU in registers and
 // writes bf16 activations (abuf, sorted row order).  Kernel 2 (down): each
 // workgroup computes a 128-row x 256-column tile of y = a W2^T, multiplies it
-// by the route's affinity and writes fp32 rows at the route's own index
-// r = t*k + j, so the final combine streams k contiguous rows per token.
+// by the route's affinity and writes fp32 rows at their sorted position (a
+// tile's rows are contiguous); the final combine gathers the k rows of a token
+// through the inverse route map.
 //
 //  * Workgroup tile 128 rows x 256 columns (gate/up: 128 gate + the matching
 //    128 up columns), 4 waves (2 x 2), each a 64 x 128 tile of
@@ -169,9 +170,10 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
                 dst = p;
             } else {
                 src = p;
-                const int r = e >= 0 ? plan.sorted_route[p] : p;
-                dst = r;
-                a = e >= 0 ? aff[r] : 1.0f;
+                // the contribution row goes to the sorted position: a tile
+                // writes contiguous rows; the combine gathers through inv_route
+                dst = p;
+                a = e >= 0 ? aff[plan.sorted_route[p]] : 1.0f;
             }
         }
         row_tok[tid] = src;

@@ -40,8 +40,9 @@ int launch_sort(const int32_t* ids, int T, int k, int E, const Plan& plan, int h
 int launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* aff,
                  int32_t* status, hipStream_t stream);
 // Both FFN variants write, for every valid route r = t*k + j, the row
-// y[r] = aff[r] * MLP_e(x_t) (fp32, H wide) and, for the shared expert, y[R + t];
-// the combine then sums k contiguous rows per token.
+// aff[r] * MLP_e(x_t) (fp32, H wide): the decode variant at y[r], the prefill
+// variant at its sorted position y[inv_route[r]]; the shared expert's row of
+// token t is y[R + t] in both.  The combine then sums the k rows of a token.
 int launch_decode_ffn(int layout, const uint16_t* x, const uint8_t* w13, const float* w13s,
                       const uint8_t* w2, const float* w2s, const SharedW& sh, const Plan& plan,
                       const float* aff, int T, int H, int I, int E, int k, uint16_t* abuf,
@@ -54,10 +55,12 @@ int launch_pack_w8(const uint8_t* src, uint8_t* dst, int64_t n_mats, int rows, i
                    hipStream_t stream);
 int prefill_tile_m();
 int prefill_supported(int H, int I);
-// Sums, per token, the k route rows whose id is valid (plus the shared row);
-// ids outside [0, E) set MOE_STATUS_BAD_EXPERT_ID in *status (if not NULL).
-int launch_combine(const float* ybuf, const int32_t* ids, int T, int H, int k, int E,
-                   int has_shared, int32_t* status, float* out, hipStream_t stream);
+// Sums, per token, the k route rows whose id is valid (plus the shared row at
+// R + t); route r's row is inv_route[r] when inv_route is given (prefill
+// producers write at the sorted position), else r.  Ids outside [0, E) set
+// MOE_STATUS_BAD_EXPERT_ID in *status (if not NULL).
+int launch_combine(const float* ybuf, const int32_t* ids, const int32_t* inv_route, int T, int H,
+                   int k, int E, int has_shared, int32_t* status, float* out, hipStream_t stream);
 // Decode variant helpers: the M tile, whether the fused one-workgroup-per-
 // expert kernel applies, and its self-routed form (no sort: each workgroup
 // scans the ids for its expert; at most decode_self_routed_max_routes() routes).
