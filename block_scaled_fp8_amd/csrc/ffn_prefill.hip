@@ -38,16 +38,21 @@
 //  * FP8 is converted exactly to bf16 after the LDS read; the fp32 block scale
 //    of each 128-wide K block is applied by rescaling the accumulators when the
 //    block starts (running scale), never by rounding it into bf16.
-//  * Work list: the sort builds per-segment tile prefixes; the grid covers the
-//    worst case and idle workgroups exit.  The real work list is split evenly
-//    over the 8 XCDs, each taking a contiguous range, so consecutive tiles
-//    (same expert, neighbouring rows) share one L2 and no XCD idles.
+//  * Work list: the sort lists every full 128-row tile first and the partial
+//    last tiles after them; XCD x takes row tiles x, x+8, ... (all column
+//    blocks of each), so every XCD gets an equal share of both kinds and the
+//    last round of workgroups holds the cheap partial tiles, whose empty
+//    32-row MFMA groups are skipped.  The grid covers the worst case and idle
+//    workgroups exit.
+#include <type_traits>
+
 #include "common.hpp"
 #include "plan.hpp"
 
 namespace moe {
 
 constexpr int PF_BK = 64;  // K per stage
+constexpr int PF_XCD_RUN = 8;  // consecutive row tiles an XCD takes at a time
 
 // Workgroup tile BM rows x BN columns, WM x WN waves of 64 x 128 each (2 x 4
 // MFMA tiles of 32 x 32), STAGES LDS stages of 64-wide K, OCC workgroups per
@@ -122,7 +127,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ abuf_in,
     const uint8_t* __restrict__ wexp, const float* __restrict__ sexp,
     const uint8_t* __restrict__ wsh, const float* __restrict__ ssh, Plan plan,
-    const float* __restrict__ aff, int T, int H, int I, int k, int nblk, int xcd_split,
+    const float* __restrict__ aff, int T, int H, int I, int k, int nblk,
     uint16_t* __restrict__ abuf_out, float* __restrict__ ybuf) {
     constexpr int BM = C::BM, BN = C::BN;
     extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -131,26 +136,26 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
     __shared__ float row_aff[BM];
 
     // ---- which tile.  Workgroups are dealt round-robin over the 8 XCDs
-    //      (id % 8); the real work list (tiles x column blocks, known only on
-    //      the device) is split into 8 contiguous ranges, one per XCD, so that
-    //      every XCD gets an equal share and neighbouring tiles of an expert
-    //      share one L2.  The grid covers the worst case; the rest exit.
+    //      (id % 8).  The sort's tile list is cut into blocks of PF_XCD_RUN
+    //      consecutive row tiles, dealt round-robin to the XCDs; XCD x walks
+    //      its blocks in order, each row tile with all its column blocks.  So
+    //      every XCD gets an equal share of the full tiles (listed first) and
+    //      of the partial ones (listed last: the last round of workgroups is
+    //      the cheapest), while consecutive tiles of one expert stay on one
+    //      XCD and share its weights in L2.  The grid covers the worst case;
+    //      the rest exit.
     const int bid = blockIdx.x;
     const int nseg = plan.seg_n[0];
-    const int total = plan.seg_tile0[nseg] * nblk;
-    int lin = bid;
-    if (xcd_split) {
-        const int chunk = (total + 7) >> 3;
-        if ((bid >> 3) >= chunk) return;
-        lin = (bid & 7) * chunk + (bid >> 3);
-    }
-    if (lin >= total) return;
-    const int tile = lin / nblk, nb = lin - tile * nblk;
+    const int ntiles = plan.seg_tile0[nseg];
+    const int jx = bid >> 3, q = jx / nblk;
+    const int tile = (q / PF_XCD_RUN) * (8 * PF_XCD_RUN) + (bid & 7) * PF_XCD_RUN + q % PF_XCD_RUN;
+    const int nb = jx - q * nblk;
+    if (tile >= ntiles) return;
     const int seg = plan.tile_seg[tile];
+    const int m0 = plan.tile_row[tile];  // first row inside the segment
     const int e = plan.seg_expert[seg];
     const int srow0 = plan.seg_row0[seg];
     const int srows = plan.seg_rows[seg];
-    const int m0 = (tile - plan.seg_tile0[seg]) * BM;  // first row inside the segment
 
     const int K = MODE == PF_GATEUP ? H : I;
     const int Nrows = MODE == PF_GATEUP ? 2 * I : H;     // rows of the weight matrix
@@ -300,27 +305,36 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
     //      around the LDS reads, so their waits stay partial.
     const int nk = K / PF_BK;  // even and >= 2 since K % 128 == 0
     constexpr int PER_STAGE = C::A_INSTR + C::B_INSTR;
+    // MFMA row groups (32 rows) of this wave that hold rows of the segment:
+    // a partial last tile skips the empty ones (their rows are never stored)
+    const int rows_here = min(srows - m0, BM);
+    const int mt_active =
+        __builtin_amdgcn_readfirstlane(min(C::MT, max(0, rows_here - wm * (BM / C::WM) + 31) >> 5));
+    auto kloop = [&](auto mta_c) {
+    constexpr int MTA = decltype(mta_c)::value;
     u32x4 ah[2][C::MT][2], bh[2][C::NT];
     auto read_half = [&](int stage, int p, u32x4 (&a)[C::MT][2], u32x4 (&b)[C::NT]) {
         const char* st = smem + stage * C::STAGE;
 #pragma unroll
-        for (int mt = 0; mt < C::MT; ++mt)
+        for (int mt = 0; mt < MTA; ++mt)
 #pragma unroll
             for (int j = 0; j < 2; ++j) a[mt][j] = *reinterpret_cast<const u32x4*>(st + a_off[mt][2 * p + j]);
+        if (MTA > 0)
 #pragma unroll
-        for (int nt = 0; nt < C::NT; ++nt) b[nt] = *reinterpret_cast<const u32x4*>(st + b_off[nt][p]);
+            for (int nt = 0; nt < C::NT; ++nt) b[nt] = *reinterpret_cast<const u32x4*>(st + b_off[nt][p]);
     };
     // Sub-step j of a half.  rescale: the half opens a new K block, and each
     // accumulator is multiplied by its group's factor right before its first
     // MFMA of the block.
     auto mma_sub = [&](const u32x4 (&a)[C::MT][2], const u32x4 (&b)[C::NT], int j, bool rescale,
                        const float (&rr)[2]) {
+        if (MTA == 0) return;
 #pragma unroll
         for (int nt = 0; nt < C::NT; ++nt) {
             const bf16x8 bf = j == 0 ? fp8x8_to_bf16x8(b[nt][0], b[nt][1]) : fp8x8_to_bf16x8(b[nt][2], b[nt][3]);
             const float f = MODE == PF_GATEUP ? rr[nt >> 1] : rr[0];
 #pragma unroll
-            for (int mt = 0; mt < C::MT; ++mt) {
+            for (int mt = 0; mt < MTA; ++mt) {
                 if (rescale)
 #pragma unroll
                     for (int i = 0; i < 16; ++i) acc[mt][nt][i] *= f;
@@ -390,6 +404,10 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
         mma_sub(ah[1], bh[1], 1, false, one);
         __builtin_amdgcn_sched_barrier(0);
     }
+    };
+    if (mt_active >= 2) kloop(std::integral_constant<int, 2>{});
+    else if (mt_active == 1) kloop(std::integral_constant<int, 1>{});
+    else kloop(std::integral_constant<int, 0>{});
 
     // ---- epilogue. 32x32 accumulator layout: lane l holds column l%32 and,
     //      for register i, row 8*(i/4) + 4*(l/32) + i%4.
@@ -429,9 +447,8 @@ static int launch_pf(const uint16_t* x, const uint16_t* abuf_in, const uint8_t* 
     const int nblk = MODE == PF_GATEUP ? 2 * I / C::BN : H / C::BN;
     const long R = (long)T * k;
     const long max_tiles = (R + C::BM - 1) / C::BM + E + (has_shared ? (T + C::BM - 1) / C::BM : 0);
-    long grid = max_tiles * nblk;
-    if (grid % 8 != 0) grid += 8 - grid % 8;  // 8 * ceil(total / 8) <= grid for any total <= grid
-    const int xcd_split = 1;
+    // XCD x's workgroup j handles the (j / nblk)-th row tile of its blocks
+    const long grid = 8L * nblk * PF_XCD_RUN * ((max_tiles + 8 * PF_XCD_RUN - 1) / (8 * PF_XCD_RUN));
     if (grid > 0x7FFFFFFFL) {
         set_error("prefill: too many tiles");
         return MOE_EUNSUPPORTED;
@@ -440,7 +457,7 @@ static int launch_pf(const uint16_t* x, const uint16_t* abuf_in, const uint8_t* 
     const size_t lds = (size_t)C::STAGES * C::STAGE + (size_t)(C::BN / 128) * kbp * 4;
     prof_begin(MODE == PF_GATEUP ? "prefill_gateup_swiglu" : "prefill_down", stream);
     prefill_gemm_kernel<MODE, LAYOUT, C><<<(unsigned)grid, C::THREADS, lds, stream>>>(
-        x, abuf_in, wexp, sexp, wsh, ssh, plan, aff, T, H, I, k, nblk, xcd_split, abuf_out, ybuf);
+        x, abuf_in, wexp, sexp, wsh, ssh, plan, aff, T, H, I, k, nblk, abuf_out, ybuf);
     prof_end(stream);
     return check_launch(MODE == PF_GATEUP ? "prefill_gemm_kernel<gateup>" : "prefill_gemm_kernel<down>");
 }
@@ -468,7 +485,7 @@ int launch_prefill_ffn(int layout, const uint16_t* x, const uint8_t* w13, const 
         return MOE_EUNSUPPORTED;
     }
     if (!plan.seg_n || !plan.seg_expert || !plan.seg_row0 || !plan.seg_rows || !plan.seg_tile0 ||
-        !plan.tile_seg || !plan.sorted_route) {
+        !plan.tile_seg || !plan.tile_row || !plan.sorted_route) {
         set_error("prefill variant needs the segment list and the tile map of the sort");
         return MOE_EINVAL;
     }

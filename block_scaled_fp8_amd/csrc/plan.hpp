@@ -19,7 +19,12 @@ struct Plan {
     int32_t* seg_row0;      // [E+1] first row in sorted space
     int32_t* seg_rows;      // [E+1] rows in the segment
     int32_t* seg_tile0;     // [E+2] prefix of ceil(rows / tile_m)
-    int32_t* tile_seg;      // [seg_tile0[nseg]] segment of each tile, or null (not built)
+    // Tile list of the prefill variant, or null (not built): every full tile
+    // of every segment in segment order, then the partial last tiles (in
+    // segment order).  tile_seg[i] is the segment, tile_row[i] the first row
+    // of tile i inside its segment.
+    int32_t* tile_seg;      // [seg_tile0[nseg]]
+    int32_t* tile_row;      // [seg_tile0[nseg]]
 };
 
 // One expert's weights outside the routed arrays (the shared expert).
