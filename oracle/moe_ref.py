@@ -22,7 +22,7 @@ Sources (page title, then section):
   PR #5988), description: tokens sorted by expert with an inverse route map,
   an FP32 route reduction, and one always-on shared expert.
 
-Readings where the pages are silent (each one is listed in the design doc):
+Readings where the pages are silent:
 
 * selection is taken on the fp32 logits (softmax is strictly increasing, so the
   chosen set is the same as on the probabilities), ties go to the lower expert
