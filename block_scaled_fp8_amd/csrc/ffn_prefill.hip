@@ -71,7 +71,11 @@ struct PfCfg {
     static constexpr int B_INSTR = B_BYTES / 1024 / WAVES;
     static constexpr int MT = BM / WM / 32;
     static constexpr int NT = BN / WN / 32;
-    static_assert(BM / WM == 64 && BN / WN == 128, "wave tile is 64 x 128");
+    static constexpr int WROWS = BM / WM;  // rows of a wave tile
+    // 64 x 128: the running-scale rescale needs the 128 accumulators in
+    // architectural VGPRs beside the operand fragments (a 128-row wave tile
+    // does not fit)
+    static_assert(WROWS == 64 && BN / WN == 128, "wave tile is 64 x 128");
     static_assert(BM == 128, "tile prefixes are built for 128-row tiles");
     static_assert(A_INSTR >= 1 && B_INSTR >= 1, "every wave issues loads");
 };
@@ -236,7 +240,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
     uint32_t a_off[C::MT][4];
 #pragma unroll
     for (int mt = 0; mt < C::MT; ++mt) {
-        const int row = wm * 64 + mt * 32 + ln;
+        const int row = wm * C::WROWS + mt * 32 + ln;
 #pragma unroll
         for (int s = 0; s < 4; ++s) a_off[mt][s] = row * 128 + (((4 * lg + s) ^ ((row >> 1) & 7)) * 16);
     }
@@ -309,7 +313,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
     // a partial last tile skips the empty ones (their rows are never stored)
     const int rows_here = min(srows - m0, BM);
     const int mt_active =
-        __builtin_amdgcn_readfirstlane(min(C::MT, max(0, rows_here - wm * (BM / C::WM) + 31) >> 5));
+        __builtin_amdgcn_readfirstlane(min(C::MT, max(0, rows_here - wm * C::WROWS + 31) >> 5));
     auto kloop = [&](auto mta_c) {
     constexpr int MTA = decltype(mta_c)::value;
     u32x4 ah[2][C::MT][2], bh[2][C::NT];
@@ -415,7 +419,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
     for (int mt = 0; mt < C::MT; ++mt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            const int row = wm * 64 + mt * 32 + 8 * (i >> 2) + 4 * lg + (i & 3);
+            const int row = wm * C::WROWS + mt * 32 + 8 * (i >> 2) + 4 * lg + (i & 3);
             const int dst = row_dst[row];
             if (dst < 0) continue;
             if (MODE == PF_GATEUP) {
