@@ -35,7 +35,8 @@ __device__ __forceinline__ float from_ordered(uint32_t o) {
 #define MOE_DPP_ROR4 0x124
 #define MOE_DPP_ROR8 0x128
 
-__device__ __forceinline__ uint32_t dpp_max(uint32_t v, int ctrl) {
+template <bool MAX>
+__device__ __forceinline__ uint32_t dpp_red(uint32_t v, int ctrl) {
     uint32_t o = 0;
     switch (ctrl) {  // the control must be a literal
         case MOE_DPP_QP_1032: o = __builtin_amdgcn_update_dpp(0, (int)v, MOE_DPP_QP_1032, 0xF, 0xF, false); break;
@@ -43,29 +44,38 @@ __device__ __forceinline__ uint32_t dpp_max(uint32_t v, int ctrl) {
         case MOE_DPP_ROR4: o = __builtin_amdgcn_update_dpp(0, (int)v, MOE_DPP_ROR4, 0xF, 0xF, false); break;
         default: o = __builtin_amdgcn_update_dpp(0, (int)v, MOE_DPP_ROR8, 0xF, 0xF, false); break;
     }
-    return o > v ? o : v;
+    return MAX ? (o > v ? o : v) : (o < v ? o : v);
 }
 
-// Wave-wide maximum, returned as a wave-uniform value: a butterfly inside each
-// 16-lane row (DPP), then the four row maxima read as scalars.
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-    v = dpp_max(v, MOE_DPP_QP_1032);
-    v = dpp_max(v, MOE_DPP_QP_2301);
-    v = dpp_max(v, MOE_DPP_ROR4);
-    v = dpp_max(v, MOE_DPP_ROR8);
+// Wave-wide maximum (MAX) or minimum, returned as a wave-uniform value: a
+// butterfly inside each 16-lane row (DPP), then the four row results read as
+// scalars.
+template <bool MAX>
+__device__ __forceinline__ uint32_t wave_red_u32(uint32_t v) {
+    v = dpp_red<MAX>(v, MOE_DPP_QP_1032);
+    v = dpp_red<MAX>(v, MOE_DPP_QP_2301);
+    v = dpp_red<MAX>(v, MOE_DPP_ROR4);
+    v = dpp_red<MAX>(v, MOE_DPP_ROR8);
     const uint32_t r0 = __builtin_amdgcn_readlane((int)v, 0);
     const uint32_t r1 = __builtin_amdgcn_readlane((int)v, 16);
     const uint32_t r2 = __builtin_amdgcn_readlane((int)v, 32);
     const uint32_t r3 = __builtin_amdgcn_readlane((int)v, 48);
-    const uint32_t a = r0 > r1 ? r0 : r1, b = r2 > r3 ? r2 : r3;
-    return a > b ? a : b;
+    if (MAX) {
+        const uint32_t a = r0 > r1 ? r0 : r1, b = r2 > r3 ? r2 : r3;
+        return a > b ? a : b;
+    }
+    const uint32_t a = r0 < r1 ? r0 : r1, b = r2 < r3 ? r2 : r3;
+    return a < b ? a : b;
 }
 
-// Each of the k passes takes the wave-wide maximum of the ordered logit bits,
-// then the lowest expert index holding that maximum (one ballot per register
-// slot: slot i holds experts 64*i + lane, so the first slot with a hit and its
-// lowest lane give the lowest index).  The chosen entry leaves the candidate
-// set; padding entries are never candidates.
+// Selection.  Each lane first orders its own NPL entries (slot i holds expert
+// 64*i + lane) by key, larger first and lower slot first among equal keys, so
+// its head is its best remaining candidate.  Each of the k passes then takes
+// the wave-wide maximum of the lane heads; when one lane holds it, that
+// lane's head is the choice, and when several lanes tie, the lowest expert
+// index among their heads (a wave minimum).  Either way the chosen entry is
+// the largest key with the lowest expert index, and it leaves its lane's list.
+// Padding entries (expert >= E) are never candidates.
 template <int NPL>
 __global__ __launch_bounds__(256) void route_topk_softmax_kernel(
     const float* __restrict__ logits, int T, int E, int k,
@@ -75,36 +85,57 @@ __global__ __launch_bounds__(256) void route_topk_softmax_kernel(
     if (t >= T) return;
     const float* row = logits + (size_t)t * E;
 
-    uint32_t o[NPL];
-    bool cand[NPL];
+    uint32_t key[NPL];
+    int slot[NPL];  // -1: no candidate
     bool bad = false;
 #pragma unroll
     for (int i = 0; i < NPL; ++i) {
         const int e = lane + MOE_WAVE * i;
-        cand[i] = e < E;
-        const float v = cand[i] ? row[e] : 0.0f;
-        bad |= cand[i] && !__builtin_isfinite(v);
-        o[i] = cand[i] ? ordered_bits(v) : 0u;
+        const bool in = e < E;
+        const float v = in ? row[e] : 0.0f;
+        bad |= in && !__builtin_isfinite(v);
+        key[i] = in ? ordered_bits(v) : 0u;
+        slot[i] = in ? i : -1;
     }
     if (status && __ballot(bad) != 0ull && lane == 0) atomicOr(status, MOE_STATUS_NONFINITE_LOGIT);
+    // insertion order of (key desc, slot asc); empty entries (slot -1) last
+#pragma unroll
+    for (int a = 1; a < NPL; ++a)
+#pragma unroll
+        for (int b = a; b > 0; --b) {
+            const bool lo_empty = slot[b - 1] < 0, hi_full = slot[b] >= 0;
+            const bool sw = hi_full && (lo_empty || key[b] > key[b - 1] ||
+                                        (key[b] == key[b - 1] && slot[b] < slot[b - 1]));
+            const uint32_t k0 = key[b - 1], k1 = key[b];
+            const int s0 = slot[b - 1], s1 = slot[b];
+            key[b - 1] = sw ? k1 : k0;
+            key[b] = sw ? k0 : k1;
+            slot[b - 1] = sw ? s1 : s0;
+            slot[b] = sw ? s0 : s1;
+        }
 
     uint32_t my_o = 0, top_o = 0;
     int my_id = 0;
     for (int j = 0; j < k; ++j) {
-        uint32_t best = 0;
-#pragma unroll
-        for (int i = 0; i < NPL; ++i)
-            if (cand[i] && o[i] > best) best = o[i];
-        const uint32_t gmax = wave_max_u32(best);
-        int sel = -1;
-#pragma unroll
-        for (int i = 0; i < NPL; ++i) {
-            const uint64_t hit = __ballot(cand[i] && o[i] == gmax);
-            if (sel < 0 && hit != 0ull) sel = __builtin_ctzll(hit) + MOE_WAVE * i;
+        const bool has = slot[0] >= 0;
+        const uint32_t gmax = wave_red_u32<true>(has ? key[0] : 0u);
+        const bool at = has && key[0] == gmax;
+        const uint64_t hit = __ballot(at);
+        int sel;
+        if (__popcll(hit) == 1) {
+            const int wl = (int)__builtin_ctzll(hit);
+            sel = __builtin_amdgcn_readlane(slot[0], wl) * MOE_WAVE + wl;
+        } else {  // equal keys in several lanes: the lowest expert index
+            sel = (int)wave_red_u32<false>(at ? (uint32_t)(slot[0] * MOE_WAVE + lane) : 0xFFFFFFFFu);
         }
+        if (lane == (sel & (MOE_WAVE - 1))) {  // the winner drops its head
 #pragma unroll
-        for (int i = 0; i < NPL; ++i)
-            if (lane + MOE_WAVE * i == sel) cand[i] = false;
+            for (int i = 0; i + 1 < NPL; ++i) {
+                key[i] = key[i + 1];
+                slot[i] = slot[i + 1];
+            }
+            slot[NPL - 1] = -1;
+        }
         if (j == 0) top_o = gmax;
         if (lane == j) {
             my_id = sel;
