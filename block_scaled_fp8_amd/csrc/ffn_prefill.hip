@@ -39,11 +39,14 @@
 //    of each 128-wide K block is applied by rescaling the accumulators when the
 //    block starts (running scale), never by rounding it into bf16.
 //  * Work list: the sort lists every full 128-row tile first and the partial
-//    last tiles after them; XCD x takes row tiles x, x+8, ... (all column
-//    blocks of each), so every XCD gets an equal share of both kinds and the
-//    last round of workgroups holds the cheap partial tiles, whose empty
-//    32-row MFMA groups are skipped.  The grid covers the worst case and idle
-//    workgroups exit.
+//    last tiles after them; the list is cut into runs of 8 row tiles dealt
+//    round-robin to the 8 XCDs (all column blocks of a row tile on one XCD),
+//    so every XCD gets an equal share of both kinds and the last round of
+//    workgroups holds the cheap partial tiles, whose empty 32-row MFMA groups
+//    are skipped.  The grid covers the worst case and idle workgroups exit.
+//  * Epilogue: a lane's row-table entries come in 16-byte LDS reads before
+//    any store (gate/up: SwiGLU, bf16 stores; down: affinity scale, fp32
+//    non-temporal stores).
 #include <type_traits>
 
 #include "common.hpp"
@@ -72,10 +75,14 @@ struct PfCfg {
     static constexpr int MT = BM / WM / 32;
     static constexpr int NT = BN / WN / 32;
     static constexpr int WROWS = BM / WM;  // rows of a wave tile
-    // 64 x 128: the running-scale rescale needs the 128 accumulators in
-    // architectural VGPRs beside the operand fragments (a 128-row wave tile
-    // does not fit)
-    static_assert(WROWS == 64 && BN / WN == 128, "wave tile is 64 x 128");
+    static constexpr int WCOLS = BN / WN;  // columns of a wave tile
+    // 64 x 128, 128 fp32 accumulators per lane: the running-scale rescale
+    // needs them in architectural VGPRs beside the operand fragments, so a
+    // 128 x 128 wave tile does not fit; 128 x 64 (each weight converted by one
+    // wave instead of two, activations read twice as often) measured slower.
+    // Gate/up: a wave's columns are 64 gate and the matching 64 up columns,
+    // each half inside one 128-column scale block.
+    static_assert(WROWS == 64 && WCOLS == 128, "wave tile is 64 x 128");
     static_assert(BM == 128, "tile prefixes are built for 128-row tiles");
     static_assert(A_INSTR >= 1 && B_INSTR >= 1, "every wave issues loads");
 };
@@ -135,9 +142,9 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
     uint16_t* __restrict__ abuf_out, float* __restrict__ ybuf) {
     constexpr int BM = C::BM, BN = C::BN;
     extern __shared__ __attribute__((aligned(16))) char smem[];
-    __shared__ int row_tok[BM];     // activation row source (token or abuf row)
-    __shared__ int row_dst[BM];     // output row (abuf row / route index), -1 if padding
-    __shared__ float row_aff[BM];
+    __shared__ int row_tok[BM];  // activation row source (token or abuf row)
+    __shared__ __attribute__((aligned(16))) int row_dst[BM];  // output row, -1 if padding
+    __shared__ __attribute__((aligned(16))) float row_aff[BM];
 
     // ---- which tile.  Workgroups are dealt round-robin over the 8 XCDs
     //      (id % 8).  The sort's tile list is cut into blocks of PF_XCD_RUN
@@ -232,31 +239,37 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
                        smem);
     };
 
-    // ---- wave tile: rows wm*64 .. +64, columns wn*128 .. +128 of the WG tile
+    // ---- wave tile: rows wm*WROWS .. +WROWS, columns wn*WCOLS .. +WCOLS of
+    //      the WG tile
     const int wm = wave / C::WN;
     const int wn = wave % C::WN;
     const int ln = lane & 31, lg = lane >> 5;
-    // LDS byte offsets of this lane's operand pieces inside a stage
-    uint32_t a_off[C::MT][4];
+    // LDS byte offsets of this lane's operand pieces inside a stage, for the
+    // first 32-row / 32-column MFMA tile; the others sit at constant distances
+    // (a_step, b_step), which the LDS reads take as immediate offsets.
+    // Activation piece s (16 K) of row r: the swizzle (r / 2) % 8 is the same
+    // for rows 32 apart.
+    uint32_t a_off[4];
+    {
+        const int row = wm * C::WROWS + ln;
 #pragma unroll
-    for (int mt = 0; mt < C::MT; ++mt) {
-        const int row = wm * C::WROWS + mt * 32 + ln;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) a_off[mt][s] = row * 128 + (((4 * lg + s) ^ ((row >> 1) & 7)) * 16);
+        for (int s = 0; s < 4; ++s) a_off[s] = row * 128 + (((4 * lg + s) ^ ((row >> 1) & 7)) * 16);
     }
-    // weight LDS tiles of each 32-column MFMA tile (MODE 0: nt 0,1 gate, 2,3 the matching up)
-    uint32_t b_off[C::NT][2];
-#pragma unroll
-    for (int nt = 0; nt < C::NT; ++nt) {
-        int t16;
-        if (MODE == PF_GATEUP)
-            t16 = (nt < 2 ? 0 : HALF_T) + wn * 4 + (nt & 1) * 2;
-        else
-            t16 = wn * 8 + nt * 2;
+    // weights: 32-column MFMA tile nt spans 16-row tiles t16(nt), t16(nt) + 1
+    // (MODE 0: the first NT/2 tiles are gate columns, the rest the matching up
+    // columns); the lane's 16 bytes for half p sit p * 256 bytes further on
+    uint32_t b_off;
+    {
+        const int t16 = MODE == PF_GATEUP ? wn * (C::WCOLS / 32) : wn * (C::WCOLS / 16);
         const int tt = t16 + (ln >> 4), r = ln & 15;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) b_off[nt][h] = C::A_BYTES + tt * 1024 + ((2 * lg + h) * 16 + r) * 16;
+        b_off = C::A_BYTES + tt * 1024 + (2 * lg * 16 + r) * 16;
     }
+    auto a_step = [](int mt) { return mt * 32 * 128; };
+    auto b_step = [](int nt) {
+        if (MODE == PF_GATEUP)
+            return ((nt < C::NT / 2 ? 0 : HALF_T) + (nt % (C::NT / 2)) * 2) * 1024;
+        return nt * 2 * 1024;
+    };
     // ---- block scales of the workgroup's columns, staged once in LDS by
     //      direct-to-LDS loads issued before the first operand stages (so the
     //      first stage wait covers them).  Table row j < NR/2 (MODE 0: gate;
@@ -283,10 +296,10 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
     // this wave's table rows: g = 0 its gate (or only) columns, g = 1 its up columns
     int sj[2];
     if (MODE == PF_GATEUP) {
-        sj[0] = (wn * 64) >> 7;
+        sj[0] = (wn * (C::WCOLS / 2)) >> 7;
         sj[1] = NR / 2 + sj[0];
     } else {
-        sj[0] = sj[1] = (wn * 128) >> 7;
+        sj[0] = sj[1] = (wn * C::WCOLS) >> 7;
     }
 
     f32x16 acc[C::MT][C::NT];
@@ -322,10 +335,12 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
 #pragma unroll
         for (int mt = 0; mt < MTA; ++mt)
 #pragma unroll
-            for (int j = 0; j < 2; ++j) a[mt][j] = *reinterpret_cast<const u32x4*>(st + a_off[mt][2 * p + j]);
+            for (int j = 0; j < 2; ++j)
+                a[mt][j] = *reinterpret_cast<const u32x4*>(st + a_off[2 * p + j] + a_step(mt));
         if (MTA > 0)
 #pragma unroll
-            for (int nt = 0; nt < C::NT; ++nt) b[nt] = *reinterpret_cast<const u32x4*>(st + b_off[nt][p]);
+            for (int nt = 0; nt < C::NT; ++nt)
+                b[nt] = *reinterpret_cast<const u32x4*>(st + b_off + p * 256 + b_step(nt));
     };
     // Sub-step j of a half.  rescale: the half opens a new K block, and each
     // accumulator is multiplied by its group's factor right before its first
@@ -336,7 +351,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
 #pragma unroll
         for (int nt = 0; nt < C::NT; ++nt) {
             const bf16x8 bf = j == 0 ? fp8x8_to_bf16x8(b[nt][0], b[nt][1]) : fp8x8_to_bf16x8(b[nt][2], b[nt][3]);
-            const float f = MODE == PF_GATEUP ? rr[nt >> 1] : rr[0];
+            const float f = MODE == PF_GATEUP ? rr[nt / (C::NT / 2)] : rr[0];
 #pragma unroll
             for (int mt = 0; mt < MTA; ++mt) {
                 if (rescale)
@@ -414,23 +429,35 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
     else kloop(std::integral_constant<int, 0>{});
 
     // ---- epilogue. 32x32 accumulator layout: lane l holds column l%32 and,
-    //      for register i, row 8*(i/4) + 4*(l/32) + i%4.
+    //      for register i, row 8*(i/4) + 4*(l/32) + i%4.  The row table
+    //      entries of a lane's rows (four consecutive rows per i/4) are read
+    //      with 16-byte LDS reads, all before the first store, so the stores
+    //      do not wait on LDS one row at a time.
+    int4 dst4[C::MT][4];
+    float4 aff4[C::MT][4];
+#pragma unroll
+    for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int r0 = wm * C::WROWS + mt * 32 + 8 * q + 4 * lg;
+            dst4[mt][q] = *reinterpret_cast<const int4*>(row_dst + r0);
+            if (MODE == PF_DOWN) aff4[mt][q] = *reinterpret_cast<const float4*>(row_aff + r0);
+        }
 #pragma unroll
     for (int mt = 0; mt < C::MT; ++mt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            const int row = wm * C::WROWS + mt * 32 + 8 * (i >> 2) + 4 * lg + (i & 3);
-            const int dst = row_dst[row];
+            const int dst = dst4[mt][i >> 2][i & 3];
             if (dst < 0) continue;
             if (MODE == PF_GATEUP) {
-                uint16_t* orow = abuf_out + (size_t)dst * I + nb * (BN / 2) + wn * 64 + ln;
+                uint16_t* orow = abuf_out + (size_t)dst * I + nb * (BN / 2) + wn * (C::WCOLS / 2) + ln;
 #pragma unroll
-                for (int nt = 0; nt < 2; ++nt)
+                for (int nt = 0; nt < C::NT / 2; ++nt)
                     orow[nt * 32] = f32_to_bf16_bits(
-                        swiglu_fast(acc[mt][nt][i] * seff[0], acc[mt][nt + 2][i] * seff[1]));
+                        swiglu_fast(acc[mt][nt][i] * seff[0], acc[mt][nt + C::NT / 2][i] * seff[1]));
             } else {
-                const float a = row_aff[row];
-                float* orow = ybuf + (size_t)dst * H + nb * BN + wn * 128 + ln;
+                const float a = aff4[mt][i >> 2][i & 3];
+                float* orow = ybuf + (size_t)dst * H + nb * BN + wn * C::WCOLS + ln;
                 // each contribution row is read once, by the combine: streaming
                 // (non-temporal) stores keep it from occupying the caches
 #pragma unroll
