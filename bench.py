@@ -235,7 +235,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill-workload", default="prefill8k_skew",
                     help="secondary MFMA-bound workload reported in the 'prefill' object ('' = skip)")
-    ap.add_argument("--prefill-steps", type=int, default=20)
+    ap.add_argument("--prefill-steps", type=int, default=50)
+    ap.add_argument("--prefill-warmup", type=int, default=50,
+                    help="untimed prefill steps first: the GPU idles while the prefill inputs "
+                         "are generated, and its clock needs some milliseconds of work to settle")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB, 5 times (PMC byte-counter "
@@ -316,7 +319,8 @@ def main():
         pcfg = synth.CONFIGS[args.prefill_workload]
         del m
         torch.cuda.empty_cache()
-        pm = measure(pcfg, 2, args.prefill_steps, 3, "auto", args.layout, args.seed, dev)
+        pm = measure(pcfg, 2, args.prefill_steps, args.prefill_warmup, "auto", args.layout,
+                     args.seed, dev)
         result["prefill"] = prefill_summary(pcfg, pm)
         del pm
         torch.cuda.empty_cache()

@@ -35,7 +35,7 @@ int check_launch(const char* what) {
 // Workspace carve-up for moe_fused_w8a16 (256-byte aligned pieces).
 struct FusedLayout {
     size_t counts, offsets, sorted_route, inv_route, seg_n, seg_expert, seg_row0, seg_rows,
-        seg_tile0, tile_seg, tile_row, sort_scratch, abuf, ybuf, total;
+        seg_tile0, tile_info, tile_n, sort_scratch, abuf, ybuf, total;
 };
 
 static FusedLayout fused_layout(int T, int H, int I, int E, int k, int has_shared) {
@@ -60,8 +60,8 @@ static FusedLayout fused_layout(int T, int H, int I, int E, int k, int has_share
     // prefill tiles: at most ceil(R / tile) + one partial tile per segment
     const size_t tm = (size_t)prefill_tile_m();
     const size_t max_tiles = (R + tm - 1) / tm + E + 1 + (has_shared ? ((size_t)T + tm - 1) / tm : 0);
-    L.tile_seg = take(sizeof(int32_t) * max_tiles);
-    L.tile_row = take(sizeof(int32_t) * max_tiles);
+    L.tile_info = take(sizeof(int4) * max_tiles);
+    L.tile_n = take(sizeof(int32_t));
     L.sort_scratch = take(sort_scratch_bytes((int)R, E));
     L.abuf = take(sizeof(uint16_t) * rows * I);
     L.ybuf = take(sizeof(float) * (rows + 1) * H);  // + one trash row for padded stores
@@ -209,8 +209,8 @@ int moe_fused_w8a16(const void* x, const uint8_t* w13, const float* w13_scale,
     p.seg_row0 = reinterpret_cast<int32_t*>(base + L.seg_row0);
     p.seg_rows = reinterpret_cast<int32_t*>(base + L.seg_rows);
     p.seg_tile0 = reinterpret_cast<int32_t*>(base + L.seg_tile0);
-    p.tile_seg = variant == MOE_VARIANT_PREFILL ? reinterpret_cast<int32_t*>(base + L.tile_seg) : nullptr;
-    p.tile_row = variant == MOE_VARIANT_PREFILL ? reinterpret_cast<int32_t*>(base + L.tile_row) : nullptr;
+    p.tile_info = variant == MOE_VARIANT_PREFILL ? reinterpret_cast<int4*>(base + L.tile_info) : nullptr;
+    p.tile_n = variant == MOE_VARIANT_PREFILL ? reinterpret_cast<int32_t*>(base + L.tile_n) : nullptr;
     uint16_t* abuf = reinterpret_cast<uint16_t*>(base + L.abuf);
     float* ybuf = reinterpret_cast<float*>(base + L.ybuf);
     hipStream_t s = (hipStream_t)stream;
@@ -232,12 +232,14 @@ int moe_fused_w8a16(const void* x, const uint8_t* w13, const float* w13_scale,
             rc = launch_decode_ffn(weight_layout, xb, w13, w13_scale, w2, w2_scale, sh, p, aff, T,
                                    H, I, E, k, abuf, ybuf, s);
         else
-            rc = launch_prefill_ffn(weight_layout, xb, w13, w13_scale, w2, w2_scale, sh, p, aff, T,
-                                    H, I, E, k, abuf, ybuf, s);
+            rc = launch_prefill_ffn(weight_layout, xb, w13, w13_scale, w2, w2_scale, sh, p, T, H,
+                                    I, E, k, abuf, ybuf, s);
     }
     if (rc) return rc;
-    return launch_combine(ybuf, ids, variant == MOE_VARIANT_PREFILL ? p.inv_route : nullptr, T, H,
-                          k, E, has_shared, status, out, s);
+    const bool gathered = variant == MOE_VARIANT_PREFILL;
+    return launch_combine(ybuf, ids, gathered ? p.inv_route : nullptr,
+                          gathered ? aff : nullptr, T, H, k, E,
+                          has_shared, status, out, s);
 }
 
 int moe_pack_w8(const uint8_t* src, uint8_t* dst, int64_t n_mats, int rows, int cols,

@@ -247,6 +247,7 @@ template <int KMAX, bool GATHER>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ ybuf,
                                                       const int32_t* __restrict__ ids,
                                                       const int32_t* __restrict__ inv_route,
+                                                      const float* __restrict__ aff,
                                                       int T, int H, int k, int E, int has_shared,
                                                       int32_t* __restrict__ status,
                                                       float* __restrict__ out) {
@@ -255,11 +256,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     if (h >= H) return;
     f32x4 v[KMAX];
     int id[KMAX];
+    float a[KMAX];
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {
         if (j < k) {
             const size_t r = (size_t)t * k + j;
             id[j] = ids[r];
+            a[j] = GATHER ? aff[r] : 1.0f;
             const int p = GATHER ? inv_route[r] : (int)r;
             const size_t row = p >= 0 ? (size_t)p : 0;  // a dropped route: any row, masked below
             v[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(ybuf + row * H + h));
@@ -278,7 +281,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
             const bool ok = id[j] >= 0 && id[j] < E;  // an invalid id's route is dropped
             bad |= !ok;
 #pragma unroll
-            for (int c = 0; c < 4; ++c) sum[c] += ok ? v[j][c] : 0.0f;
+            for (int c = 0; c < 4; ++c) sum[c] += ok ? (GATHER ? a[j] * v[j][c] : v[j][c]) : 0.0f;
         }
     }
     if (bad && status && h == 0) atomicOr(status, MOE_STATUS_BAD_EXPERT_ID);
@@ -359,24 +362,29 @@ int launch_decode_ffn(int layout, const uint16_t* x, const uint8_t* w13, const f
                                          aff, T, H, I, k, abuf, ybuf, stream);
 }
 
-int launch_combine(const float* ybuf, const int32_t* ids, const int32_t* inv_route, int T, int H,
-                   int k, int E, int has_shared, int32_t* status, float* out, hipStream_t stream) {
+int launch_combine(const float* ybuf, const int32_t* ids, const int32_t* inv_route,
+                   const float* aff, int T, int H, int k, int E, int has_shared, int32_t* status,
+                   float* out, hipStream_t stream) {
+    if (inv_route && !aff) {
+        set_error("combine: the gathered form needs the affinities");
+        return MOE_EINVAL;
+    }
     const dim3 grid((H / 4 + 255) / 256, T), block(256);
     prof_begin("combine", stream);
     if (inv_route) {
         if (k <= 8)
-            combine_kernel<8, true><<<grid, block, 0, stream>>>(ybuf, ids, inv_route, T, H, k, E,
+            combine_kernel<8, true><<<grid, block, 0, stream>>>(ybuf, ids, inv_route, aff, T, H, k, E,
                                                                 has_shared, status, out);
         else
             combine_kernel<MOE_MAX_TOPK, true><<<grid, block, 0, stream>>>(
-                ybuf, ids, inv_route, T, H, k, E, has_shared, status, out);
+                ybuf, ids, inv_route, aff, T, H, k, E, has_shared, status, out);
     } else {
         if (k <= 8)
-            combine_kernel<8, false><<<grid, block, 0, stream>>>(ybuf, ids, inv_route, T, H, k, E,
+            combine_kernel<8, false><<<grid, block, 0, stream>>>(ybuf, ids, inv_route, aff, T, H, k, E,
                                                                  has_shared, status, out);
         else
             combine_kernel<MOE_MAX_TOPK, false><<<grid, block, 0, stream>>>(
-                ybuf, ids, inv_route, T, H, k, E, has_shared, status, out);
+                ybuf, ids, inv_route, aff, T, H, k, E, has_shared, status, out);
     }
     prof_end(stream);
     return check_launch("combine_kernel");

@@ -138,13 +138,12 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ abuf_in,
     const uint8_t* __restrict__ wexp, const float* __restrict__ sexp,
     const uint8_t* __restrict__ wsh, const float* __restrict__ ssh, Plan plan,
-    const float* __restrict__ aff, int T, int H, int I, int k, int nblk,
+    int T, int H, int I, int k, int nblk, int max_tiles,
     uint16_t* __restrict__ abuf_out, float* __restrict__ ybuf) {
     constexpr int BM = C::BM, BN = C::BN;
     extern __shared__ __attribute__((aligned(16))) char smem[];
-    __shared__ int row_tok[BM];  // activation row source (token or abuf row)
-    __shared__ __attribute__((aligned(16))) int row_dst[BM];  // output row, -1 if padding
-    __shared__ __attribute__((aligned(16))) float row_aff[BM];
+    __shared__ int row_tok[BM];  // gate/up: token row of x
+    __shared__ __attribute__((aligned(16))) int row_dst[BM];  // gate/up: output row, -1 if padding
 
     // ---- which tile.  Workgroups are dealt round-robin over the 8 XCDs
     //      (id % 8).  The sort's tile list is cut into blocks of PF_XCD_RUN
@@ -156,17 +155,17 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
     //      XCD and share its weights in L2.  The grid covers the worst case;
     //      the rest exit.
     const int bid = blockIdx.x;
-    const int nseg = plan.seg_n[0];
-    const int ntiles = plan.seg_tile0[nseg];
     const int jx = bid >> 3, q = jx / nblk;
     const int tile = (q / PF_XCD_RUN) * (8 * PF_XCD_RUN) + (bid & 7) * PF_XCD_RUN + q % PF_XCD_RUN;
     const int nb = jx - q * nblk;
+    // the tile's record is read together with the tile count (one round trip;
+    // the index is clamped to the list's capacity, the record then unused)
+    const int ntiles = plan.tile_n[0];
+    const int4 ti = plan.tile_info[min(tile, max_tiles - 1)];
     if (tile >= ntiles) return;
-    const int seg = plan.tile_seg[tile];
-    const int m0 = plan.tile_row[tile];  // first row inside the segment
-    const int e = plan.seg_expert[seg];
-    const int srow0 = plan.seg_row0[seg];
-    const int srows = plan.seg_rows[seg];
+    const int e = ti.x;          // expert, -1 = shared
+    const int p0 = ti.y;         // first sorted row of the tile
+    const int rows_here = ti.z;  // rows in the tile (1 .. BM)
 
     const int K = MODE == PF_GATEUP ? H : I;
     const int Nrows = MODE == PF_GATEUP ? 2 * I : H;     // rows of the weight matrix
@@ -175,28 +174,20 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
     const int R = T * k;
 
     const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
-    if (tid < BM) {
-        const int m = m0 + tid;
-        int src = 0, dst = -1;
-        float a = 0.0f;
-        if (m < srows) {
-            const int p = srow0 + m;
-            if (MODE == PF_GATEUP) {
-                src = e >= 0 ? plan.sorted_route[p] / k : p - R;
-                dst = p;
-            } else {
-                src = p;
-                // the contribution row goes to the sorted position: a tile
-                // writes contiguous rows; the combine gathers through inv_route
-                dst = p;
-                a = e >= 0 ? aff[plan.sorted_route[p]] : 1.0f;
-            }
+    // Rows of the tile: row m is sorted row p0 + m (m < rows_here); padding
+    // rows read a valid row and are never stored.  Gate/up gathers token rows
+    // of x through the sorted route map (shared expert: token p - R); down
+    // reads the activations at the sorted rows themselves, so its loads need
+    // no table.  Both write at the sorted row.
+    if (MODE == PF_GATEUP) {
+        if (tid < BM) {
+            const int p = p0 + tid;
+            const bool valid = tid < rows_here;
+            row_tok[tid] = valid ? (e >= 0 ? plan.sorted_route[p] / k : p - R) : 0;
+            row_dst[tid] = valid ? p : -1;
         }
-        row_tok[tid] = src;
-        row_dst[tid] = dst;
-        row_aff[tid] = a;
+        __syncthreads();
     }
-    __syncthreads();
 
     // ---- per-lane global sources of the staged tiles
     // activations: instruction q of wave w fills rows (w*A_INSTR + q)*8 .. +8, 128 B each
@@ -206,8 +197,9 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
     for (int q = 0; q < C::A_INSTR; ++q) {
         const int row = (wave * C::A_INSTR + q) * 8 + ar_sub;
         const int sw = apiece ^ ((row >> 1) & 7);  // swizzled piece this lane fetches
-        const uint16_t* base = MODE == PF_GATEUP ? x + (size_t)row_tok[row] * H
-                                                 : abuf_in + (size_t)row_tok[row] * I;
+        const uint16_t* base = MODE == PF_GATEUP
+                                   ? x + (size_t)row_tok[row] * H
+                                   : abuf_in + (size_t)(p0 + (row < rows_here ? row : 0)) * I;
         asrc[q] = base + sw * 8;
     }
     // weights: instruction q of wave w fills 16-row tile w*B_INSTR + q
@@ -324,7 +316,6 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
     constexpr int PER_STAGE = C::A_INSTR + C::B_INSTR;
     // MFMA row groups (32 rows) of this wave that hold rows of the segment:
     // a partial last tile skips the empty ones (their rows are never stored)
-    const int rows_here = min(srows - m0, BM);
     const int mt_active =
         __builtin_amdgcn_readfirstlane(min(C::MT, max(0, rows_here - wm * C::WROWS + 31) >> 5));
     auto kloop = [&](auto mta_c) {
@@ -429,19 +420,23 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
     else kloop(std::integral_constant<int, 0>{});
 
     // ---- epilogue. 32x32 accumulator layout: lane l holds column l%32 and,
-    //      for register i, row 8*(i/4) + 4*(l/32) + i%4.  The row table
-    //      entries of a lane's rows (four consecutive rows per i/4) are read
-    //      with 16-byte LDS reads, all before the first store, so the stores
-    //      do not wait on LDS one row at a time.
+    //      for register i, row 8*(i/4) + 4*(l/32) + i%4.  Gate/up: the row
+    //      table entries of a lane's rows (four consecutive rows per i/4) are
+    //      read with 16-byte LDS reads, all before the first store, so the
+    //      stores do not wait on LDS one row at a time; down: row m goes to
+    //      sorted row p0 + m.
     int4 dst4[C::MT][4];
-    float4 aff4[C::MT][4];
 #pragma unroll
     for (int mt = 0; mt < C::MT; ++mt)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int r0 = wm * C::WROWS + mt * 32 + 8 * q + 4 * lg;
-            dst4[mt][q] = *reinterpret_cast<const int4*>(row_dst + r0);
-            if (MODE == PF_DOWN) aff4[mt][q] = *reinterpret_cast<const float4*>(row_aff + r0);
+            if (MODE == PF_GATEUP) {
+                dst4[mt][q] = *reinterpret_cast<const int4*>(row_dst + r0);
+            } else {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) dst4[mt][q][c] = r0 + c < rows_here ? p0 + r0 + c : -1;
+            }
         }
 #pragma unroll
     for (int mt = 0; mt < C::MT; ++mt)
@@ -456,13 +451,13 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
                     orow[nt * 32] = f32_to_bf16_bits(
                         swiglu_fast(acc[mt][nt][i] * seff[0], acc[mt][nt + C::NT / 2][i] * seff[1]));
             } else {
-                const float a = aff4[mt][i >> 2][i & 3];
-                float* orow = ybuf + (size_t)dst * H + nb * BN + wn * C::WCOLS + ln;
+                // y of the route (the combine multiplies it by the affinity);
                 // each contribution row is read once, by the combine: streaming
                 // (non-temporal) stores keep it from occupying the caches
+                float* orow = ybuf + (size_t)dst * H + nb * BN + wn * C::WCOLS + ln;
 #pragma unroll
                 for (int nt = 0; nt < C::NT; ++nt)
-                    __builtin_nontemporal_store(acc[mt][nt][i] * seff[0] * a, orow + nt * 32);
+                    __builtin_nontemporal_store(acc[mt][nt][i] * seff[0], orow + nt * 32);
             }
         }
 }
@@ -473,11 +468,12 @@ static inline int K_of(int H, int I) { return MODE == PF_GATEUP ? H : I; }
 template <int MODE, int LAYOUT, class C>
 static int launch_pf(const uint16_t* x, const uint16_t* abuf_in, const uint8_t* wexp,
                      const float* sexp, const uint8_t* wsh, const float* ssh, const Plan& plan,
-                     const float* aff, int T, int H, int I, int E, int k, int has_shared,
-                     uint16_t* abuf_out, float* ybuf, hipStream_t stream) {
+                     int T, int H, int I, int E, int k, int has_shared, uint16_t* abuf_out,
+                     float* ybuf, hipStream_t stream) {
     const int nblk = MODE == PF_GATEUP ? 2 * I / C::BN : H / C::BN;
     const long R = (long)T * k;
     const long max_tiles = (R + C::BM - 1) / C::BM + E + (has_shared ? (T + C::BM - 1) / C::BM : 0);
+    // (the sort's tile list has room for at least this many records)
     // XCD x's workgroup j handles the (j / nblk)-th row tile of its blocks
     const long grid = 8L * nblk * PF_XCD_RUN * ((max_tiles + 8 * PF_XCD_RUN - 1) / (8 * PF_XCD_RUN));
     if (grid > 0x7FFFFFFFL) {
@@ -488,7 +484,7 @@ static int launch_pf(const uint16_t* x, const uint16_t* abuf_in, const uint8_t* 
     const size_t lds = (size_t)C::STAGES * C::STAGE + (size_t)(C::BN / 128) * kbp * 4;
     prof_begin(MODE == PF_GATEUP ? "prefill_gateup_swiglu" : "prefill_down", stream);
     prefill_gemm_kernel<MODE, LAYOUT, C><<<(unsigned)grid, C::THREADS, lds, stream>>>(
-        x, abuf_in, wexp, sexp, wsh, ssh, plan, aff, T, H, I, k, nblk, abuf_out, ybuf);
+        x, abuf_in, wexp, sexp, wsh, ssh, plan, T, H, I, k, nblk, (int)max_tiles, abuf_out, ybuf);
     prof_end(stream);
     return check_launch(MODE == PF_GATEUP ? "prefill_gemm_kernel<gateup>" : "prefill_gemm_kernel<down>");
 }
@@ -496,35 +492,34 @@ static int launch_pf(const uint16_t* x, const uint16_t* abuf_in, const uint8_t* 
 template <int LAYOUT, class C>
 static int launch_prefill_c(const uint16_t* x, const uint8_t* w13, const float* w13s,
                             const uint8_t* w2, const float* w2s, const SharedW& sh,
-                            const Plan& plan, const float* aff, int T, int H, int I, int E, int k,
-                            uint16_t* abuf, float* ybuf, hipStream_t stream) {
+                            const Plan& plan, int T, int H, int I, int E, int k, uint16_t* abuf,
+                            float* ybuf, hipStream_t stream) {
     const int hs = sh.w13 != nullptr;
-    int rc = launch_pf<PF_GATEUP, LAYOUT, C>(x, nullptr, w13, w13s, sh.w13, sh.w13_scale, plan,
-                                             aff, T, H, I, E, k, hs, abuf, ybuf, stream);
+    int rc = launch_pf<PF_GATEUP, LAYOUT, C>(x, nullptr, w13, w13s, sh.w13, sh.w13_scale, plan, T,
+                                             H, I, E, k, hs, abuf, ybuf, stream);
     if (rc == MOE_OK)
-        rc = launch_pf<PF_DOWN, LAYOUT, C>(x, abuf, w2, w2s, sh.w2, sh.w2_scale, plan, aff, T, H,
-                                           I, E, k, hs, abuf, ybuf, stream);
+        rc = launch_pf<PF_DOWN, LAYOUT, C>(x, abuf, w2, w2s, sh.w2, sh.w2_scale, plan, T, H, I, E,
+                                           k, hs, abuf, ybuf, stream);
     return rc;
 }
 
 int launch_prefill_ffn(int layout, const uint16_t* x, const uint8_t* w13, const float* w13s,
                        const uint8_t* w2, const float* w2s, const SharedW& sh, const Plan& plan,
-                       const float* aff, int T, int H, int I, int E, int k, uint16_t* abuf,
-                       float* ybuf, hipStream_t stream) {
+                       int T, int H, int I, int E, int k, uint16_t* abuf, float* ybuf,
+                       hipStream_t stream) {
     if (!prefill_supported(H, I)) {
         set_error("prefill variant needs H %% 256 == 0, 2I %% 256 == 0 and H, I <= 65536 (got H=%d, I=%d)", H, I);
         return MOE_EUNSUPPORTED;
     }
-    if (!plan.seg_n || !plan.seg_expert || !plan.seg_row0 || !plan.seg_rows || !plan.seg_tile0 ||
-        !plan.tile_seg || !plan.tile_row || !plan.sorted_route) {
-        set_error("prefill variant needs the segment list and the tile map of the sort");
+    if (!plan.tile_info || !plan.tile_n || !plan.sorted_route) {
+        set_error("prefill variant needs the tile list of the sort");
         return MOE_EINVAL;
     }
     if (layout == LAYOUT_TILED)
-        return launch_prefill_c<LAYOUT_TILED, PfTile>(x, w13, w13s, w2, w2s, sh, plan, aff, T, H, I,
-                                                      E, k, abuf, ybuf, stream);
-    return launch_prefill_c<LAYOUT_ROWMAJOR, PfTile>(x, w13, w13s, w2, w2s, sh, plan, aff, T, H, I,
-                                                     E, k, abuf, ybuf, stream);
+        return launch_prefill_c<LAYOUT_TILED, PfTile>(x, w13, w13s, w2, w2s, sh, plan, T, H, I, E,
+                                                      k, abuf, ybuf, stream);
+    return launch_prefill_c<LAYOUT_ROWMAJOR, PfTile>(x, w13, w13s, w2, w2s, sh, plan, T, H, I, E,
+                                                     k, abuf, ybuf, stream);
 }
 
 }  // namespace moe

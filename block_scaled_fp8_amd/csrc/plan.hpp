@@ -21,10 +21,10 @@ struct Plan {
     int32_t* seg_tile0;     // [E+2] prefix of ceil(rows / tile_m)
     // Tile list of the prefill variant, or null (not built): every full tile
     // of every segment in segment order, then the partial last tiles (in
-    // segment order).  tile_seg[i] is the segment, tile_row[i] the first row
-    // of tile i inside its segment.
-    int32_t* tile_seg;      // [seg_tile0[nseg]]
-    int32_t* tile_row;      // [seg_tile0[nseg]]
+    // segment order).  tile_info[i] = {expert (-1 = shared), first sorted row
+    // of the tile, rows in the tile (1 .. tile_m), 0}; tile_n[0] = tiles.
+    int4* tile_info;        // [at most ceil(R / tile_m) + E + shared tiles]
+    int32_t* tile_n;        // [1]
 };
 
 // One expert's weights outside the routed arrays (the shared expert).
@@ -52,20 +52,23 @@ int launch_decode_ffn(int layout, const uint16_t* x, const uint8_t* w13, const f
                       const uint8_t* w2, const float* w2s, const SharedW& sh, const Plan& plan,
                       const float* aff, int T, int H, int I, int E, int k, uint16_t* abuf,
                       float* ybuf, hipStream_t stream);
+// Writes y (without the affinity) of every route at its sorted row of ybuf.
 int launch_prefill_ffn(int layout, const uint16_t* x, const uint8_t* w13, const float* w13s,
                        const uint8_t* w2, const float* w2s, const SharedW& sh, const Plan& plan,
-                       const float* aff, int T, int H, int I, int E, int k, uint16_t* abuf,
-                       float* ybuf, hipStream_t stream);
+                       int T, int H, int I, int E, int k, uint16_t* abuf, float* ybuf,
+                       hipStream_t stream);
 int launch_pack_w8(const uint8_t* src, uint8_t* dst, int64_t n_mats, int rows, int cols,
                    hipStream_t stream);
 int prefill_tile_m();
 int prefill_supported(int H, int I);
 // Sums, per token, the k route rows whose id is valid (plus the shared row at
-// R + t); route r's row is inv_route[r] when inv_route is given (prefill
-// producers write at the sorted position), else r.  Ids outside [0, E) set
+// R + t).  Decode producers write aff * y at row r (inv_route and aff null);
+// prefill producers write y at the route's sorted position, and the sum takes
+// aff[r] * ybuf[inv_route[r]] (the same fp32 product).  Ids outside [0, E) set
 // MOE_STATUS_BAD_EXPERT_ID in *status (if not NULL).
-int launch_combine(const float* ybuf, const int32_t* ids, const int32_t* inv_route, int T, int H,
-                   int k, int E, int has_shared, int32_t* status, float* out, hipStream_t stream);
+int launch_combine(const float* ybuf, const int32_t* ids, const int32_t* inv_route,
+                   const float* aff, int T, int H, int k, int E, int has_shared, int32_t* status,
+                   float* out, hipStream_t stream);
 // Decode variant helpers: the M tile, whether the fused one-workgroup-per-
 // expert kernel applies, and its self-routed form (no sort: each workgroup
 // scans the ids for its expert; at most decode_self_routed_max_routes() routes).

@@ -110,10 +110,10 @@ __device__ void wave_place(const int32_t* __restrict__ ids, int r_begin, int r_e
 }
 
 // Segment list from counts/offsets held in LDS (one block, all threads).
-// flags, tiles, fulls: LDS scratch of E+2 ints each.
+// flags, tiles, fulls, segx: LDS scratch of E+2 ints each.
 template <int NT>
 __device__ void build_segments(const int* cnt, const int* off, int E, int R, int T, int has_shared,
-                               int tile_m, int* flags, int* tiles, int* fulls, int* tmp,
+                               int tile_m, int* flags, int* tiles, int* fulls, int* segx, int* tmp,
                                const Plan& plan) {
     const int tid = threadIdx.x;
     for (int e = tid; e < E; e += NT) flags[e] = cnt[e] > 0 ? 1 : 0;
@@ -126,6 +126,7 @@ __device__ void build_segments(const int* cnt, const int* off, int E, int R, int
             plan.seg_expert[i] = e;
             plan.seg_row0[i] = off[e];
             plan.seg_rows[i] = cnt[e];
+            segx[i] = e;
             tiles[i] = (cnt[e] + tile_m - 1) / tile_m;
             fulls[i] = cnt[e] / tile_m;
         }
@@ -133,6 +134,7 @@ __device__ void build_segments(const int* cnt, const int* off, int E, int R, int
         plan.seg_expert[nrouted] = -1;
         plan.seg_row0[nrouted] = R;
         plan.seg_rows[nrouted] = T;
+        segx[nrouted] = -1;
         tiles[nrouted] = (T + tile_m - 1) / tile_m;
         fulls[nrouted] = T / tile_m;
     }
@@ -144,25 +146,25 @@ __device__ void build_segments(const int* cnt, const int* off, int E, int R, int
         plan.seg_tile0[nseg] = ntiles;
         plan.seg_n[0] = nseg;
     }
-    if (plan.tile_seg) {
+    if (plan.tile_info) {
         // ordered tile list: full tiles first (segment s's at fulls[s] ..),
         // then the partial ones (segment s's at nfull + #partials before s,
         // which is tiles[s] - fulls[s] with both as exclusive prefixes)
         constexpr int NW = NT / MOE_WAVE;
         const int w = tid / MOE_WAVE, lane = lane_id();
         for (int s = w; s < nseg; s += NW) {
+            const int e = segx[s];
+            const int row0 = e >= 0 ? off[e] : R, rows = e >= 0 ? cnt[e] : T;
             const int f0 = fulls[s], f1 = s + 1 < nseg ? fulls[s + 1] : nfull;
             const int t0 = tiles[s], t1 = s + 1 < nseg ? tiles[s + 1] : ntiles;
-            for (int j = lane; j < f1 - f0; j += MOE_WAVE) {
-                plan.tile_seg[f0 + j] = s;
-                plan.tile_row[f0 + j] = j * tile_m;
-            }
+            for (int j = lane; j < f1 - f0; j += MOE_WAVE)
+                plan.tile_info[f0 + j] = make_int4(e, row0 + j * tile_m, tile_m, 0);
             if (lane == 0 && t1 - t0 > f1 - f0) {
-                const int i = nfull + (t0 - f0);
-                plan.tile_seg[i] = s;
-                plan.tile_row[i] = (f1 - f0) * tile_m;
+                const int done = (f1 - f0) * tile_m;
+                plan.tile_info[nfull + (t0 - f0)] = make_int4(e, row0 + done, rows - done, 0);
             }
         }
+        if (tid == 0) plan.tile_n[0] = ntiles;
     }
 }
 
@@ -179,7 +181,8 @@ __global__ __launch_bounds__(SORT_SMALL_THREADS) void sort_small_kernel(
     int* flags = off + E + 1;            // [E+2]
     int* tiles = flags + E + 2;          // [E+2]
     int* fulls = tiles + E + 2;          // [E+2]
-    int* tmp = fulls + E + 2;            // [NW+1]
+    int* segx = fulls + E + 2;           // [E+2]
+    int* tmp = segx + E + 2;             // [NW+1]
     const int R = T * k;
     const int tid = threadIdx.x, w = tid / MOE_WAVE, lane = lane_id();
     const int sub = ((R + NW - 1) / NW + MOE_WAVE - 1) / MOE_WAVE * MOE_WAVE;
@@ -216,7 +219,7 @@ __global__ __launch_bounds__(SORT_SMALL_THREADS) void sort_small_kernel(
     wave_place(ids, r0, r1, E, whist + w * E, plan.sorted_route, plan.inv_route);
     if (want_segments) {
         __syncthreads();
-        build_segments<NT>(cnt, off, E, R, T, has_shared, tile_m, flags, tiles, fulls, tmp, plan);
+        build_segments<NT>(cnt, off, E, R, T, has_shared, tile_m, flags, tiles, fulls, segx, tmp, plan);
     }
 }
 
@@ -247,6 +250,7 @@ __global__ __launch_bounds__(1024) void sort_scan_kernel(int T, int k, int E, in
     __shared__ int flags[MOE_MAX_EXPERTS + 2];
     __shared__ int tiles[MOE_MAX_EXPERTS + 2];
     __shared__ int fulls[MOE_MAX_EXPERTS + 2];
+    __shared__ int segx[MOE_MAX_EXPERTS + 2];
     __shared__ int tmp[NT / MOE_WAVE + 1];
     const int R = T * k, tid = threadIdx.x, lane = lane_id(), w = tid / MOE_WAVE;
     constexpr int NW = NT / MOE_WAVE;
@@ -307,7 +311,7 @@ __global__ __launch_bounds__(1024) void sort_scan_kernel(int T, int k, int E, in
     for (int p = total + tid; p < R; p += NT) plan.sorted_route[p] = -1;
     if (want_segments) {
         __syncthreads();
-        build_segments<NT>(cnt, off, E, R, T, has_shared, tile_m, flags, tiles, fulls, tmp, plan);
+        build_segments<NT>(cnt, off, E, R, T, has_shared, tile_m, flags, tiles, fulls, segx, tmp, plan);
     }
 }
 
@@ -348,7 +352,7 @@ int launch_sort(const int32_t* ids, int T, int k, int E, const Plan& plan, int h
     const int want_segments = plan.seg_n != nullptr;
     if (R <= SORT_SMALL_MAX_ROUTES) {
         constexpr int NW = SORT_SMALL_THREADS / MOE_WAVE;
-        const size_t lds = sizeof(int) * ((size_t)NW * E + E + (E + 1) + 3 * (E + 2) + NW + 1);
+        const size_t lds = sizeof(int) * ((size_t)NW * E + E + (E + 1) + 4 * (E + 2) + NW + 1);
         prof_begin("sort_small", stream);
         sort_small_kernel<<<1, SORT_SMALL_THREADS, lds, stream>>>(ids, T, k, E, plan, want_segments,
                                                                   has_shared, tile_m, status);
