@@ -238,98 +238,70 @@ __global__ __launch_bounds__(SORT_THREADS) void sort_count_kernel(
     for (int e = tid; e < E; e += SORT_THREADS) ghist[(size_t)e * nb + blockIdx.x] = hist[e];
 }
 
-// One workgroup: ghist[e][b] -> exclusive starts (expert-major), counts,
-// offsets, tail fill and the segment list.
-__global__ __launch_bounds__(1024) void sort_scan_kernel(int T, int k, int E, int nb,
-                                                         int32_t* __restrict__ ghist, Plan plan,
-                                                         int want_segments, int has_shared,
-                                                         int tile_m) {
-    constexpr int NT = 1024;
-    __shared__ int cnt[MOE_MAX_EXPERTS];
-    __shared__ int off[MOE_MAX_EXPERTS + 1];
-    __shared__ int flags[MOE_MAX_EXPERTS + 2];
-    __shared__ int tiles[MOE_MAX_EXPERTS + 2];
-    __shared__ int fulls[MOE_MAX_EXPERTS + 2];
-    __shared__ int segx[MOE_MAX_EXPERTS + 2];
-    __shared__ int tmp[NT / MOE_WAVE + 1];
-    const int R = T * k, tid = threadIdx.x, lane = lane_id(), w = tid / MOE_WAVE;
-    constexpr int NW = NT / MOE_WAVE;
-    // one flat exclusive scan over the expert-major table (entry e*nb + b), in
-    // rounds of NT*V entries: thread tid takes V consecutive entries, all of
-    // them loaded before any is used (one memory round trip per round);
-    // per-expert totals come from LDS atomics (order-independent sums)
-    constexpr int V = 8;
-    for (int e = tid; e < E; e += NT) cnt[e] = 0;
-    __syncthreads();
-    const int n = E * nb;
-    int carry = 0;  // the same in every thread
-    for (int base = 0; base < n; base += NT * V) {
-        const int i0 = base + tid * V;
-        int v[V];
-        int local = 0;
-#pragma unroll
-        for (int q = 0; q < V; ++q) {
-            v[q] = i0 + q < n ? ghist[i0 + q] : 0;
-            local += v[q];
-        }
-#pragma unroll
-        for (int q = 0; q < V; ++q)
-            if (v[q] != 0) atomicAdd(&cnt[(i0 + q) / nb], v[q]);
-        const int incl = wave_incl_scan_i32(local);
-        if (lane == MOE_WAVE - 1) tmp[w] = incl;
-        __syncthreads();
-        if (tid < MOE_WAVE) {
-            const int x = tid < NW ? tmp[tid] : 0;
-            const int sc = wave_incl_scan_i32(x);
-            if (tid < NW) tmp[tid] = sc - x;
-            if (tid == NW - 1) tmp[NW] = sc;
-        }
-        __syncthreads();
-        int run = carry + tmp[w] + incl - local;
-#pragma unroll
-        for (int q = 0; q < V; ++q) {
-            const int i = i0 + q;
-            if (i < n) {
-                ghist[i] = run;
-                if (i % nb == 0) off[i / nb] = run;  // expert e starts at its block 0
-            }
-            run += v[q];
-        }
-        carry += tmp[NW];
-        __syncthreads();  // tmp is rewritten by the next round
-    }
-    const int total = carry;
-    __syncthreads();
-    for (int e = tid; e < E; e += NT) {
-        plan.counts[e] = cnt[e];
-        plan.offsets[e] = off[e];
-    }
-    if (tid == 0) {
-        plan.offsets[E] = total;
-        off[E] = total;
-    }
-    for (int p = total + tid; p < R; p += NT) plan.sorted_route[p] = -1;
-    if (want_segments) {
-        __syncthreads();
-        build_segments<NT>(cnt, off, E, R, T, has_shared, tile_m, flags, tiles, fulls, segx, tmp, plan);
-    }
-}
-
+// Blocks 0 .. nb-1 place the routes of their chunk; block nb writes the
+// counts, offsets, tail fill and the segment list.  Every block derives what
+// it needs from the per-(expert, block) counts ghist[e][b] of sort_count:
+// expert e's total, its exclusive start over experts (offsets) and, for a
+// placement block b, the routes of expert e in earlier chunks.  (The table is
+// E x nb ints, read by every block; this replaces a separate one-workgroup
+// scan kernel and its launch.)
 __global__ __launch_bounds__(SORT_THREADS) void sort_place_kernel(
-    const int32_t* __restrict__ ids, int R, int E, int nb, const int32_t* __restrict__ gbase,
-    int32_t* __restrict__ sorted_route, int32_t* __restrict__ inv_route) {
-    constexpr int NW = SORT_THREADS / MOE_WAVE;
+    const int32_t* __restrict__ ids, int T, int k, int E, int nb,
+    const int32_t* __restrict__ ghist, Plan plan, int want_segments, int has_shared, int tile_m) {
+    constexpr int NT = SORT_THREADS, NW = NT / MOE_WAVE;
     constexpr int SUB = SORT_CHUNK / NW;
-    extern __shared__ int whist[];  // [NW][E]
-    const int tid = threadIdx.x, w = tid / MOE_WAVE, lane = lane_id();
-    for (int i = tid; i < NW * E; i += SORT_THREADS) whist[i] = 0;
+    extern __shared__ int lds[];
+    int* whist = lds;               // [NW][E]
+    int* cnt = whist + NW * E;      // [E]
+    int* off = cnt + E;             // [E+1]
+    int* pre = off + E + 1;         // [E]
+    int* flags = pre + E;           // [E+2]
+    int* tiles = flags + E + 2;     // [E+2]
+    int* fulls = tiles + E + 2;     // [E+2]
+    int* segx = fulls + E + 2;      // [E+2]
+    int* tmp = segx + E + 2;        // [NW+1]
+    const int R = T * k, tid = threadIdx.x, w = tid / MOE_WAVE, lane = lane_id();
+    const int b = blockIdx.x;
+    for (int e = tid; e < E; e += NT) {
+        const int32_t* row = ghist + (size_t)e * nb;
+        int tot = 0, before = 0;
+#pragma unroll 8
+        for (int j = 0; j < nb; ++j) {
+            const int v = row[j];
+            before += j < b ? v : 0;
+            tot += v;
+        }
+        cnt[e] = tot;
+        off[e] = tot;
+        pre[e] = before;
+    }
     __syncthreads();
-    const int c0 = blockIdx.x * SORT_CHUNK;
+    const int total = lds_excl_scan<NT>(off, E, tmp);
+    if (b == nb) {
+        for (int e = tid; e < E; e += NT) {
+            plan.counts[e] = cnt[e];
+            plan.offsets[e] = off[e];
+        }
+        if (tid == 0) {
+            plan.offsets[E] = total;
+            off[E] = total;
+        }
+        for (int p = total + tid; p < R; p += NT) plan.sorted_route[p] = -1;
+        if (want_segments) {
+            __syncthreads();
+            build_segments<NT>(cnt, off, E, R, T, has_shared, tile_m, flags, tiles, fulls, segx, tmp,
+                               plan);
+        }
+        return;
+    }
+    for (int i = tid; i < NW * E; i += NT) whist[i] = 0;
+    __syncthreads();
+    const int c0 = b * SORT_CHUNK;
     const int r0 = min(R, c0 + w * SUB), r1 = min(R, r0 + SUB);
     count_range(ids, r0 + lane, r1, MOE_WAVE, E, whist + w * E);
     __syncthreads();
-    for (int e = tid; e < E; e += SORT_THREADS) {
-        int run = gbase[(size_t)e * nb + blockIdx.x];
+    for (int e = tid; e < E; e += NT) {
+        int run = off[e] + pre[e];
         for (int v = 0; v < NW; ++v) {
             const int c = whist[v * E + e];
             whist[v * E + e] = run;
@@ -337,7 +309,7 @@ __global__ __launch_bounds__(SORT_THREADS) void sort_place_kernel(
         }
     }
     __syncthreads();
-    wave_place(ids, r0, r1, E, whist + w * E, sorted_route, inv_route);
+    wave_place(ids, r0, r1, E, whist + w * E, plan.sorted_route, plan.inv_route);
 }
 
 size_t sort_scratch_bytes(int R, int E) {
@@ -365,15 +337,11 @@ int launch_sort(const int32_t* ids, int T, int k, int E, const Plan& plan, int h
     sort_count_kernel<<<nb, SORT_THREADS, sizeof(int) * E, stream>>>(ids, R, E, nb, ghist, status);
     prof_end(stream);
     if (int rc = check_launch("sort_count_kernel")) return rc;
-    prof_begin("sort_scan", stream);
-    sort_scan_kernel<<<1, 1024, 0, stream>>>(T, k, E, nb, ghist, plan, want_segments, has_shared,
-                                             tile_m);
-    prof_end(stream);
-    if (int rc = check_launch("sort_scan_kernel")) return rc;
     constexpr int NW = SORT_THREADS / MOE_WAVE;
+    const size_t lds = sizeof(int) * ((size_t)NW * E + E + (E + 1) + E + 4 * (E + 2) + NW + 1);
     prof_begin("sort_place", stream);
-    sort_place_kernel<<<nb, SORT_THREADS, sizeof(int) * NW * E, stream>>>(
-        ids, R, E, nb, ghist, plan.sorted_route, plan.inv_route);
+    sort_place_kernel<<<nb + 1, SORT_THREADS, lds, stream>>>(ids, T, k, E, nb, ghist, plan,
+                                                             want_segments, has_shared, tile_m);
     prof_end(stream);
     return check_launch("sort_place_kernel");
 }
