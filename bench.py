@@ -193,6 +193,34 @@ def profiled_traffic(kernel, workload):
     return int(got["traffic_bytes_per_launch"])
 
 
+def vendor_gemm(cfg, dev, warmup=200, reps=50):
+    """Same-box context for the MFMA fraction: the rate of torch.matmul (the
+    vendor bf16 GEMM library) on the dense product with the gate/up shape of
+    the prefill workload, [T*k, H] x [H, 2I], random N(0,1) x N(0,0.02) bf16.
+    It does none of the method's work (no fp8 decode, row gather, block scales
+    or SwiGLU) and is never part of a step."""
+    import torch
+    M, K, N = cfg.T * cfg.k, cfg.H, 2 * cfg.I
+    g = torch.Generator(device=dev).manual_seed(1)
+    a = torch.randn(M, K, device=dev, dtype=torch.bfloat16, generator=g)
+    b = torch.randn(K, N, device=dev, dtype=torch.bfloat16, generator=g) * 0.02
+    for _ in range(warmup):
+        c = a @ b
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        c = a @ b
+    e.record()
+    torch.cuda.synchronize()
+    us = s.elapsed_time(e) * 1e3 / reps
+    tf = 2.0 * M * N * K / (us * 1e-6) / 1e12
+    del a, b, c
+    torch.cuda.empty_cache()
+    return {"what": "torch.matmul bf16, dense [T*k, H] x [H, 2I]", "M": M, "N": N, "K": K,
+            "avg_us": round(us, 2), "TFLOP_per_s": round(tf, 1),
+            "frac": round(tf / BF16_PEAK_TFLOPS, 4)}
+
+
 def prefill_summary(cfg, m):
     """MFMA roofline of the prefill workload (secondary object of the JSON line)."""
     R = cfg.T * cfg.k + (cfg.T if cfg.shared else 0)
@@ -240,6 +268,8 @@ def main():
                     help="untimed prefill steps first: the GPU idles while the prefill inputs "
                          "are generated, and its clock needs some milliseconds of work to settle")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-vendor-gemm", action="store_true",
+                    help="skip timing torch.matmul at the gate/up shape (context only)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB, 5 times (PMC byte-counter "
                          "calibration)")
@@ -324,6 +354,9 @@ def main():
         result["prefill"] = prefill_summary(pcfg, pm)
         del pm
         torch.cuda.empty_cache()
+        if not args.no_vendor_gemm:
+            log("vendor bf16 GEMM at the gate/up shape (context) ...")
+            result["prefill"]["vendor_bf16_gemm"] = vendor_gemm(pcfg, dev)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         case = dict(x=x, logits=logits, **wsets[0])
