@@ -20,8 +20,9 @@
 // through the inverse route map.
 //
 //  * Workgroup tile 128 rows x 256 columns (gate/up: 128 gate + the matching
-//    128 up columns), 4 waves (2 x 2), each a 64 x 128 tile of
-//    v_mfma_f32_32x32x16_bf16 (2 x 4 MFMA tiles, 128 fp32 accumulators).
+//    128 up columns), 4 waves (2 x 2), each a 64 x 128 tile with 128 fp32
+//    accumulators: gate/up as 4 x 8 tiles of v_mfma_f32_16x16x32_bf16, down
+//    as 2 x 4 tiles of v_mfma_f32_32x32x16_bf16.
 //    Two workgroups share a CU (64 KB of stages each, 2 waves per SIMD), so
 //    one workgroup's prologue, epilogue and barrier waits overlap the other's
 //    MFMAs; measured, this beats one 8-wave 128 x 512 workgroup per CU.
@@ -60,9 +61,12 @@ constexpr int PF_XCD_RUN = 8;  // consecutive row tiles an XCD takes at a time
 // Workgroup tile BM rows x BN columns, WM x WN waves of 64 x 128 each (2 x 4
 // MFMA tiles of 32 x 32), STAGES LDS stages of 64-wide K, OCC workgroups per
 // CU (the register budget follows from it).
-template <int BM_, int BN_, int WM_, int WN_, int STAGES_, int OCC_>
+template <int BM_, int BN_, int WM_, int WN_, int STAGES_, int OCC_, int M16_ = 0>
 struct PfCfg {
     static constexpr int OCC = OCC_;
+    // MFMA shape: v_mfma_f32_16x16x32_bf16 (M16) or v_mfma_f32_32x32x16_bf16
+    static constexpr bool M16 = M16_ != 0;
+    static constexpr int MS = M16 ? 16 : 32;  // rows = columns of one MFMA tile
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
     static constexpr int THREADS = WM * WN * MOE_WAVE;
     static constexpr int WAVES = WM * WN;
@@ -72,8 +76,8 @@ struct PfCfg {
     static constexpr int STAGE = A_BYTES + B_BYTES;
     static constexpr int A_INSTR = A_BYTES / 1024 / WAVES;  // 1 KB loads per wave per stage
     static constexpr int B_INSTR = B_BYTES / 1024 / WAVES;
-    static constexpr int MT = BM / WM / 32;
-    static constexpr int NT = BN / WN / 32;
+    static constexpr int MT = BM / WM / MS;
+    static constexpr int NT = BN / WN / MS;
     static constexpr int WROWS = BM / WM;  // rows of a wave tile
     static constexpr int WCOLS = BN / WN;  // columns of a wave tile
     // 64 x 128, 128 fp32 accumulators per lane: the running-scale rescale
@@ -87,8 +91,14 @@ struct PfCfg {
     static_assert(A_INSTR >= 1 && B_INSTR >= 1, "every wave issues loads");
 };
 // 4 waves and 64 KB of stages: two workgroups share a CU, so one's prologue,
-// epilogue and barrier waits overlap the other's MFMAs.
-using PfTile = PfCfg<128, 256, 2, 2, 2, 2>;
+// epilogue and barrier waits overlap the other's MFMAs.  Gate/up multiplies
+// with 16x16x32 MFMAs: on random operands the chip holds a higher clock for
+// them than for 32x32x16 (register-only loops: 1.94 against 1.71 PFLOP/s),
+// and the kernel measured 2.5% faster.  Down keeps 32x32x16: its fp32 rows
+// go out in 128-byte row pieces instead of 64-byte ones, which measured 4%
+// faster there.
+using PfGateUp = PfCfg<128, 256, 2, 2, 2, 2, 1>;
+using PfDown = PfCfg<128, 256, 2, 2, 2, 2, 0>;
 constexpr int PF_BM = 128;
 
 int prefill_tile_m() { return PF_BM; }
@@ -106,6 +116,10 @@ enum { PF_GATEUP = 0, PF_DOWN = 1 };
 // divide; exp(-g) overflowing to +inf gives the correct limit 0.
 __device__ __forceinline__ float swiglu_fast(float g, float u) {
     return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+}
+
+__device__ __forceinline__ float uniform_f32(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
 }
 
 __device__ __forceinline__ void lds_load16(const void* g, uint32_t lds_byte_addr_uniform, void* lds_base) {
@@ -190,17 +204,21 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
     }
 
     // ---- per-lane global sources of the staged tiles
-    // activations: instruction q of wave w fills rows (w*A_INSTR + q)*8 .. +8, 128 B each
+    // activations: instruction q of wave w fills rows (w*A_INSTR + q)*8 .. +8,
+    // 128 B each; the lane's source is a 32-bit byte offset from the matrix
+    // (the launcher checks that the matrix is under 4 GB), so the loads
+    // address through a scalar base
     const int ar_sub = lane >> 3, apiece = lane & 7;
-    const uint16_t* asrc[C::A_INSTR];
+    const char* abase = MODE == PF_GATEUP ? reinterpret_cast<const char*>(x)
+                                          : reinterpret_cast<const char*>(abuf_in);
+    uint32_t asrc[C::A_INSTR];
 #pragma unroll
     for (int q = 0; q < C::A_INSTR; ++q) {
         const int row = (wave * C::A_INSTR + q) * 8 + ar_sub;
         const int sw = apiece ^ ((row >> 1) & 7);  // swizzled piece this lane fetches
-        const uint16_t* base = MODE == PF_GATEUP
-                                   ? x + (size_t)row_tok[row] * H
-                                   : abuf_in + (size_t)(p0 + (row < rows_here ? row : 0)) * I;
-        asrc[q] = base + sw * 8;
+        const uint32_t src_row = MODE == PF_GATEUP ? (uint32_t)row_tok[row]
+                                                   : (uint32_t)(p0 + (row < rows_here ? row : 0));
+        asrc[q] = src_row * (uint32_t)(2 * (MODE == PF_GATEUP ? H : I)) + sw * 16;
     }
     // weights: instruction q of wave w fills 16-row tile w*B_INSTR + q
     constexpr int HALF_T = BN / 2 / 16;  // gate tiles in a gate/up tile (MODE 0)
@@ -224,7 +242,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
         const uint32_t sbase = st * C::STAGE;
 #pragma unroll
         for (int q = 0; q < C::A_INSTR; ++q)
-            lds_load16(asrc[q] + kc * PF_BK, sbase + (wave * C::A_INSTR + q) * 1024, smem);
+            lds_load16(abase + (asrc[q] + (uint32_t)kc * (PF_BK * 2)), sbase + (wave * C::A_INSTR + q) * 1024, smem);
 #pragma unroll
         for (int q = 0; q < C::B_INSTR; ++q)
             lds_load16(bbase[q] + (size_t)kc * CS + blane, sbase + C::A_BYTES + (wave * C::B_INSTR + q) * 1024,
@@ -241,26 +259,42 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
     // (a_step, b_step), which the LDS reads take as immediate offsets.
     // Activation piece s (16 K) of row r: the swizzle (r / 2) % 8 is the same
     // for rows 32 apart.
+    //
+    // K order inside a 64-wide step (any order works if both operands use it;
+    // each lane's 8 K values are one 8-K block kb of the step):
+    //   32x32x16: sub-step s (16 K, four per step), lane half lg: kb = 4 lg + s;
+    //   16x16x32: sub-step s (32 K, two per step), lane quarter g: kb = 4 s + g.
+    // An activation piece (16 bytes) is one kb of a row; a weight lane of the
+    // staged 1 KB chunk holds kbs 2 (L / 16), 2 (L / 16) + 1 of row L % 16.
+    const int l16 = lane & 15, g16 = lane >> 4;
     uint32_t a_off[4];
-    {
+    uint32_t b_off;
+    const int t16 = MODE == PF_GATEUP ? wn * (C::WCOLS / 32) : wn * (C::WCOLS / 16);
+    if constexpr (C::M16) {
+        const int row = wm * C::WROWS + l16;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) a_off[s] = row * 128 + (((4 * s + g16) ^ ((row >> 1) & 7)) * 16);
+        a_off[2] = a_off[3] = 0;  // (two sub-steps per step)
+        // 16-column tile nt is 16-row weight tile t16(nt); sub-step s's 8
+        // bytes sit s * 512 bytes further on
+        b_off = C::A_BYTES + t16 * 1024 + ((g16 >> 1) * 16 + l16) * 16 + (g16 & 1) * 8;
+    } else {
         const int row = wm * C::WROWS + ln;
 #pragma unroll
         for (int s = 0; s < 4; ++s) a_off[s] = row * 128 + (((4 * lg + s) ^ ((row >> 1) & 7)) * 16);
-    }
-    // weights: 32-column MFMA tile nt spans 16-row tiles t16(nt), t16(nt) + 1
-    // (MODE 0: the first NT/2 tiles are gate columns, the rest the matching up
-    // columns); the lane's 16 bytes for half p sit p * 256 bytes further on
-    uint32_t b_off;
-    {
-        const int t16 = MODE == PF_GATEUP ? wn * (C::WCOLS / 32) : wn * (C::WCOLS / 16);
+        // 32-column tile nt spans 16-row tiles t16(nt), t16(nt) + 1; the
+        // lane's 16 bytes for half p sit p * 256 bytes further on
         const int tt = t16 + (ln >> 4), r = ln & 15;
         b_off = C::A_BYTES + tt * 1024 + (2 * lg * 16 + r) * 16;
     }
-    auto a_step = [](int mt) { return mt * 32 * 128; };
+    // (MODE 0: the first NT/2 MFMA column tiles are gate columns, the rest the
+    // matching up columns)
+    auto a_step = [](int mt) { return mt * C::MS * 128; };
     auto b_step = [](int nt) {
+        constexpr int T16 = C::MS / 16;  // 16-row weight tiles per MFMA column tile
         if (MODE == PF_GATEUP)
-            return ((nt < C::NT / 2 ? 0 : HALF_T) + (nt % (C::NT / 2)) * 2) * 1024;
-        return nt * 2 * 1024;
+            return ((nt < C::NT / 2 ? 0 : HALF_T) + (nt % (C::NT / 2)) * T16) * 1024;
+        return nt * T16 * 1024;
     };
     // ---- block scales of the workgroup's columns, staged once in LDS by
     //      direct-to-LDS loads issued before the first operand stages (so the
@@ -294,13 +328,15 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
         sj[0] = sj[1] = (wn * C::WCOLS) >> 7;
     }
 
-    f32x16 acc[C::MT][C::NT];
+    using Acc = std::conditional_t<C::M16, f32x4, f32x16>;
+    constexpr int AR = C::M16 ? 4 : 16;  // accumulator registers per MFMA tile
+    Acc acc[C::MT][C::NT];
 #pragma unroll
     for (int mt = 0; mt < C::MT; ++mt)
 #pragma unroll
         for (int nt = 0; nt < C::NT; ++nt)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) acc[mt][nt][i] = 0.0f;
+            for (int i = 0; i < AR; ++i) acc[mt][nt][i] = 0.0f;
     float seff[2] = {0.0f, 0.0f};
 
     // ---- K loop, software-pipelined by half steps.  Half p of a 64-wide step
@@ -316,40 +352,71 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
     constexpr int PER_STAGE = C::A_INSTR + C::B_INSTR;
     // MFMA row groups (32 rows) of this wave that hold rows of the segment:
     // a partial last tile skips the empty ones (their rows are never stored)
-    const int mt_active =
-        __builtin_amdgcn_readfirstlane(min(C::MT, max(0, rows_here - wm * C::WROWS + 31) >> 5));
+    const int mt_active = __builtin_amdgcn_readfirstlane(
+        min(C::MT, max(0, rows_here - wm * C::WROWS + C::MS - 1) / C::MS));
     auto kloop = [&](auto mta_c) {
     constexpr int MTA = decltype(mta_c)::value;
-    u32x4 ah[2][C::MT][2], bh[2][C::NT];
-    auto read_half = [&](int stage, int p, u32x4 (&a)[C::MT][2], u32x4 (&b)[C::NT]) {
+    // operand registers of a half step (32 K): 32x32 -- two activation
+    // pieces per row group and 16 weight bytes per column tile; 16x16 -- one
+    // activation piece per row group and 8 weight bytes per column tile
+    constexpr int AP = C::M16 ? 1 : 2;
+    using BFrag = std::conditional_t<C::M16, u32x2, u32x4>;
+    u32x4 ah[2][C::MT][AP];
+    BFrag bh[2][C::NT];
+    auto read_half = [&](int stage, int p, u32x4 (&a)[C::MT][AP], BFrag (&b)[C::NT]) {
         const char* st = smem + stage * C::STAGE;
 #pragma unroll
         for (int mt = 0; mt < MTA; ++mt)
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
-                a[mt][j] = *reinterpret_cast<const u32x4*>(st + a_off[2 * p + j] + a_step(mt));
+            for (int j = 0; j < AP; ++j)
+                a[mt][j] = *reinterpret_cast<const u32x4*>(st + a_off[AP * p + j] + a_step(mt));
         if (MTA > 0)
 #pragma unroll
             for (int nt = 0; nt < C::NT; ++nt)
-                b[nt] = *reinterpret_cast<const u32x4*>(st + b_off + p * 256 + b_step(nt));
+                b[nt] = *reinterpret_cast<const BFrag*>(st + b_off + p * (C::M16 ? 512 : 256) + b_step(nt));
     };
-    // Sub-step j of a half.  rescale: the half opens a new K block, and each
-    // accumulator is multiplied by its group's factor right before its first
-    // MFMA of the block.
-    auto mma_sub = [&](const u32x4 (&a)[C::MT][2], const u32x4 (&b)[C::NT], int j, bool rescale,
+    // Part j of a half: 32x32 -- sub-step j (16 K) of every tile; 16x16 --
+    // the half's 32 K for column tiles j*NT/2 .. (j+1)*NT/2 - 1 (gate/up: j = 0
+    // the gate tiles, j = 1 the up tiles).  rescale: the half opens a new K
+    // block, and each accumulator is multiplied by its group's factor right
+    // before its first MFMA of the block.
+    auto mma_sub = [&](const u32x4 (&a)[C::MT][AP], const BFrag (&b)[C::NT], int j, bool rescale,
                        const float (&rr)[2]) {
         if (MTA == 0) return;
+        if (C::M16 && rescale) {
+            // 16x16: every accumulator of the block's first half is rescaled
+            // before part 0's MFMAs
+#pragma unroll
+            for (int nt = 0; nt < C::NT; ++nt) {
+                const float f = MODE == PF_GATEUP ? rr[nt / (C::NT / 2)] : rr[0];
+#pragma unroll
+                for (int mt = 0; mt < MTA; ++mt)
+#pragma unroll
+                    for (int i = 0; i < AR; ++i) acc[mt][nt][i] *= f;
+            }
+            rescale = false;
+        }
 #pragma unroll
         for (int nt = 0; nt < C::NT; ++nt) {
-            const bf16x8 bf = j == 0 ? fp8x8_to_bf16x8(b[nt][0], b[nt][1]) : fp8x8_to_bf16x8(b[nt][2], b[nt][3]);
+            if (C::M16 && nt / (C::NT / 2) != j) continue;
+            bf16x8 bf;
+            if constexpr (C::M16)
+                bf = fp8x8_to_bf16x8(b[nt][0], b[nt][1]);
+            else
+                bf = j == 0 ? fp8x8_to_bf16x8(b[nt][0], b[nt][1]) : fp8x8_to_bf16x8(b[nt][2], b[nt][3]);
             const float f = MODE == PF_GATEUP ? rr[nt / (C::NT / 2)] : rr[0];
 #pragma unroll
             for (int mt = 0; mt < MTA; ++mt) {
                 if (rescale)
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) acc[mt][nt][i] *= f;
-                acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[mt][j]), bf, acc[mt][nt], 0, 0, 0);
+                    for (int i = 0; i < AR; ++i) acc[mt][nt][i] *= f;
+                if constexpr (C::M16)
+                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[mt][0]), bf, acc[mt][nt], 0, 0, 0);
+                else
+                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[mt][j]), bf, acc[mt][nt], 0, 0, 0);
             }
+            // (16x16: one converted weight fragment live at a time)
+            if constexpr (C::M16) __builtin_amdgcn_sched_barrier(0);
         }
     };
     // step kc + 1 landed (with three stages step kc + 2 may still be in
@@ -381,8 +448,9 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
         for (int g = 0; g < 2; ++g) {
             const float sn = snext[g];
             const bool take = sn != 0.0f;
-            rr[g] = take && seff[g] != 0.0f ? seff[g] * __builtin_amdgcn_rcpf(sn) : 1.0f;
-            seff[g] = take ? sn : seff[g];
+            // (wave-uniform: kept in scalar registers)
+            rr[g] = uniform_f32(take && seff[g] != 0.0f ? seff[g] * __builtin_amdgcn_rcpf(sn) : 1.0f);
+            seff[g] = uniform_f32(take ? sn : seff[g]);
         }
         const int kn = kb + 1 < kblocks ? kb + 1 : kb;
         snext[0] = sc_tab[sj[0] * kbp + kn];
@@ -415,22 +483,33 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
         __builtin_amdgcn_sched_barrier(0);
     }
     };
-    if (mt_active >= 2) kloop(std::integral_constant<int, 2>{});
-    else if (mt_active == 1) kloop(std::integral_constant<int, 1>{});
-    else kloop(std::integral_constant<int, 0>{});
+    if constexpr (C::MT == 4) {
+        // three active groups run the full loop (cheaper than another copy)
+        if (mt_active >= 3) kloop(std::integral_constant<int, 4>{});
+        else if (mt_active == 2) kloop(std::integral_constant<int, 2>{});
+        else if (mt_active == 1) kloop(std::integral_constant<int, 1>{});
+        else kloop(std::integral_constant<int, 0>{});
+    } else {
+        if (mt_active >= 2) kloop(std::integral_constant<int, 2>{});
+        else if (mt_active == 1) kloop(std::integral_constant<int, 1>{});
+        else kloop(std::integral_constant<int, 0>{});
+    }
 
-    // ---- epilogue. 32x32 accumulator layout: lane l holds column l%32 and,
-    //      for register i, row 8*(i/4) + 4*(l/32) + i%4.  Gate/up: the row
-    //      table entries of a lane's rows (four consecutive rows per i/4) are
-    //      read with 16-byte LDS reads, all before the first store, so the
-    //      stores do not wait on LDS one row at a time; down: row m goes to
-    //      sorted row p0 + m.
-    int4 dst4[C::MT][4];
+    // ---- epilogue.  Accumulator layouts: 32x32 -- lane l holds column l%32
+    //      and, for register i, row 8*(i/4) + 4*(l/32) + i%4; 16x16 -- column
+    //      l%16, row 4*(l/16) + i.  Gate/up: the row table entries of a lane's
+    //      rows (four consecutive rows per group of four registers) are read
+    //      with 16-byte LDS reads, all before the first store, so the stores
+    //      do not wait on LDS one row at a time; down: row m goes to sorted
+    //      row p0 + m.
+    constexpr int RQ = AR / 4;                   // groups of four rows per MFMA tile
+    const int ocol = C::M16 ? l16 : ln;          // the lane's column in a tile
+    int4 dst4[C::MT][RQ];
 #pragma unroll
     for (int mt = 0; mt < C::MT; ++mt)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int r0 = wm * C::WROWS + mt * 32 + 8 * q + 4 * lg;
+        for (int q = 0; q < RQ; ++q) {
+            const int r0 = wm * C::WROWS + mt * C::MS + (C::M16 ? 4 * g16 : 8 * q + 4 * lg);
             if (MODE == PF_GATEUP) {
                 dst4[mt][q] = *reinterpret_cast<const int4*>(row_dst + r0);
             } else {
@@ -441,23 +520,23 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
 #pragma unroll
     for (int mt = 0; mt < C::MT; ++mt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
+        for (int i = 0; i < AR; ++i) {
             const int dst = dst4[mt][i >> 2][i & 3];
             if (dst < 0) continue;
             if (MODE == PF_GATEUP) {
-                uint16_t* orow = abuf_out + (size_t)dst * I + nb * (BN / 2) + wn * (C::WCOLS / 2) + ln;
+                uint16_t* orow = abuf_out + (size_t)dst * I + nb * (BN / 2) + wn * (C::WCOLS / 2) + ocol;
 #pragma unroll
                 for (int nt = 0; nt < C::NT / 2; ++nt)
-                    orow[nt * 32] = f32_to_bf16_bits(
+                    orow[nt * C::MS] = f32_to_bf16_bits(
                         swiglu_fast(acc[mt][nt][i] * seff[0], acc[mt][nt + C::NT / 2][i] * seff[1]));
             } else {
                 // y of the route (the combine multiplies it by the affinity);
                 // each contribution row is read once, by the combine: streaming
                 // (non-temporal) stores keep it from occupying the caches
-                float* orow = ybuf + (size_t)dst * H + nb * BN + wn * C::WCOLS + ln;
+                float* orow = ybuf + (size_t)dst * H + nb * BN + wn * C::WCOLS + ocol;
 #pragma unroll
                 for (int nt = 0; nt < C::NT; ++nt)
-                    __builtin_nontemporal_store(acc[mt][nt][i] * seff[0], orow + nt * 32);
+                    __builtin_nontemporal_store(acc[mt][nt][i] * seff[0], orow + nt * C::MS);
             }
         }
 }
@@ -480,6 +559,12 @@ static int launch_pf(const uint16_t* x, const uint16_t* abuf_in, const uint8_t* 
         set_error("prefill: too many tiles");
         return MOE_EUNSUPPORTED;
     }
+    // activation rows are addressed by 32-bit byte offsets
+    const size_t a_bytes = MODE == PF_GATEUP ? (size_t)T * H * 2 : (size_t)(R + (has_shared ? T : 0)) * I * 2;
+    if (a_bytes > 0xFFFFFFFFull) {
+        set_error("prefill: activation matrix over 4 GB");
+        return MOE_EUNSUPPORTED;
+    }
     const size_t kbp = ((size_t)K_of<MODE>(H, I) / 128 + 63) / 64 * 64;
     const size_t lds = (size_t)C::STAGES * C::STAGE + (size_t)(C::BN / 128) * kbp * 4;
     prof_begin(MODE == PF_GATEUP ? "prefill_gateup_swiglu" : "prefill_down", stream);
@@ -489,17 +574,17 @@ static int launch_pf(const uint16_t* x, const uint16_t* abuf_in, const uint8_t* 
     return check_launch(MODE == PF_GATEUP ? "prefill_gemm_kernel<gateup>" : "prefill_gemm_kernel<down>");
 }
 
-template <int LAYOUT, class C>
+template <int LAYOUT>
 static int launch_prefill_c(const uint16_t* x, const uint8_t* w13, const float* w13s,
                             const uint8_t* w2, const float* w2s, const SharedW& sh,
                             const Plan& plan, int T, int H, int I, int E, int k, uint16_t* abuf,
                             float* ybuf, hipStream_t stream) {
     const int hs = sh.w13 != nullptr;
-    int rc = launch_pf<PF_GATEUP, LAYOUT, C>(x, nullptr, w13, w13s, sh.w13, sh.w13_scale, plan, T,
-                                             H, I, E, k, hs, abuf, ybuf, stream);
+    int rc = launch_pf<PF_GATEUP, LAYOUT, PfGateUp>(x, nullptr, w13, w13s, sh.w13, sh.w13_scale,
+                                                    plan, T, H, I, E, k, hs, abuf, ybuf, stream);
     if (rc == MOE_OK)
-        rc = launch_pf<PF_DOWN, LAYOUT, C>(x, abuf, w2, w2s, sh.w2, sh.w2_scale, plan, T, H, I, E,
-                                           k, hs, abuf, ybuf, stream);
+        rc = launch_pf<PF_DOWN, LAYOUT, PfDown>(x, abuf, w2, w2s, sh.w2, sh.w2_scale, plan, T, H, I,
+                                                E, k, hs, abuf, ybuf, stream);
     return rc;
 }
 
@@ -516,10 +601,10 @@ int launch_prefill_ffn(int layout, const uint16_t* x, const uint8_t* w13, const 
         return MOE_EINVAL;
     }
     if (layout == LAYOUT_TILED)
-        return launch_prefill_c<LAYOUT_TILED, PfTile>(x, w13, w13s, w2, w2s, sh, plan, T, H, I, E,
-                                                      k, abuf, ybuf, stream);
-    return launch_prefill_c<LAYOUT_ROWMAJOR, PfTile>(x, w13, w13s, w2, w2s, sh, plan, T, H, I, E,
-                                                     k, abuf, ybuf, stream);
+        return launch_prefill_c<LAYOUT_TILED>(x, w13, w13s, w2, w2s, sh, plan, T, H, I, E, k, abuf,
+                                              ybuf, stream);
+    return launch_prefill_c<LAYOUT_ROWMAJOR>(x, w13, w13s, w2, w2s, sh, plan, T, H, I, E, k, abuf,
+                                             ybuf, stream);
 }
 
 }  // namespace moe
