@@ -265,6 +265,38 @@ def test_fused_single_expert_dense(variant, layout):
     assert_out_close(np_(out), ref, what=f"E=1/{variant}/{layout}")
 
 
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_fused_at_expert_and_topk_limits(variant, layout):
+    """E = 1024 experts and k = 16 (the interface's limits) with the shared expert."""
+    cfg = synth.MoeConfig("limits", T=40, H=256, I=128, E=1024, k=16, shared=True)
+    c = gpu_case(cfg, seed=11)
+    ids, aff = binding.route(c["logits"], cfg.k)
+    ref_ids, ref_aff = oracle.route_softmax_topk(np_(c["logits"]), cfg.k)
+    assert np.array_equal(np_(ids), ref_ids)
+    out = _fused(c, ids, aff, variant=variant, layout=layout)
+    ref = oracle_rows(c, ref_ids, ref_aff, np.arange(cfg.T))
+    assert_out_close(np_(out), ref, what=f"E=1024,k=16/{variant}/{layout}")
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_empty_batch_on_device(variant):
+    """T = 0 through the binding: route and the fused call are no-ops, the
+    sort returns zero counts and offsets."""
+    cfg = synth.MoeConfig("empty", T=3, H=256, I=128, E=8, k=2)
+    c = gpu_case(cfg, seed=12)
+    ids, aff = binding.route(c["logits"][:0], cfg.k)
+    assert tuple(ids.shape) == (0, cfg.k) and tuple(aff.shape) == (0, cfg.k)
+    counts, offsets, sorted_route, inv_route = binding.sort(ids, cfg.E)
+    torch.cuda.synchronize()
+    assert int(counts.abs().sum()) == 0 and int(offsets.abs().sum()) == 0
+    assert sorted_route.numel() == 0 and inv_route.numel() == 0
+    out = binding.fused_w8a16(c["x"][:0], c["w13"], c["w13_scale"], c["w2"], c["w2_scale"], ids,
+                              aff, variant=variant)
+    torch.cuda.synchronize()
+    assert tuple(out.shape) == (0, cfg.H)
+
+
 def test_fused_bad_ids_are_dropped():
     cfg = synth.MoeConfig("bad", T=6, H=256, I=128, E=8, k=2)
     c = gpu_case(cfg, seed=8)
