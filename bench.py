@@ -193,6 +193,52 @@ def profiled_traffic(kernel, workload):
     return int(got["traffic_bytes_per_launch"])
 
 
+def fused_call_graph(cfg, m, samples=7, replays=50):
+    """One moe_fused_w8a16 call (sort + expert FFN + expert sum, from ids and
+    affinities to out) per weight set, captured once in a HIP graph; the
+    median over `samples` of `replays` graph launches, per call."""
+    import statistics
+
+    import torch
+    runs, L = m["runs"], m["L"]
+    for r in runs:
+        r()  # route once: the graph replays the fused calls on these ids
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for r in runs:
+            r.fused()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for r in runs:
+            r.fused()
+    for _ in range(10):
+        g.replay()
+    torch.cuda.synchronize()
+    per_call = []
+    for _ in range(samples):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(replays):
+            g.replay()
+        e.record()
+        torch.cuda.synchronize()
+        per_call.append(s.elapsed_time(e) * 1e3 / (replays * L))
+    us = statistics.median(per_call)
+    R = cfg.T * cfg.k
+    flops = step_flops(cfg, cfg.shared)
+    nbytes = step_bytes(cfg, m["n_active"], cfg.shared) - 4 * cfg.T * cfg.E  # no logits
+    del g
+    return {"protocol": f"HIP graph of one fused call per weight set ({L} sets), median of "
+                        f"{samples} samples x {replays} replays",
+            "us_per_call": round(us, 2), "tokens_per_s": round(cfg.T / (us * 1e-6), 1),
+            "routes": R, "TFLOP_per_s": round(flops / (us * 1e-6) / 1e12, 1),
+            "mfma_frac": round(flops / (us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "GB_per_s": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def vendor_gemm(cfg, dev, warmup=200, reps=50):
     """Same-box context for the MFMA fraction: the rate of torch.matmul (the
     vendor bf16 GEMM library) on the dense product with the gate/up shape of
@@ -345,6 +391,8 @@ def main():
                  "ms_per_step_profiled": round(ms_profiled, 5)},
         "kernels": kernels,
     }
+    log("fused call in a HIP graph ...")
+    result["fused_call"] = fused_call_graph(cfg, m)
     if args.prefill_workload:
         pcfg = synth.CONFIGS[args.prefill_workload]
         del m
@@ -352,6 +400,8 @@ def main():
         pm = measure(pcfg, 2, args.prefill_steps, args.prefill_warmup, "auto", args.layout,
                      args.seed, dev)
         result["prefill"] = prefill_summary(pcfg, pm)
+        log("prefill fused call in a HIP graph ...")
+        result["prefill"]["fused_call"] = fused_call_graph(pcfg, pm)
         del pm
         torch.cuda.empty_cache()
         if not args.no_vendor_gemm:

@@ -310,3 +310,9 @@ class MoeStep:
             rc = self._lib.moe_fused_w8a16(*self._fused_args, st)
         _check(rc)
         return self.out
+
+    def fused(self):
+        """Enqueue only the fused call (sort + expert FFN + expert sum) on the
+        ids and affinities of the last routing pass."""
+        _check(self._lib.moe_fused_w8a16(*self._fused_args, _stream(self._dev)))
+        return self.out
