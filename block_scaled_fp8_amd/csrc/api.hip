@@ -197,6 +197,9 @@ int moe_fused_w8a16(const void* x, const uint8_t* w13, const float* w13_scale,
     if (variant == MOE_VARIANT_AUTO)
         variant = ((long long)T * k <= 32LL * E || !prefill_supported(H, I)) ? MOE_VARIANT_DECODE
                                                                              : MOE_VARIANT_PREFILL;
+    if (variant == MOE_VARIANT_PREFILL) {
+        if (int rc = prefill_check(T, H, I, E, k, has_shared)) return rc;
+    }
 
     char* base = static_cast<char*>(ws);
     Plan p;

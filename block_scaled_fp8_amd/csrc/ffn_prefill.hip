@@ -14,10 +14,10 @@
 // gfx950 design.  Kernel 1 (gate/up): each workgroup computes a 128-row x
 // (128 gate + 128 up) tile of one segment, applies SwiGLU in registers and
 // writes bf16 activations (abuf, sorted row order).  Kernel 2 (down): each
-// workgroup computes a 128-row x 256-column tile of y = a W2^T, multiplies it
-// by the route's affinity and writes fp32 rows at their sorted position (a
-// tile's rows are contiguous); the final combine gathers the k rows of a token
-// through the inverse route map.
+// workgroup computes a 128-row x 256-column tile of y = a W2^T and writes
+// fp32 rows at their sorted position (a tile's rows are contiguous); the final
+// combine gathers the k rows of a token through the inverse route map and
+// applies the affinities.
 //
 //  * Workgroup tile 128 rows x 256 columns (gate/up: 128 gate + the matching
 //    128 up columns), 4 waves (2 x 2), each a 64 x 128 tile with 128 fp32
@@ -41,13 +41,15 @@
 //    block starts (running scale), never by rounding it into bf16.
 //  * Work list: the sort lists every full 128-row tile first and the partial
 //    last tiles after them; the list is cut into runs of 8 row tiles dealt
-//    round-robin to the 8 XCDs (all column blocks of a row tile on one XCD),
-//    so every XCD gets an equal share of both kinds and the last round of
-//    workgroups holds the cheap partial tiles, whose empty 32-row MFMA groups
-//    are skipped.  The grid covers the worst case and idle workgroups exit.
-//  * Epilogue: a lane's row-table entries come in 16-byte LDS reads before
-//    any store (gate/up: SwiGLU, bf16 stores; down: affinity scale, fp32
-//    non-temporal stores).
+//    round-robin to the 8 XCDs (all column blocks of a row tile on one XCD,
+//    so consecutive tiles of one expert share its weights in L2), and the
+//    last round of workgroups holds the cheap partial tiles, whose empty
+//    MFMA row groups (16 rows gate/up, 32 down) are skipped.  The grid covers
+//    the worst case and idle workgroups exit.
+//  * Epilogue: gate/up reads a lane's row-table entries with 16-byte LDS
+//    reads before any store, applies SwiGLU and stores bf16; down stores its
+//    fp32 rows with non-temporal stores.
+#include <algorithm>
 #include <type_traits>
 
 #include "common.hpp"
@@ -163,11 +165,13 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
     //      (id % 8).  The sort's tile list is cut into blocks of PF_XCD_RUN
     //      consecutive row tiles, dealt round-robin to the XCDs; XCD x walks
     //      its blocks in order, each row tile with all its column blocks.  So
-    //      every XCD gets an equal share of the full tiles (listed first) and
-    //      of the partial ones (listed last: the last round of workgroups is
-    //      the cheapest), while consecutive tiles of one expert stay on one
-    //      XCD and share its weights in L2.  The grid covers the worst case;
-    //      the rest exit.
+    //      every XCD gets an equal share of the full tiles (listed first, to
+    //      within one block) before the partial ones (listed last: the last
+    //      round of workgroups is the cheapest), while consecutive tiles of
+    //      one expert stay on one XCD and share its weights in L2.  (Dealing
+    //      the trailing tiles one at a time instead measured slower: the last
+    //      full tiles lose that sharing.)  The grid covers the worst case; the
+    //      rest exit.
     const int bid = blockIdx.x;
     const int jx = bid >> 3, q = jx / nblk;
     const int tile = (q / PF_XCD_RUN) * (8 * PF_XCD_RUN) + (bid & 7) * PF_XCD_RUN + q % PF_XCD_RUN;
@@ -586,6 +590,26 @@ static int launch_prefill_c(const uint16_t* x, const uint8_t* w13, const float* 
         rc = launch_pf<PF_DOWN, LAYOUT, PfDown>(x, abuf, w2, w2s, sh.w2, sh.w2_scale, plan, T, H, I,
                                                 E, k, hs, abuf, ybuf, stream);
     return rc;
+}
+
+// Host-side checks of a prefill call, before anything is launched.
+int prefill_check(int T, int H, int I, int E, int k, int has_shared) {
+    if (!prefill_supported(H, I)) {
+        set_error("prefill variant needs H %% 256 == 0, 2I %% 256 == 0 and H, I <= 65536 (got H=%d, I=%d)", H, I);
+        return MOE_EUNSUPPORTED;
+    }
+    const long R = (long)T * k, rows = R + (has_shared ? T : 0);
+    if ((long)T * H * 2 > 0xFFFFFFFFL || rows * I * 2 > 0xFFFFFFFFL) {
+        set_error("prefill: activation matrix over 4 GB");
+        return MOE_EUNSUPPORTED;
+    }
+    const long tiles = (R + PF_BM - 1) / PF_BM + E + (has_shared ? (T + PF_BM - 1) / PF_BM : 0);
+    const long nblk = std::max(2L * I, (long)H) / 256;
+    if (8L * nblk * PF_XCD_RUN * ((tiles + 8 * PF_XCD_RUN - 1) / (8 * PF_XCD_RUN)) > 0x7FFFFFFFL) {
+        set_error("prefill: too many tiles");
+        return MOE_EUNSUPPORTED;
+    }
+    return MOE_OK;
 }
 
 int launch_prefill_ffn(int layout, const uint16_t* x, const uint8_t* w13, const float* w13s,

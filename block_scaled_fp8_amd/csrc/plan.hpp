@@ -61,6 +61,8 @@ int launch_pack_w8(const uint8_t* src, uint8_t* dst, int64_t n_mats, int rows, i
                    hipStream_t stream);
 int prefill_tile_m();
 int prefill_supported(int H, int I);
+// MOE_OK, or MOE_EUNSUPPORTED with the error message set.
+int prefill_check(int T, int H, int I, int E, int k, int has_shared);
 // Sums, per token, the k route rows whose id is valid (plus the shared row at
 // R + t).  Decode producers write aff * y at row r (inv_route and aff null);
 // prefill producers write y at the route's sorted position, and the sum takes

@@ -99,6 +99,10 @@ def test_fused_argument_checks():
     lib.moe_fused_w8a16.argtypes[12] = ctypes.POINTER(binding.ExpertW8)
     assert lib.moe_fused_w8a16(*a) == binding.MOE_EINVAL
     assert b"shared" in lib.moe_last_error()
+    # the prefill variant needs H and 2I in multiples of 256: refused before any launch
+    ws384 = lib.moe_fused_workspace_bytes(64, 384, 128, 256, 8, 0, 2)
+    assert lib.moe_fused_w8a16(*args(64, 384, 128, 256, 8, ws384, 2)) == binding.MOE_EUNSUPPORTED
+    assert b"prefill variant needs" in lib.moe_last_error()
     # T == 0 is a no-op
     assert lib.moe_fused_w8a16(*args(0, 2048, 512, 256, 8, 0)) == binding.MOE_OK
 
