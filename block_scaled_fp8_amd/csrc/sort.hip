@@ -20,7 +20,7 @@
 namespace moe {
 
 constexpr int SORT_SMALL_THREADS = 1024;      // single-workgroup path
-constexpr int SORT_SMALL_MAX_ROUTES = 16384;
+constexpr int SORT_SMALL_MAX_ROUTES = 4096;  // measured: one workgroup is as fast up to here, slower above
 constexpr int SORT_CHUNK = 2048;              // routes per workgroup, multi-workgroup path
 constexpr int SORT_THREADS = 256;
 
