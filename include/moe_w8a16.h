@@ -158,7 +158,8 @@ typedef struct {
  * H and I must be multiples of 128 (else MOE_EUNSUPPORTED); T >= 0; T == 0
  * is a no-op.  MOE_VARIANT_PREFILL also needs H and 2I to be multiples of
  * 256 (else MOE_EUNSUPPORTED); MOE_VARIANT_AUTO picks the decode variant for
- * such shapes and for batches of at most 32 routes per expert.  The expert FFN computes in bf16 x bf16 products with fp32
+ * such shapes and for batches of at most 16 routes per expert and 4096 routes
+ * in all, the prefill variant otherwise.  The expert FFN computes in bf16 x bf16 products with fp32
  * accumulation; each 128-wide K block's partial sum is multiplied by its
  * fp32 block scale; the SwiGLU output is rounded to bf16 before the down GEMM.
  */
