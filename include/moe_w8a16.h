@@ -63,7 +63,7 @@ enum {
 };
 
 enum {
-    MOE_VARIANT_AUTO = 0,     /* decode when T*k/E <= 32 routes per expert, else prefill */
+    MOE_VARIANT_AUTO = 0,     /* decode for T*k <= 16E and T*k <= 4096, else prefill */
     MOE_VARIANT_DECODE = 1,   /* weight-streaming kernels, one workgroup per (expert, N tile) */
     MOE_VARIANT_PREFILL = 2   /* grouped bf16-MFMA GEMM over 128-row tiles of sorted routes */
 };
@@ -159,8 +159,9 @@ typedef struct {
  * is a no-op.  MOE_VARIANT_PREFILL also needs H and 2I to be multiples of
  * 256 (else MOE_EUNSUPPORTED); MOE_VARIANT_AUTO picks the decode variant for
  * such shapes and for batches of at most 16 routes per expert and 4096 routes
- * in all, the prefill variant otherwise.  The expert FFN computes in bf16 x bf16 products with fp32
- * accumulation; each 128-wide K block's partial sum is multiplied by its
+ * in all, the prefill variant otherwise.  The expert FFN computes in bf16 x
+ * bf16 products with fp32 accumulation; each 128-wide K block's partial sum
+ * is multiplied by its
  * fp32 block scale; the SwiGLU output is rounded to bf16 before the down GEMM.
  */
 size_t moe_fused_workspace_bytes(int T, int H, int I, int E, int k,
