@@ -128,7 +128,7 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_ffn_kernel(
         auto issue = [&](int d, int c) {
 #pragma unroll
             for (int j = 0; j < DEC_NTILE; ++j)
-                bq[d][j] = *reinterpret_cast<const u32x4*>(bptr[j] + (size_t)c * chunk_stride<LAYOUT>());
+                bq[d][j] = load_stream16(bptr[j] + (size_t)c * chunk_stride<LAYOUT>());
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
                 const u32x4* ap = reinterpret_cast<const u32x4*>(aptr[mt] + (size_t)c * 64);

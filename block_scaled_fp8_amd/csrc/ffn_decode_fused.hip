@@ -196,8 +196,7 @@ __global__ __launch_bounds__(DF_THREADS) void decode_fused_kernel(
 #pragma unroll
             for (int j = 0; j < NT; ++j) {
                 const int r = (j < HALF ? 0 : I) + (g * HALF + (j % HALF)) * 16;
-                bq[d][j] = *reinterpret_cast<const u32x4*>(tile_lane_ptr<LAYOUT>(W13, r, H, lane) +
-                                                           (size_t)c * CS);
+                bq[d][j] = load_stream16(tile_lane_ptr<LAYOUT>(W13, r, H, lane) + (size_t)c * CS);
             }
         };
         auto issue1_a = [&](int d, int c) {
@@ -217,8 +216,8 @@ __global__ __launch_bounds__(DF_THREADS) void decode_fused_kernel(
             const int g = ig % G2;
 #pragma unroll
             for (int j = 0; j < NT; ++j)
-                bq[d][j] = *reinterpret_cast<const u32x4*>(
-                    tile_lane_ptr<LAYOUT>(W2, (g * NT + j) * 16, I, lane) + (size_t)ic * CS);
+                bq[d][j] = load_stream16(tile_lane_ptr<LAYOUT>(W2, (g * NT + j) * 16, I, lane) +
+                                         (size_t)ic * CS);
             if (++ic == nch2) { ic = 0; ig += DF_WAVES; }
         };
 
