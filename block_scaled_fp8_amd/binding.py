@@ -24,7 +24,8 @@ VARIANTS = {"auto": 0, "decode": 1, "prefill": 2}
 LAYOUTS = {"rowmajor": 0, "tiled": 1}
 
 EXPORTED = (
-    "moe_last_error", "moe_route", "moe_sort_workspace_bytes", "moe_sort",
+    "moe_last_error", "moe_route", "moe_route_proj_workspace_bytes", "moe_route_proj",
+    "moe_sort_workspace_bytes", "moe_sort",
     "moe_fused_workspace_bytes", "moe_fused_w8a16", "moe_decode_e4m3fn", "moe_pack_w8",
     "moe_profile_enable", "moe_profile_collect", "moe_profile_count", "moe_profile_stat",
 )
@@ -63,6 +64,10 @@ def load_library():
     lib.moe_last_error.argtypes = []
     lib.moe_route.restype = i32
     lib.moe_route.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp]
+    lib.moe_route_proj_workspace_bytes.restype = sz
+    lib.moe_route_proj_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.moe_route_proj.restype = i32
+    lib.moe_route_proj.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
     lib.moe_sort_workspace_bytes.restype = sz
     lib.moe_sort_workspace_bytes.argtypes = [i32, i32, i32]
     lib.moe_sort.restype = i32
@@ -130,6 +135,36 @@ def route(logits: torch.Tensor, k: int, status: torch.Tensor | None = None):
         _need(status, "status", torch.int32, dev)
     _check(lib.moe_route(_ptr(logits), T, E, k, _ptr(ids), _ptr(aff), _ptr(status), _stream(dev)))
     return ids, aff
+
+
+def route_proj_workspace_bytes(T: int, H: int, E: int) -> int:
+    return int(load_library().moe_route_proj_workspace_bytes(T, H, E))
+
+
+def route_proj(x: torch.Tensor, wg: torch.Tensor, k: int, logits: bool = False,
+               status: torch.Tensor | None = None, ws=None):
+    """Router projection then routing: x [T, H] bf16, wg [E, H] bf16 ->
+    (ids [T, k] int32, aff [T, k] fp32), plus the fp32 logits [T, E] when
+    ``logits`` is true."""
+    lib = load_library()
+    _need(x, "x", torch.bfloat16)
+    dev = x.device
+    _need(wg, "wg", torch.bfloat16, dev)
+    T, H = x.shape
+    E = wg.shape[0]
+    if wg.shape[1] != H:
+        raise ValueError(f"wg has shape {tuple(wg.shape)}, expected [E, {H}]")
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    aff = torch.empty((T, k), dtype=torch.float32, device=dev)
+    lg = torch.empty((T, E), dtype=torch.float32, device=dev) if logits else None
+    if ws is None:
+        need = int(lib.moe_route_proj_workspace_bytes(T, H, E))
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    if status is not None:
+        _need(status, "status", torch.int32, dev)
+    _check(lib.moe_route_proj(_ptr(x), _ptr(wg), T, H, E, k, _ptr(lg), _ptr(ids), _ptr(aff),
+                              _ptr(status), _ptr(ws), ws.numel(), _stream(dev)))
+    return (ids, aff, lg) if logits else (ids, aff)
 
 
 def sort_workspace_bytes(T: int, k: int, E: int) -> int:

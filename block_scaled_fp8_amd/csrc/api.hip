@@ -109,6 +109,40 @@ int moe_route(const float* logits, int T, int E, int k, int32_t* ids, float* aff
     return launch_route(logits, T, E, k, ids, aff, status, (hipStream_t)stream);
 }
 
+size_t moe_route_proj_workspace_bytes(int T, int H, int E) {
+    if (T < 1 || H < 64 || H % 64 || E < 1 || E > MOE_MAX_EXPERTS) return 0;
+    return route_proj_workspace_bytes(T, H, E);
+}
+
+int moe_route_proj(const void* x, const void* wg, int T, int H, int E, int k, float* logits,
+                   int32_t* ids, float* aff, int32_t* status, void* ws, size_t ws_bytes,
+                   void* stream) {
+    g_err[0] = 0;
+    if (int rc = check_route_args(T, E, k)) return rc;
+    if (H < 64 || H % 64) {
+        set_error("moe_route_proj: H must be a positive multiple of 64 (got %d)", H);
+        return MOE_EUNSUPPORTED;
+    }
+    if (T == 0) return MOE_OK;
+    if (!x || !wg || !ids || !aff) {
+        set_error("moe_route_proj: x, wg, ids and aff must be non-NULL");
+        return MOE_EINVAL;
+    }
+    if (((uintptr_t)x | (uintptr_t)wg) & 15) {
+        set_error("moe_route_proj: x and wg must be 16-byte aligned");
+        return MOE_EINVAL;
+    }
+    const bool direct = route_proj_splits(T, H, E) == 1 && logits;  // no slab needed
+    const size_t need = route_proj_workspace_bytes(T, H, E);
+    if (!direct && (!ws || ws_bytes < need)) {
+        set_error("moe_route_proj: workspace of %zu bytes needed (got %zu)", need, ws_bytes);
+        return MOE_EINVAL;
+    }
+    return launch_route_proj(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wg), T,
+                             H, E, k, logits, ids, aff, status, static_cast<float*>(ws),
+                             (hipStream_t)stream);
+}
+
 size_t moe_sort_workspace_bytes(int T, int k, int E) {
     if (T < 0 || k < 1 || E < 1) return 0;
     return sort_scratch_bytes(T * k, E);

@@ -44,6 +44,16 @@ int launch_sort(const int32_t* ids, int T, int k, int E, const Plan& plan, int h
 // Kernel launchers (route.hip, ffn_decode.hip, ffn_prefill.hip, misc).
 int launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* aff,
                  int32_t* status, hipStream_t stream);
+// The router on nslab partial-logit slabs [nslab][T][E] added in slab order;
+// the sums go to logits_out when it is not NULL.
+int launch_route_slabs(const float* part, int nslab, float* logits_out, int T, int E, int k,
+                       int32_t* ids, float* aff, int32_t* status, hipStream_t stream);
+// Router projection (route_proj.hip): logits = x * wg^T, then the router.
+int route_proj_splits(int T, int H, int E);
+size_t route_proj_workspace_bytes(int T, int H, int E);
+int launch_route_proj(const uint16_t* x, const uint16_t* wg, int T, int H, int E, int k,
+                      float* logits, int32_t* ids, float* aff, int32_t* status, float* ws,
+                      hipStream_t stream);
 // Both FFN variants write, for every valid route r = t*k + j, the row
 // aff[r] * MLP_e(x_t) (fp32, H wide): the decode variant at y[r], the prefill
 // variant at its sorted position y[inv_route[r]]; the shared expert's row of

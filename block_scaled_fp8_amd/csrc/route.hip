@@ -76,14 +76,49 @@ __device__ __forceinline__ uint32_t wave_red_u32(uint32_t v) {
 // index among their heads (a wave minimum).  Either way the chosen entry is
 // the largest key with the lowest expert index, and it leaves its lane's list.
 // Padding entries (expert >= E) are never candidates.
-template <int NPL>
+//
+// SLABS: the logits arrive as nslab (<= RT_MAX_SLABS) partial sums
+// logits[s][t][e] of a K-split projection; they are added in slice order (all
+// loads issued first, a clamped duplicate masked out) and, when logits_out is
+// given, the sums are written there.
+constexpr int RT_MAX_SLABS = 8;
+
+template <int NPL, bool SLABS>
 __global__ __launch_bounds__(256) void route_topk_softmax_kernel(
-    const float* __restrict__ logits, int T, int E, int k,
-    int32_t* __restrict__ ids, float* __restrict__ aff, int32_t* __restrict__ status) {
+    const float* __restrict__ logits, int nslab, float* __restrict__ logits_out, int T, int E,
+    int k, int32_t* __restrict__ ids, float* __restrict__ aff, int32_t* __restrict__ status) {
     const int lane = lane_id();
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
     const float* row = logits + (size_t)t * E;
+
+    float lv[NPL];
+    if (SLABS) {
+        const size_t slab = (size_t)T * E;
+        float pv[RT_MAX_SLABS][NPL];
+#pragma unroll
+        for (int s = 0; s < RT_MAX_SLABS; ++s)
+#pragma unroll
+            for (int i = 0; i < NPL; ++i) {
+                const int e = min(lane + MOE_WAVE * i, E - 1);
+                pv[s][i] = row[(size_t)min(s, nslab - 1) * slab + e];
+            }
+#pragma unroll
+        for (int i = 0; i < NPL; ++i) {
+            float v = pv[0][i];
+#pragma unroll
+            for (int s = 1; s < RT_MAX_SLABS; ++s) v += s < nslab ? pv[s][i] : 0.0f;
+            lv[i] = v;
+            const int e = lane + MOE_WAVE * i;
+            if (logits_out && e < E) logits_out[(size_t)t * E + e] = v;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < NPL; ++i) {
+            const int e = lane + MOE_WAVE * i;
+            lv[i] = e < E ? row[e] : 0.0f;
+        }
+    }
 
     uint32_t key[NPL];
     int slot[NPL];  // -1: no candidate
@@ -92,7 +127,7 @@ __global__ __launch_bounds__(256) void route_topk_softmax_kernel(
     for (int i = 0; i < NPL; ++i) {
         const int e = lane + MOE_WAVE * i;
         const bool in = e < E;
-        const float v = in ? row[e] : 0.0f;
+        const float v = lv[i];
         bad |= in && !__builtin_isfinite(v);
         key[i] = in ? ordered_bits(v) : 0u;
         slot[i] = in ? i : -1;
@@ -151,23 +186,41 @@ __global__ __launch_bounds__(256) void route_topk_softmax_kernel(
     }
 }
 
-int launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* aff,
-                 int32_t* status, hipStream_t stream) {
+template <bool SLABS>
+static int launch_route_impl(const float* logits, int nslab, float* logits_out, int T, int E,
+                             int k, int32_t* ids, float* aff, int32_t* status,
+                             hipStream_t stream) {
     const int npl = (E + MOE_WAVE - 1) / MOE_WAVE;
     const dim3 grid((T + 3) / 4), block(256);
     prof_begin("route_topk_softmax", stream);
     if (npl <= 1)
-        route_topk_softmax_kernel<1><<<grid, block, 0, stream>>>(logits, T, E, k, ids, aff, status);
+        route_topk_softmax_kernel<1, SLABS><<<grid, block, 0, stream>>>(logits, nslab, logits_out, T, E, k, ids, aff, status);
     else if (npl <= 2)
-        route_topk_softmax_kernel<2><<<grid, block, 0, stream>>>(logits, T, E, k, ids, aff, status);
+        route_topk_softmax_kernel<2, SLABS><<<grid, block, 0, stream>>>(logits, nslab, logits_out, T, E, k, ids, aff, status);
     else if (npl <= 4)
-        route_topk_softmax_kernel<4><<<grid, block, 0, stream>>>(logits, T, E, k, ids, aff, status);
+        route_topk_softmax_kernel<4, SLABS><<<grid, block, 0, stream>>>(logits, nslab, logits_out, T, E, k, ids, aff, status);
     else if (npl <= 8)
-        route_topk_softmax_kernel<8><<<grid, block, 0, stream>>>(logits, T, E, k, ids, aff, status);
+        route_topk_softmax_kernel<8, SLABS><<<grid, block, 0, stream>>>(logits, nslab, logits_out, T, E, k, ids, aff, status);
     else
-        route_topk_softmax_kernel<16><<<grid, block, 0, stream>>>(logits, T, E, k, ids, aff, status);
+        route_topk_softmax_kernel<16, SLABS><<<grid, block, 0, stream>>>(logits, nslab, logits_out, T, E, k, ids, aff, status);
     prof_end(stream);
     return check_launch("route_topk_softmax_kernel");
+}
+
+int launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* aff,
+                 int32_t* status, hipStream_t stream) {
+    return launch_route_impl<false>(logits, 1, nullptr, T, E, k, ids, aff, status, stream);
+}
+
+int launch_route_slabs(const float* part, int nslab, float* logits_out, int T, int E, int k,
+                       int32_t* ids, float* aff, int32_t* status, hipStream_t stream) {
+    if (nslab < 1 || nslab > RT_MAX_SLABS) {
+        set_error("router: %d partial slabs (1..%d supported)", nslab, RT_MAX_SLABS);
+        return MOE_EINVAL;
+    }
+    if (nslab == 1 && !logits_out)
+        return launch_route_impl<false>(part, 1, nullptr, T, E, k, ids, aff, status, stream);
+    return launch_route_impl<true>(part, nslab, logits_out, T, E, k, ids, aff, status, stream);
 }
 
 }  // namespace moe

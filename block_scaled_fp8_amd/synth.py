@@ -32,6 +32,9 @@ Recipe (every draw is seeded; ``seed`` selects the stream):
 * ``w2``   uint8 [E, H, I]; ``w2_scale`` fp32 [E, H/128, I/128].
 * shared expert (optional): the same format for one expert, drawn after the
   routed experts.
+* ``wg``  bf16 [E, H] router gate weights (for the router projection):
+  N(0, 0.02) in fp32 rounded to nearest-even bf16; with x ~ N(0, 1) the
+  projected logits have standard deviation 0.02 * sqrt(H) (0.9 at H = 2048).
 """
 from __future__ import annotations
 
@@ -144,6 +147,13 @@ def make_weights(cfg: MoeConfig, seed: int, device="cpu"):
     else:
         out["shared"] = None
     return out
+
+
+def make_gate_weights(E: int, H: int, seed: int, device="cpu"):
+    """Router gate weights [E, H] bf16 ~ N(0, 0.02)."""
+    g = _gen(seed, 7, device)
+    w = torch.randn((E, H), generator=g, device=device, dtype=torch.float32) * 0.02
+    return w.to(torch.bfloat16).contiguous()
 
 
 def make_case(cfg: MoeConfig | str, seed: int = 0, device="cpu"):

@@ -93,6 +93,32 @@ int moe_route(const float* logits, int T, int E, int k,
               int32_t* ids, float* aff, int32_t* status, void* stream);
 
 /*
+ * moe_route_proj -- router projection followed by the router:
+ *     logits[t][e] = sum_h x[t][h] * wg[e][h]   (bf16 x bf16 products, fp32 sums)
+ * then exactly what moe_route computes on those fp32 logits.
+ * Sources: "spark_model/layers/nemotron_moe.rs", prefill forward (a batched
+ * gate GEMM [N, H] x [H, E]^T -> [N, E] feeds the top-K routing); "NKI
+ * Library Supported Kernel Reference", Router Top-K (router logits and top-K
+ * selection in one kernel).
+ *   x       [T, H] bf16 (raw 16-bit patterns), 16-byte aligned      (in)
+ *   wg      [E, H] bf16 gate weights, 16-byte aligned               (in)
+ *   logits  [T, E] fp32, or NULL when not wanted                     (out)
+ *   ids, aff, status: as for moe_route                               (out)
+ *   ws, ws_bytes: device scratch of moe_route_proj_workspace_bytes(T, H, E)
+ *           bytes; it may be NULL/0 when that shape runs as one K slice
+ *           and logits is given (the workspace function still returns the
+ *           size to pass in general).
+ * H must be a positive multiple of 64 (else MOE_EUNSUPPORTED); T, E and k as
+ * for moe_route; T == 0 is a no-op.  The sum over h is split into at most 8
+ * consecutive K slices whose partial sums are added in slice order, so the
+ * logits are the same from call to call.
+ */
+size_t moe_route_proj_workspace_bytes(int T, int H, int E);
+int moe_route_proj(const void* x, const void* wg, int T, int H, int E, int k, float* logits,
+                   int32_t* ids, float* aff, int32_t* status, void* ws, size_t ws_bytes,
+                   void* stream);
+
+/*
  * moe_sort -- per-expert histogram, exclusive scan, stable sorted route map
  * and its inverse.  Sources: nemotron_moe.rs page (sort by expert before the
  * grouped GEMM, unpermute-reduce after); AITER PR page (sorting and inverse

@@ -21,6 +21,8 @@ Sources (page title, then section):
 * [AITER] "Add gfx950 Q256 fused MXFP4 prefill pipeline" (ROCm/aiter
   PR #5988), description: tokens sorted by expert with an inverse route map,
   an FP32 route reduction, and one always-on shared expert.
+* [NKILIB] "NKI Library Supported Kernel Reference", Router Top-K: the router
+  computes its logits from the hidden states and then selects the top K.
 
 Readings where the pages are silent:
 
@@ -105,6 +107,25 @@ def route_softmax_topk(logits, k: int):
     sel = np.take_along_axis(p, ids.astype(np.int64), axis=1)
     aff = sel / sel.sum(axis=1, keepdims=True)
     return ids, aff
+
+
+# --------------------------------------------------------------------------
+# Router projection  ([SPARK] prefill forward: a batched gate GEMM takes the
+# normalised hidden states [N, H] and the gate weights [E, H] to gate logits
+# [N, E], which the top-K routing consumes; [NKILIB] Router Top-K: router
+# logits, then top-K selection)
+# --------------------------------------------------------------------------
+def router_logits(x, wg):
+    """logits[t, e] = sum over h of x[t, h] * wg[e, h], in float64.
+
+    x is [T, H] and wg [E, H] (bf16 values given as float32/float64).  The
+    router itself is route_softmax_topk on these logits; a device that sums in
+    fp32 routes on its own fp32 logits, so the two agree exactly only where no
+    two candidate logits lie within the fp32 summation error of each other."""
+    x = np.asarray(x, dtype=np.float64)
+    wg = np.asarray(wg, dtype=np.float64)
+    assert x.ndim == 2 and wg.ndim == 2 and x.shape[1] == wg.shape[1]
+    return x @ wg.T
 
 
 # --------------------------------------------------------------------------

@@ -22,7 +22,7 @@ def _declared_functions():
 
 def test_header_declares_the_boundary():
     names = _declared_functions()
-    for n in ("moe_route", "moe_sort", "moe_fused_w8a16", "moe_last_error",
+    for n in ("moe_route", "moe_route_proj", "moe_sort", "moe_fused_w8a16", "moe_last_error",
               "moe_sort_workspace_bytes", "moe_fused_workspace_bytes", "moe_decode_e4m3fn",
               "moe_pack_w8"):
         assert n in names
@@ -54,6 +54,34 @@ def test_route_argument_checks():
     assert lib.moe_route(fake, 4, 8, 2, None, fake, None, None) == binding.MOE_EINVAL
     # T == 0 is a no-op that never touches the device
     assert lib.moe_route(None, 0, 8, 2, None, None, None, None) == binding.MOE_OK
+    assert lib.moe_last_error() == b""
+
+
+def test_route_proj_argument_checks():
+    lib = binding.load_library()
+    f = ctypes.c_void_p(0x1000)
+    T, H, E, k = 64, 2048, 256, 8
+    need = lib.moe_route_proj_workspace_bytes(T, H, E)
+    # decode shape: four 64x64 tiles, so K is split into 8 slices of partial logits
+    assert need == 8 * T * E * 4
+    # a prefill shape fills the chip without a split: one [T, E] slab
+    assert lib.moe_route_proj_workspace_bytes(8192, 2048, 256) == 8192 * 256 * 4
+    assert lib.moe_route_proj_workspace_bytes(8, 100, 4) == 0      # H % 64 != 0
+    call = lambda T=T, H=H, E=E, k=k, x=f, wg=f, lg=f, ids=f, aff=f, ws=f, wsb=need: (  # noqa: E731
+        lib.moe_route_proj(x, wg, T, H, E, k, lg, ids, aff, None, ws, wsb, None))
+    assert call(H=96) == binding.MOE_EUNSUPPORTED
+    assert b"multiple of 64" in lib.moe_last_error()
+    assert call(k=E + 1, E=8) == binding.MOE_EINVAL
+    assert call(E=2000) == binding.MOE_EINVAL
+    assert call(x=None) == binding.MOE_EINVAL
+    assert call(aff=None) == binding.MOE_EINVAL
+    assert call(x=ctypes.c_void_p(0x1008)) == binding.MOE_EINVAL
+    assert b"aligned" in lib.moe_last_error()
+    assert call(wsb=need - 1) == binding.MOE_EINVAL
+    assert b"workspace" in lib.moe_last_error()
+    assert call(lg=None, ws=None, wsb=0) == binding.MOE_EINVAL
+    # T == 0 is a no-op that never touches the device
+    assert call(T=0, x=None, wg=None, lg=None, ids=None, aff=None, ws=None, wsb=0) == binding.MOE_OK
     assert lib.moe_last_error() == b""
 
 

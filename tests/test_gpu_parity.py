@@ -110,6 +110,89 @@ def test_route_flags_nonfinite_logits():
     assert int(status.item()) & binding.MOE_STATUS_NONFINITE_LOGIT
 
 
+# ------------------------------------------------------------ router projection
+def _proj_bound(x64, w64):
+    """Forward-error bound of an fp32 dot product of length H summed in any
+    order, the products of bf16 values being exact in fp32:
+    H * 2^-24 * sum_h |x w|, doubled for margin."""
+    return 2.0 * x64.shape[1] * 2.0 ** -24 * (np.abs(x64) @ np.abs(w64).T)
+
+
+def _check_route_proj(x, wg, k, what):
+    T, H = x.shape
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ids, aff, lg = binding.route_proj(x, wg, k, logits=True, status=status)
+    ids2, aff2 = binding.route_proj(x, wg, k)
+    _, _, lg3 = binding.route_proj(x, wg, k, logits=True)
+    torch.cuda.synchronize()
+    x64 = np_(x.float()).astype(np.float64)
+    w64 = np_(wg.float()).astype(np.float64)
+    ref = oracle.router_logits(x64, w64)
+    bound = _proj_bound(x64, w64)
+    got = np_(lg).astype(np.float64)
+    ratio = float(np.max(np.abs(got - ref) / np.maximum(bound, 1e-300)))
+    print(f"[parity] route_proj {what}: max |d|/bound = {ratio:.3g}", flush=True)
+    assert ratio <= 1.0, what
+    # the router on the device's own fp32 logits: bit-exact ids
+    r_ids, r_aff = oracle.route_softmax_topk(np_(lg), k)
+    assert np.array_equal(np_(ids), r_ids), what
+    np.testing.assert_allclose(np_(aff), r_aff, rtol=AFF_RTOL, atol=0)
+    # the same result without the logits output, and the same bits again
+    assert np.array_equal(np_(ids2), np_(ids)) and np.array_equal(np_(aff2), np_(aff))
+    assert np.array_equal(np_(lg3).view(np.uint32), np_(lg).view(np.uint32))
+    # against the float64 logits wherever every decision of the top k (the
+    # order of the k kept ones and the cut after them) is wider than twice the
+    # error bound: the ids must then be those of the exact logits
+    E = ref.shape[1]
+    srt = -np.sort(-ref, axis=1)
+    gaps = srt[:, :min(k, E - 1)] - srt[:, 1:min(k, E - 1) + 1] if E > 1 else np.full((T, 1), np.inf)
+    safe = np.all(gaps > 2.0 * bound.max(axis=1, keepdims=True), axis=1)
+    e_ids, _ = oracle.route_softmax_topk(ref, k)
+    assert np.array_equal(np_(ids)[safe], e_ids[safe]), what
+    if T >= 64 and E >= 8:
+        assert safe.mean() > 0.2, (what, float(safe.mean()))
+    assert int(status.item()) == 0
+
+
+# (T, H, E, k): K slices S = 1/2/8 with load-ring depths 1/2/4, ragged T and E,
+# the widest expert count with k = 16, and the two workload geometries
+@pytest.mark.parametrize("T,H,E,k", [(1, 64, 1, 1), (5, 256, 8, 2), (64, 2048, 256, 8),
+                                     (300, 384, 100, 6), (700, 640, 130, 4),
+                                     (2048, 1024, 512, 10), (33, 8192, 1024, 16),
+                                     (8192, 2048, 256, 8)])
+def test_route_proj_parity(T, H, E, k):
+    x = synth.make_activations(synth.MoeConfig("p", T, H, 128, E, k), seed=T + H)[0].cuda()
+    wg = synth.make_gate_weights(E, H, seed=E + k).cuda()
+    _check_route_proj(x, wg, k, f"T={T} H={H} E={E} k={k}")
+
+
+def test_route_proj_golden_rows_and_ties():
+    rows = []
+    with open(os.path.join(GOLDEN, "router_proj_closed_form.txt")) as f:
+        for ln in f:
+            if ln.strip() and not ln.startswith("#"):
+                rows.append([p.strip() for p in ln.split("|")])
+    H = 64   # the hand-worked rows are 4 wide; zero padding leaves every logit unchanged
+    for w_s, k_s, x_s, l_s, i_s, a_s in rows:
+        wg = np.zeros((4, H), np.float32)
+        wg[:, :4] = [[float(v) for v in r.split()] for r in w_s.split(";")]
+        x = np.zeros((1, H), np.float32)
+        x[0, :4] = [float(v) for v in x_s.split()]
+        ids, aff, lg = binding.route_proj(torch.from_numpy(x).to(torch.bfloat16).cuda(),
+                                          torch.from_numpy(wg).to(torch.bfloat16).cuda(),
+                                          int(k_s), logits=True)
+        assert np_(lg)[0].tolist() == [float(v) for v in l_s.split()]
+        assert np_(ids)[0].tolist() == [int(v) for v in i_s.split()]
+        np.testing.assert_allclose(np_(aff)[0], [float(v) for v in a_s.split()], rtol=AFF_RTOL)
+
+
+def test_route_proj_empty_batch():
+    x = torch.empty((0, 128), dtype=torch.bfloat16, device="cuda")
+    wg = torch.zeros((8, 128), dtype=torch.bfloat16, device="cuda")
+    ids, aff = binding.route_proj(x, wg, 2)
+    assert ids.shape == (0, 2) and aff.shape == (0, 2)
+
+
 # ------------------------------------------------------------------ sort
 def _check_sort(ids_np, E, got):
     ref = oracle.sort_by_expert(ids_np, E)

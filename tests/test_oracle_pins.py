@@ -144,6 +144,53 @@ def test_route_golden_rows():
         np.testing.assert_allclose(aff[0], [float(v) for v in a_s.split()], rtol=1e-14, atol=0)
 
 
+# ----------------------------------------------------------- router projection
+def _proj_golden_rows():
+    rows = []
+    for ln in _golden_lines("router_proj_closed_form.txt"):
+        w_s, k_s, x_s, l_s, i_s, a_s = [p.strip() for p in ln.split("|")]
+        wg = np.array([[float(v) for v in r.split()] for r in w_s.split(";")])
+        rows.append((wg, int(k_s), np.array([float(v) for v in x_s.split()]),
+                     [float(v) for v in l_s.split()], [int(v) for v in i_s.split()],
+                     [float(v) for v in a_s.split()]))
+    return rows
+
+
+def test_router_projection_golden_rows():
+    for wg, k, x, logits, ids, aff in _proj_golden_rows():
+        got = oracle.router_logits(x[None, :], wg)
+        assert got[0].tolist() == logits
+        i, a = oracle.route_softmax_topk(got, k)
+        assert list(i[0]) == ids
+        np.testing.assert_allclose(a[0], aff, rtol=1e-14, atol=0)
+
+
+def test_router_projection_basis_rows_read_weight_columns():
+    # x = the h-th unit vector selects column h of the gate weights: a
+    # transposed or mis-indexed operand fails here (T != E != H)
+    rng = np.random.default_rng(11)
+    H, E = 7, 5
+    wg = rng.standard_normal((E, H))
+    got = oracle.router_logits(np.eye(H), wg)
+    assert got.shape == (H, E)
+    assert np.array_equal(got, wg.T)
+
+
+def test_router_projection_brute_force_and_linearity():
+    rng = np.random.default_rng(12)
+    T, H, E = 3, 6, 4
+    x = rng.integers(-3, 4, size=(T, H)).astype(np.float64)
+    wg = rng.integers(-3, 4, size=(E, H)).astype(np.float64)
+    got = oracle.router_logits(x, wg)
+    for t in range(T):
+        for e in range(E):
+            assert got[t, e] == sum(int(x[t, h]) * int(wg[e, h]) for h in range(H))
+    # linear in x
+    x2 = rng.standard_normal((T, H))
+    np.testing.assert_allclose(oracle.router_logits(2.5 * x - x2, wg),
+                               2.5 * got - oracle.router_logits(x2, wg), rtol=1e-13, atol=1e-12)
+
+
 def test_affinities_closed_forms():
     rng = np.random.default_rng(2)
     logits = rng.standard_normal((16, 12)).astype(np.float32)
