@@ -267,6 +267,78 @@ def vendor_gemm(cfg, dev, warmup=200, reps=50):
             "frac": round(tf / BF16_PEAK_TFLOPS, 4)}
 
 
+def route_proj_bench(cfg, dev, sets, seed=0, samples=7, replays=20):
+    """moe_route_proj (router projection x * W_g^T, then the router) at the
+    workload's T, H, E, k: one call per gate-weight set captured in a HIP graph,
+    median per call over `samples` x `replays` graph launches; then per-kernel
+    times from the library's own events.  Rotating `sets` distinct gate
+    matrices (bf16 [E, H] each) beyond the 256 MB last-level cache makes every
+    call read its W_g from HBM."""
+    import statistics
+
+    import torch
+
+    from block_scaled_fp8_amd import binding, synth
+    T, H, E, k = cfg.T, cfg.H, cfg.E, cfg.k
+    log(f"router projection: T={T} H={H} E={E} k={k}, {sets} gate-weight sets")
+    x = synth.make_activations(cfg, seed, dev)[0]
+    wgs = [synth.make_gate_weights(E, H, seed + 100 + i, dev) for i in range(sets)]
+    ws = torch.empty(max(binding.route_proj_workspace_bytes(T, H, E), 1), dtype=torch.uint8,
+                     device=dev)
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    aff = torch.empty((T, k), dtype=torch.float32, device=dev)
+    call = lambda w: binding.route_proj(x, w, k, ws=ws, out=(ids, aff))  # noqa: E731
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for w in wgs:
+            call(w)
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for w in wgs:
+            call(w)
+    for _ in range(10):
+        g.replay()
+    torch.cuda.synchronize()
+    per_call = []
+    for _ in range(samples):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(replays):
+            g.replay()
+        e.record()
+        torch.cuda.synchronize()
+        per_call.append(s.elapsed_time(e) * 1e3 / (replays * sets))
+    del g
+    us = statistics.median(per_call)
+    binding.profile_enable(True)
+    for i in range(4 * sets):
+        call(wgs[i % sets])
+    torch.cuda.synchronize()
+    binding.profile_enable(False)
+    prof = binding.profile_collect()
+    splits = max(1, binding.route_proj_workspace_bytes(T, H, E) // (4 * T * E))
+    nbytes = 2 * E * H + 2 * T * H + 8 * T * k      # W_g, x, ids + aff
+    flops = 2.0 * T * E * H
+    gemm_us = prof["router_gemm"][1] * 1e3
+    out = {"workload": cfg.name, "T": T, "hidden": H, "experts": E, "top_k": k,
+           "k_slices": int(splits), "gate_weight_sets": sets,
+           "protocol": f"HIP graph of one call per gate-weight set, median of {samples} x "
+                       f"{replays} replays",
+           "us_per_call": round(us, 2),
+           "kernels": {n: {"launches": c, "avg_us": round(ms * 1e3, 3)} for n, (c, ms) in prof.items()},
+           "hbm": {"bytes": nbytes, "GB_per_s": round(nbytes / (us * 1e-6) / 1e9, 1),
+                   "frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
+           "mfma": {"kernel": "router_gemm", "flops": flops, "avg_us": round(gemm_us, 3),
+                    "TFLOP_per_s": round(flops / (gemm_us * 1e-6) / 1e12, 1),
+                    "frac": round(flops / (gemm_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4)}}
+    log(f"  {us:.2f} us per call; " + ", ".join(f"{n} {ms * 1e3:.2f} us" for n, (c, ms) in prof.items()))
+    del wgs, ws, x
+    torch.cuda.empty_cache()
+    return out
+
+
 def prefill_summary(cfg, m):
     """MFMA roofline of the prefill workload (secondary object of the JSON line)."""
     R = cfg.T * cfg.k + (cfg.T if cfg.shared else 0)
@@ -314,6 +386,8 @@ def main():
                     help="untimed prefill steps first: the GPU idles while the prefill inputs "
                          "are generated, and its clock needs some milliseconds of work to settle")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-route-proj", action="store_true",
+                    help="skip the router-projection measurement (moe_route_proj)")
     ap.add_argument("--no-vendor-gemm", action="store_true",
                     help="skip timing torch.matmul at the gate/up shape (context only)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -407,6 +481,11 @@ def main():
         if not args.no_vendor_gemm:
             log("vendor bf16 GEMM at the gate/up shape (context) ...")
             result["prefill"]["vendor_bf16_gemm"] = vendor_gemm(pcfg, dev)
+    if not args.no_route_proj:
+        result["route_proj"] = [route_proj_bench(cfg, dev, 320, args.seed)]
+        if args.prefill_workload:
+            result["route_proj"].append(
+                route_proj_bench(synth.CONFIGS[args.prefill_workload], dev, 4, args.seed))
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         case = dict(x=x, logits=logits, **wsets[0])

@@ -142,10 +142,10 @@ def route_proj_workspace_bytes(T: int, H: int, E: int) -> int:
 
 
 def route_proj(x: torch.Tensor, wg: torch.Tensor, k: int, logits: bool = False,
-               status: torch.Tensor | None = None, ws=None):
+               status: torch.Tensor | None = None, ws=None, out=None):
     """Router projection then routing: x [T, H] bf16, wg [E, H] bf16 ->
     (ids [T, k] int32, aff [T, k] fp32), plus the fp32 logits [T, E] when
-    ``logits`` is true."""
+    ``logits`` is true.  ``out`` = (ids, aff) writes into given tensors."""
     lib = load_library()
     _need(x, "x", torch.bfloat16)
     dev = x.device
@@ -154,8 +154,13 @@ def route_proj(x: torch.Tensor, wg: torch.Tensor, k: int, logits: bool = False,
     E = wg.shape[0]
     if wg.shape[1] != H:
         raise ValueError(f"wg has shape {tuple(wg.shape)}, expected [E, {H}]")
-    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
-    aff = torch.empty((T, k), dtype=torch.float32, device=dev)
+    if out is not None:
+        ids, aff = out
+        _need(ids, "ids", torch.int32, dev, (T, k))
+        _need(aff, "aff", torch.float32, dev, (T, k))
+    else:
+        ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+        aff = torch.empty((T, k), dtype=torch.float32, device=dev)
     lg = torch.empty((T, E), dtype=torch.float32, device=dev) if logits else None
     if ws is None:
         need = int(lib.moe_route_proj_workspace_bytes(T, H, E))
