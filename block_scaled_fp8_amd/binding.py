@@ -24,7 +24,8 @@ VARIANTS = {"auto": 0, "decode": 1, "prefill": 2}
 LAYOUTS = {"rowmajor": 0, "tiled": 1}
 
 EXPORTED = (
-    "moe_last_error", "moe_route", "moe_route_proj_workspace_bytes", "moe_route_proj",
+    "moe_last_error", "moe_route", "moe_route_sigmoid", "moe_route_proj_workspace_bytes",
+    "moe_route_proj",
     "moe_sort_workspace_bytes", "moe_sort",
     "moe_fused_workspace_bytes", "moe_fused_w8a16", "moe_decode_e4m3fn", "moe_pack_w8",
     "moe_profile_enable", "moe_profile_collect", "moe_profile_count", "moe_profile_stat",
@@ -64,6 +65,8 @@ def load_library():
     lib.moe_last_error.argtypes = []
     lib.moe_route.restype = i32
     lib.moe_route.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp]
+    lib.moe_route_sigmoid.restype = i32
+    lib.moe_route_sigmoid.argtypes = [vp, i32, i32, i32, i32, ctypes.c_float, vp, vp, vp, vp]
     lib.moe_route_proj_workspace_bytes.restype = sz
     lib.moe_route_proj_workspace_bytes.argtypes = [i32, i32, i32]
     lib.moe_route_proj.restype = i32
@@ -134,6 +137,23 @@ def route(logits: torch.Tensor, k: int, status: torch.Tensor | None = None):
     if status is not None:
         _need(status, "status", torch.int32, dev)
     _check(lib.moe_route(_ptr(logits), T, E, k, _ptr(ids), _ptr(aff), _ptr(status), _stream(dev)))
+    return ids, aff
+
+
+def route_sigmoid(logits: torch.Tensor, k: int, normalize: bool = False, scale: float = 1.0,
+                  status: torch.Tensor | None = None):
+    """Sigmoid top-k routing: logits [T, E] fp32 -> (ids [T, k] int32,
+    aff [T, k] fp32 = scale * sigma(l), optionally normalised over the k)."""
+    lib = load_library()
+    _need(logits, "logits", torch.float32)
+    T, E = logits.shape
+    dev = logits.device
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    aff = torch.empty((T, k), dtype=torch.float32, device=dev)
+    if status is not None:
+        _need(status, "status", torch.int32, dev)
+    _check(lib.moe_route_sigmoid(_ptr(logits), T, E, k, int(bool(normalize)), float(scale),
+                                 _ptr(ids), _ptr(aff), _ptr(status), _stream(dev)))
     return ids, aff
 
 

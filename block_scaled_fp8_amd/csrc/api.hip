@@ -109,6 +109,27 @@ int moe_route(const float* logits, int T, int E, int k, int32_t* ids, float* aff
     return launch_route(logits, T, E, k, ids, aff, status, (hipStream_t)stream);
 }
 
+int moe_route_sigmoid(const float* logits, int T, int E, int k, int normalize, float scale,
+                      int32_t* ids, float* aff, int32_t* status, void* stream) {
+    g_err[0] = 0;
+    if (int rc = check_route_args(T, E, k)) return rc;
+    if (normalize != 0 && normalize != 1) {
+        set_error("moe_route_sigmoid: normalize must be 0 or 1 (got %d)", normalize);
+        return MOE_EINVAL;
+    }
+    if (!(scale == scale) || scale == __builtin_inff() || scale == -__builtin_inff()) {
+        set_error("moe_route_sigmoid: scale must be finite");
+        return MOE_EINVAL;
+    }
+    if (T == 0) return MOE_OK;
+    if (!logits || !ids || !aff) {
+        set_error("moe_route_sigmoid: logits, ids and aff must be non-NULL");
+        return MOE_EINVAL;
+    }
+    return launch_route_sigmoid(logits, T, E, k, normalize, scale, ids, aff, status,
+                                (hipStream_t)stream);
+}
+
 size_t moe_route_proj_workspace_bytes(int T, int H, int E) {
     if (T < 1 || H < 64 || H % 64 || E < 1 || E > MOE_MAX_EXPERTS) return 0;
     return route_proj_workspace_bytes(T, H, E);

@@ -44,6 +44,8 @@ int launch_sort(const int32_t* ids, int T, int k, int E, const Plan& plan, int h
 // Kernel launchers (route.hip, ffn_decode.hip, ffn_prefill.hip, misc).
 int launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* aff,
                  int32_t* status, hipStream_t stream);
+int launch_route_sigmoid(const float* logits, int T, int E, int k, int normalize, float scale,
+                         int32_t* ids, float* aff, int32_t* status, hipStream_t stream);
 // The router on nslab partial-logit slabs [nslab][T][E] added in slab order;
 // the sums go to logits_out when it is not NULL.
 int launch_route_slabs(const float* part, int nslab, float* logits_out, int T, int E, int k,

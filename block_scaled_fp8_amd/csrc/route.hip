@@ -81,12 +81,17 @@ __device__ __forceinline__ uint32_t wave_red_u32(uint32_t v) {
 // logits[s][t][e] of a K-split projection; they are added in slice order (all
 // loads issued first, a clamped duplicate masked out) and, when logits_out is
 // given, the sums are written there.
+//
+// SIGMOID: the affinity of a kept expert is scale * sigma(l_j), or with
+// `normalize` scale * sigma(l_j) / sum over the kept sigma (see
+// launch_route_sigmoid); the selection is the same, sigma being increasing.
 constexpr int RT_MAX_SLABS = 8;
 
-template <int NPL, bool SLABS>
+template <int NPL, bool SLABS, bool SIGMOID>
 __global__ __launch_bounds__(256) void route_topk_softmax_kernel(
     const float* __restrict__ logits, int nslab, float* __restrict__ logits_out, int T, int E,
-    int k, int32_t* __restrict__ ids, float* __restrict__ aff, int32_t* __restrict__ status) {
+    int k, int normalize, float scale, int32_t* __restrict__ ids, float* __restrict__ aff,
+    int32_t* __restrict__ status) {
     const int lane = lane_id();
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
@@ -177,39 +182,70 @@ __global__ __launch_bounds__(256) void route_topk_softmax_kernel(
             my_o = gmax;
         }
     }
-    const float M = from_ordered(top_o);
-    const float w = lane < k ? expf(from_ordered(my_o) - M) : 0.0f;
-    const float s = wave_sum_f32(w);
+    float a;
+    if (SIGMOID) {
+        // log sigma(l) = min(l, 0) - log(1 + exp(-|l|)): finite for every finite l
+        const float lj = from_ordered(my_o);
+        const float ls = fminf(lj, 0.0f) - log1pf(expf(-fabsf(lj)));
+        if (normalize) {
+            // sigma_j / sum of the kept sigma, as a softmax over log sigma (slot
+            // 0, in lane 0, holds the largest), so tiny sigmas never divide 0 by 0
+            const float lm = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ls), 0));
+            const float w = lane < k ? expf(ls - lm) : 0.0f;
+            a = w / wave_sum_f32(w);
+        } else {
+            a = expf(ls);
+        }
+        a *= scale;
+    } else {
+        const float M = from_ordered(top_o);
+        const float w = lane < k ? expf(from_ordered(my_o) - M) : 0.0f;
+        a = w / wave_sum_f32(w);
+    }
     if (lane < k) {
         ids[(size_t)t * k + lane] = my_id;
-        aff[(size_t)t * k + lane] = w / s;
+        aff[(size_t)t * k + lane] = a;
     }
 }
 
-template <bool SLABS>
+template <bool SLABS, bool SIGMOID>
 static int launch_route_impl(const float* logits, int nslab, float* logits_out, int T, int E,
-                             int k, int32_t* ids, float* aff, int32_t* status,
-                             hipStream_t stream) {
+                             int k, int normalize, float scale, int32_t* ids, float* aff,
+                             int32_t* status, hipStream_t stream) {
     const int npl = (E + MOE_WAVE - 1) / MOE_WAVE;
     const dim3 grid((T + 3) / 4), block(256);
-    prof_begin("route_topk_softmax", stream);
+    prof_begin(SIGMOID ? "route_topk_sigmoid" : "route_topk_softmax", stream);
+#define MOE_ROUTE_LAUNCH(N)                                                                       \
+    route_topk_softmax_kernel<N, SLABS, SIGMOID><<<grid, block, 0, stream>>>(                     \
+        logits, nslab, logits_out, T, E, k, normalize, scale, ids, aff, status)
     if (npl <= 1)
-        route_topk_softmax_kernel<1, SLABS><<<grid, block, 0, stream>>>(logits, nslab, logits_out, T, E, k, ids, aff, status);
+        MOE_ROUTE_LAUNCH(1);
     else if (npl <= 2)
-        route_topk_softmax_kernel<2, SLABS><<<grid, block, 0, stream>>>(logits, nslab, logits_out, T, E, k, ids, aff, status);
+        MOE_ROUTE_LAUNCH(2);
     else if (npl <= 4)
-        route_topk_softmax_kernel<4, SLABS><<<grid, block, 0, stream>>>(logits, nslab, logits_out, T, E, k, ids, aff, status);
+        MOE_ROUTE_LAUNCH(4);
     else if (npl <= 8)
-        route_topk_softmax_kernel<8, SLABS><<<grid, block, 0, stream>>>(logits, nslab, logits_out, T, E, k, ids, aff, status);
+        MOE_ROUTE_LAUNCH(8);
     else
-        route_topk_softmax_kernel<16, SLABS><<<grid, block, 0, stream>>>(logits, nslab, logits_out, T, E, k, ids, aff, status);
+        MOE_ROUTE_LAUNCH(16);
+#undef MOE_ROUTE_LAUNCH
     prof_end(stream);
     return check_launch("route_topk_softmax_kernel");
 }
 
 int launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* aff,
                  int32_t* status, hipStream_t stream) {
-    return launch_route_impl<false>(logits, 1, nullptr, T, E, k, ids, aff, status, stream);
+    return launch_route_impl<false, false>(logits, 1, nullptr, T, E, k, 0, 1.0f, ids, aff, status,
+                                           stream);
+}
+
+// Sigmoid routing: the k largest logits (as for softmax), affinity
+// scale * sigma(l_j), or scale * sigma(l_j) / sum of the kept sigma when
+// normalize is set.
+int launch_route_sigmoid(const float* logits, int T, int E, int k, int normalize, float scale,
+                         int32_t* ids, float* aff, int32_t* status, hipStream_t stream) {
+    return launch_route_impl<false, true>(logits, 1, nullptr, T, E, k, normalize ? 1 : 0, scale,
+                                          ids, aff, status, stream);
 }
 
 int launch_route_slabs(const float* part, int nslab, float* logits_out, int T, int E, int k,
@@ -219,8 +255,10 @@ int launch_route_slabs(const float* part, int nslab, float* logits_out, int T, i
         return MOE_EINVAL;
     }
     if (nslab == 1 && !logits_out)
-        return launch_route_impl<false>(part, 1, nullptr, T, E, k, ids, aff, status, stream);
-    return launch_route_impl<true>(part, nslab, logits_out, T, E, k, ids, aff, status, stream);
+        return launch_route_impl<false, false>(part, 1, nullptr, T, E, k, 0, 1.0f, ids, aff,
+                                               status, stream);
+    return launch_route_impl<true, false>(part, nslab, logits_out, T, E, k, 0, 1.0f, ids, aff,
+                                          status, stream);
 }
 
 }  // namespace moe

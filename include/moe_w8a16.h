@@ -93,6 +93,27 @@ int moe_route(const float* logits, int T, int E, int k,
               int32_t* ids, float* aff, int32_t* status, void* stream);
 
 /*
+ * moe_route_sigmoid -- sigmoid top-k routing with a routed scaling factor.
+ * Source: "spark_model/layers/nemotron_moe.rs", module documentation and
+ * prefill forward: the gate logits go through sigmoid top-K routing, and the
+ * routed experts' weighted sum is scaled by the routed scaling factor of the
+ * model configuration.
+ *   logits    [T, E] fp32                                         (in)
+ *   normalize 0: aff = scale * sigma(l_j), sigma(l) = 1 / (1 + exp(-l));
+ *             1: aff = scale * sigma(l_j) / (sum of the k kept sigma)
+ *   scale     routed scaling factor, finite; folded into aff, so the expert
+ *             sum of moe_fused_w8a16 carries it
+ *   ids       [T, k] int32 (out): the k largest logits, ordered and tied as
+ *             in moe_route (sigma is strictly increasing, so these are the
+ *             k largest sigmoid scores)
+ *   aff       [T, k] fp32 (out); status as for moe_route.
+ * Requires the moe_route conditions, normalize in {0, 1} and a finite scale
+ * (else MOE_EINVAL).  T == 0 is a no-op.
+ */
+int moe_route_sigmoid(const float* logits, int T, int E, int k, int normalize, float scale,
+                      int32_t* ids, float* aff, int32_t* status, void* stream);
+
+/*
  * moe_route_proj -- router projection followed by the router:
  *     logits[t][e] = sum_h x[t][h] * wg[e][h]   (bf16 x bf16 products, fp32 sums)
  * then exactly what moe_route computes on those fp32 logits.

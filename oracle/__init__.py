@@ -20,6 +20,7 @@ from .moe_ref import (  # noqa: F401
     e4m3fn_decode,
     dequantize_blocks,
     route_softmax_topk,
+    route_sigmoid_topk,
     router_logits,
     sort_by_expert,
     swiglu,

@@ -110,6 +110,33 @@ def route_softmax_topk(logits, k: int):
 
 
 # --------------------------------------------------------------------------
+# Sigmoid routing  ([SPARK] module documentation: "sigmoid topK routing"; the
+# routed weighted sum is scaled by the configuration's routed scaling factor)
+# --------------------------------------------------------------------------
+def route_sigmoid_topk(logits, k: int, normalize: bool = False, scale: float = 1.0):
+    """ids int32 [T, k] and affinities float64 [T, k] of sigmoid routing.
+
+    The kept experts are the k largest sigmoid scores sigma(l) = 1/(1+exp(-l));
+    sigma is strictly increasing, so they are the k largest fp32 logits, ties
+    to the lower expert index and -0.0 equal to +0.0, slot j the j-th.  The
+    affinity is scale * sigma(l_j), or scale * sigma(l_j) / (sum of the k kept
+    sigma) when ``normalize`` (the pages do not say whether the kept scores are
+    renormalised; both readings are offered)."""
+    l32 = np.asarray(logits, dtype=np.float32)
+    T, E = l32.shape
+    assert 1 <= k <= E
+    l = l32.astype(np.float64)
+    idx = np.broadcast_to(np.arange(E), (T, E))
+    order = np.lexsort((idx, -l), axis=1)
+    ids = order[:, :k].astype(np.int32)
+    with np.errstate(over="ignore"):
+        sig = 1.0 / (1.0 + np.exp(-np.take_along_axis(l, ids.astype(np.int64), axis=1)))
+    if normalize:
+        sig = sig / sig.sum(axis=1, keepdims=True)
+    return ids, float(scale) * sig
+
+
+# --------------------------------------------------------------------------
 # Router projection  ([SPARK] prefill forward: a batched gate GEMM takes the
 # normalised hidden states [N, H] and the gate weights [E, H] to gate logits
 # [N, E], which the top-K routing consumes; [NKILIB] Router Top-K: router

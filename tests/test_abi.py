@@ -22,7 +22,7 @@ def _declared_functions():
 
 def test_header_declares_the_boundary():
     names = _declared_functions()
-    for n in ("moe_route", "moe_route_proj", "moe_sort", "moe_fused_w8a16", "moe_last_error",
+    for n in ("moe_route", "moe_route_sigmoid", "moe_route_proj", "moe_sort", "moe_fused_w8a16", "moe_last_error",
               "moe_sort_workspace_bytes", "moe_fused_workspace_bytes", "moe_decode_e4m3fn",
               "moe_pack_w8"):
         assert n in names
@@ -54,6 +54,20 @@ def test_route_argument_checks():
     assert lib.moe_route(fake, 4, 8, 2, None, fake, None, None) == binding.MOE_EINVAL
     # T == 0 is a no-op that never touches the device
     assert lib.moe_route(None, 0, 8, 2, None, None, None, None) == binding.MOE_OK
+    assert lib.moe_last_error() == b""
+
+
+def test_route_sigmoid_argument_checks():
+    lib = binding.load_library()
+    f = ctypes.c_void_p(0x1000)
+    assert lib.moe_route_sigmoid(f, 4, 8, 9, 0, 1.0, f, f, None, None) == binding.MOE_EINVAL
+    assert lib.moe_route_sigmoid(f, 4, 8, 2, 2, 1.0, f, f, None, None) == binding.MOE_EINVAL
+    assert b"normalize" in lib.moe_last_error()
+    assert lib.moe_route_sigmoid(f, 4, 8, 2, 0, float("inf"), f, f, None, None) == binding.MOE_EINVAL
+    assert lib.moe_route_sigmoid(f, 4, 8, 2, 1, float("nan"), f, f, None, None) == binding.MOE_EINVAL
+    assert b"scale" in lib.moe_last_error()
+    assert lib.moe_route_sigmoid(f, 4, 8, 2, 0, 1.0, None, f, None, None) == binding.MOE_EINVAL
+    assert lib.moe_route_sigmoid(None, 0, 8, 2, 0, 1.0, None, None, None, None) == binding.MOE_OK
     assert lib.moe_last_error() == b""
 
 

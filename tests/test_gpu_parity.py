@@ -110,6 +110,69 @@ def test_route_flags_nonfinite_logits():
     assert int(status.item()) & binding.MOE_STATUS_NONFINITE_LOGIT
 
 
+# ------------------------------------------------------------ sigmoid routing
+SIG_RTOL = 1e-5   # fp32 log-sigmoid, exp and divide against float64, |logit| <= 30
+
+
+@pytest.mark.parametrize("norm,scale", [(False, 1.0), (True, 2.5)])
+@pytest.mark.parametrize("name", synth.CONFIG_ORDER)
+def test_route_sigmoid_parity(name, norm, scale):
+    c = _case(name)
+    cfg = c["cfg"]
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ids, aff = binding.route_sigmoid(c["logits"], cfg.k, norm, scale, status)
+    torch.cuda.synchronize()
+    ref_ids, ref_aff = oracle.route_sigmoid_topk(np_(c["logits"]), cfg.k, norm, scale)
+    assert np.array_equal(np_(ids), ref_ids)
+    np.testing.assert_allclose(np_(aff), ref_aff, rtol=SIG_RTOL, atol=0)
+    assert int(status.item()) == 0
+
+
+def test_route_sigmoid_golden_rows_and_ties():
+    with open(os.path.join(GOLDEN, "route_sigmoid_closed_form.txt")) as f:
+        for ln in f:
+            if ln.strip() and not ln.startswith("#"):
+                k_s, n_s, sc_s, l_s, i_s, a_s = [p.strip() for p in ln.split("|")]
+                lg = torch.tensor([[float(v) for v in l_s.split()]], dtype=torch.float32,
+                                  device="cuda")
+                ids, aff = binding.route_sigmoid(lg, int(k_s), bool(int(n_s)), float(sc_s))
+                assert np_(ids)[0].tolist() == [int(v) for v in i_s.split()]
+                np.testing.assert_allclose(np_(aff)[0], [float(v) for v in a_s.split()],
+                                           rtol=SIG_RTOL)
+
+
+@pytest.mark.parametrize("T,E,k", [(1, 1, 1), (3, 100, 5), (7, 64, 16), (5, 1024, 16),
+                                   (9, 513, 11), (130, 65, 3)])
+def test_route_sigmoid_shapes_and_ties(T, E, k):
+    rng = np.random.default_rng(T * 1000 + E + 7)
+    vals = np.array([-1.5, -0.0, 0.0, 0.25, 1.0], dtype=np.float32)
+    logits = rng.choice(vals, size=(T, E)).astype(np.float32)
+    logits[0] = rng.standard_normal(E).astype(np.float32) * 8
+    lg = torch.from_numpy(logits).cuda()
+    for norm, scale in ((False, 1.0), (True, 0.75)):
+        ids, aff = binding.route_sigmoid(lg, k, norm, scale)
+        ref_ids, ref_aff = oracle.route_sigmoid_topk(logits, k, norm, scale)
+        assert np.array_equal(np_(ids), ref_ids)
+        np.testing.assert_allclose(np_(aff), ref_aff, rtol=SIG_RTOL)
+
+
+def test_route_sigmoid_far_tails():
+    # logits far in both tails: sigma underflows or saturates in fp32, and the
+    # normalised weights are still the ratios of the kept sigmas
+    logits = np.array([[-500.0, -520.0, -900.0, -510.0],
+                       [100.0, 30.0, -30.0, 95.0],
+                       [-80.0, -95.0, -88.0, -120.0]], dtype=np.float32)
+    lg = torch.from_numpy(logits).cuda()
+    ids, aff = binding.route_sigmoid(lg, 2, True, 1.0)
+    ref_ids, ref_aff = oracle.route_sigmoid_topk(logits, 2, True, 1.0)
+    assert np.array_equal(np_(ids), ref_ids)
+    np.testing.assert_allclose(np_(aff), ref_aff, rtol=SIG_RTOL)
+    ids, aff = binding.route_sigmoid(lg[1:], 2, False, 1.0)
+    ref_ids, ref_aff = oracle.route_sigmoid_topk(logits[1:], 2, False, 1.0)
+    assert np.array_equal(np_(ids), ref_ids)
+    np.testing.assert_allclose(np_(aff), ref_aff, rtol=SIG_RTOL, atol=1e-38)
+
+
 # ------------------------------------------------------------ router projection
 def _proj_bound(x64, w64):
     """Forward-error bound of an fp32 dot product of length H summed in any

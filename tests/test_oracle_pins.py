@@ -144,6 +144,50 @@ def test_route_golden_rows():
         np.testing.assert_allclose(aff[0], [float(v) for v in a_s.split()], rtol=1e-14, atol=0)
 
 
+# ----------------------------------------------------------- sigmoid routing
+def _sigmoid_golden_rows():
+    rows = []
+    for ln in _golden_lines("route_sigmoid_closed_form.txt"):
+        k_s, n_s, sc_s, l_s, i_s, a_s = [p.strip() for p in ln.split("|")]
+        rows.append((int(k_s), bool(int(n_s)), float(sc_s),
+                     np.array([[float(v) for v in l_s.split()]], dtype=np.float32),
+                     [int(v) for v in i_s.split()], [float(v) for v in a_s.split()]))
+    return rows
+
+
+def test_route_sigmoid_golden_rows():
+    for k, norm, scale, logits, ids, aff in _sigmoid_golden_rows():
+        i, a = oracle.route_sigmoid_topk(logits, k, norm, scale)
+        assert list(i[0]) == ids
+        np.testing.assert_allclose(a[0], aff, rtol=1e-14, atol=0)
+
+
+def test_route_sigmoid_invariants():
+    rng = np.random.default_rng(13)
+    vals = np.array([-2.0, -0.0, 0.0, 0.5, 3.0], dtype=np.float32)
+    logits = rng.choice(vals, size=(64, 9)).astype(np.float32)        # many ties
+    logits[:8] = rng.standard_normal((8, 9)).astype(np.float32) * 4
+    for k in (1, 3, 9):
+        ids_s, _ = oracle.route_softmax_topk(logits, k)
+        ids, aff = oracle.route_sigmoid_topk(logits, k)
+        # the same experts as the softmax router: both keep the k largest logits
+        assert np.array_equal(ids, ids_s)
+        sel = np.take_along_axis(logits.astype(np.float64), ids.astype(np.int64), axis=1)
+        # sigma(0) = 1/2, and the scale multiplies exactly
+        assert np.all((aff > 0) & (aff < 1))
+        np.testing.assert_allclose(oracle.route_sigmoid_topk(logits, k, scale=3.0)[1], 3.0 * aff,
+                                   rtol=1e-15)
+        assert np.all(aff[sel == 0] == 0.5)
+        # normalised: sums to the scale and keeps the ratios
+        _, an = oracle.route_sigmoid_topk(logits, k, normalize=True, scale=0.75)
+        np.testing.assert_allclose(an.sum(axis=1), 0.75, rtol=1e-14)
+        np.testing.assert_allclose(an / an[:, :1], aff / aff[:, :1], rtol=1e-13)
+    # sigma(l) + sigma(-l) = 1 on single experts
+    l1 = np.array([[1.25], [-7.0], [0.0]], dtype=np.float32)
+    np.testing.assert_allclose(oracle.route_sigmoid_topk(l1, 1)[1] + oracle.route_sigmoid_topk(-l1, 1)[1],
+                               1.0, rtol=1e-15)
+
+
 # ----------------------------------------------------------- router projection
 def _proj_golden_rows():
     rows = []
