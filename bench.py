@@ -339,6 +339,62 @@ def route_proj_bench(cfg, dev, sets, seed=0, samples=7, replays=20):
     return out
 
 
+def router_variants_bench(cfg, dev, seed=0, calls=64, samples=7, replays=20):
+    """The router alone on the workload's logits: softmax top-k (moe_route) and
+    sigmoid top-k with and without renormalisation (moe_route_sigmoid), each
+    as `calls` calls in one HIP graph, median per call.  The logits ([T, E]
+    fp32) stay in the caches between calls, so this is the launch and latency
+    cost that a step pays, not an HBM rate."""
+    import statistics
+
+    import torch
+
+    from block_scaled_fp8_amd import binding, synth
+    logits = synth.make_activations(cfg, seed, dev)[1]
+    ids = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=dev)
+    aff = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device=dev)
+    lib = binding.load_library()
+    stream = lambda: binding._stream(dev)  # noqa: E731
+    fns = {
+        "softmax": lambda: lib.moe_route(binding._ptr(logits), cfg.T, cfg.E, cfg.k,
+                                         binding._ptr(ids), binding._ptr(aff), None, stream()),
+        "sigmoid": lambda: lib.moe_route_sigmoid(binding._ptr(logits), cfg.T, cfg.E, cfg.k, 0,
+                                                 2.5, binding._ptr(ids), binding._ptr(aff),
+                                                 None, stream()),
+        "sigmoid_normalized": lambda: lib.moe_route_sigmoid(binding._ptr(logits), cfg.T, cfg.E,
+                                                            cfg.k, 1, 2.5, binding._ptr(ids),
+                                                            binding._ptr(aff), None, stream()),
+    }
+    out = {"workload": cfg.name, "T": cfg.T, "experts": cfg.E, "top_k": cfg.k,
+           "protocol": f"HIP graph of {calls} calls, median of {samples} x {replays} replays"}
+    for name, fn in fns.items():
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            assert fn() == 0
+        torch.cuda.current_stream().wait_stream(side)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(calls):
+                assert fn() == 0
+        for _ in range(5):
+            g.replay()
+        torch.cuda.synchronize()
+        per = []
+        for _ in range(samples):
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            for _ in range(replays):
+                g.replay()
+            e.record()
+            torch.cuda.synchronize()
+            per.append(s.elapsed_time(e) * 1e3 / (replays * calls))
+        del g
+        out[name] = {"us_per_call": round(statistics.median(per), 2)}
+    log(f"router variants {cfg.name}: " + ", ".join(f"{n} {out[n]['us_per_call']} us" for n in fns))
+    return out
+
+
 def prefill_summary(cfg, m):
     """MFMA roofline of the prefill workload (secondary object of the JSON line)."""
     R = cfg.T * cfg.k + (cfg.T if cfg.shared else 0)
@@ -387,7 +443,7 @@ def main():
                          "are generated, and its clock needs some milliseconds of work to settle")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-route-proj", action="store_true",
-                    help="skip the router-projection measurement (moe_route_proj)")
+                    help="skip the router measurements (moe_route_proj, router variants)")
     ap.add_argument("--no-vendor-gemm", action="store_true",
                     help="skip timing torch.matmul at the gate/up shape (context only)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -482,6 +538,10 @@ def main():
             log("vendor bf16 GEMM at the gate/up shape (context) ...")
             result["prefill"]["vendor_bf16_gemm"] = vendor_gemm(pcfg, dev)
     if not args.no_route_proj:
+        result["router_variants"] = [router_variants_bench(cfg, dev, args.seed)]
+        if args.prefill_workload:
+            result["router_variants"].append(
+                router_variants_bench(synth.CONFIGS[args.prefill_workload], dev, args.seed))
         result["route_proj"] = [route_proj_bench(cfg, dev, 320, args.seed)]
         if args.prefill_workload:
             result["route_proj"].append(
