@@ -21,13 +21,15 @@ MOE_STATUS_NONFINITE_LOGIT = 2
 MOE_MAX_EXPERTS = 1024
 MOE_MAX_TOPK = 16
 VARIANTS = {"auto": 0, "decode": 1, "prefill": 2}
+ACTIVATIONS = {"swiglu": 0, "relu2": 1}
 LAYOUTS = {"rowmajor": 0, "tiled": 1}
 
 EXPORTED = (
     "moe_last_error", "moe_route", "moe_route_sigmoid", "moe_route_proj_workspace_bytes",
     "moe_route_proj",
     "moe_sort_workspace_bytes", "moe_sort",
-    "moe_fused_workspace_bytes", "moe_fused_w8a16", "moe_decode_e4m3fn", "moe_pack_w8",
+    "moe_fused_workspace_bytes", "moe_fused_w8a16", "moe_fused_w8a16_ex", "moe_decode_e4m3fn",
+    "moe_pack_w8",
     "moe_profile_enable", "moe_profile_collect", "moe_profile_count", "moe_profile_stat",
 )
 
@@ -80,6 +82,8 @@ def load_library():
     lib.moe_fused_w8a16.restype = i32
     lib.moe_fused_w8a16.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                     ctypes.POINTER(ExpertW8), vp, vp, vp, sz, i32, i32, vp]
+    lib.moe_fused_w8a16_ex.restype = i32
+    lib.moe_fused_w8a16_ex.argtypes = list(lib.moe_fused_w8a16.argtypes[:-1]) + [i32, vp]
     lib.moe_pack_w8.restype = i32
     lib.moe_pack_w8.argtypes = [vp, vp, i64, i32, i32, vp]
     lib.moe_decode_e4m3fn.restype = i32
@@ -239,20 +243,22 @@ def pack_w8(w: torch.Tensor) -> torch.Tensor:
 
 
 def fused_w8a16(x, w13, w13_scale, w2, w2_scale, ids, aff, shared=None, out=None, ws=None,
-                status=None, variant="auto", layout="rowmajor"):
+                status=None, variant="auto", layout="rowmajor", activation="swiglu"):
     """Routed expert FFN with block-scaled FP8 weights -> out [T, H] fp32.
 
-    x bf16 [T, H]; w13 uint8 [E, 2I, H]; w13_scale fp32 [E, 2I/128, H/128];
-    w2 uint8 [E, H, I]; w2_scale fp32 [E, H/128, I/128]; ids int32 [T, k];
-    aff fp32 [T, k]; shared: None or a dict with the four tensors of one expert."""
+    x bf16 [T, H]; w13 uint8 [E, 2I, H] (activation "relu2": [E, I, H], the up
+    projection alone); w13_scale fp32 [E, rows/128, H/128]; w2 uint8 [E, H, I];
+    w2_scale fp32 [E, H/128, I/128]; ids int32 [T, k]; aff fp32 [T, k];
+    shared: None or a dict with the four tensors of one expert."""
     lib = load_library()
     _need(x, "x", torch.bfloat16)
     dev = x.device
     T, H = x.shape
     _need(w13, "w13", torch.uint8, dev)
+    act = ACTIVATIONS[activation] if isinstance(activation, str) else int(activation)
     E, I2, H2 = w13.shape
-    I = I2 // 2
-    if H2 != H or I2 % 2:
+    I = I2 // 2 if act == 0 else I2
+    if H2 != H or (act == 0 and I2 % 2):
         raise ValueError(f"w13 shape {tuple(w13.shape)} does not match x {tuple(x.shape)}")
     _need(w13_scale, "w13_scale", torch.float32, dev, (E, -(-I2 // 128), -(-H // 128)))
     _need(w2, "w2", torch.uint8, dev, (E, H, I))
@@ -281,10 +287,10 @@ def fused_w8a16(x, w13, w13_scale, w2, w2_scale, ids, aff, shared=None, out=None
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     if status is not None:
         _need(status, "status", torch.int32, dev)
-    _check(lib.moe_fused_w8a16(_ptr(x), _ptr(w13), _ptr(w13_scale), _ptr(w2), _ptr(w2_scale),
-                               _ptr(ids), _ptr(aff), T, H, I, E, k, sh_ptr, _ptr(out),
-                               _ptr(status), _ptr(ws), ws.numel(), _layout(layout), v,
-                               _stream(dev)))
+    _check(lib.moe_fused_w8a16_ex(_ptr(x), _ptr(w13), _ptr(w13_scale), _ptr(w2),
+                                  _ptr(w2_scale), _ptr(ids), _ptr(aff), T, H, I, E, k, sh_ptr,
+                                  _ptr(out), _ptr(status), _ptr(ws), ws.numel(), _layout(layout),
+                                  v, act, _stream(dev)))
     return out
 
 
@@ -298,11 +304,11 @@ def decode_e4m3fn(codes: torch.Tensor) -> torch.Tensor:
 
 
 def forward(x, logits, k, w13, w13_scale, w2, w2_scale, shared=None, variant="auto",
-            layout="rowmajor"):
+            layout="rowmajor", activation="swiglu"):
     """Whole hot path: route, then the fused sort + expert FFN."""
     ids, aff = route(logits, k)
     out = fused_w8a16(x, w13, w13_scale, w2, w2_scale, ids, aff, shared=shared, variant=variant,
-                      layout=layout)
+                      layout=layout, activation=activation)
     return ids, aff, out
 
 
@@ -330,12 +336,13 @@ class MoeStep:
     stream of the tensors' device."""
 
     def __init__(self, x, logits, k, w13, w13_scale, w2, w2_scale, shared=None,
-                 variant="auto", layout="rowmajor"):
+                 variant="auto", layout="rowmajor", activation="swiglu"):
         lib = load_library()
         dev = x.device
         T, H = x.shape
         E = w13.shape[0]
-        I = w13.shape[1] // 2
+        act = ACTIVATIONS[activation] if isinstance(activation, str) else int(activation)
+        I = w13.shape[1] // 2 if act == 0 else w13.shape[1]
         self.ids = torch.empty((T, k), dtype=torch.int32, device=dev)
         self.aff = torch.empty((T, k), dtype=torch.float32, device=dev)
         self.out = torch.empty((T, H), dtype=torch.float32, device=dev)
@@ -345,7 +352,7 @@ class MoeStep:
                               dtype=torch.uint8, device=dev)
         ids, aff = route(logits, k)
         fused_w8a16(x, w13, w13_scale, w2, w2_scale, ids, aff, shared=shared, out=self.out,
-                    ws=self.ws, variant=variant, layout=layout)
+                    ws=self.ws, variant=variant, layout=layout, activation=act)
         self._keep = (x, logits, w13, w13_scale, w2, w2_scale, shared)
         self._sh = None
         if shared is not None:
@@ -359,7 +366,7 @@ class MoeStep:
         self._fused_args = (_ptr(x), _ptr(w13), _ptr(w13_scale), _ptr(w2), _ptr(w2_scale),
                             _ptr(self.ids), _ptr(self.aff), T, H, I, E, k, self._sh,
                             _ptr(self.out), None, _ptr(self.ws), self.ws.numel(),
-                            _layout(layout), v)
+                            _layout(layout), v, act)
         self._lib = lib
         self._dev = dev
 
@@ -367,12 +374,12 @@ class MoeStep:
         st = _stream(self._dev)
         rc = self._lib.moe_route(*self._route_args, st)
         if rc == MOE_OK:
-            rc = self._lib.moe_fused_w8a16(*self._fused_args, st)
+            rc = self._lib.moe_fused_w8a16_ex(*self._fused_args, st)
         _check(rc)
         return self.out
 
     def fused(self):
         """Enqueue only the fused call (sort + expert FFN + expert sum) on the
         ids and affinities of the last routing pass."""
-        _check(self._lib.moe_fused_w8a16(*self._fused_args, _stream(self._dev)))
+        _check(self._lib.moe_fused_w8a16_ex(*self._fused_args, _stream(self._dev)))
         return self.out

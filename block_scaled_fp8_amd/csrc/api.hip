@@ -207,12 +207,18 @@ size_t moe_fused_workspace_bytes(int T, int H, int I, int E, int k, int has_shar
     return fused_layout(T, H, I, E, k, has_shared ? 1 : 0).total;
 }
 
-int moe_fused_w8a16(const void* x, const uint8_t* w13, const float* w13_scale,
-                    const uint8_t* w2, const float* w2_scale, const int32_t* ids,
-                    const float* aff, int T, int H, int I, int E, int k,
-                    const moe_expert_w8* shared, float* out, int32_t* status, void* ws,
-                    size_t ws_bytes, int weight_layout, int variant, void* stream) {
+int moe_fused_w8a16_ex(const void* x, const uint8_t* w13, const float* w13_scale,
+                       const uint8_t* w2, const float* w2_scale, const int32_t* ids,
+                       const float* aff, int T, int H, int I, int E, int k,
+                       const moe_expert_w8* shared, float* out, int32_t* status, void* ws,
+                       size_t ws_bytes, int weight_layout, int variant, int activation,
+                       void* stream) {
     g_err[0] = 0;
+    if (activation != MOE_ACT_SWIGLU && activation != MOE_ACT_RELU2) {
+        set_error("unknown activation %d", activation);
+        return MOE_EINVAL;
+    }
+    const int act = activation == MOE_ACT_RELU2 ? ACT_RELU2 : ACT_SWIGLU;
     if (int rc = check_route_args(T, E, k)) return rc;
     if (H < 128 || I < 128 || H % 128 || I % 128) {
         set_error("H and I must be positive multiples of 128 (got H=%d, I=%d)", H, I);
@@ -256,12 +262,12 @@ int moe_fused_w8a16(const void* x, const uint8_t* w13, const float* w13_scale,
     // M tile).
     if (variant == MOE_VARIANT_AUTO) {
         const long long R = (long long)T * k;
-        variant = (R <= 16LL * E && R <= decode_self_routed_max_routes()) || !prefill_supported(H, I)
+        variant = (R <= 16LL * E && R <= decode_self_routed_max_routes()) || !prefill_supported(H, I, act)
                       ? MOE_VARIANT_DECODE
                       : MOE_VARIANT_PREFILL;
     }
     if (variant == MOE_VARIANT_PREFILL) {
-        if (int rc = prefill_check(T, H, I, E, k, has_shared)) return rc;
+        if (int rc = prefill_check(T, H, I, E, k, has_shared, act)) return rc;
     }
 
     char* base = static_cast<char*>(ws);
@@ -289,23 +295,33 @@ int moe_fused_w8a16(const void* x, const uint8_t* w13, const float* w13_scale,
     if (variant == MOE_VARIANT_DECODE && decode_fused_fits(T, k, E, I, has_shared, true)) {
         // small decode batch: each expert's workgroup finds its own routes
         rc = launch_decode_fused_self(weight_layout, decode_mt(T, k, E), xb, w13, w13_scale, w2,
-                                      w2_scale, sh, ids, aff, T, H, I, E, k, ybuf, s);
+                                      w2_scale, sh, ids, aff, T, H, I, E, k, ybuf, act, s);
     } else {
         const int tile_m = variant == MOE_VARIANT_PREFILL ? prefill_tile_m() : 1;
         if ((rc = launch_sort(ids, T, k, E, p, has_shared, tile_m, status, base + L.sort_scratch, s)))
             return rc;
         if (variant == MOE_VARIANT_DECODE)
             rc = launch_decode_ffn(weight_layout, xb, w13, w13_scale, w2, w2_scale, sh, p, aff, T,
-                                   H, I, E, k, abuf, ybuf, s);
+                                   H, I, E, k, abuf, ybuf, act, s);
         else
             rc = launch_prefill_ffn(weight_layout, xb, w13, w13_scale, w2, w2_scale, sh, p, T, H,
-                                    I, E, k, abuf, ybuf, s);
+                                    I, E, k, abuf, ybuf, act, s);
     }
     if (rc) return rc;
     const bool gathered = variant == MOE_VARIANT_PREFILL;
     return launch_combine(ybuf, ids, gathered ? p.inv_route : nullptr,
                           gathered ? aff : nullptr, T, H, k, E,
                           has_shared, status, out, s);
+}
+
+int moe_fused_w8a16(const void* x, const uint8_t* w13, const float* w13_scale,
+                    const uint8_t* w2, const float* w2_scale, const int32_t* ids,
+                    const float* aff, int T, int H, int I, int E, int k,
+                    const moe_expert_w8* shared, float* out, int32_t* status, void* ws,
+                    size_t ws_bytes, int weight_layout, int variant, void* stream) {
+    return moe_fused_w8a16_ex(x, w13, w13_scale, w2, w2_scale, ids, aff, T, H, I, E, k, shared,
+                              out, status, ws, ws_bytes, weight_layout, variant, MOE_ACT_SWIGLU,
+                              stream);
 }
 
 int moe_pack_w8(const uint8_t* src, uint8_t* dst, int64_t n_mats, int rows, int cols,

@@ -78,6 +78,12 @@ __device__ __forceinline__ float swiglu(float g, float u) {
     return g / (1.0f + __expf(-g)) * u;
 }
 
+// relu(u)^2, the activation of non-gated (relu-squared) experts.
+__device__ __forceinline__ float relu2(float u) {
+    const float r = fmaxf(u, 0.0f);
+    return r * r;
+}
+
 // ---------------------------------------------------------------- wave helpers
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (MOE_WAVE - 1); }
 

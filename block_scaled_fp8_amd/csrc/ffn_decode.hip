@@ -24,7 +24,7 @@
 
 namespace moe {
 
-enum { MODE_GATEUP = 0, MODE_DOWN = 1 };
+enum { MODE_GATEUP = 0, MODE_DOWN = 1, MODE_UP = 2 };
 
 constexpr int DEC_THREADS = 256;
 constexpr int DEC_WAVES = 4;
@@ -33,6 +33,8 @@ constexpr int DEC_DEPTH = 4;   // 64-K chunks in flight per wave
 
 // MODE_GATEUP: rows = 32 gate rows + the 32 matching up rows, K = H,
 //              A = x rows of the segment's tokens, out = bf16 SwiGLU into abuf.
+// MODE_UP:     rows = 64 rows of the up projection of a non-gated expert,
+//              K = H, A = x rows, out = bf16 relu(u)^2 into abuf.
 // MODE_DOWN:   rows = 64 rows of W2, K = I, A = abuf rows, out = fp32 ybuf.
 template <int MODE, int MT, int LAYOUT>
 __global__ __launch_bounds__(DEC_THREADS) void decode_ffn_kernel(
@@ -43,8 +45,9 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_ffn_kernel(
     const float* __restrict__ sh_w2s, Plan plan, const float* __restrict__ aff, int T, int H,
     int I, int k, uint16_t* __restrict__ abuf, float* __restrict__ ybuf) {
     constexpr int MROWS = 16 * MT;
-    const int K = MODE == MODE_GATEUP ? H : I;
-    const int ntile_per_seg = MODE == MODE_GATEUP ? I / 32 : H / 64;
+    constexpr bool GATHER = MODE != MODE_DOWN;  // A rows are token rows of x
+    const int K = GATHER ? H : I;
+    const int ntile_per_seg = MODE == MODE_GATEUP ? I / 32 : (MODE == MODE_UP ? I / 64 : H / 64);
     const int seg = blockIdx.x / ntile_per_seg;
     const int nt = blockIdx.x % ntile_per_seg;
     if (seg >= plan.seg_n[0]) return;
@@ -54,9 +57,10 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_ffn_kernel(
 
     const uint8_t* W;
     const float* S;
-    if (MODE == MODE_GATEUP) {
-        W = e >= 0 ? w13 + (size_t)e * 2 * I * H : sh_w13;
-        S = e >= 0 ? w13s + (size_t)e * (2 * I / 128) * (H / 128) : sh_w13s;
+    if (GATHER) {
+        const int n13 = MODE == MODE_GATEUP ? 2 * I : I;  // rows of the expert's first matrix
+        W = e >= 0 ? w13 + (size_t)e * n13 * H : sh_w13;
+        S = e >= 0 ? w13s + (size_t)e * (n13 / 128) * (H / 128) : sh_w13s;
     } else {
         W = e >= 0 ? w2 + (size_t)e * H * I : sh_w2;
         S = e >= 0 ? w2s + (size_t)e * (H / 128) * (I / 128) : sh_w2s;
@@ -96,7 +100,7 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_ffn_kernel(
             int src = -1;
             if (m < rows) {
                 const int p = row0 + m;
-                if (MODE == MODE_GATEUP)
+                if (GATHER)
                     src = e >= 0 ? plan.sorted_route[p] / k : p - (int)R;
                 else
                     src = p;
@@ -111,7 +115,7 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_ffn_kernel(
             const int src = tok_s[mt * 16 + ln];
             avalid[mt] = src >= 0;
             const int s = src >= 0 ? src : 0;
-            aptr[mt] = (MODE == MODE_GATEUP ? x + (size_t)s * H : abuf + (size_t)s * I) + lg * 16;
+            aptr[mt] = (GATHER ? x + (size_t)s * H : abuf + (size_t)s * I) + lg * 16;
         }
 
         f32x4 acc[MT][DEC_NTILE], part[MT][DEC_NTILE];
@@ -210,6 +214,18 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_ffn_kernel(
                     }
                 }
             }
+        } else if (MODE == MODE_UP) {
+            for (int item = wave; item < MT * DEC_NTILE; item += DEC_WAVES) {
+                const int mt = item / DEC_NTILE, j = item % DEC_NTILE;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float u = 0.f;
+#pragma unroll
+                    for (int v = 0; v < DEC_WAVES; ++v) u += red[v][mt][j][i][lane];
+                    const int m = mp + mt * 16 + lg * 4 + i;
+                    if (m < rows) abuf[(size_t)(row0 + m) * I + brow[j] + ln] = f32_to_bf16_bits(relu2(u));
+                }
+            }
         } else {
             for (int item = wave; item < MT * DEC_NTILE; item += DEC_WAVES) {
                 const int mt = item / DEC_NTILE, j = item % DEC_NTILE;
@@ -295,9 +311,10 @@ static int launch_decode_mode_l(int MT, int nseg_max, const uint16_t* x, const u
                                 const SharedW& sh, const Plan& plan, const float* aff, int T,
                                 int H, int I, int k, uint16_t* abuf, float* ybuf,
                                 hipStream_t stream) {
-    const int ntile = MODE == MODE_GATEUP ? I / 32 : H / 64;
+    const int ntile = MODE == MODE_GATEUP ? I / 32 : (MODE == MODE_UP ? I / 64 : H / 64);
     const dim3 grid((unsigned)nseg_max * ntile), block(DEC_THREADS);
-    prof_begin(MODE == MODE_GATEUP ? "decode_gateup_swiglu" : "decode_down", stream);
+    prof_begin(MODE == MODE_GATEUP ? "decode_gateup_swiglu" : (MODE == MODE_UP ? "decode_up_relu2" : "decode_down"),
+               stream);
     if (MT == 1)
         decode_ffn_kernel<MODE, 1, LAYOUT><<<grid, block, 0, stream>>>(
             x, w13, w13s, w2, w2s, sh.w13, sh.w13_scale, sh.w2, sh.w2_scale, plan, aff, T, H, I, k,
@@ -307,7 +324,8 @@ static int launch_decode_mode_l(int MT, int nseg_max, const uint16_t* x, const u
             x, w13, w13s, w2, w2s, sh.w13, sh.w13_scale, sh.w2, sh.w2_scale, plan, aff, T, H, I, k,
             abuf, ybuf);
     prof_end(stream);
-    return check_launch(MODE == MODE_GATEUP ? "decode_ffn_kernel<gateup>" : "decode_ffn_kernel<down>");
+    return check_launch(MODE == MODE_GATEUP ? "decode_ffn_kernel<gateup>"
+                                            : (MODE == MODE_UP ? "decode_ffn_kernel<up>" : "decode_ffn_kernel<down>"));
 }
 
 template <int MODE>
@@ -326,7 +344,7 @@ static int launch_decode_mode(int layout, int MT, int nseg_max, const uint16_t* 
 int launch_decode_fused(int layout, int MT, const uint16_t* x, const uint8_t* w13,
                         const float* w13s, const uint8_t* w2, const float* w2s, const SharedW& sh,
                         const Plan& plan, const float* aff, int T, int H, int I, int E, int k,
-                        float* ybuf, hipStream_t stream);
+                        float* ybuf, int act, hipStream_t stream);
 
 // At most min(E, T*k) routed experts are active.  When that fills most of the
 // chip, one workgroup per active expert (ffn_decode_fused.hip) streams every
@@ -348,16 +366,20 @@ bool decode_fused_fits(int T, int k, int E, int I, int has_shared, bool self_rou
 int launch_decode_ffn(int layout, const uint16_t* x, const uint8_t* w13, const float* w13s,
                       const uint8_t* w2, const float* w2s, const SharedW& sh, const Plan& plan,
                       const float* aff, int T, int H, int I, int E, int k, uint16_t* abuf,
-                      float* ybuf, hipStream_t stream) {
+                      float* ybuf, int act, hipStream_t stream) {
     const int has_shared = sh.w13 != nullptr;
     const int nseg_max = E + has_shared;
     const int MT = decode_mt(T, k, E);
     if (decode_fused_fits(T, k, E, I, has_shared, false))
         return launch_decode_fused(layout, MT, x, w13, w13s, w2, w2s, sh, plan, aff, T, H, I, E,
-                                   k, ybuf, stream);
-    if (int rc = launch_decode_mode<MODE_GATEUP>(layout, MT, nseg_max, x, w13, w13s, w2, w2s, sh,
-                                                 plan, aff, T, H, I, k, abuf, ybuf, stream))
-        return rc;
+                                   k, ybuf, act, stream);
+    const int rc = act == ACT_RELU2
+                       ? launch_decode_mode<MODE_UP>(layout, MT, nseg_max, x, w13, w13s, w2, w2s,
+                                                     sh, plan, aff, T, H, I, k, abuf, ybuf, stream)
+                       : launch_decode_mode<MODE_GATEUP>(layout, MT, nseg_max, x, w13, w13s, w2,
+                                                         w2s, sh, plan, aff, T, H, I, k, abuf,
+                                                         ybuf, stream);
+    if (rc) return rc;
     return launch_decode_mode<MODE_DOWN>(layout, MT, nseg_max, x, w13, w13s, w2, w2s, sh, plan,
                                          aff, T, H, I, k, abuf, ybuf, stream);
 }

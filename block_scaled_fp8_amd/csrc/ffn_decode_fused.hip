@@ -61,7 +61,10 @@ size_t decode_fused_lds_bytes(int MT, int I, int self_routes) {
     return sizeof(uint16_t) * (size_t)(16 * MT) * (I + 8) + sizeof(int32_t) * (size_t)self_routes;
 }
 
-template <int MT, int DEPTH, int LAYOUT, bool SELF>
+// RELU2: a non-gated expert, w13 = the up projection [I, H] alone; a phase-1
+// group is NT up tiles (64 rows, inside one 128-row scale block) and the
+// activation is relu(u)^2.
+template <int MT, int DEPTH, int LAYOUT, bool SELF, bool RELU2>
 __global__ __launch_bounds__(DF_THREADS) void decode_fused_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ w13,
     const float* __restrict__ w13s, const uint8_t* __restrict__ w2,
@@ -130,8 +133,9 @@ __global__ __launch_bounds__(DF_THREADS) void decode_fused_kernel(
         if (e < 0) return (SELF ? R : row0) + m;
         return SELF ? rlist[m] : plan.sorted_route[row0 + m];
     };
-    const uint8_t* W13 = e >= 0 ? w13 + (size_t)e * 2 * I * H : sh_w13;
-    const float* S13 = e >= 0 ? w13s + (size_t)e * (2 * I / 128) * (H / 128) : sh_w13s;
+    const int n13 = RELU2 ? I : 2 * I;  // rows of the expert's first matrix
+    const uint8_t* W13 = e >= 0 ? w13 + (size_t)e * n13 * H : sh_w13;
+    const float* S13 = e >= 0 ? w13s + (size_t)e * (n13 / 128) * (H / 128) : sh_w13s;
     const uint8_t* W2 = e >= 0 ? w2 + (size_t)e * H * I : sh_w2;
     const float* S2 = e >= 0 ? w2s + (size_t)e * (H / 128) * (I / 128) : sh_w2s;
 
@@ -139,7 +143,7 @@ __global__ __launch_bounds__(DF_THREADS) void decode_fused_kernel(
 
     const int nch1 = H >> 6, nch2 = I >> 6;  // chunks per group, both even
     const int kb1 = H >> 7, kb2 = I >> 7;    // scale blocks along K
-    const int G1 = I / (16 * HALF), G2 = H / (16 * NT);
+    const int G1 = I / (16 * (RELU2 ? NT : HALF)), G2 = H / (16 * NT);
     const int n1 = (G1 + DF_WAVES - 1) / DF_WAVES, n2 = (G2 + DF_WAVES - 1) / DF_WAVES;
     const int tot1 = n1 * nch1, tot2 = n2 * nch2;
 
@@ -195,7 +199,7 @@ __global__ __launch_bounds__(DF_THREADS) void decode_fused_kernel(
         auto issue1_b = [&](int d, int g, int c) {
 #pragma unroll
             for (int j = 0; j < NT; ++j) {
-                const int r = (j < HALF ? 0 : I) + (g * HALF + (j % HALF)) * 16;
+                const int r = RELU2 ? (g * NT + j) * 16 : (j < HALF ? 0 : I) + (g * HALF + (j % HALF)) * 16;
                 bq[d][j] = load_stream16(tile_lane_ptr<LAYOUT>(W13, r, H, lane) + (size_t)c * CS);
             }
         };
@@ -227,10 +231,15 @@ __global__ __launch_bounds__(DF_THREADS) void decode_fused_kernel(
             const int g = pg % G1;
             if ((pc & 1) == 0) {
                 const int kb = pc >> 1;
-                const int gi = __builtin_amdgcn_readfirstlane(((g * HALF * 16) >> 7) * kb1 + kb);
-                const int ui = __builtin_amdgcn_readfirstlane(((I + g * HALF * 16) >> 7) * kb1 + kb);
-                rescale(seff0, S13[gi], 0, HALF);
-                rescale(seff1, S13[ui], HALF, NT);
+                if (RELU2) {
+                    const int ui = __builtin_amdgcn_readfirstlane(((g * NT * 16) >> 7) * kb1 + kb);
+                    rescale(seff0, S13[ui], 0, NT);
+                } else {
+                    const int gi = __builtin_amdgcn_readfirstlane(((g * HALF * 16) >> 7) * kb1 + kb);
+                    const int ui = __builtin_amdgcn_readfirstlane(((I + g * HALF * 16) >> 7) * kb1 + kb);
+                    rescale(seff0, S13[gi], 0, HALF);
+                    rescale(seff1, S13[ui], HALF, NT);
+                }
             }
             u32x4 av[MT][2];
 #pragma unroll
@@ -239,20 +248,33 @@ __global__ __launch_bounds__(DF_THREADS) void decode_fused_kernel(
                 av[mt][1] = xvalid[mt] ? aq[d][mt][1] : u32x4{0u, 0u, 0u, 0u};
             }
             mfma_chunk(d, av);
-            if (pc == nch1 - 1) {  // group done: SwiGLU into LDS (padding columns if spare)
+            if (pc == nch1 - 1) {  // group done: activations into LDS (padding columns if spare)
                 const bool real = pg < G1;
+                if (RELU2) {
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
+                    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                    for (int j = 0; j < HALF; ++j)
+                        for (int j = 0; j < NT; ++j)
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const float gv = acc[mt][j][i] * seff0;
-                            const float uv = acc[mt][HALF + j][i] * seff1;
-                            const int m = mt * 16 + lg * 4 + i;
-                            const int col = real ? (g * HALF + j) * 16 + ln : I + (ln & 7);
-                            a_lds[m * astride + col] = f32_to_bf16_bits(swiglu(gv, uv));
-                        }
+                            for (int i = 0; i < 4; ++i) {
+                                const int m = mt * 16 + lg * 4 + i;
+                                const int col = real ? (g * NT + j) * 16 + ln : I + (ln & 7);
+                                a_lds[m * astride + col] = f32_to_bf16_bits(relu2(acc[mt][j][i] * seff0));
+                            }
+                } else {
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                        for (int j = 0; j < HALF; ++j)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                const float gv = acc[mt][j][i] * seff0;
+                                const float uv = acc[mt][HALF + j][i] * seff1;
+                                const int m = mt * 16 + lg * 4 + i;
+                                const int col = real ? (g * HALF + j) * 16 + ln : I + (ln & 7);
+                                a_lds[m * astride + col] = f32_to_bf16_bits(swiglu(gv, uv));
+                            }
+                }
                 reset();
                 pc = 0;
                 pg += DF_WAVES;
@@ -352,7 +374,7 @@ __global__ __launch_bounds__(DF_THREADS) void decode_fused_kernel(
     }
 }
 
-template <int LAYOUT, bool SELF>
+template <int LAYOUT, bool SELF, bool RELU2>
 static int launch_decode_fused_l(int MT, const uint16_t* x, const uint8_t* w13, const float* w13s,
                                  const uint8_t* w2, const float* w2s, const SharedW& sh,
                                  const Plan& plan, const int32_t* ids, const float* aff, int T,
@@ -363,15 +385,31 @@ static int launch_decode_fused_l(int MT, const uint16_t* x, const uint8_t* w13, 
     float* ytrash = ybuf + ((size_t)T * k + (sh.w13 ? (size_t)T : 0)) * H;
     prof_begin("decode_fused_expert", stream);
     if (MT == 1)
-        decode_fused_kernel<1, 2, LAYOUT, SELF><<<nseg_max, DF_THREADS, lds, stream>>>(
+        decode_fused_kernel<1, 2, LAYOUT, SELF, RELU2><<<nseg_max, DF_THREADS, lds, stream>>>(
             x, w13, w13s, w2, w2s, sh.w13, sh.w13_scale, sh.w2, sh.w2_scale, plan, ids, E, aff, T,
             H, I, k, ybuf, ytrash);
     else
-        decode_fused_kernel<2, 2, LAYOUT, SELF><<<nseg_max, DF_THREADS, lds, stream>>>(
+        decode_fused_kernel<2, 2, LAYOUT, SELF, RELU2><<<nseg_max, DF_THREADS, lds, stream>>>(
             x, w13, w13s, w2, w2s, sh.w13, sh.w13_scale, sh.w2, sh.w2_scale, plan, ids, E, aff, T,
             H, I, k, ybuf, ytrash);
     prof_end(stream);
     return check_launch("decode_fused_kernel");
+}
+
+template <bool SELF>
+static int launch_decode_fused_any(int layout, int MT, const uint16_t* x, const uint8_t* w13,
+                                   const float* w13s, const uint8_t* w2, const float* w2s,
+                                   const SharedW& sh, const Plan& plan, const int32_t* ids,
+                                   const float* aff, int T, int H, int I, int E, int k,
+                                   float* ybuf, int act, hipStream_t stream) {
+#define MOE_DF_LAUNCH(L, R)                                                                      \
+    launch_decode_fused_l<L, SELF, R>(MT, x, w13, w13s, w2, w2s, sh, plan, ids, aff, T, H, I, E, \
+                                      k, ybuf, stream)
+    const bool relu2 = act == ACT_RELU2;
+    if (layout == LAYOUT_TILED)
+        return relu2 ? MOE_DF_LAUNCH(LAYOUT_TILED, true) : MOE_DF_LAUNCH(LAYOUT_TILED, false);
+    return relu2 ? MOE_DF_LAUNCH(LAYOUT_ROWMAJOR, true) : MOE_DF_LAUNCH(LAYOUT_ROWMAJOR, false);
+#undef MOE_DF_LAUNCH
 }
 
 // One workgroup per possible segment (E routed + shared); workgroups past the
@@ -379,25 +417,20 @@ static int launch_decode_fused_l(int MT, const uint16_t* x, const uint8_t* w13, 
 int launch_decode_fused(int layout, int MT, const uint16_t* x, const uint8_t* w13,
                         const float* w13s, const uint8_t* w2, const float* w2s, const SharedW& sh,
                         const Plan& plan, const float* aff, int T, int H, int I, int E, int k,
-                        float* ybuf, hipStream_t stream) {
-    if (layout == LAYOUT_TILED)
-        return launch_decode_fused_l<LAYOUT_TILED, false>(MT, x, w13, w13s, w2, w2s, sh, plan,
-                                                          nullptr, aff, T, H, I, E, k, ybuf, stream);
-    return launch_decode_fused_l<LAYOUT_ROWMAJOR, false>(MT, x, w13, w13s, w2, w2s, sh, plan,
-                                                         nullptr, aff, T, H, I, E, k, ybuf, stream);
+                        float* ybuf, int act, hipStream_t stream) {
+    return launch_decode_fused_any<false>(layout, MT, x, w13, w13s, w2, w2s, sh, plan, nullptr,
+                                          aff, T, H, I, E, k, ybuf, act, stream);
 }
 
 // The self-routed form: no sort beforehand; workgroup e scans the ids.
 int launch_decode_fused_self(int layout, int MT, const uint16_t* x, const uint8_t* w13,
                              const float* w13s, const uint8_t* w2, const float* w2s,
                              const SharedW& sh, const int32_t* ids, const float* aff, int T,
-                             int H, int I, int E, int k, float* ybuf, hipStream_t stream) {
+                             int H, int I, int E, int k, float* ybuf, int act,
+                             hipStream_t stream) {
     const Plan none{};
-    if (layout == LAYOUT_TILED)
-        return launch_decode_fused_l<LAYOUT_TILED, true>(MT, x, w13, w13s, w2, w2s, sh, none, ids,
-                                                         aff, T, H, I, E, k, ybuf, stream);
-    return launch_decode_fused_l<LAYOUT_ROWMAJOR, true>(MT, x, w13, w13s, w2, w2s, sh, none, ids,
-                                                        aff, T, H, I, E, k, ybuf, stream);
+    return launch_decode_fused_any<true>(layout, MT, x, w13, w13s, w2, w2s, sh, none, ids, aff, T,
+                                         H, I, E, k, ybuf, act, stream);
 }
 
 int decode_self_routed_max_routes() { return DF_SELF_MAX_ROUTES; }

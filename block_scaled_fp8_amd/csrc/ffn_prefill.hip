@@ -108,11 +108,16 @@ int prefill_tile_m() { return PF_BM; }
 // Widths the grouped GEMMs tile exactly (K % 128 holds for every valid call);
 // the per-tile scale table (2 rows of K / 128 floats, padded to 64) must fit
 // in LDS beside the stages, which holds for K <= 65536.
-int prefill_supported(int H, int I) {
-    return H % 256 == 0 && (2 * I) % 256 == 0 && H <= 65536 && I <= 65536;
+// relu^2 experts tile their I up columns in 256-wide blocks.
+int prefill_supported(int H, int I, int act) {
+    const int ncols = act == ACT_RELU2 ? I : 2 * I;
+    return H % 256 == 0 && ncols % 256 == 0 && H <= 65536 && I <= 65536;
 }
 
-enum { PF_GATEUP = 0, PF_DOWN = 1 };
+// PF_GATEUP: gate and up columns side by side, SwiGLU epilogue into abuf;
+// PF_UP:     the up projection of a non-gated expert, relu^2 epilogue into abuf;
+// PF_DOWN:   the down projection, fp32 rows into ybuf.
+enum { PF_GATEUP = 0, PF_DOWN = 1, PF_UP = 2 };
 
 // silu(g) * u with the hardware reciprocal (about 1 ulp) in place of an IEEE
 // divide; exp(-g) overflowing to +inf gives the correct limit 0.
@@ -185,8 +190,10 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
     const int p0 = ti.y;         // first sorted row of the tile
     const int rows_here = ti.z;  // rows in the tile (1 .. BM)
 
-    const int K = MODE == PF_GATEUP ? H : I;
-    const int Nrows = MODE == PF_GATEUP ? 2 * I : H;     // rows of the weight matrix
+    constexpr bool GATHER = MODE != PF_DOWN;   // operand rows gathered from x
+    constexpr bool PAIRED = MODE == PF_GATEUP; // gate and up columns side by side
+    const int K = GATHER ? H : I;
+    const int Nrows = MODE == PF_GATEUP ? 2 * I : (MODE == PF_UP ? I : H);  // weight rows
     const uint8_t* W = e >= 0 ? wexp + (size_t)e * Nrows * K : wsh;
     const float* S = e >= 0 ? sexp + (size_t)e * (Nrows / 128) * (K / 128) : ssh;
     const int R = T * k;
@@ -197,7 +204,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
     // of x through the sorted route map (shared expert: token p - R); down
     // reads the activations at the sorted rows themselves, so its loads need
     // no table.  Both write at the sorted row.
-    if (MODE == PF_GATEUP) {
+    if (GATHER) {
         if (tid < BM) {
             const int p = p0 + tid;
             const bool valid = tid < rows_here;
@@ -213,16 +220,16 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
     // (the launcher checks that the matrix is under 4 GB), so the loads
     // address through a scalar base
     const int ar_sub = lane >> 3, apiece = lane & 7;
-    const char* abase = MODE == PF_GATEUP ? reinterpret_cast<const char*>(x)
-                                          : reinterpret_cast<const char*>(abuf_in);
+    const char* abase = GATHER ? reinterpret_cast<const char*>(x)
+                               : reinterpret_cast<const char*>(abuf_in);
     uint32_t asrc[C::A_INSTR];
 #pragma unroll
     for (int q = 0; q < C::A_INSTR; ++q) {
         const int row = (wave * C::A_INSTR + q) * 8 + ar_sub;
         const int sw = apiece ^ ((row >> 1) & 7);  // swizzled piece this lane fetches
-        const uint32_t src_row = MODE == PF_GATEUP ? (uint32_t)row_tok[row]
-                                                   : (uint32_t)(p0 + (row < rows_here ? row : 0));
-        asrc[q] = src_row * (uint32_t)(2 * (MODE == PF_GATEUP ? H : I)) + sw * 16;
+        const uint32_t src_row = GATHER ? (uint32_t)row_tok[row]
+                                        : (uint32_t)(p0 + (row < rows_here ? row : 0));
+        asrc[q] = src_row * (uint32_t)(2 * (GATHER ? H : I)) + sw * 16;
     }
     // weights: instruction q of wave w fills 16-row tile w*B_INSTR + q
     constexpr int HALF_T = BN / 2 / 16;  // gate tiles in a gate/up tile (MODE 0)
@@ -233,7 +240,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
     for (int q = 0; q < C::B_INSTR; ++q) {
         const int t16 = wave * C::B_INSTR + q;
         int wrow;
-        if (MODE == PF_GATEUP)
+        if (PAIRED)
             wrow = (t16 < HALF_T ? 0 : I) + nb * (BN / 2) + (t16 % HALF_T) * 16;
         else
             wrow = nb * BN + t16 * 16;
@@ -273,7 +280,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
     const int l16 = lane & 15, g16 = lane >> 4;
     uint32_t a_off[4];
     uint32_t b_off;
-    const int t16 = MODE == PF_GATEUP ? wn * (C::WCOLS / 32) : wn * (C::WCOLS / 16);
+    const int t16 = PAIRED ? wn * (C::WCOLS / 32) : wn * (C::WCOLS / 16);
     if constexpr (C::M16) {
         const int row = wm * C::WROWS + l16;
 #pragma unroll
@@ -296,7 +303,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
     auto a_step = [](int mt) { return mt * C::MS * 128; };
     auto b_step = [](int nt) {
         constexpr int T16 = C::MS / 16;  // 16-row weight tiles per MFMA column tile
-        if (MODE == PF_GATEUP)
+        if (PAIRED)
             return ((nt < C::NT / 2 ? 0 : HALF_T) + (nt % (C::NT / 2)) * T16) * 1024;
         return nt * T16 * 1024;
     };
@@ -315,7 +322,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
         for (int it = wave; it < NR * nchunk; it += C::WAVES) {
             const int j = it / nchunk, c = it - j * nchunk;
             int sr;
-            if (MODE == PF_GATEUP)
+            if (PAIRED)
                 sr = j < NR / 2 ? ((nb * (BN / 2)) >> 7) + j : ((I + nb * (BN / 2)) >> 7) + j - NR / 2;
             else
                 sr = ((nb * BN) >> 7) + j;
@@ -325,7 +332,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
     }
     // this wave's table rows: g = 0 its gate (or only) columns, g = 1 its up columns
     int sj[2];
-    if (MODE == PF_GATEUP) {
+    if (PAIRED) {
         sj[0] = (wn * (C::WCOLS / 2)) >> 7;
         sj[1] = NR / 2 + sj[0];
     } else {
@@ -392,7 +399,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
             // before part 0's MFMAs
 #pragma unroll
             for (int nt = 0; nt < C::NT; ++nt) {
-                const float f = MODE == PF_GATEUP ? rr[nt / (C::NT / 2)] : rr[0];
+                const float f = PAIRED ? rr[nt / (C::NT / 2)] : rr[0];
 #pragma unroll
                 for (int mt = 0; mt < MTA; ++mt)
 #pragma unroll
@@ -408,7 +415,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
                 bf = fp8x8_to_bf16x8(b[nt][0], b[nt][1]);
             else
                 bf = j == 0 ? fp8x8_to_bf16x8(b[nt][0], b[nt][1]) : fp8x8_to_bf16x8(b[nt][2], b[nt][3]);
-            const float f = MODE == PF_GATEUP ? rr[nt / (C::NT / 2)] : rr[0];
+            const float f = PAIRED ? rr[nt / (C::NT / 2)] : rr[0];
 #pragma unroll
             for (int mt = 0; mt < MTA; ++mt) {
                 if (rescale)
@@ -514,7 +521,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
 #pragma unroll
         for (int q = 0; q < RQ; ++q) {
             const int r0 = wm * C::WROWS + mt * C::MS + (C::M16 ? 4 * g16 : 8 * q + 4 * lg);
-            if (MODE == PF_GATEUP) {
+            if (GATHER) {
                 dst4[mt][q] = *reinterpret_cast<const int4*>(row_dst + r0);
             } else {
 #pragma unroll
@@ -533,6 +540,11 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
                 for (int nt = 0; nt < C::NT / 2; ++nt)
                     orow[nt * C::MS] = f32_to_bf16_bits(
                         swiglu_fast(acc[mt][nt][i] * seff[0], acc[mt][nt + C::NT / 2][i] * seff[1]));
+            } else if (MODE == PF_UP) {
+                uint16_t* orow = abuf_out + (size_t)dst * I + nb * BN + wn * C::WCOLS + ocol;
+#pragma unroll
+                for (int nt = 0; nt < C::NT; ++nt)
+                    orow[nt * C::MS] = f32_to_bf16_bits(relu2(acc[mt][nt][i] * seff[0]));
             } else {
                 // y of the route (the combine multiplies it by the affinity);
                 // each contribution row is read once, by the combine: streaming
@@ -546,14 +558,14 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
 }
 
 template <int MODE>
-static inline int K_of(int H, int I) { return MODE == PF_GATEUP ? H : I; }
+static inline int K_of(int H, int I) { return MODE == PF_DOWN ? I : H; }
 
 template <int MODE, int LAYOUT, class C>
 static int launch_pf(const uint16_t* x, const uint16_t* abuf_in, const uint8_t* wexp,
                      const float* sexp, const uint8_t* wsh, const float* ssh, const Plan& plan,
                      int T, int H, int I, int E, int k, int has_shared, uint16_t* abuf_out,
                      float* ybuf, hipStream_t stream) {
-    const int nblk = MODE == PF_GATEUP ? 2 * I / C::BN : H / C::BN;
+    const int nblk = MODE == PF_GATEUP ? 2 * I / C::BN : (MODE == PF_UP ? I : H) / C::BN;
     const long R = (long)T * k;
     const long max_tiles = (R + C::BM - 1) / C::BM + E + (has_shared ? (T + C::BM - 1) / C::BM : 0);
     // (the sort's tile list has room for at least this many records)
@@ -564,28 +576,34 @@ static int launch_pf(const uint16_t* x, const uint16_t* abuf_in, const uint8_t* 
         return MOE_EUNSUPPORTED;
     }
     // activation rows are addressed by 32-bit byte offsets
-    const size_t a_bytes = MODE == PF_GATEUP ? (size_t)T * H * 2 : (size_t)(R + (has_shared ? T : 0)) * I * 2;
+    const size_t a_bytes = MODE != PF_DOWN ? (size_t)T * H * 2 : (size_t)(R + (has_shared ? T : 0)) * I * 2;
     if (a_bytes > 0xFFFFFFFFull) {
         set_error("prefill: activation matrix over 4 GB");
         return MOE_EUNSUPPORTED;
     }
     const size_t kbp = ((size_t)K_of<MODE>(H, I) / 128 + 63) / 64 * 64;
     const size_t lds = (size_t)C::STAGES * C::STAGE + (size_t)(C::BN / 128) * kbp * 4;
-    prof_begin(MODE == PF_GATEUP ? "prefill_gateup_swiglu" : "prefill_down", stream);
+    prof_begin(MODE == PF_GATEUP ? "prefill_gateup_swiglu" : (MODE == PF_UP ? "prefill_up_relu2" : "prefill_down"),
+               stream);
     prefill_gemm_kernel<MODE, LAYOUT, C><<<(unsigned)grid, C::THREADS, lds, stream>>>(
         x, abuf_in, wexp, sexp, wsh, ssh, plan, T, H, I, k, nblk, (int)max_tiles, abuf_out, ybuf);
     prof_end(stream);
-    return check_launch(MODE == PF_GATEUP ? "prefill_gemm_kernel<gateup>" : "prefill_gemm_kernel<down>");
+    return check_launch(MODE == PF_GATEUP ? "prefill_gemm_kernel<gateup>"
+                                          : (MODE == PF_UP ? "prefill_gemm_kernel<up>" : "prefill_gemm_kernel<down>"));
 }
 
 template <int LAYOUT>
 static int launch_prefill_c(const uint16_t* x, const uint8_t* w13, const float* w13s,
                             const uint8_t* w2, const float* w2s, const SharedW& sh,
                             const Plan& plan, int T, int H, int I, int E, int k, uint16_t* abuf,
-                            float* ybuf, hipStream_t stream) {
+                            float* ybuf, int act, hipStream_t stream) {
     const int hs = sh.w13 != nullptr;
-    int rc = launch_pf<PF_GATEUP, LAYOUT, PfGateUp>(x, nullptr, w13, w13s, sh.w13, sh.w13_scale,
-                                                    plan, T, H, I, E, k, hs, abuf, ybuf, stream);
+    int rc = act == ACT_RELU2
+                 ? launch_pf<PF_UP, LAYOUT, PfGateUp>(x, nullptr, w13, w13s, sh.w13, sh.w13_scale,
+                                                      plan, T, H, I, E, k, hs, abuf, ybuf, stream)
+                 : launch_pf<PF_GATEUP, LAYOUT, PfGateUp>(x, nullptr, w13, w13s, sh.w13,
+                                                          sh.w13_scale, plan, T, H, I, E, k, hs,
+                                                          abuf, ybuf, stream);
     if (rc == MOE_OK)
         rc = launch_pf<PF_DOWN, LAYOUT, PfDown>(x, abuf, w2, w2s, sh.w2, sh.w2_scale, plan, T, H, I,
                                                 E, k, hs, abuf, ybuf, stream);
@@ -593,9 +611,10 @@ static int launch_prefill_c(const uint16_t* x, const uint8_t* w13, const float* 
 }
 
 // Host-side checks of a prefill call, before anything is launched.
-int prefill_check(int T, int H, int I, int E, int k, int has_shared) {
-    if (!prefill_supported(H, I)) {
-        set_error("prefill variant needs H %% 256 == 0, 2I %% 256 == 0 and H, I <= 65536 (got H=%d, I=%d)", H, I);
+int prefill_check(int T, int H, int I, int E, int k, int has_shared, int act) {
+    if (!prefill_supported(H, I, act)) {
+        set_error("prefill variant needs H %% 256 == 0, %s %% 256 == 0 and H, I <= 65536 (got H=%d, I=%d)",
+                  act == ACT_RELU2 ? "I" : "2I", H, I);
         return MOE_EUNSUPPORTED;
     }
     const long R = (long)T * k, rows = R + (has_shared ? T : 0);
@@ -615,9 +634,10 @@ int prefill_check(int T, int H, int I, int E, int k, int has_shared) {
 int launch_prefill_ffn(int layout, const uint16_t* x, const uint8_t* w13, const float* w13s,
                        const uint8_t* w2, const float* w2s, const SharedW& sh, const Plan& plan,
                        int T, int H, int I, int E, int k, uint16_t* abuf, float* ybuf,
-                       hipStream_t stream) {
-    if (!prefill_supported(H, I)) {
-        set_error("prefill variant needs H %% 256 == 0, 2I %% 256 == 0 and H, I <= 65536 (got H=%d, I=%d)", H, I);
+                       int act, hipStream_t stream) {
+    if (!prefill_supported(H, I, act)) {
+        set_error("prefill variant needs H %% 256 == 0, %s %% 256 == 0 and H, I <= 65536 (got H=%d, I=%d)",
+                  act == ACT_RELU2 ? "I" : "2I", H, I);
         return MOE_EUNSUPPORTED;
     }
     if (!plan.tile_info || !plan.tile_n || !plan.sorted_route) {
@@ -626,9 +646,9 @@ int launch_prefill_ffn(int layout, const uint16_t* x, const uint8_t* w13, const 
     }
     if (layout == LAYOUT_TILED)
         return launch_prefill_c<LAYOUT_TILED>(x, w13, w13s, w2, w2s, sh, plan, T, H, I, E, k, abuf,
-                                              ybuf, stream);
+                                              ybuf, act, stream);
     return launch_prefill_c<LAYOUT_ROWMAJOR>(x, w13, w13s, w2, w2s, sh, plan, T, H, I, E, k, abuf,
-                                             ybuf, stream);
+                                             ybuf, act, stream);
 }
 
 }  // namespace moe

@@ -41,6 +41,10 @@ size_t sort_scratch_bytes(int R, int E);
 int launch_sort(const int32_t* ids, int T, int k, int E, const Plan& plan, int has_shared,
                 int tile_m, int32_t* status, void* scratch, hipStream_t stream);
 
+// Expert activation (the values of MOE_ACT_*): SwiGLU on gate and up rows of
+// w13 [2I, H], or relu(u)^2 on the up rows of a non-gated expert's w13 [I, H].
+enum { ACT_SWIGLU = 0, ACT_RELU2 = 1 };
+
 // Kernel launchers (route.hip, ffn_decode.hip, ffn_prefill.hip, misc).
 int launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* aff,
                  int32_t* status, hipStream_t stream);
@@ -63,18 +67,18 @@ int launch_route_proj(const uint16_t* x, const uint16_t* wg, int T, int H, int E
 int launch_decode_ffn(int layout, const uint16_t* x, const uint8_t* w13, const float* w13s,
                       const uint8_t* w2, const float* w2s, const SharedW& sh, const Plan& plan,
                       const float* aff, int T, int H, int I, int E, int k, uint16_t* abuf,
-                      float* ybuf, hipStream_t stream);
+                      float* ybuf, int act, hipStream_t stream);
 // Writes y (without the affinity) of every route at its sorted row of ybuf.
 int launch_prefill_ffn(int layout, const uint16_t* x, const uint8_t* w13, const float* w13s,
                        const uint8_t* w2, const float* w2s, const SharedW& sh, const Plan& plan,
-                       int T, int H, int I, int E, int k, uint16_t* abuf, float* ybuf,
+                       int T, int H, int I, int E, int k, uint16_t* abuf, float* ybuf, int act,
                        hipStream_t stream);
 int launch_pack_w8(const uint8_t* src, uint8_t* dst, int64_t n_mats, int rows, int cols,
                    hipStream_t stream);
 int prefill_tile_m();
-int prefill_supported(int H, int I);
+int prefill_supported(int H, int I, int act);
 // MOE_OK, or MOE_EUNSUPPORTED with the error message set.
-int prefill_check(int T, int H, int I, int E, int k, int has_shared);
+int prefill_check(int T, int H, int I, int E, int k, int has_shared, int act);
 // Sums, per token, the k route rows whose id is valid (plus the shared row at
 // R + t).  Decode producers write aff * y at row r (inv_route and aff null);
 // prefill producers write y at the route's sorted position, and the sum takes
@@ -93,7 +97,8 @@ int decode_self_routed_max_routes();
 int launch_decode_fused_self(int layout, int MT, const uint16_t* x, const uint8_t* w13,
                              const float* w13s, const uint8_t* w2, const float* w2s,
                              const SharedW& sh, const int32_t* ids, const float* aff, int T,
-                             int H, int I, int E, int k, float* ybuf, hipStream_t stream);
+                             int H, int I, int E, int k, float* ybuf, int act,
+                             hipStream_t stream);
 int launch_decode_e4m3fn(const uint8_t* codes, uint16_t* out, int64_t n, hipStream_t stream);
 int launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t stream);
 

@@ -28,7 +28,8 @@ Recipe (every draw is seeded; ``seed`` selects the stream):
   ``float8_e4m3fn`` cast (round to nearest even); this is input preparation
   only and plays no part in what is checked.
 * ``w13``  uint8 [E, 2I, H]: rows 0..I-1 are the gate projection, rows I..2I-1
-  the up projection; ``w13_scale`` fp32 [E, 2I/128, H/128].
+  the up projection; ``w13_scale`` fp32 [E, 2I/128, H/128].  Non-gated
+  (relu^2) experts draw the up projection alone, [E, I, H].
 * ``w2``   uint8 [E, H, I]; ``w2_scale`` fp32 [E, H/128, I/128].
 * shared expert (optional): the same format for one expert, drawn after the
   routed experts.
@@ -136,12 +137,15 @@ def make_activations(cfg: MoeConfig, seed: int, device="cpu"):
     return x.contiguous(), logits.contiguous()
 
 
-def make_weights(cfg: MoeConfig, seed: int, device="cpu"):
-    w13, w13_scale = _draw_expert_weights(cfg.E, 2 * cfg.I, cfg.H, seed, 3, device)
+def make_weights(cfg: MoeConfig, seed: int, device="cpu", activation="swiglu"):
+    """Block-scaled FP8 expert weights; activation "relu2" draws non-gated
+    experts, whose first matrix is the up projection alone ([I, H])."""
+    n13 = cfg.I if activation == "relu2" else 2 * cfg.I
+    w13, w13_scale = _draw_expert_weights(cfg.E, n13, cfg.H, seed, 3, device)
     w2, w2_scale = _draw_expert_weights(cfg.E, cfg.H, cfg.I, seed, 4, device)
     out = dict(w13=w13, w13_scale=w13_scale, w2=w2, w2_scale=w2_scale)
     if cfg.shared:
-        s13, s13s = _draw_expert_weights(1, 2 * cfg.I, cfg.H, seed, 5, device)
+        s13, s13s = _draw_expert_weights(1, n13, cfg.H, seed, 5, device)
         s2, s2s = _draw_expert_weights(1, cfg.H, cfg.I, seed, 6, device)
         out["shared"] = dict(w13=s13[0], w13_scale=s13s[0], w2=s2[0], w2_scale=s2s[0])
     else:
@@ -156,13 +160,13 @@ def make_gate_weights(E: int, H: int, seed: int, device="cpu"):
     return w.to(torch.bfloat16).contiguous()
 
 
-def make_case(cfg: MoeConfig | str, seed: int = 0, device="cpu"):
+def make_case(cfg: MoeConfig | str, seed: int = 0, device="cpu", activation="swiglu"):
     """All inputs of one workload: x, logits and the block-scaled FP8 weights."""
     if isinstance(cfg, str):
         cfg = CONFIGS[cfg]
     x, logits = make_activations(cfg, seed, device)
     case = dict(cfg=cfg, x=x, logits=logits)
-    case.update(make_weights(cfg, seed, device))
+    case.update(make_weights(cfg, seed, device, activation))
     return case
 
 

@@ -69,6 +69,11 @@ enum {
 };
 
 enum {
+    MOE_ACT_SWIGLU = 0,  /* silu(gate) * up; w13 = [gate; up] rows, [2I, H] per expert */
+    MOE_ACT_RELU2 = 1    /* relu(up)^2, non-gated experts; w13 = up rows only, [I, H] */
+};
+
+enum {
     MOE_LAYOUT_ROWMAJOR = 0,  /* FP8 weights as [rows, K], K contiguous */
     MOE_LAYOUT_TILED = 1      /* tile-coalesced, see moe_pack_w8 */
 };
@@ -178,8 +183,8 @@ int moe_pack_w8(const uint8_t* src, uint8_t* dst, int64_t n_mats, int rows, int 
 
 /* One expert's block-scaled FP8 weights (same H and I as the routed experts). */
 typedef struct {
-    const uint8_t* w13;        /* [2I, H] E4M3FN: rows 0..I-1 gate, I..2I-1 up */
-    const float* w13_scale;    /* [2I/128, H/128] fp32 */
+    const uint8_t* w13;        /* [2I, H] E4M3FN: rows 0..I-1 gate, I..2I-1 up (relu^2: [I, H] up) */
+    const float* w13_scale;    /* [2I/128, H/128] fp32 (relu^2: [I/128, H/128]) */
     const uint8_t* w2;         /* [H, I] E4M3FN */
     const float* w2_scale;     /* [H/128, I/128] fp32 */
 } moe_expert_w8;
@@ -221,6 +226,29 @@ int moe_fused_w8a16(const void* x,
                     const moe_expert_w8* shared, float* out,
                     int32_t* status, void* ws, size_t ws_bytes,
                     int weight_layout, int variant, void* stream);
+
+/*
+ * moe_fused_w8a16_ex -- moe_fused_w8a16 with a choice of expert activation.
+ * Source for MOE_ACT_RELU2: "spark_model/layers/nemotron_moe.rs", module
+ * documentation: the routed experts run an up projection, then a fused
+ * relu^2 + down projection, and the shared expert runs up + relu^2 + down.
+ *   activation MOE_ACT_SWIGLU: exactly moe_fused_w8a16.
+ *              MOE_ACT_RELU2: expert e computes y = W2[e] relu(W1[e] x)^2 with
+ *              w13 [E, I, H] holding W1 (and w13_scale [E, I/128, H/128]); the
+ *              shared expert's w13 is [I, H] likewise.  The relu^2 output is
+ *              rounded to bf16 before the down GEMM, as the SwiGLU output is.
+ *              The prefill variant then needs I % 256 == 0 instead of 2I % 256.
+ * Every other argument, the workspace size and the error behaviour are those
+ * of moe_fused_w8a16; an unknown activation gives MOE_EINVAL.
+ */
+int moe_fused_w8a16_ex(const void* x,
+                       const uint8_t* w13, const float* w13_scale,
+                       const uint8_t* w2, const float* w2_scale,
+                       const int32_t* ids, const float* aff,
+                       int T, int H, int I, int E, int k,
+                       const moe_expert_w8* shared, float* out,
+                       int32_t* status, void* ws, size_t ws_bytes,
+                       int weight_layout, int variant, int activation, void* stream);
 
 /*
  * moe_decode_e4m3fn -- decode n E4M3FN bytes to bf16 bit patterns with the

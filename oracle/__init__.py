@@ -24,6 +24,7 @@ from .moe_ref import (  # noqa: F401
     router_logits,
     sort_by_expert,
     swiglu,
+    relu2,
     expert_mlp,
     moe_ffn,
     moe_forward,

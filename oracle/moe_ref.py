@@ -186,20 +186,30 @@ def swiglu(g, u):
         return g / (1.0 + np.exp(-g)) * u
 
 
-def expert_mlp(xrows, w13, w13_scale, w2, w2_scale):
+def relu2(u):
+    """relu(u)^2 = max(u, 0)^2."""
+    return np.maximum(u, 0.0) ** 2
+
+
+def expert_mlp(xrows, w13, w13_scale, w2, w2_scale, activation="swiglu"):
     """One expert on rows of x (float64 [M, H]) -> float64 [M, H].
 
-    w13 [2I, H] (gate rows first, then up rows), w2 [H, I], both block-scaled."""
+    SwiGLU: w13 [2I, H] (gate rows first, then up rows); relu2 ([SPARK] module
+    documentation: up projection, then relu^2 and the down projection): w13
+    [I, H] is the up projection alone.  w2 [H, I]; all block-scaled."""
     W13 = dequantize_blocks(w13, w13_scale)
-    I = W13.shape[0] // 2
-    g = xrows @ W13[:I].T
-    u = xrows @ W13[I:].T
-    a = swiglu(g, u)
+    if activation == "relu2":
+        a = relu2(xrows @ W13.T)
+    else:
+        I = W13.shape[0] // 2
+        g = xrows @ W13[:I].T
+        u = xrows @ W13[I:].T
+        a = swiglu(g, u)
     W2 = dequantize_blocks(w2, w2_scale)
     return a @ W2.T
 
 
-def moe_ffn(x, w13, w13_scale, w2, w2_scale, ids, aff, shared=None):
+def moe_ffn(x, w13, w13_scale, w2, w2_scale, ids, aff, shared=None, activation="swiglu"):
     """out[t] = sum_j aff[t, j] * MLP_{ids[t, j]}(x[t]) (+ shared MLP(x[t])).
 
     x is [T, H] (bf16 values given as float32/float64), ids [T, k], aff [T, k].
@@ -212,11 +222,11 @@ def moe_ffn(x, w13, w13_scale, w2, w2_scale, ids, aff, shared=None):
     out = np.zeros((T, H), dtype=np.float64)
     for e in np.unique(ids):
         t_idx, j_idx = np.nonzero(ids == e)
-        y = expert_mlp(x[t_idx], w13[e], w13_scale[e], w2[e], w2_scale[e])
+        y = expert_mlp(x[t_idx], w13[e], w13_scale[e], w2[e], w2_scale[e], activation)
         np.add.at(out, t_idx, aff[t_idx, j_idx][:, None] * y)
     if shared is not None:
         out += expert_mlp(x, shared["w13"], shared["w13_scale"],
-                          shared["w2"], shared["w2_scale"])
+                          shared["w2"], shared["w2_scale"], activation)
     return out
 
 

@@ -11,12 +11,13 @@ OUT_TOL = 2e-2          # max |gpu - oracle| <= OUT_TOL * RMS(oracle output)
 AFF_RTOL = 2e-6         # fp32 exp/sum/divide against float64
 
 
-def gpu_case(name_or_cfg, seed=0):
+def gpu_case(name_or_cfg, seed=0, activation="swiglu"):
     cfg = synth.CONFIGS[name_or_cfg] if isinstance(name_or_cfg, str) else name_or_cfg
     dev = "cuda"
     # tiny geometries are drawn on the CPU; the large ones on the GPU
     gen_dev = "cpu" if cfg.E * 3 * cfg.H * cfg.I < (64 << 20) else dev
-    case = synth.make_case(cfg, seed, gen_dev)
+    case = synth.make_case(cfg, seed, gen_dev, activation)
+    case["activation"] = activation
     for n in ("x", "logits", "w13", "w13_scale", "w2", "w2_scale"):
         case[n] = case[n].to(dev)
     if case["shared"] is not None:
@@ -29,6 +30,7 @@ def np_(t):
 
 
 def oracle_rows(case, ids, aff, rows, with_shared=True):
+    """(The case's "activation" entry selects the expert MLP.)"""
     """Oracle output for the given token rows, copying only the experts they use."""
     rows = np.asarray(rows)
     sub_ids = np.asarray(ids)[rows]
@@ -43,7 +45,8 @@ def oracle_rows(case, ids, aff, rows, with_shared=True):
     if with_shared and case.get("shared") is not None:
         sh = {n: np_(t) for n, t in case["shared"].items()}
     x = np_(case["x"].float())[rows]
-    return oracle.moe_ffn(x, w13, w13s, w2, w2s, remap, np.asarray(aff)[rows], sh)
+    return oracle.moe_ffn(x, w13, w13s, w2, w2s, remap, np.asarray(aff)[rows], sh,
+                          activation=case.get("activation", "swiglu"))
 
 
 def assert_out_close(got, ref, tol=OUT_TOL, what=""):

@@ -23,7 +23,8 @@ def _declared_functions():
 def test_header_declares_the_boundary():
     names = _declared_functions()
     for n in ("moe_route", "moe_route_sigmoid", "moe_route_proj", "moe_sort", "moe_fused_w8a16", "moe_last_error",
-              "moe_sort_workspace_bytes", "moe_fused_workspace_bytes", "moe_decode_e4m3fn",
+              "moe_sort_workspace_bytes", "moe_fused_workspace_bytes", "moe_fused_w8a16_ex",
+              "moe_decode_e4m3fn",
               "moe_pack_w8"):
         assert n in names
     assert set(names) == set(binding.EXPORTED)
@@ -111,6 +112,21 @@ def test_sort_argument_checks():
     assert lib.moe_sort(fake, T, k, E, fake, fake, fake, fake, None, fake, need - 1, None) == binding.MOE_EINVAL
     assert b"workspace" in lib.moe_last_error()
     assert lib.moe_sort_workspace_bytes(64, 8, 256) == 0   # single-workgroup path needs none
+
+
+def test_fused_activation_checks():
+    lib = binding.load_library()
+    f = ctypes.c_void_p(0x1000)
+    o = ctypes.c_void_p(0x3000)
+    ws = lib.moe_fused_workspace_bytes(64, 2048, 512, 256, 8, 0, 0)
+    base = (f, f, f, f, f, f, f, 64, 2048, 512, 256, 8, None, o, None, f, ws, 0)
+    assert lib.moe_fused_w8a16_ex(*base, 0, 2, None) == binding.MOE_EINVAL
+    assert b"activation" in lib.moe_last_error()
+    # relu^2 prefill tiles take 256 up columns: I = 384 is rejected before any launch
+    ws384 = lib.moe_fused_workspace_bytes(8192, 2048, 384, 256, 8, 0, 2)
+    args = (f, f, f, f, f, f, f, 8192, 2048, 384, 256, 8, None, o, None, f, ws384, 0, 2)
+    assert lib.moe_fused_w8a16_ex(*args, 1, None) == binding.MOE_EUNSUPPORTED
+    assert b"I % 256" in lib.moe_last_error()
 
 
 def test_fused_argument_checks():

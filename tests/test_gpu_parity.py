@@ -31,12 +31,13 @@ def setup_module(module):
 _cases = {}
 
 
-def _case(name):
-    if name not in _cases:
+def _case(name, activation="swiglu"):
+    key = (name, activation)
+    if key not in _cases:
         _cases.clear()
         torch.cuda.empty_cache()
-        _cases[name] = gpu_case(name, seed=1)
-    return _cases[name]
+        _cases[key] = gpu_case(name, seed=1, activation=activation)
+    return _cases[key]
 
 
 # ------------------------------------------------------------------ decode step
@@ -356,6 +357,43 @@ def test_fused_parity(name, variant, layout):
     rows = sample_rows(cfg.T, FFN_SAMPLE[name], seed=2)
     ref = oracle_rows(c, ref_ids, ref_aff, rows)
     assert_out_close(np_(out)[rows], ref, what=f"{name}/{variant}/{layout}")
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("name", synth.CONFIG_ORDER)
+def test_fused_relu2_parity(name, variant, layout):
+    """Non-gated relu^2 experts (up projection alone), end to end."""
+    c = _case(name, "relu2")
+    cfg = c["cfg"]
+    ids, aff = binding.route(c["logits"], cfg.k)
+    if variant == "prefill" and cfg.I % 256:
+        # the prefill tiles take 256 up columns at a time
+        with pytest.raises(binding.MoeError) as ei:
+            _fused(c, ids, aff, variant=variant, layout=layout, activation="relu2")
+        assert ei.value.code == binding.MOE_EUNSUPPORTED
+        return
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = _fused(c, ids, aff, variant=variant, status=status, layout=layout, activation="relu2")
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    ref_ids, ref_aff = oracle.route_softmax_topk(np_(c["logits"]), cfg.k)
+    rows = sample_rows(cfg.T, FFN_SAMPLE[name], seed=3)
+    ref = oracle_rows(c, ref_ids, ref_aff, rows)
+    assert_out_close(np_(out)[rows], ref, what=f"relu2 {name}/{variant}/{layout}")
+
+
+@pytest.mark.parametrize("variant", ["auto"] + VARIANTS)
+@pytest.mark.parametrize("T", [1, 17, 130])
+def test_fused_relu2_token_boundaries_and_shared(T, variant):
+    cfg = synth.MoeConfig("r", T=T, H=512, I=256, E=16, k=4, shared=True)
+    c = gpu_case(cfg, seed=T, activation="relu2")
+    ids, aff = binding.route(c["logits"], cfg.k)
+    out = _fused(c, ids, aff, variant=variant, activation="relu2")
+    torch.cuda.synchronize()
+    ref_ids, ref_aff = oracle.route_softmax_topk(np_(c["logits"]), cfg.k)
+    ref = oracle_rows(c, ref_ids, ref_aff, np.arange(T))
+    assert_out_close(np_(out), ref, what=f"relu2 T={T}/{variant}")
 
 
 @pytest.mark.parametrize("layout", LAYOUTS)

@@ -329,6 +329,65 @@ def test_ffn_single_expert_is_dense_swiglu_mlp():
     np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
 
 
+def _torch_mlp_relu2(x, w1, w1s, w2, w2s):
+    """Dense non-gated MLP, torch CPU fp64: down(relu(up x)^2)."""
+    W1 = _torch_deq(w1, w1s)
+    W2 = _torch_deq(w2, w2s)
+    xx = torch.as_tensor(x, dtype=torch.float64)
+    return torch.nn.functional.relu(xx @ W1.T).square() @ W2.T
+
+
+def test_ffn_relu2_single_expert_and_mixture_are_dense_mlps():
+    cfg = synth.MoeConfig("t", T=7, H=384, I=256, E=3, k=1, shared=True)
+    c = synth.make_case(cfg, 14, activation="relu2")
+    assert tuple(c["w13"].shape) == (3, 256, 384)
+    w = {n: c[n].numpy() for n in ("w13", "w13_scale", "w2", "w2_scale")}
+    sh = {n: c["shared"][n].numpy() for n in ("w13", "w13_scale", "w2", "w2_scale")}
+    x = c["x"].float().numpy()
+    dense = [_torch_mlp_relu2(x, c["w13"][e], c["w13_scale"][e], c["w2"][e], c["w2_scale"][e])
+             for e in range(3)]
+    # one expert, affinity 1
+    got = oracle.moe_ffn(x, w["w13"], w["w13_scale"], w["w2"], w["w2_scale"],
+                         np.full((7, 1), 2, np.int32), np.ones((7, 1)), activation="relu2")
+    ref = dense[2].numpy()
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+    # k = E: the softmax mixture, plus the shared expert's own MLP
+    logits = c["logits"].numpy()
+    ids, aff = oracle.route_softmax_topk(logits, 3)
+    got = oracle.moe_ffn(x, w["w13"], w["w13_scale"], w["w2"], w["w2_scale"], ids, aff, sh,
+                         activation="relu2")
+    p = torch.softmax(torch.as_tensor(logits, dtype=torch.float64), dim=1)
+    ref = (sum(p[:, e:e + 1] * dense[e] for e in range(3)) +
+           _torch_mlp_relu2(x, c["shared"]["w13"], c["shared"]["w13_scale"], c["shared"]["w2"],
+                            c["shared"]["w2_scale"])).numpy()
+    np.testing.assert_allclose(got, ref, rtol=1e-11, atol=1e-12 * np.abs(ref).max())
+
+
+def test_ffn_relu2_closed_form():
+    # Worked by hand.  H = 256, I = 128, one expert.  Up codes 0x38 (1.0) with
+    # block scales 0.5 (rows 0..127, columns 0..127) and 4.0 (columns 128..255);
+    # down codes 0x30 (0.5) with scales 2.0 (rows 0..127) and 0.25 (rows 128..255).
+    #   token 0, x = e_3:     u_i = 0.5, a_i = 0.25, y_h = 128 * 0.25 * w2 =
+    #                         32 (h < 128, w2 = 1) and 4 (h >= 128, w2 = 1/8);
+    #   token 1, x = -e_200:  u_i = -4, a_i = relu(-4)^2 = 0, y = 0 exactly
+    #                         (SwiGLU would not give 0 here);
+    #   token 2, x = 2 e_0 - e_130: u_i = 2*0.5 - 4 = -3 -> 0.
+    H, I = 256, 128
+    w1 = np.full((1, I, H), 0x38, np.uint8)
+    w1s = np.array([[[0.5, 4.0]]], np.float32)
+    w2 = np.full((1, H, I), 0x30, np.uint8)
+    w2s = np.array([[[2.0], [0.25]]], np.float32)
+    x = np.zeros((3, H), np.float32)
+    x[0, 3] = 1.0
+    x[1, 200] = -1.0
+    x[2, 0], x[2, 130] = 2.0, -1.0
+    out = oracle.moe_ffn(x, w1, w1s, w2, w2s, np.zeros((3, 1), np.int32), np.ones((3, 1)),
+                         activation="relu2")
+    assert np.all(out[0, :128] == 32.0) and np.all(out[0, 128:] == 4.0)
+    assert np.all(out[1:] == 0.0)
+    assert oracle.relu2(np.array([-0.0, 0.0, -2.0, 3.0])).tolist() == [0.0, 0.0, 0.0, 9.0]
+
+
 def test_ffn_all_experts_is_softmax_mixture():
     E, T = 4, 5
     c, x, w, _ = _small_case(E=E, T=T, seed=5)
