@@ -395,6 +395,87 @@ def router_variants_bench(cfg, dev, seed=0, calls=64, samples=7, replays=20):
     return out
 
 
+def relu2_bench(cfg, dev, L, seed=0, samples=7, replays=50):
+    """The fused call (sort + expert FFN + expert sum) with non-gated relu^2
+    experts (MOE_ACT_RELU2: up projection [I, H], relu^2, down) on the
+    workload's shapes, `L` weight sets, one call per set captured in a HIP
+    graph, median per call; then per-kernel times from the library's events.
+    Algorithmic work per (route or shared row): 4*H*I flops; weights
+    2*H*I bytes (+ scales) per active expert."""
+    import statistics
+
+    import torch
+
+    from block_scaled_fp8_amd import binding, synth
+    T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
+    log(f"relu^2 experts on {cfg.name}: {L} weight sets")
+    x, logits = synth.make_activations(cfg, seed, dev)
+    runs = []
+    for i in range(L):
+        w = synth.make_weights(cfg, seed + 100 * i, dev, activation="relu2")
+        p = dict(w, w13=binding.pack_w8(w["w13"]), w2=binding.pack_w8(w["w2"]))
+        if w["shared"] is not None:
+            p["shared"] = dict(w["shared"], w13=binding.pack_w8(w["shared"]["w13"]),
+                               w2=binding.pack_w8(w["shared"]["w2"]))
+        del w
+        runs.append(binding.MoeStep(x, logits, k, p["w13"], p["w13_scale"], p["w2"],
+                                    p["w2_scale"], shared=p["shared"], layout="tiled",
+                                    activation="relu2"))
+    ids, _ = binding.route(logits, k)
+    n_active = int((torch.bincount(ids.reshape(-1).long(), minlength=E) > 0).sum().item())
+    for r in runs:
+        r()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for r in runs:
+            r.fused()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for r in runs:
+            r.fused()
+    for _ in range(20):
+        g.replay()
+    torch.cuda.synchronize()
+    per = []
+    for _ in range(samples):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(replays):
+            g.replay()
+        e.record()
+        torch.cuda.synchronize()
+        per.append(s.elapsed_time(e) * 1e3 / (replays * L))
+    del g
+    us = statistics.median(per)
+    binding.profile_enable(True)
+    for i in range(10 * L):
+        runs[i % L].fused()
+    torch.cuda.synchronize()
+    binding.profile_enable(False)
+    prof = binding.profile_collect()
+    rows = T * k + (T if cfg.shared else 0)
+    nseg = n_active + (1 if cfg.shared else 0)
+    flops = 4.0 * H * I * rows
+    wbytes = nseg * (2 * H * I + 4 * (I // 128) * (H // 128) + 4 * (H // 128) * (I // 128))
+    nbytes = wbytes + 2 * T * H + 4 * T * H + 8 * T * k
+    out = {"workload": cfg.name, "activation": "relu2", "active_experts": n_active,
+           "weight_sets": L,
+           "protocol": f"HIP graph of one fused call per weight set, median of {samples} x "
+                       f"{replays} replays",
+           "us_per_call": round(us, 2), "tokens_per_s": round(T / (us * 1e-6), 1),
+           "GB_per_s": round(nbytes / (us * 1e-6) / 1e9, 1),
+           "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+           "TFLOP_per_s": round(flops / (us * 1e-6) / 1e12, 1),
+           "mfma_frac": round(flops / (us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4),
+           "kernels": {n: {"launches": c, "avg_us": round(ms * 1e3, 3)} for n, (c, ms) in prof.items()}}
+    log(f"  {us:.1f} us per call; " + ", ".join(f"{n} {ms * 1e3:.1f} us" for n, (c, ms) in prof.items()))
+    del runs, x, logits
+    torch.cuda.empty_cache()
+    return out
+
+
 def prefill_summary(cfg, m):
     """MFMA roofline of the prefill workload (secondary object of the JSON line)."""
     R = cfg.T * cfg.k + (cfg.T if cfg.shared else 0)
@@ -442,6 +523,8 @@ def main():
                     help="untimed prefill steps first: the GPU idles while the prefill inputs "
                          "are generated, and its clock needs some milliseconds of work to settle")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-relu2", action="store_true",
+                    help="skip the relu^2-expert measurement (MOE_ACT_RELU2)")
     ap.add_argument("--no-route-proj", action="store_true",
                     help="skip the router measurements (moe_route_proj, router variants)")
     ap.add_argument("--no-vendor-gemm", action="store_true",
@@ -537,6 +620,11 @@ def main():
         if not args.no_vendor_gemm:
             log("vendor bf16 GEMM at the gate/up shape (context) ...")
             result["prefill"]["vendor_bf16_gemm"] = vendor_gemm(pcfg, dev)
+    if not args.no_relu2:
+        result["relu2"] = [relu2_bench(cfg, dev, max(1, args.weight_sets), args.seed)]
+        if args.prefill_workload:
+            result["relu2"].append(relu2_bench(synth.CONFIGS[args.prefill_workload], dev, 2,
+                                               args.seed))
     if not args.no_route_proj:
         result["router_variants"] = [router_variants_bench(cfg, dev, args.seed)]
         if args.prefill_workload:
