@@ -20,7 +20,7 @@ MOE_STATUS_BAD_EXPERT_ID = 1
 MOE_STATUS_NONFINITE_LOGIT = 2
 MOE_MAX_EXPERTS = 1024
 MOE_MAX_TOPK = 16
-VARIANTS = {"auto": 0, "decode": 1, "prefill": 2}
+VARIANTS = {"auto": 0, "decode": 1, "prefill": 2, "prefill_a8": 3}
 ACTIVATIONS = {"swiglu": 0, "relu2": 1}
 LAYOUTS = {"rowmajor": 0, "tiled": 1}
 
@@ -28,7 +28,8 @@ EXPORTED = (
     "moe_last_error", "moe_route", "moe_route_sigmoid", "moe_route_proj_workspace_bytes",
     "moe_route_proj",
     "moe_sort_workspace_bytes", "moe_sort",
-    "moe_fused_workspace_bytes", "moe_fused_w8a16", "moe_fused_w8a16_ex", "moe_decode_e4m3fn",
+    "moe_fused_workspace_bytes", "moe_fused_w8a16", "moe_fused_w8a16_ex", "moe_quant_e4m3_rows",
+    "moe_decode_e4m3fn",
     "moe_pack_w8",
     "moe_profile_enable", "moe_profile_collect", "moe_profile_count", "moe_profile_stat",
 )
@@ -86,6 +87,8 @@ def load_library():
     lib.moe_fused_w8a16_ex.argtypes = list(lib.moe_fused_w8a16.argtypes[:-1]) + [i32, vp]
     lib.moe_pack_w8.restype = i32
     lib.moe_pack_w8.argtypes = [vp, vp, i64, i32, i32, vp]
+    lib.moe_quant_e4m3_rows.restype = i32
+    lib.moe_quant_e4m3_rows.argtypes = [vp, i32, i32, vp, vp, vp]
     lib.moe_decode_e4m3fn.restype = i32
     lib.moe_decode_e4m3fn.argtypes = [vp, vp, i64, vp]
     lib.moe_profile_enable.restype = i32
@@ -292,6 +295,17 @@ def fused_w8a16(x, w13, w13_scale, w2, w2_scale, ids, aff, shared=None, out=None
                                   _ptr(out), _ptr(status), _ptr(ws), ws.numel(), _layout(layout),
                                   v, act, _stream(dev)))
     return out
+
+
+def quant_e4m3_rows(x: torch.Tensor):
+    """Per-token E4M3 quantisation: x [T, H] bf16 -> (codes [T, H] uint8, scales [T] fp32)."""
+    lib = load_library()
+    _need(x, "x", torch.bfloat16)
+    T, H = x.shape
+    codes = torch.empty((T, H), dtype=torch.uint8, device=x.device)
+    scales = torch.empty(T, dtype=torch.float32, device=x.device)
+    _check(lib.moe_quant_e4m3_rows(_ptr(x), T, H, _ptr(codes), _ptr(scales), _stream(x.device)))
+    return codes, scales
 
 
 def decode_e4m3fn(codes: torch.Tensor) -> torch.Tensor:

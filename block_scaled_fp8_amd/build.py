@@ -26,6 +26,9 @@ HIPCC_FLAGS = [
     "--offload-arch=gfx950",
     "-mcode-object-version=5",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # fp32 division correctly rounded (the activation quantiser's quotient
+    # must be the IEEE one); this is HIP's default, stated explicitly
+    "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-Wall", "-Wno-unused-result", "-Wno-unused-function",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]

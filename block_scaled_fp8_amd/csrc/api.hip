@@ -35,10 +35,12 @@ int check_launch(const char* what) {
 // Workspace carve-up for moe_fused_w8a16 (256-byte aligned pieces).
 struct FusedLayout {
     size_t counts, offsets, sorted_route, inv_route, seg_n, seg_expert, seg_row0, seg_rows,
-        seg_tile0, tile_info, tile_n, sort_scratch, abuf, ybuf, total;
+        seg_tile0, tile_info, tile_n, sort_scratch, abuf, ybuf, xq, xs, total;
 };
 
-static FusedLayout fused_layout(int T, int H, int I, int E, int k, int has_shared) {
+// (fp8 activations: the E4M3 codes and per-token scales of x are appended)
+static FusedLayout fused_layout(int T, int H, int I, int E, int k, int has_shared,
+                                bool fp8_x = false) {
     FusedLayout L;
     const size_t R = (size_t)T * k;
     const size_t rows = R + (has_shared ? (size_t)T : 0);
@@ -65,6 +67,8 @@ static FusedLayout fused_layout(int T, int H, int I, int E, int k, int has_share
     L.sort_scratch = take(sort_scratch_bytes((int)R, E));
     L.abuf = take(sizeof(uint16_t) * rows * I);
     L.ybuf = take(sizeof(float) * (rows + 1) * H);  // + one trash row for padded stores
+    L.xq = fp8_x ? take((size_t)T * H) : 0;
+    L.xs = fp8_x ? take(sizeof(float) * (size_t)T) : 0;
     L.total = o;
     return L;
 }
@@ -202,9 +206,8 @@ int moe_sort(const int32_t* ids, int T, int k, int E, int32_t* counts, int32_t* 
 
 size_t moe_fused_workspace_bytes(int T, int H, int I, int E, int k, int has_shared,
                                  int variant) {
-    (void)variant;
     if (T < 0 || H < 1 || I < 1 || E < 1 || k < 1) return 0;
-    return fused_layout(T, H, I, E, k, has_shared ? 1 : 0).total;
+    return fused_layout(T, H, I, E, k, has_shared ? 1 : 0, variant == MOE_VARIANT_PREFILL_A8).total;
 }
 
 int moe_fused_w8a16_ex(const void* x, const uint8_t* w13, const float* w13_scale,
@@ -232,7 +235,7 @@ int moe_fused_w8a16_ex(const void* x, const uint8_t* w13, const float* w13_scale
         set_error("unknown weight layout %d", weight_layout);
         return MOE_EINVAL;
     }
-    if (variant < MOE_VARIANT_AUTO || variant > MOE_VARIANT_PREFILL) {
+    if (variant < MOE_VARIANT_AUTO || variant > MOE_VARIANT_PREFILL_A8) {
         set_error("unknown variant %d", variant);
         return MOE_EINVAL;
     }
@@ -250,7 +253,8 @@ int moe_fused_w8a16_ex(const void* x, const uint8_t* w13, const float* w13_scale
         return MOE_EINVAL;
     }
     const int has_shared = shared ? 1 : 0;
-    const FusedLayout L = fused_layout(T, H, I, E, k, has_shared);
+    const bool fp8_x = variant == MOE_VARIANT_PREFILL_A8;
+    const FusedLayout L = fused_layout(T, H, I, E, k, has_shared, fp8_x);
     if (!ws || ws_bytes < L.total) {
         set_error("moe_fused_w8a16: workspace of %zu bytes needed (got %zu)", L.total, ws_bytes);
         return MOE_EINVAL;
@@ -266,7 +270,7 @@ int moe_fused_w8a16_ex(const void* x, const uint8_t* w13, const float* w13_scale
                       ? MOE_VARIANT_DECODE
                       : MOE_VARIANT_PREFILL;
     }
-    if (variant == MOE_VARIANT_PREFILL) {
+    if (variant == MOE_VARIANT_PREFILL || fp8_x) {
         if (int rc = prefill_check(T, H, I, E, k, has_shared, act)) return rc;
     }
 
@@ -281,8 +285,9 @@ int moe_fused_w8a16_ex(const void* x, const uint8_t* w13, const float* w13_scale
     p.seg_row0 = reinterpret_cast<int32_t*>(base + L.seg_row0);
     p.seg_rows = reinterpret_cast<int32_t*>(base + L.seg_rows);
     p.seg_tile0 = reinterpret_cast<int32_t*>(base + L.seg_tile0);
-    p.tile_info = variant == MOE_VARIANT_PREFILL ? reinterpret_cast<int4*>(base + L.tile_info) : nullptr;
-    p.tile_n = variant == MOE_VARIANT_PREFILL ? reinterpret_cast<int32_t*>(base + L.tile_n) : nullptr;
+    const bool pf = variant == MOE_VARIANT_PREFILL || fp8_x;
+    p.tile_info = pf ? reinterpret_cast<int4*>(base + L.tile_info) : nullptr;
+    p.tile_n = pf ? reinterpret_cast<int32_t*>(base + L.tile_n) : nullptr;
     uint16_t* abuf = reinterpret_cast<uint16_t*>(base + L.abuf);
     float* ybuf = reinterpret_cast<float*>(base + L.ybuf);
     hipStream_t s = (hipStream_t)stream;
@@ -297,18 +302,22 @@ int moe_fused_w8a16_ex(const void* x, const uint8_t* w13, const float* w13_scale
         rc = launch_decode_fused_self(weight_layout, decode_mt(T, k, E), xb, w13, w13_scale, w2,
                                       w2_scale, sh, ids, aff, T, H, I, E, k, ybuf, act, s);
     } else {
-        const int tile_m = variant == MOE_VARIANT_PREFILL ? prefill_tile_m() : 1;
+        const int tile_m = pf ? prefill_tile_m() : 1;
         if ((rc = launch_sort(ids, T, k, E, p, has_shared, tile_m, status, base + L.sort_scratch, s)))
             return rc;
         if (variant == MOE_VARIANT_DECODE)
             rc = launch_decode_ffn(weight_layout, xb, w13, w13_scale, w2, w2_scale, sh, p, aff, T,
                                    H, I, E, k, abuf, ybuf, act, s);
-        else
+        else {
+            uint8_t* xq = fp8_x ? reinterpret_cast<uint8_t*>(base + L.xq) : nullptr;
+            float* xsc = fp8_x ? reinterpret_cast<float*>(base + L.xs) : nullptr;
+            if (fp8_x && (rc = launch_quant_rows_e4m3(xb, T, H, xq, xsc, s))) return rc;
             rc = launch_prefill_ffn(weight_layout, xb, w13, w13_scale, w2, w2_scale, sh, p, T, H,
-                                    I, E, k, abuf, ybuf, act, s);
+                                    I, E, k, abuf, ybuf, act, xq, xsc, s);
+        }
     }
     if (rc) return rc;
-    const bool gathered = variant == MOE_VARIANT_PREFILL;
+    const bool gathered = pf;
     return launch_combine(ybuf, ids, gathered ? p.inv_route : nullptr,
                           gathered ? aff : nullptr, T, H, k, E,
                           has_shared, status, out, s);
@@ -345,6 +354,26 @@ int moe_pack_w8(const uint8_t* src, uint8_t* dst, int64_t n_mats, int rows, int 
         return MOE_EINVAL;
     }
     return launch_pack_w8(src, dst, n_mats, rows, cols, (hipStream_t)stream);
+}
+
+int moe_quant_e4m3_rows(const void* x, int T, int H, uint8_t* codes, float* scales,
+                        void* stream) {
+    g_err[0] = 0;
+    if (T < 0 || H < 8 || H % 8) {
+        set_error("moe_quant_e4m3_rows: need T >= 0 and H a positive multiple of 8 (got %d, %d)", T, H);
+        return MOE_EINVAL;
+    }
+    if (T == 0) return MOE_OK;
+    if (!x || !codes || !scales) {
+        set_error("moe_quant_e4m3_rows: x, codes and scales must be non-NULL");
+        return MOE_EINVAL;
+    }
+    if ((uintptr_t)x & 15 || (uintptr_t)codes & 7) {
+        set_error("moe_quant_e4m3_rows: x must be 16-byte and codes 8-byte aligned");
+        return MOE_EINVAL;
+    }
+    return launch_quant_rows_e4m3(static_cast<const uint16_t*>(x), T, H, codes, scales,
+                                  (hipStream_t)stream);
 }
 
 int moe_decode_e4m3fn(const uint8_t* codes, uint16_t* out, int64_t n, void* stream) {

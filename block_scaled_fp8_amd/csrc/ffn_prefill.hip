@@ -63,17 +63,21 @@ constexpr int PF_XCD_RUN = 8;  // consecutive row tiles an XCD takes at a time
 // Workgroup tile BM rows x BN columns, WM x WN waves of 64 x 128 each (2 x 4
 // MFMA tiles of 32 x 32), STAGES LDS stages of 64-wide K, OCC workgroups per
 // CU (the register budget follows from it).
-template <int BM_, int BN_, int WM_, int WN_, int STAGES_, int OCC_, int M16_ = 0>
+template <int BM_, int BN_, int WM_, int WN_, int STAGES_, int OCC_, int M16_ = 0, int A8_ = 0>
 struct PfCfg {
     static constexpr int OCC = OCC_;
-    // MFMA shape: v_mfma_f32_16x16x32_bf16 (M16) or v_mfma_f32_32x32x16_bf16
+    // MFMA shape: v_mfma_f32_16x16x32_bf16 (M16) or v_mfma_f32_32x32x16_bf16;
+    // A8: the activation operand is E4M3 (per-token scale) and the product
+    // runs on v_mfma_scale_f32_32x32x64_f8f6f4 with unit scales, fp8 x fp8
     static constexpr bool M16 = M16_ != 0;
+    static constexpr bool A8 = A8_ != 0;
+    static_assert(!(M16 && A8), "the fp8 path uses 32x32 tiles");
     static constexpr int MS = M16 ? 16 : 32;  // rows = columns of one MFMA tile
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
     static constexpr int THREADS = WM * WN * MOE_WAVE;
     static constexpr int WAVES = WM * WN;
     static constexpr int STAGES = STAGES_;
-    static constexpr int A_BYTES = BM * PF_BK * 2;  // bf16
+    static constexpr int A_BYTES = BM * PF_BK * (A8 ? 1 : 2);  // bf16 or E4M3
     static constexpr int B_BYTES = BN * PF_BK;      // fp8
     static constexpr int STAGE = A_BYTES + B_BYTES;
     static constexpr int A_INSTR = A_BYTES / 1024 / WAVES;  // 1 KB loads per wave per stage
@@ -101,6 +105,7 @@ struct PfCfg {
 // faster there.
 using PfGateUp = PfCfg<128, 256, 2, 2, 2, 2, 1>;
 using PfDown = PfCfg<128, 256, 2, 2, 2, 2, 0>;
+using PfGateUpA8 = PfCfg<128, 256, 2, 2, 2, 2, 0, 1>;
 constexpr int PF_BM = 128;
 
 int prefill_tile_m() { return PF_BM; }
@@ -127,6 +132,14 @@ __device__ __forceinline__ float swiglu_fast(float g, float u) {
 
 __device__ __forceinline__ float uniform_f32(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
+}
+
+// Two 16-byte operand pieces as the 32-byte register operand of the fp8 MFMA.
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x8 cat_i32x8(u32x4 a, u32x4 b) {
+    const i32x4v ai = __builtin_bit_cast(i32x4v, a), bi = __builtin_bit_cast(i32x4v, b);
+    return __builtin_shufflevector(ai, bi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 __device__ __forceinline__ void lds_load16(const void* g, uint32_t lds_byte_addr_uniform, void* lds_base) {
@@ -160,11 +173,12 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
     const uint8_t* __restrict__ wexp, const float* __restrict__ sexp,
     const uint8_t* __restrict__ wsh, const float* __restrict__ ssh, Plan plan,
     int T, int H, int I, int k, int nblk, int max_tiles,
-    uint16_t* __restrict__ abuf_out, float* __restrict__ ybuf) {
+    uint16_t* __restrict__ abuf_out, float* __restrict__ ybuf, const float* __restrict__ xscale) {
     constexpr int BM = C::BM, BN = C::BN;
     extern __shared__ __attribute__((aligned(16))) char smem[];
     __shared__ int row_tok[BM];  // gate/up: token row of x
     __shared__ __attribute__((aligned(16))) int row_dst[BM];  // gate/up: output row, -1 if padding
+    __shared__ __attribute__((aligned(16))) float row_xs[C::A8 ? BM : 1];  // A8: the row's x scale
 
     // ---- which tile.  Workgroups are dealt round-robin over the 8 XCDs
     //      (id % 8).  The sort's tile list is cut into blocks of PF_XCD_RUN
@@ -210,6 +224,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
             const bool valid = tid < rows_here;
             row_tok[tid] = valid ? (e >= 0 ? plan.sorted_route[p] / k : p - R) : 0;
             row_dst[tid] = valid ? p : -1;
+            if constexpr (C::A8) row_xs[tid] = valid ? xscale[row_tok[tid]] : 0.0f;
         }
         __syncthreads();
     }
@@ -219,17 +234,21 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
     // 128 B each; the lane's source is a 32-bit byte offset from the matrix
     // (the launcher checks that the matrix is under 4 GB), so the loads
     // address through a scalar base
-    const int ar_sub = lane >> 3, apiece = lane & 7;
+    // (A8: E4M3 rows of 64 bytes per stage, 16 rows per instruction, pieces
+    //  swizzled by (row / 4) % 4 so that the MFMA reads of 8 rows fall on
+    //  distinct banks)
+    constexpr int APR = C::A8 ? 4 : 8;  // 16-byte pieces per row per stage
+    const int ar_sub = lane / APR, apiece = lane % APR;
     const char* abase = GATHER ? reinterpret_cast<const char*>(x)
                                : reinterpret_cast<const char*>(abuf_in);
     uint32_t asrc[C::A_INSTR];
 #pragma unroll
     for (int q = 0; q < C::A_INSTR; ++q) {
-        const int row = (wave * C::A_INSTR + q) * 8 + ar_sub;
-        const int sw = apiece ^ ((row >> 1) & 7);  // swizzled piece this lane fetches
+        const int row = (wave * C::A_INSTR + q) * (64 / APR) + ar_sub;
+        const int sw = C::A8 ? apiece ^ ((row >> 2) & 3) : apiece ^ ((row >> 1) & 7);
         const uint32_t src_row = GATHER ? (uint32_t)row_tok[row]
                                         : (uint32_t)(p0 + (row < rows_here ? row : 0));
-        asrc[q] = src_row * (uint32_t)(2 * (GATHER ? H : I)) + sw * 16;
+        asrc[q] = src_row * (uint32_t)((C::A8 ? 1 : 2) * (GATHER ? H : I)) + sw * 16;
     }
     // weights: instruction q of wave w fills 16-row tile w*B_INSTR + q
     constexpr int HALF_T = BN / 2 / 16;  // gate tiles in a gate/up tile (MODE 0)
@@ -253,7 +272,8 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
         const uint32_t sbase = st * C::STAGE;
 #pragma unroll
         for (int q = 0; q < C::A_INSTR; ++q)
-            lds_load16(abase + (asrc[q] + (uint32_t)kc * (PF_BK * 2)), sbase + (wave * C::A_INSTR + q) * 1024, smem);
+            lds_load16(abase + (asrc[q] + (uint32_t)kc * (PF_BK * (C::A8 ? 1 : 2))),
+                       sbase + (wave * C::A_INSTR + q) * 1024, smem);
 #pragma unroll
         for (int q = 0; q < C::B_INSTR; ++q)
             lds_load16(bbase[q] + (size_t)kc * CS + blane, sbase + C::A_BYTES + (wave * C::B_INSTR + q) * 1024,
@@ -494,7 +514,82 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
         __builtin_amdgcn_sched_barrier(0);
     }
     };
-    if constexpr (C::MT == 4) {
+    if constexpr (C::A8) {
+        // ---- A8 K loop: one v_mfma_scale_f32_32x32x64_f8f6f4 per tile per stage
+        //      (unit scales).  Lane l feeds row (or weight row) l % 32 of a 32-row
+        //      tile with bytes [32 h, 32 h + 32) of the stage's 64 K, h = l / 32,
+        //      for both operands alike, so each product sums exactly over K.  The
+        //      weight operand's pieces sit where the 32x32 bf16 path reads them
+        //      (b_off, b_step); the activation rows are 64 bytes.
+        auto kloop_a8 = [&](auto mta_c) {
+            constexpr int MTA = decltype(mta_c)::value;
+            const int r32 = lane & 31, h8 = lane >> 5;
+            uint32_t a8_off[2];
+    #pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int row = wm * C::WROWS + r32;
+                a8_off[j] = row * 64 + (((2 * h8 + j) ^ ((row >> 2) & 3)) * 16);
+            }
+            auto stage_mma = [&](int stage, bool rescale, const float (&rr)[2]) {
+                const char* st = smem + stage * C::STAGE;
+                i32x8 av[C::MT], bv[C::NT];
+    #pragma unroll
+                for (int mt = 0; mt < MTA; ++mt)
+                    av[mt] = cat_i32x8(*reinterpret_cast<const u32x4*>(st + a8_off[0] + mt * 32 * 64),
+                                       *reinterpret_cast<const u32x4*>(st + a8_off[1] + mt * 32 * 64));
+                if (MTA > 0)
+    #pragma unroll
+                    for (int nt = 0; nt < C::NT; ++nt)
+                        bv[nt] = cat_i32x8(*reinterpret_cast<const u32x4*>(st + b_off + b_step(nt)),
+                                           *reinterpret_cast<const u32x4*>(st + b_off + b_step(nt) + 256));
+    #pragma unroll
+                for (int nt = 0; nt < C::NT; ++nt) {
+                    const float f = PAIRED ? rr[nt / (C::NT / 2)] : rr[0];
+    #pragma unroll
+                    for (int mt = 0; mt < MTA; ++mt) {
+                        if (rescale)
+    #pragma unroll
+                            for (int i = 0; i < AR; ++i) acc[mt][nt][i] *= f;
+                        acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                            av[mt], bv[nt], acc[mt][nt], 0, 0, 0, 127, 0, 127);
+                    }
+                }
+            };
+            auto next_stage = [&](int kc) {
+                wait_vmcnt<0>();             // stage kc + 1 landed in this wave
+                barrier_after_lds_reads();   // ... in every wave; stage kc read by every wave
+                if (kc + C::STAGES < nk) issue_stage(kc % C::STAGES, kc + C::STAGES);
+            };
+    #pragma unroll
+            for (int st = 0; st < C::STAGES; ++st)
+                if (st < nk) issue_stage(st, st);
+            wait_vmcnt<(C::STAGES - 1) * PER_STAGE>();
+            barrier_after_lds_reads();  // stage 0 and the scale table landed in every wave
+            float snext[2] = {sc_tab[sj[0] * kbp], sc_tab[sj[1] * kbp]};
+            const float one[2] = {1.0f, 1.0f};
+            for (int kb = 0; kb < kblocks; ++kb) {
+                const int kc = 2 * kb;
+                float rr[2];
+    #pragma unroll
+                for (int g = 0; g < 2; ++g) {
+                    const float sn = snext[g];
+                    const bool take = sn != 0.0f;
+                    rr[g] = uniform_f32(take && seff[g] != 0.0f ? seff[g] * __builtin_amdgcn_rcpf(sn) : 1.0f);
+                    seff[g] = uniform_f32(take ? sn : seff[g]);
+                }
+                const int kn = kb + 1 < kblocks ? kb + 1 : kb;
+                snext[0] = sc_tab[sj[0] * kbp + kn];
+                snext[1] = sc_tab[sj[1] * kbp + kn];
+                stage_mma(kc % C::STAGES, true, rr);
+                next_stage(kc);
+                stage_mma((kc + 1) % C::STAGES, false, one);
+                next_stage(kc + 1);
+            }
+        };
+        if (mt_active >= 2) kloop_a8(std::integral_constant<int, 2>{});
+        else if (mt_active == 1) kloop_a8(std::integral_constant<int, 1>{});
+        else kloop_a8(std::integral_constant<int, 0>{});
+    } else if constexpr (C::MT == 4) {
         // three active groups run the full loop (cheaper than another copy)
         if (mt_active >= 3) kloop(std::integral_constant<int, 4>{});
         else if (mt_active == 2) kloop(std::integral_constant<int, 2>{});
@@ -516,11 +611,13 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
     constexpr int RQ = AR / 4;                   // groups of four rows per MFMA tile
     const int ocol = C::M16 ? l16 : ln;          // the lane's column in a tile
     int4 dst4[C::MT][RQ];
+    float4 xs4[C::A8 ? C::MT : 1][C::A8 ? RQ : 1];  // A8: the x scales of those rows
 #pragma unroll
     for (int mt = 0; mt < C::MT; ++mt)
 #pragma unroll
         for (int q = 0; q < RQ; ++q) {
             const int r0 = wm * C::WROWS + mt * C::MS + (C::M16 ? 4 * g16 : 8 * q + 4 * lg);
+            if constexpr (C::A8) xs4[mt][q] = *reinterpret_cast<const float4*>(row_xs + r0);
             if (GATHER) {
                 dst4[mt][q] = *reinterpret_cast<const int4*>(row_dst + r0);
             } else {
@@ -534,17 +631,22 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
         for (int i = 0; i < AR; ++i) {
             const int dst = dst4[mt][i >> 2][i & 3];
             if (dst < 0) continue;
+            // A8: the row's activation scale joins the weight block's
+            float xsv = 1.0f;
+            if constexpr (C::A8) xsv = xs4[mt][i >> 2][i & 3];
             if (MODE == PF_GATEUP) {
                 uint16_t* orow = abuf_out + (size_t)dst * I + nb * (BN / 2) + wn * (C::WCOLS / 2) + ocol;
+                const float s0 = seff[0] * xsv, s1 = seff[1] * xsv;
 #pragma unroll
                 for (int nt = 0; nt < C::NT / 2; ++nt)
                     orow[nt * C::MS] = f32_to_bf16_bits(
-                        swiglu_fast(acc[mt][nt][i] * seff[0], acc[mt][nt + C::NT / 2][i] * seff[1]));
+                        swiglu_fast(acc[mt][nt][i] * s0, acc[mt][nt + C::NT / 2][i] * s1));
             } else if (MODE == PF_UP) {
                 uint16_t* orow = abuf_out + (size_t)dst * I + nb * BN + wn * C::WCOLS + ocol;
+                const float s0 = seff[0] * xsv;
 #pragma unroll
                 for (int nt = 0; nt < C::NT; ++nt)
-                    orow[nt * C::MS] = f32_to_bf16_bits(relu2(acc[mt][nt][i] * seff[0]));
+                    orow[nt * C::MS] = f32_to_bf16_bits(relu2(acc[mt][nt][i] * s0));
             } else {
                 // y of the route (the combine multiplies it by the affinity);
                 // each contribution row is read once, by the combine: streaming
@@ -564,7 +666,7 @@ template <int MODE, int LAYOUT, class C>
 static int launch_pf(const uint16_t* x, const uint16_t* abuf_in, const uint8_t* wexp,
                      const float* sexp, const uint8_t* wsh, const float* ssh, const Plan& plan,
                      int T, int H, int I, int E, int k, int has_shared, uint16_t* abuf_out,
-                     float* ybuf, hipStream_t stream) {
+                     float* ybuf, hipStream_t stream, const float* xscale = nullptr) {
     const int nblk = MODE == PF_GATEUP ? 2 * I / C::BN : (MODE == PF_UP ? I : H) / C::BN;
     const long R = (long)T * k;
     const long max_tiles = (R + C::BM - 1) / C::BM + E + (has_shared ? (T + C::BM - 1) / C::BM : 0);
@@ -576,17 +678,21 @@ static int launch_pf(const uint16_t* x, const uint16_t* abuf_in, const uint8_t* 
         return MOE_EUNSUPPORTED;
     }
     // activation rows are addressed by 32-bit byte offsets
-    const size_t a_bytes = MODE != PF_DOWN ? (size_t)T * H * 2 : (size_t)(R + (has_shared ? T : 0)) * I * 2;
+    const size_t a_bytes = MODE != PF_DOWN ? (size_t)T * H * (C::A8 ? 1 : 2)
+                                           : (size_t)(R + (has_shared ? T : 0)) * I * 2;
     if (a_bytes > 0xFFFFFFFFull) {
         set_error("prefill: activation matrix over 4 GB");
         return MOE_EUNSUPPORTED;
     }
     const size_t kbp = ((size_t)K_of<MODE>(H, I) / 128 + 63) / 64 * 64;
     const size_t lds = (size_t)C::STAGES * C::STAGE + (size_t)(C::BN / 128) * kbp * 4;
-    prof_begin(MODE == PF_GATEUP ? "prefill_gateup_swiglu" : (MODE == PF_UP ? "prefill_up_relu2" : "prefill_down"),
-               stream);
+    const char* pname = MODE == PF_DOWN ? "prefill_down"
+                        : MODE == PF_UP ? (C::A8 ? "prefill_up_relu2_a8" : "prefill_up_relu2")
+                                        : (C::A8 ? "prefill_gateup_swiglu_a8" : "prefill_gateup_swiglu");
+    prof_begin(pname, stream);
     prefill_gemm_kernel<MODE, LAYOUT, C><<<(unsigned)grid, C::THREADS, lds, stream>>>(
-        x, abuf_in, wexp, sexp, wsh, ssh, plan, T, H, I, k, nblk, (int)max_tiles, abuf_out, ybuf);
+        x, abuf_in, wexp, sexp, wsh, ssh, plan, T, H, I, k, nblk, (int)max_tiles, abuf_out, ybuf,
+        xscale);
     prof_end(stream);
     return check_launch(MODE == PF_GATEUP ? "prefill_gemm_kernel<gateup>"
                                           : (MODE == PF_UP ? "prefill_gemm_kernel<up>" : "prefill_gemm_kernel<down>"));
@@ -596,14 +702,27 @@ template <int LAYOUT>
 static int launch_prefill_c(const uint16_t* x, const uint8_t* w13, const float* w13s,
                             const uint8_t* w2, const float* w2s, const SharedW& sh,
                             const Plan& plan, int T, int H, int I, int E, int k, uint16_t* abuf,
-                            float* ybuf, int act, hipStream_t stream) {
+                            float* ybuf, int act, const uint8_t* xq, const float* xs,
+                            hipStream_t stream) {
     const int hs = sh.w13 != nullptr;
-    int rc = act == ACT_RELU2
+    int rc;
+    if (xq) {  // E4M3 activations with per-token scales: the fp8 x fp8 MFMA
+        const uint16_t* xa = reinterpret_cast<const uint16_t*>(xq);
+        rc = act == ACT_RELU2
+                 ? launch_pf<PF_UP, LAYOUT, PfGateUpA8>(xa, nullptr, w13, w13s, sh.w13,
+                                                        sh.w13_scale, plan, T, H, I, E, k, hs,
+                                                        abuf, ybuf, stream, xs)
+                 : launch_pf<PF_GATEUP, LAYOUT, PfGateUpA8>(xa, nullptr, w13, w13s, sh.w13,
+                                                            sh.w13_scale, plan, T, H, I, E, k, hs,
+                                                            abuf, ybuf, stream, xs);
+    } else {
+        rc = act == ACT_RELU2
                  ? launch_pf<PF_UP, LAYOUT, PfGateUp>(x, nullptr, w13, w13s, sh.w13, sh.w13_scale,
                                                       plan, T, H, I, E, k, hs, abuf, ybuf, stream)
                  : launch_pf<PF_GATEUP, LAYOUT, PfGateUp>(x, nullptr, w13, w13s, sh.w13,
                                                           sh.w13_scale, plan, T, H, I, E, k, hs,
                                                           abuf, ybuf, stream);
+    }
     if (rc == MOE_OK)
         rc = launch_pf<PF_DOWN, LAYOUT, PfDown>(x, abuf, w2, w2s, sh.w2, sh.w2_scale, plan, T, H, I,
                                                 E, k, hs, abuf, ybuf, stream);
@@ -634,7 +753,7 @@ int prefill_check(int T, int H, int I, int E, int k, int has_shared, int act) {
 int launch_prefill_ffn(int layout, const uint16_t* x, const uint8_t* w13, const float* w13s,
                        const uint8_t* w2, const float* w2s, const SharedW& sh, const Plan& plan,
                        int T, int H, int I, int E, int k, uint16_t* abuf, float* ybuf,
-                       int act, hipStream_t stream) {
+                       int act, const uint8_t* xq, const float* xs, hipStream_t stream) {
     if (!prefill_supported(H, I, act)) {
         set_error("prefill variant needs H %% 256 == 0, %s %% 256 == 0 and H, I <= 65536 (got H=%d, I=%d)",
                   act == ACT_RELU2 ? "I" : "2I", H, I);
@@ -646,9 +765,9 @@ int launch_prefill_ffn(int layout, const uint16_t* x, const uint8_t* w13, const 
     }
     if (layout == LAYOUT_TILED)
         return launch_prefill_c<LAYOUT_TILED>(x, w13, w13s, w2, w2s, sh, plan, T, H, I, E, k, abuf,
-                                              ybuf, act, stream);
+                                              ybuf, act, xq, xs, stream);
     return launch_prefill_c<LAYOUT_ROWMAJOR>(x, w13, w13s, w2, w2s, sh, plan, T, H, I, E, k, abuf,
-                                             ybuf, act, stream);
+                                             ybuf, act, xq, xs, stream);
 }
 
 }  // namespace moe

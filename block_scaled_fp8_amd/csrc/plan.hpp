@@ -72,7 +72,10 @@ int launch_decode_ffn(int layout, const uint16_t* x, const uint8_t* w13, const f
 int launch_prefill_ffn(int layout, const uint16_t* x, const uint8_t* w13, const float* w13s,
                        const uint8_t* w2, const float* w2s, const SharedW& sh, const Plan& plan,
                        int T, int H, int I, int E, int k, uint16_t* abuf, float* ybuf, int act,
-                       hipStream_t stream);
+                       const uint8_t* xq, const float* xs, hipStream_t stream);
+// Per-token E4M3 quantisation of x [T, H] bf16 -> codes [T, H], scales [T] (quant.hip).
+int launch_quant_rows_e4m3(const uint16_t* x, int T, int H, uint8_t* xq, float* xs,
+                           hipStream_t stream);
 int launch_pack_w8(const uint8_t* src, uint8_t* dst, int64_t n_mats, int rows, int cols,
                    hipStream_t stream);
 int prefill_tile_m();

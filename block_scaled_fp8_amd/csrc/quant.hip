@@ -1,0 +1,86 @@
+// Per-token E4M3 quantisation of the activations, for the prefill gate/up
+// GEMM on the FP8 MFMA (the "second precision": FP8 weights and FP8
+// activations).  Source for the format: "Gated DeltaNet (+ FP8 MoE) -- AWS
+// Neuron (NKI) kernels for Trainium2", section "FP8 MoE decode kernel": the
+// official E4M3FN format with a scale of the block maximum over 448 (the
+// weights' recipe); here one scale per token row of x.
+//
+// Row t:  s = amax_h |x[t][h]| / 448            (fp32, correctly rounded)
+//         code[h] = E4M3FN_RNE(min(max(x / s, -448), 448))   (fp32 quotient)
+// A row of zeros gets s = 0 and all-zero codes.  The encoder is written from
+// the format: below the smallest normal 2^-6 the step is 2^-9 (subnormals),
+// above it 2^(E-3) with E the fp32 exponent; both round half to even, and a
+// carry out of the 3-bit mantissa moves into the exponent field.
+#include "common.hpp"
+#include "plan.hpp"
+
+namespace moe {
+
+__device__ __forceinline__ uint32_t e4m3fn_encode_rne(float v) {
+    v = fminf(fmaxf(v, -448.0f), 448.0f);
+    const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+    const float a = fabsf(v);
+    uint32_t code;
+    if (a < 0.015625f) {
+        code = (uint32_t)rintf(a * 512.0f);  // 0..8; 8 is the smallest normal (0x08)
+    } else {
+        const int E = (int)((__float_as_uint(a) >> 23) & 0xFFu) - 127;  // -6..8
+        const float m = ldexpf(a, -E);                                   // [1, 2), exact
+        code = (uint32_t)((E + 7) << 3) + (uint32_t)rintf((m - 1.0f) * 8.0f);
+    }
+    return sign | code;
+}
+
+// One workgroup per token row; each thread takes 8 consecutive elements at a
+// time (one 16-byte load, one 8-byte store).  H % 8 == 0.
+__global__ __launch_bounds__(256) void quant_rows_e4m3_kernel(const uint16_t* __restrict__ x,
+                                                              int H, uint8_t* __restrict__ xq,
+                                                              float* __restrict__ xs) {
+    const int t = blockIdx.x;
+    const u32x4* row = reinterpret_cast<const u32x4*>(x + (size_t)t * H);
+    const int nc = H / 8;
+    float amax = 0.0f;
+    for (int c = threadIdx.x; c < nc; c += 256) {
+        const u32x4 v = row[c];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            amax = fmaxf(amax, fabsf(__uint_as_float(v[j] << 16)));
+            amax = fmaxf(amax, fabsf(__uint_as_float(v[j] & 0xFFFF0000u)));
+        }
+    }
+    __shared__ float wmax[4];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, MOE_WAVE));
+    if (lane_id() == 0) wmax[threadIdx.x >> 6] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    const float s = __fdiv_rn(amax, 448.0f);
+    if (threadIdx.x == 0) xs[t] = s;
+    uint2* out = reinterpret_cast<uint2*>(xq + (size_t)t * H);
+    for (int c = threadIdx.x; c < nc; c += 256) {
+        const u32x4 v = row[c];
+        uint32_t w[2] = {0u, 0u};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t b = (v[j >> 1] >> ((j & 1) * 16)) & 0xFFFFu;
+            const uint32_t q = s > 0.0f ? e4m3fn_encode_rne(__fdiv_rn(__uint_as_float(b << 16), s)) : 0u;
+            w[j >> 2] |= q << ((j & 3) * 8);
+        }
+        out[c] = uint2{w[0], w[1]};
+    }
+}
+
+int launch_quant_rows_e4m3(const uint16_t* x, int T, int H, uint8_t* xq, float* xs,
+                           hipStream_t stream) {
+    if (H % 8) {
+        set_error("activation quantisation needs H %% 8 == 0 (got %d)", H);
+        return MOE_EUNSUPPORTED;
+    }
+    if (T == 0) return MOE_OK;
+    prof_begin("quant_rows_e4m3", stream);
+    quant_rows_e4m3_kernel<<<T, 256, 0, stream>>>(x, H, xq, xs);
+    prof_end(stream);
+    return check_launch("quant_rows_e4m3_kernel");
+}
+
+}  // namespace moe

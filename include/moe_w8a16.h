@@ -65,7 +65,10 @@ enum {
 enum {
     MOE_VARIANT_AUTO = 0,     /* decode for T*k <= 16E and T*k <= 4096, else prefill */
     MOE_VARIANT_DECODE = 1,   /* weight-streaming kernels, one workgroup per (expert, N tile) */
-    MOE_VARIANT_PREFILL = 2   /* grouped bf16-MFMA GEMM over 128-row tiles of sorted routes */
+    MOE_VARIANT_PREFILL = 2,  /* grouped bf16-MFMA GEMM over 128-row tiles of sorted routes */
+    MOE_VARIANT_PREFILL_A8 = 3  /* the prefill GEMMs with x quantised to E4M3 per token (as
+                                   moe_quant_e4m3_rows) for the gate/up (or up) GEMM on the
+                                   FP8 MFMA; the down GEMM as PREFILL; never chosen by AUTO */
 };
 
 enum {
@@ -216,6 +219,10 @@ typedef struct {
  * is multiplied by its
  * fp32 block scale; the SwiGLU output is rounded to bf16 before the down GEMM.
  */
+/* MOE_VARIANT_PREFILL_A8 computes every expert from x_hat[t] = decode(code) * scale
+ * of moe_quant_e4m3_rows instead of x[t] (gate/up on fp8 x fp8 products, exact
+ * in fp32, with fp32 sums); the rest of the path is that of MOE_VARIANT_PREFILL,
+ * with the same shape rules.  Its workspace holds the codes and scales too. */
 size_t moe_fused_workspace_bytes(int T, int H, int I, int E, int k,
                                  int has_shared, int variant);
 int moe_fused_w8a16(const void* x,
@@ -249,6 +256,22 @@ int moe_fused_w8a16_ex(const void* x,
                        const moe_expert_w8* shared, float* out,
                        int32_t* status, void* ws, size_t ws_bytes,
                        int weight_layout, int variant, int activation, void* stream);
+
+/*
+ * moe_quant_e4m3_rows -- the per-token activation quantisation that
+ * MOE_VARIANT_PREFILL_A8 applies to x, exposed so it can be checked on its
+ * own.  For each row t:
+ *     scales[t] = max_h |x[t][h]| / 448                    (fp32, correctly rounded)
+ *     codes[t][h] = E4M3FN round-half-even of min(max(x[t][h] / scales[t], -448), 448)
+ * with the quotient in fp32; a row of zeros gets scale 0 and zero codes.  The
+ * value the GEMM then uses is decode(code) * scale.  Source of the format and
+ * of the amax / 448 rule: NKI page, section "FP8 MoE decode kernel" (official
+ * E4M3FN weights, block scale = block maximum / 448), applied per token row.
+ *   x [T, H] bf16 (16-byte aligned), codes [T, H] uint8 (8-byte aligned),
+ *   scales [T] fp32; H % 8 == 0 (else MOE_EINVAL); T == 0 is a no-op.
+ */
+int moe_quant_e4m3_rows(const void* x, int T, int H, uint8_t* codes, float* scales,
+                        void* stream);
 
 /*
  * moe_decode_e4m3fn -- decode n E4M3FN bytes to bf16 bit patterns with the

@@ -19,6 +19,9 @@ from .moe_ref import (  # noqa: F401
     e4m3fn_table,
     e4m3fn_decode,
     dequantize_blocks,
+    e4m3fn_encode_rne,
+    quantize_rows_e4m3,
+    dequantize_rows,
     route_softmax_topk,
     route_sigmoid_topk,
     router_logits,

@@ -87,6 +87,44 @@ def dequantize_blocks(codes, scales, block: int = BLOCK) -> np.ndarray:
     return vals * s
 
 
+def e4m3fn_encode_rne(v) -> np.ndarray:
+    """E4M3FN codes of values with |v| <= 448: the nearest finite value of the
+    format, a tie going to the code with an even mantissa (round half to even);
+    the sign bit is copied, so -0.0 and small negatives give 0x80."""
+    v = np.asarray(v, dtype=np.float64)
+    assert np.all(np.abs(v) <= E4M3FN_MAX)
+    mags = _TABLE[:0x7F]                      # codes 0x00..0x7E, increasing
+    a = np.abs(v)
+    hi = np.clip(np.searchsorted(mags, a, side="left"), 0, 0x7E)
+    lo = np.clip(hi - 1, 0, 0x7E)
+    d_lo, d_hi = a - mags[lo], mags[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo)
+    return (code | np.where(np.signbit(v), 0x80, 0)).astype(np.uint8)
+
+
+def quantize_rows_e4m3(x):
+    """Per-token E4M3 quantisation of activations, decided in fp32 like the
+    weights' recipe ([NKI] FP8 weights with a scale of block max / 448, here
+    per token row): s = fp32(amax / 448), code = RNE(fp32(x / s)) clamped to
+    +-448; a row of zeros gets s = 0 and zero codes.  Returns (codes uint8
+    [T, H], scales float32 [T]); the GEMM uses decode(code) * s."""
+    x32 = np.asarray(x, dtype=np.float32)
+    amax = np.abs(x32).max(axis=1)
+    s = (amax / np.float32(E4M3FN_MAX)).astype(np.float32)
+    safe = np.where(s > 0, s, np.float32(1.0)).astype(np.float32)
+    v = (x32 / safe[:, None]).astype(np.float32)
+    v = np.clip(v, -E4M3FN_MAX, E4M3FN_MAX)
+    codes = e4m3fn_encode_rne(v)
+    codes[s == 0] = 0
+    return codes, s
+
+
+def dequantize_rows(codes, scales) -> np.ndarray:
+    """x_hat[t, h] = decode(codes[t, h]) * scales[t] (float64)."""
+    return e4m3fn_decode(codes) * np.asarray(scales, dtype=np.float64)[:, None]
+
+
 # --------------------------------------------------------------------------
 # Routing: softmax -> top-k -> normalise  ([NKI] Serving contract)
 # --------------------------------------------------------------------------

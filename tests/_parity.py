@@ -29,8 +29,9 @@ def np_(t):
     return t.detach().cpu().numpy()
 
 
-def oracle_rows(case, ids, aff, rows, with_shared=True):
-    """(The case's "activation" entry selects the expert MLP.)"""
+def oracle_rows(case, ids, aff, rows, with_shared=True, xrows=None):
+    """(The case's "activation" entry selects the expert MLP; xrows, when
+    given, replaces the activation rows, e.g. by their fp8 quantisation.)"""
     """Oracle output for the given token rows, copying only the experts they use."""
     rows = np.asarray(rows)
     sub_ids = np.asarray(ids)[rows]
@@ -44,7 +45,7 @@ def oracle_rows(case, ids, aff, rows, with_shared=True):
     sh = None
     if with_shared and case.get("shared") is not None:
         sh = {n: np_(t) for n, t in case["shared"].items()}
-    x = np_(case["x"].float())[rows]
+    x = np_(case["x"].double())[rows] if xrows is None else np.asarray(xrows, dtype=np.float64)
     return oracle.moe_ffn(x, w13, w13s, w2, w2s, remap, np.asarray(aff)[rows], sh,
                           activation=case.get("activation", "swiglu"))
 

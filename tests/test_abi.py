@@ -129,6 +129,20 @@ def test_fused_activation_checks():
     assert b"I % 256" in lib.moe_last_error()
 
 
+def test_quant_e4m3_rows_argument_checks():
+    lib = binding.load_library()
+    f = ctypes.c_void_p(0x1000)
+    assert lib.moe_quant_e4m3_rows(f, 4, 12, f, f, None) == binding.MOE_EINVAL
+    assert lib.moe_quant_e4m3_rows(ctypes.c_void_p(0x1008), 4, 16, f, f, None) == binding.MOE_EINVAL
+    assert b"aligned" in lib.moe_last_error()
+    assert lib.moe_quant_e4m3_rows(f, 4, 16, None, f, None) == binding.MOE_EINVAL
+    assert lib.moe_quant_e4m3_rows(None, 0, 16, None, None, None) == binding.MOE_OK
+    # the fp8-activation variant's workspace also holds the codes and scales
+    a8 = lib.moe_fused_workspace_bytes(8192, 2048, 512, 256, 8, 0, 3)
+    pf = lib.moe_fused_workspace_bytes(8192, 2048, 512, 256, 8, 0, 2)
+    assert a8 >= pf + 8192 * 2048 + 8192 * 4
+
+
 def test_fused_argument_checks():
     lib = binding.load_library()
     f = ctypes.c_void_p(0x1000)

@@ -560,3 +560,59 @@ def test_graph_replay_with_changing_routes():
             ref_ids, ref_aff = oracle.route_softmax_topk(np_(logits), cfg.k)
             ref = oracle_rows(c, ref_ids, ref_aff, np.arange(cfg.T))
             assert_out_close(np_(got), ref, what=f"graph replay {rep}")
+
+
+# ------------------------------------------------------------ fp8 activations
+@pytest.mark.parametrize("T,H", [(1, 8), (5, 256), (333, 2048), (7, 8192), (8192, 2048)])
+def test_quant_e4m3_rows_bit_exact(T, H):
+    x = synth.make_activations(synth.MoeConfig("q", T, H, 128, 8, 1), seed=T + H)[0]
+    if T > 2:
+        x[1] = 0.0                      # a zero row: scale 0, codes 0
+        x[2, :] = 0.0
+        x[2, H // 2] = -1.5             # one element: it maps to -448 (0xFE)
+    xg = x.cuda()
+    codes, scales = binding.quant_e4m3_rows(xg)
+    torch.cuda.synchronize()
+    ref_c, ref_s = oracle.quantize_rows_e4m3(x.float().numpy())
+    assert np.array_equal(np_(scales).view(np.uint32), ref_s.view(np.uint32))
+    assert np.array_equal(np_(codes), ref_c)
+
+
+def _xhat_rows(c, rows):
+    codes, s = oracle.quantize_rows_e4m3(np_(c["x"][torch.as_tensor(rows, device=c["x"].device)].float()))
+    return oracle.dequantize_rows(codes, s)
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("name", synth.CONFIG_ORDER)
+def test_fused_prefill_a8_parity(name, layout):
+    """x quantised to E4M3 per token, gate/up on the FP8 MFMA: against the
+    oracle run on the same quantised rows."""
+    c = _case(name)
+    cfg = c["cfg"]
+    ids, aff = binding.route(c["logits"], cfg.k)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = _fused(c, ids, aff, variant="prefill_a8", status=status, layout=layout)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    ref_ids, ref_aff = oracle.route_softmax_topk(np_(c["logits"]), cfg.k)
+    rows = sample_rows(cfg.T, FFN_SAMPLE[name], seed=4)
+    ref = oracle_rows(c, ref_ids, ref_aff, rows, xrows=_xhat_rows(c, rows))
+    assert_out_close(np_(out)[rows], ref, what=f"a8 {name}/{layout}")
+
+
+@pytest.mark.parametrize("name", ["tiny", "prefill16k_wide"])
+def test_fused_prefill_a8_relu2(name):
+    c = _case(name, "relu2")
+    cfg = c["cfg"]
+    ids, aff = binding.route(c["logits"], cfg.k)
+    if cfg.I % 256:
+        with pytest.raises(binding.MoeError):
+            _fused(c, ids, aff, variant="prefill_a8", activation="relu2")
+        return
+    out = _fused(c, ids, aff, variant="prefill_a8", activation="relu2")
+    torch.cuda.synchronize()
+    ref_ids, ref_aff = oracle.route_softmax_topk(np_(c["logits"]), cfg.k)
+    rows = sample_rows(cfg.T, FFN_SAMPLE[name], seed=5)
+    ref = oracle_rows(c, ref_ids, ref_aff, rows, xrows=_xhat_rows(c, rows))
+    assert_out_close(np_(out)[rows], ref, what=f"a8 relu2 {name}")

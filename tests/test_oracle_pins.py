@@ -144,6 +144,47 @@ def test_route_golden_rows():
         np.testing.assert_allclose(aff[0], [float(v) for v in a_s.split()], rtol=1e-14, atol=0)
 
 
+# ------------------------------------------------- activation quantisation (E4M3)
+def test_e4m3_encoder_matches_torch_cast_on_ties_and_sweeps():
+    mags = oracle.e4m3fn_table()[:0x7F]
+    mids = (mags[:-1] + mags[1:]) / 2             # every tie between neighbours
+    rng = np.random.default_rng(21)
+    vals = np.concatenate([mags, mids, mids * (1 + 2.0 ** -20), mids * (1 - 2.0 ** -20),
+                           rng.uniform(-448, 448, 200000), rng.standard_normal(50000) * 1e-2,
+                           [0.0, -0.0, 448.0, -448.0, 2.0 ** -10, -(2.0 ** -10)]])
+    vals = np.concatenate([vals, -vals]).astype(np.float32)
+    vals = vals[np.abs(vals) <= 448]
+    ref = torch.from_numpy(vals).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(oracle.e4m3fn_encode_rne(vals), ref)
+
+
+def test_quantize_rows_matches_torch_and_closed_forms():
+    x = torch.randn(64, 512, generator=torch.Generator().manual_seed(22)).to(torch.bfloat16).float()
+    x[3] = 0.0
+    x[5, :] = 0.0
+    x[5, 17] = -3.0
+    xn = x.numpy()
+    codes, s = oracle.quantize_rows_e4m3(xn)
+    # the same recipe through torch's own fp32 ops and E4M3 cast
+    amax = x.abs().amax(dim=1)
+    ts = amax / 448.0
+    safe = torch.where(ts > 0, ts, torch.ones_like(ts))
+    ref = (x / safe[:, None]).clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8)
+    ref[ts == 0] = 0
+    assert np.array_equal(s, ts.numpy()) and np.array_equal(codes, ref.numpy())
+    # closed forms: the row maximum maps to +-448 (0x7E / 0xFE); a zero row to
+    # scale 0 and code 0; row [1, -2, 0.5, 4]: x/s = 112, -224, 56, 448
+    assert s[3] == 0 and np.all(codes[3] == 0)
+    assert codes[5, 17] == 0xFE and np.all(np.delete(codes[5], 17) == 0)
+    c4, s4 = oracle.quantize_rows_e4m3(np.array([[1.0, -2.0, 0.5, 4.0]], np.float32))
+    assert c4.tolist() == [[0x6E, 0xF6, 0x66, 0x7E]] and s4[0] == np.float32(4.0) / np.float32(448)
+    # dequantised values within half an E4M3 step (relative 2^-4) of x, plus the
+    # subnormal step 2^-10 * s near zero
+    xh = oracle.dequantize_rows(codes, s)
+    err = np.abs(xh - xn.astype(np.float64))
+    assert np.all(err <= 2.0 ** -4 * np.abs(xn) + 2.0 ** -10 * s[:, None] + 1e-30)
+
+
 # ----------------------------------------------------------- sigmoid routing
 def _sigmoid_golden_rows():
     rows = []
