@@ -26,6 +26,7 @@ if ROOT not in sys.path:
 METRIC = "fused FP8 MoE tokens/s + %HBM BW (decode T=64) / %MFMA peak (prefill T=8192)"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense fp8 MFMA, published
 
 
 def log(msg):
@@ -395,24 +396,27 @@ def router_variants_bench(cfg, dev, seed=0, calls=64, samples=7, replays=20):
     return out
 
 
-def relu2_bench(cfg, dev, L, seed=0, samples=7, replays=50):
-    """The fused call (sort + expert FFN + expert sum) with non-gated relu^2
-    experts (MOE_ACT_RELU2: up projection [I, H], relu^2, down) on the
-    workload's shapes, `L` weight sets, one call per set captured in a HIP
+def fused_variant_bench(cfg, dev, L, seed=0, activation="swiglu", variant="auto", samples=7,
+                        replays=50):
+    """The fused call (sort + expert FFN + expert sum) for another activation
+    (relu^2: non-gated experts, up projection [I, H], relu^2, down) or variant
+    (prefill_a8: x quantised to E4M3 per token, gate/up on the FP8 MFMA) on the
+    workload's shapes: `L` weight sets, one call per set captured in a HIP
     graph, median per call; then per-kernel times from the library's events.
-    Algorithmic work per (route or shared row): 4*H*I flops; weights
-    2*H*I bytes (+ scales) per active expert."""
+    Algorithmic work per route (or shared row): 2*H*(n13 + I) flops with
+    n13 = 2I (SwiGLU) or I (relu^2); weights (n13 + I)*H bytes (+ scales) per
+    active expert."""
     import statistics
 
     import torch
 
     from block_scaled_fp8_amd import binding, synth
     T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
-    log(f"relu^2 experts on {cfg.name}: {L} weight sets")
+    log(f"{activation} experts, variant {variant}, on {cfg.name}: {L} weight sets")
     x, logits = synth.make_activations(cfg, seed, dev)
     runs = []
     for i in range(L):
-        w = synth.make_weights(cfg, seed + 100 * i, dev, activation="relu2")
+        w = synth.make_weights(cfg, seed + 100 * i, dev, activation=activation)
         p = dict(w, w13=binding.pack_w8(w["w13"]), w2=binding.pack_w8(w["w2"]))
         if w["shared"] is not None:
             p["shared"] = dict(w["shared"], w13=binding.pack_w8(w["shared"]["w13"]),
@@ -420,7 +424,7 @@ def relu2_bench(cfg, dev, L, seed=0, samples=7, replays=50):
         del w
         runs.append(binding.MoeStep(x, logits, k, p["w13"], p["w13_scale"], p["w2"],
                                     p["w2_scale"], shared=p["shared"], layout="tiled",
-                                    activation="relu2"))
+                                    variant=variant, activation=activation))
     ids, _ = binding.route(logits, k)
     n_active = int((torch.bincount(ids.reshape(-1).long(), minlength=E) > 0).sum().item())
     for r in runs:
@@ -457,19 +461,28 @@ def relu2_bench(cfg, dev, L, seed=0, samples=7, replays=50):
     prof = binding.profile_collect()
     rows = T * k + (T if cfg.shared else 0)
     nseg = n_active + (1 if cfg.shared else 0)
-    flops = 4.0 * H * I * rows
-    wbytes = nseg * (2 * H * I + 4 * (I // 128) * (H // 128) + 4 * (H // 128) * (I // 128))
+    n13 = I if activation == "relu2" else 2 * I
+    flops = 2.0 * H * (n13 + I) * rows
+    wbytes = nseg * ((n13 + I) * H + 4 * (n13 // 128) * (H // 128) + 4 * (H // 128) * (I // 128))
     nbytes = wbytes + 2 * T * H + 4 * T * H + 8 * T * k
-    out = {"workload": cfg.name, "activation": "relu2", "active_experts": n_active,
-           "weight_sets": L,
+    out = {"workload": cfg.name, "activation": activation, "variant": variant,
+           "active_experts": n_active, "weight_sets": L,
            "protocol": f"HIP graph of one fused call per weight set, median of {samples} x "
                        f"{replays} replays",
            "us_per_call": round(us, 2), "tokens_per_s": round(T / (us * 1e-6), 1),
            "GB_per_s": round(nbytes / (us * 1e-6) / 1e9, 1),
            "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
            "TFLOP_per_s": round(flops / (us * 1e-6) / 1e12, 1),
-           "mfma_frac": round(flops / (us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4),
+           "mfma_frac_bf16": round(flops / (us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4),
            "kernels": {n: {"launches": c, "avg_us": round(ms * 1e3, 3)} for n, (c, ms) in prof.items()}}
+    a8 = [n for n in prof if n.endswith("_a8")]
+    if a8:
+        # the fp8 x fp8 gate/up (or up) GEMM against the FP8 MFMA peak
+        kus = prof[a8[0]][1] * 1e3
+        kfl = 2.0 * H * n13 * rows
+        out["fp8_gemm"] = {"kernel": a8[0], "avg_us": round(kus, 3), "flops": kfl,
+                           "TFLOP_per_s": round(kfl / (kus * 1e-6) / 1e12, 1),
+                           "peak": FP8_PEAK_TFLOPS, "frac": round(kfl / (kus * 1e-6) / 1e12 / FP8_PEAK_TFLOPS, 4)}
     log(f"  {us:.1f} us per call; " + ", ".join(f"{n} {ms * 1e3:.1f} us" for n, (c, ms) in prof.items()))
     del runs, x, logits
     torch.cuda.empty_cache()
@@ -523,6 +536,8 @@ def main():
                     help="untimed prefill steps first: the GPU idles while the prefill inputs "
                          "are generated, and its clock needs some milliseconds of work to settle")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-a8", action="store_true",
+                    help="skip the fp8-activation prefill measurement (MOE_VARIANT_PREFILL_A8)")
     ap.add_argument("--no-relu2", action="store_true",
                     help="skip the relu^2-expert measurement (MOE_ACT_RELU2)")
     ap.add_argument("--no-route-proj", action="store_true",
@@ -621,10 +636,14 @@ def main():
             log("vendor bf16 GEMM at the gate/up shape (context) ...")
             result["prefill"]["vendor_bf16_gemm"] = vendor_gemm(pcfg, dev)
     if not args.no_relu2:
-        result["relu2"] = [relu2_bench(cfg, dev, max(1, args.weight_sets), args.seed)]
+        result["relu2"] = [fused_variant_bench(cfg, dev, max(1, args.weight_sets), args.seed,
+                                               activation="relu2")]
         if args.prefill_workload:
-            result["relu2"].append(relu2_bench(synth.CONFIGS[args.prefill_workload], dev, 2,
-                                               args.seed))
+            result["relu2"].append(fused_variant_bench(synth.CONFIGS[args.prefill_workload], dev,
+                                                       2, args.seed, activation="relu2"))
+    if args.prefill_workload and not args.no_a8:
+        result["prefill_a8"] = fused_variant_bench(synth.CONFIGS[args.prefill_workload], dev, 2,
+                                                   args.seed, variant="prefill_a8")
     if not args.no_route_proj:
         result["router_variants"] = [router_variants_bench(cfg, dev, args.seed)]
         if args.prefill_workload:
