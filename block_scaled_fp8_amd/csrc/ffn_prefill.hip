@@ -105,7 +105,7 @@ struct PfCfg {
 // faster there.
 using PfGateUp = PfCfg<128, 256, 2, 2, 2, 2, 1>;
 using PfDown = PfCfg<128, 256, 2, 2, 2, 2, 0>;
-using PfGateUpA8 = PfCfg<128, 256, 2, 2, 2, 2, 0, 1>;
+using PfGateUpA8 = PfCfg<128, 256, 2, 2, 3, 2, 0, 1>;
 constexpr int PF_BM = 128;
 
 int prefill_tile_m() { return PF_BM; }
@@ -556,7 +556,10 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
                 }
             };
             auto next_stage = [&](int kc) {
-                wait_vmcnt<0>();             // stage kc + 1 landed in this wave
+                // stage kc + 1 landed in this wave (with three stages, kc + 2 may
+                // still be in flight)
+                if (C::STAGES >= 3 && kc + 2 < nk) wait_vmcnt<(C::STAGES >= 3 ? PER_STAGE : 0)>();
+                else wait_vmcnt<0>();
                 barrier_after_lds_reads();   // ... in every wave; stage kc read by every wave
                 if (kc + C::STAGES < nk) issue_stage(kc % C::STAGES, kc + C::STAGES);
             };

@@ -31,42 +31,64 @@ __device__ __forceinline__ uint32_t e4m3fn_encode_rne(float v) {
     return sign | code;
 }
 
-// One workgroup per token row; each thread takes 8 consecutive elements at a
-// time (one 16-byte load, one 8-byte store).  H % 8 == 0.
+// One wave per token row, four rows per workgroup, no barrier.  Lane l takes
+// the 8-element chunks l, l + 64, ...; rows of up to NCH * 512 elements stay
+// in registers between the maximum and the encoding (NCH = 0: any width, the
+// row is read twice, the second time from the cache).  H % 8 == 0.
+template <int NCH>
 __global__ __launch_bounds__(256) void quant_rows_e4m3_kernel(const uint16_t* __restrict__ x,
-                                                              int H, uint8_t* __restrict__ xq,
+                                                              int T, int H,
+                                                              uint8_t* __restrict__ xq,
                                                               float* __restrict__ xs) {
-    const int t = blockIdx.x;
+    const int lane = lane_id();
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;  // whole waves
     const u32x4* row = reinterpret_cast<const u32x4*>(x + (size_t)t * H);
     const int nc = H / 8;
-    float amax = 0.0f;
-    for (int c = threadIdx.x; c < nc; c += 256) {
-        const u32x4 v = row[c];
+    auto chunk_max = [](const u32x4& v, float m) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            amax = fmaxf(amax, fabsf(__uint_as_float(v[j] << 16)));
-            amax = fmaxf(amax, fabsf(__uint_as_float(v[j] & 0xFFFF0000u)));
+            m = fmaxf(m, fabsf(__uint_as_float(v[j] << 16)));
+            m = fmaxf(m, fabsf(__uint_as_float(v[j] & 0xFFFF0000u)));
         }
+        return m;
+    };
+    float amax = 0.0f;
+    u32x4 v[NCH > 0 ? NCH : 1];
+    if constexpr (NCH > 0) {
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) {
+            const int c = lane + 64 * j;
+            v[j] = c < nc ? row[c] : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) amax = chunk_max(v[j], amax);
+    } else {
+        for (int c = lane; c < nc; c += 64) amax = chunk_max(row[c], amax);
     }
-    __shared__ float wmax[4];
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, MOE_WAVE));
-    if (lane_id() == 0) wmax[threadIdx.x >> 6] = amax;
-    __syncthreads();
-    amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
     const float s = __fdiv_rn(amax, 448.0f);
-    if (threadIdx.x == 0) xs[t] = s;
+    if (lane == 0) xs[t] = s;
     uint2* out = reinterpret_cast<uint2*>(xq + (size_t)t * H);
-    for (int c = threadIdx.x; c < nc; c += 256) {
-        const u32x4 v = row[c];
+    auto encode_chunk = [&](const u32x4& c8) {
         uint32_t w[2] = {0u, 0u};
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const uint32_t b = (v[j >> 1] >> ((j & 1) * 16)) & 0xFFFFu;
+            const uint32_t b = (c8[j >> 1] >> ((j & 1) * 16)) & 0xFFFFu;
             const uint32_t q = s > 0.0f ? e4m3fn_encode_rne(__fdiv_rn(__uint_as_float(b << 16), s)) : 0u;
             w[j >> 2] |= q << ((j & 3) * 8);
         }
-        out[c] = uint2{w[0], w[1]};
+        return uint2{w[0], w[1]};
+    };
+    if constexpr (NCH > 0) {
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) {
+            const int c = lane + 64 * j;
+            if (c < nc) out[c] = encode_chunk(v[j]);
+        }
+    } else {
+        for (int c = lane; c < nc; c += 64) out[c] = encode_chunk(row[c]);
     }
 }
 
@@ -77,8 +99,19 @@ int launch_quant_rows_e4m3(const uint16_t* x, int T, int H, uint8_t* xq, float* 
         return MOE_EUNSUPPORTED;
     }
     if (T == 0) return MOE_OK;
+    const int nc = H / 8;
+    const dim3 grid((T + 3) / 4), block(256);
     prof_begin("quant_rows_e4m3", stream);
-    quant_rows_e4m3_kernel<<<T, 256, 0, stream>>>(x, H, xq, xs);
+    if (nc <= 64)
+        quant_rows_e4m3_kernel<1><<<grid, block, 0, stream>>>(x, T, H, xq, xs);
+    else if (nc <= 128)
+        quant_rows_e4m3_kernel<2><<<grid, block, 0, stream>>>(x, T, H, xq, xs);
+    else if (nc <= 256)
+        quant_rows_e4m3_kernel<4><<<grid, block, 0, stream>>>(x, T, H, xq, xs);
+    else if (nc <= 512)
+        quant_rows_e4m3_kernel<8><<<grid, block, 0, stream>>>(x, T, H, xq, xs);
+    else
+        quant_rows_e4m3_kernel<0><<<grid, block, 0, stream>>>(x, T, H, xq, xs);
     prof_end(stream);
     return check_launch("quant_rows_e4m3_kernel");
 }
