@@ -566,8 +566,11 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
     #pragma unroll
             for (int st = 0; st < C::STAGES; ++st)
                 if (st < nk) issue_stage(st, st);
-            wait_vmcnt<(C::STAGES - 1) * PER_STAGE>();
-            barrier_after_lds_reads();  // stage 0 and the scale table landed in every wave
+            // stage 0 and the scale table landed (with fewer K stages than
+            // buffers, e.g. K = 128 on three stages, wait for everything)
+            if (nk >= C::STAGES) wait_vmcnt<(C::STAGES - 1) * PER_STAGE>();
+            else wait_vmcnt<0>();
+            barrier_after_lds_reads();  // ... in every wave
             float snext[2] = {sc_tab[sj[0] * kbp], sc_tab[sj[1] * kbp]};
             const float one[2] = {1.0f, 1.0f};
             for (int kb = 0; kb < kblocks; ++kb) {

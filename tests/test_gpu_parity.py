@@ -602,6 +602,21 @@ def test_fused_prefill_a8_parity(name, layout):
     assert_out_close(np_(out)[rows], ref, what=f"a8 {name}/{layout}")
 
 
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_fused_prefill_a8_shortest_k(layout):
+    """The fp8 gate/up GEMM at the smallest supported H (256: four 64-wide K
+    stages on three LDS buffers) and I = 256, every row checked."""
+    cfg = synth.MoeConfig("a8k", T=300, H=256, I=256, E=8, k=2, shared=True)
+    c = gpu_case(cfg, seed=256)
+    ids, aff = binding.route(c["logits"], cfg.k)
+    out = _fused(c, ids, aff, variant="prefill_a8", layout=layout)
+    torch.cuda.synchronize()
+    ref_ids, ref_aff = oracle.route_softmax_topk(np_(c["logits"]), cfg.k)
+    rows = np.arange(cfg.T)
+    ref = oracle_rows(c, ref_ids, ref_aff, rows, xrows=_xhat_rows(c, rows))
+    assert_out_close(np_(out), ref, what=f"a8 H=256/{layout}")
+
+
 @pytest.mark.parametrize("name", ["tiny", "prefill16k_wide"])
 def test_fused_prefill_a8_relu2(name):
     c = _case(name, "relu2")
