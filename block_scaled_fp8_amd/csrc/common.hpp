@@ -74,6 +74,39 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
 
 // ---------------------------------------------------------------- SwiGLU
 // silu(g) * u with silu(g) = g / (1 + exp(-g)).
+// Prefill contributions leave the down GEMM as the top 24 bits of their fp32
+// value (sign, 8-bit exponent, 15 fraction bits: 16 significant bits), rounded
+// to nearest even: at most 2^-17 relative, far below the bf16 rounding of the
+// activations that feed the same GEMM.  A row of H values is stored as two
+// planes: the upper 16 bits of each value (2*H bytes), then the low 8 bits
+// (H bytes), so that a lane's run of consecutive values is one contiguous
+// piece in each plane.  (Finite inputs only.)
+__device__ __forceinline__ uint32_t f32_to_f24_bits(float f) {
+    const uint32_t u = __float_as_uint(f);
+    return (u + 0x7Fu + ((u >> 8) & 1u)) >> 8;
+}
+// 8 values -> hi plane (4 words: value j in bits 16*(j%2) of word j/2) and
+// lo plane (2 words: value j in bits 8*(j%4) of word j/4)
+__device__ __forceinline__ void split_f24x8(f32x4 a, f32x4 b, u32x4& hi, u32x2& lo) {
+    uint32_t w[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        w[j] = f32_to_f24_bits(a[j]);
+        w[4 + j] = f32_to_f24_bits(b[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) hi[j] = (w[2 * j] >> 8) | ((w[2 * j + 1] >> 8) << 16);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+        lo[j] = (w[4 * j] & 0xFFu) | ((w[4 * j + 1] & 0xFFu) << 8) | ((w[4 * j + 2] & 0xFFu) << 16) |
+                ((w[4 * j + 3] & 0xFFu) << 24);
+}
+__device__ __forceinline__ float join_f24(u32x4 hi, u32x2 lo, int j) {
+    const uint32_t h16 = (hi[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+    const uint32_t l8 = (lo[j >> 2] >> (8 * (j & 3))) & 0xFFu;
+    return __uint_as_float((h16 << 16) | (l8 << 8));
+}
+
 __device__ __forceinline__ float swiglu(float g, float u) {
     return g / (1.0f + __expf(-g)) * u;
 }

@@ -252,18 +252,15 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_ffn_kernel(
 // multiplied each row by its affinity.  Source: AITER PR page (FP32 route
 // reduction); NKI page (affinity scale -> expert-sum, shared expert added after
 // the routed sum).
-// Sum of the k route rows of a token (slot order) plus its shared-expert row.
-// All loads are issued before any is used: the ids only select (a row of an
-// invalid route was never written and may hold anything, so it is masked, not
-// multiplied), which keeps one memory round trip per thread.  ybuf is read
-// once, so its loads bypass the caches' retention (non-temporal).
-// GATHER: route r's row sits at inv_route[r] (the prefill producers write at
-// the sorted position); otherwise at r itself.
-template <int KMAX, bool GATHER>
+// Sum of the k route rows of a token (slot order) plus its shared-expert row,
+// decode form: route r's row aff[r] * y is fp32 row r of ybuf.  All loads are
+// issued before any is used: the ids only select (a row of an invalid route
+// was never written and may hold anything, so it is masked, not multiplied),
+// which keeps one memory round trip per thread.  ybuf is read once, so its
+// loads bypass the caches' retention (non-temporal).
+template <int KMAX>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ ybuf,
                                                       const int32_t* __restrict__ ids,
-                                                      const int32_t* __restrict__ inv_route,
-                                                      const float* __restrict__ aff,
                                                       int T, int H, int k, int E, int has_shared,
                                                       int32_t* __restrict__ status,
                                                       float* __restrict__ out) {
@@ -272,16 +269,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     if (h >= H) return;
     f32x4 v[KMAX];
     int id[KMAX];
-    float a[KMAX];
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {
         if (j < k) {
             const size_t r = (size_t)t * k + j;
             id[j] = ids[r];
-            a[j] = GATHER ? aff[r] : 1.0f;
-            const int p = GATHER ? inv_route[r] : (int)r;
-            const size_t row = p >= 0 ? (size_t)p : 0;  // a dropped route: any row, masked below
-            v[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(ybuf + row * H + h));
+            v[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(ybuf + r * H + h));
         }
     }
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -297,12 +290,75 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
             const bool ok = id[j] >= 0 && id[j] < E;  // an invalid id's route is dropped
             bad |= !ok;
 #pragma unroll
-            for (int c = 0; c < 4; ++c) sum[c] += ok ? (GATHER ? a[j] * v[j][c] : v[j][c]) : 0.0f;
+            for (int c = 0; c < 4; ++c) sum[c] += ok ? v[j][c] : 0.0f;
         }
     }
     if (bad && status && h == 0) atomicOr(status, MOE_STATUS_BAD_EXPERT_ID);
     // routed sum in slot order first, then the shared expert
     *reinterpret_cast<f32x4*>(out + (size_t)t * H + h) = sum + acc;
+}
+
+// Prefill form: the producers write y of route r (no affinity) at its sorted
+// row inv_route[r] as 24-bit values in two planes per row (upper 16 bits at
+// byte 2*col, low 8 bits at byte 2*H + col; row stride 3*H; the shared row of
+// token t is row R + t).  A thread owns 8 columns (a 16-byte and an 8-byte
+// load per row), widens them to fp32 and adds aff[r] * y over the slots in
+// order, eight slots' loads in flight at a time, then the shared row.
+constexpr int COMBINE_G_THREADS = 256;
+__global__ __launch_bounds__(COMBINE_G_THREADS) void combine_gather_kernel(
+    const uint8_t* __restrict__ ybytes, const int32_t* __restrict__ ids,
+    const int32_t* __restrict__ inv_route, const float* __restrict__ aff, int T, int H, int k,
+    int E, int has_shared, int32_t* __restrict__ status, float* __restrict__ out) {
+    constexpr int G = 8;  // slots per batch of loads
+    const int t = blockIdx.y;
+    const int h = (blockIdx.x * COMBINE_G_THREADS + threadIdx.x) * 8;
+    if (h >= H) return;
+    const size_t rowb = (size_t)H * 3;
+    auto load_row = [&](size_t row, u32x4& hi, u32x2& lo) {
+        const uint8_t* p = ybytes + row * rowb;
+        hi = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + 2 * (size_t)h));
+        lo = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p + 2 * (size_t)H + h));
+    };
+    float sum[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) sum[c] = 0.0f;
+    bool bad = false;
+    for (int j0 = 0; j0 < k; j0 += G) {
+        u32x4 vh[G];
+        u32x2 vl[G];
+        int id[G];
+        float a[G];
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            if (j0 + j < k) {
+                const size_t r = (size_t)t * k + j0 + j;
+                id[j] = ids[r];
+                a[j] = aff[r];
+                const int p = inv_route[r];
+                load_row(p >= 0 ? (size_t)p : 0, vh[j], vl[j]);  // a dropped route: masked below
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            if (j0 + j < k) {
+                const bool ok = id[j] >= 0 && id[j] < E;  // an invalid id's route is dropped
+                bad |= !ok;
+#pragma unroll
+                for (int c = 0; c < 8; ++c) sum[c] += ok ? a[j] * join_f24(vh[j], vl[j], c) : 0.0f;
+            }
+        }
+    }
+    if (has_shared) {
+        u32x4 sh;
+        u32x2 sl;
+        load_row((size_t)T * k + t, sh, sl);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) sum[c] += join_f24(sh, sl, c);
+    }
+    if (bad && status && h == 0) atomicOr(status, MOE_STATUS_BAD_EXPERT_ID);
+    f32x4* o = reinterpret_cast<f32x4*>(out + (size_t)t * H + h);
+    o[0] = f32x4{sum[0], sum[1], sum[2], sum[3]};
+    o[1] = f32x4{sum[4], sum[5], sum[6], sum[7]};
 }
 
 template <int MODE, int LAYOUT>
@@ -391,22 +447,20 @@ int launch_combine(const float* ybuf, const int32_t* ids, const int32_t* inv_rou
         set_error("combine: the gathered form needs the affinities");
         return MOE_EINVAL;
     }
-    const dim3 grid((H / 4 + 255) / 256, T), block(256);
     prof_begin("combine", stream);
     if (inv_route) {
-        if (k <= 8)
-            combine_kernel<8, true><<<grid, block, 0, stream>>>(ybuf, ids, inv_route, aff, T, H, k, E,
-                                                                has_shared, status, out);
-        else
-            combine_kernel<MOE_MAX_TOPK, true><<<grid, block, 0, stream>>>(
-                ybuf, ids, inv_route, aff, T, H, k, E, has_shared, status, out);
+        // (H % 256 == 0 on the prefill path, so a thread's 8 columns are whole)
+        const dim3 grid((H / 8 + COMBINE_G_THREADS - 1) / COMBINE_G_THREADS, T);
+        combine_gather_kernel<<<grid, COMBINE_G_THREADS, 0, stream>>>(
+            reinterpret_cast<const uint8_t*>(ybuf), ids, inv_route, aff, T, H, k, E, has_shared,
+            status, out);
     } else {
+        const dim3 grid((H / 4 + 255) / 256, T), block(256);
         if (k <= 8)
-            combine_kernel<8, false><<<grid, block, 0, stream>>>(ybuf, ids, inv_route, aff, T, H, k, E,
-                                                                 has_shared, status, out);
+            combine_kernel<8><<<grid, block, 0, stream>>>(ybuf, ids, T, H, k, E, has_shared, status, out);
         else
-            combine_kernel<MOE_MAX_TOPK, false><<<grid, block, 0, stream>>>(
-                ybuf, ids, inv_route, aff, T, H, k, E, has_shared, status, out);
+            combine_kernel<MOE_MAX_TOPK><<<grid, block, 0, stream>>>(ybuf, ids, T, H, k, E, has_shared,
+                                                                    status, out);
     }
     prof_end(stream);
     return check_launch("combine_kernel");

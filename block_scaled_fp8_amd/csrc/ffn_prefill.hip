@@ -14,10 +14,11 @@
 // gfx950 design.  Kernel 1 (gate/up): each workgroup computes a 128-row x
 // (128 gate + 128 up) tile of one segment, applies SwiGLU in registers and
 // writes bf16 activations (abuf, sorted row order).  Kernel 2 (down): each
-// workgroup computes a 128-row x 256-column tile of y = a W2^T and writes
-// fp32 rows at their sorted position (a tile's rows are contiguous); the final
-// combine gathers the k rows of a token through the inverse route map and
-// applies the affinities.
+// workgroup computes a 128-row x 256-column tile of y = a W2^T and writes its
+// rows at their sorted position (a tile's rows are contiguous) as 24-bit
+// values, the top 24 bits of fp32 rounded to nearest even; the final combine
+// gathers the k rows of a token through the inverse route map, widens them
+// and applies the affinities in fp32.
 //
 //  * Workgroup tile 128 rows x 256 columns (gate/up: 128 gate + the matching
 //    128 up columns), 4 waves (2 x 2), each a 64 x 128 tile with 128 fp32
@@ -47,8 +48,9 @@
 //    MFMA row groups (16 rows gate/up, 32 down) are skipped.  The grid covers
 //    the worst case and idle workgroups exit.
 //  * Epilogue: gate/up reads a lane's row-table entries with 16-byte LDS
-//    reads before any store, applies SwiGLU and stores bf16; down stores its
-//    fp32 rows with non-temporal stores.
+//    reads before any store, applies SwiGLU and stores bf16; down turns its
+//    accumulators into row pieces through LDS and stores them packed with
+//    non-temporal stores.
 #include <algorithm>
 #include <type_traits>
 
@@ -100,9 +102,9 @@ struct PfCfg {
 // epilogue and barrier waits overlap the other's MFMAs.  Gate/up multiplies
 // with 16x16x32 MFMAs: on random operands the chip holds a higher clock for
 // them than for 32x32x16 (register-only loops: 1.94 against 1.71 PFLOP/s),
-// and the kernel measured 2.5% faster.  Down keeps 32x32x16: its fp32 rows
-// go out in 128-byte row pieces instead of 64-byte ones, which measured 4%
-// faster there.
+// and the kernel measured 2.5% faster.  Down keeps 32x32x16 (it measured 4%
+// faster when its fp32 rows left the accumulators directly, in 128-byte row
+// pieces instead of 64-byte ones; they now pass through LDS).
 using PfGateUp = PfCfg<128, 256, 2, 2, 2, 2, 1>;
 using PfDown = PfCfg<128, 256, 2, 2, 2, 2, 0>;
 using PfGateUpA8 = PfCfg<128, 256, 2, 2, 3, 2, 0, 1>;
@@ -121,7 +123,7 @@ int prefill_supported(int H, int I, int act) {
 
 // PF_GATEUP: gate and up columns side by side, SwiGLU epilogue into abuf;
 // PF_UP:     the up projection of a non-gated expert, relu^2 epilogue into abuf;
-// PF_DOWN:   the down projection, fp32 rows into ybuf.
+// PF_DOWN:   the down projection, 24-bit packed rows into ybuf.
 enum { PF_GATEUP = 0, PF_DOWN = 1, PF_UP = 2 };
 
 // silu(g) * u with the hardware reciprocal (about 1 ulp) in place of an IEEE
@@ -614,6 +616,55 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
     //      with 16-byte LDS reads, all before the first store, so the stores
     //      do not wait on LDS one row at a time; down: row m goes to sorted
     //      row p0 + m.
+    if constexpr (MODE == PF_DOWN) {
+        // Down: the tile's rows are the sorted rows p0 .. p0 + rows_here - 1,
+        // written as 24-bit values in two planes per row (the upper 16 bits
+        // at byte 2*col, the low 8 bits at byte 2*H + col; row stride 3*H;
+        // the combine widens them and multiplies by the affinity).  The MFMA
+        // layout gives a lane one column of many rows, so each 32-row slab of
+        // a wave tile goes through LDS (the stage buffers, free once every
+        // wave has left the K loop): a lane then holds 8 consecutive columns
+        // of one row and writes one 16-byte and one 8-byte streaming store,
+        // 16 lanes covering a row's 128 columns (256 + 128 contiguous bytes).
+        static_assert(!C::M16 && C::MS == 32 && C::WCOLS == 128 && C::MT * 32 == C::WROWS,
+                      "down epilogue: 64 x 128 wave tiles of 32 x 32 MFMAs");
+        static_assert(C::WAVES * 32 * 128 * 4 <= C::STAGES * C::STAGE, "slabs fit the stages");
+        __syncthreads();  // every wave is done reading the K stages
+        float* slab = reinterpret_cast<float*>(smem) + wave * (32 * 128);
+        uint8_t* ybytes = reinterpret_cast<uint8_t*>(ybuf);
+        const size_t rowb = (size_t)H * 3;
+        const int col0 = nb * BN + wn * C::WCOLS;  // first column of the wave tile
+        const float sc = seff[0];
+#pragma unroll
+        for (int mt = 0; mt < C::MT; ++mt) {
+#pragma unroll
+            for (int nt = 0; nt < C::NT; ++nt)
+#pragma unroll
+                for (int i = 0; i < AR; ++i)
+                    slab[(8 * (i >> 2) + 4 * lg + (i & 3)) * 128 + nt * 32 + ln] = acc[mt][nt][i] * sc;
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the slab is written
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int r = 4 * q + (lane >> 4);   // row of the slab
+                const int c = 8 * (lane & 15);       // the lane's first column
+                const int m = wm * C::WROWS + mt * 32 + r;  // row of the tile
+                const f32x4 v0 = *reinterpret_cast<const f32x4*>(slab + r * 128 + c);
+                const f32x4 v1 = *reinterpret_cast<const f32x4*>(slab + r * 128 + c + 4);
+                if (m < rows_here) {
+                    u32x4 hi;
+                    u32x2 lo;
+                    split_f24x8(v0, v1, hi, lo);
+                    uint8_t* rowp = ybytes + (size_t)(p0 + m) * rowb;
+                    __builtin_nontemporal_store(hi, reinterpret_cast<u32x4*>(rowp + 2 * (size_t)(col0 + c)));
+                    __builtin_nontemporal_store(lo, reinterpret_cast<u32x2*>(rowp + 2 * (size_t)H + col0 + c));
+                }
+            }
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // the slab is read before it is rewritten
+            __builtin_amdgcn_wave_barrier();
+        }
+        return;
+    }
     constexpr int RQ = AR / 4;                   // groups of four rows per MFMA tile
     const int ocol = C::M16 ? l16 : ln;          // the lane's column in a tile
     int4 dst4[C::MT][RQ];
@@ -653,14 +704,6 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
 #pragma unroll
                 for (int nt = 0; nt < C::NT; ++nt)
                     orow[nt * C::MS] = f32_to_bf16_bits(relu2(acc[mt][nt][i] * s0));
-            } else {
-                // y of the route (the combine multiplies it by the affinity);
-                // each contribution row is read once, by the combine: streaming
-                // (non-temporal) stores keep it from occupying the caches
-                float* orow = ybuf + (size_t)dst * H + nb * BN + wn * C::WCOLS + ocol;
-#pragma unroll
-                for (int nt = 0; nt < C::NT; ++nt)
-                    __builtin_nontemporal_store(acc[mt][nt][i] * seff[0], orow + nt * C::MS);
             }
         }
 }
