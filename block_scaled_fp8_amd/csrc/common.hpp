@@ -74,37 +74,34 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
 
 // ---------------------------------------------------------------- SwiGLU
 // silu(g) * u with silu(g) = g / (1 + exp(-g)).
-// Prefill contributions leave the down GEMM as the top 24 bits of their fp32
-// value (sign, 8-bit exponent, 15 fraction bits: 16 significant bits), rounded
-// to nearest even: at most 2^-17 relative, far below the bf16 rounding of the
-// activations that feed the same GEMM.  A row of H values is stored as two
-// planes: the upper 16 bits of each value (2*H bytes), then the low 8 bits
-// (H bytes), so that a lane's run of consecutive values is one contiguous
-// piece in each plane.  (Finite inputs only.)
-__device__ __forceinline__ uint32_t f32_to_f24_bits(float f) {
-    const uint32_t u = __float_as_uint(f);
-    return (u + 0x7Fu + ((u >> 8) & 1u)) >> 8;
-}
-// 8 values -> hi plane (4 words: value j in bits 16*(j%2) of word j/2) and
-// lo plane (2 words: value j in bits 8*(j%4) of word j/4)
-__device__ __forceinline__ void split_f24x8(f32x4 a, f32x4 b, u32x4& hi, u32x2& lo) {
-    uint32_t w[8];
+// Prefill contributions leave the down GEMM in a block floating-point form:
+// each run of 8 consecutive values of a row shares one exponent byte ex (the
+// fp32 exponent field of the run's largest magnitude) and each value keeps a
+// 16-bit signed mantissa m = rint(v * 2^(141 - ex)) saturated to |m| <= 32767,
+// so that v = m * 2^(ex - 141) to within 2^-15 of the run's largest magnitude
+// (2^-14 where the rounding saturates).  A row
+// of H values is a mantissa plane (2*H bytes) then an exponent plane (H/8
+// bytes).  (Finite inputs only.)
+__device__ __forceinline__ void bfp16x8_encode(f32x4 a, f32x4 b, u32x4& mant, uint32_t& ex) {
+    float amax = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        w[j] = f32_to_f24_bits(a[j]);
-        w[4 + j] = f32_to_f24_bits(b[j]);
+    for (int j = 0; j < 4; ++j) amax = fmaxf(amax, fmaxf(fabsf(a[j]), fabsf(b[j])));
+    ex = (__float_as_uint(amax) >> 23) & 0xFFu;
+    const int sh = 141 - (int)ex;
+    uint32_t m[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const float v = j < 4 ? a[j] : b[j - 4];
+        const float q = fminf(fmaxf(rintf(ldexpf(v, sh)), -32767.0f), 32767.0f);
+        m[j] = (uint32_t)(int32_t)q & 0xFFFFu;
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) hi[j] = (w[2 * j] >> 8) | ((w[2 * j + 1] >> 8) << 16);
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-        lo[j] = (w[4 * j] & 0xFFu) | ((w[4 * j + 1] & 0xFFu) << 8) | ((w[4 * j + 2] & 0xFFu) << 16) |
-                ((w[4 * j + 3] & 0xFFu) << 24);
+    for (int j = 0; j < 4; ++j) mant[j] = m[2 * j] | (m[2 * j + 1] << 16);
 }
-__device__ __forceinline__ float join_f24(u32x4 hi, u32x2 lo, int j) {
-    const uint32_t h16 = (hi[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
-    const uint32_t l8 = (lo[j >> 2] >> (8 * (j & 3))) & 0xFFu;
-    return __uint_as_float((h16 << 16) | (l8 << 8));
+// value j of a run: the sign-extended 16-bit mantissa times 2^(ex - 141)
+__device__ __forceinline__ float bfp16_value(u32x4 mant, uint32_t ex, int j) {
+    const int m = (int)(int16_t)((mant[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
+    return ldexpf((float)m, (int)ex - 141);
 }
 
 __device__ __forceinline__ float swiglu(float g, float u) {

@@ -299,11 +299,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 }
 
 // Prefill form: the producers write y of route r (no affinity) at its sorted
-// row inv_route[r] as 24-bit values in two planes per row (upper 16 bits at
-// byte 2*col, low 8 bits at byte 2*H + col; row stride 3*H; the shared row of
-// token t is row R + t).  A thread owns 8 columns (a 16-byte and an 8-byte
-// load per row), widens them to fp32 and adds aff[r] * y over the slots in
-// order, eight slots' loads in flight at a time, then the shared row.
+// row inv_route[r] in the block floating-point form of bfp16x8_encode (16-bit
+// mantissas at byte 2*col, one exponent byte per 8 columns at byte
+// 2*H + col/8; row stride 2*H + H/8; the shared row of token t is row R + t).
+// A thread owns one run of 8 columns (a 16-byte and a 1-byte load per row),
+// widens it to fp32 and adds aff[r] * y over the slots in order, eight slots'
+// loads in flight at a time, then the shared row.
 constexpr int COMBINE_G_THREADS = 256;
 __global__ __launch_bounds__(COMBINE_G_THREADS) void combine_gather_kernel(
     const uint8_t* __restrict__ ybytes, const int32_t* __restrict__ ids,
@@ -313,11 +314,11 @@ __global__ __launch_bounds__(COMBINE_G_THREADS) void combine_gather_kernel(
     const int t = blockIdx.y;
     const int h = (blockIdx.x * COMBINE_G_THREADS + threadIdx.x) * 8;
     if (h >= H) return;
-    const size_t rowb = (size_t)H * 3;
-    auto load_row = [&](size_t row, u32x4& hi, u32x2& lo) {
+    const size_t rowb = (size_t)H * 2 + (size_t)(H / 8);
+    auto load_row = [&](size_t row, u32x4& mant, uint32_t& ex) {
         const uint8_t* p = ybytes + row * rowb;
-        hi = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + 2 * (size_t)h));
-        lo = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p + 2 * (size_t)H + h));
+        mant = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + 2 * (size_t)h));
+        ex = __builtin_nontemporal_load(p + 2 * (size_t)H + h / 8);
     };
     float sum[8];
 #pragma unroll
@@ -325,7 +326,7 @@ __global__ __launch_bounds__(COMBINE_G_THREADS) void combine_gather_kernel(
     bool bad = false;
     for (int j0 = 0; j0 < k; j0 += G) {
         u32x4 vh[G];
-        u32x2 vl[G];
+        uint32_t vl[G];
         int id[G];
         float a[G];
 #pragma unroll
@@ -344,16 +345,16 @@ __global__ __launch_bounds__(COMBINE_G_THREADS) void combine_gather_kernel(
                 const bool ok = id[j] >= 0 && id[j] < E;  // an invalid id's route is dropped
                 bad |= !ok;
 #pragma unroll
-                for (int c = 0; c < 8; ++c) sum[c] += ok ? a[j] * join_f24(vh[j], vl[j], c) : 0.0f;
+                for (int c = 0; c < 8; ++c) sum[c] += ok ? a[j] * bfp16_value(vh[j], vl[j], c) : 0.0f;
             }
         }
     }
     if (has_shared) {
         u32x4 sh;
-        u32x2 sl;
-        load_row((size_t)T * k + t, sh, sl);
+        uint32_t se;
+        load_row((size_t)T * k + t, sh, se);
 #pragma unroll
-        for (int c = 0; c < 8; ++c) sum[c] += join_f24(sh, sl, c);
+        for (int c = 0; c < 8; ++c) sum[c] += bfp16_value(sh, se, c);
     }
     if (bad && status && h == 0) atomicOr(status, MOE_STATUS_BAD_EXPERT_ID);
     f32x4* o = reinterpret_cast<f32x4*>(out + (size_t)t * H + h);

@@ -15,8 +15,9 @@
 // (128 gate + 128 up) tile of one segment, applies SwiGLU in registers and
 // writes bf16 activations (abuf, sorted row order).  Kernel 2 (down): each
 // workgroup computes a 128-row x 256-column tile of y = a W2^T and writes its
-// rows at their sorted position (a tile's rows are contiguous) as 24-bit
-// values, the top 24 bits of fp32 rounded to nearest even; the final combine
+// rows at their sorted position (a tile's rows are contiguous) in a block
+// floating-point form (8 values share an exponent byte, 16-bit mantissas:
+// common.hpp, bfp16x8_encode); the final combine
 // gathers the k rows of a token through the inverse route map, widens them
 // and applies the affinities in fp32.
 //
@@ -123,7 +124,7 @@ int prefill_supported(int H, int I, int act) {
 
 // PF_GATEUP: gate and up columns side by side, SwiGLU epilogue into abuf;
 // PF_UP:     the up projection of a non-gated expert, relu^2 epilogue into abuf;
-// PF_DOWN:   the down projection, 24-bit packed rows into ybuf.
+// PF_DOWN:   the down projection, block floating-point rows into ybuf.
 enum { PF_GATEUP = 0, PF_DOWN = 1, PF_UP = 2 };
 
 // silu(g) * u with the hardware reciprocal (about 1 ulp) in place of an IEEE
@@ -618,21 +619,22 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
     //      row p0 + m.
     if constexpr (MODE == PF_DOWN) {
         // Down: the tile's rows are the sorted rows p0 .. p0 + rows_here - 1,
-        // written as 24-bit values in two planes per row (the upper 16 bits
-        // at byte 2*col, the low 8 bits at byte 2*H + col; row stride 3*H;
-        // the combine widens them and multiplies by the affinity).  The MFMA
-        // layout gives a lane one column of many rows, so each 32-row slab of
-        // a wave tile goes through LDS (the stage buffers, free once every
-        // wave has left the K loop): a lane then holds 8 consecutive columns
-        // of one row and writes one 16-byte and one 8-byte streaming store,
-        // 16 lanes covering a row's 128 columns (256 + 128 contiguous bytes).
+        // written in the block floating-point form of bfp16x8_encode (16-bit
+        // mantissas at byte 2*col, one exponent byte per 8 columns at byte
+        // 2*H + col/8; row stride 2*H + H/8; the combine widens them and
+        // multiplies by the affinity).  The MFMA layout gives a lane one
+        // column of many rows, so each 32-row slab of a wave tile goes through
+        // LDS (the stage buffers, free once every wave has left the K loop): a
+        // lane then holds 8 consecutive columns of one row, encodes them as
+        // one run and writes a 16-byte and a 1-byte streaming store, 16 lanes
+        // covering a row's 128 columns (256 + 16 contiguous bytes).
         static_assert(!C::M16 && C::MS == 32 && C::WCOLS == 128 && C::MT * 32 == C::WROWS,
                       "down epilogue: 64 x 128 wave tiles of 32 x 32 MFMAs");
         static_assert(C::WAVES * 32 * 128 * 4 <= C::STAGES * C::STAGE, "slabs fit the stages");
         __syncthreads();  // every wave is done reading the K stages
         float* slab = reinterpret_cast<float*>(smem) + wave * (32 * 128);
         uint8_t* ybytes = reinterpret_cast<uint8_t*>(ybuf);
-        const size_t rowb = (size_t)H * 3;
+        const size_t rowb = (size_t)H * 2 + (size_t)(H / 8);
         const int col0 = nb * BN + wn * C::WCOLS;  // first column of the wave tile
         const float sc = seff[0];
 #pragma unroll
@@ -652,12 +654,12 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
                 const f32x4 v0 = *reinterpret_cast<const f32x4*>(slab + r * 128 + c);
                 const f32x4 v1 = *reinterpret_cast<const f32x4*>(slab + r * 128 + c + 4);
                 if (m < rows_here) {
-                    u32x4 hi;
-                    u32x2 lo;
-                    split_f24x8(v0, v1, hi, lo);
+                    u32x4 mant;
+                    uint32_t ex;
+                    bfp16x8_encode(v0, v1, mant, ex);
                     uint8_t* rowp = ybytes + (size_t)(p0 + m) * rowb;
-                    __builtin_nontemporal_store(hi, reinterpret_cast<u32x4*>(rowp + 2 * (size_t)(col0 + c)));
-                    __builtin_nontemporal_store(lo, reinterpret_cast<u32x2*>(rowp + 2 * (size_t)H + col0 + c));
+                    __builtin_nontemporal_store(mant, reinterpret_cast<u32x4*>(rowp + 2 * (size_t)(col0 + c)));
+                    __builtin_nontemporal_store((uint8_t)ex, rowp + 2 * (size_t)H + (col0 + c) / 8);
                 }
             }
             __builtin_amdgcn_s_waitcnt(0xC07F);  // the slab is read before it is rewritten

@@ -69,9 +69,9 @@ int launch_decode_ffn(int layout, const uint16_t* x, const uint8_t* w13, const f
                       const float* aff, int T, int H, int I, int E, int k, uint16_t* abuf,
                       float* ybuf, int act, hipStream_t stream);
 // Writes y (without the affinity) of every route at its sorted row of ybuf,
-// as 24-bit values (the top 24 bits of fp32, round to nearest even) in two
-// planes per row: upper 16 bits at byte 2*col, low 8 bits at byte 2*H + col,
-// row stride 3*H bytes.
+// in a block floating-point form: 16-bit mantissas at byte 2*col and one
+// exponent byte per run of 8 columns at byte 2*H + col/8, row stride
+// 2*H + H/8 bytes (common.hpp, bfp16x8_encode).
 int launch_prefill_ffn(int layout, const uint16_t* x, const uint8_t* w13, const float* w13s,
                        const uint8_t* w2, const float* w2s, const SharedW& sh, const Plan& plan,
                        int T, int H, int I, int E, int k, uint16_t* abuf, float* ybuf, int act,
@@ -87,8 +87,8 @@ int prefill_supported(int H, int I, int act);
 int prefill_check(int T, int H, int I, int E, int k, int has_shared, int act);
 // Sums, per token, the k route rows whose id is valid (plus the shared row at
 // R + t).  Decode producers write aff * y at row r (inv_route and aff null);
-// prefill producers write y at the route's sorted position in the 24-bit
-// layout of launch_prefill_ffn, and the sum takes aff[r] * y widened to fp32.
+// prefill producers write y at the route's sorted position in the block
+// floating-point layout of launch_prefill_ffn, and the sum takes aff[r] * y widened to fp32.
 // Ids outside [0, E) set
 // MOE_STATUS_BAD_EXPERT_ID in *status (if not NULL).
 int launch_combine(const float* ybuf, const int32_t* ids, const int32_t* inv_route,
