@@ -48,10 +48,9 @@
 //    last round of workgroups holds the cheap partial tiles, whose empty
 //    MFMA row groups (16 rows gate/up, 32 down) are skipped.  The grid covers
 //    the worst case and idle workgroups exit.
-//  * Epilogue: gate/up reads a lane's row-table entries with 16-byte LDS
-//    reads before any store, applies SwiGLU and stores bf16; down turns its
-//    accumulators into row pieces through LDS and stores them packed with
-//    non-temporal stores.
+//  * Epilogue: gate/up applies SwiGLU (up: relu^2) and down encodes its
+//    contributions; both turn the accumulators into row pieces through LDS
+//    so that a lane stores 16 contiguous bytes of a row.
 #include <algorithm>
 #include <type_traits>
 
@@ -180,7 +179,6 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
     constexpr int BM = C::BM, BN = C::BN;
     extern __shared__ __attribute__((aligned(16))) char smem[];
     __shared__ int row_tok[BM];  // gate/up: token row of x
-    __shared__ __attribute__((aligned(16))) int row_dst[BM];  // gate/up: output row, -1 if padding
     __shared__ __attribute__((aligned(16))) float row_xs[C::A8 ? BM : 1];  // A8: the row's x scale
 
     // ---- which tile.  Workgroups are dealt round-robin over the 8 XCDs
@@ -226,7 +224,6 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
             const int p = p0 + tid;
             const bool valid = tid < rows_here;
             row_tok[tid] = valid ? (e >= 0 ? plan.sorted_route[p] / k : p - R) : 0;
-            row_dst[tid] = valid ? p : -1;
             if constexpr (C::A8) row_xs[tid] = valid ? xscale[row_tok[tid]] : 0.0f;
         }
         __syncthreads();
@@ -612,11 +609,10 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
 
     // ---- epilogue.  Accumulator layouts: 32x32 -- lane l holds column l%32
     //      and, for register i, row 8*(i/4) + 4*(l/32) + i%4; 16x16 -- column
-    //      l%16, row 4*(l/16) + i.  Gate/up: the row table entries of a lane's
-    //      rows (four consecutive rows per group of four registers) are read
-    //      with 16-byte LDS reads, all before the first store, so the stores
-    //      do not wait on LDS one row at a time; down: row m goes to sorted
-    //      row p0 + m.
+    //      l%16, row 4*(l/16) + i.  Row m of the tile goes to sorted row p0 + m
+    //      (m < rows_here).  Both epilogues pass a wave tile's results through
+    //      LDS (the stage buffers, free once every wave has left the K loop) so
+    //      that a lane stores a run of consecutive columns of one row.
     if constexpr (MODE == PF_DOWN) {
         // Down: the tile's rows are the sorted rows p0 .. p0 + rows_here - 1,
         // written in the block floating-point form of bfp16x8_encode (16-bit
@@ -667,47 +663,49 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
         }
         return;
     }
-    constexpr int RQ = AR / 4;                   // groups of four rows per MFMA tile
-    const int ocol = C::M16 ? l16 : ln;          // the lane's column in a tile
-    int4 dst4[C::MT][RQ];
-    float4 xs4[C::A8 ? C::MT : 1][C::A8 ? RQ : 1];  // A8: the x scales of those rows
-#pragma unroll
-    for (int mt = 0; mt < C::MT; ++mt)
-#pragma unroll
-        for (int q = 0; q < RQ; ++q) {
-            const int r0 = wm * C::WROWS + mt * C::MS + (C::M16 ? 4 * g16 : 8 * q + 4 * lg);
-            if constexpr (C::A8) xs4[mt][q] = *reinterpret_cast<const float4*>(row_xs + r0);
-            if (GATHER) {
-                dst4[mt][q] = *reinterpret_cast<const int4*>(row_dst + r0);
-            } else {
-#pragma unroll
-                for (int c = 0; c < 4; ++c) dst4[mt][q][c] = r0 + c < rows_here ? p0 + r0 + c : -1;
-            }
-        }
+    // Gate/up (SwiGLU of the paired gate and up columns) and up (relu^2):
+    // bf16 activations, OUTC per wave row, into the wave's slab, then 8
+    // consecutive columns (16 bytes) per lane and store, OUTC/8 lanes per row.
+    constexpr int OUTC = MODE == PF_GATEUP ? C::WCOLS / 2 : C::WCOLS;
+    constexpr int LPR = OUTC / 8;              // lanes per row
+    constexpr int RPS = MOE_WAVE / LPR;        // rows per store step
+    static_assert(C::WAVES * C::WROWS * OUTC * 2 <= C::STAGES * C::STAGE, "slabs fit the stages");
+    __syncthreads();  // every wave is done reading the K stages
+    uint16_t* slab = reinterpret_cast<uint16_t*>(smem) + wave * (C::WROWS * OUTC);
+    const int ocol = C::M16 ? l16 : ln;  // the lane's column in an MFMA tile
 #pragma unroll
     for (int mt = 0; mt < C::MT; ++mt)
 #pragma unroll
         for (int i = 0; i < AR; ++i) {
-            const int dst = dst4[mt][i >> 2][i & 3];
-            if (dst < 0) continue;
+            const int r = mt * C::MS + (C::M16 ? 4 * g16 + i : 8 * (i >> 2) + 4 * lg + (i & 3));
             // A8: the row's activation scale joins the weight block's
             float xsv = 1.0f;
-            if constexpr (C::A8) xsv = xs4[mt][i >> 2][i & 3];
-            if (MODE == PF_GATEUP) {
-                uint16_t* orow = abuf_out + (size_t)dst * I + nb * (BN / 2) + wn * (C::WCOLS / 2) + ocol;
+            if constexpr (C::A8) xsv = row_xs[wm * C::WROWS + r];
+            if constexpr (MODE == PF_GATEUP) {
                 const float s0 = seff[0] * xsv, s1 = seff[1] * xsv;
 #pragma unroll
                 for (int nt = 0; nt < C::NT / 2; ++nt)
-                    orow[nt * C::MS] = f32_to_bf16_bits(
+                    slab[r * OUTC + nt * C::MS + ocol] = f32_to_bf16_bits(
                         swiglu_fast(acc[mt][nt][i] * s0, acc[mt][nt + C::NT / 2][i] * s1));
-            } else if (MODE == PF_UP) {
-                uint16_t* orow = abuf_out + (size_t)dst * I + nb * BN + wn * C::WCOLS + ocol;
+            } else {
                 const float s0 = seff[0] * xsv;
 #pragma unroll
                 for (int nt = 0; nt < C::NT; ++nt)
-                    orow[nt * C::MS] = f32_to_bf16_bits(relu2(acc[mt][nt][i] * s0));
+                    slab[r * OUTC + nt * C::MS + ocol] = f32_to_bf16_bits(relu2(acc[mt][nt][i] * s0));
             }
         }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the slab is written
+    __builtin_amdgcn_wave_barrier();
+    const int colbase = MODE == PF_GATEUP ? nb * (BN / 2) + wn * (C::WCOLS / 2) : nb * BN + wn * C::WCOLS;
+#pragma unroll
+    for (int q = 0; q < C::WROWS / RPS; ++q) {
+        const int r = q * RPS + lane / LPR;
+        const int c = 8 * (lane % LPR);
+        const int m = wm * C::WROWS + r;  // row of the tile
+        const u32x4 v = *reinterpret_cast<const u32x4*>(slab + r * OUTC + c);
+        if (m < rows_here)
+            *reinterpret_cast<u32x4*>(abuf_out + (size_t)(p0 + m) * I + colbase + c) = v;
+    }
 }
 
 template <int MODE>
