@@ -520,13 +520,17 @@ def test_variants_agree(layout):
     assert np.max(np.abs(d - p)) <= 2e-2 * rms
 
 
-def test_graph_replay_with_changing_routes():
+@pytest.mark.parametrize("variant", ["auto", "prefill", "prefill_a8"])
+def test_graph_replay_with_changing_routes(variant):
     """Capture route + fused once; replay with new logits and zero routing
-    weights and compare every replay with the eager result."""
+    weights and compare every replay with the eager result (auto: the split
+    decode kernels at this size; prefill: the grouped GEMMs, compact
+    contributions and gather combine; prefill_a8: with x quantised)."""
     cfg = synth.MoeConfig("g", T=48, H=512, I=256, E=32, k=4)
     c = gpu_case(cfg, seed=9)
     logits = c["logits"].clone()
-    ws = torch.empty(binding.fused_workspace_bytes(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k),
+    ws = torch.empty(binding.fused_workspace_bytes(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k,
+                                                   variant=variant),
                      dtype=torch.uint8, device="cuda")
     out = torch.empty((cfg.T, cfg.H), dtype=torch.float32, device="cuda")
     scale_aff = torch.ones(1, device="cuda")
@@ -534,7 +538,7 @@ def test_graph_replay_with_changing_routes():
     def step():
         ids, aff = binding.route(logits, cfg.k)
         binding.fused_w8a16(c["x"], c["w13"], c["w13_scale"], c["w2"], c["w2_scale"], ids,
-                            aff * scale_aff, out=out, ws=ws)
+                            aff * scale_aff, out=out, ws=ws, variant=variant)
 
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -558,8 +562,10 @@ def test_graph_replay_with_changing_routes():
             assert torch.all(got == 0)
         else:
             ref_ids, ref_aff = oracle.route_softmax_topk(np_(logits), cfg.k)
-            ref = oracle_rows(c, ref_ids, ref_aff, np.arange(cfg.T))
-            assert_out_close(np_(got), ref, what=f"graph replay {rep}")
+            rows = np.arange(cfg.T)
+            xr = _xhat_rows(c, rows) if variant == "prefill_a8" else None
+            ref = oracle_rows(c, ref_ids, ref_aff, rows, xrows=xr)
+            assert_out_close(np_(got), ref, what=f"graph replay {variant} {rep}")
 
 
 # ------------------------------------------------------------ fp8 activations
