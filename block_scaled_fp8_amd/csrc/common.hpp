@@ -69,7 +69,9 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
     uint32_t u = __float_as_uint(f);
     uint32_t r = u + 0x7FFFu + ((u >> 16) & 1u);
-    return (uint16_t)(r >> 16);
+    // a NaN stays a (quiet) NaN: rounding its payload could carry into the
+    // exponent or the sign
+    return (u & 0x7FFFFFFFu) > 0x7F800000u ? (uint16_t)((u >> 16) | 0x0040u) : (uint16_t)(r >> 16);
 }
 
 // ---------------------------------------------------------------- SwiGLU
@@ -79,9 +81,10 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
 // fp32 exponent field of the run's largest magnitude) and each value keeps a
 // 16-bit signed mantissa m = rint(v * 2^(141 - ex)) saturated to |m| <= 32767,
 // so that v = m * 2^(ex - 141) to within 2^-15 of the run's largest magnitude
-// (2^-14 where the rounding saturates).  A row
-// of H values is a mantissa plane (2*H bytes) then an exponent plane (H/8
-// bytes).  (Finite inputs only.)
+// (2^-14 where the rounding saturates).  A row of H values is a mantissa
+// plane (2*H bytes) then an exponent plane (H/8 bytes).  Non-finite values
+// stay non-finite: the unused mantissa -32768 marks a NaN, and an infinity
+// sets the run's exponent to 255, whose saturated mantissa decodes to inf.
 __device__ __forceinline__ void bfp16x8_encode(f32x4 a, f32x4 b, u32x4& mant, uint32_t& ex) {
     float amax = 0.0f;
 #pragma unroll
@@ -93,7 +96,7 @@ __device__ __forceinline__ void bfp16x8_encode(f32x4 a, f32x4 b, u32x4& mant, ui
     for (int j = 0; j < 8; ++j) {
         const float v = j < 4 ? a[j] : b[j - 4];
         const float q = fminf(fmaxf(rintf(ldexpf(v, sh)), -32767.0f), 32767.0f);
-        m[j] = (uint32_t)(int32_t)q & 0xFFFFu;
+        m[j] = v != v ? 0x8000u : (uint32_t)(int32_t)q & 0xFFFFu;
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) mant[j] = m[2 * j] | (m[2 * j + 1] << 16);
@@ -101,7 +104,7 @@ __device__ __forceinline__ void bfp16x8_encode(f32x4 a, f32x4 b, u32x4& mant, ui
 // value j of a run: the sign-extended 16-bit mantissa times 2^(ex - 141)
 __device__ __forceinline__ float bfp16_value(u32x4 mant, uint32_t ex, int j) {
     const int m = (int)(int16_t)((mant[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
-    return ldexpf((float)m, (int)ex - 141);
+    return m == -32768 ? __builtin_nanf("") : ldexpf((float)m, (int)ex - 141);
 }
 
 __device__ __forceinline__ float swiglu(float g, float u) {

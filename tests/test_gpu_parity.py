@@ -500,6 +500,26 @@ def test_fused_bad_ids_are_dropped():
     assert_out_close(np_(out), ref, what="bad ids dropped")
 
 
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_fused_nan_activation_row(variant, layout):
+    """A NaN in one token's activations makes that token's whole output row
+    NaN, as the float64 oracle's does, through the fp32 decode rows and the
+    prefill's compact contributions alike; every other row still matches."""
+    cfg = synth.MoeConfig("nan", T=40, H=512, I=256, E=16, k=4, shared=True)
+    c = gpu_case(cfg, seed=21)
+    t0 = 7
+    c["x"][t0, 100] = float("nan")
+    ids, aff = binding.route(c["logits"], cfg.k)
+    out = np_(_fused(c, ids, aff, variant=variant, layout=layout))
+    torch.cuda.synchronize()
+    ref_ids, ref_aff = oracle.route_softmax_topk(np_(c["logits"]), cfg.k)
+    assert np.all(np.isnan(oracle_rows(c, ref_ids, ref_aff, np.array([t0]))))
+    assert np.all(np.isnan(out[t0])), f"{variant}: {int(np.sum(~np.isnan(out[t0])))} non-NaN values"
+    rows = np.array([t for t in range(cfg.T) if t != t0])
+    assert_out_close(out[rows], oracle_rows(c, ref_ids, ref_aff, rows), what=f"nan row {variant}")
+
+
 @pytest.mark.parametrize("variant", VARIANTS)
 def test_fused_is_deterministic(variant):
     c = _case("decode512")
