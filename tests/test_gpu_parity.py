@@ -481,7 +481,11 @@ def test_empty_batch_on_device(variant):
     assert tuple(out.shape) == (0, cfg.H)
 
 
-def test_fused_bad_ids_are_dropped():
+@pytest.mark.parametrize("variant", ["auto", "prefill", "prefill_a8"])
+def test_fused_bad_ids_are_dropped(variant):
+    """An id outside [0, E) drops its route and sets the status bit (auto: the
+    decode path at this size; prefill: through the inverse route map and the
+    compact contributions)."""
     cfg = synth.MoeConfig("bad", T=6, H=256, I=128, E=8, k=2)
     c = gpu_case(cfg, seed=8)
     ids_np = synth.random_ids(cfg.T, 2, 8, seed=8).numpy()
@@ -489,15 +493,17 @@ def test_fused_bad_ids_are_dropped():
     ids_np[2, 1] = 99
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
     out = _fused(c, torch.from_numpy(ids_np).cuda(), torch.from_numpy(aff_np).cuda(),
-                 status=status)
+                 status=status, variant=variant)
     torch.cuda.synchronize()
     assert int(status.item()) & binding.MOE_STATUS_BAD_EXPERT_ID
     aff_ref = aff_np.copy()
     aff_ref[2, 1] = 0.0
     ids_ref = ids_np.copy()
     ids_ref[2, 1] = 0
-    ref = oracle_rows(c, ids_ref, aff_ref, np.arange(cfg.T))
-    assert_out_close(np_(out), ref, what="bad ids dropped")
+    rows = np.arange(cfg.T)
+    xr = _xhat_rows(c, rows) if variant == "prefill_a8" else None
+    ref = oracle_rows(c, ids_ref, aff_ref, rows, xrows=xr)
+    assert_out_close(np_(out), ref, what=f"bad ids dropped ({variant})")
 
 
 @pytest.mark.parametrize("layout", LAYOUTS)
