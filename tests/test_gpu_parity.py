@@ -275,7 +275,7 @@ def test_sort_parity(name):
 
 @pytest.mark.parametrize("T,k,E", [(1, 1, 1), (1, 8, 256), (37, 3, 7), (2048, 8, 256),
                                    (2049, 8, 256), (4096, 4, 1024), (5000, 10, 512),
-                                   (16384, 1, 3)])
+                                   (16384, 1, 3), (4097, 1, 64), (1025, 4, 33)])
 def test_sort_random_ids(T, k, E):
     ids_np = synth.random_ids(T, k, E, seed=T + k, distinct=False).numpy()
     _check_sort(ids_np, E, binding.sort(torch.from_numpy(ids_np).cuda(), E))
