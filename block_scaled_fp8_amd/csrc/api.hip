@@ -38,9 +38,14 @@ struct FusedLayout {
         seg_tile0, tile_info, tile_n, sort_scratch, abuf, ybuf, xq, xs, total;
 };
 
-// (fp8 activations: the E4M3 codes and per-token scales of x are appended)
-static FusedLayout fused_layout(int T, int H, int I, int E, int k, int has_shared,
-                                bool fp8_x = false) {
+// The pieces before ybuf do not depend on the variant.  ybuf holds one
+// contribution row per route (+ shared rows + a trash row): fp32 for the
+// decode variant, block floating point (2 bytes a value + one exponent byte
+// per 8) for the prefill ones; AUTO is sized for either.  The fp8-activation
+// variant appends the E4M3 codes and per-token scales of x.
+static FusedLayout fused_layout(int T, int H, int I, int E, int k, int has_shared, int variant) {
+    const bool fp8_x = variant == MOE_VARIANT_PREFILL_A8;
+    const bool compact = variant == MOE_VARIANT_PREFILL || fp8_x;
     FusedLayout L;
     const size_t R = (size_t)T * k;
     const size_t rows = R + (has_shared ? (size_t)T : 0);
@@ -66,7 +71,8 @@ static FusedLayout fused_layout(int T, int H, int I, int E, int k, int has_share
     L.tile_n = take(sizeof(int32_t));
     L.sort_scratch = take(sort_scratch_bytes((int)R, E));
     L.abuf = take(sizeof(uint16_t) * rows * I);
-    L.ybuf = take(sizeof(float) * (rows + 1) * H);  // + one trash row for padded stores
+    const size_t yrow = compact ? 2 * (size_t)H + (size_t)H / 8 : sizeof(float) * (size_t)H;
+    L.ybuf = take(yrow * (rows + 1));  // + one trash row for padded stores
     L.xq = fp8_x ? take((size_t)T * H) : 0;
     L.xs = fp8_x ? take(sizeof(float) * (size_t)T) : 0;
     L.total = o;
@@ -207,7 +213,8 @@ int moe_sort(const int32_t* ids, int T, int k, int E, int32_t* counts, int32_t* 
 size_t moe_fused_workspace_bytes(int T, int H, int I, int E, int k, int has_shared,
                                  int variant) {
     if (T < 0 || H < 1 || I < 1 || E < 1 || k < 1) return 0;
-    return fused_layout(T, H, I, E, k, has_shared ? 1 : 0, variant == MOE_VARIANT_PREFILL_A8).total;
+    if (variant < MOE_VARIANT_AUTO || variant > MOE_VARIANT_PREFILL_A8) return 0;
+    return fused_layout(T, H, I, E, k, has_shared ? 1 : 0, variant).total;
 }
 
 int moe_fused_w8a16_ex(const void* x, const uint8_t* w13, const float* w13_scale,
@@ -252,13 +259,24 @@ int moe_fused_w8a16_ex(const void* x, const uint8_t* w13, const float* w13_scale
         set_error("moe_fused_w8a16: out must not alias x");
         return MOE_EINVAL;
     }
+    // 16-byte vector loads and stores (and direct-to-LDS loads) on x, the
+    // weights, out and the workspace; 4-byte ones on the scales, ids and aff
+    {
+        uintptr_t a16 = (uintptr_t)x | (uintptr_t)w13 | (uintptr_t)w2 | (uintptr_t)out |
+                        (uintptr_t)ws;
+        uintptr_t a4 = (uintptr_t)w13_scale | (uintptr_t)w2_scale | (uintptr_t)ids | (uintptr_t)aff;
+        if (shared) {
+            a16 |= (uintptr_t)shared->w13 | (uintptr_t)shared->w2;
+            a4 |= (uintptr_t)shared->w13_scale | (uintptr_t)shared->w2_scale;
+        }
+        if ((a16 & 15) || (a4 & 3)) {
+            set_error("moe_fused_w8a16: x, w13, w2, out and ws must be 16-byte aligned, the "
+                      "scales, ids and aff 4-byte aligned");
+            return MOE_EINVAL;
+        }
+    }
     const int has_shared = shared ? 1 : 0;
     const bool fp8_x = variant == MOE_VARIANT_PREFILL_A8;
-    const FusedLayout L = fused_layout(T, H, I, E, k, has_shared, fp8_x);
-    if (!ws || ws_bytes < L.total) {
-        set_error("moe_fused_w8a16: workspace of %zu bytes needed (got %zu)", L.total, ws_bytes);
-        return MOE_EINVAL;
-    }
     // AUTO: the decode variant up to 16 routes per expert and the self-routed
     // batch size, the prefill GEMMs above.  Measured at H = 2048, I = 512,
     // E = 256, k = 8: T = 512 decode 172 / prefill 195 us, T = 768 267 / 204,
@@ -269,6 +287,11 @@ int moe_fused_w8a16_ex(const void* x, const uint8_t* w13, const float* w13_scale
         variant = (R <= 16LL * E && R <= decode_self_routed_max_routes()) || !prefill_supported(H, I, act)
                       ? MOE_VARIANT_DECODE
                       : MOE_VARIANT_PREFILL;
+    }
+    const FusedLayout L = fused_layout(T, H, I, E, k, has_shared, variant);
+    if (!ws || ws_bytes < L.total) {
+        set_error("moe_fused_w8a16: workspace of %zu bytes needed (got %zu)", L.total, ws_bytes);
+        return MOE_EINVAL;
     }
     if (variant == MOE_VARIANT_PREFILL || fp8_x) {
         if (int rc = prefill_check(T, H, I, E, k, has_shared, act)) return rc;
@@ -297,7 +320,7 @@ int moe_fused_w8a16_ex(const void* x, const uint8_t* w13, const float* w13_scale
 
     const uint16_t* xb = static_cast<const uint16_t*>(x);
     int rc;
-    if (variant == MOE_VARIANT_DECODE && decode_fused_fits(T, k, E, I, has_shared, true)) {
+    if (variant == MOE_VARIANT_DECODE && decode_fused_fits(T, k, E, H, I, has_shared, true)) {
         // small decode batch: each expert's workgroup finds its own routes
         rc = launch_decode_fused_self(weight_layout, decode_mt(T, k, E), xb, w13, w13_scale, w2,
                                       w2_scale, sh, ids, aff, T, H, I, E, k, ybuf, act, s);

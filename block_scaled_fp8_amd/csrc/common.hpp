@@ -38,6 +38,21 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
     return r;
 }
 
+// The same conversion times 2^e, where e is the exponent of `pow2` (the
+// converter uses only the exponent field of its scale operand, an E8M0
+// scale: 0.0f means 2^-127).  Exact while every product is a normal bf16
+// value (e >= -117); smaller results are flushed to zero.
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16x8_scaled(uint32_t lo, uint32_t hi, float pow2) {
+    bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, pow2, false);
+    bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, pow2, true);
+    bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, pow2, false);
+    bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, pow2, true);
+    bf16x8 r;
+    r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+    r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+    return r;
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {
     return __builtin_bit_cast(bf16x8, v);
 }

@@ -411,11 +411,13 @@ int launch_decode_fused(int layout, int MT, const uint16_t* x, const uint8_t* w1
 int decode_mt(int T, int k, int E) { return ((long)T * k <= 4L * E) ? 1 : 2; }
 
 // The fused one-workgroup-per-expert kernel pays off once most CUs get an
-// expert, and needs its activations (and, self-routed, the route list) in LDS.
-bool decode_fused_fits(int T, int k, int E, int I, int has_shared, bool self_routed) {
+// expert, and needs its activations (and, self-routed, the route list) in LDS;
+// it addresses x by 32-bit element offsets.
+bool decode_fused_fits(int T, int k, int E, int H, int I, int has_shared, bool self_routed) {
     const long R = (long)T * k;
     const long max_active = std::min<long>(E, R) + has_shared;
     if (max_active < 128) return false;
+    if ((long long)T * H >= (1LL << 32)) return false;
     if (self_routed && R > decode_self_routed_max_routes()) return false;
     return decode_fused_lds_bytes(decode_mt(T, k, E), I, self_routed ? (int)R : 0) <= 64 * 1024;
 }
@@ -427,7 +429,7 @@ int launch_decode_ffn(int layout, const uint16_t* x, const uint8_t* w13, const f
     const int has_shared = sh.w13 != nullptr;
     const int nseg_max = E + has_shared;
     const int MT = decode_mt(T, k, E);
-    if (decode_fused_fits(T, k, E, I, has_shared, false))
+    if (decode_fused_fits(T, k, E, H, I, has_shared, false))
         return launch_decode_fused(layout, MT, x, w13, w13s, w2, w2s, sh, plan, aff, T, H, I, E,
                                    k, ybuf, act, stream);
     const int rc = act == ACT_RELU2

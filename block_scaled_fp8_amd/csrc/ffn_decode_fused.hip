@@ -19,12 +19,12 @@
 // v_mfma_f32_16x16x32_bf16 after an exact FP8 -> bf16 conversion; the token
 // operand uses the same K permutation, so every MFMA computes exact K sums.
 //
-// Block scales: the accumulator of a tile is kept in units of the scale of
-// the 128-wide K block being summed; entering a new block multiplies it by
-// s_old / s_new, and the final value is multiplied by the last scale.  The
-// scale is therefore applied in fp32 and never rounded into bf16, with one
-// accumulator set instead of a partial plus a total.  A block whose scale is
-// zero holds only zero weights and leaves the running scale unchanged.
+// Block scales: the MFMAs of each 128-wide K block accumulate a fresh fp32
+// partial, which joins the tile's total as total += scale * partial when the
+// block ends.  Every block is therefore weighted by exactly its own fp32
+// scale, whatever the scales of its neighbours: a zero scale adds exactly 0
+// (for finite activations), and subnormal or widely different scales are
+// multiplied in as they are.  The scale is never rounded into bf16.
 #include "common.hpp"
 #include "plan.hpp"
 
@@ -72,8 +72,10 @@ __global__ __launch_bounds__(DF_THREADS) void decode_fused_kernel(
     const float* __restrict__ sh_w13s, const uint8_t* __restrict__ sh_w2,
     const float* __restrict__ sh_w2s, Plan plan, const int32_t* __restrict__ ids, int E,
     const float* __restrict__ aff, int T, int H, int I, int k, float* __restrict__ ybuf,
-    float* __restrict__ ytrash) {
-    static_assert(DEPTH == 1 || DEPTH == 2, "chunks per 128-wide scale block");
+    int ytrash_row) {
+    // two 64-wide chunks per 128-wide scale block, two in flight: the chunk
+    // in flight slot d is the block's first (d = 0) or second (d = 1) half
+    static_assert(DEPTH == 2, "chunks per 128-wide scale block");
     constexpr int MROWS = 16 * MT, NT = DF_NT, HALF = DF_HALF;
     constexpr int CS = chunk_stride<LAYOUT>();
     extern __shared__ uint16_t a_lds[];  // [MROWS][I + 8] bf16 SwiGLU activations
@@ -149,34 +151,33 @@ __global__ __launch_bounds__(DF_THREADS) void decode_fused_kernel(
 
     for (int mp = 0; mp < rows; mp += MROWS) {
         if (mp > 0) __syncthreads();  // the previous pass has finished reading a_lds
-        const uint16_t* xp[MT];
+        // (32-bit offsets and indices keep the registers for the block totals)
+        uint32_t xoff[MT];   // element offset of this lane's x row piece (x is under 4 GB)
         bool xvalid[MT];
-        const uint16_t* ap[MT];
-        float* yrow[MT][4];  // y destination of this lane's output rows (trash row if padded)
+        uint32_t aoff[MT];   // element offset of this lane's activation row piece in a_lds
+        int yrow[MT][4];     // y row of this lane's output rows (the trash row if padded)
         float yaff[MT][4];   // affinity of each of those routes
         u32x4 bq[DEPTH][NT];
         u32x4 aq[DEPTH][MT][2];
-        f32x4 acc[MT][NT];
-        float seff0 = 0.0f, seff1 = 0.0f;  // running scales (phase 1: gate, up; phase 2: seff0)
+        f32x4 acc[MT][NT];  // partial sums of the current 128-wide K block
+        f32x4 tot[MT][NT];  // scaled totals of the finished blocks
+        float sc0 = 0.0f, sc1 = 0.0f;  // scales of the current block (phase 1: gate, up; phase 2: sc0)
         auto reset = [&]() {
 #pragma unroll
             for (int j = 0; j < NT; ++j)
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt) acc[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-            seff0 = 0.0f;
-            seff1 = 0.0f;
-        };
-        auto rescale = [&](float& seff, float sn, int j0, int j1) {
-            if (sn != 0.0f) {
-                if (seff != 0.0f) {
-                    const float r = seff * __builtin_amdgcn_rcpf(sn);
-#pragma unroll
-                    for (int j = j0; j < j1; ++j)
-#pragma unroll
-                        for (int mt = 0; mt < MT; ++mt) acc[mt][j] *= r;
+                for (int mt = 0; mt < MT; ++mt) {
+                    acc[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    tot[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
                 }
-                seff = sn;
-            }
+        };
+        // the block ends: its partial, times its own scale, joins the total
+        // (the block's first MFMAs start the next partial from zero)
+        auto fold = [&](float sc, int j0, int j1) {
+#pragma unroll
+            for (int j = j0; j < j1; ++j)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) tot[mt][j] += sc * acc[mt][j];
         };
         auto mfma_chunk = [&](int d, const u32x4 (&av)[MT][2]) {
 #pragma unroll
@@ -187,8 +188,9 @@ __global__ __launch_bounds__(DF_THREADS) void decode_fused_kernel(
                                             : fp8x8_to_bf16x8(bq[d][j][2], bq[d][j][3]);
 #pragma unroll
                     for (int mt = 0; mt < MT; ++mt)
-                        acc[mt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[mt][s]),
-                                                                             b, acc[mt][j], 0, 0, 0);
+                        acc[mt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            as_bf16x8(av[mt][s]), b,
+                            d == 0 && s == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[mt][j], 0, 0, 0);
                 }
         };
 
@@ -206,7 +208,7 @@ __global__ __launch_bounds__(DF_THREADS) void decode_fused_kernel(
         auto issue1_a = [&](int d, int c) {
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
-                const u32x4* q = reinterpret_cast<const u32x4*>(xp[mt] + c * 64);
+                const u32x4* q = reinterpret_cast<const u32x4*>(x + xoff[mt] + c * 64);
                 aq[d][mt][0] = q[0];
                 aq[d][mt][1] = q[1];
             }
@@ -229,16 +231,16 @@ __global__ __launch_bounds__(DF_THREADS) void decode_fused_kernel(
         int pg = wave, pc = 0;
         auto proc1 = [&](int d) {
             const int g = pg % G1;
-            if ((pc & 1) == 0) {
+            if (d == 0) {  // a block starts: its scales
                 const int kb = pc >> 1;
                 if (RELU2) {
                     const int ui = __builtin_amdgcn_readfirstlane(((g * NT * 16) >> 7) * kb1 + kb);
-                    rescale(seff0, S13[ui], 0, NT);
+                    sc0 = S13[ui];
                 } else {
                     const int gi = __builtin_amdgcn_readfirstlane(((g * HALF * 16) >> 7) * kb1 + kb);
                     const int ui = __builtin_amdgcn_readfirstlane(((I + g * HALF * 16) >> 7) * kb1 + kb);
-                    rescale(seff0, S13[gi], 0, HALF);
-                    rescale(seff1, S13[ui], HALF, NT);
+                    sc0 = S13[gi];
+                    sc1 = S13[ui];
                 }
             }
             u32x4 av[MT][2];
@@ -248,6 +250,14 @@ __global__ __launch_bounds__(DF_THREADS) void decode_fused_kernel(
                 av[mt][1] = xvalid[mt] ? aq[d][mt][1] : u32x4{0u, 0u, 0u, 0u};
             }
             mfma_chunk(d, av);
+            if (d == 1) {  // the block's second chunk: fold it
+                if (RELU2) {
+                    fold(sc0, 0, NT);
+                } else {
+                    fold(sc0, 0, HALF);
+                    fold(sc1, HALF, NT);
+                }
+            }
             if (pc == nch1 - 1) {  // group done: activations into LDS (padding columns if spare)
                 const bool real = pg < G1;
                 if (RELU2) {
@@ -259,7 +269,7 @@ __global__ __launch_bounds__(DF_THREADS) void decode_fused_kernel(
                             for (int i = 0; i < 4; ++i) {
                                 const int m = mt * 16 + lg * 4 + i;
                                 const int col = real ? (g * NT + j) * 16 + ln : I + (ln & 7);
-                                a_lds[m * astride + col] = f32_to_bf16_bits(relu2(acc[mt][j][i] * seff0));
+                                a_lds[m * astride + col] = f32_to_bf16_bits(relu2(tot[mt][j][i]));
                             }
                 } else {
 #pragma unroll
@@ -268,8 +278,8 @@ __global__ __launch_bounds__(DF_THREADS) void decode_fused_kernel(
                         for (int j = 0; j < HALF; ++j)
 #pragma unroll
                             for (int i = 0; i < 4; ++i) {
-                                const float gv = acc[mt][j][i] * seff0;
-                                const float uv = acc[mt][HALF + j][i] * seff1;
+                                const float gv = tot[mt][j][i];
+                                const float uv = tot[mt][HALF + j][i];
                                 const int m = mt * 16 + lg * 4 + i;
                                 const int col = real ? (g * HALF + j) * 16 + ln : I + (ln & 7);
                                 a_lds[m * astride + col] = f32_to_bf16_bits(swiglu(gv, uv));
@@ -284,28 +294,30 @@ __global__ __launch_bounds__(DF_THREADS) void decode_fused_kernel(
         };
         auto proc2 = [&](int d) {
             const int g = pg % G2;
-            if ((pc & 1) == 0) {
+            if (d == 0) {
                 const int si = __builtin_amdgcn_readfirstlane(((g * NT * 16) >> 7) * kb2 + (pc >> 1));
-                rescale(seff0, S2[si], 0, NT);
+                sc0 = S2[si];
             }
             u32x4 av[MT][2];
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
-                const u32x4* q = reinterpret_cast<const u32x4*>(ap[mt] + pc * 64);
+                const u32x4* q = reinterpret_cast<const u32x4*>(a_lds + aoff[mt] + pc * 64);
                 av[mt][0] = q[0];
                 av[mt][1] = q[1];
             }
             mfma_chunk(d, av);
+            if (d == 1) fold(sc0, 0, NT);
             if (pc == nch2 - 1) {  // group done: fp32 rows of the routes (trash if spare)
                 const bool real = pg < G2;
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        float* dst = real ? yrow[mt][i] + g * NT * 16 + ln : ytrash + ln;
-                        const float sc = seff0 * yaff[mt][i];
+                        float* dst = ybuf + (size_t)(real ? yrow[mt][i] : ytrash_row) * H +
+                                     (real ? g * NT * 16 : 0) + ln;
+                        const float a = yaff[mt][i];
 #pragma unroll
-                        for (int j = 0; j < NT; ++j) dst[j * 16] = acc[mt][j][i] * sc;
+                        for (int j = 0; j < NT; ++j) dst[j * 16] = tot[mt][j][i] * a;
                     }
                 reset();
                 pc = 0;
@@ -327,8 +339,8 @@ __global__ __launch_bounds__(DF_THREADS) void decode_fused_kernel(
             int t = -1;
             if (m < rows) t = e >= 0 ? route_of(m) / k : route_of(m) - R;
             xvalid[mt] = t >= 0;
-            xp[mt] = x + (size_t)(t >= 0 ? t : 0) * H + lg * 16;
-            ap[mt] = a_lds + (mt * 16 + ln) * astride + lg * 16;
+            xoff[mt] = (uint32_t)(t >= 0 ? t : 0) * (uint32_t)H + lg * 16;
+            aoff[mt] = (uint32_t)((mt * 16 + ln) * astride + lg * 16);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int mi = mp + mt * 16 + lg * 4 + i;
@@ -338,7 +350,7 @@ __global__ __launch_bounds__(DF_THREADS) void decode_fused_kernel(
                     r = route_of(mi);
                     a = e >= 0 ? aff[r] : 1.0f;
                 }
-                yrow[mt][i] = r >= 0 ? ybuf + (size_t)r * H : ytrash;
+                yrow[mt][i] = r >= 0 ? r : ytrash_row;
                 yaff[mt][i] = a;
             }
         }
@@ -382,7 +394,7 @@ static int launch_decode_fused_l(int MT, const uint16_t* x, const uint8_t* w13, 
     const int nseg_max = E + (sh.w13 ? 1 : 0);
     const size_t lds = decode_fused_lds_bytes(MT, I, SELF ? T * k : 0);
     // the trash row sits right after the last real row of y
-    float* ytrash = ybuf + ((size_t)T * k + (sh.w13 ? (size_t)T : 0)) * H;
+    const int ytrash = T * k + (sh.w13 ? T : 0);
     prof_begin("decode_fused_expert", stream);
     if (MT == 1)
         decode_fused_kernel<1, 2, LAYOUT, SELF, RELU2><<<nseg_max, DF_THREADS, lds, stream>>>(

@@ -39,8 +39,10 @@
 //    Weight tiles: one 16-row x 64-byte chunk per instruction, stored in lane
 //    order (the tile-coalesced layout is this chunk order in memory).
 //  * FP8 is converted exactly to bf16 after the LDS read; the fp32 block scale
-//    of each 128-wide K block is applied by rescaling the accumulators when the
-//    block starts (running scale), never by rounding it into bf16.
+//    of each 128-wide K block is never rounded into bf16: its power of two is
+//    folded exactly into the conversion, and its mantissa is applied by
+//    rescaling the accumulators when the block starts (running scale); a
+//    zero-scale block's MFMAs are skipped.
 //  * Work list: the sort lists every full 128-row tile first and the partial
 //    last tiles after them; the list is cut into runs of 8 row tiles dealt
 //    round-robin to the 8 XCDs (all column blocks of a row tile on one XCD,
@@ -368,7 +370,58 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
         for (int nt = 0; nt < C::NT; ++nt)
 #pragma unroll
             for (int i = 0; i < AR; ++i) acc[mt][nt][i] = 0.0f;
-    float seff[2] = {0.0f, 0.0f};
+
+    // ---- block scales.  Group g (g = 0 the wave's gate or only columns, g = 1
+    //      its up columns) sums over K blocks b with scales s_b.  Each s_b is
+    //      split as m_b * 2^(eref + d_b), 1 <= |m_b| < 2, where eref is the
+    //      largest exponent among the group's nonzero scales (so d_b <= 0):
+    //      the power of two 2^d_b is folded exactly into the weight operand
+    //      (the bf16 conversion's exponent-only scale, or the fp8 MFMA's E8M0
+    //      B scale), and the accumulators are kept in units of m_cur * 2^eref,
+    //      rescaled by m_old / m_new (a ratio in (1/2, 2), so it can neither
+    //      overflow nor lose the sum) when a block starts.  A block whose scale
+    //      is zero adds exactly nothing: its MFMAs are skipped (a wave-uniform
+    //      branch).  Weights stay exact while d_b >= -117 (E4M3FN times 2^d_b
+    //      then stays a normal bf16 value); a block more than 2^117 below the
+    //      group's largest scale has its smallest codes flushed to zero.
+    float mcur[2] = {1.0f, 1.0f};  // mantissa of the accumulator unit
+    int eref[2] = {0, 0};
+    float csc[2] = {1.0f, 1.0f};   // 2^d of the current block as a conversion scale
+    int bsc[2] = {127, 127};       // the same as an E8M0 byte
+    bool zs[2] = {false, false};   // the current block's scale is zero
+    // (once the scale table is in LDS) the largest exponent of each group
+    auto scale_prologue = [&]() {
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+            int mx = -1000;
+            for (int c = 0; c < kbp; c += 64) {
+                const float v = sc_tab[sj[g] * kbp + c + lane];
+                int ex;
+                (void)frexpf(v, &ex);
+                mx = v != 0.0f ? max(mx, ex - 1) : mx;
+            }
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) mx = max(mx, __shfl_xor(mx, o, MOE_WAVE));
+            eref[g] = __builtin_amdgcn_readfirstlane(mx == -1000 ? 0 : mx);
+        }
+    };
+    // a K block starts: its scales sn[g] give the rescale factors rr[g]
+    auto enter_block = [&](const float (&sn)[2], float (&rr)[2]) {
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+            const float s = sn[g];
+            const bool z = s == 0.0f;
+            int ex;
+            const float m = 2.0f * frexpf(s, &ex);
+            const int byte = max(ex - 1 - eref[g] + 127, 0);
+            // (wave-uniform: kept in scalar registers)
+            rr[g] = uniform_f32(z ? 1.0f : mcur[g] * __builtin_amdgcn_rcpf(m));
+            mcur[g] = uniform_f32(z ? mcur[g] : m);
+            bsc[g] = __builtin_amdgcn_readfirstlane(byte);
+            csc[g] = __builtin_bit_cast(float, (uint32_t)bsc[g] << 23);
+            zs[g] = __builtin_amdgcn_readfirstlane((int)z) != 0;
+        }
+    };
 
     // ---- K loop, software-pipelined by half steps.  Half p of a 64-wide step
     //      covers sub-steps 2p, 2p+1 (16 K each): A pieces 2p, 2p+1 and 16-byte
@@ -430,12 +483,15 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
 #pragma unroll
         for (int nt = 0; nt < C::NT; ++nt) {
             if (C::M16 && nt / (C::NT / 2) != j) continue;
+            const int gi = PAIRED ? nt / (C::NT / 2) : 0;
+            if (zs[gi]) continue;  // a zero block scale: nothing to add
             bf16x8 bf;
             if constexpr (C::M16)
-                bf = fp8x8_to_bf16x8(b[nt][0], b[nt][1]);
+                bf = fp8x8_to_bf16x8_scaled(b[nt][0], b[nt][1], csc[gi]);
             else
-                bf = j == 0 ? fp8x8_to_bf16x8(b[nt][0], b[nt][1]) : fp8x8_to_bf16x8(b[nt][2], b[nt][3]);
-            const float f = PAIRED ? rr[nt / (C::NT / 2)] : rr[0];
+                bf = j == 0 ? fp8x8_to_bf16x8_scaled(b[nt][0], b[nt][1], csc[gi])
+                            : fp8x8_to_bf16x8_scaled(b[nt][2], b[nt][3], csc[gi]);
+            const float f = rr[gi];
 #pragma unroll
             for (int mt = 0; mt < MTA; ++mt) {
                 if (rescale)
@@ -468,21 +524,14 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
     if (nk >= C::STAGES) wait_vmcnt<(C::STAGES - 1) * PER_STAGE>();
     else wait_vmcnt<PER_STAGE>();  // nk == 2: stages 0 and 1 issued
     barrier_after_lds_reads();     // stage 0 and the scale table landed in every wave
+    scale_prologue();
     float snext[2] = {sc_tab[sj[0] * kbp], sc_tab[sj[1] * kbp]};
     read_half(0, 0, ah[0], bh[0]);
     const float one[2] = {1.0f, 1.0f};
     for (int kb = 0; kb < kblocks; ++kb) {
         const int kc = 2 * kb;
-        // running scale: a zero scale (all-zero block) keeps the current one
         float rr[2];
-#pragma unroll
-        for (int g = 0; g < 2; ++g) {
-            const float sn = snext[g];
-            const bool take = sn != 0.0f;
-            // (wave-uniform: kept in scalar registers)
-            rr[g] = uniform_f32(take && seff[g] != 0.0f ? seff[g] * __builtin_amdgcn_rcpf(sn) : 1.0f);
-            seff[g] = uniform_f32(take ? sn : seff[g]);
-        }
+        enter_block(snext, rr);
         const int kn = kb + 1 < kblocks ? kb + 1 : kb;
         snext[0] = sc_tab[sj[0] * kbp + kn];
         snext[1] = sc_tab[sj[1] * kbp + kn];
@@ -544,14 +593,17 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
                                            *reinterpret_cast<const u32x4*>(st + b_off + b_step(nt) + 256));
     #pragma unroll
                 for (int nt = 0; nt < C::NT; ++nt) {
-                    const float f = PAIRED ? rr[nt / (C::NT / 2)] : rr[0];
+                    const int gi = PAIRED ? nt / (C::NT / 2) : 0;
+                    if (zs[gi]) continue;  // a zero block scale: nothing to add
+                    const float f = rr[gi];
     #pragma unroll
                     for (int mt = 0; mt < MTA; ++mt) {
                         if (rescale)
     #pragma unroll
                             for (int i = 0; i < AR; ++i) acc[mt][nt][i] *= f;
+                        // (the block's power of two as the B operand's E8M0 scale)
                         acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                            av[mt], bv[nt], acc[mt][nt], 0, 0, 0, 127, 0, 127);
+                            av[mt], bv[nt], acc[mt][nt], 0, 0, 0, 127, 0, bsc[gi]);
                     }
                 }
             };
@@ -571,18 +623,13 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
             if (nk >= C::STAGES) wait_vmcnt<(C::STAGES - 1) * PER_STAGE>();
             else wait_vmcnt<0>();
             barrier_after_lds_reads();  // ... in every wave
+            scale_prologue();
             float snext[2] = {sc_tab[sj[0] * kbp], sc_tab[sj[1] * kbp]};
             const float one[2] = {1.0f, 1.0f};
             for (int kb = 0; kb < kblocks; ++kb) {
                 const int kc = 2 * kb;
                 float rr[2];
-    #pragma unroll
-                for (int g = 0; g < 2; ++g) {
-                    const float sn = snext[g];
-                    const bool take = sn != 0.0f;
-                    rr[g] = uniform_f32(take && seff[g] != 0.0f ? seff[g] * __builtin_amdgcn_rcpf(sn) : 1.0f);
-                    seff[g] = uniform_f32(take ? sn : seff[g]);
-                }
+                enter_block(snext, rr);
                 const int kn = kb + 1 < kblocks ? kb + 1 : kb;
                 snext[0] = sc_tab[sj[0] * kbp + kn];
                 snext[1] = sc_tab[sj[1] * kbp + kn];
@@ -632,14 +679,17 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
         uint8_t* ybytes = reinterpret_cast<uint8_t*>(ybuf);
         const size_t rowb = (size_t)H * 2 + (size_t)(H / 8);
         const int col0 = nb * BN + wn * C::WCOLS;  // first column of the wave tile
-        const float sc = seff[0];
+        // the accumulator unit is mcur * 2^eref: the power of two goes in last
+        // (an exact exponent shift unless the product is subnormal)
+        const float sm = mcur[0];
+        const int se = eref[0];
 #pragma unroll
         for (int mt = 0; mt < C::MT; ++mt) {
 #pragma unroll
             for (int nt = 0; nt < C::NT; ++nt)
 #pragma unroll
                 for (int i = 0; i < AR; ++i)
-                    slab[(8 * (i >> 2) + 4 * lg + (i & 3)) * 128 + nt * 32 + ln] = acc[mt][nt][i] * sc;
+                    slab[(8 * (i >> 2) + 4 * lg + (i & 3)) * 128 + nt * 32 + ln] = ldexpf(acc[mt][nt][i] * sm, se);
             __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the slab is written
             __builtin_amdgcn_wave_barrier();
 #pragma unroll
@@ -681,17 +731,20 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
             // A8: the row's activation scale joins the weight block's
             float xsv = 1.0f;
             if constexpr (C::A8) xsv = row_xs[wm * C::WROWS + r];
+            // value = acc * mcur * x scale * 2^eref, the power of two last (an
+            // exact exponent shift unless the result is subnormal)
+            const float s0 = mcur[0] * xsv, s1 = mcur[1] * xsv;
             if constexpr (MODE == PF_GATEUP) {
-                const float s0 = seff[0] * xsv, s1 = seff[1] * xsv;
 #pragma unroll
                 for (int nt = 0; nt < C::NT / 2; ++nt)
                     slab[r * OUTC + nt * C::MS + ocol] = f32_to_bf16_bits(
-                        swiglu_fast(acc[mt][nt][i] * s0, acc[mt][nt + C::NT / 2][i] * s1));
+                        swiglu_fast(ldexpf(acc[mt][nt][i] * s0, eref[0]),
+                                    ldexpf(acc[mt][nt + C::NT / 2][i] * s1, eref[1])));
             } else {
-                const float s0 = seff[0] * xsv;
 #pragma unroll
                 for (int nt = 0; nt < C::NT; ++nt)
-                    slab[r * OUTC + nt * C::MS + ocol] = f32_to_bf16_bits(relu2(acc[mt][nt][i] * s0));
+                    slab[r * OUTC + nt * C::MS + ocol] =
+                        f32_to_bf16_bits(relu2(ldexpf(acc[mt][nt][i] * s0, eref[0])));
             }
         }
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the slab is written

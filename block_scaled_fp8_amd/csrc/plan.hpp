@@ -98,7 +98,7 @@ int launch_combine(const float* ybuf, const int32_t* ids, const int32_t* inv_rou
 // expert kernel applies, and its self-routed form (no sort: each workgroup
 // scans the ids for its expert; at most decode_self_routed_max_routes() routes).
 int decode_mt(int T, int k, int E);
-bool decode_fused_fits(int T, int k, int E, int I, int has_shared, bool self_routed);
+bool decode_fused_fits(int T, int k, int E, int H, int I, int has_shared, bool self_routed);
 size_t decode_fused_lds_bytes(int MT, int I, int self_routes);
 int decode_self_routed_max_routes();
 int launch_decode_fused_self(int layout, int MT, const uint16_t* x, const uint8_t* w13,

@@ -81,7 +81,9 @@ enum {
     MOE_LAYOUT_TILED = 1      /* tile-coalesced, see moe_pack_w8 */
 };
 
-/* Message describing the most recent failure on the calling thread ("" if none). */
+/* Message describing the most recent failure on the calling thread ("" if none).
+ * Interface plumbing, not from the pages: a thread-local buffer owned by the
+ * library, valid until the thread's next call into it; never NULL. */
 const char* moe_last_error(void);
 
 /*
@@ -148,6 +150,10 @@ int moe_route_proj(const void* x, const void* wg, int T, int H, int E, int k, fl
                    void* stream);
 
 /*
+ * moe_sort_workspace_bytes -- device scratch that moe_sort needs for (T, k, E);
+ * interface plumbing, not from the pages.  0 for invalid sizes (T < 0, k < 1,
+ * E < 1) or when no scratch is needed.
+ *
  * moe_sort -- per-expert histogram, exclusive scan, stable sorted route map
  * and its inverse.  Sources: nemotron_moe.rs page (sort by expert before the
  * grouped GEMM, unpermute-reduce after); AITER PR page (sorting and inverse
@@ -215,14 +221,31 @@ typedef struct {
  * 256 (else MOE_EUNSUPPORTED); MOE_VARIANT_AUTO picks the decode variant for
  * such shapes and for batches of at most 16 routes per expert and 4096 routes
  * in all, the prefill variant otherwise.  The expert FFN computes in bf16 x
- * bf16 products with fp32 accumulation; each 128-wide K block's partial sum
- * is multiplied by its
- * fp32 block scale; the SwiGLU output is rounded to bf16 before the down GEMM.
+ * bf16 products with fp32 accumulation; the SwiGLU output is rounded to bf16
+ * before the down GEMM.
+ * Block scales: any finite fp32 value (zero, subnormal or negative included;
+ * NaN and infinity are out of contract).  Each 128-wide K block is weighted
+ * by its own scale: a zero-scale block adds exactly 0 whatever its codes.
+ * The decode variant multiplies each block's fp32 partial sum by its scale.
+ * The prefill variants fold the scale's power of two exactly into the bf16
+ * (or fp8) weight operand and apply its mantissa to the fp32 accumulators;
+ * this is exact while a block's scale is at most 2^117 below the largest
+ * scale of its 128-row scale row, and beyond that the block's smallest
+ * codes are flushed to zero.
+ * Alignment: x, w13, w2, out, ws and the shared expert's w13 and w2 must be
+ * 16-byte aligned; the scales, ids and aff 4-byte aligned (else MOE_EINVAL).
  */
 /* MOE_VARIANT_PREFILL_A8 computes every expert from x_hat[t] = decode(code) * scale
  * of moe_quant_e4m3_rows instead of x[t] (gate/up on fp8 x fp8 products, exact
  * in fp32, with fp32 sums); the rest of the path is that of MOE_VARIANT_PREFILL,
- * with the same shape rules.  Its workspace holds the codes and scales too. */
+ * with the same shape rules.  Its workspace holds the codes and scales too.
+ *
+ * moe_fused_workspace_bytes -- device scratch of a moe_fused_w8a16(_ex) call
+ * with these sizes and this variant (interface plumbing, not from the pages):
+ * the sort maps, the prefill tile list, the activations between the GEMMs and
+ * one contribution row per route (fp32 for the decode variant, 2.125 bytes a
+ * value for the prefill ones; AUTO is sized for either).  0 for invalid
+ * sizes.  A call checks ws_bytes against the size of the variant it runs. */
 size_t moe_fused_workspace_bytes(int T, int H, int I, int E, int k,
                                  int has_shared, int variant);
 int moe_fused_w8a16(const void* x,

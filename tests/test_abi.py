@@ -179,6 +179,44 @@ def test_fused_argument_checks():
     assert lib.moe_fused_w8a16(*args(0, 2048, 512, 256, 8, 0)) == binding.MOE_OK
 
 
+def test_fused_alignment_checks():
+    """16-byte vector accesses on x, the weights, out and the workspace and
+    4-byte ones on the scales, ids and affinities: misaligned pointers are
+    refused before any launch."""
+    lib = binding.load_library()
+    f = 0x1000
+    ws = lib.moe_fused_workspace_bytes(64, 2048, 512, 256, 8, 0, 0)
+
+    def call(**over):
+        p = dict(x=f, w13=f, w13s=f, w2=f, w2s=f, ids=f, aff=f, out=0x3000, ws=0x5000)
+        p.update(over)
+        v = lambda a: ctypes.c_void_p(a)  # noqa: E731
+        return lib.moe_fused_w8a16(v(p["x"]), v(p["w13"]), v(p["w13s"]), v(p["w2"]), v(p["w2s"]),
+                                   v(p["ids"]), v(p["aff"]), 64, 2048, 512, 256, 8, None,
+                                   v(p["out"]), None, v(p["ws"]), ws, 0, 0, None)
+
+    for name, addr in (("x", 0x1008), ("w13", 0x1004), ("w2", 0x1001), ("out", 0x3008),
+                       ("ws", 0x5004), ("w13s", 0x1002), ("w2s", 0x1001), ("ids", 0x1002),
+                       ("aff", 0x1003)):
+        assert call(**{name: addr}) == binding.MOE_EINVAL, name
+        assert b"aligned" in lib.moe_last_error(), name
+
+
+def test_workspace_is_sized_per_variant():
+    """Decode rows of contributions are fp32 (4 bytes a value), prefill rows
+    block floating point (2 bytes a value + an exponent byte per 8); AUTO is
+    sized for either."""
+    lib = binding.load_library()
+    T, H, I, E, k = 16384, 8192, 256, 512, 10
+    rows = T * k + T + 1
+    dec = lib.moe_fused_workspace_bytes(T, H, I, E, k, 1, 1)
+    pf = lib.moe_fused_workspace_bytes(T, H, I, E, k, 1, 2)
+    auto = lib.moe_fused_workspace_bytes(T, H, I, E, k, 1, 0)
+    assert dec >= rows * 4 * H and pf >= rows * (2 * H + H // 8)
+    assert pf < rows * 4 * H < dec and auto == dec
+    assert lib.moe_fused_workspace_bytes(T, H, I, E, k, 1, 9) == 0
+
+
 def test_workspace_grows_with_shared_expert():
     lib = binding.load_library()
     a = lib.moe_fused_workspace_bytes(512, 2048, 512, 256, 8, 0, 0)
