@@ -13,13 +13,54 @@ import oracle
 from block_scaled_fp8_amd import binding, synth
 
 from _parity import (AFF_RTOL, assert_out_close, gpu_case, np_, oracle_rows, pack_reference,
-                     sample_rows, tiled_case)
+                     tiled_case)
 
 pytestmark = pytest.mark.gpu
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
-FFN_SAMPLE = {"tiny": 4, "decode64": 64, "decode512": 64, "prefill8k_skew": 24,
-              "prefill16k_wide": 6}
+# Output rows compared with the oracle: every row of every workload up to the
+# 8192-token one; at the 16384-token width (whose float64 oracle over all
+# rows would take minutes) a structured sample: for every segment (each
+# active expert, and the shared expert), the tokens owning its first sorted
+# row, its last sorted row and the last row of its last full 128-row tile,
+# plus random tokens.
+FULL_ROWS = {"tiny", "decode64", "decode512", "prefill8k_skew"}
+TILE_M = 128
+
+
+def structured_rows(ids, E, T, has_shared, extra=64, seed=2):
+    _, offsets, sorted_route, _ = oracle.sort_by_expert(ids, E)
+    k = ids.shape[1]
+    pick = set()
+    for e in range(E):
+        o, n = int(offsets[e]), int(offsets[e + 1] - offsets[e])
+        if n == 0:
+            continue
+        rows = [o, o + n - 1] + ([o + (n // TILE_M) * TILE_M - 1] if n >= TILE_M else [])
+        pick.update(int(sorted_route[p]) // k for p in rows)
+    if has_shared:  # the shared segment holds token t at its row t
+        pick.update([0, T - 1] + ([(T // TILE_M) * TILE_M - 1] if T >= TILE_M else []))
+    rng = np.random.default_rng(seed)
+    pick.update(rng.choice(T, size=min(extra, T), replace=False).tolist())
+    return np.array(sorted(pick))
+
+
+def check_rows(name, cfg, ids):
+    if name in FULL_ROWS:
+        return np.arange(cfg.T)
+    return structured_rows(np.asarray(ids), cfg.E, cfg.T, cfg.shared)
+
+
+_oracle = {}
+
+
+def oracle_cached(key, c, ids, aff, rows, xrows=None):
+    """The oracle's rows for one workload, kept while the tests of one
+    workload run (it does not depend on the variant or the layout)."""
+    if key not in _oracle:
+        _oracle.clear()
+        _oracle[key] = oracle_rows(c, ids, aff, rows, xrows=xrows)
+    return _oracle[key]
 
 
 def setup_module(module):
@@ -354,9 +395,9 @@ def test_fused_parity(name, variant, layout):
     assert int(status.item()) == 0
     ref_ids, ref_aff = oracle.route_softmax_topk(np_(c["logits"]), cfg.k)
     assert np.array_equal(np_(ids), ref_ids)
-    rows = sample_rows(cfg.T, FFN_SAMPLE[name], seed=2)
-    ref = oracle_rows(c, ref_ids, ref_aff, rows)
-    assert_out_close(np_(out)[rows], ref, what=f"{name}/{variant}/{layout}")
+    rows = check_rows(name, cfg, ref_ids)
+    ref = oracle_cached((name, "swiglu"), c, ref_ids, ref_aff, rows)
+    assert_out_close(np_(out)[rows], ref, what=f"{name}/{variant}/{layout} ({len(rows)} rows)")
 
 
 @pytest.mark.parametrize("layout", LAYOUTS)
@@ -378,9 +419,9 @@ def test_fused_relu2_parity(name, variant, layout):
     torch.cuda.synchronize()
     assert int(status.item()) == 0
     ref_ids, ref_aff = oracle.route_softmax_topk(np_(c["logits"]), cfg.k)
-    rows = sample_rows(cfg.T, FFN_SAMPLE[name], seed=3)
-    ref = oracle_rows(c, ref_ids, ref_aff, rows)
-    assert_out_close(np_(out)[rows], ref, what=f"relu2 {name}/{variant}/{layout}")
+    rows = check_rows(name, cfg, ref_ids)
+    ref = oracle_cached((name, "relu2"), c, ref_ids, ref_aff, rows)
+    assert_out_close(np_(out)[rows], ref, what=f"relu2 {name}/{variant}/{layout} ({len(rows)} rows)")
 
 
 @pytest.mark.parametrize("variant", ["auto"] + VARIANTS)
@@ -407,6 +448,40 @@ def test_fused_token_boundaries(T, variant, layout):
     ref_ids, ref_aff = oracle.route_softmax_topk(np_(c["logits"]), cfg.k)
     ref = oracle_rows(c, ref_ids, ref_aff, np.arange(T))
     assert_out_close(np_(out), ref, what=f"T={T}/{variant}/{layout}")
+
+
+# Segment sizes around the 16-, 32-, 64- and 128-row edges of the prefill
+# tiles (16-row MFMA row groups in gate/up, 32 in down, 128-row tiles) and
+# the decode kernels' 16-row passes; the last expert (81 routes) makes the
+# 833 tokens of k = 2 whose shared segment ends in a 65-row partial tile.
+SEG_SIZES = [1, 15, 16, 17, 31, 32, 33, 63, 64, 65, 96, 127, 128, 129, 255, 256, 257, 81]
+
+
+@pytest.mark.parametrize("shared", [False, True])
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("variant,activation", [("prefill", "swiglu"), ("prefill_a8", "swiglu"),
+                                                ("decode", "swiglu"), ("prefill", "relu2"),
+                                                ("prefill_a8", "relu2")])
+def test_fused_segment_size_sweep(variant, activation, layout, shared):
+    """Crafted ids give the experts exactly SEG_SIZES routes each (tokens
+    shuffled, so each segment's rows come from scattered tokens); every
+    output row is compared with the oracle."""
+    E, k = len(SEG_SIZES), 2
+    labels = np.repeat(np.arange(E, dtype=np.int32), SEG_SIZES)
+    np.random.default_rng(31).shuffle(labels)
+    T = labels.size // k
+    ids_np = labels.reshape(T, k)
+    assert T % TILE_M == 65 and np.array_equal(oracle.sort_by_expert(ids_np, E)[0], SEG_SIZES)
+    cfg = synth.MoeConfig("seg", T=T, H=512, I=256, E=E, k=k, shared=shared)
+    c = gpu_case(cfg, seed=31, activation=activation)
+    aff_np = synth.random_affinities(T, k, seed=31).numpy()
+    out = _fused(c, torch.from_numpy(ids_np).cuda(), torch.from_numpy(aff_np).cuda(),
+                 variant=variant, shared=shared, layout=layout, activation=activation)
+    torch.cuda.synchronize()
+    rows = np.arange(T)
+    xr = _xhat_rows(c, rows) if variant == "prefill_a8" else None
+    ref = oracle_rows(c, ids_np, aff_np, rows, with_shared=shared, xrows=xr)
+    assert_out_close(np_(out), ref, what=f"segments {variant}/{activation}/{layout}/shared={shared}")
 
 
 @pytest.mark.parametrize("layout", LAYOUTS)
@@ -629,9 +704,9 @@ def test_fused_prefill_a8_parity(name, layout):
     torch.cuda.synchronize()
     assert int(status.item()) == 0
     ref_ids, ref_aff = oracle.route_softmax_topk(np_(c["logits"]), cfg.k)
-    rows = sample_rows(cfg.T, FFN_SAMPLE[name], seed=4)
-    ref = oracle_rows(c, ref_ids, ref_aff, rows, xrows=_xhat_rows(c, rows))
-    assert_out_close(np_(out)[rows], ref, what=f"a8 {name}/{layout}")
+    rows = check_rows(name, cfg, ref_ids)
+    ref = oracle_cached((name, "swiglu", "a8"), c, ref_ids, ref_aff, rows, xrows=_xhat_rows(c, rows))
+    assert_out_close(np_(out)[rows], ref, what=f"a8 {name}/{layout} ({len(rows)} rows)")
 
 
 @pytest.mark.parametrize("layout", LAYOUTS)
@@ -661,6 +736,7 @@ def test_fused_prefill_a8_relu2(name):
     out = _fused(c, ids, aff, variant="prefill_a8", activation="relu2")
     torch.cuda.synchronize()
     ref_ids, ref_aff = oracle.route_softmax_topk(np_(c["logits"]), cfg.k)
-    rows = sample_rows(cfg.T, FFN_SAMPLE[name], seed=5)
-    ref = oracle_rows(c, ref_ids, ref_aff, rows, xrows=_xhat_rows(c, rows))
-    assert_out_close(np_(out)[rows], ref, what=f"a8 relu2 {name}")
+    rows = check_rows(name, cfg, ref_ids)
+    ref = oracle_cached((name, "relu2", "a8"), c, ref_ids, ref_aff, rows,
+                        xrows=_xhat_rows(c, rows))
+    assert_out_close(np_(out)[rows], ref, what=f"a8 relu2 {name} ({len(rows)} rows)")
