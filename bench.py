@@ -38,8 +38,12 @@ def expert_bytes(H, I):
     return 3 * H * I + 4 * (2 * I // 128) * (H // 128) + 4 * (H // 128) * (I // 128)
 
 
-def kernel_bytes(name, cfg, n_active, with_shared):
-    """Algorithmic HBM bytes one launch of a kernel must move."""
+def kernel_work(name, cfg, n_active, with_shared):
+    """(bound, algorithmic work of one launch) of a kernel: HBM bytes that the
+    method itself must move through it, or MFMA flops.  Only the method's
+    data counts (the active experts' weights and scales, x, out, ids and
+    affinities, logits); per-route contribution rows, activations between
+    the GEMMs and the sort maps are implementation traffic and do not."""
     T, H, I, k = cfg.T, cfg.H, cfg.I, cfg.k
     R = T * k
     nseg = n_active + (1 if with_shared else 0)
@@ -47,16 +51,16 @@ def kernel_bytes(name, cfg, n_active, with_shared):
     w13 = 2 * I * H + 4 * (2 * I // 128) * (H // 128)
     w2 = H * I + 4 * (H // 128) * (I // 128)
     if name == "decode_fused_expert":
-        return nseg * (w13 + w2) + 2 * T * H + 4 * rows * H
-    if name.endswith("gateup_swiglu"):
-        return nseg * w13 + 2 * T * H + 2 * rows * I
-    if name.endswith("down"):
-        return nseg * w2 + 2 * rows * I + 4 * rows * H
+        return "hbm", nseg * (w13 + w2) + 2 * T * H + 8 * R
+    if name == "prefill_gateup_swiglu":
+        return "mfma", 2.0 * rows * 2 * I * H
+    if name == "prefill_down":
+        return "mfma", 2.0 * rows * H * I
     if name == "combine":
-        return 4 * rows * H + 8 * R + 4 * T * H
+        return "hbm", 4 * T * H + 8 * R
     if name == "route_topk_softmax":
-        return 4 * T * cfg.E + 8 * R
-    return None
+        return "hbm", 4 * T * cfg.E + 8 * R
+    return None, None
 
 
 def step_bytes(cfg, n_active, with_shared):
@@ -104,7 +108,13 @@ def cpu_baseline(case, cfg, max_tokens):
     oracle.moe_ffn(x, w13, w13s, w2, w2s, remap, aff, sh)
     t3 = time.perf_counter()
     secs = (t1 - t0) + (t3 - t2)
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except Exception:  # pragma: no cover
+        affinity = None
     return {"value": round(n / secs, 2), "unit": "tokens/s", "cores": int(threads),
+            "cores_note": "threads of the BLAS pool the oracle ran on",
+            "host_cpus": os.cpu_count(), "host_cpus_usable": affinity,
             "kind": "oracle",
             "sample": f"{n} of {cfg.T} tokens of {cfg.name}: route + sort + expert FFN in numpy "
                       f"float64 ({len(uniq)} experts dequantised); host copy of weights not timed",
@@ -192,6 +202,50 @@ def profiled_traffic(kernel, workload):
     if h.hexdigest()[:16] != got["source_sha256"]:
         return None
     return int(got["traffic_bytes_per_launch"])
+
+
+def roofline_of(prof, cfg, n_active, kernel=None):
+    """Roofline object for `kernel` (default: the FFN kernel with the largest
+    total time): algorithmic work per launch / its average HIP-event
+    duration, against the published peak of its bound."""
+    if kernel is None:
+        ffn = [n for n in prof if n in ("decode_fused_expert", "prefill_gateup_swiglu",
+                                        "prefill_down")]
+        kernel = max(ffn, key=lambda n: prof[n][0] * prof[n][1])
+    bound, work = kernel_work(kernel, cfg, n_active, cfg.shared)
+    us = prof[kernel][1] * 1e3
+    if bound == "hbm":
+        ach, peak, unit = work / (us * 1e-6) / 1e9, HBM_PEAK_GBS, "GB/s"
+    else:
+        ach, peak, unit = work / (us * 1e-6) / 1e12, BF16_PEAK_TFLOPS, "TFLOP/s"
+    out = {"bound": bound, "kernel": kernel, "achieved": round(ach, 1), "peak": peak,
+           "unit": unit, "frac": round(ach / peak, 4),
+           "traffic": profiled_traffic(kernel, cfg.name), "traffic_unit": "bytes per launch",
+           "avg_us": round(us, 3)}
+    out["bytes_per_launch" if bound == "hbm" else "flops_per_launch"] = work
+    return out
+
+
+def workload_report(cfg, m):
+    """Step, per-kernel, roofline and fused-call figures of one workload."""
+    flops = step_flops(cfg, cfg.shared)
+    sb = step_bytes(cfg, m["n_active"], cfg.shared)
+    ms = m["ms_per_step"]
+    prof = m["prof"]
+    out = {"workload": cfg.name, "T": cfg.T, "hidden": cfg.H, "moe_inter": cfg.I,
+           "experts": cfg.E, "top_k": cfg.k, "shared_expert": cfg.shared,
+           "active_experts": m["n_active"], "weight_sets": m["L"],
+           "ms_per_step": round(ms, 5), "tokens_per_s": round(cfg.T / (ms * 1e-3), 1),
+           "step": {"algorithmic_bytes": sb, "GB_per_s": round(sb / (ms * 1e-3) / 1e9, 1),
+                    "hbm_frac": round(sb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                    "TFLOP_per_s": round(flops / (ms * 1e-3) / 1e12, 1),
+                    "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)},
+           "kernels": {n: {"launches": c, "avg_us": round(t * 1e3, 3)} for n, (c, t) in prof.items()},
+           "roofline": roofline_of(prof, cfg, m["n_active"])}
+    if "prefill_down" in prof:
+        out["contributions"] = ("per-route rows in block floating point (8 values share an "
+                                "exponent byte, 16-bit mantissas), summed in fp32")
+    return out
 
 
 def fused_call_graph(cfg, m, samples=7, replays=50):
@@ -489,34 +543,6 @@ def fused_variant_bench(cfg, dev, L, seed=0, activation="swiglu", variant="auto"
     return out
 
 
-def prefill_summary(cfg, m):
-    """MFMA roofline of the prefill workload (secondary object of the JSON line)."""
-    R = cfg.T * cfg.k + (cfg.T if cfg.shared else 0)
-    flops_gateup = 2.0 * R * 2 * cfg.I * cfg.H
-    flops_down = 2.0 * R * cfg.H * cfg.I
-    tot = flops_gateup + flops_down
-    prof = m["prof"]
-    out = {"workload": cfg.name, "T": cfg.T, "hidden": cfg.H, "moe_inter": cfg.I,
-           "experts": cfg.E, "top_k": cfg.k, "shared_expert": cfg.shared,
-           "active_experts": m["n_active"],
-           "ms_per_step": round(m["ms_per_step"], 5),
-           "tokens_per_s": round(cfg.T / (m["ms_per_step"] * 1e-3), 1),
-           "TFLOP_per_s": round(tot / (m["ms_per_step"] * 1e-3) / 1e12, 1),
-           "mfma_frac_step": round(tot / (m["ms_per_step"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
-           "kernels": {n: {"launches": c, "avg_us": round(ms * 1e3, 3)} for n, (c, ms) in prof.items()}}
-    if "prefill_gateup_swiglu" in prof:
-        us = prof["prefill_gateup_swiglu"][1] * 1e3
-        ach = flops_gateup / (us * 1e-6) / 1e12
-        out["roofline"] = {"bound": "mfma", "kernel": "prefill_gateup_swiglu",
-                           "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS,
-                           "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4),
-                           "traffic": profiled_traffic("prefill_gateup_swiglu", cfg.name),
-                           "traffic_unit": "bytes per launch",
-                           "flops_per_launch": flops_gateup,
-                           "avg_us": round(us, 3)}
-    return out
-
-
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -544,6 +570,10 @@ def main():
                     help="skip the router measurements (moe_route_proj, router variants)")
     ap.add_argument("--no-vendor-gemm", action="store_true",
                     help="skip timing torch.matmul at the gate/up shape (context only)")
+    ap.add_argument("--no-extra-workloads", action="store_true",
+                    help="skip the decode512 and prefill16k_wide objects")
+    ap.add_argument("--no-rowmajor", action="store_true",
+                    help="skip the fused call on row-major (unpacked) weights")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB, 5 times (PMC byte-counter "
                          "calibration)")
@@ -579,17 +609,6 @@ def main():
     n_active, ms_per_step, ms_profiled, prof = m["n_active"], m["ms_per_step"], m["ms_profiled"], m["prof"]
     x, logits, wsets, L = m["x"], m["logits"], m["wsets"], m["L"]
     kernels = {n: {"launches": c, "avg_us": round(ms * 1e3, 3)} for n, (c, ms) in prof.items()}
-    dom = max(prof.items(), key=lambda kv: kv[1][0] * kv[1][1])[0]
-    dom_bytes = kernel_bytes(dom, cfg, n_active, cfg.shared)
-    dom_ms = prof[dom][1]
-    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9 if dom_bytes else None
-    roofline = {"bound": "hbm", "kernel": dom,
-                "achieved": round(achieved, 1) if achieved else None,
-                "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4) if achieved else None,
-                "traffic": profiled_traffic(dom, cfg.name),
-                "traffic_unit": "bytes per launch",
-                "bytes_per_launch": dom_bytes, "avg_us": round(dom_ms * 1e3, 3)}
 
     sb = step_bytes(cfg, n_active, cfg.shared)
     sf = step_flops(cfg, cfg.shared)
@@ -611,8 +630,11 @@ def main():
                    "experts": cfg.E, "top_k": cfg.k, "shared_expert": cfg.shared,
                    "weights": "E4M3FN, fp32 128x128 block scales", "weight_sets": L,
                    "variant": args.variant, "weight_layout": args.layout,
+                   "weight_prep": ("packed once at load time into the tile-coalesced layout "
+                                   "(moe_pack_w8), outside the timed steps")
+                                  if args.layout == "tiled" else "as given (row-major)",
                    "active_experts": n_active},
-        "roofline": roofline,
+        "roofline": roofline_of(prof, cfg, n_active),
         "step": {"algorithmic_bytes": sb, "GB_per_s": round(sb / (ms_per_step * 1e-3) / 1e9, 1),
                  "hbm_frac": round(sb / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                  "TFLOP_per_s": round(sf / (ms_per_step * 1e-3) / 1e12, 2),
@@ -621,20 +643,37 @@ def main():
     }
     log("fused call in a HIP graph ...")
     result["fused_call"] = fused_call_graph(cfg, m)
-    if args.prefill_workload:
-        pcfg = synth.CONFIGS[args.prefill_workload]
-        del m
+    if args.layout == "tiled" and not args.no_rowmajor:
+        log("fused call on the row-major weights (no packing) ...")
+        rm = dict(m, runs=[binding.MoeStep(x, logits, cfg.k, w["w13"], w["w13_scale"], w["w2"],
+                                           w["w2_scale"], shared=w["shared"], variant=args.variant,
+                                           layout="rowmajor") for w in wsets])
+        result["fused_call_rowmajor"] = fused_call_graph(cfg, rm)
+        del rm
+    case0 = dict(x=x, logits=logits, **wsets[0]) if not args.no_cpu_baseline else None
+    del m, wsets
+    torch.cuda.empty_cache()
+    # the other workloads: decode at 512 tokens (HBM-bound) and the two
+    # prefill workloads (MFMA-bound), each with its own step, kernels,
+    # roofline and graph-timed fused call
+    extra = [(args.prefill_workload, "prefill", 2, args.prefill_steps)]
+    if not args.no_extra_workloads:
+        extra += [("decode512", "decode512", max(1, args.weight_sets), args.steps),
+                  ("prefill16k_wide", "prefill16k_wide", 2, max(5, args.prefill_steps // 5))]
+    for wname, key, nsets, nsteps in extra:
+        if not wname:
+            continue
+        wcfg = synth.CONFIGS[wname]
+        wm = measure(wcfg, nsets, nsteps, args.prefill_warmup if wcfg.T > 4096 else args.warmup,
+                     "auto", args.layout, args.seed, dev)
+        result[key] = workload_report(wcfg, wm)
+        log(f"{wname} fused call in a HIP graph ...")
+        result[key]["fused_call"] = fused_call_graph(wcfg, wm, replays=50 if wcfg.T <= 8192 else 10)
+        del wm
         torch.cuda.empty_cache()
-        pm = measure(pcfg, 2, args.prefill_steps, args.prefill_warmup, "auto", args.layout,
-                     args.seed, dev)
-        result["prefill"] = prefill_summary(pcfg, pm)
-        log("prefill fused call in a HIP graph ...")
-        result["prefill"]["fused_call"] = fused_call_graph(pcfg, pm)
-        del pm
-        torch.cuda.empty_cache()
-        if not args.no_vendor_gemm:
+        if key == "prefill" and not args.no_vendor_gemm:
             log("vendor bf16 GEMM at the gate/up shape (context) ...")
-            result["prefill"]["vendor_bf16_gemm"] = vendor_gemm(pcfg, dev)
+            result[key]["vendor_bf16_gemm"] = vendor_gemm(wcfg, dev)
     if not args.no_relu2:
         result["relu2"] = [fused_variant_bench(cfg, dev, max(1, args.weight_sets), args.seed,
                                                activation="relu2")]
@@ -653,10 +692,9 @@ def main():
         if args.prefill_workload:
             result["route_proj"].append(
                 route_proj_bench(synth.CONFIGS[args.prefill_workload], dev, 4, args.seed))
-    if not args.no_cpu_baseline:
+    if case0 is not None:
         log("cpu baseline (oracle) ...")
-        case = dict(x=x, logits=logits, **wsets[0])
-        result["cpu_baseline"] = cpu_baseline(case, cfg, args.cpu_tokens)
+        result["cpu_baseline"] = cpu_baseline(case0, cfg, args.cpu_tokens)
     print(json.dumps(result), flush=True)
 
 
