@@ -20,6 +20,7 @@ MOE_STATUS_BAD_EXPERT_ID = 1
 MOE_STATUS_NONFINITE_LOGIT = 2
 MOE_MAX_EXPERTS = 1024
 MOE_MAX_TOPK = 16
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 VARIANTS = {"auto": 0, "decode": 1, "prefill": 2, "prefill_a8": 3}
 ACTIVATIONS = {"swiglu": 0, "relu2": 1}
 LAYOUTS = {"rowmajor": 0, "tiled": 1}
@@ -28,7 +29,8 @@ EXPORTED = (
     "moe_last_error", "moe_route", "moe_route_sigmoid", "moe_route_proj_workspace_bytes",
     "moe_route_proj",
     "moe_sort_workspace_bytes", "moe_sort",
-    "moe_fused_workspace_bytes", "moe_fused_w8a16", "moe_fused_w8a16_ex", "moe_quant_e4m3_rows",
+    "moe_fused_workspace_bytes", "moe_fused_w8a16", "moe_fused_w8a16_ex",
+    "moe_fused_w8a16_noalloc", "moe_quant_e4m3_rows",
     "moe_decode_e4m3fn",
     "moe_pack_w8",
     "moe_profile_enable", "moe_profile_collect", "moe_profile_count", "moe_profile_stat",
@@ -85,6 +87,9 @@ def load_library():
                                     ctypes.POINTER(ExpertW8), vp, vp, vp, sz, i32, i32, vp]
     lib.moe_fused_w8a16_ex.restype = i32
     lib.moe_fused_w8a16_ex.argtypes = list(lib.moe_fused_w8a16.argtypes[:-1]) + [i32, vp]
+    lib.moe_fused_w8a16_noalloc.restype = i32
+    lib.moe_fused_w8a16_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                            ctypes.POINTER(ExpertW8), vp, vp, i32, i32, i32, vp]
     lib.moe_pack_w8.restype = i32
     lib.moe_pack_w8.argtypes = [vp, vp, i64, i32, i32, vp]
     lib.moe_quant_e4m3_rows.restype = i32
@@ -285,16 +290,30 @@ def fused_w8a16(x, w13, w13_scale, w2, w2_scale, ids, aff, shared=None, out=None
         out = torch.empty((T, H), dtype=torch.float32, device=dev)
     else:
         _need(out, "out", torch.float32, dev, (T, H))
+    if status is not None:
+        _need(status, "status", torch.int32, dev)
+    head = (_ptr(x), _ptr(w13), _ptr(w13_scale), _ptr(w2), _ptr(w2_scale), _ptr(ids), _ptr(aff),
+            T, H, I, E, k, sh_ptr, _ptr(out), _ptr(status))
+    if isinstance(ws, str) and ws == "noalloc":
+        # the library's own device scratch array: no workspace argument
+        _check(lib.moe_fused_w8a16_noalloc(*head, _layout(layout), v, act, _stream(dev)))
+        return out
     need = int(lib.moe_fused_workspace_bytes(T, H, I, E, k, int(shared is not None), v))
     if ws is None:
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    if status is not None:
-        _need(status, "status", torch.int32, dev)
-    _check(lib.moe_fused_w8a16_ex(_ptr(x), _ptr(w13), _ptr(w13_scale), _ptr(w2),
-                                  _ptr(w2_scale), _ptr(ids), _ptr(aff), T, H, I, E, k, sh_ptr,
-                                  _ptr(out), _ptr(status), _ptr(ws), ws.numel(), _layout(layout),
-                                  v, act, _stream(dev)))
+    _check(lib.moe_fused_w8a16_ex(*head, _ptr(ws), ws.numel(), _layout(layout), v, act,
+                                  _stream(dev)))
     return out
+
+
+def fused_w8a16_noalloc(x, w13, w13_scale, w2, w2_scale, ids, aff, out, shared=None,
+                        status=None, variant="auto", layout="rowmajor", activation="swiglu"):
+    """fused_w8a16 through moe_fused_w8a16_noalloc: the same call with the
+    library's device scratch array as its workspace (``out`` is required, so
+    that nothing is allocated)."""
+    return fused_w8a16(x, w13, w13_scale, w2, w2_scale, ids, aff, shared=shared, out=out,
+                       ws="noalloc", status=status, variant=variant, layout=layout,
+                       activation=activation)
 
 
 def quant_e4m3_rows(x: torch.Tensor):

@@ -9,6 +9,8 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "common.hpp"
 #include "plan.hpp"
 
@@ -77,6 +79,19 @@ static FusedLayout fused_layout(int T, int H, int I, int E, int k, int has_share
     L.xs = fp8_x ? take(sizeof(float) * (size_t)T) : 0;
     L.total = o;
     return L;
+}
+
+// AUTO: the decode variant up to 16 routes per expert and the self-routed
+// batch size, the prefill GEMMs above.  Measured at H = 2048, I = 512,
+// E = 256, k = 8: T = 512 decode 172 / prefill 195 us, T = 768 267 / 204,
+// T = 1024 296 / 218 (past 4096 routes decode needs the sort and a second
+// M tile).
+static int resolve_variant(int T, int H, int I, int E, int k, int act, int variant) {
+    if (variant != MOE_VARIANT_AUTO) return variant;
+    const long long R = (long long)T * k;
+    return (R <= 16LL * E && R <= decode_self_routed_max_routes()) || !prefill_supported(H, I, act)
+               ? MOE_VARIANT_DECODE
+               : MOE_VARIANT_PREFILL;
 }
 
 static int check_route_args(int T, int E, int k) {
@@ -277,17 +292,7 @@ int moe_fused_w8a16_ex(const void* x, const uint8_t* w13, const float* w13_scale
     }
     const int has_shared = shared ? 1 : 0;
     const bool fp8_x = variant == MOE_VARIANT_PREFILL_A8;
-    // AUTO: the decode variant up to 16 routes per expert and the self-routed
-    // batch size, the prefill GEMMs above.  Measured at H = 2048, I = 512,
-    // E = 256, k = 8: T = 512 decode 172 / prefill 195 us, T = 768 267 / 204,
-    // T = 1024 296 / 218 (past 4096 routes decode needs the sort and a second
-    // M tile).
-    if (variant == MOE_VARIANT_AUTO) {
-        const long long R = (long long)T * k;
-        variant = (R <= 16LL * E && R <= decode_self_routed_max_routes()) || !prefill_supported(H, I, act)
-                      ? MOE_VARIANT_DECODE
-                      : MOE_VARIANT_PREFILL;
-    }
+    variant = resolve_variant(T, H, I, E, k, act, variant);
     const FusedLayout L = fused_layout(T, H, I, E, k, has_shared, variant);
     if (!ws || ws_bytes < L.total) {
         set_error("moe_fused_w8a16: workspace of %zu bytes needed (got %zu)", L.total, ws_bytes);
@@ -354,6 +359,86 @@ int moe_fused_w8a16(const void* x, const uint8_t* w13, const float* w13_scale,
     return moe_fused_w8a16_ex(x, w13, w13_scale, w2, w2_scale, ids, aff, T, H, I, E, k, shared,
                               out, status, ws, ws_bytes, weight_layout, variant, MOE_ACT_SWIGLU,
                               stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- no-allocation entry
+// The workspace of moe_fused_w8a16_noalloc: one file-scope device array.  Each
+// GPU the library runs on holds its own copy until the process ends; host
+// code never uses the array's name as an address (it is a host-side stand-in
+// there), only the device address taken once per device below.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace moe {
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of this device's copy of `scratch` (the device must be
+// current), taken on its first use and kept.
+int scratch_address(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        set_error("moe_fused_w8a16_noalloc: no usable current device (%s)",
+                  e != hipSuccess ? hipGetErrorString(e) : "device index out of range");
+        return MOE_EHIP;
+    }
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr) {
+            set_error("moe_fused_w8a16_noalloc: hipGetSymbolAddress(scratch) failed: %s",
+                      hipGetErrorString(e));
+            return MOE_EHIP;
+        }
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return MOE_OK;
+}
+}  // namespace
+}  // namespace moe
+
+extern "C" {
+
+int moe_fused_w8a16_noalloc(const void* x, const uint8_t* w13, const float* w13_scale,
+                            const uint8_t* w2, const float* w2_scale, const int32_t* ids,
+                            const float* aff, int T, int H, int I, int E, int k,
+                            const moe_expert_w8* shared, float* out, int32_t* status,
+                            int weight_layout, int variant, int activation, void* stream) {
+    g_err[0] = 0;
+    if (activation != MOE_ACT_SWIGLU && activation != MOE_ACT_RELU2) {
+        set_error("unknown activation %d", activation);
+        return MOE_EINVAL;
+    }
+    if (int rc = check_route_args(T, E, k)) return rc;
+    if (H < 128 || I < 128 || H % 128 || I % 128) {
+        set_error("H and I must be positive multiples of 128 (got H=%d, I=%d)", H, I);
+        return MOE_EUNSUPPORTED;
+    }
+    if (variant < MOE_VARIANT_AUTO || variant > MOE_VARIANT_PREFILL_A8) {
+        set_error("unknown variant %d", variant);
+        return MOE_EINVAL;
+    }
+    if (T == 0) return MOE_OK;
+    const int act = activation == MOE_ACT_RELU2 ? ACT_RELU2 : ACT_SWIGLU;
+    const int v = resolve_variant(T, H, I, E, k, act, variant);
+    const size_t need = fused_layout(T, H, I, E, k, shared ? 1 : 0, v).total;
+    if (need > (size_t)MOE_NOALLOC_SCRATCH_BYTES) {
+        set_error("moe_fused_w8a16_noalloc: this call needs %zu bytes of workspace, more than the "
+                  "%zu-byte device scratch array (use moe_fused_w8a16 with a workspace)",
+                  need, (size_t)MOE_NOALLOC_SCRATCH_BYTES);
+        return MOE_EUNSUPPORTED;
+    }
+    void* ws = nullptr;
+    if (int rc = scratch_address(&ws)) return rc;
+    return moe_fused_w8a16_ex(x, w13, w13_scale, w2, w2_scale, ids, aff, T, H, I, E, k, shared,
+                              out, status, ws, (size_t)MOE_NOALLOC_SCRATCH_BYTES, weight_layout, v,
+                              activation, stream);
 }
 
 int moe_pack_w8(const uint8_t* src, uint8_t* dst, int64_t n_mats, int rows, int cols,

@@ -281,6 +281,35 @@ int moe_fused_w8a16_ex(const void* x,
                        int weight_layout, int variant, int activation, void* stream);
 
 /*
+ * moe_fused_w8a16_noalloc -- moe_fused_w8a16_ex for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same call, kernels and results, with
+ * no workspace argument.  Its workspace is one device array of
+ * MOE_NOALLOC_SCRATCH_BYTES inside the library; each GPU it runs on holds its
+ * own copy from the first call on that device until the process ends.
+ *   Every argument means what it means for moe_fused_w8a16_ex; the call runs
+ *   on the current device, and `stream` must belong to it.
+ *   A call whose workspace (moe_fused_workspace_bytes of the variant it runs;
+ *   AUTO resolved as moe_fused_w8a16 resolves it) exceeds the array returns
+ *   MOE_EUNSUPPORTED before anything is enqueued, with moe_last_error()
+ *   saying so.  The array keeps the last call's contents; nothing in it needs
+ *   to start at zero.  Calls on one GPU share the array, so calls that
+ *   overlap on one GPU (other streams, or other threads) race: serialise
+ *   them.  Nothing is allocated or freed: not by this call, its kernels or
+ *   the library routines it uses.  At 64 MiB the array fits, for example,
+ *   the decode variant at T = 512, H = 2048, I = 512, E = 256, k = 8.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+int moe_fused_w8a16_noalloc(const void* x,
+                            const uint8_t* w13, const float* w13_scale,
+                            const uint8_t* w2, const float* w2_scale,
+                            const int32_t* ids, const float* aff,
+                            int T, int H, int I, int E, int k,
+                            const moe_expert_w8* shared, float* out,
+                            int32_t* status, int weight_layout, int variant, int activation,
+                            void* stream);
+
+/*
  * moe_quant_e4m3_rows -- the per-token activation quantisation that
  * MOE_VARIANT_PREFILL_A8 applies to x, exposed so it can be checked on its
  * own.  For each row t:
