@@ -451,7 +451,7 @@ def router_variants_bench(cfg, dev, seed=0, calls=64, samples=7, replays=20):
 
 
 def fused_variant_bench(cfg, dev, L, seed=0, activation="swiglu", variant="auto", samples=7,
-                        replays=50):
+                        replays=50, weight_format="e4m3_128"):
     """The fused call (sort + expert FFN + expert sum) for another activation
     (relu^2: non-gated experts, up projection [I, H], relu^2, down) or variant
     (prefill_a8: x quantised to E4M3 per token, gate/up on the FP8 MFMA) on the
@@ -466,19 +466,19 @@ def fused_variant_bench(cfg, dev, L, seed=0, activation="swiglu", variant="auto"
 
     from block_scaled_fp8_amd import binding, synth
     T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
-    log(f"{activation} experts, variant {variant}, on {cfg.name}: {L} weight sets")
+    log(f"{activation} experts, variant {variant}, {weight_format} weights, on {cfg.name}: "
+        f"{L} weight sets")
     x, logits = synth.make_activations(cfg, seed, dev)
     runs = []
     for i in range(L):
-        w = synth.make_weights(cfg, seed + 100 * i, dev, activation=activation)
-        p = dict(w, w13=binding.pack_w8(w["w13"]), w2=binding.pack_w8(w["w2"]))
-        if w["shared"] is not None:
-            p["shared"] = dict(w["shared"], w13=binding.pack_w8(w["shared"]["w13"]),
-                               w2=binding.pack_w8(w["shared"]["w2"]))
+        w = synth.make_weights(cfg, seed + 100 * i, dev, activation=activation,
+                               weight_format=weight_format)
+        p = binding.pack_weights(w, weight_format)
         del w
         runs.append(binding.MoeStep(x, logits, k, p["w13"], p["w13_scale"], p["w2"],
                                     p["w2_scale"], shared=p["shared"], layout="tiled",
-                                    variant=variant, activation=activation))
+                                    variant=variant, activation=activation,
+                                    weight_format=weight_format))
     ids, _ = binding.route(logits, k)
     n_active = int((torch.bincount(ids.reshape(-1).long(), minlength=E) > 0).sum().item())
     for r in runs:
@@ -517,10 +517,13 @@ def fused_variant_bench(cfg, dev, L, seed=0, activation="swiglu", variant="auto"
     nseg = n_active + (1 if cfg.shared else 0)
     n13 = I if activation == "relu2" else 2 * I
     flops = 2.0 * H * (n13 + I) * rows
-    wbytes = nseg * ((n13 + I) * H + 4 * (n13 // 128) * (H // 128) + 4 * (H // 128) * (I // 128))
+    if weight_format == "mxfp4":   # half a byte a weight + one scale byte per 32
+        wbytes = nseg * ((n13 + I) * H // 2 + (n13 + I) * H // 32)
+    else:
+        wbytes = nseg * ((n13 + I) * H + 4 * (n13 // 128) * (H // 128) + 4 * (H // 128) * (I // 128))
     nbytes = wbytes + 2 * T * H + 4 * T * H + 8 * T * k
     out = {"workload": cfg.name, "activation": activation, "variant": variant,
-           "active_experts": n_active, "weight_sets": L,
+           "weights": weight_format, "active_experts": n_active, "weight_sets": L,
            "protocol": f"HIP graph of one fused call per weight set, median of {samples} x "
                        f"{replays} replays",
            "us_per_call": round(us, 2), "tokens_per_s": round(T / (us * 1e-6), 1),
@@ -529,6 +532,15 @@ def fused_variant_bench(cfg, dev, L, seed=0, activation="swiglu", variant="auto"
            "TFLOP_per_s": round(flops / (us * 1e-6) / 1e12, 1),
            "mfma_frac_bf16": round(flops / (us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4),
            "kernels": {n: {"launches": c, "avg_us": round(ms * 1e3, 3)} for n, (c, ms) in prof.items()}}
+    if "decode_fused_expert_mxfp4" in prof:
+        # the weight-streaming kernel against HBM: weights + scales, x, ids and aff
+        kus = prof["decode_fused_expert_mxfp4"][1] * 1e3
+        kb = wbytes + 2 * T * H + 8 * T * k
+        out["roofline"] = {"bound": "hbm", "kernel": "decode_fused_expert_mxfp4",
+                           "bytes_per_launch": kb, "avg_us": round(kus, 3),
+                           "achieved": round(kb / (kus * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                           "unit": "GB/s",
+                           "frac": round(kb / (kus * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
     a8 = [n for n in prof if n.endswith("_a8")]
     if a8:
         # the fp8 x fp8 gate/up (or up) GEMM against the FP8 MFMA peak
@@ -570,6 +582,8 @@ def main():
                     help="skip the router measurements (moe_route_proj, router variants)")
     ap.add_argument("--no-vendor-gemm", action="store_true",
                     help="skip timing torch.matmul at the gate/up shape (context only)")
+    ap.add_argument("--no-mxfp4", action="store_true",
+                    help="skip the MXFP4-weight measurement (moe_fused_mxfp4)")
     ap.add_argument("--no-extra-workloads", action="store_true",
                     help="skip the decode512 and prefill16k_wide objects")
     ap.add_argument("--no-rowmajor", action="store_true",
@@ -680,6 +694,14 @@ def main():
         if args.prefill_workload:
             result["relu2"].append(fused_variant_bench(synth.CONFIGS[args.prefill_workload], dev,
                                                        2, args.seed, activation="relu2"))
+    if not args.no_mxfp4:
+        # MXFP4 weights (E2M1 codes, E8M0 per 32): the weight stream halves
+        result["mxfp4"] = [fused_variant_bench(cfg, dev, max(1, args.weight_sets), args.seed,
+                                               weight_format="mxfp4")]
+        if not args.no_extra_workloads:
+            result["mxfp4"].append(fused_variant_bench(synth.CONFIGS["decode512"], dev,
+                                                       max(1, args.weight_sets), args.seed,
+                                                       weight_format="mxfp4"))
     if args.prefill_workload and not args.no_a8:
         result["prefill_a8"] = fused_variant_bench(synth.CONFIGS[args.prefill_workload], dev, 2,
                                                    args.seed, variant="prefill_a8")

@@ -30,9 +30,9 @@ EXPORTED = (
     "moe_route_proj",
     "moe_sort_workspace_bytes", "moe_sort",
     "moe_fused_workspace_bytes", "moe_fused_w8a16", "moe_fused_w8a16_ex",
-    "moe_fused_w8a16_noalloc", "moe_quant_e4m3_rows",
+    "moe_fused_w8a16_noalloc", "moe_fused_mxfp4", "moe_quant_e4m3_rows",
     "moe_decode_e4m3fn",
-    "moe_pack_w8",
+    "moe_pack_w8", "moe_pack_mx_scales",
     "moe_profile_enable", "moe_profile_collect", "moe_profile_count", "moe_profile_stat",
 )
 
@@ -87,9 +87,13 @@ def load_library():
                                     ctypes.POINTER(ExpertW8), vp, vp, vp, sz, i32, i32, vp]
     lib.moe_fused_w8a16_ex.restype = i32
     lib.moe_fused_w8a16_ex.argtypes = list(lib.moe_fused_w8a16.argtypes[:-1]) + [i32, vp]
+    lib.moe_fused_mxfp4.restype = i32
+    lib.moe_fused_mxfp4.argtypes = list(lib.moe_fused_w8a16_ex.argtypes)
     lib.moe_fused_w8a16_noalloc.restype = i32
     lib.moe_fused_w8a16_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                             ctypes.POINTER(ExpertW8), vp, vp, i32, i32, i32, vp]
+    lib.moe_pack_mx_scales.restype = i32
+    lib.moe_pack_mx_scales.argtypes = [vp, vp, i64, i32, i32, vp]
     lib.moe_pack_w8.restype = i32
     lib.moe_pack_w8.argtypes = [vp, vp, i64, i32, i32, vp]
     lib.moe_quant_e4m3_rows.restype = i32
@@ -250,27 +254,70 @@ def pack_w8(w: torch.Tensor) -> torch.Tensor:
     return out
 
 
-def fused_w8a16(x, w13, w13_scale, w2, w2_scale, ids, aff, shared=None, out=None, ws=None,
-                status=None, variant="auto", layout="rowmajor", activation="swiglu"):
-    """Routed expert FFN with block-scaled FP8 weights -> out [T, H] fp32.
+def pack_mx_scales(s: torch.Tensor) -> torch.Tensor:
+    """MXFP4 E8M0 scales [..., rows, K/32] uint8 -> the tiled layout's order
+    (same shape and bytes, reordered on the GPU)."""
+    lib = load_library()
+    _need(s, "s", torch.uint8)
+    rows, cols = s.shape[-2], s.shape[-1]
+    n = s.numel() // max(1, rows * cols)
+    out = torch.empty_like(s)
+    _check(lib.moe_pack_mx_scales(_ptr(s), _ptr(out), n, rows, cols, _stream(s.device)))
+    return out
 
-    x bf16 [T, H]; w13 uint8 [E, 2I, H] (activation "relu2": [E, I, H], the up
-    projection alone); w13_scale fp32 [E, rows/128, H/128]; w2 uint8 [E, H, I];
-    w2_scale fp32 [E, H/128, I/128]; ids int32 [T, k]; aff fp32 [T, k];
-    shared: None or a dict with the four tensors of one expert."""
+
+def pack_weights(w: dict, weight_format="e4m3_128") -> dict:
+    """A copy of one weight set (w13, w13_scale, w2, w2_scale and an optional
+    "shared" dict of the same) in the tiled layout: codes by pack_w8 and,
+    for MXFP4, scales by pack_mx_scales."""
+    mx = weight_format == "mxfp4"
+
+    def one(d):
+        r = dict(d, w13=pack_w8(d["w13"]), w2=pack_w8(d["w2"]))
+        if mx:
+            r["w13_scale"] = pack_mx_scales(d["w13_scale"])
+            r["w2_scale"] = pack_mx_scales(d["w2_scale"])
+        return r
+
+    out = one(w)
+    if w.get("shared") is not None:
+        out["shared"] = one(w["shared"])
+    return out
+
+
+def fused_w8a16(x, w13, w13_scale, w2, w2_scale, ids, aff, shared=None, out=None, ws=None,
+                status=None, variant="auto", layout="rowmajor", activation="swiglu",
+                weight_format="e4m3_128"):
+    """Routed expert FFN with block-scaled weights -> out [T, H] fp32.
+
+    x bf16 [T, H]; ids int32 [T, k]; aff fp32 [T, k]; shared: None or a dict
+    with the four tensors of one expert.  weight_format "e4m3_128": w13 uint8
+    [E, 2I, H] (activation "relu2": [E, I, H], the up projection alone),
+    w13_scale fp32 [E, rows/128, H/128], w2 uint8 [E, H, I], w2_scale fp32
+    [E, H/128, I/128].  weight_format "mxfp4" (moe_fused_mxfp4): w13 uint8
+    [E, rows, H/2] (two E2M1 codes a byte), w13_scale uint8 E8M0 [E, rows,
+    H/32], w2 [E, H, I/2], w2_scale [E, H, I/32]."""
     lib = load_library()
     _need(x, "x", torch.bfloat16)
     dev = x.device
     T, H = x.shape
     _need(w13, "w13", torch.uint8, dev)
     act = ACTIVATIONS[activation] if isinstance(activation, str) else int(activation)
+    mx = weight_format == "mxfp4"
+    if not mx and weight_format != "e4m3_128":
+        raise ValueError(f"unknown weight format {weight_format!r}")
     E, I2, H2 = w13.shape
     I = I2 // 2 if act == 0 else I2
-    if H2 != H or (act == 0 and I2 % 2):
+    if (H2 * 2 if mx else H2) != H or (act == 0 and I2 % 2):
         raise ValueError(f"w13 shape {tuple(w13.shape)} does not match x {tuple(x.shape)}")
-    _need(w13_scale, "w13_scale", torch.float32, dev, (E, -(-I2 // 128), -(-H // 128)))
-    _need(w2, "w2", torch.uint8, dev, (E, H, I))
-    _need(w2_scale, "w2_scale", torch.float32, dev, (E, -(-H // 128), -(-I // 128)))
+    if mx:
+        _need(w13_scale, "w13_scale", torch.uint8, dev, (E, I2, H // 32))
+        _need(w2, "w2", torch.uint8, dev, (E, H, I // 2))
+        _need(w2_scale, "w2_scale", torch.uint8, dev, (E, H, I // 32))
+    else:
+        _need(w13_scale, "w13_scale", torch.float32, dev, (E, -(-I2 // 128), -(-H // 128)))
+        _need(w2, "w2", torch.uint8, dev, (E, H, I))
+        _need(w2_scale, "w2_scale", torch.float32, dev, (E, -(-H // 128), -(-I // 128)))
     _need(ids, "ids", torch.int32, dev)
     k = ids.shape[1] if ids.dim() == 2 else -1
     if ids.dim() != 2 or ids.shape[0] != T:
@@ -278,10 +325,11 @@ def fused_w8a16(x, w13, w13_scale, w2, w2_scale, ids, aff, shared=None, out=None
     _need(aff, "aff", torch.float32, dev, (T, k))
     sh_ptr = None
     if shared is not None:
-        _need(shared["w13"], "shared.w13", torch.uint8, dev, (I2, H))
-        _need(shared["w13_scale"], "shared.w13_scale", torch.float32, dev, w13_scale.shape[1:])
-        _need(shared["w2"], "shared.w2", torch.uint8, dev, (H, I))
-        _need(shared["w2_scale"], "shared.w2_scale", torch.float32, dev, w2_scale.shape[1:])
+        sdt = torch.uint8 if mx else torch.float32
+        _need(shared["w13"], "shared.w13", torch.uint8, dev, w13.shape[1:])
+        _need(shared["w13_scale"], "shared.w13_scale", sdt, dev, w13_scale.shape[1:])
+        _need(shared["w2"], "shared.w2", torch.uint8, dev, w2.shape[1:])
+        _need(shared["w2_scale"], "shared.w2_scale", sdt, dev, w2_scale.shape[1:])
         sh = ExpertW8(shared["w13"].data_ptr(), shared["w13_scale"].data_ptr(),
                       shared["w2"].data_ptr(), shared["w2_scale"].data_ptr())
         sh_ptr = ctypes.pointer(sh)
@@ -296,13 +344,17 @@ def fused_w8a16(x, w13, w13_scale, w2, w2_scale, ids, aff, shared=None, out=None
             T, H, I, E, k, sh_ptr, _ptr(out), _ptr(status))
     if isinstance(ws, str) and ws == "noalloc":
         # the library's own device scratch array: no workspace argument
+        if mx:
+            raise ValueError("the no-allocation entry point takes E4M3FN weights")
         _check(lib.moe_fused_w8a16_noalloc(*head, _layout(layout), v, act, _stream(dev)))
         return out
-    need = int(lib.moe_fused_workspace_bytes(T, H, I, E, k, int(shared is not None), v))
+    # (MXFP4 weights run the decode variant's kernels: its workspace)
+    need = int(lib.moe_fused_workspace_bytes(T, H, I, E, k, int(shared is not None),
+                                             VARIANTS["decode"] if mx else v))
     if ws is None:
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    _check(lib.moe_fused_w8a16_ex(*head, _ptr(ws), ws.numel(), _layout(layout), v, act,
-                                  _stream(dev)))
+    fn = lib.moe_fused_mxfp4 if mx else lib.moe_fused_w8a16_ex
+    _check(fn(*head, _ptr(ws), ws.numel(), _layout(layout), v, act, _stream(dev)))
     return out
 
 
@@ -369,7 +421,8 @@ class MoeStep:
     stream of the tensors' device."""
 
     def __init__(self, x, logits, k, w13, w13_scale, w2, w2_scale, shared=None,
-                 variant="auto", layout="rowmajor", activation="swiglu"):
+                 variant="auto", layout="rowmajor", activation="swiglu",
+                 weight_format="e4m3_128"):
         lib = load_library()
         dev = x.device
         T, H = x.shape
@@ -380,12 +433,15 @@ class MoeStep:
         self.aff = torch.empty((T, k), dtype=torch.float32, device=dev)
         self.out = torch.empty((T, H), dtype=torch.float32, device=dev)
         # one checked call validates every argument and sizes the workspace
+        mx = weight_format == "mxfp4"
         self.ws = torch.empty(max(1, fused_workspace_bytes(T, H, I, E, k, shared is not None,
-                                                           variant)),
+                                                           "decode" if mx else variant)),
                               dtype=torch.uint8, device=dev)
         ids, aff = route(logits, k)
         fused_w8a16(x, w13, w13_scale, w2, w2_scale, ids, aff, shared=shared, out=self.out,
-                    ws=self.ws, variant=variant, layout=layout, activation=act)
+                    ws=self.ws, variant=variant, layout=layout, activation=act,
+                    weight_format=weight_format)
+        self._fused_fn = lib.moe_fused_mxfp4 if mx else lib.moe_fused_w8a16_ex
         self._keep = (x, logits, w13, w13_scale, w2, w2_scale, shared)
         self._sh = None
         if shared is not None:
@@ -407,12 +463,12 @@ class MoeStep:
         st = _stream(self._dev)
         rc = self._lib.moe_route(*self._route_args, st)
         if rc == MOE_OK:
-            rc = self._lib.moe_fused_w8a16_ex(*self._fused_args, st)
+            rc = self._fused_fn(*self._fused_args, st)
         _check(rc)
         return self.out
 
     def fused(self):
         """Enqueue only the fused call (sort + expert FFN + expert sum) on the
         ids and affinities of the last routing pass."""
-        _check(self._lib.moe_fused_w8a16_ex(*self._fused_args, _stream(self._dev)))
+        _check(self._fused_fn(*self._fused_args, _stream(self._dev)))
         return self.out

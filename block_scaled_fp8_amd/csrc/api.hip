@@ -232,13 +232,18 @@ size_t moe_fused_workspace_bytes(int T, int H, int I, int E, int k, int has_shar
     return fused_layout(T, H, I, E, k, has_shared ? 1 : 0, variant).total;
 }
 
-int moe_fused_w8a16_ex(const void* x, const uint8_t* w13, const float* w13_scale,
-                       const uint8_t* w2, const float* w2_scale, const int32_t* ids,
-                       const float* aff, int T, int H, int I, int E, int k,
-                       const moe_expert_w8* shared, float* out, int32_t* status, void* ws,
-                       size_t ws_bytes, int weight_layout, int variant, int activation,
-                       void* stream) {
+}  // extern "C"
+
+namespace moe {
+// The fused call for both stored weight formats.  `who` names the entry point
+// in error messages; `sh` is the shared expert (w13 == nullptr: none).
+static int fused_impl(const char* who, const void* x, const uint8_t* w13, const void* w13_scale,
+                      const uint8_t* w2, const void* w2_scale, const int32_t* ids, const float* aff,
+                      int T, int H, int I, int E, int k, const SharedW* shared, float* out,
+                      int32_t* status, void* ws, size_t ws_bytes, int weight_layout, int variant,
+                      int activation, int wfmt, void* stream) {
     g_err[0] = 0;
+    const bool mx4 = wfmt == WFMT_MXFP4;
     if (activation != MOE_ACT_SWIGLU && activation != MOE_ACT_RELU2) {
         set_error("unknown activation %d", activation);
         return MOE_EINVAL;
@@ -261,45 +266,60 @@ int moe_fused_w8a16_ex(const void* x, const uint8_t* w13, const float* w13_scale
         set_error("unknown variant %d", variant);
         return MOE_EINVAL;
     }
+    if (mx4 && (variant == MOE_VARIANT_PREFILL || variant == MOE_VARIANT_PREFILL_A8)) {
+        set_error("%s: MXFP4 weights run the weight-streaming (decode) kernels only", who);
+        return MOE_EUNSUPPORTED;
+    }
     if (T == 0) return MOE_OK;
     if (!x || !w13 || !w13_scale || !w2 || !w2_scale || !ids || !aff || !out) {
-        set_error("moe_fused_w8a16: x, weights, scales, ids, aff and out must be non-NULL");
+        set_error("%s: x, weights, scales, ids, aff and out must be non-NULL", who);
         return MOE_EINVAL;
     }
     if (shared && (!shared->w13 || !shared->w13_scale || !shared->w2 || !shared->w2_scale)) {
-        set_error("moe_fused_w8a16: shared expert descriptor has a NULL member");
+        set_error("%s: shared expert descriptor has a NULL member", who);
         return MOE_EINVAL;
     }
     if ((const void*)out == x) {
-        set_error("moe_fused_w8a16: out must not alias x");
+        set_error("%s: out must not alias x", who);
         return MOE_EINVAL;
     }
     // 16-byte vector loads and stores (and direct-to-LDS loads) on x, the
-    // weights, out and the workspace; 4-byte ones on the scales, ids and aff
+    // weights, out and the workspace; 4-byte ones on the fp32 scales, ids and
+    // aff (E8M0 scales are read a byte at a time)
     {
         uintptr_t a16 = (uintptr_t)x | (uintptr_t)w13 | (uintptr_t)w2 | (uintptr_t)out |
                         (uintptr_t)ws;
-        uintptr_t a4 = (uintptr_t)w13_scale | (uintptr_t)w2_scale | (uintptr_t)ids | (uintptr_t)aff;
+        uintptr_t a4 = (uintptr_t)ids | (uintptr_t)aff;
+        if (!mx4) a4 |= (uintptr_t)w13_scale | (uintptr_t)w2_scale;
         if (shared) {
             a16 |= (uintptr_t)shared->w13 | (uintptr_t)shared->w2;
-            a4 |= (uintptr_t)shared->w13_scale | (uintptr_t)shared->w2_scale;
+            if (!mx4) a4 |= (uintptr_t)shared->w13_scale | (uintptr_t)shared->w2_scale;
         }
         if ((a16 & 15) || (a4 & 3)) {
-            set_error("moe_fused_w8a16: x, w13, w2, out and ws must be 16-byte aligned, the "
-                      "scales, ids and aff 4-byte aligned");
+            set_error("%s: x, w13, w2, out and ws must be 16-byte aligned, the %sids and aff "
+                      "4-byte aligned", who, mx4 ? "" : "scales, ");
             return MOE_EINVAL;
         }
     }
     const int has_shared = shared ? 1 : 0;
     const bool fp8_x = variant == MOE_VARIANT_PREFILL_A8;
-    variant = resolve_variant(T, H, I, E, k, act, variant);
+    variant = mx4 ? MOE_VARIANT_DECODE : resolve_variant(T, H, I, E, k, act, variant);
     const FusedLayout L = fused_layout(T, H, I, E, k, has_shared, variant);
     if (!ws || ws_bytes < L.total) {
-        set_error("moe_fused_w8a16: workspace of %zu bytes needed (got %zu)", L.total, ws_bytes);
+        set_error("%s: workspace of %zu bytes needed (got %zu)", who, L.total, ws_bytes);
         return MOE_EINVAL;
     }
     if (variant == MOE_VARIANT_PREFILL || fp8_x) {
         if (int rc = prefill_check(T, H, I, E, k, has_shared, act)) return rc;
+    }
+    // MXFP4 weights: the one-workgroup-per-expert kernel at every size
+    const long long R = (long long)T * k;
+    const bool mx_self = R <= decode_self_routed_max_routes();
+    if (mx4 && (decode_fused_lds_bytes(decode_mt(T, k, E), I, mx_self ? (int)R : 0) > 64 * 1024 ||
+                (long long)T * H >= (1LL << 32))) {
+        set_error("%s: MXFP4 weights need the activations of one expert pass in 64 KB of LDS "
+                  "and T*H < 2^32 (got T=%d, H=%d, I=%d)", who, T, H, I);
+        return MOE_EUNSUPPORTED;
     }
 
     char* base = static_cast<char*>(ws);
@@ -319,29 +339,33 @@ int moe_fused_w8a16_ex(const void* x, const uint8_t* w13, const float* w13_scale
     uint16_t* abuf = reinterpret_cast<uint16_t*>(base + L.abuf);
     float* ybuf = reinterpret_cast<float*>(base + L.ybuf);
     hipStream_t s = (hipStream_t)stream;
-
-    SharedW sh{nullptr, nullptr, nullptr, nullptr};
-    if (shared) sh = SharedW{shared->w13, shared->w13_scale, shared->w2, shared->w2_scale};
+    const SharedW sh = shared ? *shared : SharedW{nullptr, nullptr, nullptr, nullptr};
+    const float* w13f = static_cast<const float*>(w13_scale);
+    const float* w2f = static_cast<const float*>(w2_scale);
 
     const uint16_t* xb = static_cast<const uint16_t*>(x);
     int rc;
-    if (variant == MOE_VARIANT_DECODE && decode_fused_fits(T, k, E, H, I, has_shared, true)) {
+    if (variant == MOE_VARIANT_DECODE &&
+        (mx4 ? mx_self : decode_fused_fits(T, k, E, H, I, has_shared, true))) {
         // small decode batch: each expert's workgroup finds its own routes
         rc = launch_decode_fused_self(weight_layout, decode_mt(T, k, E), xb, w13, w13_scale, w2,
-                                      w2_scale, sh, ids, aff, T, H, I, E, k, ybuf, act, s);
+                                      w2_scale, sh, ids, aff, T, H, I, E, k, ybuf, act, wfmt, s);
     } else {
         const int tile_m = pf ? prefill_tile_m() : 1;
         if ((rc = launch_sort(ids, T, k, E, p, has_shared, tile_m, status, base + L.sort_scratch, s)))
             return rc;
-        if (variant == MOE_VARIANT_DECODE)
-            rc = launch_decode_ffn(weight_layout, xb, w13, w13_scale, w2, w2_scale, sh, p, aff, T,
-                                   H, I, E, k, abuf, ybuf, act, s);
+        if (mx4)
+            rc = launch_decode_fused(weight_layout, decode_mt(T, k, E), xb, w13, w13_scale, w2,
+                                     w2_scale, sh, p, aff, T, H, I, E, k, ybuf, act, wfmt, s);
+        else if (variant == MOE_VARIANT_DECODE)
+            rc = launch_decode_ffn(weight_layout, xb, w13, w13f, w2, w2f, sh, p, aff, T, H, I, E,
+                                   k, abuf, ybuf, act, s);
         else {
             uint8_t* xq = fp8_x ? reinterpret_cast<uint8_t*>(base + L.xq) : nullptr;
             float* xsc = fp8_x ? reinterpret_cast<float*>(base + L.xs) : nullptr;
             if (fp8_x && (rc = launch_quant_rows_e4m3(xb, T, H, xq, xsc, s))) return rc;
-            rc = launch_prefill_ffn(weight_layout, xb, w13, w13_scale, w2, w2_scale, sh, p, T, H,
-                                    I, E, k, abuf, ybuf, act, xq, xsc, s);
+            rc = launch_prefill_ffn(weight_layout, xb, w13, w13f, w2, w2f, sh, p, T, H, I, E, k,
+                                    abuf, ybuf, act, xq, xsc, s);
         }
     }
     if (rc) return rc;
@@ -349,6 +373,35 @@ int moe_fused_w8a16_ex(const void* x, const uint8_t* w13, const float* w13_scale
     return launch_combine(ybuf, ids, gathered ? p.inv_route : nullptr,
                           gathered ? aff : nullptr, T, H, k, E,
                           has_shared, status, out, s);
+}
+}  // namespace moe
+
+extern "C" {
+
+int moe_fused_w8a16_ex(const void* x, const uint8_t* w13, const float* w13_scale,
+                       const uint8_t* w2, const float* w2_scale, const int32_t* ids,
+                       const float* aff, int T, int H, int I, int E, int k,
+                       const moe_expert_w8* shared, float* out, int32_t* status, void* ws,
+                       size_t ws_bytes, int weight_layout, int variant, int activation,
+                       void* stream) {
+    SharedW sh{};
+    if (shared) sh = SharedW{shared->w13, shared->w13_scale, shared->w2, shared->w2_scale};
+    return fused_impl("moe_fused_w8a16", x, w13, w13_scale, w2, w2_scale, ids, aff, T, H, I, E, k,
+                      shared ? &sh : nullptr, out, status, ws, ws_bytes, weight_layout, variant,
+                      activation, WFMT_E4M3_128, stream);
+}
+
+int moe_fused_mxfp4(const void* x, const uint8_t* w13, const uint8_t* w13_scale,
+                    const uint8_t* w2, const uint8_t* w2_scale, const int32_t* ids,
+                    const float* aff, int T, int H, int I, int E, int k,
+                    const moe_expert_mx4* shared, float* out, int32_t* status, void* ws,
+                    size_t ws_bytes, int weight_layout, int variant, int activation,
+                    void* stream) {
+    SharedW sh{};
+    if (shared) sh = SharedW{shared->w13, shared->w13_scale, shared->w2, shared->w2_scale};
+    return fused_impl("moe_fused_mxfp4", x, w13, w13_scale, w2, w2_scale, ids, aff, T, H, I, E, k,
+                      shared ? &sh : nullptr, out, status, ws, ws_bytes, weight_layout, variant,
+                      activation, WFMT_MXFP4, stream);
 }
 
 int moe_fused_w8a16(const void* x, const uint8_t* w13, const float* w13_scale,
@@ -462,6 +515,29 @@ int moe_pack_w8(const uint8_t* src, uint8_t* dst, int64_t n_mats, int rows, int 
         return MOE_EINVAL;
     }
     return launch_pack_w8(src, dst, n_mats, rows, cols, (hipStream_t)stream);
+}
+
+int moe_pack_mx_scales(const uint8_t* src, uint8_t* dst, int64_t n_mats, int rows, int cols,
+                       void* stream) {
+    g_err[0] = 0;
+    if (n_mats < 0 || rows < 0 || cols < 0 || rows % 16 || cols % 4) {
+        set_error("moe_pack_mx_scales: need n_mats, rows, cols >= 0, rows %% 16 == 0, "
+                  "cols %% 4 == 0 (got %lld, %d, %d)", (long long)n_mats, rows, cols);
+        return MOE_EINVAL;
+    }
+    if (n_mats == 0 || rows == 0 || cols == 0) return MOE_OK;
+    if (!src || !dst) {
+        set_error("moe_pack_mx_scales: src and dst must be non-NULL");
+        return MOE_EINVAL;
+    }
+    const size_t bytes = (size_t)n_mats * rows * cols;
+    const char* a = reinterpret_cast<const char*>(src);
+    const char* b = reinterpret_cast<const char*>(dst);
+    if (a < b + bytes && b < a + bytes) {
+        set_error("moe_pack_mx_scales: src and dst overlap");
+        return MOE_EINVAL;
+    }
+    return launch_pack_mx_scales(src, dst, n_mats, rows, cols, (hipStream_t)stream);
 }
 
 int moe_quant_e4m3_rows(const void* x, int T, int H, uint8_t* codes, float* scales,

@@ -53,6 +53,22 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16x8_scaled(uint32_t lo, uint32_t h
     return r;
 }
 
+// Eight E2M1 (FP4) codes (one dword: element 2b in the low nibble of byte b,
+// 2b + 1 in its high nibble) to eight bf16 times 2^e, e the exponent of
+// `pow2` (an E8M0 scale given as fp32: only the exponent field is used).
+// Every E2M1 value times 2^e is a bf16 value while it stays in the normal
+// range, so this is exact there.  Each conversion's two results are read as
+// one 32-bit word: reading the second bf16 element of this builtin's result
+// on its own was measured to return the first one.
+__device__ __forceinline__ bf16x8 fp4x8_to_bf16x8_scaled(uint32_t w, float pow2) {
+    u32x4 r;
+    r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, pow2, 0));
+    r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, pow2, 1));
+    r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, pow2, 2));
+    r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, pow2, 3));
+    return __builtin_bit_cast(bf16x8, r);
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {
     return __builtin_bit_cast(bf16x8, v);
 }

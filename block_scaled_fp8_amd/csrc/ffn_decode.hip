@@ -374,11 +374,13 @@ static int launch_decode_mode_l(int MT, int nseg_max, const uint16_t* x, const u
                stream);
     if (MT == 1)
         decode_ffn_kernel<MODE, 1, LAYOUT><<<grid, block, 0, stream>>>(
-            x, w13, w13s, w2, w2s, sh.w13, sh.w13_scale, sh.w2, sh.w2_scale, plan, aff, T, H, I, k,
+            x, w13, w13s, w2, w2s, sh.w13, static_cast<const float*>(sh.w13_scale), sh.w2,
+            static_cast<const float*>(sh.w2_scale), plan, aff, T, H, I, k,
             abuf, ybuf);
     else
         decode_ffn_kernel<MODE, 2, LAYOUT><<<grid, block, 0, stream>>>(
-            x, w13, w13s, w2, w2s, sh.w13, sh.w13_scale, sh.w2, sh.w2_scale, plan, aff, T, H, I, k,
+            x, w13, w13s, w2, w2s, sh.w13, static_cast<const float*>(sh.w13_scale), sh.w2,
+            static_cast<const float*>(sh.w2_scale), plan, aff, T, H, I, k,
             abuf, ybuf);
     prof_end(stream);
     return check_launch(MODE == MODE_GATEUP ? "decode_ffn_kernel<gateup>"
@@ -397,11 +399,6 @@ static int launch_decode_mode(int layout, int MT, int nseg_max, const uint16_t* 
     return launch_decode_mode_l<MODE, LAYOUT_ROWMAJOR>(MT, nseg_max, x, w13, w13s, w2, w2s, sh,
                                                        plan, aff, T, H, I, k, abuf, ybuf, stream);
 }
-
-int launch_decode_fused(int layout, int MT, const uint16_t* x, const uint8_t* w13,
-                        const float* w13s, const uint8_t* w2, const float* w2s, const SharedW& sh,
-                        const Plan& plan, const float* aff, int T, int H, int I, int E, int k,
-                        float* ybuf, int act, hipStream_t stream);
 
 // At most min(E, T*k) routed experts are active.  When that fills most of the
 // chip, one workgroup per active expert (ffn_decode_fused.hip) streams every
@@ -431,7 +428,7 @@ int launch_decode_ffn(int layout, const uint16_t* x, const uint8_t* w13, const f
     const int MT = decode_mt(T, k, E);
     if (decode_fused_fits(T, k, E, H, I, has_shared, false))
         return launch_decode_fused(layout, MT, x, w13, w13s, w2, w2s, sh, plan, aff, T, H, I, E,
-                                   k, ybuf, act, stream);
+                                   k, ybuf, act, WFMT_E4M3_128, stream);
     const int rc = act == ACT_RELU2
                        ? launch_decode_mode<MODE_UP>(layout, MT, nseg_max, x, w13, w13s, w2, w2s,
                                                      sh, plan, aff, T, H, I, k, abuf, ybuf, stream)

@@ -64,13 +64,23 @@ size_t decode_fused_lds_bytes(int MT, int I, int self_routes) {
 // RELU2: a non-gated expert, w13 = the up projection [I, H] alone; a phase-1
 // group is NT up tiles (64 rows, inside one 128-row scale block) and the
 // activation is relu(u)^2.
-template <int MT, int DEPTH, int LAYOUT, bool SELF, bool RELU2>
+//
+// MX4: MXFP4 weights (two E2M1 codes a byte, element 2j in the low nibble of
+// byte j; one E8M0 scale per 32 consecutive elements of a row).  A chunk is
+// then 128 K (the same 16 bytes a lane, 64 bytes a row): lane quarter g holds
+// K [32g, 32g + 32) of the chunk, exactly one scale block, and its scale,
+// a power of two, is applied exactly by the bf16 conversion (converter scale
+// operand), so the MFMAs accumulate over all of K with no rescaling.  Four
+// MFMA sub-steps per chunk, sub-step s taking K [32g + 8s, 32g + 8s + 8) of
+// both operands.  Scales are void pointers: fp32 [rows/128][K/128] blocks, or
+// E8M0 bytes [rows][K/32] for MX4.
+template <int MT, int DEPTH, int LAYOUT, bool SELF, bool RELU2, bool MX4>
 __global__ __launch_bounds__(DF_THREADS) void decode_fused_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ w13,
-    const float* __restrict__ w13s, const uint8_t* __restrict__ w2,
-    const float* __restrict__ w2s, const uint8_t* __restrict__ sh_w13,
-    const float* __restrict__ sh_w13s, const uint8_t* __restrict__ sh_w2,
-    const float* __restrict__ sh_w2s, Plan plan, const int32_t* __restrict__ ids, int E,
+    const void* __restrict__ w13s, const uint8_t* __restrict__ w2,
+    const void* __restrict__ w2s, const uint8_t* __restrict__ sh_w13,
+    const void* __restrict__ sh_w13s, const uint8_t* __restrict__ sh_w2,
+    const void* __restrict__ sh_w2s, Plan plan, const int32_t* __restrict__ ids, int E,
     const float* __restrict__ aff, int T, int H, int I, int k, float* __restrict__ ybuf,
     int ytrash_row) {
     // two 64-wide chunks per 128-wide scale block, two in flight: the chunk
@@ -136,17 +146,32 @@ __global__ __launch_bounds__(DF_THREADS) void decode_fused_kernel(
         return SELF ? rlist[m] : plan.sorted_route[row0 + m];
     };
     const int n13 = RELU2 ? I : 2 * I;  // rows of the expert's first matrix
-    const uint8_t* W13 = e >= 0 ? w13 + (size_t)e * n13 * H : sh_w13;
-    const float* S13 = e >= 0 ? w13s + (size_t)e * (n13 / 128) * (H / 128) : sh_w13s;
-    const uint8_t* W2 = e >= 0 ? w2 + (size_t)e * H * I : sh_w2;
-    const float* S2 = e >= 0 ? w2s + (size_t)e * (H / 128) * (I / 128) : sh_w2s;
+    constexpr int KC = MX4 ? 128 : 64;  // K per 64-byte chunk of a weight row
+    constexpr int NS = KC / 32;         // MFMA sub-steps (16-byte activation pieces) per chunk
+    const int H8 = MX4 ? H / 2 : H, I8 = MX4 ? I / 2 : I;  // weight row strides in bytes
+    const uint8_t* W13 = e >= 0 ? w13 + (size_t)e * n13 * H8 : sh_w13;
+    const uint8_t* W2 = e >= 0 ? w2 + (size_t)e * H * I8 : sh_w2;
+    // fp32 128x128 block scales, or (MX4) E8M0 bytes per 32 elements of a row
+    const size_t s13n = MX4 ? (size_t)n13 * (H / 32) : (size_t)(n13 / 128) * (H / 128);
+    const size_t s2n = MX4 ? (size_t)H * (I / 32) : (size_t)(H / 128) * (I / 128);
+    const void* S13v = e >= 0 ? static_cast<const char*>(w13s) + (MX4 ? 1 : 4) * (size_t)e * s13n : sh_w13s;
+    const void* S2v = e >= 0 ? static_cast<const char*>(w2s) + (MX4 ? 1 : 4) * (size_t)e * s2n : sh_w2s;
+    const float* S13 = static_cast<const float*>(S13v);
+    const float* S2 = static_cast<const float*>(S2v);
+    const uint8_t* M13 = static_cast<const uint8_t*>(S13v);
+    const uint8_t* M2 = static_cast<const uint8_t*>(S2v);
 
     const int ln = lane & 15, lg = lane >> 4;
 
-    const int nch1 = H >> 6, nch2 = I >> 6;  // chunks per group, both even
-    const int kb1 = H >> 7, kb2 = I >> 7;    // scale blocks along K
+    const int nch1 = H / KC, nch2 = I / KC;  // chunks per group (even unless MX4)
+    const int kb1 = H >> 7, kb2 = I >> 7;    // 128-wide scale blocks along K
     const int G1 = I / (16 * (RELU2 ? NT : HALF)), G2 = H / (16 * NT);
-    const int n1 = (G1 + DF_WAVES - 1) / DF_WAVES, n2 = (G2 + DF_WAVES - 1) / DF_WAVES;
+    int n1 = (G1 + DF_WAVES - 1) / DF_WAVES, n2 = (G2 + DF_WAVES - 1) / DF_WAVES;
+    // the stream advances DEPTH = 2 positions at a time, so each phase takes an
+    // even number of chunks: with an odd chunk count (MX4, K = 128 * odd) a
+    // wave streams one more spare group, whose results go to padding
+    n1 += (nch1 & n1 & 1);
+    n2 += (nch2 & n2 & 1);
     const int tot1 = n1 * nch1, tot2 = n2 * nch2;
 
     for (int mp = 0; mp < rows; mp += MROWS) {
@@ -158,7 +183,8 @@ __global__ __launch_bounds__(DF_THREADS) void decode_fused_kernel(
         int yrow[MT][4];     // y row of this lane's output rows (the trash row if padded)
         float yaff[MT][4];   // affinity of each of those routes
         u32x4 bq[DEPTH][NT];
-        u32x4 aq[DEPTH][MT][2];
+        uint32_t sq[DEPTH][NT];  // MX4: the lane's E8M0 scale byte of each tile's chunk
+        u32x4 aq[DEPTH][MT][NS];
         f32x4 acc[MT][NT];  // partial sums of the current 128-wide K block
         f32x4 tot[MT][NT];  // scaled totals of the finished blocks
         float sc0 = 0.0f, sc1 = 0.0f;  // scales of the current block (phase 1: gate, up; phase 2: sc0)
@@ -179,18 +205,23 @@ __global__ __launch_bounds__(DF_THREADS) void decode_fused_kernel(
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) tot[mt][j] += sc * acc[mt][j];
         };
-        auto mfma_chunk = [&](int d, const u32x4 (&av)[MT][2]) {
+        auto mfma_chunk = [&](int d, const u32x4 (&av)[MT][NS]) {
 #pragma unroll
-            for (int s = 0; s < 2; ++s)
+            for (int s = 0; s < NS; ++s)
 #pragma unroll
                 for (int j = 0; j < NT; ++j) {
-                    const bf16x8 b = s == 0 ? fp8x8_to_bf16x8(bq[d][j][0], bq[d][j][1])
-                                            : fp8x8_to_bf16x8(bq[d][j][2], bq[d][j][3]);
+                    bf16x8 b;
+                    if constexpr (MX4)
+                        b = fp4x8_to_bf16x8_scaled(bq[d][j][s], __uint_as_float(sq[d][j] << 23));
+                    else
+                        b = s == 0 ? fp8x8_to_bf16x8(bq[d][j][0], bq[d][j][1])
+                                   : fp8x8_to_bf16x8(bq[d][j][2], bq[d][j][3]);
 #pragma unroll
                     for (int mt = 0; mt < MT; ++mt)
                         acc[mt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                             as_bf16x8(av[mt][s]), b,
-                            d == 0 && s == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[mt][j], 0, 0, 0);
+                            !MX4 && d == 0 && s == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[mt][j],
+                            0, 0, 0);
                 }
         };
 
@@ -198,19 +229,25 @@ __global__ __launch_bounds__(DF_THREADS) void decode_fused_kernel(
         //      I/16 + g*HALF + j; phase-2 group g has W2 row tiles g*NT + j.
         //      Groups past the real count re-stream group g % G.
         int ig = wave, ic = 0;  // issue cursor (group, chunk)
+        // (MX4: row r's scale of K [KC c + 32 lg, +32) is byte r * K/32 + 4c + lg,
+        //  or in the tiled layout byte ((r / 16) * K/128 + c) * 64 + lane)
         auto issue1_b = [&](int d, int g, int c) {
 #pragma unroll
             for (int j = 0; j < NT; ++j) {
                 const int r = RELU2 ? (g * NT + j) * 16 : (j < HALF ? 0 : I) + (g * HALF + (j % HALF)) * 16;
-                bq[d][j] = load_stream16(tile_lane_ptr<LAYOUT>(W13, r, H, lane) + (size_t)c * CS);
+                bq[d][j] = load_stream16(tile_lane_ptr<LAYOUT>(W13, r, H8, lane) + (size_t)c * CS);
+                if constexpr (MX4)
+                    sq[d][j] = LAYOUT == LAYOUT_TILED
+                                   ? M13[((size_t)(r >> 4) * (H / 128) + c) * 64 + lane]
+                                   : M13[(size_t)(r + ln) * (H / 32) + 4 * c + lg];
             }
         };
         auto issue1_a = [&](int d, int c) {
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
-                const u32x4* q = reinterpret_cast<const u32x4*>(x + xoff[mt] + c * 64);
-                aq[d][mt][0] = q[0];
-                aq[d][mt][1] = q[1];
+                const u32x4* q = reinterpret_cast<const u32x4*>(x + xoff[mt] + c * KC);
+#pragma unroll
+                for (int s = 0; s < NS; ++s) aq[d][mt][s] = q[s];
             }
         };
         auto issue1 = [&](int d) {
@@ -221,17 +258,26 @@ __global__ __launch_bounds__(DF_THREADS) void decode_fused_kernel(
         auto issue2 = [&](int d) {
             const int g = ig % G2;
 #pragma unroll
-            for (int j = 0; j < NT; ++j)
-                bq[d][j] = load_stream16(tile_lane_ptr<LAYOUT>(W2, (g * NT + j) * 16, I, lane) +
+            for (int j = 0; j < NT; ++j) {
+                bq[d][j] = load_stream16(tile_lane_ptr<LAYOUT>(W2, (g * NT + j) * 16, I8, lane) +
                                          (size_t)ic * CS);
+                if constexpr (MX4)
+                    sq[d][j] = LAYOUT == LAYOUT_TILED
+                                   ? M2[((size_t)(g * NT + j) * (I / 128) + ic) * 64 + lane]
+                                   : M2[(size_t)((g * NT + j) * 16 + ln) * (I / 32) + 4 * ic + lg];
+            }
             if (++ic == nch2) { ic = 0; ig += DF_WAVES; }
         };
+
+        // a tile's result at the end of its group: the scaled block totals,
+        // or (MX4, scales applied in the conversion) the accumulator itself
+        auto res = [&](int mt, int j, int i) -> float { return MX4 ? acc[mt][j][i] : tot[mt][j][i]; };
 
         // ---- process side
         int pg = wave, pc = 0;
         auto proc1 = [&](int d) {
             const int g = pg % G1;
-            if (d == 0) {  // a block starts: its scales
+            if (!MX4 && d == 0) {  // a block starts: its scales
                 const int kb = pc >> 1;
                 if (RELU2) {
                     const int ui = __builtin_amdgcn_readfirstlane(((g * NT * 16) >> 7) * kb1 + kb);
@@ -243,14 +289,14 @@ __global__ __launch_bounds__(DF_THREADS) void decode_fused_kernel(
                     sc1 = S13[ui];
                 }
             }
-            u32x4 av[MT][2];
+            u32x4 av[MT][NS];
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                av[mt][0] = xvalid[mt] ? aq[d][mt][0] : u32x4{0u, 0u, 0u, 0u};
-                av[mt][1] = xvalid[mt] ? aq[d][mt][1] : u32x4{0u, 0u, 0u, 0u};
-            }
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int s = 0; s < NS; ++s)
+                    av[mt][s] = xvalid[mt] ? aq[d][mt][s] : u32x4{0u, 0u, 0u, 0u};
             mfma_chunk(d, av);
-            if (d == 1) {  // the block's second chunk: fold it
+            if (!MX4 && d == 1) {  // the block's second chunk: fold it
                 if (RELU2) {
                     fold(sc0, 0, NT);
                 } else {
@@ -269,7 +315,7 @@ __global__ __launch_bounds__(DF_THREADS) void decode_fused_kernel(
                             for (int i = 0; i < 4; ++i) {
                                 const int m = mt * 16 + lg * 4 + i;
                                 const int col = real ? (g * NT + j) * 16 + ln : I + (ln & 7);
-                                a_lds[m * astride + col] = f32_to_bf16_bits(relu2(tot[mt][j][i]));
+                                a_lds[m * astride + col] = f32_to_bf16_bits(relu2(res(mt, j, i)));
                             }
                 } else {
 #pragma unroll
@@ -278,8 +324,8 @@ __global__ __launch_bounds__(DF_THREADS) void decode_fused_kernel(
                         for (int j = 0; j < HALF; ++j)
 #pragma unroll
                             for (int i = 0; i < 4; ++i) {
-                                const float gv = tot[mt][j][i];
-                                const float uv = tot[mt][HALF + j][i];
+                                const float gv = res(mt, j, i);
+                                const float uv = res(mt, HALF + j, i);
                                 const int m = mt * 16 + lg * 4 + i;
                                 const int col = real ? (g * HALF + j) * 16 + ln : I + (ln & 7);
                                 a_lds[m * astride + col] = f32_to_bf16_bits(swiglu(gv, uv));
@@ -294,19 +340,19 @@ __global__ __launch_bounds__(DF_THREADS) void decode_fused_kernel(
         };
         auto proc2 = [&](int d) {
             const int g = pg % G2;
-            if (d == 0) {
+            if (!MX4 && d == 0) {
                 const int si = __builtin_amdgcn_readfirstlane(((g * NT * 16) >> 7) * kb2 + (pc >> 1));
                 sc0 = S2[si];
             }
-            u32x4 av[MT][2];
+            u32x4 av[MT][NS];
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
-                const u32x4* q = reinterpret_cast<const u32x4*>(a_lds + aoff[mt] + pc * 64);
-                av[mt][0] = q[0];
-                av[mt][1] = q[1];
+                const u32x4* q = reinterpret_cast<const u32x4*>(a_lds + aoff[mt] + pc * KC);
+#pragma unroll
+                for (int s = 0; s < NS; ++s) av[mt][s] = q[s];
             }
             mfma_chunk(d, av);
-            if (d == 1) fold(sc0, 0, NT);
+            if (!MX4 && d == 1) fold(sc0, 0, NT);
             if (pc == nch2 - 1) {  // group done: fp32 rows of the routes (trash if spare)
                 const bool real = pg < G2;
 #pragma unroll
@@ -317,7 +363,7 @@ __global__ __launch_bounds__(DF_THREADS) void decode_fused_kernel(
                                      (real ? g * NT * 16 : 0) + ln;
                         const float a = yaff[mt][i];
 #pragma unroll
-                        for (int j = 0; j < NT; ++j) dst[j * 16] = tot[mt][j][i] * a;
+                        for (int j = 0; j < NT; ++j) dst[j * 16] = res(mt, j, i) * a;
                     }
                 reset();
                 pc = 0;
@@ -339,8 +385,8 @@ __global__ __launch_bounds__(DF_THREADS) void decode_fused_kernel(
             int t = -1;
             if (m < rows) t = e >= 0 ? route_of(m) / k : route_of(m) - R;
             xvalid[mt] = t >= 0;
-            xoff[mt] = (uint32_t)(t >= 0 ? t : 0) * (uint32_t)H + lg * 16;
-            aoff[mt] = (uint32_t)((mt * 16 + ln) * astride + lg * 16);
+            xoff[mt] = (uint32_t)(t >= 0 ? t : 0) * (uint32_t)H + lg * (KC / 4);
+            aoff[mt] = (uint32_t)((mt * 16 + ln) * astride + lg * (KC / 4));
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int mi = mp + mt * 16 + lg * 4 + i;
@@ -386,22 +432,22 @@ __global__ __launch_bounds__(DF_THREADS) void decode_fused_kernel(
     }
 }
 
-template <int LAYOUT, bool SELF, bool RELU2>
-static int launch_decode_fused_l(int MT, const uint16_t* x, const uint8_t* w13, const float* w13s,
-                                 const uint8_t* w2, const float* w2s, const SharedW& sh,
+template <int LAYOUT, bool SELF, bool RELU2, bool MX4>
+static int launch_decode_fused_l(int MT, const uint16_t* x, const uint8_t* w13, const void* w13s,
+                                 const uint8_t* w2, const void* w2s, const SharedW& sh,
                                  const Plan& plan, const int32_t* ids, const float* aff, int T,
                                  int H, int I, int E, int k, float* ybuf, hipStream_t stream) {
     const int nseg_max = E + (sh.w13 ? 1 : 0);
     const size_t lds = decode_fused_lds_bytes(MT, I, SELF ? T * k : 0);
     // the trash row sits right after the last real row of y
     const int ytrash = T * k + (sh.w13 ? T : 0);
-    prof_begin("decode_fused_expert", stream);
+    prof_begin(MX4 ? "decode_fused_expert_mxfp4" : "decode_fused_expert", stream);
     if (MT == 1)
-        decode_fused_kernel<1, 2, LAYOUT, SELF, RELU2><<<nseg_max, DF_THREADS, lds, stream>>>(
+        decode_fused_kernel<1, 2, LAYOUT, SELF, RELU2, MX4><<<nseg_max, DF_THREADS, lds, stream>>>(
             x, w13, w13s, w2, w2s, sh.w13, sh.w13_scale, sh.w2, sh.w2_scale, plan, ids, E, aff, T,
             H, I, k, ybuf, ytrash);
     else
-        decode_fused_kernel<2, 2, LAYOUT, SELF, RELU2><<<nseg_max, DF_THREADS, lds, stream>>>(
+        decode_fused_kernel<2, 2, LAYOUT, SELF, RELU2, MX4><<<nseg_max, DF_THREADS, lds, stream>>>(
             x, w13, w13s, w2, w2s, sh.w13, sh.w13_scale, sh.w2, sh.w2_scale, plan, ids, E, aff, T,
             H, I, k, ybuf, ytrash);
     prof_end(stream);
@@ -410,39 +456,43 @@ static int launch_decode_fused_l(int MT, const uint16_t* x, const uint8_t* w13, 
 
 template <bool SELF>
 static int launch_decode_fused_any(int layout, int MT, const uint16_t* x, const uint8_t* w13,
-                                   const float* w13s, const uint8_t* w2, const float* w2s,
+                                   const void* w13s, const uint8_t* w2, const void* w2s,
                                    const SharedW& sh, const Plan& plan, const int32_t* ids,
                                    const float* aff, int T, int H, int I, int E, int k,
-                                   float* ybuf, int act, hipStream_t stream) {
-#define MOE_DF_LAUNCH(L, R)                                                                      \
-    launch_decode_fused_l<L, SELF, R>(MT, x, w13, w13s, w2, w2s, sh, plan, ids, aff, T, H, I, E, \
-                                      k, ybuf, stream)
-    const bool relu2 = act == ACT_RELU2;
-    if (layout == LAYOUT_TILED)
-        return relu2 ? MOE_DF_LAUNCH(LAYOUT_TILED, true) : MOE_DF_LAUNCH(LAYOUT_TILED, false);
-    return relu2 ? MOE_DF_LAUNCH(LAYOUT_ROWMAJOR, true) : MOE_DF_LAUNCH(LAYOUT_ROWMAJOR, false);
+                                   float* ybuf, int act, int wfmt, hipStream_t stream) {
+#define MOE_DF_LAUNCH(L, R, M)                                                                      \
+    launch_decode_fused_l<L, SELF, R, M>(MT, x, w13, w13s, w2, w2s, sh, plan, ids, aff, T, H, I, E, \
+                                         k, ybuf, stream)
+#define MOE_DF_LAYOUT(L, M) \
+    (act == ACT_RELU2 ? MOE_DF_LAUNCH(L, true, M) : MOE_DF_LAUNCH(L, false, M))
+    if (wfmt == WFMT_MXFP4)
+        return layout == LAYOUT_TILED ? MOE_DF_LAYOUT(LAYOUT_TILED, true)
+                                      : MOE_DF_LAYOUT(LAYOUT_ROWMAJOR, true);
+    return layout == LAYOUT_TILED ? MOE_DF_LAYOUT(LAYOUT_TILED, false)
+                                  : MOE_DF_LAYOUT(LAYOUT_ROWMAJOR, false);
+#undef MOE_DF_LAYOUT
 #undef MOE_DF_LAUNCH
 }
 
 // One workgroup per possible segment (E routed + shared); workgroups past the
 // number of active segments exit at once.
 int launch_decode_fused(int layout, int MT, const uint16_t* x, const uint8_t* w13,
-                        const float* w13s, const uint8_t* w2, const float* w2s, const SharedW& sh,
+                        const void* w13s, const uint8_t* w2, const void* w2s, const SharedW& sh,
                         const Plan& plan, const float* aff, int T, int H, int I, int E, int k,
-                        float* ybuf, int act, hipStream_t stream) {
+                        float* ybuf, int act, int wfmt, hipStream_t stream) {
     return launch_decode_fused_any<false>(layout, MT, x, w13, w13s, w2, w2s, sh, plan, nullptr,
-                                          aff, T, H, I, E, k, ybuf, act, stream);
+                                          aff, T, H, I, E, k, ybuf, act, wfmt, stream);
 }
 
 // The self-routed form: no sort beforehand; workgroup e scans the ids.
 int launch_decode_fused_self(int layout, int MT, const uint16_t* x, const uint8_t* w13,
-                             const float* w13s, const uint8_t* w2, const float* w2s,
+                             const void* w13s, const uint8_t* w2, const void* w2s,
                              const SharedW& sh, const int32_t* ids, const float* aff, int T,
-                             int H, int I, int E, int k, float* ybuf, int act,
+                             int H, int I, int E, int k, float* ybuf, int act, int wfmt,
                              hipStream_t stream) {
     const Plan none{};
     return launch_decode_fused_any<true>(layout, MT, x, w13, w13s, w2, w2s, sh, none, ids, aff, T,
-                                         H, I, E, k, ybuf, act, stream);
+                                         H, I, E, k, ybuf, act, wfmt, stream);
 }
 
 int decode_self_routed_max_routes() { return DF_SELF_MAX_ROUTES; }

@@ -812,21 +812,21 @@ static int launch_prefill_c(const uint16_t* x, const uint8_t* w13, const float* 
         const uint16_t* xa = reinterpret_cast<const uint16_t*>(xq);
         rc = act == ACT_RELU2
                  ? launch_pf<PF_UP, LAYOUT, PfGateUpA8>(xa, nullptr, w13, w13s, sh.w13,
-                                                        sh.w13_scale, plan, T, H, I, E, k, hs,
+                                                        static_cast<const float*>(sh.w13_scale), plan, T, H, I, E, k, hs,
                                                         abuf, ybuf, stream, xs)
                  : launch_pf<PF_GATEUP, LAYOUT, PfGateUpA8>(xa, nullptr, w13, w13s, sh.w13,
-                                                            sh.w13_scale, plan, T, H, I, E, k, hs,
+                                                            static_cast<const float*>(sh.w13_scale), plan, T, H, I, E, k, hs,
                                                             abuf, ybuf, stream, xs);
     } else {
         rc = act == ACT_RELU2
-                 ? launch_pf<PF_UP, LAYOUT, PfGateUp>(x, nullptr, w13, w13s, sh.w13, sh.w13_scale,
+                 ? launch_pf<PF_UP, LAYOUT, PfGateUp>(x, nullptr, w13, w13s, sh.w13, static_cast<const float*>(sh.w13_scale),
                                                       plan, T, H, I, E, k, hs, abuf, ybuf, stream)
                  : launch_pf<PF_GATEUP, LAYOUT, PfGateUp>(x, nullptr, w13, w13s, sh.w13,
-                                                          sh.w13_scale, plan, T, H, I, E, k, hs,
+                                                          static_cast<const float*>(sh.w13_scale), plan, T, H, I, E, k, hs,
                                                           abuf, ybuf, stream);
     }
     if (rc == MOE_OK)
-        rc = launch_pf<PF_DOWN, LAYOUT, PfDown>(x, abuf, w2, w2s, sh.w2, sh.w2_scale, plan, T, H, I,
+        rc = launch_pf<PF_DOWN, LAYOUT, PfDown>(x, abuf, w2, w2s, sh.w2, static_cast<const float*>(sh.w2_scale), plan, T, H, I,
                                                 E, k, hs, abuf, ybuf, stream);
     return rc;
 }

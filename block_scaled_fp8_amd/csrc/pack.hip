@@ -46,4 +46,36 @@ int launch_pack_w8(const uint8_t* src, uint8_t* dst, int64_t n_mats, int rows, i
     return check_launch("pack_w8_kernel");
 }
 
+// MXFP4 scales for the tiled layout: for matrices [rows, cols] of E8M0 bytes
+// (cols = K / 32), the byte lane l of a wave consumes for 16-row tile t and
+// 128-wide K chunk c, S[16t + l%16][4c + l/16], is stored at (t * cols/4 + c)
+// * 64 + l, so a wave's scale load of one tile chunk is one 64-byte line.
+__global__ __launch_bounds__(256) void pack_mx_scales_kernel(const uint8_t* __restrict__ src,
+                                                             uint8_t* __restrict__ dst,
+                                                             int64_t n, int rows, int cols) {
+    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (q >= n) return;
+    const int64_t per_mat = (int64_t)rows * cols;
+    const int64_t mat = q / per_mat;
+    int64_t r = q - mat * per_mat;
+    const int lane = (int)(r & 63);
+    r >>= 6;
+    const int nch = cols / 4;
+    const int c = (int)(r % nch);
+    const int t = (int)(r / nch);
+    dst[q] = src[mat * per_mat + (int64_t)(16 * t + (lane & 15)) * cols + 4 * c + (lane >> 4)];
+}
+
+int launch_pack_mx_scales(const uint8_t* src, uint8_t* dst, int64_t n_mats, int rows, int cols,
+                          hipStream_t stream) {
+    const int64_t n = n_mats * (int64_t)rows * cols;
+    const int64_t blocks = (n + 255) / 256;
+    if (blocks > 0x7FFFFFFFLL) {
+        set_error("moe_pack_mx_scales: too many bytes in one call");
+        return MOE_EINVAL;
+    }
+    pack_mx_scales_kernel<<<(unsigned)blocks, 256, 0, stream>>>(src, dst, n, rows, cols);
+    return check_launch("pack_mx_scales_kernel");
+}
+
 }  // namespace moe

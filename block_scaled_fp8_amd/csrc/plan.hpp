@@ -27,12 +27,17 @@ struct Plan {
     int32_t* tile_n;        // [1]
 };
 
-// One expert's weights outside the routed arrays (the shared expert).
+// Stored weight formats: E4M3FN codes with fp32 128x128 block scales, or
+// MXFP4 (E2M1 codes two a byte, E8M0 scale bytes per 32 elements of a row).
+enum { WFMT_E4M3_128 = 0, WFMT_MXFP4 = 1 };
+
+// One expert's weights outside the routed arrays (the shared expert); the
+// scales are fp32 (WFMT_E4M3_128) or E8M0 bytes (WFMT_MXFP4).
 struct SharedW {
     const uint8_t* w13;
-    const float* w13_scale;
+    const void* w13_scale;
     const uint8_t* w2;
-    const float* w2_scale;
+    const void* w2_scale;
 };
 
 // Sort entry used by moe_sort and moe_fused_w8a16 (sort.hip).  `plan.seg_*`
@@ -81,6 +86,8 @@ int launch_quant_rows_e4m3(const uint16_t* x, int T, int H, uint8_t* xq, float* 
                            hipStream_t stream);
 int launch_pack_w8(const uint8_t* src, uint8_t* dst, int64_t n_mats, int rows, int cols,
                    hipStream_t stream);
+int launch_pack_mx_scales(const uint8_t* src, uint8_t* dst, int64_t n_mats, int rows, int cols,
+                          hipStream_t stream);
 int prefill_tile_m();
 int prefill_supported(int H, int I, int act);
 // MOE_OK, or MOE_EUNSUPPORTED with the error message set.
@@ -102,10 +109,15 @@ bool decode_fused_fits(int T, int k, int E, int H, int I, int has_shared, bool s
 size_t decode_fused_lds_bytes(int MT, int I, int self_routes);
 int decode_self_routed_max_routes();
 int launch_decode_fused_self(int layout, int MT, const uint16_t* x, const uint8_t* w13,
-                             const float* w13s, const uint8_t* w2, const float* w2s,
+                             const void* w13s, const uint8_t* w2, const void* w2s,
                              const SharedW& sh, const int32_t* ids, const float* aff, int T,
-                             int H, int I, int E, int k, float* ybuf, int act,
+                             int H, int I, int E, int k, float* ybuf, int act, int wfmt,
                              hipStream_t stream);
+// The same kernel after the sort (one workgroup per segment of the plan).
+int launch_decode_fused(int layout, int MT, const uint16_t* x, const uint8_t* w13,
+                        const void* w13s, const uint8_t* w2, const void* w2s, const SharedW& sh,
+                        const Plan& plan, const float* aff, int T, int H, int I, int E, int k,
+                        float* ybuf, int act, int wfmt, hipStream_t stream);
 int launch_decode_e4m3fn(const uint8_t* codes, uint16_t* out, int64_t n, hipStream_t stream);
 int launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t stream);
 

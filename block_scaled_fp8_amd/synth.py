@@ -31,6 +31,10 @@ Recipe (every draw is seeded; ``seed`` selects the stream):
   the up projection; ``w13_scale`` fp32 [E, 2I/128, H/128].  Non-gated
   (relu^2) experts draw the up projection alone, [E, I, H].
 * ``w2``   uint8 [E, H, I]; ``w2_scale`` fp32 [E, H/128, I/128].
+* MXFP4 weights (``weight_format="mxfp4"``, from the same draws): ``w13``
+  uint8 [E, 2I, H/2] and ``w2`` [E, H, I/2], two E2M1 codes a byte (element
+  2j in the low nibble of byte j), with uint8 E8M0 scales [E, 2I, H/32] and
+  [E, H, I/32], one per 32 consecutive elements of a row (``quantize_mx``).
 * shared expert (optional): the same format for one expert, drawn after the
   routed experts.
 * ``wg``  bf16 [E, H] router gate weights (for the router projection):
@@ -102,18 +106,52 @@ def quantize_blocks(w: torch.Tensor):
     return codes.contiguous(), scale.contiguous()
 
 
+# E2M1 magnitudes by code (codes 0..7; bit 3 is the sign)
+_E2M1_GRID = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
+
+
+def quantize_mx(w: torch.Tensor):
+    """fp32 [..., R, C] -> MXFP4: (uint8 [..., R, C/2] with element 2j in the
+    low nibble of byte j and 2j+1 in the high nibble, uint8 E8M0 scales
+    [..., R, C/32]).  Per block of 32 consecutive elements of a row: shared
+    exponent X = floor(log2(max|w|)) - 2 (2 = the largest E2M1 exponent), the
+    scale byte X + 127 clamped to 0..254, then each w / 2^X rounded to the
+    nearest E2M1 value (ties to the even code), saturating at +-6.  An all-zero
+    block gets scale byte 0 and zero codes."""
+    *lead, R, C = w.shape
+    assert C % 32 == 0, C
+    blk = w.reshape(*lead, R, C // 32, 32)
+    amax = blk.abs().amax(dim=-1)
+    X = torch.floor(torch.log2(torch.where(amax > 0, amax, torch.ones_like(amax)))) - 2
+    sbyte = torch.where(amax > 0, (X + 127).clamp(0, 254), torch.zeros_like(X))
+    X = sbyte - 127
+    q = (blk / torch.exp2(X)[..., None]).clamp(-6.0, 6.0)
+    a = q.abs()
+    grid = torch.tensor(_E2M1_GRID, dtype=torch.float32, device=w.device)
+    lo = (torch.searchsorted(grid, a.contiguous(), right=True) - 1).clamp(0, 7)
+    hi = (lo + 1).clamp(max=7)
+    d_lo, d_hi = a - grid[lo], grid[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = torch.where(pick_hi, hi, lo) | torch.where(torch.signbit(q), 8, 0)
+    code = code.to(torch.uint8).reshape(*lead, R, C)
+    packed = (code[..., 0::2] | (code[..., 1::2] << 4)).contiguous()
+    return packed, sbyte.to(torch.uint8).contiguous()
+
+
 def _draw_expert_weights(n: int, rows: int, cols: int, seed: int, tag: int, device,
-                         chunk_elems: int = 1 << 28):
+                         chunk_elems: int = 1 << 28, weight_format: str = "e4m3_128"):
     """n matrices [rows, cols] ~ N(0, 0.02), quantised; drawn in chunks of experts."""
-    codes = torch.empty((n, rows, cols), dtype=torch.uint8, device=device)
-    scales = torch.empty((n, rows // BLOCK, cols // BLOCK), dtype=torch.float32, device=device)
+    mx = weight_format == "mxfp4"
+    codes = torch.empty((n, rows, cols // 2 if mx else cols), dtype=torch.uint8, device=device)
+    scales = torch.empty((n, rows, cols // 32) if mx else (n, rows // BLOCK, cols // BLOCK),
+                         dtype=torch.uint8 if mx else torch.float32, device=device)
     per = max(1, chunk_elems // (rows * cols))
     for e0 in range(0, n, per):
         e1 = min(n, e0 + per)
         g = _gen(seed, tag * 65536 + e0, device)
         w = torch.randn((e1 - e0, rows, cols), generator=g, device=device,
                         dtype=torch.float32) * 0.02
-        c, s = quantize_blocks(w)
+        c, s = quantize_mx(w) if mx else quantize_blocks(w)
         codes[e0:e1] = c
         scales[e0:e1] = s
         del w, c, s
@@ -137,16 +175,21 @@ def make_activations(cfg: MoeConfig, seed: int, device="cpu"):
     return x.contiguous(), logits.contiguous()
 
 
-def make_weights(cfg: MoeConfig, seed: int, device="cpu", activation="swiglu"):
-    """Block-scaled FP8 expert weights; activation "relu2" draws non-gated
-    experts, whose first matrix is the up projection alone ([I, H])."""
+def make_weights(cfg: MoeConfig, seed: int, device="cpu", activation="swiglu",
+                 weight_format="e4m3_128"):
+    """Block-scaled expert weights: "e4m3_128" (E4M3FN codes, fp32 128x128
+    block scales) or "mxfp4" (quantize_mx: E2M1 codes two a byte, E8M0 scales
+    per 32 elements of a row), from the same N(0, 0.02) draws.  Activation
+    "relu2" draws non-gated experts, whose first matrix is the up projection
+    alone ([I, H])."""
     n13 = cfg.I if activation == "relu2" else 2 * cfg.I
-    w13, w13_scale = _draw_expert_weights(cfg.E, n13, cfg.H, seed, 3, device)
-    w2, w2_scale = _draw_expert_weights(cfg.E, cfg.H, cfg.I, seed, 4, device)
+    f = dict(weight_format=weight_format)
+    w13, w13_scale = _draw_expert_weights(cfg.E, n13, cfg.H, seed, 3, device, **f)
+    w2, w2_scale = _draw_expert_weights(cfg.E, cfg.H, cfg.I, seed, 4, device, **f)
     out = dict(w13=w13, w13_scale=w13_scale, w2=w2, w2_scale=w2_scale)
     if cfg.shared:
-        s13, s13s = _draw_expert_weights(1, n13, cfg.H, seed, 5, device)
-        s2, s2s = _draw_expert_weights(1, cfg.H, cfg.I, seed, 6, device)
+        s13, s13s = _draw_expert_weights(1, n13, cfg.H, seed, 5, device, **f)
+        s2, s2s = _draw_expert_weights(1, cfg.H, cfg.I, seed, 6, device, **f)
         out["shared"] = dict(w13=s13[0], w13_scale=s13s[0], w2=s2[0], w2_scale=s2s[0])
     else:
         out["shared"] = None
@@ -160,13 +203,14 @@ def make_gate_weights(E: int, H: int, seed: int, device="cpu"):
     return w.to(torch.bfloat16).contiguous()
 
 
-def make_case(cfg: MoeConfig | str, seed: int = 0, device="cpu", activation="swiglu"):
-    """All inputs of one workload: x, logits and the block-scaled FP8 weights."""
+def make_case(cfg: MoeConfig | str, seed: int = 0, device="cpu", activation="swiglu",
+              weight_format="e4m3_128"):
+    """All inputs of one workload: x, logits and the block-scaled weights."""
     if isinstance(cfg, str):
         cfg = CONFIGS[cfg]
     x, logits = make_activations(cfg, seed, device)
-    case = dict(cfg=cfg, x=x, logits=logits)
-    case.update(make_weights(cfg, seed, device, activation))
+    case = dict(cfg=cfg, x=x, logits=logits, weight_format=weight_format)
+    case.update(make_weights(cfg, seed, device, activation, weight_format))
     return case
 
 

@@ -310,6 +310,68 @@ int moe_fused_w8a16_noalloc(const void* x,
                             void* stream);
 
 /*
+ * moe_pack_mx_scales -- offline preparation of MXFP4 scales for
+ * MOE_LAYOUT_TILED (interface plumbing for the tiled layout, not from the
+ * pages): for each of n_mats matrices S[rows, cols] of E8M0 bytes (cols =
+ * K/32; rows % 16 == 0, cols % 4 == 0) the packed matrix P holds, for tile
+ * t < rows/16, chunk c < cols/4 and lane l < 64,
+ *     P[(t * (cols/4) + c) * 64 + l] = S[16t + l%16][4c + l/16],
+ * so that one wave's scale bytes of a 16-row, 128-element chunk are one
+ * 64-byte line.  src and dst are device pointers of n_mats*rows*cols bytes
+ * and must not overlap.
+ */
+int moe_pack_mx_scales(const uint8_t* src, uint8_t* dst, int64_t n_mats, int rows, int cols,
+                       void* stream);
+
+/* One expert's MXFP4 weights (same H and I as the routed experts). */
+typedef struct {
+    const uint8_t* w13;        /* [2I, H/2] E2M1 codes two a byte (relu^2: [I, H/2]) */
+    const uint8_t* w13_scale;  /* [2I, H/32] E8M0 (relu^2: [I, H/32]) */
+    const uint8_t* w2;         /* [H, I/2] */
+    const uint8_t* w2_scale;   /* [H, I/32] */
+} moe_expert_mx4;
+
+/*
+ * moe_fused_mxfp4 -- moe_fused_w8a16_ex with MXFP4 expert weights (W4A16).
+ * Sources: "Add gfx950 Q256 fused MXFP4 prefill pipeline" (ROCm/aiter
+ * PR #5988), description: the experts' weights are MXFP4; "NKI Library
+ * Supported Kernel Reference", Blockwise MM Block MX (MXFP4/MXFP8 MoE).  The
+ * pages do not spell the encoding out; the OCP Microscaling definition is
+ * taken: each element an E2M1 code (1 sign, 2 exponent bits with bias 1,
+ * 1 mantissa bit: +-{0, 0.5, 1, 1.5, 2, 3, 4, 6}), each run of 32
+ * consecutive elements of a row sharing one E8M0 scale byte s (2^(s - 127);
+ * 255 = NaN is out of contract).
+ *   w13        [E, 2I, H/2] bytes: element 2j of a row in the low nibble of
+ *              byte j, element 2j+1 in its high nibble (relu^2: [E, I, H/2])
+ *   w13_scale  [E, 2I, H/32] E8M0 bytes (relu^2: [E, I, H/32])
+ *   w2         [E, H, I/2], w2_scale [E, H, I/32], likewise
+ *              weight value = E2M1(code) * 2^(scale - 127)
+ *   shared     host pointer to a moe_expert_mx4, or NULL
+ *   weight_layout  MOE_LAYOUT_TILED: the code bytes packed by moe_pack_w8
+ *              (rows, cols = K/2) and the scales by moe_pack_mx_scales
+ *              (rows, cols = K/32); MOE_LAYOUT_ROWMAJOR: both as above
+ * Everything else as moe_fused_w8a16_ex; the workspace is that of
+ * MOE_VARIANT_DECODE (moe_fused_workspace_bytes).  The weights are streamed
+ * by the one-workgroup-per-expert decode kernel at every batch size:
+ * MOE_VARIANT_AUTO and MOE_VARIANT_DECODE run it, the prefill variants give
+ * MOE_EUNSUPPORTED, and so do shapes whose 16- or 32-row activation pass does
+ * not fit 64 KB of LDS (16 or 32 * (I + 8) * 2 bytes, plus 4 bytes a route
+ * when T*k <= 4096) or with T*H >= 2^32.  The E8M0 scale is applied exactly
+ * in the conversion to bf16 (every E2M1 value times a power of two is a
+ * bf16 value while it stays in bf16's normal range; smaller products are
+ * flushed to zero), products are summed in fp32 and the SwiGLU output is
+ * rounded to bf16 before the down GEMM.  Scales need no alignment.
+ */
+int moe_fused_mxfp4(const void* x,
+                    const uint8_t* w13, const uint8_t* w13_scale,
+                    const uint8_t* w2, const uint8_t* w2_scale,
+                    const int32_t* ids, const float* aff,
+                    int T, int H, int I, int E, int k,
+                    const moe_expert_mx4* shared, float* out,
+                    int32_t* status, void* ws, size_t ws_bytes,
+                    int weight_layout, int variant, int activation, void* stream);
+
+/*
  * moe_quant_e4m3_rows -- the per-token activation quantisation that
  * MOE_VARIANT_PREFILL_A8 applies to x, exposed so it can be checked on its
  * own.  For each row t:

@@ -1,4 +1,5 @@
-"""CPU oracle for the routed MoE expert FFN with block-scaled E4M3FN weights.
+"""CPU oracle for the routed MoE expert FFN with block-scaled E4M3FN weights
+(and MXFP4 weights: E2M1 codes with E8M0 scales per 32 elements).
 
 TEST INFRASTRUCTURE ONLY.  Nothing on the product path imports, calls or runs
 anything in this package: only the test suite, the package's smoke check and
@@ -10,7 +11,7 @@ statement of the method; see ``moe_ref`` for the citation of each step.
 
 Parity status: every function here is pinned by ``tests/test_oracle_pins.py``
 against values that do not come from the oracle itself (torch's own E4M3FN
-cast, brute-force enumeration, closed forms computed by hand, library dense
+and E8M0 casts, E2M1 values worked by hand from the format, brute-force enumeration, closed forms computed by hand, library dense
 MLPs, invariants).  Outputs at the full workload sizes have no printed values
 on the pages; they are pinned only through those invariants.
 """
@@ -19,6 +20,11 @@ from .moe_ref import (  # noqa: F401
     e4m3fn_table,
     e4m3fn_decode,
     dequantize_blocks,
+    e2m1_table,
+    e8m0_value,
+    unpack_fp4,
+    dequantize_mx,
+    dequantize_weights,
     e4m3fn_encode_rne,
     quantize_rows_e4m3,
     dequantize_rows,

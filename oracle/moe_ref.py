@@ -126,6 +126,74 @@ def dequantize_rows(codes, scales) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
+# MXFP4 weights  ([AITER] description: the prefill pipeline's weights are
+# MXFP4; [NKILIB] Blockwise MM Block MX: MXFP4/MXFP8 MoE).  The pages name the
+# format without spelling it out; this follows the OCP Microscaling (MX)
+# definition: FP4 E2M1 elements, one E8M0 scale per 32 consecutive elements.
+# --------------------------------------------------------------------------
+MX_BLOCK = 32
+
+
+def _e2m1_value(code: int) -> float:
+    """Value of one E2M1 code (4 bits): 1 sign bit, 2 exponent bits (bias 1),
+    1 mantissa bit, subnormal at exponent 0, no infinities or NaN."""
+    s = (code >> 3) & 1
+    e = (code >> 1) & 0x3
+    m = code & 0x1
+    if e == 0:                       # subnormal: 0.m * 2^(1-1)
+        mag = m / 2.0
+    else:                            # normal: 1.m * 2^(e-1)
+        mag = (1.0 + m / 2.0) * 2.0 ** (e - 1)
+    return -mag if s else mag
+
+
+def e2m1_table() -> np.ndarray:
+    """The value of each of the 16 E2M1 codes, float64."""
+    return np.array([_e2m1_value(c) for c in range(16)], dtype=np.float64)
+
+
+_E2M1 = e2m1_table()
+
+
+def e8m0_value(s) -> np.ndarray:
+    """E8M0 scale bytes: 2^(s - 127) for s = 0..254; 255 is NaN."""
+    s = np.asarray(s, dtype=np.int64)
+    v = np.ldexp(1.0, s - 127)
+    return np.where(s == 255, np.nan, v)
+
+
+def unpack_fp4(packed) -> np.ndarray:
+    """[..., C/2] bytes -> [..., C] E2M1 codes: element 2j is the low nibble of
+    byte j and element 2j+1 its high nibble."""
+    b = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(b.shape[:-1] + (2 * b.shape[-1],), dtype=np.uint8)
+    out[..., 0::2] = b & 0x0F
+    out[..., 1::2] = b >> 4
+    return out
+
+
+def dequantize_mx(packed, scales, block: int = MX_BLOCK) -> np.ndarray:
+    """W[r, c] = E2M1(code[r, c]) * 2^(scales[r, c // 32] - 127) (float64).
+
+    ``packed`` is [..., R, C/2] uint8 (two codes a byte), ``scales`` [..., R,
+    C/32] uint8 E8M0."""
+    vals = _E2M1[unpack_fp4(packed)]
+    s = np.repeat(e8m0_value(scales), block, axis=-1)
+    assert s.shape == vals.shape, (s.shape, vals.shape)
+    return vals * s
+
+
+def dequantize_weights(codes, scales, weight_format: str = "e4m3_128") -> np.ndarray:
+    """Dequantised float64 weights of either stored format: "e4m3_128"
+    (E4M3FN codes, fp32 128x128 block scales) or "mxfp4" (E2M1 codes two a
+    byte, E8M0 scales per 32 elements of a row)."""
+    if weight_format == "mxfp4":
+        return dequantize_mx(codes, scales)
+    assert weight_format == "e4m3_128", weight_format
+    return dequantize_blocks(codes, scales)
+
+
+# --------------------------------------------------------------------------
 # Routing: softmax -> top-k -> normalise  ([NKI] Serving contract)
 # --------------------------------------------------------------------------
 def route_softmax_topk(logits, k: int):
@@ -229,13 +297,15 @@ def relu2(u):
     return np.maximum(u, 0.0) ** 2
 
 
-def expert_mlp(xrows, w13, w13_scale, w2, w2_scale, activation="swiglu"):
+def expert_mlp(xrows, w13, w13_scale, w2, w2_scale, activation="swiglu",
+               weight_format="e4m3_128"):
     """One expert on rows of x (float64 [M, H]) -> float64 [M, H].
 
     SwiGLU: w13 [2I, H] (gate rows first, then up rows); relu2 ([SPARK] module
     documentation: up projection, then relu^2 and the down projection): w13
-    [I, H] is the up projection alone.  w2 [H, I]; all block-scaled."""
-    W13 = dequantize_blocks(w13, w13_scale)
+    [I, H] is the up projection alone.  w2 [H, I]; all block-scaled (see
+    dequantize_weights for the two formats)."""
+    W13 = dequantize_weights(w13, w13_scale, weight_format)
     if activation == "relu2":
         a = relu2(xrows @ W13.T)
     else:
@@ -243,11 +313,12 @@ def expert_mlp(xrows, w13, w13_scale, w2, w2_scale, activation="swiglu"):
         g = xrows @ W13[:I].T
         u = xrows @ W13[I:].T
         a = swiglu(g, u)
-    W2 = dequantize_blocks(w2, w2_scale)
+    W2 = dequantize_weights(w2, w2_scale, weight_format)
     return a @ W2.T
 
 
-def moe_ffn(x, w13, w13_scale, w2, w2_scale, ids, aff, shared=None, activation="swiglu"):
+def moe_ffn(x, w13, w13_scale, w2, w2_scale, ids, aff, shared=None, activation="swiglu",
+            weight_format="e4m3_128"):
     """out[t] = sum_j aff[t, j] * MLP_{ids[t, j]}(x[t]) (+ shared MLP(x[t])).
 
     x is [T, H] (bf16 values given as float32/float64), ids [T, k], aff [T, k].
@@ -260,11 +331,12 @@ def moe_ffn(x, w13, w13_scale, w2, w2_scale, ids, aff, shared=None, activation="
     out = np.zeros((T, H), dtype=np.float64)
     for e in np.unique(ids):
         t_idx, j_idx = np.nonzero(ids == e)
-        y = expert_mlp(x[t_idx], w13[e], w13_scale[e], w2[e], w2_scale[e], activation)
+        y = expert_mlp(x[t_idx], w13[e], w13_scale[e], w2[e], w2_scale[e], activation,
+                       weight_format)
         np.add.at(out, t_idx, aff[t_idx, j_idx][:, None] * y)
     if shared is not None:
         out += expert_mlp(x, shared["w13"], shared["w13_scale"],
-                          shared["w2"], shared["w2_scale"], activation)
+                          shared["w2"], shared["w2_scale"], activation, weight_format)
     return out
 
 

@@ -11,12 +11,12 @@ OUT_TOL = 2e-2          # max |gpu - oracle| <= OUT_TOL * RMS(oracle output)
 AFF_RTOL = 2e-6         # fp32 exp/sum/divide against float64
 
 
-def gpu_case(name_or_cfg, seed=0, activation="swiglu"):
+def gpu_case(name_or_cfg, seed=0, activation="swiglu", weight_format="e4m3_128"):
     cfg = synth.CONFIGS[name_or_cfg] if isinstance(name_or_cfg, str) else name_or_cfg
     dev = "cuda"
     # tiny geometries are drawn on the CPU; the large ones on the GPU
     gen_dev = "cpu" if cfg.E * 3 * cfg.H * cfg.I < (64 << 20) else dev
-    case = synth.make_case(cfg, seed, gen_dev, activation)
+    case = synth.make_case(cfg, seed, gen_dev, activation, weight_format)
     case["activation"] = activation
     for n in ("x", "logits", "w13", "w13_scale", "w2", "w2_scale"):
         case[n] = case[n].to(dev)
@@ -47,7 +47,8 @@ def oracle_rows(case, ids, aff, rows, with_shared=True, xrows=None):
         sh = {n: np_(t) for n, t in case["shared"].items()}
     x = np_(case["x"].double())[rows] if xrows is None else np.asarray(xrows, dtype=np.float64)
     return oracle.moe_ffn(x, w13, w13s, w2, w2s, remap, np.asarray(aff)[rows], sh,
-                          activation=case.get("activation", "swiglu"))
+                          activation=case.get("activation", "swiglu"),
+                          weight_format=case.get("weight_format", "e4m3_128"))
 
 
 def assert_out_close(got, ref, tol=OUT_TOL, what=""):
@@ -86,14 +87,7 @@ def pack_reference(w):
 
 
 def tiled_case(case):
-    """A copy of a GPU case whose expert weights are packed for the tiled layout."""
+    """A copy of a GPU case whose expert weights are packed for the tiled
+    layout (MXFP4 scales too)."""
     from block_scaled_fp8_amd import binding
-    out = dict(case)
-    out["w13"] = binding.pack_w8(case["w13"])
-    out["w2"] = binding.pack_w8(case["w2"])
-    if case.get("shared") is not None:
-        sh = dict(case["shared"])
-        sh["w13"] = binding.pack_w8(sh["w13"])
-        sh["w2"] = binding.pack_w8(sh["w2"])
-        out["shared"] = sh
-    return out
+    return binding.pack_weights(case, case.get("weight_format", "e4m3_128"))

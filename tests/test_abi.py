@@ -230,6 +230,34 @@ def test_binding_refuses_cpu_tensors():
         binding.route(torch.zeros((4, 8), dtype=torch.float32), 2)
 
 
+def test_pack_mx_scales_argument_checks():
+    lib = binding.load_library()
+    f = ctypes.c_void_p(0x1000)
+    g = ctypes.c_void_p(0x1000 + 8 * 256 * 64)
+    assert lib.moe_pack_mx_scales(f, g, 8, 250, 64, None) == binding.MOE_EINVAL   # rows % 16
+    assert lib.moe_pack_mx_scales(f, g, 8, 256, 6, None) == binding.MOE_EINVAL    # cols % 4
+    assert lib.moe_pack_mx_scales(f, ctypes.c_void_p(0x1040), 8, 256, 64, None) == binding.MOE_EINVAL
+    assert b"overlap" in lib.moe_last_error()
+    assert lib.moe_pack_mx_scales(None, None, 0, 256, 64, None) == binding.MOE_OK
+
+
+def test_mxfp4_argument_checks():
+    """moe_fused_mxfp4 refuses the prefill variants and unknown arguments
+    before any launch; its E8M0 scales need no alignment."""
+    lib = binding.load_library()
+    f, o = ctypes.c_void_p(0x1000), ctypes.c_void_p(0x3000)
+    ws = lib.moe_fused_workspace_bytes(64, 2048, 512, 256, 8, 0, 1)
+    args = lambda variant, act=0, s13=f, ws_ptr=f: (  # noqa: E731
+        f, f, s13, f, f, f, f, 64, 2048, 512, 256, 8, None, o, None, ws_ptr, ws, 0, variant, act, None)
+    for v in (2, 3):
+        assert lib.moe_fused_mxfp4(*args(v)) == binding.MOE_EUNSUPPORTED
+        assert b"MXFP4" in lib.moe_last_error()
+    assert lib.moe_fused_mxfp4(*args(1, 2)) == binding.MOE_EINVAL
+    assert b"activation" in lib.moe_last_error()
+    assert lib.moe_fused_mxfp4(*args(1, 0, f, ctypes.c_void_p(0x1004))) == binding.MOE_EINVAL
+    assert b"aligned" in lib.moe_last_error()
+
+
 def test_pack_argument_checks():
     lib = binding.load_library()
     f = ctypes.c_void_p(0x1000)

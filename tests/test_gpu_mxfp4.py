@@ -1,0 +1,169 @@
+"""GPU parity of the MXFP4-weight path (moe_fused_mxfp4, W4A16) against the
+float64 oracle on the same codes and scales.
+
+MXFP4 as named by "Add gfx950 Q256 fused MXFP4 prefill pipeline" (ROCm/aiter
+PR #5988) and "NKI Library Supported Kernel Reference" (Blockwise MM Block
+MX), read as the OCP Microscaling format: E2M1 codes, one E8M0 scale per 32
+consecutive elements of a row.  Same bar as the FP8 path: routing ids exact,
+max |gpu - oracle| <= 2e-2 * RMS(oracle output), every row up to the
+8192-token workload and the structured sample at 16384 tokens.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_scaled_fp8_amd import binding, synth
+
+from _parity import assert_out_close, gpu_case, np_, oracle_rows, tiled_case
+from test_gpu_parity import check_rows
+
+pytestmark = pytest.mark.gpu
+
+_cases = {}
+_oracle = {}
+
+
+def setup_module(module):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    binding.load_library()
+
+
+def _case(name, activation):
+    key = (name, activation)
+    if key not in _cases:
+        _cases.clear()
+        _oracle.clear()
+        torch.cuda.empty_cache()
+        c = gpu_case(name, seed=1, activation=activation, weight_format="mxfp4")
+        c["tiled"] = tiled_case(c)
+        _cases[key] = c
+    return _cases[key]
+
+
+def _run(c, ids, aff, layout, activation, variant="auto", shared=True, status=None):
+    g = c["tiled"] if layout == "tiled" else c
+    return binding.fused_w8a16(g["x"], g["w13"], g["w13_scale"], g["w2"], g["w2_scale"], ids, aff,
+                               shared=g["shared"] if shared else None, variant=variant,
+                               layout=layout, activation=activation, weight_format="mxfp4",
+                               status=status)
+
+
+@pytest.mark.parametrize("layout", ["rowmajor", "tiled"])
+@pytest.mark.parametrize("activation", ["swiglu", "relu2"])
+@pytest.mark.parametrize("name", synth.CONFIG_ORDER)
+def test_mxfp4_parity(name, activation, layout):
+    c = _case(name, activation)
+    cfg = c["cfg"]
+    ids, aff = binding.route(c["logits"], cfg.k)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = _run(c, ids, aff, layout, activation, status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    ref_ids, ref_aff = oracle.route_softmax_topk(np_(c["logits"]), cfg.k)
+    assert np.array_equal(np_(ids), ref_ids)
+    rows = check_rows(name, cfg, ref_ids)
+    if activation not in _oracle:
+        _oracle[activation] = oracle_rows(c, ref_ids, ref_aff, rows)
+    assert_out_close(np_(out)[rows], _oracle[activation],
+                     what=f"mxfp4 {name}/{activation}/{layout} ({len(rows)} rows)")
+
+
+# odd chunk counts (H/128 = 3, I/128 = 1 or 3), token boundaries and both
+# self-routed (T*k <= 4096) and sorted (T*k > 4096) forms
+@pytest.mark.parametrize("layout", ["rowmajor", "tiled"])
+@pytest.mark.parametrize("T,H,I,E,k", [(1, 384, 128, 16, 4), (17, 384, 384, 16, 4),
+                                       (37, 256, 128, 8, 2), (130, 384, 256, 130, 8),
+                                       (1100, 256, 128, 64, 4)])
+def test_mxfp4_shapes(T, H, I, E, k, layout):
+    cfg = synth.MoeConfig("mxs", T=T, H=H, I=I, E=E, k=k, shared=True)
+    c = gpu_case(cfg, seed=T + H, weight_format="mxfp4")
+    g = tiled_case(c) if layout == "tiled" else c
+    ids, aff = binding.route(c["logits"], k)
+    out = binding.fused_w8a16(g["x"], g["w13"], g["w13_scale"], g["w2"], g["w2_scale"], ids, aff,
+                              shared=g["shared"], layout=layout, weight_format="mxfp4")
+    torch.cuda.synchronize()
+    ref_ids, ref_aff = oracle.route_softmax_topk(np_(c["logits"]), k)
+    ref = oracle_rows(c, ref_ids, ref_aff, np.arange(T))
+    assert_out_close(np_(out), ref, what=f"mxfp4 T={T} H={H} I={I} E={E} k={k}/{layout}")
+
+
+def test_mxfp4_scale_bytes_at_the_ends_and_zero_affinities():
+    """Scale bytes 1 (2^-126) and 140 (2^13) on some blocks, the rest as drawn;
+    outputs stay finite and match the oracle; zero affinities give exactly 0."""
+    cfg = synth.MoeConfig("mxe", T=24, H=256, I=256, E=8, k=2)
+    c = gpu_case(cfg, seed=5, weight_format="mxfp4")
+    c["w13_scale"][:, ::7, 1] = 1
+    c["w2_scale"][:, ::5, 0] = 1
+    c["w13_scale"][3, 0, 0] = 140   # one gate block of expert 3: 2^13 instead of about 2^-9
+    ids, aff = binding.route(c["logits"], cfg.k)
+    out = binding.fused_w8a16(c["x"], c["w13"], c["w13_scale"], c["w2"], c["w2_scale"], ids, aff,
+                              weight_format="mxfp4")
+    torch.cuda.synchronize()
+    ref_ids, ref_aff = oracle.route_softmax_topk(np_(c["logits"]), cfg.k)
+    ref = oracle_rows(c, ref_ids, ref_aff, np.arange(cfg.T))
+    assert np.all(np.isfinite(ref))
+    assert_out_close(np_(out), ref, what="mxfp4 scale bytes 1 and 140")
+    zero = torch.zeros_like(aff)
+    out0 = binding.fused_w8a16(c["x"], c["w13"], c["w13_scale"], c["w2"], c["w2_scale"], ids,
+                               zero, weight_format="mxfp4")
+    torch.cuda.synchronize()
+    assert int(torch.count_nonzero(out0).item()) == 0
+
+
+@pytest.mark.parametrize("shape", [(1, 16, 4), (3, 256, 64), (2, 1024, 16)])
+def test_pack_mx_scales_matches_reference(shape):
+    g = torch.Generator().manual_seed(sum(shape))
+    sc = torch.randint(0, 256, shape, generator=g, dtype=torch.int64).to(torch.uint8)
+    got = np_(binding.pack_mx_scales(sc.cuda()))
+    n, R, C = shape
+    ref = np.empty(n * R * C, np.uint8)
+    src = sc.numpy()
+    for m in range(n):
+        for t in range(R // 16):
+            for c in range(C // 4):
+                for l in range(64):
+                    ref[m * R * C + (t * (C // 4) + c) * 64 + l] = src[m, 16 * t + l % 16, 4 * c + l // 16]
+    assert np.array_equal(got.reshape(-1), ref)
+
+
+def test_mxfp4_prefill_variants_are_refused():
+    cfg = synth.MoeConfig("mxp", T=8, H=256, I=256, E=8, k=2)
+    c = gpu_case(cfg, seed=6, weight_format="mxfp4")
+    ids, aff = binding.route(c["logits"], cfg.k)
+    for v in ("prefill", "prefill_a8"):
+        with pytest.raises(binding.MoeError) as ei:
+            binding.fused_w8a16(c["x"], c["w13"], c["w13_scale"], c["w2"], c["w2_scale"], ids,
+                                aff, variant=v, weight_format="mxfp4")
+        assert ei.value.code == binding.MOE_EUNSUPPORTED
+
+
+def test_mxfp4_is_deterministic_and_graph_replays():
+    cfg = synth.MoeConfig("mxg", T=64, H=512, I=256, E=128, k=4, shared=True)
+    c = gpu_case(cfg, seed=7, weight_format="mxfp4")
+    ids, aff = binding.route(c["logits"], cfg.k)
+    a = _run(c, ids, aff, "rowmajor", "swiglu")
+    b = _run(c, ids, aff, "rowmajor", "swiglu")
+    assert torch.equal(a, b)
+    ws = torch.empty(binding.fused_workspace_bytes(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, True,
+                                                   "decode"), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(a)
+
+    def step():
+        binding.fused_w8a16(c["x"], c["w13"], c["w13_scale"], c["w2"], c["w2_scale"], ids, aff,
+                            shared=c["shared"], out=out, ws=ws, weight_format="mxfp4")
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(3):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, a)

@@ -27,6 +27,126 @@ def _golden_lines(name):
         return [ln.strip() for ln in f if ln.strip() and not ln.startswith("#")]
 
 
+# ----------------------------------------------------------------- MXFP4
+def _e2m1_golden():
+    out = {}
+    for ln in _golden_lines("e2m1_values.txt"):
+        code, val = ln.split()[:2]
+        out[int(code, 16)] = float(val)
+    return out
+
+
+def test_e2m1_table_matches_hand_values():
+    gold = _e2m1_golden()
+    assert sorted(gold) == list(range(16))
+    got = oracle.e2m1_table()
+    for c, v in gold.items():
+        assert got[c] == v and np.signbit(got[c]) == np.signbit(v), hex(c)
+
+
+def test_e2m1_structure():
+    t = oracle.e2m1_table()
+    assert np.all(np.diff(t[:8]) > 0)               # magnitudes increase with the code
+    assert np.array_equal(t[8:], -t[:8])            # the sign bit mirrors them
+    # every value is exact in bf16 (8 significant bits) and in E4M3FN
+    bf = torch.tensor(t, dtype=torch.float64).to(torch.bfloat16).double().numpy()
+    assert np.array_equal(bf, t)
+    f8 = torch.tensor(t, dtype=torch.float64).to(torch.float8_e4m3fn).double().numpy()
+    assert np.array_equal(f8, t)
+
+
+def test_e8m0_matches_torch_cast():
+    codes = torch.arange(256, dtype=torch.int64).to(torch.uint8)
+    ref = codes.view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    got = oracle.e8m0_value(codes.numpy())
+    assert np.isnan(got[255]) and np.isnan(ref[255])
+    assert np.array_equal(got[:255], ref[:255])
+    assert got[127] == 1.0 and got[0] == 2.0 ** -127 and got[254] == 2.0 ** 127
+
+
+def test_unpack_fp4_nibble_order():
+    # byte j holds element 2j in its low nibble and 2j+1 in its high nibble
+    packed = np.array([[0x71, 0x0F, 0xA3]], np.uint8)
+    assert oracle.unpack_fp4(packed).tolist() == [[1, 7, 15, 0, 3, 10]]
+    vals = oracle.dequantize_mx(np.tile(packed, (1, 32 // 3 + 1))[:, :16],
+                                np.array([[127]], np.uint8))
+    assert vals[0, :6].tolist() == [0.5, 6.0, -6.0, 0.0, 1.5, -1.0]
+
+
+def test_dequantize_mx_block_indexing():
+    # one scale byte 130 (x8) among 127s (x1): exactly that row's 32-element block scales
+    R, C = 4, 128
+    rng = np.random.default_rng(3)
+    packed = rng.integers(0, 256, (R, C // 2), dtype=np.uint8)
+    sc = np.full((R, C // 32), 127, np.uint8)
+    sc[2, 1] = 130
+    got = oracle.dequantize_mx(packed, sc)
+    g = _e2m1_golden()
+    codes = np.empty((R, C), np.int64)
+    codes[:, 0::2], codes[:, 1::2] = packed & 15, packed >> 4
+    ref = np.vectorize(lambda c: g[c])(codes)
+    ref[2, 32:64] *= 8.0
+    assert np.array_equal(got, ref)
+
+
+def test_mx_quantiser_round_trip():
+    w = torch.randn(3, 64, 256, generator=torch.Generator().manual_seed(9)) * 0.02
+    packed, sc = synth.quantize_mx(w)
+    d = oracle.dequantize_mx(packed.numpy(), sc.numpy())
+    step = np.repeat(oracle.e8m0_value(sc.numpy()), 32, -1)     # 2^X of each block
+    q = w.double().numpy() / step
+    # inside the E2M1 range the error is at most half a grid spacing (<= 1 unit
+    # of 2^X between 4 and 6); beyond 6 the value saturates at 6
+    inside = np.abs(q) <= 6
+    assert np.all(np.abs(d - w.double().numpy())[inside] <= 1.0 * step[inside])
+    assert np.all(np.abs(d[~inside]) == 6 * step[~inside])
+    # values on the grid times a power of two come back exactly
+    gridw = torch.tensor(oracle.e2m1_table()[[1, 2, 3, 4, 5, 6, 7, 9, 15]] * 2.0 ** -9,
+                         dtype=torch.float32).repeat(1, 32)[:, :32 * 4].reshape(1, 1, -1)
+    gridw[..., 0] = 6 * 2.0 ** -9          # every block holds the largest value
+    gridw[..., 32] = gridw[..., 64] = gridw[..., 96] = 6 * 2.0 ** -9
+    p2, s2 = synth.quantize_mx(gridw)
+    assert np.array_equal(oracle.dequantize_mx(p2.numpy(), s2.numpy()), gridw.double().numpy())
+
+
+def _torch_deq_mx(packed, sc):
+    """MXFP4 dequantisation with the hand-worked E2M1 values and torch's
+    float8_e8m0fnu cast (independent of the oracle's code)."""
+    g = _e2m1_golden()
+    lut = torch.tensor([g[c] for c in range(16)], dtype=torch.float64)
+    p = torch.as_tensor(packed).to(torch.int64)
+    codes = torch.stack([p & 15, p >> 4], dim=-1).flatten(-2)
+    s = torch.as_tensor(sc).view(torch.float8_e8m0fnu).to(torch.float64)
+    return lut[codes] * s.repeat_interleave(32, -1)
+
+
+def test_ffn_mxfp4_single_expert_and_mixture_are_dense_mlps():
+    E, T = 3, 5
+    cfg = synth.MoeConfig("mx", T=T, H=256, I=128, E=E, k=1)
+    c = synth.make_case(cfg, 12, weight_format="mxfp4")
+    x = c["x"].float().numpy()
+    w = {n: c[n].numpy() for n in ("w13", "w13_scale", "w2", "w2_scale")}
+    xx = torch.as_tensor(x, dtype=torch.float64)
+
+    def dense(e):
+        W13 = _torch_deq_mx(c["w13"][e], c["w13_scale"][e])
+        W2 = _torch_deq_mx(c["w2"][e], c["w2_scale"][e])
+        I = W13.shape[0] // 2
+        return (torch.nn.functional.silu(xx @ W13[:I].T) * (xx @ W13[I:].T)) @ W2.T
+
+    got = oracle.moe_ffn(x, w["w13"], w["w13_scale"], w["w2"], w["w2_scale"],
+                         np.full((T, 1), 1, np.int32), np.ones((T, 1)), weight_format="mxfp4")
+    ref = dense(1).numpy()
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+    logits = c["logits"].numpy()
+    ids, aff = oracle.route_softmax_topk(logits, E)
+    got = oracle.moe_ffn(x, w["w13"], w["w13_scale"], w["w2"], w["w2_scale"], ids, aff,
+                         weight_format="mxfp4")
+    p = torch.softmax(torch.as_tensor(logits, dtype=torch.float64), dim=1)
+    ref = sum(p[:, e:e + 1] * dense(e) for e in range(E)).numpy()
+    np.testing.assert_allclose(got, ref, rtol=1e-11, atol=1e-12 * np.abs(ref).max())
+
+
 # ----------------------------------------------------------------- E4M3FN
 def test_e4m3fn_all_codes_match_torch_cast():
     codes = torch.arange(256, dtype=torch.int64).to(torch.uint8)
