@@ -57,8 +57,19 @@ constexpr int DF_HALF = DF_NT / 2;
 constexpr int DF_SELF_MAX_ROUTES = 4096;
 constexpr int DF_SELF_IDS_PER_THREAD = DF_SELF_MAX_ROUTES / DF_THREADS;
 
-size_t decode_fused_lds_bytes(int MT, int I, int self_routes) {
-    return sizeof(uint16_t) * (size_t)(16 * MT) * (I + 8) + sizeof(int32_t) * (size_t)self_routes;
+// LDS: the SwiGLU activations [16 MT][I + 8], then (x staged) the pass's
+// token rows of x [16 MT][H + 8], then (self-routed) the expert's routes.
+size_t decode_fused_lds_bytes(int MT, int I, int self_routes, int H) {
+    return sizeof(uint16_t) * (size_t)(16 * MT) * (I + 8) +
+           (H > 0 ? sizeof(uint16_t) * (size_t)(16 * MT) * (H + 8) : 0) +
+           sizeof(int32_t) * (size_t)self_routes;
+}
+
+// The pass's x rows go to LDS (and every wave reads its operands there
+// instead of re-reading them from L2 for each weight chunk) when a row is a
+// whole number of 1 KB wave loads and everything fits one workgroup's LDS.
+bool decode_fused_x_in_lds(int MT, int H, int I, int self_routes) {
+    return H % 512 == 0 && decode_fused_lds_bytes(MT, I, self_routes, H) <= 160 * 1024;
 }
 
 // RELU2: a non-gated expert, w13 = the up projection [I, H] alone; a phase-1
@@ -74,7 +85,10 @@ size_t decode_fused_lds_bytes(int MT, int I, int self_routes) {
 // MFMA sub-steps per chunk, sub-step s taking K [32g + 8s, 32g + 8s + 8) of
 // both operands.  Scales are void pointers: fp32 [rows/128][K/128] blocks, or
 // E8M0 bytes [rows][K/32] for MX4.
-template <int MT, int DEPTH, int LAYOUT, bool SELF, bool RELU2, bool MX4>
+//
+// XLDS: the token rows of each pass are staged in LDS once (direct-to-LDS
+// wave loads), and phase 1 reads its activation operands there.
+template <int MT, int DEPTH, int LAYOUT, bool SELF, bool RELU2, bool MX4, bool XLDS>
 __global__ __launch_bounds__(DF_THREADS) void decode_fused_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ w13,
     const void* __restrict__ w13s, const uint8_t* __restrict__ w2,
@@ -90,10 +104,12 @@ __global__ __launch_bounds__(DF_THREADS) void decode_fused_kernel(
     constexpr int CS = chunk_stride<LAYOUT>();
     extern __shared__ uint16_t a_lds[];  // [MROWS][I + 8] bf16 SwiGLU activations
     const int astride = I + 8;  // +16 bytes per row: conflict-free 16-byte column reads
+    const int xstride = H + 8;  // (XLDS) x rows, padded likewise
+    uint16_t* x_lds = a_lds + (size_t)MROWS * astride;
     const int lane = lane_id(), wave = wave_id();
     const int R = T * k;
     int e, row0, rows;
-    int32_t* rlist = reinterpret_cast<int32_t*>(a_lds + (size_t)MROWS * astride);  // SELF: routes of e
+    int32_t* rlist = reinterpret_cast<int32_t*>(x_lds + (XLDS ? (size_t)MROWS * xstride : 0));  // SELF: routes of e
     if (SELF) {
         const int b = blockIdx.x;
         if (b > E || (b == E && sh_w13 == nullptr)) return;
@@ -252,7 +268,7 @@ __global__ __launch_bounds__(DF_THREADS) void decode_fused_kernel(
         };
         auto issue1 = [&](int d) {
             issue1_b(d, ig % G1, ic);
-            issue1_a(d, ic);
+            if (!XLDS) issue1_a(d, ic);
             if (++ic == nch1) { ic = 0; ig += DF_WAVES; }
         };
         auto issue2 = [&](int d) {
@@ -291,10 +307,12 @@ __global__ __launch_bounds__(DF_THREADS) void decode_fused_kernel(
             }
             u32x4 av[MT][NS];
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
+            for (int mt = 0; mt < MT; ++mt) {
+                const u32x4* q = reinterpret_cast<const u32x4*>(x_lds + xoff[mt] + pc * KC);
 #pragma unroll
                 for (int s = 0; s < NS; ++s)
-                    av[mt][s] = xvalid[mt] ? aq[d][mt][s] : u32x4{0u, 0u, 0u, 0u};
+                    av[mt][s] = !xvalid[mt] ? u32x4{0u, 0u, 0u, 0u} : XLDS ? q[s] : aq[d][mt][s];
+            }
             mfma_chunk(d, av);
             if (!MX4 && d == 1) {  // the block's second chunk: fold it
                 if (RELU2) {
@@ -374,11 +392,16 @@ __global__ __launch_bounds__(DF_THREADS) void decode_fused_kernel(
         };
 
         reset();
-        // weight prologue first (it needs only the expert), then the token ids
+        // weight prologue first (it needs only the expert), then the token ids;
+        // the first DEPTH stream positions may cross a group end (one chunk a
+        // group: MX4 with K = 128)
+        int pcd[DEPTH];
 #pragma unroll
-        for (int d = 0; d < DEPTH; ++d) issue1_b(d, ig % G1, d);
-        ic = DEPTH;
-        if (ic == nch1) { ic = 0; ig += DF_WAVES; }
+        for (int d = 0; d < DEPTH; ++d) {
+            pcd[d] = ic;
+            issue1_b(d, ig % G1, ic);
+            if (++ic == nch1) { ic = 0; ig += DF_WAVES; }
+        }
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
             const int m = mp + mt * 16 + ln;
@@ -387,6 +410,8 @@ __global__ __launch_bounds__(DF_THREADS) void decode_fused_kernel(
             xvalid[mt] = t >= 0;
             xoff[mt] = (uint32_t)(t >= 0 ? t : 0) * (uint32_t)H + lg * (KC / 4);
             aoff[mt] = (uint32_t)((mt * 16 + ln) * astride + lg * (KC / 4));
+            // (XLDS: the phase-1 operand offset in x_lds, from x_lds)
+            if (XLDS) xoff[mt] = (uint32_t)((mt * 16 + ln) * xstride + lg * (KC / 4));
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int mi = mp + mt * 16 + lg * 4 + i;
@@ -400,8 +425,25 @@ __global__ __launch_bounds__(DF_THREADS) void decode_fused_kernel(
                 yaff[mt][i] = a;
             }
         }
+        if constexpr (XLDS) {
+            // stage the pass's token rows: wave w loads rows w, w + 8, ...; a
+            // wave load moves 1 KB of one row (padding rows read token 0)
+            const int per_row = H / 512;
+            for (int r = wave; r < MROWS; r += DF_WAVES) {
+                const int m = mp + r;
+                int t = 0;
+                if (m < rows) t = e >= 0 ? route_of(m) / k : route_of(m) - R;
+                t = __builtin_amdgcn_readfirstlane(t < 0 ? 0 : t);
+                const uint16_t* src = x + (size_t)t * H + lane * 8;
+                char* dst = reinterpret_cast<char*>(x_lds) + (size_t)r * xstride * 2;
+                for (int i = 0; i < per_row; ++i)
+                    __builtin_amdgcn_global_load_lds(src + i * 512, dst + i * 1024, 16, 0, 0);
+            }
+            __syncthreads();  // (waits for the loads too) every x row is in LDS
+        } else {
 #pragma unroll
-        for (int d = 0; d < DEPTH; ++d) issue1_a(d, d);
+            for (int d = 0; d < DEPTH; ++d) issue1_a(d, pcd[d]);
+        }
         int p0 = 0;
         for (; p0 + DEPTH < tot1; p0 += DEPTH) {
 #pragma unroll
@@ -438,18 +480,27 @@ static int launch_decode_fused_l(int MT, const uint16_t* x, const uint8_t* w13, 
                                  const Plan& plan, const int32_t* ids, const float* aff, int T,
                                  int H, int I, int E, int k, float* ybuf, hipStream_t stream) {
     const int nseg_max = E + (sh.w13 ? 1 : 0);
-    const size_t lds = decode_fused_lds_bytes(MT, I, SELF ? T * k : 0);
+    const int routes = SELF ? T * k : 0;
+    // (x rows in LDS: MXFP4 16-row passes whose rows fit; see
+    // decode_fused_x_in_lds.  Measured on decode64: MXFP4 72.4 -> 70.3 us,
+    // while the E4M3FN stream went from 115.9 to 117.8 us, so it keeps its
+    // operand loads from L2)
+    const bool xlds = MX4 && MT == 1 && decode_fused_x_in_lds(MT, H, I, routes);
+    const size_t lds = decode_fused_lds_bytes(MT, I, routes, xlds ? H : 0);
     // the trash row sits right after the last real row of y
     const int ytrash = T * k + (sh.w13 ? T : 0);
     prof_begin(MX4 ? "decode_fused_expert_mxfp4" : "decode_fused_expert", stream);
-    if (MT == 1)
-        decode_fused_kernel<1, 2, LAYOUT, SELF, RELU2, MX4><<<nseg_max, DF_THREADS, lds, stream>>>(
-            x, w13, w13s, w2, w2s, sh.w13, sh.w13_scale, sh.w2, sh.w2_scale, plan, ids, E, aff, T,
-            H, I, k, ybuf, ytrash);
+#define MOE_DF_KERNEL(MTV, XL)                                                                       \
+    decode_fused_kernel<MTV, 2, LAYOUT, SELF, RELU2, MX4, XL><<<nseg_max, DF_THREADS, lds, stream>>>( \
+        x, w13, w13s, w2, w2s, sh.w13, sh.w13_scale, sh.w2, sh.w2_scale, plan, ids, E, aff, T, H, I, \
+        k, ybuf, ytrash)
+    if (MX4 && MT == 1 && xlds)
+        MOE_DF_KERNEL(1, MX4);
+    else if (MT == 1)
+        MOE_DF_KERNEL(1, false);
     else
-        decode_fused_kernel<2, 2, LAYOUT, SELF, RELU2, MX4><<<nseg_max, DF_THREADS, lds, stream>>>(
-            x, w13, w13s, w2, w2s, sh.w13, sh.w13_scale, sh.w2, sh.w2_scale, plan, ids, E, aff, T,
-            H, I, k, ybuf, ytrash);
+        MOE_DF_KERNEL(2, false);
+#undef MOE_DF_KERNEL
     prof_end(stream);
     return check_launch("decode_fused_kernel");
 }
