@@ -132,6 +132,49 @@ __device__ __forceinline__ void bfp16x8_encode(f32x4 a, f32x4 b, u32x4& mant, ui
 #pragma unroll
     for (int j = 0; j < 4; ++j) mant[j] = m[2 * j] | (m[2 * j + 1] << 16);
 }
+// The same form for the values ldexp(a_j * sm, se) (an accumulator run, its
+// fp32 unit mantissa sm and power of two se), in about four VALU operations a
+// value.  Let f be the exponent field of fl(max |a_j| * sm): the run's
+// exponent byte is then f + se, and its mantissas rint(a_j * sm * 2^(141 - f))
+// depend on a and sm only.  One FMA forms a_j * c + 1.5 * 2^23 with
+// c = sm * 2^(141 - f): |a_j * c| < 2^15, so the sum is rounded to the nearest
+// integer n (ties to even) in the binade [2^23, 2^24), whose low 16 bits are
+// n as a 16-bit two's complement; a clamp at 1.5 * 2^23 +- 32767 saturates n.
+// (One rounding of the exact product, where bfp16x8_encode of the separately
+// rounded a_j * sm may differ by one unit on a near-tie.)  Runs this cannot
+// hold exactly -- a non-finite or zero largest magnitude, f < 14 (c not a
+// normal float) or an exponent byte outside 1..254 -- take bfp16x8_encode of
+// ldexp(a_j * sm, se).
+__device__ __forceinline__ void bfp16x8_encode_scaled(f32x4 a, f32x4 b, float sm, int se, u32x4& mant,
+                                                      uint32_t& ex) {
+    uint32_t mx = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        mx = max(mx, max(__float_as_uint(a[j]) & 0x7FFFFFFFu, __float_as_uint(b[j]) & 0x7FFFFFFFu));
+    const int f = (int)((__float_as_uint(__uint_as_float(mx) * sm) >> 23) & 0xFFu);
+    const int e = f + se;
+    if (mx < 0x7F800000u && f >= 14 && f <= 254 && e >= 1 && e <= 254) {
+        constexpr float MAGIC = 12582912.0f;  // 1.5 * 2^23
+        const float c = sm * __uint_as_float((uint32_t)(268 - f) << 23);  // sm * 2^(141 - f)
+        uint32_t m[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float y = __builtin_fmaf(j < 4 ? a[j] : b[j - 4], c, MAGIC);
+            m[j] = __float_as_uint(__builtin_amdgcn_fmed3f(y, MAGIC - 32767.0f, MAGIC + 32767.0f));
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) mant[j] = __builtin_amdgcn_perm(m[2 * j + 1], m[2 * j], 0x05040100u);
+        ex = (uint32_t)e;
+    } else {
+        f32x4 va, vb;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            va[j] = ldexpf(a[j] * sm, se);
+            vb[j] = ldexpf(b[j] * sm, se);
+        }
+        bfp16x8_encode(va, vb, mant, ex);
+    }
+}
 // value j of a run: the sign-extended 16-bit mantissa times 2^(ex - 141)
 __device__ __forceinline__ float bfp16_value(u32x4 mant, uint32_t ex, int j) {
     const int m = (int)(int16_t)((mant[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);

@@ -679,8 +679,9 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
         uint8_t* ybytes = reinterpret_cast<uint8_t*>(ybuf);
         const size_t rowb = (size_t)H * 2 + (size_t)(H / 8);
         const int col0 = nb * BN + wn * C::WCOLS;  // first column of the wave tile
-        // the accumulator unit is mcur * 2^eref: the power of two goes in last
-        // (an exact exponent shift unless the product is subnormal)
+        // the accumulator unit is mcur * 2^eref: the slab holds the raw
+        // accumulators and the encoder applies the unit (the power of two
+        // goes into the exponent byte)
         const float sm = mcur[0];
         const int se = eref[0];
 #pragma unroll
@@ -689,7 +690,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
             for (int nt = 0; nt < C::NT; ++nt)
 #pragma unroll
                 for (int i = 0; i < AR; ++i)
-                    slab[(8 * (i >> 2) + 4 * lg + (i & 3)) * 128 + nt * 32 + ln] = ldexpf(acc[mt][nt][i] * sm, se);
+                    slab[(8 * (i >> 2) + 4 * lg + (i & 3)) * 128 + nt * 32 + ln] = acc[mt][nt][i];
             __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the slab is written
             __builtin_amdgcn_wave_barrier();
 #pragma unroll
@@ -702,7 +703,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
                 if (m < rows_here) {
                     u32x4 mant;
                     uint32_t ex;
-                    bfp16x8_encode(v0, v1, mant, ex);
+                    bfp16x8_encode_scaled(v0, v1, sm, se, mant, ex);
                     uint8_t* rowp = ybytes + (size_t)(p0 + m) * rowb;
                     __builtin_nontemporal_store(mant, reinterpret_cast<u32x4*>(rowp + 2 * (size_t)(col0 + c)));
                     __builtin_nontemporal_store((uint8_t)ex, rowp + 2 * (size_t)H + (col0 + c) / 8);
