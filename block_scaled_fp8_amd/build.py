@@ -45,14 +45,17 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-def build_library(verbose: bool = False, jobs: int = 8) -> str:
+def build_library(verbose: bool = False, jobs: int = 8, extra_flags=(), lib_path: str = LIB_PATH,
+                  build_dir: str = BUILD_DIR) -> str:
+    """Compiles every source and links lib_path.  extra_flags go to every
+    compile (e.g. host-only sanitizer flags, each after -Xarch_host)."""
     hipcc = _hipcc()
-    os.makedirs(BUILD_DIR, exist_ok=True)
+    os.makedirs(build_dir, exist_ok=True)
     srcs = sources()
 
     def compile_one(src):
-        obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-        cmd = [hipcc, *HIPCC_FLAGS, "-c", src, "-o", obj]
+        obj = os.path.join(build_dir, os.path.basename(src) + ".o")
+        cmd = [hipcc, *HIPCC_FLAGS, *extra_flags, "-c", src, "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
@@ -62,13 +65,13 @@ def build_library(verbose: bool = False, jobs: int = 8) -> str:
 
     with ThreadPoolExecutor(max_workers=max(1, min(jobs, len(srcs)))) as ex:
         objs = list(ex.map(compile_one, srcs))
-    tmp = LIB_PATH + ".tmp"
+    tmp = lib_path + ".tmp"
     cmd = [hipcc, "-shared", "-fPIC", "--offload-arch=gfx950", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, lib_path)
+    return lib_path
 
 
 if __name__ == "__main__":
