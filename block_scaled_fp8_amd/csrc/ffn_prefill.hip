@@ -296,7 +296,8 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
     // K order inside a 64-wide step (any order works if both operands use it;
     // each lane's 8 K values are one 8-K block kb of the step):
     //   32x32x16: sub-step s (16 K, four per step), lane half lg: kb = 4 lg + s;
-    //   16x16x32: sub-step s (32 K, two per step), lane quarter g: kb = 4 s + g.
+    //   16x16x32: sub-step s (32 K, two per step), lane quarter g: kb = 2 g + s,
+    //   so that one 16-byte weight read serves both sub-steps.
     // An activation piece (16 bytes) is one kb of a row; a weight lane of the
     // staged 1 KB chunk holds kbs 2 (L / 16), 2 (L / 16) + 1 of row L % 16.
     const int l16 = lane & 15, g16 = lane >> 4;
@@ -306,11 +307,11 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
     if constexpr (C::M16) {
         const int row = wm * C::WROWS + l16;
 #pragma unroll
-        for (int s = 0; s < 2; ++s) a_off[s] = row * 128 + (((4 * s + g16) ^ ((row >> 1) & 7)) * 16);
+        for (int s = 0; s < 2; ++s) a_off[s] = row * 128 + (((2 * g16 + s) ^ ((row >> 1) & 7)) * 16);
         a_off[2] = a_off[3] = 0;  // (two sub-steps per step)
-        // 16-column tile nt is 16-row weight tile t16(nt); sub-step s's 8
-        // bytes sit s * 512 bytes further on
-        b_off = C::A_BYTES + t16 * 1024 + ((g16 >> 1) * 16 + l16) * 16 + (g16 & 1) * 8;
+        // 16-column tile nt is 16-row weight tile t16(nt); the lane's 16
+        // bytes (sub-step 0 then 1) are piece g16 of row l16: lane order
+        b_off = C::A_BYTES + t16 * 1024 + lane * 16;
     } else {
         const int row = wm * C::WROWS + ln;
 #pragma unroll
@@ -447,6 +448,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
     using BFrag = std::conditional_t<C::M16, u32x2, u32x4>;
     u32x4 ah[2][C::MT][AP];
     BFrag bh[2][C::NT];
+    u32x2 bz[C::NT];  // 16x16: sub-step 1's weight bytes, read with sub-step 0's
     auto read_half = [&](int stage, int p, u32x4 (&a)[C::MT][AP], BFrag (&b)[C::NT]) {
         const char* st = smem + stage * C::STAGE;
 #pragma unroll
@@ -454,10 +456,22 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
 #pragma unroll
             for (int j = 0; j < AP; ++j)
                 a[mt][j] = *reinterpret_cast<const u32x4*>(st + a_off[AP * p + j] + a_step(mt));
-        if (MTA > 0)
+        if (MTA > 0) {
 #pragma unroll
-            for (int nt = 0; nt < C::NT; ++nt)
-                b[nt] = *reinterpret_cast<const BFrag*>(st + b_off + p * (C::M16 ? 512 : 256) + b_step(nt));
+            for (int nt = 0; nt < C::NT; ++nt) {
+                if constexpr (C::M16) {
+                    if (p == 0) {
+                        const u32x4 w = *reinterpret_cast<const u32x4*>(st + b_off + b_step(nt));
+                        b[nt] = u32x2{w[0], w[1]};
+                        bz[nt] = u32x2{w[2], w[3]};
+                    } else {
+                        b[nt] = bz[nt];
+                    }
+                } else {
+                    b[nt] = *reinterpret_cast<const BFrag*>(st + b_off + p * 256 + b_step(nt));
+                }
+            }
+        }
     };
     // Part j of a half: 32x32 -- sub-step j (16 K) of every tile; 16x16 --
     // the half's 32 K for column tiles j*NT/2 .. (j+1)*NT/2 - 1 (gate/up: j = 0
