@@ -540,7 +540,9 @@ def fused_variant_bench(cfg, dev, L, seed=0, activation="swiglu", variant="auto"
                            "bytes_per_launch": kb, "avg_us": round(kus, 3),
                            "achieved": round(kb / (kus * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBS,
                            "unit": "GB/s",
-                           "frac": round(kb / (kus * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+                           "frac": round(kb / (kus * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                           "traffic": profiled_traffic("decode_fused_expert_mxfp4", cfg.name),
+                           "traffic_unit": "bytes per launch"}
     a8 = [n for n in prof if n.endswith("_a8")]
     if a8:
         # the fp8 x fp8 gate/up (or up) GEMM against the FP8 MFMA peak
