@@ -59,10 +59,12 @@ constexpr int DF_SELF_IDS_PER_THREAD = DF_SELF_MAX_ROUTES / DF_THREADS;
 
 // LDS: the SwiGLU activations [16 MT][I + 8], then (x staged) the pass's
 // token rows of x [16 MT][H + 8], then (self-routed) the expert's routes.
-size_t decode_fused_lds_bytes(int MT, int I, int self_routes, int H) {
-    return sizeof(uint16_t) * (size_t)(16 * MT) * (I + 8) +
-           (H > 0 ? sizeof(uint16_t) * (size_t)(16 * MT) * (H + 8) : 0) +
-           sizeof(int32_t) * (size_t)self_routes;
+// alias: x and the activations share one region (the activations are written
+// once phase 1 has read all of x).
+size_t decode_fused_lds_bytes(int MT, int I, int self_routes, int H, bool alias) {
+    const size_t a = sizeof(uint16_t) * (size_t)(16 * MT) * (I + 8);
+    const size_t xb = H > 0 ? sizeof(uint16_t) * (size_t)(16 * MT) * (H + 8) : 0;
+    return (alias ? std::max(a, xb) : a + xb) + sizeof(int32_t) * (size_t)self_routes;
 }
 
 // The pass's x rows go to LDS (and every wave reads its operands there
@@ -70,6 +72,14 @@ size_t decode_fused_lds_bytes(int MT, int I, int self_routes, int H) {
 // whole number of 1 KB wave loads and everything fits one workgroup's LDS.
 bool decode_fused_x_in_lds(int MT, int H, int I, int self_routes) {
     return H % 512 == 0 && decode_fused_lds_bytes(MT, I, self_routes, H) <= 160 * 1024;
+}
+
+// Phase-1 groups per wave (as the kernel counts them).
+static int decode_fused_groups1(int H, int I, bool relu2, bool mx4) {
+    const int nch1 = H / (mx4 ? 128 : 64);
+    const int G1 = I / (16 * (relu2 ? DF_NT : DF_HALF));
+    int n1 = (G1 + DF_WAVES - 1) / DF_WAVES;
+    return n1 + (nch1 & n1 & 1);
 }
 
 // RELU2: a non-gated expert, w13 = the up projection [I, H] alone; a phase-1
@@ -88,7 +98,10 @@ bool decode_fused_x_in_lds(int MT, int H, int I, int self_routes) {
 //
 // XLDS: the token rows of each pass are staged in LDS once (direct-to-LDS
 // wave loads), and phase 1 reads its activation operands there.
-template <int MT, int DEPTH, int LAYOUT, bool SELF, bool RELU2, bool MX4, bool XLDS>
+// XA (with XLDS; at most two phase-1 groups a wave): x and the activations
+// share LDS.  Phase 1 keeps its SwiGLU results in registers, and they go to
+// LDS once every wave has read the last of x.
+template <int MT, int DEPTH, int LAYOUT, bool SELF, bool RELU2, bool MX4, bool XLDS, bool XA = false>
 __global__ __launch_bounds__(DF_THREADS) void decode_fused_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ w13,
     const void* __restrict__ w13s, const uint8_t* __restrict__ w2,
@@ -100,16 +113,19 @@ __global__ __launch_bounds__(DF_THREADS) void decode_fused_kernel(
     // two 64-wide chunks per 128-wide scale block, two in flight: the chunk
     // in flight slot d is the block's first (d = 0) or second (d = 1) half
     static_assert(DEPTH == 2, "chunks per 128-wide scale block");
+    static_assert(!XA || XLDS, "the shared region holds staged x rows");
     constexpr int MROWS = 16 * MT, NT = DF_NT, HALF = DF_HALF;
     constexpr int CS = chunk_stride<LAYOUT>();
     extern __shared__ uint16_t a_lds[];  // [MROWS][I + 8] bf16 SwiGLU activations
     const int astride = I + 8;  // +16 bytes per row: conflict-free 16-byte column reads
     const int xstride = H + 8;  // (XLDS) x rows, padded likewise
-    uint16_t* x_lds = a_lds + (size_t)MROWS * astride;
+    uint16_t* x_lds = XA ? a_lds : a_lds + (size_t)MROWS * astride;
+    const size_t region = XA ? (size_t)MROWS * (size_t)max(astride, xstride)
+                             : (size_t)MROWS * astride + (XLDS ? (size_t)MROWS * xstride : 0);
     const int lane = lane_id(), wave = wave_id();
     const int R = T * k;
     int e, row0, rows;
-    int32_t* rlist = reinterpret_cast<int32_t*>(x_lds + (XLDS ? (size_t)MROWS * xstride : 0));  // SELF: routes of e
+    int32_t* rlist = reinterpret_cast<int32_t*>(a_lds + region);  // SELF: routes of e
     if (SELF) {
         const int b = blockIdx.x;
         if (b > E || (b == E && sh_w13 == nullptr)) return;
@@ -203,6 +219,10 @@ __global__ __launch_bounds__(DF_THREADS) void decode_fused_kernel(
         u32x4 aq[DEPTH][MT][NS];
         f32x4 acc[MT][NT];  // partial sums of the current 128-wide K block
         f32x4 tot[MT][NT];  // scaled totals of the finished blocks
+        // XA: the bf16 activations of the wave's first and second phase-1
+        // groups, two a register, until x has been read
+        constexpr int JN = RELU2 ? NT : HALF;
+        uint32_t hold0[MT][JN][2], hold1[MT][JN][2];
         float sc0 = 0.0f, sc1 = 0.0f;  // scales of the current block (phase 1: gate, up; phase 2: sc0)
         auto reset = [&]() {
 #pragma unroll
@@ -221,9 +241,14 @@ __global__ __launch_bounds__(DF_THREADS) void decode_fused_kernel(
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) tot[mt][j] += sc * acc[mt][j];
         };
-        auto mfma_chunk = [&](int d, const u32x4 (&av)[MT][NS]) {
+        // av(mt, s): the activation operand of row tile mt, sub-step s (read
+        // at its sub-step, so only one sub-step's pieces are live at a time)
+        auto mfma_chunk = [&](int d, auto&& av) {
 #pragma unroll
-            for (int s = 0; s < NS; ++s)
+            for (int s = 0; s < NS; ++s) {
+                u32x4 a[MT];
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) a[mt] = av(mt, s);
 #pragma unroll
                 for (int j = 0; j < NT; ++j) {
                     bf16x8 b;
@@ -235,10 +260,14 @@ __global__ __launch_bounds__(DF_THREADS) void decode_fused_kernel(
 #pragma unroll
                     for (int mt = 0; mt < MT; ++mt)
                         acc[mt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            as_bf16x8(av[mt][s]), b,
+                            as_bf16x8(a[mt]), b,
                             !MX4 && d == 0 && s == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[mt][j],
                             0, 0, 0);
                 }
+                // (MX4: keeps the scheduler from hoisting every sub-step's
+                // operand reads, which spilled the 32-row passes)
+                if constexpr (MX4) __builtin_amdgcn_sched_barrier(0);
+            }
         };
 
         // ---- issue side: phase-1 group g has gate tiles g*HALF+j and up tiles
@@ -305,15 +334,13 @@ __global__ __launch_bounds__(DF_THREADS) void decode_fused_kernel(
                     sc1 = S13[ui];
                 }
             }
-            u32x4 av[MT][NS];
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                const u32x4* q = reinterpret_cast<const u32x4*>(x_lds + xoff[mt] + pc * KC);
-#pragma unroll
-                for (int s = 0; s < NS; ++s)
-                    av[mt][s] = !xvalid[mt] ? u32x4{0u, 0u, 0u, 0u} : XLDS ? q[s] : aq[d][mt][s];
-            }
-            mfma_chunk(d, av);
+            mfma_chunk(d, [&](int mt, int s) -> u32x4 {
+                if (!xvalid[mt]) return u32x4{0u, 0u, 0u, 0u};
+                if constexpr (XLDS)
+                    return reinterpret_cast<const u32x4*>(x_lds + xoff[mt] + pc * KC)[s];
+                else
+                    return aq[d][mt][s];
+            });
             if (!MX4 && d == 1) {  // the block's second chunk: fold it
                 if (RELU2) {
                     fold(sc0, 0, NT);
@@ -324,29 +351,33 @@ __global__ __launch_bounds__(DF_THREADS) void decode_fused_kernel(
             }
             if (pc == nch1 - 1) {  // group done: activations into LDS (padding columns if spare)
                 const bool real = pg < G1;
-                if (RELU2) {
+                // activation (mt, j, i) of the group, as bf16 bits
+                auto act = [&](int mt, int j, int i) -> uint32_t {
+                    return RELU2 ? f32_to_bf16_bits(relu2(res(mt, j, i)))
+                                 : f32_to_bf16_bits(swiglu(res(mt, j, i), res(mt, HALF + j, i)));
+                };
+                if constexpr (XA) {
+                    const bool first = pg < DF_WAVES;  // (the wave's groups are wave, wave + 8)
 #pragma unroll
                     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                        for (int j = 0; j < NT; ++j)
+                        for (int j = 0; j < JN; ++j)
 #pragma unroll
-                            for (int i = 0; i < 4; ++i) {
-                                const int m = mt * 16 + lg * 4 + i;
-                                const int col = real ? (g * NT + j) * 16 + ln : I + (ln & 7);
-                                a_lds[m * astride + col] = f32_to_bf16_bits(relu2(res(mt, j, i)));
+                            for (int h = 0; h < 2; ++h) {
+                                const uint32_t v = act(mt, j, 2 * h) | (act(mt, j, 2 * h + 1) << 16);
+                                if (first) hold0[mt][j][h] = v;
+                                else hold1[mt][j][h] = v;
                             }
                 } else {
 #pragma unroll
                     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                        for (int j = 0; j < HALF; ++j)
+                        for (int j = 0; j < JN; ++j)
 #pragma unroll
                             for (int i = 0; i < 4; ++i) {
-                                const float gv = res(mt, j, i);
-                                const float uv = res(mt, HALF + j, i);
                                 const int m = mt * 16 + lg * 4 + i;
-                                const int col = real ? (g * HALF + j) * 16 + ln : I + (ln & 7);
-                                a_lds[m * astride + col] = f32_to_bf16_bits(swiglu(gv, uv));
+                                const int col = real ? (g * JN + j) * 16 + ln : I + (ln & 7);
+                                a_lds[m * astride + col] = (uint16_t)act(mt, j, i);
                             }
                 }
                 reset();
@@ -362,14 +393,9 @@ __global__ __launch_bounds__(DF_THREADS) void decode_fused_kernel(
                 const int si = __builtin_amdgcn_readfirstlane(((g * NT * 16) >> 7) * kb2 + (pc >> 1));
                 sc0 = S2[si];
             }
-            u32x4 av[MT][NS];
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                const u32x4* q = reinterpret_cast<const u32x4*>(a_lds + aoff[mt] + pc * KC);
-#pragma unroll
-                for (int s = 0; s < NS; ++s) av[mt][s] = q[s];
-            }
-            mfma_chunk(d, av);
+            mfma_chunk(d, [&](int mt, int s) -> u32x4 {
+                return reinterpret_cast<const u32x4*>(a_lds + aoff[mt] + pc * KC)[s];
+            });
             if (!MX4 && d == 1) fold(sc0, 0, NT);
             if (pc == nch2 - 1) {  // group done: fp32 rows of the routes (trash if spare)
                 const bool real = pg < G2;
@@ -459,6 +485,27 @@ __global__ __launch_bounds__(DF_THREADS) void decode_fused_kernel(
             proc1(d);
             issue2(d);
         }
+        if constexpr (XA) {
+            __syncthreads();  // every wave has read the last of x: its region takes the activations
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const int pgh = wave + hh * DF_WAVES;
+                if (pgh >= n1 * DF_WAVES) break;  // (uniform) the wave's groups
+                const int g = pgh % G1;
+                const bool real = pgh < G1;
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int j = 0; j < JN; ++j)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const uint32_t v = (hh == 0 ? hold0 : hold1)[mt][j][i >> 1];
+                            const int m = mt * 16 + lg * 4 + i;
+                            const int col = real ? (g * JN + j) * 16 + ln : I + (ln & 7);
+                            a_lds[m * astride + col] = (uint16_t)((i & 1) ? v >> 16 : v & 0xFFFFu);
+                        }
+            }
+        }
         __syncthreads();  // every activation column is in LDS
         pg = wave;
         pc = 0;
@@ -486,20 +533,30 @@ static int launch_decode_fused_l(int MT, const uint16_t* x, const uint8_t* w13, 
     // while the E4M3FN stream went from 115.9 to 117.8 us, so it keeps its
     // operand loads from L2)
     const bool xlds = MX4 && MT == 1 && decode_fused_x_in_lds(MT, H, I, routes);
-    const size_t lds = decode_fused_lds_bytes(MT, I, routes, xlds ? H : 0);
+    // (32-row SwiGLU passes: x and the activations share LDS when a row is
+    // whole 1 KB wave loads, a wave holds at most two phase-1 groups and it
+    // fits.  Each chunk's x operand is then read from LDS instead of L2:
+    // measured on decode512, MXFP4 124.6 -> 100.8 us, E4M3FN 154.6 -> 151.8 us.
+    // relu^2 keeps four tiles a group in registers and spills too much.)
+    const bool xa = !xlds && !RELU2 && MT == 2 && H % 512 == 0 &&
+                    decode_fused_groups1(H, I, RELU2, MX4) <= 2 &&
+                    decode_fused_lds_bytes(MT, I, routes, H, true) <= 160 * 1024;
+    const size_t lds = decode_fused_lds_bytes(MT, I, routes, (xlds || xa) ? H : 0, xa);
     // the trash row sits right after the last real row of y
     const int ytrash = T * k + (sh.w13 ? T : 0);
     prof_begin(MX4 ? "decode_fused_expert_mxfp4" : "decode_fused_expert", stream);
-#define MOE_DF_KERNEL(MTV, XL)                                                                       \
-    decode_fused_kernel<MTV, 2, LAYOUT, SELF, RELU2, MX4, XL><<<nseg_max, DF_THREADS, lds, stream>>>( \
-        x, w13, w13s, w2, w2s, sh.w13, sh.w13_scale, sh.w2, sh.w2_scale, plan, ids, E, aff, T, H, I, \
+#define MOE_DF_KERNEL(MTV, XL, XAV)                                                                       \
+    decode_fused_kernel<MTV, 2, LAYOUT, SELF, RELU2, MX4, XL, XAV><<<nseg_max, DF_THREADS, lds, stream>>>( \
+        x, w13, w13s, w2, w2s, sh.w13, sh.w13_scale, sh.w2, sh.w2_scale, plan, ids, E, aff, T, H, I,      \
         k, ybuf, ytrash)
     if (MX4 && MT == 1 && xlds)
-        MOE_DF_KERNEL(1, MX4);
+        MOE_DF_KERNEL(1, MX4, false);
     else if (MT == 1)
-        MOE_DF_KERNEL(1, false);
+        MOE_DF_KERNEL(1, false, false);
+    else if (xa)
+        MOE_DF_KERNEL(2, true, true);
     else
-        MOE_DF_KERNEL(2, false);
+        MOE_DF_KERNEL(2, false, false);
 #undef MOE_DF_KERNEL
     prof_end(stream);
     return check_launch("decode_fused_kernel");

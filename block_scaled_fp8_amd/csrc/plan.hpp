@@ -106,7 +106,7 @@ int launch_combine(const float* ybuf, const int32_t* ids, const int32_t* inv_rou
 // scans the ids for its expert; at most decode_self_routed_max_routes() routes).
 int decode_mt(int T, int k, int E);
 bool decode_fused_fits(int T, int k, int E, int H, int I, int has_shared, bool self_routed);
-size_t decode_fused_lds_bytes(int MT, int I, int self_routes, int H = 0);
+size_t decode_fused_lds_bytes(int MT, int I, int self_routes, int H = 0, bool alias = false);
 bool decode_fused_x_in_lds(int MT, int H, int I, int self_routes);
 int decode_self_routed_max_routes();
 int launch_decode_fused_self(int layout, int MT, const uint16_t* x, const uint8_t* w13,
