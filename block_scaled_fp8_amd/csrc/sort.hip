@@ -24,6 +24,7 @@ constexpr int SORT_SMALL_MAX_ROUTES = 4096;  // measured: one workgroup is as fa
 constexpr int SORT_CHUNK = 1024;              // routes per workgroup, multi-workgroup path (measured at
                                               // R = 65536: 2048 -> 18.3 us, 1024 -> 13.7, 512 -> 15.6)
 constexpr int SORT_THREADS = 256;
+constexpr int SORT_SCAN_MIN_CHUNKS = 128;  // from this many chunks on, sort_scan runs first
 
 // Exclusive scan of arr[0..n) held in LDS, in place; returns the total.
 // Every thread of the block must call it.  tmp holds NT/64 + 1 ints.
@@ -151,16 +152,16 @@ __device__ void build_segments(const int* cnt, const int* off, int E, int R, int
         // ordered tile list: full tiles first (segment s's at fulls[s] ..),
         // then the partial ones (segment s's at nfull + #partials before s,
         // which is tiles[s] - fulls[s] with both as exclusive prefixes)
-        constexpr int NW = NT / MOE_WAVE;
-        const int w = tid / MOE_WAVE, lane = lane_id();
-        for (int s = w; s < nseg; s += NW) {
+        // (one thread per segment: most segments hold a few tiles, and a wave
+        // per segment made this block the sort's longest)
+        for (int s = tid; s < nseg; s += NT) {
             const int e = segx[s];
             const int row0 = e >= 0 ? off[e] : R, rows = e >= 0 ? cnt[e] : T;
             const int f0 = fulls[s], f1 = s + 1 < nseg ? fulls[s + 1] : nfull;
             const int t0 = tiles[s], t1 = s + 1 < nseg ? tiles[s + 1] : ntiles;
-            for (int j = lane; j < f1 - f0; j += MOE_WAVE)
+            for (int j = 0; j < f1 - f0; ++j)
                 plan.tile_info[f0 + j] = make_int4(e, row0 + j * tile_m, tile_m, 0);
-            if (lane == 0 && t1 - t0 > f1 - f0) {
+            if (t1 - t0 > f1 - f0) {
                 const int done = (f1 - f0) * tile_m;
                 plan.tile_info[nfull + (t0 - f0)] = make_int4(e, row0 + done, rows - done, 0);
             }
@@ -239,16 +240,38 @@ __global__ __launch_bounds__(SORT_THREADS) void sort_count_kernel(
     for (int e = tid; e < E; e += SORT_THREADS) ghist[(size_t)e * nb + blockIdx.x] = hist[e];
 }
 
+// One wave per expert e: the row ghist[e][0 .. nb) of per-chunk counts
+// becomes its exclusive prefix over the chunks (in place: the routes of
+// expert e in earlier chunks), and totals[e] the expert's count.
+__global__ __launch_bounds__(SORT_THREADS) void sort_scan_kernel(int32_t* __restrict__ ghist, int E,
+                                                                 int nb, int32_t* __restrict__ totals) {
+    constexpr int NW = SORT_THREADS / MOE_WAVE;
+    const int lane = lane_id();
+    const int e = blockIdx.x * NW + wave_id();
+    if (e >= E) return;
+    int32_t* row = ghist + (size_t)e * nb;
+    int carry = 0;
+    for (int j0 = 0; j0 < nb; j0 += MOE_WAVE) {
+        const int j = j0 + lane;
+        const int v = j < nb ? row[j] : 0;
+        const int incl = wave_incl_scan_i32(v);
+        if (j < nb) row[j] = carry + incl - v;
+        carry += __builtin_amdgcn_readlane(incl, MOE_WAVE - 1);
+    }
+    if (lane == 0) totals[e] = carry;
+}
+
 // Blocks 0 .. nb-1 place the routes of their chunk; block nb writes the
-// counts, offsets, tail fill and the segment list.  Every block derives what
-// it needs from the per-(expert, block) counts ghist[e][b] of sort_count:
-// expert e's total, its exclusive start over experts (offsets) and, for a
-// placement block b, the routes of expert e in earlier chunks.  (The table is
-// E x nb ints, read by every block; this replaces a separate one-workgroup
-// scan kernel and its launch.)
+// counts, offsets, tail fill and the segment list.  Every block needs the
+// expert totals (and derives the offsets, their exclusive scan) and, for
+// placement block b, the routes of each expert in earlier chunks: with
+// `totals`, from sort_scan's results (one column of the table); without, by
+// summing the rows of the count table itself (cheaper than a third launch
+// while the table is short).
 __global__ __launch_bounds__(SORT_THREADS) void sort_place_kernel(
     const int32_t* __restrict__ ids, int T, int k, int E, int nb,
-    const int32_t* __restrict__ ghist, Plan plan, int want_segments, int has_shared, int tile_m) {
+    const int32_t* __restrict__ ghist, const int32_t* __restrict__ totals, Plan plan,
+    int want_segments, int has_shared, int tile_m) {
     constexpr int NT = SORT_THREADS, NW = NT / MOE_WAVE;
     constexpr int SUB = SORT_CHUNK / NW;
     extern __shared__ int lds[];
@@ -264,13 +287,18 @@ __global__ __launch_bounds__(SORT_THREADS) void sort_place_kernel(
     const int R = T * k, tid = threadIdx.x, w = tid / MOE_WAVE, lane = lane_id();
     const int b = blockIdx.x;
     for (int e = tid; e < E; e += NT) {
-        const int32_t* row = ghist + (size_t)e * nb;
         int tot = 0, before = 0;
+        if (totals) {
+            tot = totals[e];
+            before = b < nb ? ghist[(size_t)e * nb + b] : 0;
+        } else {
+            const int32_t* row = ghist + (size_t)e * nb;
 #pragma unroll 8
-        for (int j = 0; j < nb; ++j) {
-            const int v = row[j];
-            before += j < b ? v : 0;
-            tot += v;
+            for (int j = 0; j < nb; ++j) {
+                const int v = row[j];
+                before += j < b ? v : 0;
+                tot += v;
+            }
         }
         cnt[e] = tot;
         off[e] = tot;
@@ -313,10 +341,11 @@ __global__ __launch_bounds__(SORT_THREADS) void sort_place_kernel(
     wave_place(ids, r0, r1, E, whist + w * E, plan.sorted_route, plan.inv_route);
 }
 
+// The per-(expert, chunk) count table, then the expert totals.
 size_t sort_scratch_bytes(int R, int E) {
     if (R <= SORT_SMALL_MAX_ROUTES) return 0;
     const size_t nb = (size_t)(R + SORT_CHUNK - 1) / SORT_CHUNK;
-    return halign(nb * (size_t)E * sizeof(int32_t));
+    return halign(nb * (size_t)E * sizeof(int32_t)) + halign((size_t)E * sizeof(int32_t));
 }
 
 int launch_sort(const int32_t* ids, int T, int k, int E, const Plan& plan, int has_shared,
@@ -334,14 +363,26 @@ int launch_sort(const int32_t* ids, int T, int k, int E, const Plan& plan, int h
     }
     const int nb = (R + SORT_CHUNK - 1) / SORT_CHUNK;
     int32_t* ghist = static_cast<int32_t*>(scratch);
+    int32_t* totals = reinterpret_cast<int32_t*>(static_cast<char*>(scratch) +
+                                                 halign((size_t)nb * E * sizeof(int32_t)));
     prof_begin("sort_count", stream);
     sort_count_kernel<<<nb, SORT_THREADS, sizeof(int) * E, stream>>>(ids, R, E, nb, ghist, status);
     prof_end(stream);
     if (int rc = check_launch("sort_count_kernel")) return rc;
     constexpr int NW = SORT_THREADS / MOE_WAVE;
+    // (measured: at 64 chunks the scan's launch costs more than the sums it
+    // saves; at 160 chunks the placement went from 50 to 16 us with it)
+    if (nb >= SORT_SCAN_MIN_CHUNKS) {
+        prof_begin("sort_scan", stream);
+        sort_scan_kernel<<<(E + NW - 1) / NW, SORT_THREADS, 0, stream>>>(ghist, E, nb, totals);
+        prof_end(stream);
+        if (int rc = check_launch("sort_scan_kernel")) return rc;
+    } else {
+        totals = nullptr;
+    }
     const size_t lds = sizeof(int) * ((size_t)NW * E + E + (E + 1) + E + 4 * (E + 2) + NW + 1);
     prof_begin("sort_place", stream);
-    sort_place_kernel<<<nb + 1, SORT_THREADS, lds, stream>>>(ids, T, k, E, nb, ghist, plan,
+    sort_place_kernel<<<nb + 1, SORT_THREADS, lds, stream>>>(ids, T, k, E, nb, ghist, totals, plan,
                                                              want_segments, has_shared, tile_m);
     prof_end(stream);
     return check_launch("sort_place_kernel");
