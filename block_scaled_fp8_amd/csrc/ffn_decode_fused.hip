@@ -56,6 +56,9 @@ constexpr int DF_HALF = DF_NT / 2;
 // no separate sort launch.  Workgroup E is the shared expert.
 constexpr int DF_SELF_MAX_ROUTES = 4096;
 constexpr int DF_SELF_IDS_PER_THREAD = DF_SELF_MAX_ROUTES / DF_THREADS;
+// dynamic LDS a workgroup may take: 160 KB less room for the kernel's static
+// arrays (the route scan's per-round wave counts)
+constexpr size_t DF_LDS_DYNAMIC_MAX = 160 * 1024 - 1024;
 
 // LDS: the SwiGLU activations [16 MT][I + 8], then (x staged) the pass's
 // token rows of x [16 MT][H + 8], then (self-routed) the expert's routes.
@@ -71,7 +74,7 @@ size_t decode_fused_lds_bytes(int MT, int I, int self_routes, int H, bool alias)
 // instead of re-reading them from L2 for each weight chunk) when a row is a
 // whole number of 1 KB wave loads and everything fits one workgroup's LDS.
 bool decode_fused_x_in_lds(int MT, int H, int I, int self_routes) {
-    return H % 512 == 0 && decode_fused_lds_bytes(MT, I, self_routes, H) <= 160 * 1024;
+    return H % 512 == 0 && decode_fused_lds_bytes(MT, I, self_routes, H) <= DF_LDS_DYNAMIC_MAX;
 }
 
 // Phase-1 groups per wave (as the kernel counts them).
@@ -133,32 +136,40 @@ __global__ __launch_bounds__(DF_THREADS) void decode_fused_kernel(
         row0 = 0;
         rows = T;
         if (e >= 0) {
-            __shared__ int wcnt[DF_WAVES];
+            // every round's per-wave counts first (one barrier), then the
+            // positions: round c, wave w's hits follow all earlier rounds'
+            // and round c's earlier waves'
+            __shared__ int wcnt[DF_SELF_IDS_PER_THREAD][DF_WAVES];
             int idv[DF_SELF_IDS_PER_THREAD];
+            uint64_t hm[DF_SELF_IDS_PER_THREAD];
 #pragma unroll
             for (int c = 0; c < DF_SELF_IDS_PER_THREAD; ++c) {
                 const int r = c * DF_THREADS + (int)threadIdx.x;
                 idv[c] = r < R ? ids[r] : -1;
             }
+#pragma unroll
+            for (int c = 0; c < DF_SELF_IDS_PER_THREAD; ++c) {
+                if (c * DF_THREADS >= R) break;  // uniform
+                hm[c] = __ballot(idv[c] == e);
+                if (lane == 0) wcnt[c][wave] = (int)__popcll(hm[c]);
+            }
+            __syncthreads();
             int base = 0;
 #pragma unroll
             for (int c = 0; c < DF_SELF_IDS_PER_THREAD; ++c) {
                 if (c * DF_THREADS >= R) break;  // uniform
-                const bool hit = idv[c] == e;
-                const uint64_t m = __ballot(hit);
-                if (lane == 0) wcnt[wave] = (int)__popcll(m);
-                __syncthreads();
                 int woff = 0, tot = 0;
 #pragma unroll
                 for (int w = 0; w < DF_WAVES; ++w) {
-                    const int cw = wcnt[w];
+                    const int cw = wcnt[c][w];
                     woff += w < wave ? cw : 0;
                     tot += cw;
                 }
-                if (hit) rlist[base + woff + (int)__popcll(m & lanemask_lt())] = c * DF_THREADS + (int)threadIdx.x;
+                if (idv[c] == e)
+                    rlist[base + woff + (int)__popcll(hm[c] & lanemask_lt())] = c * DF_THREADS + (int)threadIdx.x;
                 base += tot;
-                __syncthreads();  // wcnt is rewritten next round; rlist complete after the last
             }
+            __syncthreads();  // rlist complete
             rows = base;
             if (rows == 0) return;  // the same value in every thread
         }
@@ -540,7 +551,7 @@ static int launch_decode_fused_l(int MT, const uint16_t* x, const uint8_t* w13, 
     // relu^2 keeps four tiles a group in registers and spills too much.)
     const bool xa = !xlds && !RELU2 && MT == 2 && H % 512 == 0 &&
                     decode_fused_groups1(H, I, RELU2, MX4) <= 2 &&
-                    decode_fused_lds_bytes(MT, I, routes, H, true) <= 160 * 1024;
+                    decode_fused_lds_bytes(MT, I, routes, H, true) <= DF_LDS_DYNAMIC_MAX;
     const size_t lds = decode_fused_lds_bytes(MT, I, routes, (xlds || xa) ? H : 0, xa);
     // the trash row sits right after the last real row of y
     const int ytrash = T * k + (sh.w13 ? T : 0);
