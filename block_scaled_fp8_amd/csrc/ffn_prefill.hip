@@ -110,17 +110,23 @@ struct PfCfg {
 using PfGateUp = PfCfg<128, 256, 2, 2, 2, 2, 1>;
 using PfDown = PfCfg<128, 256, 2, 2, 2, 2, 0>;
 using PfGateUpA8 = PfCfg<128, 256, 2, 2, 3, 2, 0, 1>;
+// relu^2 up projections whose I is an odd multiple of 128: 128-column tiles
+// of two waves (the 256-column tile would run past the matrix)
+using PfUpNarrow = PfCfg<128, 128, 2, 1, 2, 2, 1>;
+using PfUpNarrowA8 = PfCfg<128, 128, 2, 1, 3, 2, 0, 1>;
 constexpr int PF_BM = 128;
 
 int prefill_tile_m() { return PF_BM; }
 
 // Widths the grouped GEMMs tile exactly (K % 128 holds for every valid call);
 // the per-tile scale table (2 rows of K / 128 floats, padded to 64) must fit
-// in LDS beside the stages, which holds for K <= 65536.
-// relu^2 experts tile their I up columns in 256-wide blocks.
+// in LDS beside the stages, which holds for K <= 65536.  Down tiles H in
+// 256-column blocks; relu^2 experts tile their I up columns in 256-column
+// blocks, or 128-column ones when I is an odd multiple of 128.
 int prefill_supported(int H, int I, int act) {
     const int ncols = act == ACT_RELU2 ? I : 2 * I;
-    return H % 256 == 0 && ncols % 256 == 0 && H <= 65536 && I <= 65536;
+    return H % 256 == 0 && ncols % 128 == 0 && (act == ACT_RELU2 || ncols % 256 == 0) && H <= 65536 &&
+           I <= 65536;
 }
 
 // PF_GATEUP: gate and up columns side by side, SwiGLU epilogue into abuf;
@@ -823,22 +829,29 @@ static int launch_prefill_c(const uint16_t* x, const uint8_t* w13, const float* 
                             hipStream_t stream) {
     const int hs = sh.w13 != nullptr;
     int rc;
+    const float* ss = static_cast<const float*>(sh.w13_scale);
+    const bool narrow = act == ACT_RELU2 && I % 256 != 0;  // (I % 128 == 0)
     if (xq) {  // E4M3 activations with per-token scales: the fp8 x fp8 MFMA
         const uint16_t* xa = reinterpret_cast<const uint16_t*>(xq);
-        rc = act == ACT_RELU2
-                 ? launch_pf<PF_UP, LAYOUT, PfGateUpA8>(xa, nullptr, w13, w13s, sh.w13,
-                                                        static_cast<const float*>(sh.w13_scale), plan, T, H, I, E, k, hs,
-                                                        abuf, ybuf, stream, xs)
-                 : launch_pf<PF_GATEUP, LAYOUT, PfGateUpA8>(xa, nullptr, w13, w13s, sh.w13,
-                                                            static_cast<const float*>(sh.w13_scale), plan, T, H, I, E, k, hs,
-                                                            abuf, ybuf, stream, xs);
+        if (act != ACT_RELU2)
+            rc = launch_pf<PF_GATEUP, LAYOUT, PfGateUpA8>(xa, nullptr, w13, w13s, sh.w13, ss, plan, T, H, I,
+                                                          E, k, hs, abuf, ybuf, stream, xs);
+        else if (narrow)
+            rc = launch_pf<PF_UP, LAYOUT, PfUpNarrowA8>(xa, nullptr, w13, w13s, sh.w13, ss, plan, T, H, I, E,
+                                                        k, hs, abuf, ybuf, stream, xs);
+        else
+            rc = launch_pf<PF_UP, LAYOUT, PfGateUpA8>(xa, nullptr, w13, w13s, sh.w13, ss, plan, T, H, I, E, k,
+                                                      hs, abuf, ybuf, stream, xs);
     } else {
-        rc = act == ACT_RELU2
-                 ? launch_pf<PF_UP, LAYOUT, PfGateUp>(x, nullptr, w13, w13s, sh.w13, static_cast<const float*>(sh.w13_scale),
-                                                      plan, T, H, I, E, k, hs, abuf, ybuf, stream)
-                 : launch_pf<PF_GATEUP, LAYOUT, PfGateUp>(x, nullptr, w13, w13s, sh.w13,
-                                                          static_cast<const float*>(sh.w13_scale), plan, T, H, I, E, k, hs,
-                                                          abuf, ybuf, stream);
+        if (act != ACT_RELU2)
+            rc = launch_pf<PF_GATEUP, LAYOUT, PfGateUp>(x, nullptr, w13, w13s, sh.w13, ss, plan, T, H, I, E, k,
+                                                        hs, abuf, ybuf, stream);
+        else if (narrow)
+            rc = launch_pf<PF_UP, LAYOUT, PfUpNarrow>(x, nullptr, w13, w13s, sh.w13, ss, plan, T, H, I, E, k,
+                                                      hs, abuf, ybuf, stream);
+        else
+            rc = launch_pf<PF_UP, LAYOUT, PfGateUp>(x, nullptr, w13, w13s, sh.w13, ss, plan, T, H, I, E, k, hs,
+                                                    abuf, ybuf, stream);
     }
     if (rc == MOE_OK)
         rc = launch_pf<PF_DOWN, LAYOUT, PfDown>(x, abuf, w2, w2s, sh.w2, static_cast<const float*>(sh.w2_scale), plan, T, H, I,
@@ -849,8 +862,8 @@ static int launch_prefill_c(const uint16_t* x, const uint8_t* w13, const float* 
 // Host-side checks of a prefill call, before anything is launched.
 int prefill_check(int T, int H, int I, int E, int k, int has_shared, int act) {
     if (!prefill_supported(H, I, act)) {
-        set_error("prefill variant needs H %% 256 == 0, %s %% 256 == 0 and H, I <= 65536 (got H=%d, I=%d)",
-                  act == ACT_RELU2 ? "I" : "2I", H, I);
+        set_error("prefill variant needs H %% 256 == 0, %s and H, I <= 65536 (got H=%d, I=%d)",
+                  act == ACT_RELU2 ? "I % 128 == 0" : "2I % 256 == 0", H, I);
         return MOE_EUNSUPPORTED;
     }
     const long R = (long)T * k, rows = R + (has_shared ? T : 0);
@@ -859,7 +872,7 @@ int prefill_check(int T, int H, int I, int E, int k, int has_shared, int act) {
         return MOE_EUNSUPPORTED;
     }
     const long tiles = (R + PF_BM - 1) / PF_BM + E + (has_shared ? (T + PF_BM - 1) / PF_BM : 0);
-    const long nblk = std::max(2L * I, (long)H) / 256;
+    const long nblk = std::max(std::max(2L * I, (long)H) / 256, (long)I / 128);
     if (8L * nblk * PF_XCD_RUN * ((tiles + 8 * PF_XCD_RUN - 1) / (8 * PF_XCD_RUN)) > 0x7FFFFFFFL) {
         set_error("prefill: too many tiles");
         return MOE_EUNSUPPORTED;
@@ -872,8 +885,8 @@ int launch_prefill_ffn(int layout, const uint16_t* x, const uint8_t* w13, const 
                        int T, int H, int I, int E, int k, uint16_t* abuf, float* ybuf,
                        int act, const uint8_t* xq, const float* xs, hipStream_t stream) {
     if (!prefill_supported(H, I, act)) {
-        set_error("prefill variant needs H %% 256 == 0, %s %% 256 == 0 and H, I <= 65536 (got H=%d, I=%d)",
-                  act == ACT_RELU2 ? "I" : "2I", H, I);
+        set_error("prefill variant needs H %% 256 == 0, %s and H, I <= 65536 (got H=%d, I=%d)",
+                  act == ACT_RELU2 ? "I % 128 == 0" : "2I % 256 == 0", H, I);
         return MOE_EUNSUPPORTED;
     }
     if (!plan.tile_info || !plan.tile_n || !plan.sorted_route) {

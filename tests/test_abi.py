@@ -122,11 +122,12 @@ def test_fused_activation_checks():
     base = (f, f, f, f, f, f, f, 64, 2048, 512, 256, 8, None, o, None, f, ws, 0)
     assert lib.moe_fused_w8a16_ex(*base, 0, 2, None) == binding.MOE_EINVAL
     assert b"activation" in lib.moe_last_error()
-    # relu^2 prefill tiles take 256 up columns: I = 384 is rejected before any launch
-    ws384 = lib.moe_fused_workspace_bytes(8192, 2048, 384, 256, 8, 0, 2)
-    args = (f, f, f, f, f, f, f, 8192, 2048, 384, 256, 8, None, o, None, f, ws384, 0, 2)
+    # prefill down tiles take 256 output columns: relu^2 with H = 384 is
+    # rejected before any launch
+    ws384 = lib.moe_fused_workspace_bytes(8192, 384, 512, 256, 8, 0, 2)
+    args = (f, f, f, f, f, f, f, 8192, 384, 512, 256, 8, None, o, None, f, ws384, 0, 2)
     assert lib.moe_fused_w8a16_ex(*args, 1, None) == binding.MOE_EUNSUPPORTED
-    assert b"I % 256" in lib.moe_last_error()
+    assert b"H % 256" in lib.moe_last_error()
 
 
 def test_quant_e4m3_rows_argument_checks():

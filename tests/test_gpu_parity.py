@@ -408,12 +408,7 @@ def test_fused_relu2_parity(name, variant, layout):
     c = _case(name, "relu2")
     cfg = c["cfg"]
     ids, aff = binding.route(c["logits"], cfg.k)
-    if variant == "prefill" and cfg.I % 256:
-        # the prefill tiles take 256 up columns at a time
-        with pytest.raises(binding.MoeError) as ei:
-            _fused(c, ids, aff, variant=variant, layout=layout, activation="relu2")
-        assert ei.value.code == binding.MOE_EUNSUPPORTED
-        return
+    # (an I that is an odd multiple of 128 runs the prefill's 128-column up tiles)
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
     out = _fused(c, ids, aff, variant=variant, status=status, layout=layout, activation="relu2")
     torch.cuda.synchronize()
@@ -724,15 +719,30 @@ def test_fused_prefill_a8_shortest_k(layout):
     assert_out_close(np_(out), ref, what=f"a8 H=256/{layout}")
 
 
+@pytest.mark.parametrize("layout", ["rowmajor", "tiled"])
+@pytest.mark.parametrize("variant", ["prefill", "prefill_a8"])
+def test_fused_relu2_prefill_odd_column_blocks(variant, layout):
+    """relu^2 up projections with I an odd multiple of 128 (three 128-column
+    blocks here) through the prefill GEMMs, with full and partial row tiles
+    and the shared expert: every row against the oracle."""
+    cfg = synth.MoeConfig("r384", T=300, H=512, I=384, E=8, k=2, shared=True)
+    c = gpu_case(cfg, seed=384, activation="relu2")
+    ids, aff = binding.route(c["logits"], cfg.k)
+    out = _fused(c, ids, aff, variant=variant, layout=layout, activation="relu2")
+    torch.cuda.synchronize()
+    ref_ids, ref_aff = oracle.route_softmax_topk(np_(c["logits"]), cfg.k)
+    rows = np.arange(cfg.T)
+    xr = _xhat_rows(c, rows) if variant == "prefill_a8" else None
+    ref = oracle_rows(c, ref_ids, ref_aff, rows, xrows=xr)
+    assert_out_close(np_(out), ref, what=f"relu2 I=384 {variant}/{layout}")
+
+
 @pytest.mark.parametrize("name", ["tiny", "prefill16k_wide"])
 def test_fused_prefill_a8_relu2(name):
     c = _case(name, "relu2")
     cfg = c["cfg"]
     ids, aff = binding.route(c["logits"], cfg.k)
-    if cfg.I % 256:
-        with pytest.raises(binding.MoeError):
-            _fused(c, ids, aff, variant="prefill_a8", activation="relu2")
-        return
+    # (tiny: I = 128 runs the 128-column up tiles)
     out = _fused(c, ids, aff, variant="prefill_a8", activation="relu2")
     torch.cuda.synchronize()
     ref_ids, ref_aff = oracle.route_softmax_topk(np_(c["logits"]), cfg.k)
