@@ -66,9 +66,9 @@ static FusedLayout fused_layout(int T, int H, int I, int E, int k, int has_share
     L.seg_row0 = take(sizeof(int32_t) * (E + 1));
     L.seg_rows = take(sizeof(int32_t) * (E + 1));
     L.seg_tile0 = take(sizeof(int32_t) * (E + 2));
-    // prefill tiles: at most ceil(R / tile) + one partial tile per segment
-    const size_t tm = (size_t)prefill_tile_m();
-    const size_t max_tiles = (R + tm - 1) / tm + E + 1 + (has_shared ? ((size_t)T + tm - 1) / tm : 0);
+    // row tiles (prefill: 128 rows; the sorted decode kernel: 16 or 32): at
+    // most ceil(R / tile) + one partial tile per segment, sized for 16 rows
+    const size_t max_tiles = decode_fused_tile_capacity(T, k, E, has_shared, 16);
     L.tile_info = take(sizeof(int4) * max_tiles);
     L.tile_n = take(sizeof(int32_t));
     L.sort_scratch = take(sort_scratch_bytes((int)R, E));
@@ -334,8 +334,8 @@ static int fused_impl(const char* who, const void* x, const uint8_t* w13, const 
     p.seg_rows = reinterpret_cast<int32_t*>(base + L.seg_rows);
     p.seg_tile0 = reinterpret_cast<int32_t*>(base + L.seg_tile0);
     const bool pf = variant == MOE_VARIANT_PREFILL || fp8_x;
-    p.tile_info = pf ? reinterpret_cast<int4*>(base + L.tile_info) : nullptr;
-    p.tile_n = pf ? reinterpret_cast<int32_t*>(base + L.tile_n) : nullptr;
+    p.tile_info = reinterpret_cast<int4*>(base + L.tile_info);
+    p.tile_n = reinterpret_cast<int32_t*>(base + L.tile_n);
     uint16_t* abuf = reinterpret_cast<uint16_t*>(base + L.abuf);
     float* ybuf = reinterpret_cast<float*>(base + L.ybuf);
     hipStream_t s = (hipStream_t)stream;
@@ -351,7 +351,8 @@ static int fused_impl(const char* who, const void* x, const uint8_t* w13, const 
         rc = launch_decode_fused_self(weight_layout, decode_mt(T, k, E), xb, w13, w13_scale, w2,
                                       w2_scale, sh, ids, aff, T, H, I, E, k, ybuf, act, wfmt, s);
     } else {
-        const int tile_m = pf ? prefill_tile_m() : 1;
+        // (the sorted decode kernel takes one row tile of its pass height per workgroup)
+        const int tile_m = pf ? prefill_tile_m() : 16 * decode_mt(T, k, E);
         if ((rc = launch_sort(ids, T, k, E, p, has_shared, tile_m, status, base + L.sort_scratch, s)))
             return rc;
         if (mx4)

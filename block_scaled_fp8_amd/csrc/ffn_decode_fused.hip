@@ -174,14 +174,17 @@ __global__ __launch_bounds__(DF_THREADS) void decode_fused_kernel(
             if (rows == 0) return;  // the same value in every thread
         }
     } else {
-        // the segment fields are loaded together (arrays hold E+1 >= gridDim.x
-        // entries), so one memory latency passes before the weights are known
-        const int seg = blockIdx.x;
-        const int nseg = plan.seg_n[0];
-        e = plan.seg_expert[seg];
-        row0 = plan.seg_row0[seg];
-        rows = plan.seg_rows[seg];
-        if (seg >= nseg) return;
+        // one row tile of the sort's list (at most MROWS rows of one
+        // segment; the list holds gridDim.x records): the record and the
+        // tile count load together, so one memory latency passes before
+        // the weights are known
+        const int tile = blockIdx.x;
+        const int ntiles = plan.tile_n[0];
+        const int4 ti = plan.tile_info[tile];
+        if (tile >= ntiles) return;
+        e = ti.x;
+        row0 = ti.y;
+        rows = ti.z;
     }
     // route index of the m-th row of this workgroup (shared expert: R + token)
     auto route_of = [&](int m) -> int {
@@ -537,7 +540,20 @@ static int launch_decode_fused_l(int MT, const uint16_t* x, const uint8_t* w13, 
                                  const uint8_t* w2, const void* w2s, const SharedW& sh,
                                  const Plan& plan, const int32_t* ids, const float* aff, int T,
                                  int H, int I, int E, int k, float* ybuf, hipStream_t stream) {
-    const int nseg_max = E + (sh.w13 ? 1 : 0);
+    // self-routed: one workgroup per possible segment (E routed + shared);
+    // sorted: one per row tile of 16 MT rows (a segment longer than one
+    // pass spreads over several workgroups).  Workgroups past the real
+    // count exit at once.
+    const size_t nwg = SELF ? (size_t)E + (sh.w13 ? 1 : 0)
+                            : decode_fused_tile_capacity(T, k, E, sh.w13 ? 1 : 0, 16 * MT);
+    if (!SELF && (!plan.tile_info || !plan.tile_n)) {
+        set_error("decode: the sorted fused kernel needs the sort's tile list");
+        return MOE_EINVAL;
+    }
+    if (nwg > 0x7FFFFFFFu) {
+        set_error("decode: too many row tiles");
+        return MOE_EUNSUPPORTED;
+    }
     const int routes = SELF ? T * k : 0;
     // (x rows in LDS: MXFP4 16-row passes whose rows fit; see
     // decode_fused_x_in_lds.  Measured on decode64: MXFP4 72.4 -> 70.3 us,
@@ -557,7 +573,7 @@ static int launch_decode_fused_l(int MT, const uint16_t* x, const uint8_t* w13, 
     const int ytrash = T * k + (sh.w13 ? T : 0);
     prof_begin(MX4 ? "decode_fused_expert_mxfp4" : "decode_fused_expert", stream);
 #define MOE_DF_KERNEL(MTV, XL, XAV)                                                                       \
-    decode_fused_kernel<MTV, 2, LAYOUT, SELF, RELU2, MX4, XL, XAV><<<nseg_max, DF_THREADS, lds, stream>>>( \
+    decode_fused_kernel<MTV, 2, LAYOUT, SELF, RELU2, MX4, XL, XAV><<<(unsigned)nwg, DF_THREADS, lds, stream>>>( \
         x, w13, w13s, w2, w2s, sh.w13, sh.w13_scale, sh.w2, sh.w2_scale, plan, ids, E, aff, T, H, I,      \
         k, ybuf, ytrash)
     if (MX4 && MT == 1 && xlds)
@@ -593,8 +609,12 @@ static int launch_decode_fused_any(int layout, int MT, const uint16_t* x, const 
 #undef MOE_DF_LAUNCH
 }
 
-// One workgroup per possible segment (E routed + shared); workgroups past the
-// number of active segments exit at once.
+size_t decode_fused_tile_capacity(int T, int k, int E, int has_shared, int tile_m) {
+    const size_t R = (size_t)T * k, tm = (size_t)tile_m;
+    return (R + tm - 1) / tm + (size_t)E + 1 + (has_shared ? ((size_t)T + tm - 1) / tm : 0);
+}
+
+// The sorted form: one workgroup per row tile of the sort's list.
 int launch_decode_fused(int layout, int MT, const uint16_t* x, const uint8_t* w13,
                         const void* w13s, const uint8_t* w2, const void* w2s, const SharedW& sh,
                         const Plan& plan, const float* aff, int T, int H, int I, int E, int k,

@@ -109,6 +109,9 @@ bool decode_fused_fits(int T, int k, int E, int H, int I, int has_shared, bool s
 size_t decode_fused_lds_bytes(int MT, int I, int self_routes, int H = 0, bool alias = false);
 bool decode_fused_x_in_lds(int MT, int H, int I, int self_routes);
 int decode_self_routed_max_routes();
+// Row tiles of tile_m rows over all segments, at most (the sort's tile list
+// holds this many records when built with tile_m >= the given size).
+size_t decode_fused_tile_capacity(int T, int k, int E, int has_shared, int tile_m);
 int launch_decode_fused_self(int layout, int MT, const uint16_t* x, const uint8_t* w13,
                              const void* w13s, const uint8_t* w2, const void* w2s,
                              const SharedW& sh, const int32_t* ids, const float* aff, int T,
