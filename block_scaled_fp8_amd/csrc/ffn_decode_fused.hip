@@ -1,5 +1,6 @@
-// Decode variant, one workgroup per active expert: gate/up GEMM -> SwiGLU ->
-// down GEMM in a single launch, the SwiGLU activations kept in LDS.
+// Decode variant, one workgroup per active expert (or, after the sort, per
+// row tile of an expert's routes): gate/up GEMM -> SwiGLU -> down GEMM in a
+// single launch, the SwiGLU activations kept in LDS.
 //
 // Source: "Gated DeltaNet (+ FP8 MoE) -- AWS Neuron (NKI) kernels for
 // Trainium2", section "FP8 MoE decode kernel (moe_fused_w8_35b)": the fused
@@ -44,7 +45,7 @@ constexpr int DF_NT = 4;  // weight tiles (16 rows each) per wave pass
 // Every wave runs the same, static sequence: all chunk counts are even
 // (K % 128 == 0); a wave with fewer real groups than the others re-streams a
 // valid tile and writes its results into LDS padding columns or a trash row of
-// y; rows past the segment write to the trash row too.  With no conditional
+// y; rows past the workgroup's routes write to the trash row too.  With no conditional
 // loads or stores (global stores also count on the vector-memory counter of
 // gfx9-class GPUs), the compiler's wait counts stay partial and the pipeline
 // never drains mid-stream.

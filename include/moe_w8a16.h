@@ -64,7 +64,9 @@ enum {
 
 enum {
     MOE_VARIANT_AUTO = 0,     /* decode for T*k <= 16E and T*k <= 4096, else prefill */
-    MOE_VARIANT_DECODE = 1,   /* weight-streaming kernels, one workgroup per (expert, N tile) */
+    MOE_VARIANT_DECODE = 1,   /* weight-streaming kernels: one workgroup per active expert
+                                 (or per 16/32-row tile of its routes past 4096 routes), or per
+                                 (expert, N tile) with few active experts */
     MOE_VARIANT_PREFILL = 2,  /* grouped bf16-MFMA GEMM over 128-row tiles of sorted routes */
     MOE_VARIANT_PREFILL_A8 = 3  /* the prefill GEMMs with x quantised to E4M3 per token (as
                                    moe_quant_e4m3_rows) for the gate/up (or up) GEMM on the
@@ -242,7 +244,7 @@ typedef struct {
  *
  * moe_fused_workspace_bytes -- device scratch of a moe_fused_w8a16(_ex) call
  * with these sizes and this variant (interface plumbing, not from the pages):
- * the sort maps, the prefill tile list, the activations between the GEMMs and
+ * the sort maps, the row-tile list, the activations between the GEMMs and
  * one contribution row per route (fp32 for the decode variant, 2.125 bytes a
  * value for the prefill ones; AUTO is sized for either).  0 for invalid
  * sizes.  A call checks ws_bytes against the size of the variant it runs. */
