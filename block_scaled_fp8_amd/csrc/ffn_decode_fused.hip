@@ -50,6 +50,7 @@ constexpr int DF_NT = 4;  // weight tiles (16 rows each) per wave pass
 // gfx9-class GPUs), the compiler's wait counts stay partial and the pipeline
 // never drains mid-stream.
 constexpr int DF_HALF = DF_NT / 2;
+constexpr int DF_XCD_RUN = 8;  // sorted form: consecutive row tiles an XCD takes at a time
 
 // Self-routed mode (decode batches of at most DF_SELF_MAX_ROUTES routes): the
 // workgroup of expert e finds its own routes by scanning the ids (wave ballots,
@@ -113,7 +114,7 @@ __global__ __launch_bounds__(DF_THREADS) void decode_fused_kernel(
     const void* __restrict__ sh_w13s, const uint8_t* __restrict__ sh_w2,
     const void* __restrict__ sh_w2s, Plan plan, const int32_t* __restrict__ ids, int E,
     const float* __restrict__ aff, int T, int H, int I, int k, float* __restrict__ ybuf,
-    int ytrash_row) {
+    int ytrash_row, int tile_cap) {
     // two 64-wide chunks per 128-wide scale block, two in flight: the chunk
     // in flight slot d is the block's first (d = 0) or second (d = 1) half
     static_assert(DEPTH == 2, "chunks per 128-wide scale block");
@@ -176,12 +177,16 @@ __global__ __launch_bounds__(DF_THREADS) void decode_fused_kernel(
         }
     } else {
         // one row tile of the sort's list (at most MROWS rows of one
-        // segment; the list holds gridDim.x records): the record and the
-        // tile count load together, so one memory latency passes before
-        // the weights are known
-        const int tile = blockIdx.x;
+        // segment).  Runs of DF_XCD_RUN consecutive tiles go to one XCD
+        // (workgroups are dealt round-robin over the 8 XCDs), so the tiles of
+        // one expert re-read its weights from that XCD's L2.  The record and
+        // the tile count load together, so one memory latency passes before
+        // the weights are known (the index is clamped to the list's
+        // capacity, the record then unused).
+        const int b = blockIdx.x, j = b >> 3;
+        const int tile = (j / DF_XCD_RUN) * (8 * DF_XCD_RUN) + (b & 7) * DF_XCD_RUN + j % DF_XCD_RUN;
         const int ntiles = plan.tile_n[0];
-        const int4 ti = plan.tile_info[tile];
+        const int4 ti = plan.tile_info[min(tile, tile_cap - 1)];
         if (tile >= ntiles) return;
         e = ti.x;
         row0 = ti.y;
@@ -545,8 +550,11 @@ static int launch_decode_fused_l(int MT, const uint16_t* x, const uint8_t* w13, 
     // sorted: one per row tile of 16 MT rows (a segment longer than one
     // pass spreads over several workgroups).  Workgroups past the real
     // count exit at once.
+    // (sorted: the grid is the capacity rounded up to whole rounds of
+    // 8 * DF_XCD_RUN, so that the tile dealing covers every index below it)
+    const size_t cap = SELF ? 0 : decode_fused_tile_capacity(T, k, E, sh.w13 ? 1 : 0, 16 * MT);
     const size_t nwg = SELF ? (size_t)E + (sh.w13 ? 1 : 0)
-                            : decode_fused_tile_capacity(T, k, E, sh.w13 ? 1 : 0, 16 * MT);
+                            : (cap + 8 * DF_XCD_RUN - 1) / (8 * DF_XCD_RUN) * (8 * DF_XCD_RUN);
     if (!SELF && (!plan.tile_info || !plan.tile_n)) {
         set_error("decode: the sorted fused kernel needs the sort's tile list");
         return MOE_EINVAL;
@@ -576,7 +584,7 @@ static int launch_decode_fused_l(int MT, const uint16_t* x, const uint8_t* w13, 
 #define MOE_DF_KERNEL(MTV, XL, XAV)                                                                       \
     decode_fused_kernel<MTV, 2, LAYOUT, SELF, RELU2, MX4, XL, XAV><<<(unsigned)nwg, DF_THREADS, lds, stream>>>( \
         x, w13, w13s, w2, w2s, sh.w13, sh.w13_scale, sh.w2, sh.w2_scale, plan, ids, E, aff, T, H, I,      \
-        k, ybuf, ytrash)
+        k, ybuf, ytrash, (int)cap)
     if (MX4 && MT == 1 && xlds)
         MOE_DF_KERNEL(1, MX4, false);
     else if (MT == 1)
