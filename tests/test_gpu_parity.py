@@ -260,11 +260,13 @@ def _check_route_proj(x, wg, k, what):
 
 
 # (T, H, E, k): K slices S = 1/2/8 with load-ring depths 1/2/4, ragged T and E,
-# the widest expert count with k = 16, and the two workload geometries
+# the widest expert count with k = 16, the two workload geometries, and more
+# ragged shapes with an odd number of K stages
 @pytest.mark.parametrize("T,H,E,k", [(1, 64, 1, 1), (5, 256, 8, 2), (64, 2048, 256, 8),
                                      (300, 384, 100, 6), (700, 640, 130, 4),
                                      (2048, 1024, 512, 10), (33, 8192, 1024, 16),
-                                     (8192, 2048, 256, 8)])
+                                     (8192, 2048, 256, 8), (1500, 768, 200, 8),
+                                     (1024, 320, 64, 4)])
 def test_route_proj_parity(T, H, E, k):
     x = synth.make_activations(synth.MoeConfig("p", T, H, 128, E, k), seed=T + H)[0].cuda()
     wg = synth.make_gate_weights(E, H, seed=E + k).cuda()
