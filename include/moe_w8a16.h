@@ -354,8 +354,10 @@ typedef struct {
  *              (rows, cols = K/32); MOE_LAYOUT_ROWMAJOR: both as above
  * Everything else as moe_fused_w8a16_ex; the workspace is that of
  * MOE_VARIANT_DECODE (moe_fused_workspace_bytes).  The weights are streamed
- * by the one-workgroup-per-expert decode kernel at every batch size:
- * MOE_VARIANT_AUTO and MOE_VARIANT_DECODE run it, the prefill variants give
+ * by the weight-streaming decode kernel at every batch size (one workgroup
+ * per active expert up to 4096 routes, above that one per 32-row tile of an
+ * expert's sorted routes): MOE_VARIANT_AUTO and MOE_VARIANT_DECODE run it,
+ * the prefill variants give
  * MOE_EUNSUPPORTED, and so do shapes whose 16- or 32-row activation pass does
  * not fit 64 KB of LDS (16 or 32 * (I + 8) * 2 bytes, plus 4 bytes a route
  * when T*k <= 4096) or with T*H >= 2^32.  The E8M0 scale is applied exactly
