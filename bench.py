@@ -532,7 +532,26 @@ def fused_variant_bench(cfg, dev, L, seed=0, activation="swiglu", variant="auto"
            "TFLOP_per_s": round(flops / (us * 1e-6) / 1e12, 1),
            "mfma_frac_bf16": round(flops / (us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4),
            "kernels": {n: {"launches": c, "avg_us": round(ms * 1e3, 3)} for n, (c, ms) in prof.items()}}
-    if "decode_fused_expert_mxfp4" in prof and T * k > 16 * E:
+    mxg = [n for n in ("prefill_gateup_swiglu_mxfp4", "prefill_up_relu2_mxfp4") if n in prof]
+    if mxg:
+        # the grouped gate/up (or up) GEMM on MXFP4 weights, against the bf16
+        # MFMA peak it runs on (the codes are widened to bf16 on chip)
+        kus = prof[mxg[0]][1] * 1e3
+        kfl = 2.0 * H * n13 * rows
+        out["roofline"] = {"bound": "mfma", "kernel": mxg[0], "flops_per_launch": kfl,
+                           "avg_us": round(kus, 3),
+                           "achieved": round(kfl / (kus * 1e-6) / 1e12, 1),
+                           "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                           "frac": round(kfl / (kus * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                           "traffic": profiled_traffic(mxg[0], cfg.name),
+                           "traffic_unit": "bytes per launch"}
+        if "prefill_down_mxfp4" in prof:
+            dus = prof["prefill_down_mxfp4"][1] * 1e3
+            dfl = 2.0 * H * I * rows
+            out["down_gemm"] = {"kernel": "prefill_down_mxfp4", "avg_us": round(dus, 3),
+                                "TFLOP_per_s": round(dfl / (dus * 1e-6) / 1e12, 1),
+                                "frac": round(dfl / (dus * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+    elif "decode_fused_expert_mxfp4" in prof and T * k > 16 * E:
         # prefill sizes: the method is MFMA-bound (its weights once are a
         # small part); the weight-streaming kernel re-reads each expert's
         # weights once per 32-row tile, so it is reported against the bf16
@@ -722,6 +741,10 @@ def main():
         if args.prefill_workload:
             result["mxfp4"].append(fused_variant_bench(synth.CONFIGS[args.prefill_workload], dev,
                                                        2, args.seed, weight_format="mxfp4"))
+        if not args.no_extra_workloads and args.prefill_workload != "prefill16k_wide":
+            # the wide geometry of the MXFP4 prefill figures on the pages
+            result["mxfp4"].append(fused_variant_bench(synth.CONFIGS["prefill16k_wide"], dev, 1,
+                                                       args.seed, weight_format="mxfp4"))
     if args.prefill_workload and not args.no_a8:
         result["prefill_a8"] = fused_variant_bench(synth.CONFIGS[args.prefill_workload], dev, 2,
                                                    args.seed, variant="prefill_a8")

@@ -348,9 +348,7 @@ def fused_w8a16(x, w13, w13_scale, w2, w2_scale, ids, aff, shared=None, out=None
             raise ValueError("the no-allocation entry point takes E4M3FN weights")
         _check(lib.moe_fused_w8a16_noalloc(*head, _layout(layout), v, act, _stream(dev)))
         return out
-    # (MXFP4 weights run the decode variant's kernels: its workspace)
-    need = int(lib.moe_fused_workspace_bytes(T, H, I, E, k, int(shared is not None),
-                                             VARIANTS["decode"] if mx else v))
+    need = int(lib.moe_fused_workspace_bytes(T, H, I, E, k, int(shared is not None), v))
     if ws is None:
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     fn = lib.moe_fused_mxfp4 if mx else lib.moe_fused_w8a16_ex
@@ -435,7 +433,7 @@ class MoeStep:
         # one checked call validates every argument and sizes the workspace
         mx = weight_format == "mxfp4"
         self.ws = torch.empty(max(1, fused_workspace_bytes(T, H, I, E, k, shared is not None,
-                                                           "decode" if mx else variant)),
+                                                           variant)),
                               dtype=torch.uint8, device=dev)
         ids, aff = route(logits, k)
         fused_w8a16(x, w13, w13_scale, w2, w2_scale, ids, aff, shared=shared, out=self.out,

@@ -266,8 +266,8 @@ static int fused_impl(const char* who, const void* x, const uint8_t* w13, const 
         set_error("unknown variant %d", variant);
         return MOE_EINVAL;
     }
-    if (mx4 && (variant == MOE_VARIANT_PREFILL || variant == MOE_VARIANT_PREFILL_A8)) {
-        set_error("%s: MXFP4 weights run the weight-streaming (decode) kernels only", who);
+    if (mx4 && variant == MOE_VARIANT_PREFILL_A8) {
+        set_error("%s: MXFP4 weights multiply bf16 activations (no fp8-activation variant)", who);
         return MOE_EUNSUPPORTED;
     }
     if (T == 0) return MOE_OK;
@@ -303,7 +303,17 @@ static int fused_impl(const char* who, const void* x, const uint8_t* w13, const 
     }
     const int has_shared = shared ? 1 : 0;
     const bool fp8_x = variant == MOE_VARIANT_PREFILL_A8;
-    variant = mx4 ? MOE_VARIANT_DECODE : resolve_variant(T, H, I, E, k, act, variant);
+    // the prefill GEMMs stage MXFP4 scales with 4-byte loads
+    const bool mx_sc4 = !mx4 || ((((uintptr_t)w13_scale | (uintptr_t)w2_scale |
+                                  (shared ? (uintptr_t)shared->w13_scale | (uintptr_t)shared->w2_scale : 0)) &
+                                 3) == 0);
+    if (mx4 && variant == MOE_VARIANT_PREFILL && !mx_sc4) {
+        set_error("%s: the prefill variant needs 4-byte aligned MXFP4 scale arrays", who);
+        return MOE_EINVAL;
+    }
+    const int auto_pick = variant == MOE_VARIANT_AUTO;
+    variant = resolve_variant(T, H, I, E, k, act, variant);
+    if (auto_pick && mx4 && !mx_sc4) variant = MOE_VARIANT_DECODE;
     const FusedLayout L = fused_layout(T, H, I, E, k, has_shared, variant);
     if (!ws || ws_bytes < L.total) {
         set_error("%s: workspace of %zu bytes needed (got %zu)", who, L.total, ws_bytes);
@@ -312,11 +322,13 @@ static int fused_impl(const char* who, const void* x, const uint8_t* w13, const 
     if (variant == MOE_VARIANT_PREFILL || fp8_x) {
         if (int rc = prefill_check(T, H, I, E, k, has_shared, act)) return rc;
     }
-    // MXFP4 weights: the one-workgroup-per-expert kernel at every size
+    // MXFP4 weights, decode variant: the weight-streaming kernel (self-routed
+    // or on row tiles of the sort)
     const long long R = (long long)T * k;
     const bool mx_self = R <= decode_self_routed_max_routes();
-    if (mx4 && (decode_fused_lds_bytes(decode_mt(T, k, E), I, mx_self ? (int)R : 0) > 64 * 1024 ||
-                (long long)T * H >= (1LL << 32))) {
+    if (mx4 && variant == MOE_VARIANT_DECODE &&
+        (decode_fused_lds_bytes(decode_mt(T, k, E), I, mx_self ? (int)R : 0) > 64 * 1024 ||
+         (long long)T * H >= (1LL << 32))) {
         set_error("%s: MXFP4 weights need the activations of one expert pass in 64 KB of LDS "
                   "and T*H < 2^32 (got T=%d, H=%d, I=%d)", who, T, H, I);
         return MOE_EUNSUPPORTED;
@@ -355,7 +367,7 @@ static int fused_impl(const char* who, const void* x, const uint8_t* w13, const 
         const int tile_m = pf ? prefill_tile_m() : 16 * decode_mt(T, k, E);
         if ((rc = launch_sort(ids, T, k, E, p, has_shared, tile_m, status, base + L.sort_scratch, s)))
             return rc;
-        if (mx4)
+        if (mx4 && variant == MOE_VARIANT_DECODE)
             rc = launch_decode_fused(weight_layout, decode_mt(T, k, E), xb, w13, w13_scale, w2,
                                      w2_scale, sh, p, aff, T, H, I, E, k, ybuf, act, wfmt, s);
         else if (variant == MOE_VARIANT_DECODE)
@@ -365,8 +377,8 @@ static int fused_impl(const char* who, const void* x, const uint8_t* w13, const 
             uint8_t* xq = fp8_x ? reinterpret_cast<uint8_t*>(base + L.xq) : nullptr;
             float* xsc = fp8_x ? reinterpret_cast<float*>(base + L.xs) : nullptr;
             if (fp8_x && (rc = launch_quant_rows_e4m3(xb, T, H, xq, xsc, s))) return rc;
-            rc = launch_prefill_ffn(weight_layout, xb, w13, w13f, w2, w2f, sh, p, T, H, I, E, k,
-                                    abuf, ybuf, act, xq, xsc, s);
+            rc = launch_prefill_ffn(weight_layout, xb, w13, w13_scale, w2, w2_scale, sh, p, T, H, I,
+                                    E, k, abuf, ybuf, act, xq, xsc, wfmt, s);
         }
     }
     if (rc) return rc;

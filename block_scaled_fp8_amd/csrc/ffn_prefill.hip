@@ -53,6 +53,12 @@
 //  * Epilogue: gate/up applies SwiGLU (up: relu^2) and down encodes its
 //    contributions; both turn the accumulators into row pieces through LDS
 //    so that a lane stores 16 contiguous bytes of a row.
+//  * MXFP4 weights ("Add gfx950 Q256 fused MXFP4 prefill pipeline": E2M1
+//    codes with an E8M0 scale per 32 elements of a row) run the same
+//    kernels on 32x32 tiles: a stage holds 32 code bytes a weight row and
+//    the scale bytes of its 128-wide K chunk; each lane's 16 code bytes of a
+//    step are exactly one scale block, whose power of two the bf16
+//    conversion applies, so no running scale is needed.
 #include <algorithm>
 #include <type_traits>
 
@@ -67,7 +73,8 @@ constexpr int PF_XCD_RUN = 8;  // consecutive row tiles an XCD takes at a time
 // Workgroup tile BM rows x BN columns, WM x WN waves of 64 x 128 each (2 x 4
 // MFMA tiles of 32 x 32), STAGES LDS stages of 64-wide K, OCC workgroups per
 // CU (the register budget follows from it).
-template <int BM_, int BN_, int WM_, int WN_, int STAGES_, int OCC_, int M16_ = 0, int A8_ = 0>
+template <int BM_, int BN_, int WM_, int WN_, int STAGES_, int OCC_, int M16_ = 0, int A8_ = 0,
+          int MX4_ = 0>
 struct PfCfg {
     static constexpr int OCC = OCC_;
     // MFMA shape: v_mfma_f32_16x16x32_bf16 (M16) or v_mfma_f32_32x32x16_bf16;
@@ -76,16 +83,26 @@ struct PfCfg {
     static constexpr bool M16 = M16_ != 0;
     static constexpr bool A8 = A8_ != 0;
     static_assert(!(M16 && A8), "the fp8 path uses 32x32 tiles");
+    // MX4: MXFP4 weights (E2M1 codes, two a byte, one E8M0 scale per 32
+    // elements of a row); a stage holds 32 code bytes of each weight row and
+    // the scale bytes of the 128-wide K chunk the step lies in
+    static constexpr bool MX4 = MX4_ != 0;
+    static_assert(!(MX4 && A8), "MXFP4 weights multiply bf16 activations");
+    static_assert(!(MX4 && M16), "MXFP4 weights use 32x32 tiles");
     static constexpr int MS = M16 ? 16 : 32;  // rows = columns of one MFMA tile
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
     static constexpr int THREADS = WM * WN * MOE_WAVE;
     static constexpr int WAVES = WM * WN;
     static constexpr int STAGES = STAGES_;
     static constexpr int A_BYTES = BM * PF_BK * (A8 ? 1 : 2);  // bf16 or E4M3
-    static constexpr int B_BYTES = BN * PF_BK;      // fp8
-    static constexpr int STAGE = A_BYTES + B_BYTES;
+    static constexpr int B_BYTES = BN * PF_BK / (MX4 ? 2 : 1);  // fp8 or E2M1
+    static constexpr int TB = MX4 ? 512 : 1024;    // bytes of a 16-row weight tile per stage
+    static constexpr int S_BYTES = MX4 ? BN * 4 : 0;  // E8M0: 4 scale bytes a row
+    static constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES;
     static constexpr int A_INSTR = A_BYTES / 1024 / WAVES;  // 1 KB loads per wave per stage
     static constexpr int B_INSTR = B_BYTES / 1024 / WAVES;
+    static constexpr int S_INSTR = MX4 ? 1 : 0;    // 256-byte scale loads per wave per stage
+    static_assert(!MX4 || S_BYTES == WAVES * 256, "each wave stages the scales of 64 rows");
     static constexpr int MT = BM / WM / MS;
     static constexpr int NT = BN / WN / MS;
     static constexpr int WROWS = BM / WM;  // rows of a wave tile
@@ -114,6 +131,12 @@ using PfGateUpA8 = PfCfg<128, 256, 2, 2, 3, 2, 0, 1>;
 // of two waves (the 256-column tile would run past the matrix)
 using PfUpNarrow = PfCfg<128, 128, 2, 1, 2, 2, 1>;
 using PfUpNarrowA8 = PfCfg<128, 128, 2, 1, 3, 2, 0, 1>;
+// MXFP4 weights: the same tiles on 32x32x16 MFMAs (a lane's 16 code bytes
+// of a step are one scale block; with 16x16 tiles the per-half code and scale
+// operands spilled registers)
+using PfGateUpMx = PfCfg<128, 256, 2, 2, 2, 2, 0, 0, 1>;
+using PfDownMx = PfCfg<128, 256, 2, 2, 2, 2, 0, 0, 1>;
+using PfUpNarrowMx = PfCfg<128, 128, 2, 1, 2, 2, 0, 0, 1>;
 constexpr int PF_BM = 128;
 
 int prefill_tile_m() { return PF_BM; }
@@ -133,6 +156,15 @@ int prefill_supported(int H, int I, int act) {
 // PF_UP:     the up projection of a non-gated expert, relu^2 epilogue into abuf;
 // PF_DOWN:   the down projection, block floating-point rows into ybuf.
 enum { PF_GATEUP = 0, PF_DOWN = 1, PF_UP = 2 };
+
+// LDS the epilogue passes a tile's results through (from byte 0; the launch
+// gives the kernel at least this much): fp32 32-row slabs of 128 columns a
+// wave (down), or the wave's bf16 activation rows.
+template <int MODE, class C>
+constexpr int pf_epilogue_lds() {
+    return MODE == PF_DOWN ? C::WAVES * 32 * 128 * 4
+                           : C::WAVES * C::WROWS * (MODE == PF_GATEUP ? C::WCOLS / 2 : C::WCOLS) * 2;
+}
 
 // silu(g) * u with the hardware reciprocal (about 1 ulp) in place of an IEEE
 // divide; exp(-g) overflowing to +inf gives the correct limit 0.
@@ -180,8 +212,8 @@ __device__ __forceinline__ void barrier_after_lds_reads() {
 template <int MODE, int LAYOUT, class C>
 __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ abuf_in,
-    const uint8_t* __restrict__ wexp, const float* __restrict__ sexp,
-    const uint8_t* __restrict__ wsh, const float* __restrict__ ssh, Plan plan,
+    const uint8_t* __restrict__ wexp, const void* __restrict__ sexp,
+    const uint8_t* __restrict__ wsh, const void* __restrict__ ssh, Plan plan,
     int T, int H, int I, int k, int nblk, int max_tiles,
     uint16_t* __restrict__ abuf_out, float* __restrict__ ybuf, const float* __restrict__ xscale) {
     constexpr int BM = C::BM, BN = C::BN;
@@ -217,8 +249,14 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
     constexpr bool PAIRED = MODE == PF_GATEUP; // gate and up columns side by side
     const int K = GATHER ? H : I;
     const int Nrows = MODE == PF_GATEUP ? 2 * I : (MODE == PF_UP ? I : H);  // weight rows
-    const uint8_t* W = e >= 0 ? wexp + (size_t)e * Nrows * K : wsh;
-    const float* S = e >= 0 ? sexp + (size_t)e * (Nrows / 128) * (K / 128) : ssh;
+    // weight rows of KB bytes; scales: fp32 [Nrows/128][K/128] blocks, or
+    // (MX4) E8M0 bytes [Nrows][K/32]
+    const int KB = C::MX4 ? K / 2 : K;
+    const uint8_t* W = e >= 0 ? wexp + (size_t)e * Nrows * KB : wsh;
+    const float* S = e >= 0 ? static_cast<const float*>(sexp) + (size_t)e * (Nrows / 128) * (K / 128)
+                            : static_cast<const float*>(ssh);
+    const uint8_t* SX = e >= 0 ? static_cast<const uint8_t*>(sexp) + (size_t)e * Nrows * (K / 32)
+                               : static_cast<const uint8_t*>(ssh);
     const int R = T * k;
 
     const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
@@ -258,23 +296,46 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
                                         : (uint32_t)(p0 + (row < rows_here ? row : 0));
         asrc[q] = src_row * (uint32_t)((C::A8 ? 1 : 2) * (GATHER ? H : I)) + sw * 16;
     }
-    // weights: instruction q of wave w fills 16-row tile w*B_INSTR + q
+    // weights: instruction q of wave w fills 16-row tile w*B_INSTR + q (MX4:
+    // the step's 512 bytes of tiles 2 (w*B_INSTR + q) and the next one, from
+    // lanes 0-31 and 32-63; a 16-row tile's staged piece holds 32-K quarter j
+    // of its row r at 16-byte position 16 j + r, as in a 64-byte chunk of
+    // the tiled layout)
     constexpr int HALF_T = BN / 2 / 16;  // gate tiles in a gate/up tile (MODE 0)
+    // weight row of the WG's 16-row tile t (MODE 0: gate tiles, then up)
+    auto tile_row = [&](int t) {
+        return PAIRED ? (t < HALF_T ? 0 : I) + nb * (BN / 2) + (t % HALF_T) * 16 : nb * BN + t * 16;
+    };
     // (a wave-uniform tile base plus one per-lane offset, so the loads address
     //  through a scalar base; the lane's 16 bytes follow tile_lane_ptr)
     const uint8_t* bbase[C::B_INSTR];
 #pragma unroll
     for (int q = 0; q < C::B_INSTR; ++q) {
-        const int t16 = wave * C::B_INSTR + q;
-        int wrow;
-        if (PAIRED)
-            wrow = (t16 < HALF_T ? 0 : I) + nb * (BN / 2) + (t16 % HALF_T) * 16;
-        else
-            wrow = nb * BN + t16 * 16;
-        bbase[q] = W + (size_t)wrow * K;  // the tiled layout keeps whole 16-row tiles in place
+        const int t16 = (C::MX4 ? 2 : 1) * (wave * C::B_INSTR + q);
+        // the tiled layout keeps whole 16-row tiles in place
+        bbase[q] = W + (size_t)tile_row(t16) * KB;
     }
-    const uint32_t blane = LAYOUT == LAYOUT_TILED ? lane * 16 : (lane & 15) * K + (lane >> 4) * 16;
-    constexpr int CS = chunk_stride<LAYOUT>();
+    uint32_t blane;
+    if constexpr (C::MX4)
+        blane = (lane >> 5) * 16u * KB +
+                (LAYOUT == LAYOUT_TILED ? (lane & 31) * 16 : (lane & 15) * KB + ((lane >> 4) & 1) * 16);
+    else
+        blane = LAYOUT == LAYOUT_TILED ? lane * 16 : (lane & 15) * K + (lane >> 4) * 16;
+    // bytes from one step's weight piece to the next
+    constexpr int CS = C::MX4 ? (LAYOUT == LAYOUT_TILED ? 512 : 32) : chunk_stride<LAYOUT>();
+    // MX4 scales of the 128-wide K chunk the step lies in (both steps of a
+    // chunk stage the same bytes): lanes 16 i .. 16 i + 15 of wave w stage the
+    // 64 bytes of 16-row tile 4 w + i at byte 64 (4 w + i) of the scale area,
+    // 4 bytes a lane -- the tiled layout's scale chunk of the tile as it is
+    // (byte 16 j + r: 32-K quarter j, row r), or row-major the 4 bytes of row
+    // r (byte 4 r + j).
+    uint32_t ssrc = 0;
+    if constexpr (C::MX4) {
+        const int tw = 4 * wave + (lane >> 4), r = lane & 15;
+        ssrc = LAYOUT == LAYOUT_TILED ? (uint32_t)(tile_row(tw) >> 4) * (uint32_t)(K / 128) * 64u + r * 4
+                                      : (uint32_t)(tile_row(tw) + r) * (uint32_t)(K / 32);
+    }
+    constexpr uint32_t SCS = LAYOUT == LAYOUT_TILED ? 64 : 4;  // per 128-K chunk
 
     auto issue_stage = [&](int st, int kc) {
         const uint32_t sbase = st * C::STAGE;
@@ -286,6 +347,9 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
         for (int q = 0; q < C::B_INSTR; ++q)
             lds_load16(bbase[q] + (size_t)kc * CS + blane, sbase + C::A_BYTES + (wave * C::B_INSTR + q) * 1024,
                        smem);
+        if constexpr (C::MX4)
+            __builtin_amdgcn_global_load_lds(SX + (ssrc + (uint32_t)(kc >> 1) * SCS),
+                                             smem + sbase + C::A_BYTES + C::B_BYTES + wave * 256, 4, 0, 0);
     };
 
     // ---- wave tile: rows wm*WROWS .. +WROWS, columns wn*WCOLS .. +WCOLS of
@@ -306,10 +370,18 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
     //   so that one 16-byte weight read serves both sub-steps.
     // An activation piece (16 bytes) is one kb of a row; a weight lane of the
     // staged 1 KB chunk holds kbs 2 (L / 16), 2 (L / 16) + 1 of row L % 16.
+    //
+    // MX4 (32 code bytes a row per step, 32x32 tiles): the lane's 16 bytes
+    // are quarter lg of its row, K [32 lg, 32 lg + 32), one scale block;
+    // sub-step s takes bytes 4s .. 4s + 3 (element 2i of a byte is its low
+    // nibble), so K block 4 lg + s as above.  The lane's scale byte sits at
+    // s_off + s_step(nt) in the stage, plus 32 (tiled) or 2 (row-major) for
+    // the second step of a chunk.
     const int l16 = lane & 15, g16 = lane >> 4;
     uint32_t a_off[4];
-    uint32_t b_off;
+    uint32_t b_off, s_off = 0;
     const int t16 = PAIRED ? wn * (C::WCOLS / 32) : wn * (C::WCOLS / 16);
+    constexpr uint32_t S_AREA = C::A_BYTES + C::B_BYTES;
     if constexpr (C::M16) {
         const int row = wm * C::WROWS + l16;
 #pragma unroll
@@ -325,17 +397,24 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
         // 32-column tile nt spans 16-row tiles t16(nt), t16(nt) + 1; the
         // lane's 16 bytes for half p sit p * 256 bytes further on
         const int tt = t16 + (ln >> 4), r = ln & 15;
-        b_off = C::A_BYTES + tt * 1024 + (2 * lg * 16 + r) * 16;
+        if constexpr (C::MX4) {
+            b_off = C::A_BYTES + tt * 512 + (lg * 16 + r) * 16;
+            s_off = S_AREA + tt * 64 + (LAYOUT == LAYOUT_TILED ? lg * 16 + r : r * 4 + lg);
+        } else {
+            b_off = C::A_BYTES + tt * 1024 + (2 * lg * 16 + r) * 16;
+        }
     }
+    constexpr uint32_t S_PAR = LAYOUT == LAYOUT_TILED ? 32 : 2;
     // (MODE 0: the first NT/2 MFMA column tiles are gate columns, the rest the
     // matching up columns)
     auto a_step = [](int mt) { return mt * C::MS * 128; };
-    auto b_step = [](int nt) {
+    auto t_step = [](int nt) {  // first 16-row weight tile of column tile nt, from t16
         constexpr int T16 = C::MS / 16;  // 16-row weight tiles per MFMA column tile
-        if (PAIRED)
-            return ((nt < C::NT / 2 ? 0 : HALF_T) + (nt % (C::NT / 2)) * T16) * 1024;
-        return nt * T16 * 1024;
+        if (PAIRED) return (nt < C::NT / 2 ? 0 : HALF_T) + (nt % (C::NT / 2)) * T16;
+        return nt * T16;
     };
+    auto b_step = [&](int nt) { return t_step(nt) * C::TB; };
+    auto s_step = [&](int nt) { return t_step(nt) * 64; };
     // ---- block scales of the workgroup's columns, staged once in LDS by
     //      direct-to-LDS loads issued before the first operand stages (so the
     //      first stage wait covers them).  Table row j < NR/2 (MODE 0: gate;
@@ -346,7 +425,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
     const int kblocks = K >> 7;
     const int kbp = (kblocks + 63) & ~63;
     float* sc_tab = reinterpret_cast<float*>(smem + C::STAGES * C::STAGE);
-    {
+    if constexpr (!C::MX4) {
         const int nchunk = kbp >> 6;
         for (int it = wave; it < NR * nchunk; it += C::WAVES) {
             const int j = it / nchunk, c = it - j * nchunk;
@@ -440,7 +519,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
     //      covers the two steps of one 128-wide K block and is branch-free
     //      around the LDS reads, so their waits stay partial.
     const int nk = K / PF_BK;  // even and >= 2 since K % 128 == 0
-    constexpr int PER_STAGE = C::A_INSTR + C::B_INSTR;
+    constexpr int PER_STAGE = C::A_INSTR + C::B_INSTR + C::S_INSTR;  // loads per wave per stage
     // MFMA row groups (32 rows) of this wave that hold rows of the segment:
     // a partial last tile skips the empty ones (their rows are never stored)
     const int mt_active = __builtin_amdgcn_readfirstlane(
@@ -454,8 +533,13 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
     using BFrag = std::conditional_t<C::M16, u32x2, u32x4>;
     u32x4 ah[2][C::MT][AP];
     BFrag bh[2][C::NT];
-    u32x2 bz[C::NT];  // 16x16: sub-step 1's weight bytes, read with sub-step 0's
-    auto read_half = [&](int stage, int p, u32x4 (&a)[C::MT][AP], BFrag (&b)[C::NT]) {
+    // the second half's weight operands, read with the first half's: 16x16 --
+    // sub-step 1's bytes; MX4 -- sub-steps 2, 3 and the scale
+    BFrag bz[C::NT];
+    // MX4 operands {codes, codes, scale, -}: the scale is its E8M0 byte as the
+    // exponent field of an fp32 (the converter reads only that field).  par:
+    // the step's position in its 128-K chunk.
+    auto read_half = [&](int stage, int p, u32x4 (&a)[C::MT][AP], BFrag (&b)[C::NT], int par) {
         const char* st = smem + stage * C::STAGE;
 #pragma unroll
         for (int mt = 0; mt < MTA; ++mt)
@@ -465,11 +549,21 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
         if (MTA > 0) {
 #pragma unroll
             for (int nt = 0; nt < C::NT; ++nt) {
-                if constexpr (C::M16) {
+                if constexpr (C::MX4) {
+                    if (p == 0) {
+                        const uint32_t sc = (uint32_t)*reinterpret_cast<const uint8_t*>(
+                                                st + s_off + par * S_PAR + s_step(nt)) << 23;
+                        const u32x4 w = *reinterpret_cast<const u32x4*>(st + b_off + b_step(nt));
+                        b[nt] = BFrag{w[0], w[1], sc, 0u};
+                        bz[nt] = BFrag{w[2], w[3], sc, 0u};
+                    } else {
+                        b[nt] = bz[nt];
+                    }
+                } else if constexpr (C::M16) {
                     if (p == 0) {
                         const u32x4 w = *reinterpret_cast<const u32x4*>(st + b_off + b_step(nt));
-                        b[nt] = u32x2{w[0], w[1]};
-                        bz[nt] = u32x2{w[2], w[3]};
+                        b[nt] = BFrag{w[0], w[1]};
+                        bz[nt] = BFrag{w[2], w[3]};
                     } else {
                         b[nt] = bz[nt];
                     }
@@ -487,6 +581,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
     auto mma_sub = [&](const u32x4 (&a)[C::MT][AP], const BFrag (&b)[C::NT], int j, bool rescale,
                        const float (&rr)[2]) {
         if (MTA == 0) return;
+        if (C::MX4) rescale = false;  // (the scales are in the operands)
         if (C::M16 && rescale) {
             // 16x16: every accumulator of the block's first half is rescaled
             // before part 0's MFMAs
@@ -506,7 +601,9 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
             const int gi = PAIRED ? nt / (C::NT / 2) : 0;
             if (zs[gi]) continue;  // a zero block scale: nothing to add
             bf16x8 bf;
-            if constexpr (C::M16)
+            if constexpr (C::MX4)
+                bf = fp4x8_to_bf16x8_scaled(b[nt][j], __uint_as_float(b[nt][2]));
+            else if constexpr (C::M16)
                 bf = fp8x8_to_bf16x8_scaled(b[nt][0], b[nt][1], csc[gi]);
             else
                 bf = j == 0 ? fp8x8_to_bf16x8_scaled(b[nt][0], b[nt][1], csc[gi])
@@ -529,13 +626,14 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
     // step kc + 1 landed (with three stages step kc + 2 may still be in
     // flight); the barrier also orders every wave's reads of buffer kc before
     // its refill
-    auto next_step = [&](int kc) {
+    // (par: the position of step kc + 1 in its 128-K chunk)
+    auto next_step = [&](int kc, int par) {
         if (C::STAGES >= 3 && kc + 2 < nk) wait_vmcnt<(C::STAGES >= 3 ? PER_STAGE : 0)>();
         else wait_vmcnt<0>();
         barrier_after_lds_reads();
         if (kc + C::STAGES < nk) issue_stage(kc % C::STAGES, kc + C::STAGES);
         // past the last step this reads a stale buffer whose values are unused
-        read_half((kc + 1) % C::STAGES, 0, ah[0], bh[0]);
+        read_half((kc + 1) % C::STAGES, 0, ah[0], bh[0], par);
     };
 
 #pragma unroll
@@ -544,27 +642,33 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
     if (nk >= C::STAGES) wait_vmcnt<(C::STAGES - 1) * PER_STAGE>();
     else wait_vmcnt<PER_STAGE>();  // nk == 2: stages 0 and 1 issued
     barrier_after_lds_reads();     // stage 0 and the scale table landed in every wave
-    scale_prologue();
-    float snext[2] = {sc_tab[sj[0] * kbp], sc_tab[sj[1] * kbp]};
-    read_half(0, 0, ah[0], bh[0]);
+    float snext[2] = {1.0f, 1.0f};
+    if constexpr (!C::MX4) {
+        scale_prologue();
+        snext[0] = sc_tab[sj[0] * kbp];
+        snext[1] = sc_tab[sj[1] * kbp];
+    }
+    read_half(0, 0, ah[0], bh[0], 0);
     const float one[2] = {1.0f, 1.0f};
     for (int kb = 0; kb < kblocks; ++kb) {
         const int kc = 2 * kb;
-        float rr[2];
-        enter_block(snext, rr);
-        const int kn = kb + 1 < kblocks ? kb + 1 : kb;
-        snext[0] = sc_tab[sj[0] * kbp + kn];
-        snext[1] = sc_tab[sj[1] * kbp + kn];
+        float rr[2] = {1.0f, 1.0f};
+        if constexpr (!C::MX4) {
+            enter_block(snext, rr);
+            const int kn = kb + 1 < kblocks ? kb + 1 : kb;
+            snext[0] = sc_tab[sj[0] * kbp + kn];
+            snext[1] = sc_tab[sj[1] * kbp + kn];
+        }
 
         // the reads of the second half go out after the first sub-step's MFMAs,
         // whose operands were read a whole half earlier
         mma_sub(ah[0], bh[0], 0, true, rr);
         __builtin_amdgcn_sched_barrier(0);
-        read_half(kc % C::STAGES, 1, ah[1], bh[1]);
+        read_half(kc % C::STAGES, 1, ah[1], bh[1], 0);
         __builtin_amdgcn_sched_barrier(0);
         mma_sub(ah[0], bh[0], 1, false, one);
         __builtin_amdgcn_sched_barrier(0);
-        next_step(kc);
+        next_step(kc, 1);
         __builtin_amdgcn_sched_barrier(0);
         mma_sub(ah[1], bh[1], 0, false, one);
         mma_sub(ah[1], bh[1], 1, false, one);
@@ -572,11 +676,11 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
 
         mma_sub(ah[0], bh[0], 0, false, one);
         __builtin_amdgcn_sched_barrier(0);
-        read_half((kc + 1) % C::STAGES, 1, ah[1], bh[1]);
+        read_half((kc + 1) % C::STAGES, 1, ah[1], bh[1], 1);
         __builtin_amdgcn_sched_barrier(0);
         mma_sub(ah[0], bh[0], 1, false, one);
         __builtin_amdgcn_sched_barrier(0);
-        next_step(kc + 1);
+        next_step(kc + 1, 0);
         __builtin_amdgcn_sched_barrier(0);
         mma_sub(ah[1], bh[1], 0, false, one);
         mma_sub(ah[1], bh[1], 1, false, one);
@@ -693,7 +797,6 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
         // covering a row's 128 columns (256 + 16 contiguous bytes).
         static_assert(!C::M16 && C::MS == 32 && C::WCOLS == 128 && C::MT * 32 == C::WROWS,
                       "down epilogue: 64 x 128 wave tiles of 32 x 32 MFMAs");
-        static_assert(C::WAVES * 32 * 128 * 4 <= C::STAGES * C::STAGE, "slabs fit the stages");
         __syncthreads();  // every wave is done reading the K stages
         float* slab = reinterpret_cast<float*>(smem) + wave * (32 * 128);
         uint8_t* ybytes = reinterpret_cast<uint8_t*>(ybuf);
@@ -740,7 +843,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
     constexpr int OUTC = MODE == PF_GATEUP ? C::WCOLS / 2 : C::WCOLS;
     constexpr int LPR = OUTC / 8;              // lanes per row
     constexpr int RPS = MOE_WAVE / LPR;        // rows per store step
-    static_assert(C::WAVES * C::WROWS * OUTC * 2 <= C::STAGES * C::STAGE, "slabs fit the stages");
+    static_assert(C::WAVES * C::WROWS * OUTC * 2 == pf_epilogue_lds<MODE, C>(), "slab size");
     __syncthreads();  // every wave is done reading the K stages
     uint16_t* slab = reinterpret_cast<uint16_t*>(smem) + wave * (C::WROWS * OUTC);
     const int ocol = C::M16 ? l16 : ln;  // the lane's column in an MFMA tile
@@ -787,7 +890,7 @@ static inline int K_of(int H, int I) { return MODE == PF_DOWN ? I : H; }
 
 template <int MODE, int LAYOUT, class C>
 static int launch_pf(const uint16_t* x, const uint16_t* abuf_in, const uint8_t* wexp,
-                     const float* sexp, const uint8_t* wsh, const float* ssh, const Plan& plan,
+                     const void* sexp, const uint8_t* wsh, const void* ssh, const Plan& plan,
                      int T, int H, int I, int E, int k, int has_shared, uint16_t* abuf_out,
                      float* ybuf, hipStream_t stream, const float* xscale = nullptr) {
     const int nblk = MODE == PF_GATEUP ? 2 * I / C::BN : (MODE == PF_UP ? I : H) / C::BN;
@@ -808,10 +911,15 @@ static int launch_pf(const uint16_t* x, const uint16_t* abuf_in, const uint8_t* 
         return MOE_EUNSUPPORTED;
     }
     const size_t kbp = ((size_t)K_of<MODE>(H, I) / 128 + 63) / 64 * 64;
-    const size_t lds = (size_t)C::STAGES * C::STAGE + (size_t)(C::BN / 128) * kbp * 4;
-    const char* pname = MODE == PF_DOWN ? "prefill_down"
-                        : MODE == PF_UP ? (C::A8 ? "prefill_up_relu2_a8" : "prefill_up_relu2")
-                                        : (C::A8 ? "prefill_gateup_swiglu_a8" : "prefill_gateup_swiglu");
+    // stages, the fp32 scale table (MX4: none) and at least the epilogue's slabs
+    const size_t lds = std::max((size_t)C::STAGES * C::STAGE + (C::MX4 ? 0 : (size_t)(C::BN / 128) * kbp * 4),
+                                (size_t)pf_epilogue_lds<MODE, C>());
+    const char* pname =
+        MODE == PF_DOWN ? (C::MX4 ? "prefill_down_mxfp4" : "prefill_down")
+        : MODE == PF_UP ? (C::A8 ? "prefill_up_relu2_a8" : C::MX4 ? "prefill_up_relu2_mxfp4" : "prefill_up_relu2")
+                        : (C::A8    ? "prefill_gateup_swiglu_a8"
+                           : C::MX4 ? "prefill_gateup_swiglu_mxfp4"
+                                    : "prefill_gateup_swiglu");
     prof_begin(pname, stream);
     prefill_gemm_kernel<MODE, LAYOUT, C><<<(unsigned)grid, C::THREADS, lds, stream>>>(
         x, abuf_in, wexp, sexp, wsh, ssh, plan, T, H, I, k, nblk, (int)max_tiles, abuf_out, ybuf,
@@ -822,15 +930,30 @@ static int launch_pf(const uint16_t* x, const uint16_t* abuf_in, const uint8_t* 
 }
 
 template <int LAYOUT>
-static int launch_prefill_c(const uint16_t* x, const uint8_t* w13, const float* w13s,
-                            const uint8_t* w2, const float* w2s, const SharedW& sh,
+static int launch_prefill_c(const uint16_t* x, const uint8_t* w13, const void* w13s,
+                            const uint8_t* w2, const void* w2s, const SharedW& sh,
                             const Plan& plan, int T, int H, int I, int E, int k, uint16_t* abuf,
-                            float* ybuf, int act, const uint8_t* xq, const float* xs,
+                            float* ybuf, int act, const uint8_t* xq, const float* xs, bool mx4,
                             hipStream_t stream) {
     const int hs = sh.w13 != nullptr;
     int rc;
-    const float* ss = static_cast<const float*>(sh.w13_scale);
+    const void* ss = sh.w13_scale;
     const bool narrow = act == ACT_RELU2 && I % 256 != 0;  // (I % 128 == 0)
+    if (mx4) {  // MXFP4 weights, bf16 activations
+        if (act != ACT_RELU2)
+            rc = launch_pf<PF_GATEUP, LAYOUT, PfGateUpMx>(x, nullptr, w13, w13s, sh.w13, ss, plan, T, H, I, E,
+                                                          k, hs, abuf, ybuf, stream);
+        else if (narrow)
+            rc = launch_pf<PF_UP, LAYOUT, PfUpNarrowMx>(x, nullptr, w13, w13s, sh.w13, ss, plan, T, H, I, E, k,
+                                                        hs, abuf, ybuf, stream);
+        else
+            rc = launch_pf<PF_UP, LAYOUT, PfGateUpMx>(x, nullptr, w13, w13s, sh.w13, ss, plan, T, H, I, E, k,
+                                                      hs, abuf, ybuf, stream);
+        if (rc == MOE_OK)
+            rc = launch_pf<PF_DOWN, LAYOUT, PfDownMx>(x, abuf, w2, w2s, sh.w2, sh.w2_scale, plan, T, H, I, E, k,
+                                                      hs, abuf, ybuf, stream);
+        return rc;
+    }
     if (xq) {  // E4M3 activations with per-token scales: the fp8 x fp8 MFMA
         const uint16_t* xa = reinterpret_cast<const uint16_t*>(xq);
         if (act != ACT_RELU2)
@@ -854,8 +977,8 @@ static int launch_prefill_c(const uint16_t* x, const uint8_t* w13, const float* 
                                                     abuf, ybuf, stream);
     }
     if (rc == MOE_OK)
-        rc = launch_pf<PF_DOWN, LAYOUT, PfDown>(x, abuf, w2, w2s, sh.w2, static_cast<const float*>(sh.w2_scale), plan, T, H, I,
-                                                E, k, hs, abuf, ybuf, stream);
+        rc = launch_pf<PF_DOWN, LAYOUT, PfDown>(x, abuf, w2, w2s, sh.w2, sh.w2_scale, plan, T, H, I, E, k, hs,
+                                                abuf, ybuf, stream);
     return rc;
 }
 
@@ -880,10 +1003,14 @@ int prefill_check(int T, int H, int I, int E, int k, int has_shared, int act) {
     return MOE_OK;
 }
 
-int launch_prefill_ffn(int layout, const uint16_t* x, const uint8_t* w13, const float* w13s,
-                       const uint8_t* w2, const float* w2s, const SharedW& sh, const Plan& plan,
+int launch_prefill_ffn(int layout, const uint16_t* x, const uint8_t* w13, const void* w13s,
+                       const uint8_t* w2, const void* w2s, const SharedW& sh, const Plan& plan,
                        int T, int H, int I, int E, int k, uint16_t* abuf, float* ybuf,
-                       int act, const uint8_t* xq, const float* xs, hipStream_t stream) {
+                       int act, const uint8_t* xq, const float* xs, int wfmt, hipStream_t stream) {
+    if (wfmt == WFMT_MXFP4 && xq) {
+        set_error("prefill variant: MXFP4 weights multiply bf16 activations");
+        return MOE_EUNSUPPORTED;
+    }
     if (!prefill_supported(H, I, act)) {
         set_error("prefill variant needs H %% 256 == 0, %s and H, I <= 65536 (got H=%d, I=%d)",
                   act == ACT_RELU2 ? "I % 128 == 0" : "2I % 256 == 0", H, I);
@@ -895,9 +1022,9 @@ int launch_prefill_ffn(int layout, const uint16_t* x, const uint8_t* w13, const 
     }
     if (layout == LAYOUT_TILED)
         return launch_prefill_c<LAYOUT_TILED>(x, w13, w13s, w2, w2s, sh, plan, T, H, I, E, k, abuf,
-                                              ybuf, act, xq, xs, stream);
+                                              ybuf, act, xq, xs, wfmt == WFMT_MXFP4, stream);
     return launch_prefill_c<LAYOUT_ROWMAJOR>(x, w13, w13s, w2, w2s, sh, plan, T, H, I, E, k, abuf,
-                                             ybuf, act, xq, xs, stream);
+                                             ybuf, act, xq, xs, wfmt == WFMT_MXFP4, stream);
 }
 
 }  // namespace moe

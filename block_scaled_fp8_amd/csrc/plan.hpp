@@ -76,11 +76,13 @@ int launch_decode_ffn(int layout, const uint16_t* x, const uint8_t* w13, const f
 // Writes y (without the affinity) of every route at its sorted row of ybuf,
 // in a block floating-point form: 16-bit mantissas at byte 2*col and one
 // exponent byte per run of 8 columns at byte 2*H + col/8, row stride
-// 2*H + H/8 bytes (common.hpp, bfp16x8_encode).
-int launch_prefill_ffn(int layout, const uint16_t* x, const uint8_t* w13, const float* w13s,
-                       const uint8_t* w2, const float* w2s, const SharedW& sh, const Plan& plan,
+// 2*H + H/8 bytes (common.hpp, bfp16x8_encode).  Scales are fp32 128x128
+// blocks, or (wfmt WFMT_MXFP4, bf16 activations only: xq NULL) E8M0 bytes,
+// 4-byte aligned.
+int launch_prefill_ffn(int layout, const uint16_t* x, const uint8_t* w13, const void* w13s,
+                       const uint8_t* w2, const void* w2s, const SharedW& sh, const Plan& plan,
                        int T, int H, int I, int E, int k, uint16_t* abuf, float* ybuf, int act,
-                       const uint8_t* xq, const float* xs, hipStream_t stream);
+                       const uint8_t* xq, const float* xs, int wfmt, hipStream_t stream);
 // Per-token E4M3 quantisation of x [T, H] bf16 -> codes [T, H], scales [T] (quant.hip).
 int launch_quant_rows_e4m3(const uint16_t* x, int T, int H, uint8_t* xq, float* xs,
                            hipStream_t stream);

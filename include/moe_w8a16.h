@@ -352,19 +352,23 @@ typedef struct {
  *   weight_layout  MOE_LAYOUT_TILED: the code bytes packed by moe_pack_w8
  *              (rows, cols = K/2) and the scales by moe_pack_mx_scales
  *              (rows, cols = K/32); MOE_LAYOUT_ROWMAJOR: both as above
- * Everything else as moe_fused_w8a16_ex; the workspace is that of
- * MOE_VARIANT_DECODE (moe_fused_workspace_bytes).  The weights are streamed
- * by the weight-streaming decode kernel at every batch size (one workgroup
- * per active expert up to 4096 routes, above that one per 32-row tile of an
- * expert's sorted routes): MOE_VARIANT_AUTO and MOE_VARIANT_DECODE run it,
- * the prefill variants give
- * MOE_EUNSUPPORTED, and so do shapes whose 16- or 32-row activation pass does
- * not fit 64 KB of LDS (16 or 32 * (I + 8) * 2 bytes, plus 4 bytes a route
- * when T*k <= 4096) or with T*H >= 2^32.  The E8M0 scale is applied exactly
- * in the conversion to bf16 (every E2M1 value times a power of two is a
- * bf16 value while it stays in bf16's normal range; smaller products are
- * flushed to zero), products are summed in fp32 and the SwiGLU output is
- * rounded to bf16 before the down GEMM.  Scales need no alignment.
+ * Everything else as moe_fused_w8a16_ex, including the workspace
+ * (moe_fused_workspace_bytes with the same variant) and AUTO's choice:
+ *   MOE_VARIANT_DECODE   the weight-streaming kernel (one workgroup per
+ *              active expert up to 4096 routes, above that one per 16- or
+ *              32-row tile of an expert's sorted routes); shapes whose
+ *              activation pass does not fit 64 KB of LDS (16 or 32 *
+ *              (I + 8) * 2 bytes, plus 4 bytes a route when T*k <= 4096) or
+ *              with T*H >= 2^32 give MOE_EUNSUPPORTED
+ *   MOE_VARIANT_PREFILL  the grouped GEMMs (same shape limits as the E4M3FN
+ *              weights); the E8M0 arrays (routed and shared) must then be
+ *              4-byte aligned, else MOE_EINVAL -- AUTO takes the decode
+ *              kernels for unaligned scale arrays instead
+ *   MOE_VARIANT_PREFILL_A8  MOE_EUNSUPPORTED (bf16 activations only)
+ * The E8M0 scale is applied exactly in the conversion to bf16 (every E2M1
+ * value times a power of two is a bf16 value while it stays in bf16's normal
+ * range; smaller products are flushed to zero), products are summed in fp32
+ * and the SwiGLU output is rounded to bf16 before the down GEMM.
  */
 int moe_fused_mxfp4(const void* x,
                     const uint8_t* w13, const uint8_t* w13_scale,

@@ -50,15 +50,20 @@ def _run(c, ids, aff, layout, activation, variant="auto", shared=True, status=No
                                status=status)
 
 
+# (AUTO: the decode kernels up to 16 routes per expert, the grouped GEMMs
+# above; the large workloads also run the decode kernels' row-tile form)
+@pytest.mark.parametrize("variant", ["auto", "decode"])
 @pytest.mark.parametrize("layout", ["rowmajor", "tiled"])
 @pytest.mark.parametrize("activation", ["swiglu", "relu2"])
 @pytest.mark.parametrize("name", synth.CONFIG_ORDER)
-def test_mxfp4_parity(name, activation, layout):
+def test_mxfp4_parity(name, activation, layout, variant):
     c = _case(name, activation)
     cfg = c["cfg"]
+    if variant == "decode" and cfg.routes <= 16 * cfg.E:
+        pytest.skip("AUTO already runs the decode kernels here")
     ids, aff = binding.route(c["logits"], cfg.k)
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
-    out = _run(c, ids, aff, layout, activation, status=status)
+    out = _run(c, ids, aff, layout, activation, variant=variant, status=status)
     torch.cuda.synchronize()
     assert int(status.item()) == 0
     ref_ids, ref_aff = oracle.route_softmax_topk(np_(c["logits"]), cfg.k)
@@ -67,11 +72,11 @@ def test_mxfp4_parity(name, activation, layout):
     if activation not in _oracle:
         _oracle[activation] = oracle_rows(c, ref_ids, ref_aff, rows)
     assert_out_close(np_(out)[rows], _oracle[activation],
-                     what=f"mxfp4 {name}/{activation}/{layout} ({len(rows)} rows)")
+                     what=f"mxfp4 {name}/{activation}/{layout}/{variant} ({len(rows)} rows)")
 
 
-# odd chunk counts (H/128 = 3, I/128 = 1 or 3), token boundaries and both
-# self-routed (T*k <= 4096) and sorted (T*k > 4096) forms
+# the decode kernels: odd chunk counts (H/128 = 3, I/128 = 1 or 3), token
+# boundaries and both self-routed (T*k <= 4096) and sorted (T*k > 4096) forms
 @pytest.mark.parametrize("layout", ["rowmajor", "tiled"])
 @pytest.mark.parametrize("T,H,I,E,k", [(1, 384, 128, 16, 4), (17, 384, 384, 16, 4),
                                        (37, 256, 128, 8, 2), (130, 384, 256, 130, 8),
@@ -82,14 +87,16 @@ def test_mxfp4_shapes(T, H, I, E, k, layout):
     g = tiled_case(c) if layout == "tiled" else c
     ids, aff = binding.route(c["logits"], k)
     out = binding.fused_w8a16(g["x"], g["w13"], g["w13_scale"], g["w2"], g["w2_scale"], ids, aff,
-                              shared=g["shared"], layout=layout, weight_format="mxfp4")
+                              shared=g["shared"], layout=layout, weight_format="mxfp4",
+                              variant="decode")
     torch.cuda.synchronize()
     ref_ids, ref_aff = oracle.route_softmax_topk(np_(c["logits"]), k)
     ref = oracle_rows(c, ref_ids, ref_aff, np.arange(T))
     assert_out_close(np_(out), ref, what=f"mxfp4 T={T} H={H} I={I} E={E} k={k}/{layout}")
 
 
-def test_mxfp4_scale_bytes_at_the_ends_and_zero_affinities():
+@pytest.mark.parametrize("variant", ["decode", "prefill"])
+def test_mxfp4_scale_bytes_at_the_ends_and_zero_affinities(variant):
     """Scale bytes 1 (2^-126) and 140 (2^13) on some blocks, the rest as drawn;
     outputs stay finite and match the oracle; zero affinities give exactly 0."""
     cfg = synth.MoeConfig("mxe", T=24, H=256, I=256, E=8, k=2)
@@ -99,17 +106,72 @@ def test_mxfp4_scale_bytes_at_the_ends_and_zero_affinities():
     c["w13_scale"][3, 0, 0] = 140   # one gate block of expert 3: 2^13 instead of about 2^-9
     ids, aff = binding.route(c["logits"], cfg.k)
     out = binding.fused_w8a16(c["x"], c["w13"], c["w13_scale"], c["w2"], c["w2_scale"], ids, aff,
-                              weight_format="mxfp4")
+                              weight_format="mxfp4", variant=variant)
     torch.cuda.synchronize()
     ref_ids, ref_aff = oracle.route_softmax_topk(np_(c["logits"]), cfg.k)
     ref = oracle_rows(c, ref_ids, ref_aff, np.arange(cfg.T))
     assert np.all(np.isfinite(ref))
-    assert_out_close(np_(out), ref, what="mxfp4 scale bytes 1 and 140")
+    assert_out_close(np_(out), ref, what=f"mxfp4 {variant} scale bytes 1 and 140")
     zero = torch.zeros_like(aff)
     out0 = binding.fused_w8a16(c["x"], c["w13"], c["w13_scale"], c["w2"], c["w2_scale"], ids,
-                               zero, weight_format="mxfp4")
+                               zero, weight_format="mxfp4", variant=variant)
     torch.cuda.synchronize()
     assert int(torch.count_nonzero(out0).item()) == 0
+
+
+# The grouped-GEMM (prefill) variant on MXFP4 weights: several 128-row tiles
+# with ragged tails, down K = 128 (a single 128-wide chunk), 3 column blocks
+# of 256, relu^2 up projections of an odd number of 128-column blocks (I = 384)
+# and the shared expert's rows.
+@pytest.mark.parametrize("layout", ["rowmajor", "tiled"])
+@pytest.mark.parametrize("activation", ["swiglu", "relu2"])
+@pytest.mark.parametrize("T,H,I,E,k", [(300, 512, 256, 8, 2), (257, 256, 384, 16, 4),
+                                       (129, 768, 128, 4, 1)])
+def test_mxfp4_prefill_shapes(T, H, I, E, k, activation, layout):
+    cfg = synth.MoeConfig("mxp", T=T, H=H, I=I, E=E, k=k, shared=True)
+    c = gpu_case(cfg, seed=T + I, activation=activation, weight_format="mxfp4")
+    g = tiled_case(c) if layout == "tiled" else c
+    ids, aff = binding.route(c["logits"], k)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = binding.fused_w8a16(g["x"], g["w13"], g["w13_scale"], g["w2"], g["w2_scale"], ids, aff,
+                              shared=g["shared"], variant="prefill", layout=layout,
+                              activation=activation, weight_format="mxfp4", status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    ref_ids, ref_aff = oracle.route_softmax_topk(np_(c["logits"]), k)
+    ref = oracle_rows(c, ref_ids, ref_aff, np.arange(T))
+    assert_out_close(np_(out), ref,
+                     what=f"mxfp4 prefill T={T} H={H} I={I} E={E} k={k}/{activation}/{layout}")
+
+
+def test_mxfp4_unaligned_scales_take_the_decode_kernels():
+    """The prefill GEMMs stage E8M0 scales 4 bytes at a time: on scale arrays
+    that are not 4-byte aligned AUTO runs the decode kernels (same result),
+    and an explicit prefill variant is refused."""
+    cfg = synth.MoeConfig("mxu", T=300, H=256, I=256, E=8, k=2)
+    c = gpu_case(cfg, seed=9, weight_format="mxfp4")
+
+    def shifted(t):
+        buf = torch.empty(t.numel() + 1, dtype=torch.uint8, device=t.device)
+        v = buf[1:].view(t.shape)
+        v.copy_(t)
+        return v
+
+    s13, s2 = shifted(c["w13_scale"]), shifted(c["w2_scale"])
+    assert s13.data_ptr() % 4 != 0
+    ids, aff = binding.route(c["logits"], cfg.k)
+    out = binding.fused_w8a16(c["x"], c["w13"], s13, c["w2"], s2, ids, aff, weight_format="mxfp4")
+    ref_out = binding.fused_w8a16(c["x"], c["w13"], c["w13_scale"], c["w2"], c["w2_scale"], ids,
+                                  aff, weight_format="mxfp4", variant="decode")
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref_out)
+    ref_ids, ref_aff = oracle.route_softmax_topk(np_(c["logits"]), cfg.k)
+    assert_out_close(np_(out), oracle_rows(c, ref_ids, ref_aff, np.arange(cfg.T)),
+                     what="mxfp4 unaligned scales, auto")
+    with pytest.raises(binding.MoeError) as ei:
+        binding.fused_w8a16(c["x"], c["w13"], s13, c["w2"], s2, ids, aff, variant="prefill",
+                            weight_format="mxfp4")
+    assert ei.value.code == binding.MOE_EINVAL
 
 
 @pytest.mark.parametrize("shape", [(1, 16, 4), (3, 256, 64), (2, 1024, 16)])
@@ -128,31 +190,32 @@ def test_pack_mx_scales_matches_reference(shape):
     assert np.array_equal(got.reshape(-1), ref)
 
 
-def test_mxfp4_prefill_variants_are_refused():
+def test_mxfp4_prefill_a8_is_refused():
     cfg = synth.MoeConfig("mxp", T=8, H=256, I=256, E=8, k=2)
     c = gpu_case(cfg, seed=6, weight_format="mxfp4")
     ids, aff = binding.route(c["logits"], cfg.k)
-    for v in ("prefill", "prefill_a8"):
-        with pytest.raises(binding.MoeError) as ei:
-            binding.fused_w8a16(c["x"], c["w13"], c["w13_scale"], c["w2"], c["w2_scale"], ids,
-                                aff, variant=v, weight_format="mxfp4")
-        assert ei.value.code == binding.MOE_EUNSUPPORTED
+    with pytest.raises(binding.MoeError) as ei:
+        binding.fused_w8a16(c["x"], c["w13"], c["w13_scale"], c["w2"], c["w2_scale"], ids,
+                            aff, variant="prefill_a8", weight_format="mxfp4")
+    assert ei.value.code == binding.MOE_EUNSUPPORTED
 
 
-def test_mxfp4_is_deterministic_and_graph_replays():
+@pytest.mark.parametrize("variant", ["decode", "prefill"])
+def test_mxfp4_is_deterministic_and_graph_replays(variant):
     cfg = synth.MoeConfig("mxg", T=64, H=512, I=256, E=128, k=4, shared=True)
     c = gpu_case(cfg, seed=7, weight_format="mxfp4")
     ids, aff = binding.route(c["logits"], cfg.k)
-    a = _run(c, ids, aff, "rowmajor", "swiglu")
-    b = _run(c, ids, aff, "rowmajor", "swiglu")
+    a = _run(c, ids, aff, "rowmajor", "swiglu", variant=variant)
+    b = _run(c, ids, aff, "rowmajor", "swiglu", variant=variant)
     assert torch.equal(a, b)
     ws = torch.empty(binding.fused_workspace_bytes(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, True,
-                                                   "decode"), dtype=torch.uint8, device="cuda")
+                                                   variant), dtype=torch.uint8, device="cuda")
     out = torch.empty_like(a)
 
     def step():
         binding.fused_w8a16(c["x"], c["w13"], c["w13_scale"], c["w2"], c["w2_scale"], ids, aff,
-                            shared=c["shared"], out=out, ws=ws, weight_format="mxfp4")
+                            shared=c["shared"], out=out, ws=ws, weight_format="mxfp4",
+                            variant=variant)
 
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
