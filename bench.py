@@ -745,6 +745,14 @@ def main():
             # the wide geometry of the MXFP4 prefill figures on the pages
             result["mxfp4"].append(fused_variant_bench(synth.CONFIGS["prefill16k_wide"], dev, 1,
                                                        args.seed, weight_format="mxfp4"))
+        if args.prefill_workload and not args.no_a8:
+            # x quantised to E4M3 per token: gate/up as E4M3 x E2M1 on the FP8 MFMA
+            for wname in dict.fromkeys([args.prefill_workload] +
+                                       ([] if args.no_extra_workloads else ["prefill16k_wide"])):
+                result["mxfp4"].append(fused_variant_bench(synth.CONFIGS[wname], dev,
+                                                           2 if wname == "prefill8k_skew" else 1,
+                                                           args.seed, variant="prefill_a8",
+                                                           weight_format="mxfp4"))
     if args.prefill_workload and not args.no_a8:
         result["prefill_a8"] = fused_variant_bench(synth.CONFIGS[args.prefill_workload], dev, 2,
                                                    args.seed, variant="prefill_a8")

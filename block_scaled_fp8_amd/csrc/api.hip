@@ -266,10 +266,6 @@ static int fused_impl(const char* who, const void* x, const uint8_t* w13, const 
         set_error("unknown variant %d", variant);
         return MOE_EINVAL;
     }
-    if (mx4 && variant == MOE_VARIANT_PREFILL_A8) {
-        set_error("%s: MXFP4 weights multiply bf16 activations (no fp8-activation variant)", who);
-        return MOE_EUNSUPPORTED;
-    }
     if (T == 0) return MOE_OK;
     if (!x || !w13 || !w13_scale || !w2 || !w2_scale || !ids || !aff || !out) {
         set_error("%s: x, weights, scales, ids, aff and out must be non-NULL", who);
@@ -307,8 +303,8 @@ static int fused_impl(const char* who, const void* x, const uint8_t* w13, const 
     const bool mx_sc4 = !mx4 || ((((uintptr_t)w13_scale | (uintptr_t)w2_scale |
                                   (shared ? (uintptr_t)shared->w13_scale | (uintptr_t)shared->w2_scale : 0)) &
                                  3) == 0);
-    if (mx4 && variant == MOE_VARIANT_PREFILL && !mx_sc4) {
-        set_error("%s: the prefill variant needs 4-byte aligned MXFP4 scale arrays", who);
+    if (mx4 && (variant == MOE_VARIANT_PREFILL || fp8_x) && !mx_sc4) {
+        set_error("%s: the prefill variants need 4-byte aligned MXFP4 scale arrays", who);
         return MOE_EINVAL;
     }
     const int auto_pick = variant == MOE_VARIANT_AUTO;

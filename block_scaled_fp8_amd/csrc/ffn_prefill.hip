@@ -85,9 +85,10 @@ struct PfCfg {
     static_assert(!(M16 && A8), "the fp8 path uses 32x32 tiles");
     // MX4: MXFP4 weights (E2M1 codes, two a byte, one E8M0 scale per 32
     // elements of a row); a stage holds 32 code bytes of each weight row and
-    // the scale bytes of the 128-wide K chunk the step lies in
+    // the scale bytes of the 128-wide K chunk the step lies in.  With A8 the
+    // product is E4M3 x E2M1 on the scaled MFMA, the lane's E8M0 byte its B
+    // scale.
     static constexpr bool MX4 = MX4_ != 0;
-    static_assert(!(MX4 && A8), "MXFP4 weights multiply bf16 activations");
     static_assert(!(MX4 && M16), "MXFP4 weights use 32x32 tiles");
     static constexpr int MS = M16 ? 16 : 32;  // rows = columns of one MFMA tile
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
@@ -137,6 +138,8 @@ using PfUpNarrowA8 = PfCfg<128, 128, 2, 1, 3, 2, 0, 1>;
 using PfGateUpMx = PfCfg<128, 256, 2, 2, 2, 2, 0, 0, 1>;
 using PfDownMx = PfCfg<128, 256, 2, 2, 2, 2, 0, 0, 1>;
 using PfUpNarrowMx = PfCfg<128, 128, 2, 1, 2, 2, 0, 0, 1>;
+using PfGateUpMxA8 = PfCfg<128, 256, 2, 2, 3, 2, 0, 1, 1>;
+using PfUpNarrowMxA8 = PfCfg<128, 128, 2, 1, 3, 2, 0, 1, 1>;
 constexpr int PF_BM = 128;
 
 int prefill_tile_m() { return PF_BM; }
@@ -694,6 +697,13 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
         //      for both operands alike, so each product sums exactly over K.  The
         //      weight operand's pieces sit where the 32x32 bf16 path reads them
         //      (b_off, b_step); the activation rows are 64 bytes.
+        //      MX4: the lane's 32 K of its weight row are its 16 E2M1 code
+        //      bytes, one scale block, whose E8M0 byte is the MFMA's B scale
+        //      for the lane.  With an E2M1 B operand the MFMA pairs B lane half
+        //      h's codes 0-15 with A lane half 0's bytes 16h .. 16h + 15 and
+        //      codes 16-31 with A lane half 1's (measured on gfx950 with
+        //      one-hot operands), so A lane half h carries the 16-K pieces h
+        //      and h + 2 of the step.
         auto kloop_a8 = [&](auto mta_c) {
             constexpr int MTA = decltype(mta_c)::value;
             const int r32 = lane & 31, h8 = lane >> 5;
@@ -701,22 +711,39 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
     #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 const int row = wm * C::WROWS + r32;
-                a8_off[j] = row * 64 + (((2 * h8 + j) ^ ((row >> 2) & 3)) * 16);
+                const int piece = C::MX4 ? h8 + 2 * j : 2 * h8 + j;
+                a8_off[j] = row * 64 + ((piece ^ ((row >> 2) & 3)) * 16);
             }
-            auto stage_mma = [&](int stage, bool rescale, const float (&rr)[2]) {
+            // (par: the stage's position in its 128-K chunk, for the MX4 scales)
+            auto stage_mma = [&](int stage, bool rescale, const float (&rr)[2], int par) {
                 const char* st = smem + stage * C::STAGE;
                 i32x8 av[C::MT], bv[C::NT];
+                int bs[C::NT];  // MX4: the lane's E8M0 byte of each column tile
     #pragma unroll
                 for (int mt = 0; mt < MTA; ++mt)
                     av[mt] = cat_i32x8(*reinterpret_cast<const u32x4*>(st + a8_off[0] + mt * 32 * 64),
                                        *reinterpret_cast<const u32x4*>(st + a8_off[1] + mt * 32 * 64));
                 if (MTA > 0)
     #pragma unroll
-                    for (int nt = 0; nt < C::NT; ++nt)
-                        bv[nt] = cat_i32x8(*reinterpret_cast<const u32x4*>(st + b_off + b_step(nt)),
-                                           *reinterpret_cast<const u32x4*>(st + b_off + b_step(nt) + 256));
+                    for (int nt = 0; nt < C::NT; ++nt) {
+                        if constexpr (C::MX4) {
+                            bv[nt] = cat_i32x8(*reinterpret_cast<const u32x4*>(st + b_off + b_step(nt)),
+                                               u32x4{0u, 0u, 0u, 0u});
+                            bs[nt] = *reinterpret_cast<const uint8_t*>(st + s_off + par * S_PAR + s_step(nt));
+                        } else {
+                            bv[nt] = cat_i32x8(*reinterpret_cast<const u32x4*>(st + b_off + b_step(nt)),
+                                               *reinterpret_cast<const u32x4*>(st + b_off + b_step(nt) + 256));
+                        }
+                    }
     #pragma unroll
                 for (int nt = 0; nt < C::NT; ++nt) {
+                    if constexpr (C::MX4) {
+    #pragma unroll
+                        for (int mt = 0; mt < MTA; ++mt)
+                            acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                                av[mt], bv[nt], acc[mt][nt], 0, 4, 0, 127, 0, bs[nt]);
+                        continue;
+                    }
                     const int gi = PAIRED ? nt / (C::NT / 2) : 0;
                     if (zs[gi]) continue;  // a zero block scale: nothing to add
                     const float f = rr[gi];
@@ -747,19 +774,25 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
             if (nk >= C::STAGES) wait_vmcnt<(C::STAGES - 1) * PER_STAGE>();
             else wait_vmcnt<0>();
             barrier_after_lds_reads();  // ... in every wave
-            scale_prologue();
-            float snext[2] = {sc_tab[sj[0] * kbp], sc_tab[sj[1] * kbp]};
+            float snext[2] = {1.0f, 1.0f};
+            if constexpr (!C::MX4) {
+                scale_prologue();
+                snext[0] = sc_tab[sj[0] * kbp];
+                snext[1] = sc_tab[sj[1] * kbp];
+            }
             const float one[2] = {1.0f, 1.0f};
             for (int kb = 0; kb < kblocks; ++kb) {
                 const int kc = 2 * kb;
-                float rr[2];
-                enter_block(snext, rr);
-                const int kn = kb + 1 < kblocks ? kb + 1 : kb;
-                snext[0] = sc_tab[sj[0] * kbp + kn];
-                snext[1] = sc_tab[sj[1] * kbp + kn];
-                stage_mma(kc % C::STAGES, true, rr);
+                float rr[2] = {1.0f, 1.0f};
+                if constexpr (!C::MX4) {
+                    enter_block(snext, rr);
+                    const int kn = kb + 1 < kblocks ? kb + 1 : kb;
+                    snext[0] = sc_tab[sj[0] * kbp + kn];
+                    snext[1] = sc_tab[sj[1] * kbp + kn];
+                }
+                stage_mma(kc % C::STAGES, true, rr, 0);
                 next_stage(kc);
-                stage_mma((kc + 1) % C::STAGES, false, one);
+                stage_mma((kc + 1) % C::STAGES, false, one, 1);
                 next_stage(kc + 1);
             }
         };
@@ -916,10 +949,11 @@ static int launch_pf(const uint16_t* x, const uint16_t* abuf_in, const uint8_t* 
                                 (size_t)pf_epilogue_lds<MODE, C>());
     const char* pname =
         MODE == PF_DOWN ? (C::MX4 ? "prefill_down_mxfp4" : "prefill_down")
-        : MODE == PF_UP ? (C::A8 ? "prefill_up_relu2_a8" : C::MX4 ? "prefill_up_relu2_mxfp4" : "prefill_up_relu2")
-                        : (C::A8    ? "prefill_gateup_swiglu_a8"
-                           : C::MX4 ? "prefill_gateup_swiglu_mxfp4"
-                                    : "prefill_gateup_swiglu");
+        : MODE == PF_UP
+            ? (C::A8 ? (C::MX4 ? "prefill_up_relu2_mxfp4_a8" : "prefill_up_relu2_a8")
+                     : (C::MX4 ? "prefill_up_relu2_mxfp4" : "prefill_up_relu2"))
+            : (C::A8 ? (C::MX4 ? "prefill_gateup_swiglu_mxfp4_a8" : "prefill_gateup_swiglu_a8")
+                     : (C::MX4 ? "prefill_gateup_swiglu_mxfp4" : "prefill_gateup_swiglu"));
     prof_begin(pname, stream);
     prefill_gemm_kernel<MODE, LAYOUT, C><<<(unsigned)grid, C::THREADS, lds, stream>>>(
         x, abuf_in, wexp, sexp, wsh, ssh, plan, T, H, I, k, nblk, (int)max_tiles, abuf_out, ybuf,
@@ -939,6 +973,22 @@ static int launch_prefill_c(const uint16_t* x, const uint8_t* w13, const void* w
     int rc;
     const void* ss = sh.w13_scale;
     const bool narrow = act == ACT_RELU2 && I % 256 != 0;  // (I % 128 == 0)
+    if (mx4 && xq) {  // MXFP4 weights, E4M3 activations: gate/up on the scaled MFMA
+        const uint16_t* xa = reinterpret_cast<const uint16_t*>(xq);
+        if (act != ACT_RELU2)
+            rc = launch_pf<PF_GATEUP, LAYOUT, PfGateUpMxA8>(xa, nullptr, w13, w13s, sh.w13, ss, plan, T, H, I,
+                                                            E, k, hs, abuf, ybuf, stream, xs);
+        else if (narrow)
+            rc = launch_pf<PF_UP, LAYOUT, PfUpNarrowMxA8>(xa, nullptr, w13, w13s, sh.w13, ss, plan, T, H, I, E,
+                                                          k, hs, abuf, ybuf, stream, xs);
+        else
+            rc = launch_pf<PF_UP, LAYOUT, PfGateUpMxA8>(xa, nullptr, w13, w13s, sh.w13, ss, plan, T, H, I, E, k,
+                                                        hs, abuf, ybuf, stream, xs);
+        if (rc == MOE_OK)
+            rc = launch_pf<PF_DOWN, LAYOUT, PfDownMx>(x, abuf, w2, w2s, sh.w2, sh.w2_scale, plan, T, H, I, E, k,
+                                                      hs, abuf, ybuf, stream);
+        return rc;
+    }
     if (mx4) {  // MXFP4 weights, bf16 activations
         if (act != ACT_RELU2)
             rc = launch_pf<PF_GATEUP, LAYOUT, PfGateUpMx>(x, nullptr, w13, w13s, sh.w13, ss, plan, T, H, I, E,
@@ -1007,10 +1057,7 @@ int launch_prefill_ffn(int layout, const uint16_t* x, const uint8_t* w13, const 
                        const uint8_t* w2, const void* w2s, const SharedW& sh, const Plan& plan,
                        int T, int H, int I, int E, int k, uint16_t* abuf, float* ybuf,
                        int act, const uint8_t* xq, const float* xs, int wfmt, hipStream_t stream) {
-    if (wfmt == WFMT_MXFP4 && xq) {
-        set_error("prefill variant: MXFP4 weights multiply bf16 activations");
-        return MOE_EUNSUPPORTED;
-    }
+
     if (!prefill_supported(H, I, act)) {
         set_error("prefill variant needs H %% 256 == 0, %s and H, I <= 65536 (got H=%d, I=%d)",
                   act == ACT_RELU2 ? "I % 128 == 0" : "2I % 256 == 0", H, I);

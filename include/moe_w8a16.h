@@ -364,7 +364,11 @@ typedef struct {
  *              weights); the E8M0 arrays (routed and shared) must then be
  *              4-byte aligned, else MOE_EINVAL -- AUTO takes the decode
  *              kernels for unaligned scale arrays instead
- *   MOE_VARIANT_PREFILL_A8  MOE_EUNSUPPORTED (bf16 activations only)
+ *   MOE_VARIANT_PREFILL_A8  likewise, with x quantised to E4M3 per token as
+ *              for E4M3FN weights; the gate/up (relu^2: up) GEMM multiplies
+ *              E4M3 by E2M1 codes on the scaled FP8 MFMA, each 32-element
+ *              block's E8M0 byte as the MFMA's weight scale, and the down
+ *              GEMM stays bf16 x MXFP4
  * The E8M0 scale is applied exactly in the conversion to bf16 (every E2M1
  * value times a power of two is a bf16 value while it stays in bf16's normal
  * range; smaller products are flushed to zero), products are summed in fp32

@@ -16,7 +16,7 @@ import oracle
 from block_scaled_fp8_amd import binding, synth
 
 from _parity import assert_out_close, gpu_case, np_, oracle_rows, tiled_case
-from test_gpu_parity import check_rows
+from test_gpu_parity import _xhat_rows, check_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -51,16 +51,17 @@ def _run(c, ids, aff, layout, activation, variant="auto", shared=True, status=No
 
 
 # (AUTO: the decode kernels up to 16 routes per expert, the grouped GEMMs
-# above; the large workloads also run the decode kernels' row-tile form)
-@pytest.mark.parametrize("variant", ["auto", "decode"])
+# above; the large workloads also run the decode kernels' row-tile form and
+# the grouped GEMMs with x quantised to E4M3 per token)
+@pytest.mark.parametrize("variant", ["auto", "decode", "prefill_a8"])
 @pytest.mark.parametrize("layout", ["rowmajor", "tiled"])
 @pytest.mark.parametrize("activation", ["swiglu", "relu2"])
 @pytest.mark.parametrize("name", synth.CONFIG_ORDER)
 def test_mxfp4_parity(name, activation, layout, variant):
     c = _case(name, activation)
     cfg = c["cfg"]
-    if variant == "decode" and cfg.routes <= 16 * cfg.E:
-        pytest.skip("AUTO already runs the decode kernels here")
+    if variant != "auto" and cfg.routes <= 16 * cfg.E:
+        pytest.skip("decode-sized batch: AUTO runs the decode kernels")
     ids, aff = binding.route(c["logits"], cfg.k)
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
     out = _run(c, ids, aff, layout, activation, variant=variant, status=status)
@@ -69,9 +70,11 @@ def test_mxfp4_parity(name, activation, layout, variant):
     ref_ids, ref_aff = oracle.route_softmax_topk(np_(c["logits"]), cfg.k)
     assert np.array_equal(np_(ids), ref_ids)
     rows = check_rows(name, cfg, ref_ids)
-    if activation not in _oracle:
-        _oracle[activation] = oracle_rows(c, ref_ids, ref_aff, rows)
-    assert_out_close(np_(out)[rows], _oracle[activation],
+    key = (activation, variant == "prefill_a8")
+    if key not in _oracle:
+        xr = _xhat_rows(c, rows) if variant == "prefill_a8" else None
+        _oracle[key] = oracle_rows(c, ref_ids, ref_aff, rows, xrows=xr)
+    assert_out_close(np_(out)[rows], _oracle[key],
                      what=f"mxfp4 {name}/{activation}/{layout}/{variant} ({len(rows)} rows)")
 
 
@@ -95,7 +98,7 @@ def test_mxfp4_shapes(T, H, I, E, k, layout):
     assert_out_close(np_(out), ref, what=f"mxfp4 T={T} H={H} I={I} E={E} k={k}/{layout}")
 
 
-@pytest.mark.parametrize("variant", ["decode", "prefill"])
+@pytest.mark.parametrize("variant", ["decode", "prefill", "prefill_a8"])
 def test_mxfp4_scale_bytes_at_the_ends_and_zero_affinities(variant):
     """Scale bytes 1 (2^-126) and 140 (2^13) on some blocks, the rest as drawn;
     outputs stay finite and match the oracle; zero affinities give exactly 0."""
@@ -109,7 +112,9 @@ def test_mxfp4_scale_bytes_at_the_ends_and_zero_affinities(variant):
                               weight_format="mxfp4", variant=variant)
     torch.cuda.synchronize()
     ref_ids, ref_aff = oracle.route_softmax_topk(np_(c["logits"]), cfg.k)
-    ref = oracle_rows(c, ref_ids, ref_aff, np.arange(cfg.T))
+    rows = np.arange(cfg.T)
+    xr = _xhat_rows(c, rows) if variant == "prefill_a8" else None
+    ref = oracle_rows(c, ref_ids, ref_aff, rows, xrows=xr)
     assert np.all(np.isfinite(ref))
     assert_out_close(np_(out), ref, what=f"mxfp4 {variant} scale bytes 1 and 140")
     zero = torch.zeros_like(aff)
@@ -168,10 +173,11 @@ def test_mxfp4_unaligned_scales_take_the_decode_kernels():
     ref_ids, ref_aff = oracle.route_softmax_topk(np_(c["logits"]), cfg.k)
     assert_out_close(np_(out), oracle_rows(c, ref_ids, ref_aff, np.arange(cfg.T)),
                      what="mxfp4 unaligned scales, auto")
-    with pytest.raises(binding.MoeError) as ei:
-        binding.fused_w8a16(c["x"], c["w13"], s13, c["w2"], s2, ids, aff, variant="prefill",
-                            weight_format="mxfp4")
-    assert ei.value.code == binding.MOE_EINVAL
+    for v in ("prefill", "prefill_a8"):
+        with pytest.raises(binding.MoeError) as ei:
+            binding.fused_w8a16(c["x"], c["w13"], s13, c["w2"], s2, ids, aff, variant=v,
+                                weight_format="mxfp4")
+        assert ei.value.code == binding.MOE_EINVAL
 
 
 @pytest.mark.parametrize("shape", [(1, 16, 4), (3, 256, 64), (2, 1024, 16)])
@@ -190,17 +196,30 @@ def test_pack_mx_scales_matches_reference(shape):
     assert np.array_equal(got.reshape(-1), ref)
 
 
-def test_mxfp4_prefill_a8_is_refused():
-    cfg = synth.MoeConfig("mxp", T=8, H=256, I=256, E=8, k=2)
-    c = gpu_case(cfg, seed=6, weight_format="mxfp4")
-    ids, aff = binding.route(c["logits"], cfg.k)
-    with pytest.raises(binding.MoeError) as ei:
-        binding.fused_w8a16(c["x"], c["w13"], c["w13_scale"], c["w2"], c["w2_scale"], ids,
-                            aff, variant="prefill_a8", weight_format="mxfp4")
-    assert ei.value.code == binding.MOE_EUNSUPPORTED
+# x quantised to E4M3 per token, gate/up (or up) as E4M3 x E2M1 on the scaled
+# MFMA with the weights' E8M0 bytes as its B scales: against the oracle run on
+# the same quantised rows
+@pytest.mark.parametrize("layout", ["rowmajor", "tiled"])
+@pytest.mark.parametrize("activation", ["swiglu", "relu2"])
+@pytest.mark.parametrize("T,H,I,E,k", [(300, 512, 256, 8, 2), (257, 256, 384, 16, 4),
+                                       (129, 768, 128, 4, 1)])
+def test_mxfp4_prefill_a8_shapes(T, H, I, E, k, activation, layout):
+    cfg = synth.MoeConfig("mxq", T=T, H=H, I=I, E=E, k=k, shared=True)
+    c = gpu_case(cfg, seed=T + I + 1, activation=activation, weight_format="mxfp4")
+    g = tiled_case(c) if layout == "tiled" else c
+    ids, aff = binding.route(c["logits"], k)
+    out = binding.fused_w8a16(g["x"], g["w13"], g["w13_scale"], g["w2"], g["w2_scale"], ids, aff,
+                              shared=g["shared"], variant="prefill_a8", layout=layout,
+                              activation=activation, weight_format="mxfp4")
+    torch.cuda.synchronize()
+    ref_ids, ref_aff = oracle.route_softmax_topk(np_(c["logits"]), k)
+    rows = np.arange(T)
+    ref = oracle_rows(c, ref_ids, ref_aff, rows, xrows=_xhat_rows(c, rows))
+    assert_out_close(np_(out), ref,
+                     what=f"mxfp4 prefill_a8 T={T} H={H} I={I} E={E} k={k}/{activation}/{layout}")
 
 
-@pytest.mark.parametrize("variant", ["decode", "prefill"])
+@pytest.mark.parametrize("variant", ["decode", "prefill", "prefill_a8"])
 def test_mxfp4_is_deterministic_and_graph_replays(variant):
     cfg = synth.MoeConfig("mxg", T=64, H=512, I=256, E=128, k=4, shared=True)
     c = gpu_case(cfg, seed=7, weight_format="mxfp4")
