@@ -110,6 +110,8 @@ int launch_quant_rows_e4m3(const uint16_t* x, int T, int H, uint8_t* xq, float* 
         quant_rows_e4m3_kernel<4><<<grid, block, 0, stream>>>(x, T, H, xq, xs);
     else if (nc <= 512)
         quant_rows_e4m3_kernel<8><<<grid, block, 0, stream>>>(x, T, H, xq, xs);
+    else if (nc <= 1024)
+        quant_rows_e4m3_kernel<16><<<grid, block, 0, stream>>>(x, T, H, xq, xs);
     else
         quant_rows_e4m3_kernel<0><<<grid, block, 0, stream>>>(x, T, H, xq, xs);
     prof_end(stream);

@@ -667,8 +667,8 @@ def test_graph_replay_with_changing_routes(variant):
 
 
 # ------------------------------------------------------------ fp8 activations
-@pytest.mark.parametrize("T,H", [(1, 8), (5, 256), (3, 1024), (333, 2048), (9, 4096), (7, 8192),
-                                 (8192, 2048)])
+@pytest.mark.parametrize("T,H", [(1, 8), (5, 256), (3, 1024), (333, 2048), (9, 4096), (3, 4104),
+                                 (7, 8192), (2, 8200), (8192, 2048)])
 def test_quant_e4m3_rows_bit_exact(T, H):
     x = synth.make_activations(synth.MoeConfig("q", T, H, 128, 8, 1), seed=T + H)[0]
     if T > 2:
