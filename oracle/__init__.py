@@ -27,6 +27,7 @@ from .moe_ref import (  # noqa: F401
     dequantize_weights,
     e4m3fn_encode_rne,
     quantize_rows_e4m3,
+    quantize_rows_mxfp4,
     dequantize_rows,
     route_softmax_topk,
     route_sigmoid_topk,

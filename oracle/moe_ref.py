@@ -183,6 +183,38 @@ def dequantize_mx(packed, scales, block: int = MX_BLOCK) -> np.ndarray:
     return vals * s
 
 
+def quantize_rows_mxfp4(x):
+    """MXFP4 quantisation of activation rows (x of bf16 values, [T, H], H % 32
+    == 0), by the OCP rule the synthetic MXFP4 weights use: each run of 32
+    consecutive elements of a row shares the E8M0 exponent
+    X = floor(log2(max |x|)) - 2, clamped to [-127, 127] (an all-zero run
+    takes X = -127), so that the run's largest magnitude lands in [4, 8); each
+    element becomes the E2M1 value nearest to |x| / 2^X, a tie going to the
+    even code and magnitudes above 6 saturating to 6, with the sign bit of x
+    (a negative element that rounds to 0 keeps its sign bit).  Every step is
+    exact for bf16 inputs: the division is a power-of-two scaling and the
+    rounding compares with the midpoints of the E2M1 grid.
+
+    Returns (codes uint8 [T, H/2], two a byte as the weights, scales uint8
+    [T, H/32] E8M0); dequantize_mx of the pair gives x_hat."""
+    xf = np.asarray(x, dtype=np.float64)
+    T, H = xf.shape
+    assert H % MX_BLOCK == 0, H
+    blk = xf.reshape(T, H // MX_BLOCK, MX_BLOCK)
+    amax = np.abs(blk).max(axis=2)
+    _, e = np.frexp(amax)  # amax = m * 2^e with m in [0.5, 1): floor(log2 amax) = e - 1
+    X = np.clip(np.where(amax > 0, e - 1 - 2, -127), -127, 127)
+    v = np.abs(blk) / np.ldexp(1.0, X)[..., None]
+    # the grid 0, 1/2, 1, 3/2, 2, 3, 4, 6: a code counts the midpoints below
+    # |x| / 2^X; at a midpoint the even code wins, so 1/4, 5/4, 5/2 and 5 round
+    # down and 3/4, 7/4 and 7/2 up
+    mag = ((v > 0.25).astype(np.uint8) + (v >= 0.75) + (v > 1.25) + (v >= 1.75) +
+           (v > 2.5) + (v >= 3.5) + (v > 5.0)).astype(np.uint8)
+    codes = (mag | (np.signbit(blk).astype(np.uint8) << 3)).reshape(T, H)
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    return packed, (X + 127).astype(np.uint8)
+
+
 def dequantize_weights(codes, scales, weight_format: str = "e4m3_128") -> np.ndarray:
     """Dequantised float64 weights of either stored format: "e4m3_128"
     (E4M3FN codes, fp32 128x128 block scales) or "mxfp4" (E2M1 codes two a

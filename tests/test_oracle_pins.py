@@ -109,6 +109,84 @@ def test_mx_quantiser_round_trip():
     assert np.array_equal(oracle.dequantize_mx(p2.numpy(), s2.numpy()), gridw.double().numpy())
 
 
+def _mx_act_cases():
+    out = []
+    for ln in _golden_lines("mxfp4_rounding.txt"):
+        v, code = ln.split()[:2]
+        out.append((float(v), int(code, 16)))
+    return out
+
+
+@pytest.mark.parametrize("X", [-9, 0, 100, -120])
+def test_mxfp4_activation_quantiser_hand_cases(X):
+    """Each hand-worked case as element 1 of its own 32-element run whose
+    element 0 is 4 * 2^X, so the run's exponent is X (a saturating case is
+    itself the run's largest, still below 8 * 2^X)."""
+    cases = _mx_act_cases()
+    x = np.zeros((1, 32 * len(cases)))
+    for i, (v, _) in enumerate(cases):
+        x[0, 32 * i] = 4.0 * 2.0 ** X
+        x[0, 32 * i + 1] = v * 2.0 ** X
+    packed, sc = oracle.quantize_rows_mxfp4(x)
+    codes = oracle.unpack_fp4(packed)[0]
+    assert np.all(sc == X + 127)
+    for i, (v, code) in enumerate(cases):
+        assert codes[32 * i] == 0x6
+        assert codes[32 * i + 1] == code, (v, codes[32 * i + 1], code)
+        assert np.all(codes[32 * i + 2:32 * i + 32] == 0)
+
+
+def test_mxfp4_activation_quantiser_zero_and_clamped_runs():
+    """An all-zero run takes the byte 0 (X = -127) and zero codes; a run whose
+    exponent would fall below -127 is clamped there (2^-126 / 2^-127 = 2)."""
+    x = np.zeros((2, 64))
+    x[1, 32] = 2.0 ** -126
+    x[1, 33] = -(2.0 ** -127)
+    packed, sc = oracle.quantize_rows_mxfp4(x)
+    assert sc.tolist() == [[0, 0], [0, 0]]
+    codes = oracle.unpack_fp4(packed)
+    assert np.all(codes[0] == 0) and np.all(codes[1, :32] == 0)
+    assert codes[1, 32] == 0x4 and codes[1, 33] == 0xA       # 2 and -1
+    assert np.array_equal(oracle.dequantize_mx(packed, sc)[1, 32:34], x[1, 32:34])
+
+
+def test_mxfp4_activation_quantiser_matches_brute_force():
+    """Random bf16 rows, many of them on E2M1 midpoints: the exponent by a
+    search over integers and each code by enumerating the 8 magnitudes
+    (nearest, a tie to the even code) give the same bytes."""
+    g = torch.Generator().manual_seed(21)
+    base = torch.randn(3, 256, generator=g) * torch.tensor([1.0, 1e-3, 30.0])[:, None]
+    mids = torch.tensor([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 7.0])
+    pick = mids[torch.randint(0, 8, (3, 256), generator=g)]
+    sgn = torch.where(torch.rand(3, 256, generator=g) < 0.5, -1.0, 1.0)
+    x = torch.where(torch.rand(3, 256, generator=g) < 0.4, pick * sgn * 2.0 ** -3, base)
+    x[:, ::32] = 4.0 * 2.0 ** -3 * (torch.arange(3)[:, None] + 1)   # vary the runs' largest
+    x[2, 64:96] = 0.0
+    x = x.to(torch.bfloat16).double().numpy()
+    packed, sc = oracle.quantize_rows_mxfp4(x)
+    mags = oracle.e2m1_table()[:8]
+    codes = oracle.unpack_fp4(packed)
+    for t in range(x.shape[0]):
+        for b in range(x.shape[1] // 32):
+            run = x[t, 32 * b:32 * b + 32]
+            amax = float(np.max(np.abs(run)))
+            X = -127
+            if amax > 0:
+                k = -200
+                while 2.0 ** (k + 1) <= amax:
+                    k += 1
+                X = max(-127, min(127, k - 2))
+            assert sc[t, b] == X + 127
+            for j, xv in enumerate(run):
+                v = abs(xv) / 2.0 ** X
+                d = np.abs(mags - v)
+                best = [c for c in range(8) if d[c] == d.min()]
+                c = best[0] if len(best) == 1 else [c for c in best if c % 2 == 0][0]
+                if np.signbit(xv):
+                    c |= 8
+                assert codes[t, 32 * b + j] == c, (t, b, j, xv)
+
+
 def _torch_deq_mx(packed, sc):
     """MXFP4 dequantisation with the hand-worked E2M1 values and torch's
     float8_e8m0fnu cast (independent of the oracle's code)."""
