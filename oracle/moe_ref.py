@@ -193,7 +193,9 @@ def quantize_rows_mxfp4(x):
     even code and magnitudes above 6 saturating to 6, with the sign bit of x
     (a negative element that rounds to 0 keeps its sign bit).  Every step is
     exact for bf16 inputs: the division is a power-of-two scaling and the
-    rounding compares with the midpoints of the E2M1 grid.
+    rounding compares with the midpoints of the E2M1 grid.  A run holding a
+    NaN or an infinity (out of contract, but never made finite) takes the
+    E8M0 NaN byte 255 and zero codes, so its x_hat is NaN.
 
     Returns (codes uint8 [T, H/2], two a byte as the weights, scales uint8
     [T, H/32] E8M0); dequantize_mx of the pair gives x_hat."""
@@ -201,6 +203,8 @@ def quantize_rows_mxfp4(x):
     T, H = xf.shape
     assert H % MX_BLOCK == 0, H
     blk = xf.reshape(T, H // MX_BLOCK, MX_BLOCK)
+    bad = ~np.all(np.isfinite(blk), axis=2)
+    blk = np.where(bad[..., None], 0.0, blk)
     amax = np.abs(blk).max(axis=2)
     _, e = np.frexp(amax)  # amax = m * 2^e with m in [0.5, 1): floor(log2 amax) = e - 1
     X = np.clip(np.where(amax > 0, e - 1 - 2, -127), -127, 127)
@@ -210,9 +214,11 @@ def quantize_rows_mxfp4(x):
     # down and 3/4, 7/4 and 7/2 up
     mag = ((v > 0.25).astype(np.uint8) + (v >= 0.75) + (v > 1.25) + (v >= 1.75) +
            (v > 2.5) + (v >= 3.5) + (v > 5.0)).astype(np.uint8)
-    codes = (mag | (np.signbit(blk).astype(np.uint8) << 3)).reshape(T, H)
+    codes = (mag | (np.signbit(blk).astype(np.uint8) << 3))
+    codes[bad] = 0
+    codes = codes.reshape(T, H)
     packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
-    return packed, (X + 127).astype(np.uint8)
+    return packed, np.where(bad, 255, X + 127).astype(np.uint8)
 
 
 def dequantize_weights(codes, scales, weight_format: str = "e4m3_128") -> np.ndarray:

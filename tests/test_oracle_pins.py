@@ -150,6 +150,20 @@ def test_mxfp4_activation_quantiser_zero_and_clamped_runs():
     assert np.array_equal(oracle.dequantize_mx(packed, sc)[1, 32:34], x[1, 32:34])
 
 
+def test_mxfp4_activation_quantiser_marks_non_finite_runs():
+    """A run holding a NaN or an infinity takes the E8M0 NaN byte 255 and zero
+    codes (its x_hat is NaN); the other runs of the row are unaffected."""
+    x = np.full((1, 96), 1.5)
+    x[0, 3] = np.nan
+    x[0, 40] = -np.inf
+    packed, sc = oracle.quantize_rows_mxfp4(x)
+    assert sc.tolist() == [[255, 255, 125]]
+    codes = oracle.unpack_fp4(packed)[0]
+    assert np.all(codes[:64] == 0) and np.all(codes[64:] == 0x7)   # 1.5 / 2^-2 = 6
+    xh = oracle.dequantize_mx(packed, sc)[0]
+    assert np.all(np.isnan(xh[:64])) and np.all(xh[64:] == 1.5)
+
+
 def test_mxfp4_activation_quantiser_matches_brute_force():
     """Random bf16 rows, many of them on E2M1 midpoints: the exponent by a
     search over integers and each code by enumerating the 8 magnitudes
