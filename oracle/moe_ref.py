@@ -107,9 +107,13 @@ def quantize_rows_e4m3(x):
     """Per-token E4M3 quantisation of activations, decided in fp32 like the
     weights' recipe ([NKI] FP8 weights with a scale of block max / 448, here
     per token row): s = fp32(amax / 448), code = RNE(fp32(x / s)) clamped to
-    +-448; a row of zeros gets s = 0 and zero codes.  Returns (codes uint8
-    [T, H], scales float32 [T]); the GEMM uses decode(code) * s."""
+    +-448; a row of zeros gets s = 0 and zero codes.  A row holding a NaN or
+    an infinity (out of contract, but never made finite) gets a NaN scale and
+    zero codes, so its x_hat is NaN.  Returns (codes uint8 [T, H], scales
+    float32 [T]); the GEMM uses decode(code) * s."""
     x32 = np.asarray(x, dtype=np.float32)
+    bad = ~np.all(np.isfinite(x32), axis=1)
+    x32 = np.where(bad[:, None], np.float32(0.0), x32)
     amax = np.abs(x32).max(axis=1)
     s = (amax / np.float32(E4M3FN_MAX)).astype(np.float32)
     safe = np.where(s > 0, s, np.float32(1.0)).astype(np.float32)
@@ -117,6 +121,7 @@ def quantize_rows_e4m3(x):
     v = np.clip(v, -E4M3FN_MAX, E4M3FN_MAX)
     codes = e4m3fn_encode_rne(v)
     codes[s == 0] = 0
+    s[bad] = np.float32(np.nan)
     return codes, s
 
 

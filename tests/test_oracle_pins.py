@@ -150,6 +150,19 @@ def test_mxfp4_activation_quantiser_zero_and_clamped_runs():
     assert np.array_equal(oracle.dequantize_mx(packed, sc)[1, 32:34], x[1, 32:34])
 
 
+def test_e4m3_row_quantiser_marks_non_finite_rows():
+    """A row holding a NaN or an infinity gets a NaN scale and zero codes (its
+    x_hat is NaN); the finite rows are quantised as before."""
+    x = np.ones((3, 16), np.float32)
+    x[0, 3] = np.nan
+    x[2, 7] = -np.inf
+    codes, s = oracle.quantize_rows_e4m3(x)
+    assert np.isnan(s[0]) and np.isnan(s[2]) and s[1] == np.float32(1.0 / 448.0)
+    assert np.all(codes[[0, 2]] == 0) and np.all(codes[1] == 0x7E)      # 448
+    xh = oracle.dequantize_rows(codes, s)
+    assert np.all(np.isnan(xh[[0, 2]])) and np.allclose(xh[1], 1.0, rtol=1e-6)
+
+
 def test_mxfp4_activation_quantiser_marks_non_finite_runs():
     """A run holding a NaN or an infinity takes the E8M0 NaN byte 255 and zero
     codes (its x_hat is NaN); the other runs of the row are unaffected."""
