@@ -21,7 +21,7 @@ MOE_STATUS_NONFINITE_LOGIT = 2
 MOE_MAX_EXPERTS = 1024
 MOE_MAX_TOPK = 16
 MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
-VARIANTS = {"auto": 0, "decode": 1, "prefill": 2, "prefill_a8": 3}
+VARIANTS = {"auto": 0, "decode": 1, "prefill": 2, "prefill_a8": 3, "prefill_a4": 4}
 ACTIVATIONS = {"swiglu": 0, "relu2": 1}
 LAYOUTS = {"rowmajor": 0, "tiled": 1}
 
@@ -30,7 +30,7 @@ EXPORTED = (
     "moe_route_proj",
     "moe_sort_workspace_bytes", "moe_sort",
     "moe_fused_workspace_bytes", "moe_fused_w8a16", "moe_fused_w8a16_ex",
-    "moe_fused_w8a16_noalloc", "moe_fused_mxfp4", "moe_quant_e4m3_rows",
+    "moe_fused_w8a16_noalloc", "moe_fused_mxfp4", "moe_quant_e4m3_rows", "moe_quant_mxfp4_rows",
     "moe_decode_e4m3fn",
     "moe_pack_w8", "moe_pack_mx_scales",
     "moe_profile_enable", "moe_profile_collect", "moe_profile_count", "moe_profile_stat",
@@ -98,6 +98,8 @@ def load_library():
     lib.moe_pack_w8.argtypes = [vp, vp, i64, i32, i32, vp]
     lib.moe_quant_e4m3_rows.restype = i32
     lib.moe_quant_e4m3_rows.argtypes = [vp, i32, i32, vp, vp, vp]
+    lib.moe_quant_mxfp4_rows.restype = i32
+    lib.moe_quant_mxfp4_rows.argtypes = [vp, i32, i32, vp, vp, vp]
     lib.moe_decode_e4m3fn.restype = i32
     lib.moe_decode_e4m3fn.argtypes = [vp, vp, i64, vp]
     lib.moe_profile_enable.restype = i32
@@ -374,6 +376,18 @@ def quant_e4m3_rows(x: torch.Tensor):
     codes = torch.empty((T, H), dtype=torch.uint8, device=x.device)
     scales = torch.empty(T, dtype=torch.float32, device=x.device)
     _check(lib.moe_quant_e4m3_rows(_ptr(x), T, H, _ptr(codes), _ptr(scales), _stream(x.device)))
+    return codes, scales
+
+
+def quant_mxfp4_rows(x: torch.Tensor):
+    """MXFP4 quantisation of activation rows: x [T, H] bf16 -> (codes [T, H/2]
+    uint8, two E2M1 a byte; scales [T, H/32] uint8 E8M0)."""
+    lib = load_library()
+    _need(x, "x", torch.bfloat16)
+    T, H = x.shape
+    codes = torch.empty((T, H // 2), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((T, H // 32), dtype=torch.uint8, device=x.device)
+    _check(lib.moe_quant_mxfp4_rows(_ptr(x), T, H, _ptr(codes), _ptr(scales), _stream(x.device)))
     return codes, scales
 
 

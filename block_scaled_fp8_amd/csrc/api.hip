@@ -47,7 +47,8 @@ struct FusedLayout {
 // variant appends the E4M3 codes and per-token scales of x.
 static FusedLayout fused_layout(int T, int H, int I, int E, int k, int has_shared, int variant) {
     const bool fp8_x = variant == MOE_VARIANT_PREFILL_A8;
-    const bool compact = variant == MOE_VARIANT_PREFILL || fp8_x;
+    const bool fp4_x = variant == MOE_VARIANT_PREFILL_A4;
+    const bool compact = variant == MOE_VARIANT_PREFILL || fp8_x || fp4_x;
     FusedLayout L;
     const size_t R = (size_t)T * k;
     const size_t rows = R + (has_shared ? (size_t)T : 0);
@@ -75,8 +76,8 @@ static FusedLayout fused_layout(int T, int H, int I, int E, int k, int has_share
     L.abuf = take(sizeof(uint16_t) * rows * I);
     const size_t yrow = compact ? 2 * (size_t)H + (size_t)H / 8 : sizeof(float) * (size_t)H;
     L.ybuf = take(yrow * (rows + 1));  // + one trash row for padded stores
-    L.xq = fp8_x ? take((size_t)T * H) : 0;
-    L.xs = fp8_x ? take(sizeof(float) * (size_t)T) : 0;
+    L.xq = fp8_x ? take((size_t)T * H) : fp4_x ? take((size_t)T * H / 2) : 0;
+    L.xs = fp8_x ? take(sizeof(float) * (size_t)T) : fp4_x ? take((size_t)T * (H / 32)) : 0;
     L.total = o;
     return L;
 }
@@ -228,7 +229,7 @@ int moe_sort(const int32_t* ids, int T, int k, int E, int32_t* counts, int32_t* 
 size_t moe_fused_workspace_bytes(int T, int H, int I, int E, int k, int has_shared,
                                  int variant) {
     if (T < 0 || H < 1 || I < 1 || E < 1 || k < 1) return 0;
-    if (variant < MOE_VARIANT_AUTO || variant > MOE_VARIANT_PREFILL_A8) return 0;
+    if (variant < MOE_VARIANT_AUTO || variant > MOE_VARIANT_PREFILL_A4) return 0;
     return fused_layout(T, H, I, E, k, has_shared ? 1 : 0, variant).total;
 }
 
@@ -262,9 +263,13 @@ static int fused_impl(const char* who, const void* x, const uint8_t* w13, const 
         set_error("unknown weight layout %d", weight_layout);
         return MOE_EINVAL;
     }
-    if (variant < MOE_VARIANT_AUTO || variant > MOE_VARIANT_PREFILL_A8) {
+    if (variant < MOE_VARIANT_AUTO || variant > MOE_VARIANT_PREFILL_A4) {
         set_error("unknown variant %d", variant);
         return MOE_EINVAL;
+    }
+    if (variant == MOE_VARIANT_PREFILL_A4 && !mx4) {
+        set_error("%s: MXFP4 activations (MOE_VARIANT_PREFILL_A4) need MXFP4 weights", who);
+        return MOE_EUNSUPPORTED;
     }
     if (T == 0) return MOE_OK;
     if (!x || !w13 || !w13_scale || !w2 || !w2_scale || !ids || !aff || !out) {
@@ -299,11 +304,12 @@ static int fused_impl(const char* who, const void* x, const uint8_t* w13, const 
     }
     const int has_shared = shared ? 1 : 0;
     const bool fp8_x = variant == MOE_VARIANT_PREFILL_A8;
+    const bool fp4_x = variant == MOE_VARIANT_PREFILL_A4;
     // the prefill GEMMs stage MXFP4 scales with 4-byte loads
     const bool mx_sc4 = !mx4 || ((((uintptr_t)w13_scale | (uintptr_t)w2_scale |
                                   (shared ? (uintptr_t)shared->w13_scale | (uintptr_t)shared->w2_scale : 0)) &
                                  3) == 0);
-    if (mx4 && (variant == MOE_VARIANT_PREFILL || fp8_x) && !mx_sc4) {
+    if (mx4 && (variant == MOE_VARIANT_PREFILL || fp8_x || fp4_x) && !mx_sc4) {
         set_error("%s: the prefill variants need 4-byte aligned MXFP4 scale arrays", who);
         return MOE_EINVAL;
     }
@@ -315,7 +321,7 @@ static int fused_impl(const char* who, const void* x, const uint8_t* w13, const 
         set_error("%s: workspace of %zu bytes needed (got %zu)", who, L.total, ws_bytes);
         return MOE_EINVAL;
     }
-    if (variant == MOE_VARIANT_PREFILL || fp8_x) {
+    if (variant == MOE_VARIANT_PREFILL || fp8_x || fp4_x) {
         if (int rc = prefill_check(T, H, I, E, k, has_shared, act)) return rc;
     }
     // MXFP4 weights, decode variant: the weight-streaming kernel (self-routed
@@ -341,7 +347,7 @@ static int fused_impl(const char* who, const void* x, const uint8_t* w13, const 
     p.seg_row0 = reinterpret_cast<int32_t*>(base + L.seg_row0);
     p.seg_rows = reinterpret_cast<int32_t*>(base + L.seg_rows);
     p.seg_tile0 = reinterpret_cast<int32_t*>(base + L.seg_tile0);
-    const bool pf = variant == MOE_VARIANT_PREFILL || fp8_x;
+    const bool pf = variant == MOE_VARIANT_PREFILL || fp8_x || fp4_x;
     p.tile_info = reinterpret_cast<int4*>(base + L.tile_info);
     p.tile_n = reinterpret_cast<int32_t*>(base + L.tile_n);
     uint16_t* abuf = reinterpret_cast<uint16_t*>(base + L.abuf);
@@ -370,11 +376,14 @@ static int fused_impl(const char* who, const void* x, const uint8_t* w13, const 
             rc = launch_decode_ffn(weight_layout, xb, w13, w13f, w2, w2f, sh, p, aff, T, H, I, E,
                                    k, abuf, ybuf, act, s);
         else {
-            uint8_t* xq = fp8_x ? reinterpret_cast<uint8_t*>(base + L.xq) : nullptr;
-            float* xsc = fp8_x ? reinterpret_cast<float*>(base + L.xs) : nullptr;
-            if (fp8_x && (rc = launch_quant_rows_e4m3(xb, T, H, xq, xsc, s))) return rc;
+            uint8_t* xq = fp8_x || fp4_x ? reinterpret_cast<uint8_t*>(base + L.xq) : nullptr;
+            void* xsc = fp8_x || fp4_x ? static_cast<void*>(base + L.xs) : nullptr;
+            if (fp8_x && (rc = launch_quant_rows_e4m3(xb, T, H, xq, static_cast<float*>(xsc), s))) return rc;
+            if (fp4_x && (rc = launch_quant_rows_mxfp4(xb, T, H, xq, static_cast<uint8_t*>(xsc), s)))
+                return rc;
             rc = launch_prefill_ffn(weight_layout, xb, w13, w13_scale, w2, w2_scale, sh, p, T, H, I,
-                                    E, k, abuf, ybuf, act, xq, xsc, wfmt, s);
+                                    E, k, abuf, ybuf, act, xq, xsc,
+                                    fp4_x ? AFMT_MXFP4 : fp8_x ? AFMT_E4M3 : AFMT_BF16, wfmt, s);
         }
     }
     if (rc) return rc;
@@ -482,9 +491,13 @@ int moe_fused_w8a16_noalloc(const void* x, const uint8_t* w13, const float* w13_
         set_error("H and I must be positive multiples of 128 (got H=%d, I=%d)", H, I);
         return MOE_EUNSUPPORTED;
     }
-    if (variant < MOE_VARIANT_AUTO || variant > MOE_VARIANT_PREFILL_A8) {
+    if (variant < MOE_VARIANT_AUTO || variant > MOE_VARIANT_PREFILL_A4) {
         set_error("unknown variant %d", variant);
         return MOE_EINVAL;
+    }
+    if (variant == MOE_VARIANT_PREFILL_A4) {
+        set_error("moe_fused_w8a16_noalloc: MXFP4 activations need MXFP4 weights");
+        return MOE_EUNSUPPORTED;
     }
     if (T == 0) return MOE_OK;
     const int act = activation == MOE_ACT_RELU2 ? ACT_RELU2 : ACT_SWIGLU;
@@ -567,6 +580,25 @@ int moe_quant_e4m3_rows(const void* x, int T, int H, uint8_t* codes, float* scal
     }
     return launch_quant_rows_e4m3(static_cast<const uint16_t*>(x), T, H, codes, scales,
                                   (hipStream_t)stream);
+}
+
+int moe_quant_mxfp4_rows(const void* x, int T, int H, uint8_t* codes, uint8_t* scales, void* stream) {
+    g_err[0] = 0;
+    if (T < 0 || H < 32 || H % 32) {
+        set_error("moe_quant_mxfp4_rows: need T >= 0 and H a positive multiple of 32 (got %d, %d)", T, H);
+        return MOE_EINVAL;
+    }
+    if (T == 0) return MOE_OK;
+    if (!x || !codes || !scales) {
+        set_error("moe_quant_mxfp4_rows: x, codes and scales must be non-NULL");
+        return MOE_EINVAL;
+    }
+    if ((uintptr_t)x & 15 || (uintptr_t)codes & 15) {
+        set_error("moe_quant_mxfp4_rows: x and codes must be 16-byte aligned");
+        return MOE_EINVAL;
+    }
+    return launch_quant_rows_mxfp4(static_cast<const uint16_t*>(x), T, H, codes, scales,
+                                   (hipStream_t)stream);
 }
 
 int moe_decode_e4m3fn(const uint8_t* codes, uint16_t* out, int64_t n, void* stream) {

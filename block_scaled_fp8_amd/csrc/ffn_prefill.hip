@@ -74,7 +74,7 @@ constexpr int PF_XCD_RUN = 8;  // consecutive row tiles an XCD takes at a time
 // MFMA tiles of 32 x 32), STAGES LDS stages of 64-wide K, OCC workgroups per
 // CU (the register budget follows from it).
 template <int BM_, int BN_, int WM_, int WN_, int STAGES_, int OCC_, int M16_ = 0, int A8_ = 0,
-          int MX4_ = 0>
+          int MX4_ = 0, int A4_ = 0>
 struct PfCfg {
     static constexpr int OCC = OCC_;
     // MFMA shape: v_mfma_f32_16x16x32_bf16 (M16) or v_mfma_f32_32x32x16_bf16;
@@ -90,20 +90,30 @@ struct PfCfg {
     // scale.
     static constexpr bool MX4 = MX4_ != 0;
     static_assert(!(MX4 && M16), "MXFP4 weights use 32x32 tiles");
+    // A4 (with A8 and MX4): the activation operand is MXFP4 too (E2M1 codes,
+    // 32 bytes a row per stage), E2M1 x E2M1 on the scaled MFMA with per-lane
+    // scales on both sides.  A4_ = 1: each stage also stages its rows' E8M0
+    // bytes of the 128-K chunk; A4_ = 2 (XT): the tile's rows' E8M0 bytes
+    // for all of K are staged once, in a table after the stages
+    static constexpr bool A4 = A4_ != 0;
+    static constexpr bool XT = A4_ == 2;
+    static_assert(!A4 || (A8 && MX4), "MXFP4 activations pair with MXFP4 weights");
     static constexpr int MS = M16 ? 16 : 32;  // rows = columns of one MFMA tile
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
     static constexpr int THREADS = WM * WN * MOE_WAVE;
     static constexpr int WAVES = WM * WN;
     static constexpr int STAGES = STAGES_;
-    static constexpr int A_BYTES = BM * PF_BK * (A8 ? 1 : 2);  // bf16 or E4M3
+    static constexpr int A_BYTES = A4 ? BM * PF_BK / 2 : BM * PF_BK * (A8 ? 1 : 2);  // bf16, E4M3 or E2M1
     static constexpr int B_BYTES = BN * PF_BK / (MX4 ? 2 : 1);  // fp8 or E2M1
     static constexpr int TB = MX4 ? 512 : 1024;    // bytes of a 16-row weight tile per stage
     static constexpr int S_BYTES = MX4 ? BN * 4 : 0;  // E8M0: 4 scale bytes a row
-    static constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES;
+    static constexpr int SA_BYTES = A4 && !XT ? WAVES * 256 : 0;  // 4 scale bytes a row (staged twice with 4 waves)
+    static constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES + SA_BYTES;
     static constexpr int A_INSTR = A_BYTES / 1024 / WAVES;  // 1 KB loads per wave per stage
     static constexpr int B_INSTR = B_BYTES / 1024 / WAVES;
-    static constexpr int S_INSTR = MX4 ? 1 : 0;    // 256-byte scale loads per wave per stage
+    static constexpr int S_INSTR = (MX4 ? 1 : 0) + (A4 && !XT ? 1 : 0);  // 256-byte scale loads per wave per stage
     static_assert(!MX4 || S_BYTES == WAVES * 256, "each wave stages the scales of 64 rows");
+    static_assert(!A4 || WAVES * 64 >= BM, "the activation rows' scales fit one load a wave");
     static constexpr int MT = BM / WM / MS;
     static constexpr int NT = BN / WN / MS;
     static constexpr int WROWS = BM / WM;  // rows of a wave tile
@@ -140,6 +150,17 @@ using PfDownMx = PfCfg<128, 256, 2, 2, 2, 2, 0, 0, 1>;
 using PfUpNarrowMx = PfCfg<128, 128, 2, 1, 2, 2, 0, 0, 1>;
 using PfGateUpMxA8 = PfCfg<128, 256, 2, 2, 3, 2, 0, 1, 1>;
 using PfUpNarrowMxA8 = PfCfg<128, 128, 2, 1, 3, 2, 0, 1, 1>;
+using PfGateUpMxA4 = PfCfg<128, 256, 2, 2, 3, 2, 0, 1, 1, 1>;
+using PfUpNarrowMxA4 = PfCfg<128, 128, 2, 1, 3, 2, 0, 1, 1, 1>;
+using PfGateUpMxA4T = PfCfg<128, 256, 2, 2, 3, 2, 0, 1, 1, 2>;
+using PfUpNarrowMxA4T = PfCfg<128, 128, 2, 1, 3, 2, 0, 1, 1, 2>;
+// the x-scale table (XT): 128 rows of H/32 bytes, at most 32 KB; a row is a
+// power-of-two number of 16-byte pieces (the slot swizzle XORs piece indices)
+constexpr int PF_XT_MAX_H = 8192;
+static bool prefill_xscale_table(int H) {
+    const int pieces = H / 512;
+    return H % 512 == 0 && H <= PF_XT_MAX_H && (pieces & (pieces - 1)) == 0;
+}
 constexpr int PF_BM = 128;
 
 int prefill_tile_m() { return PF_BM; }
@@ -218,11 +239,12 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
     const uint8_t* __restrict__ wexp, const void* __restrict__ sexp,
     const uint8_t* __restrict__ wsh, const void* __restrict__ ssh, Plan plan,
     int T, int H, int I, int k, int nblk, int max_tiles,
-    uint16_t* __restrict__ abuf_out, float* __restrict__ ybuf, const float* __restrict__ xscale) {
+    uint16_t* __restrict__ abuf_out, float* __restrict__ ybuf, const void* __restrict__ xscale) {
     constexpr int BM = C::BM, BN = C::BN;
     extern __shared__ __attribute__((aligned(16))) char smem[];
     __shared__ int row_tok[BM];  // gate/up: token row of x
-    __shared__ __attribute__((aligned(16))) float row_xs[C::A8 ? BM : 1];  // A8: the row's x scale
+    constexpr bool XS_ROW = C::A8 && !C::A4;  // a per-token fp32 x scale (E4M3 activations)
+    __shared__ __attribute__((aligned(16))) float row_xs[XS_ROW ? BM : 1];  // the row's x scale
 
     // ---- which tile.  Workgroups are dealt round-robin over the 8 XCDs
     //      (id % 8).  The sort's tile list is cut into blocks of PF_XCD_RUN
@@ -273,7 +295,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
             const int p = p0 + tid;
             const bool valid = tid < rows_here;
             row_tok[tid] = valid ? (e >= 0 ? plan.sorted_route[p] / k : p - R) : 0;
-            if constexpr (C::A8) row_xs[tid] = valid ? xscale[row_tok[tid]] : 0.0f;
+            if constexpr (XS_ROW) row_xs[tid] = valid ? static_cast<const float*>(xscale)[row_tok[tid]] : 0.0f;
         }
         __syncthreads();
     }
@@ -286,7 +308,11 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
     // (A8: E4M3 rows of 64 bytes per stage, 16 rows per instruction, pieces
     //  swizzled by (row / 4) % 4 so that the MFMA reads of 8 rows fall on
     //  distinct banks)
-    constexpr int APR = C::A8 ? 4 : 8;  // 16-byte pieces per row per stage
+    // (A4: E2M1 rows of 32 bytes per stage, 32 rows per instruction, the two
+    //  pieces swapped on rows 8..15 of each 16 so that the reads of 16 rows
+    //  fall on distinct banks)
+    constexpr int APR = C::A4 ? 2 : (C::A8 ? 4 : 8);  // 16-byte pieces per row per stage
+    constexpr int AROW = APR * 16;                    // bytes of an activation row per stage
     const int ar_sub = lane / APR, apiece = lane % APR;
     const char* abase = GATHER ? reinterpret_cast<const char*>(x)
                                : reinterpret_cast<const char*>(abuf_in);
@@ -294,10 +320,11 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
 #pragma unroll
     for (int q = 0; q < C::A_INSTR; ++q) {
         const int row = (wave * C::A_INSTR + q) * (64 / APR) + ar_sub;
-        const int sw = C::A8 ? apiece ^ ((row >> 2) & 3) : apiece ^ ((row >> 1) & 7);
+        const int sw = C::A4 ? apiece ^ ((row >> 3) & 1) : C::A8 ? apiece ^ ((row >> 2) & 3) : apiece ^ ((row >> 1) & 7);
         const uint32_t src_row = GATHER ? (uint32_t)row_tok[row]
                                         : (uint32_t)(p0 + (row < rows_here ? row : 0));
-        asrc[q] = src_row * (uint32_t)((C::A8 ? 1 : 2) * (GATHER ? H : I)) + sw * 16;
+        const uint32_t kdim = GATHER ? H : I;
+        asrc[q] = src_row * (C::A4 ? kdim / 2 : (C::A8 ? 1u : 2u) * kdim) + sw * 16;
     }
     // weights: instruction q of wave w fills 16-row tile w*B_INSTR + q (MX4:
     // the step's 512 bytes of tiles 2 (w*B_INSTR + q) and the next one, from
@@ -339,12 +366,18 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
                                       : (uint32_t)(tile_row(tw) + r) * (uint32_t)(K / 32);
     }
     constexpr uint32_t SCS = LAYOUT == LAYOUT_TILED ? 64 : 4;  // per 128-K chunk
+    // A4: lane l of wave w stages the 4 E8M0 bytes of activation row
+    // (64 w + l) % BM (row-major [T][H/32]) for the step's 128-K chunk, at
+    // byte 4 row of the stage's activation-scale area (with four waves the
+    // rows are staged twice, the second copy unused)
+    uint32_t xsrc = 0;
+    if constexpr (C::A4 && !C::XT) xsrc = (uint32_t)row_tok[(64 * wave + lane) % BM] * (uint32_t)(H / 32);
 
     auto issue_stage = [&](int st, int kc) {
         const uint32_t sbase = st * C::STAGE;
 #pragma unroll
         for (int q = 0; q < C::A_INSTR; ++q)
-            lds_load16(abase + (asrc[q] + (uint32_t)kc * (PF_BK * (C::A8 ? 1 : 2))),
+            lds_load16(abase + (asrc[q] + (uint32_t)kc * AROW),
                        sbase + (wave * C::A_INSTR + q) * 1024, smem);
 #pragma unroll
         for (int q = 0; q < C::B_INSTR; ++q)
@@ -353,6 +386,10 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
         if constexpr (C::MX4)
             __builtin_amdgcn_global_load_lds(SX + (ssrc + (uint32_t)(kc >> 1) * SCS),
                                              smem + sbase + C::A_BYTES + C::B_BYTES + wave * 256, 4, 0, 0);
+        if constexpr (C::A4 && !C::XT)
+            __builtin_amdgcn_global_load_lds(static_cast<const uint8_t*>(xscale) + (xsrc + (uint32_t)(kc >> 1) * 4),
+                                             smem + sbase + C::A_BYTES + C::B_BYTES + C::S_BYTES + wave * 256, 4,
+                                             0, 0);
     };
 
     // ---- wave tile: rows wm*WROWS .. +WROWS, columns wn*WCOLS .. +WCOLS of
@@ -439,6 +476,23 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
                 sr = ((nb * BN) >> 7) + j;
             const int kb = min(c * 64 + lane, kblocks - 1);
             __builtin_amdgcn_global_load_lds(S + (size_t)sr * kblocks + kb, sc_tab + j * kbp + c * 64, 4, 0, 0);
+        }
+    }
+    // XT: the tile's E8M0 bytes of x for all of K, [128 rows][H/32 bytes] at
+    // byte STAGES * STAGE, staged once with 16-byte direct-to-LDS loads that
+    // the first stage wait covers.  Row r's 16-byte piece p sits at slot
+    // p ^ (r % pieces) of the row, so that the 32 rows of a wave reading
+    // the same block fall on different banks (two rows a bank at H = 8192).
+    if constexpr (C::XT) {
+        const int rowb = H / 32, pieces = rowb / 16;  // H % 512 == 0: whole pieces
+        const int n = BM * pieces;                    // 16-byte loads, a multiple of 64
+        for (int it = wave; it * 64 < n; it += C::WAVES) {
+            const int d = it * 64 + lane, r = d / pieces, slot = d - r * pieces;
+            const int p = slot ^ (r & (pieces - 1));
+            // (through the device helper: a 16-byte direct load written in the
+            //  kernel body itself left the kernel's host launch stub undefined)
+            lds_load16(static_cast<const uint8_t*>(xscale) + ((size_t)row_tok[r] * rowb + p * 16),
+                       C::STAGES * C::STAGE + it * 1024, smem);
         }
     }
     // this wave's table rows: g = 0 its gate (or only) columns, g = 1 its up columns
@@ -714,15 +768,40 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
                 const int piece = C::MX4 ? h8 + 2 * j : 2 * h8 + j;
                 a8_off[j] = row * 64 + ((piece ^ ((row >> 2) & 3)) * 16);
             }
+            // A4: E2M1 x E2M1 pairs A lane (row, h) with B lane (column, h) in
+            // the natural order (measured like the E4M3 pairing), so the lane
+            // reads piece h of its 32-byte row; its E8M0 byte for the step's
+            // block h sits at byte 4 row + 2 par + h of the scale area
+            const int arow = wm * C::WROWS + r32;
+            const uint32_t a4_off = arow * 32 + ((h8 ^ ((arow >> 3) & 1)) * 16);
+            const uint32_t sa_off = C::A_BYTES + C::B_BYTES + C::S_BYTES + arow * 4 + h8;
+            // XT: block 2 kc + h of row arow is byte 2 (kc % 8) + h of piece
+            // kc / 8, stored at slot (kc / 8) ^ (arow % pieces); the row
+            // groups mt sit 32 rows apart (the same slot order)
+            const int xt_rowb = H / 32, xt_mask = xt_rowb / 16 - 1;
+            const uint32_t xt_row = C::STAGES * C::STAGE + arow * xt_rowb + h8;
             // (par: the stage's position in its 128-K chunk, for the MX4 scales)
-            auto stage_mma = [&](int stage, bool rescale, const float (&rr)[2], int par) {
+            auto stage_mma = [&](int stage, bool rescale, const float (&rr)[2], int par, int kc) {
                 const char* st = smem + stage * C::STAGE;
                 i32x8 av[C::MT], bv[C::NT];
                 int bs[C::NT];  // MX4: the lane's E8M0 byte of each column tile
+                int sa[C::MT];  // A4: the lane's E8M0 byte of each row group
     #pragma unroll
-                for (int mt = 0; mt < MTA; ++mt)
-                    av[mt] = cat_i32x8(*reinterpret_cast<const u32x4*>(st + a8_off[0] + mt * 32 * 64),
-                                       *reinterpret_cast<const u32x4*>(st + a8_off[1] + mt * 32 * 64));
+                for (int mt = 0; mt < MTA; ++mt) {
+                    if constexpr (C::A4) {
+                        av[mt] = cat_i32x8(*reinterpret_cast<const u32x4*>(st + a4_off + mt * 32 * 32),
+                                           u32x4{0u, 0u, 0u, 0u});
+                        if constexpr (C::XT)
+                            sa[mt] = *reinterpret_cast<const uint8_t*>(
+                                smem + xt_row + ((((kc >> 3) ^ (arow & xt_mask)) * 16) + 2 * (kc & 7)) +
+                                mt * 32 * xt_rowb);
+                        else
+                            sa[mt] = *reinterpret_cast<const uint8_t*>(st + sa_off + par * 2 + mt * 32 * 4);
+                    } else {
+                        av[mt] = cat_i32x8(*reinterpret_cast<const u32x4*>(st + a8_off[0] + mt * 32 * 64),
+                                           *reinterpret_cast<const u32x4*>(st + a8_off[1] + mt * 32 * 64));
+                    }
+                }
                 if (MTA > 0)
     #pragma unroll
                     for (int nt = 0; nt < C::NT; ++nt) {
@@ -737,6 +816,13 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
                     }
     #pragma unroll
                 for (int nt = 0; nt < C::NT; ++nt) {
+                    if constexpr (C::A4) {
+    #pragma unroll
+                        for (int mt = 0; mt < MTA; ++mt)
+                            acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                                av[mt], bv[nt], acc[mt][nt], 4, 4, 0, sa[mt], 0, bs[nt]);
+                        continue;
+                    }
                     if constexpr (C::MX4) {
     #pragma unroll
                         for (int mt = 0; mt < MTA; ++mt)
@@ -790,9 +876,9 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
                     snext[0] = sc_tab[sj[0] * kbp + kn];
                     snext[1] = sc_tab[sj[1] * kbp + kn];
                 }
-                stage_mma(kc % C::STAGES, true, rr, 0);
+                stage_mma(kc % C::STAGES, true, rr, 0, kc);
                 next_stage(kc);
-                stage_mma((kc + 1) % C::STAGES, false, one, 1);
+                stage_mma((kc + 1) % C::STAGES, false, one, 1, kc + 1);
                 next_stage(kc + 1);
             }
         };
@@ -887,7 +973,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
             const int r = mt * C::MS + (C::M16 ? 4 * g16 + i : 8 * (i >> 2) + 4 * lg + (i & 3));
             // A8: the row's activation scale joins the weight block's
             float xsv = 1.0f;
-            if constexpr (C::A8) xsv = row_xs[wm * C::WROWS + r];
+            if constexpr (XS_ROW) xsv = row_xs[wm * C::WROWS + r];
             // value = acc * mcur * x scale * 2^eref, the power of two last (an
             // exact exponent shift unless the result is subnormal)
             const float s0 = mcur[0] * xsv, s1 = mcur[1] * xsv;
@@ -925,7 +1011,7 @@ template <int MODE, int LAYOUT, class C>
 static int launch_pf(const uint16_t* x, const uint16_t* abuf_in, const uint8_t* wexp,
                      const void* sexp, const uint8_t* wsh, const void* ssh, const Plan& plan,
                      int T, int H, int I, int E, int k, int has_shared, uint16_t* abuf_out,
-                     float* ybuf, hipStream_t stream, const float* xscale = nullptr) {
+                     float* ybuf, hipStream_t stream, const void* xscale = nullptr) {
     const int nblk = MODE == PF_GATEUP ? 2 * I / C::BN : (MODE == PF_UP ? I : H) / C::BN;
     const long R = (long)T * k;
     const long max_tiles = (R + C::BM - 1) / C::BM + E + (has_shared ? (T + C::BM - 1) / C::BM : 0);
@@ -937,7 +1023,7 @@ static int launch_pf(const uint16_t* x, const uint16_t* abuf_in, const uint8_t* 
         return MOE_EUNSUPPORTED;
     }
     // activation rows are addressed by 32-bit byte offsets
-    const size_t a_bytes = MODE != PF_DOWN ? (size_t)T * H * (C::A8 ? 1 : 2)
+    const size_t a_bytes = MODE != PF_DOWN ? (C::A4 ? (size_t)T * H / 2 : (size_t)T * H * (C::A8 ? 1 : 2))
                                            : (size_t)(R + (has_shared ? T : 0)) * I * 2;
     if (a_bytes > 0xFFFFFFFFull) {
         set_error("prefill: activation matrix over 4 GB");
@@ -945,15 +1031,22 @@ static int launch_pf(const uint16_t* x, const uint16_t* abuf_in, const uint8_t* 
     }
     const size_t kbp = ((size_t)K_of<MODE>(H, I) / 128 + 63) / 64 * 64;
     // stages, the fp32 scale table (MX4: none) and at least the epilogue's slabs
-    const size_t lds = std::max((size_t)C::STAGES * C::STAGE + (C::MX4 ? 0 : (size_t)(C::BN / 128) * kbp * 4),
-                                (size_t)pf_epilogue_lds<MODE, C>());
+    // (XT: the x-scale table instead)
+    const size_t tab = C::XT ? (size_t)C::BM * (H / 32) : C::MX4 ? 0 : (size_t)(C::BN / 128) * kbp * 4;
+    const size_t lds = std::max((size_t)C::STAGES * C::STAGE + tab, (size_t)pf_epilogue_lds<MODE, C>());
+    if (C::XT && !prefill_xscale_table(H)) {
+        set_error("prefill: x-scale table needs H = 512 * 2^j <= %d", PF_XT_MAX_H);
+        return MOE_EINVAL;
+    }
     const char* pname =
         MODE == PF_DOWN ? (C::MX4 ? "prefill_down_mxfp4" : "prefill_down")
         : MODE == PF_UP
-            ? (C::A8 ? (C::MX4 ? "prefill_up_relu2_mxfp4_a8" : "prefill_up_relu2_a8")
-                     : (C::MX4 ? "prefill_up_relu2_mxfp4" : "prefill_up_relu2"))
-            : (C::A8 ? (C::MX4 ? "prefill_gateup_swiglu_mxfp4_a8" : "prefill_gateup_swiglu_a8")
-                     : (C::MX4 ? "prefill_gateup_swiglu_mxfp4" : "prefill_gateup_swiglu"));
+            ? (C::A4 ? "prefill_up_relu2_mxfp4_a4"
+               : C::A8 ? (C::MX4 ? "prefill_up_relu2_mxfp4_a8" : "prefill_up_relu2_a8")
+                       : (C::MX4 ? "prefill_up_relu2_mxfp4" : "prefill_up_relu2"))
+            : (C::A4 ? "prefill_gateup_swiglu_mxfp4_a4"
+               : C::A8 ? (C::MX4 ? "prefill_gateup_swiglu_mxfp4_a8" : "prefill_gateup_swiglu_a8")
+                       : (C::MX4 ? "prefill_gateup_swiglu_mxfp4" : "prefill_gateup_swiglu"));
     prof_begin(pname, stream);
     prefill_gemm_kernel<MODE, LAYOUT, C><<<(unsigned)grid, C::THREADS, lds, stream>>>(
         x, abuf_in, wexp, sexp, wsh, ssh, plan, T, H, I, k, nblk, (int)max_tiles, abuf_out, ybuf,
@@ -967,12 +1060,44 @@ template <int LAYOUT>
 static int launch_prefill_c(const uint16_t* x, const uint8_t* w13, const void* w13s,
                             const uint8_t* w2, const void* w2s, const SharedW& sh,
                             const Plan& plan, int T, int H, int I, int E, int k, uint16_t* abuf,
-                            float* ybuf, int act, const uint8_t* xq, const float* xs, bool mx4,
+                            float* ybuf, int act, const uint8_t* xq, const void* xs, int afmt, bool mx4,
                             hipStream_t stream) {
     const int hs = sh.w13 != nullptr;
     int rc;
     const void* ss = sh.w13_scale;
     const bool narrow = act == ACT_RELU2 && I % 256 != 0;  // (I % 128 == 0)
+    if (mx4 && afmt == AFMT_MXFP4 && prefill_xscale_table(H)) {  // ... x scales from a per-tile table
+        const uint16_t* xa = reinterpret_cast<const uint16_t*>(xq);
+        if (act != ACT_RELU2)
+            rc = launch_pf<PF_GATEUP, LAYOUT, PfGateUpMxA4T>(xa, nullptr, w13, w13s, sh.w13, ss, plan, T, H, I,
+                                                             E, k, hs, abuf, ybuf, stream, xs);
+        else if (narrow)
+            rc = launch_pf<PF_UP, LAYOUT, PfUpNarrowMxA4T>(xa, nullptr, w13, w13s, sh.w13, ss, plan, T, H, I, E,
+                                                           k, hs, abuf, ybuf, stream, xs);
+        else
+            rc = launch_pf<PF_UP, LAYOUT, PfGateUpMxA4T>(xa, nullptr, w13, w13s, sh.w13, ss, plan, T, H, I, E, k,
+                                                         hs, abuf, ybuf, stream, xs);
+        if (rc == MOE_OK)
+            rc = launch_pf<PF_DOWN, LAYOUT, PfDownMx>(x, abuf, w2, w2s, sh.w2, sh.w2_scale, plan, T, H, I, E, k,
+                                                      hs, abuf, ybuf, stream);
+        return rc;
+    }
+    if (mx4 && afmt == AFMT_MXFP4) {  // MXFP4 weights and activations: E2M1 x E2M1 gate/up
+        const uint16_t* xa = reinterpret_cast<const uint16_t*>(xq);
+        if (act != ACT_RELU2)
+            rc = launch_pf<PF_GATEUP, LAYOUT, PfGateUpMxA4>(xa, nullptr, w13, w13s, sh.w13, ss, plan, T, H, I,
+                                                            E, k, hs, abuf, ybuf, stream, xs);
+        else if (narrow)
+            rc = launch_pf<PF_UP, LAYOUT, PfUpNarrowMxA4>(xa, nullptr, w13, w13s, sh.w13, ss, plan, T, H, I, E,
+                                                          k, hs, abuf, ybuf, stream, xs);
+        else
+            rc = launch_pf<PF_UP, LAYOUT, PfGateUpMxA4>(xa, nullptr, w13, w13s, sh.w13, ss, plan, T, H, I, E, k,
+                                                        hs, abuf, ybuf, stream, xs);
+        if (rc == MOE_OK)
+            rc = launch_pf<PF_DOWN, LAYOUT, PfDownMx>(x, abuf, w2, w2s, sh.w2, sh.w2_scale, plan, T, H, I, E, k,
+                                                      hs, abuf, ybuf, stream);
+        return rc;
+    }
     if (mx4 && xq) {  // MXFP4 weights, E4M3 activations: gate/up on the scaled MFMA
         const uint16_t* xa = reinterpret_cast<const uint16_t*>(xq);
         if (act != ACT_RELU2)
@@ -1056,7 +1181,15 @@ int prefill_check(int T, int H, int I, int E, int k, int has_shared, int act) {
 int launch_prefill_ffn(int layout, const uint16_t* x, const uint8_t* w13, const void* w13s,
                        const uint8_t* w2, const void* w2s, const SharedW& sh, const Plan& plan,
                        int T, int H, int I, int E, int k, uint16_t* abuf, float* ybuf,
-                       int act, const uint8_t* xq, const float* xs, int wfmt, hipStream_t stream) {
+                       int act, const uint8_t* xq, const void* xs, int afmt, int wfmt, hipStream_t stream) {
+    if (afmt == AFMT_MXFP4 && wfmt != WFMT_MXFP4) {
+        set_error("prefill variant: MXFP4 activations need MXFP4 weights");
+        return MOE_EUNSUPPORTED;
+    }
+    if (afmt != AFMT_BF16 && !(xq && xs)) {
+        set_error("prefill variant: quantised activations missing");
+        return MOE_EINVAL;
+    }
 
     if (!prefill_supported(H, I, act)) {
         set_error("prefill variant needs H %% 256 == 0, %s and H, I <= 65536 (got H=%d, I=%d)",
@@ -1069,9 +1202,9 @@ int launch_prefill_ffn(int layout, const uint16_t* x, const uint8_t* w13, const 
     }
     if (layout == LAYOUT_TILED)
         return launch_prefill_c<LAYOUT_TILED>(x, w13, w13s, w2, w2s, sh, plan, T, H, I, E, k, abuf,
-                                              ybuf, act, xq, xs, wfmt == WFMT_MXFP4, stream);
+                                              ybuf, act, xq, xs, afmt, wfmt == WFMT_MXFP4, stream);
     return launch_prefill_c<LAYOUT_ROWMAJOR>(x, w13, w13s, w2, w2s, sh, plan, T, H, I, E, k, abuf,
-                                             ybuf, act, xq, xs, wfmt == WFMT_MXFP4, stream);
+                                             ybuf, act, xq, xs, afmt, wfmt == WFMT_MXFP4, stream);
 }
 
 }  // namespace moe

@@ -30,6 +30,9 @@ struct Plan {
 // Stored weight formats: E4M3FN codes with fp32 128x128 block scales, or
 // MXFP4 (E2M1 codes two a byte, E8M0 scale bytes per 32 elements of a row).
 enum { WFMT_E4M3_128 = 0, WFMT_MXFP4 = 1 };
+// activation operand of the prefill gate/up GEMM: bf16 x, x quantised to
+// E4M3 per token (fp32 scale a row), or x quantised to MXFP4 (E8M0 a run of 32)
+enum { AFMT_BF16 = 0, AFMT_E4M3 = 1, AFMT_MXFP4 = 2 };
 
 // One expert's weights outside the routed arrays (the shared expert); the
 // scales are fp32 (WFMT_E4M3_128) or E8M0 bytes (WFMT_MXFP4).
@@ -76,16 +79,21 @@ int launch_decode_ffn(int layout, const uint16_t* x, const uint8_t* w13, const f
 // Writes y (without the affinity) of every route at its sorted row of ybuf,
 // in a block floating-point form: 16-bit mantissas at byte 2*col and one
 // exponent byte per run of 8 columns at byte 2*H + col/8, row stride
-// 2*H + H/8 bytes (common.hpp, bfp16x8_encode).  Scales are fp32 128x128
-// blocks, or (wfmt WFMT_MXFP4, bf16 activations only: xq NULL) E8M0 bytes,
-// 4-byte aligned.
+// 2*H + H/8 bytes (common.hpp, bfp16x8_encode).  Weight scales are fp32
+// 128x128 blocks, or (wfmt WFMT_MXFP4) E8M0 bytes, 4-byte aligned.  afmt
+// AFMT_E4M3: xq [T, H] codes, xs fp32 [T]; AFMT_MXFP4 (MXFP4 weights only):
+// xq [T, H/2], xs E8M0 bytes [T, H/32]; AFMT_BF16: both unused.
 int launch_prefill_ffn(int layout, const uint16_t* x, const uint8_t* w13, const void* w13s,
                        const uint8_t* w2, const void* w2s, const SharedW& sh, const Plan& plan,
                        int T, int H, int I, int E, int k, uint16_t* abuf, float* ybuf, int act,
-                       const uint8_t* xq, const float* xs, int wfmt, hipStream_t stream);
+                       const uint8_t* xq, const void* xs, int afmt, int wfmt, hipStream_t stream);
 // Per-token E4M3 quantisation of x [T, H] bf16 -> codes [T, H], scales [T] (quant.hip).
 int launch_quant_rows_e4m3(const uint16_t* x, int T, int H, uint8_t* xq, float* xs,
                            hipStream_t stream);
+// MXFP4 quantisation of x [T, H] bf16 -> codes [T, H/2] (two E2M1 a byte),
+// E8M0 scales [T, H/32] (quant.hip).  H % 32 == 0.
+int launch_quant_rows_mxfp4(const uint16_t* x, int T, int H, uint8_t* codes, uint8_t* scales,
+                            hipStream_t stream);
 int launch_pack_w8(const uint8_t* src, uint8_t* dst, int64_t n_mats, int rows, int cols,
                    hipStream_t stream);
 int launch_pack_mx_scales(const uint8_t* src, uint8_t* dst, int64_t n_mats, int rows, int cols,

@@ -7,7 +7,8 @@
 //
 // Row t:  s = amax_h |x[t][h]| / 448            (fp32, correctly rounded)
 //         code[h] = E4M3FN_RNE(min(max(x / s, -448), 448))   (fp32 quotient)
-// A row of zeros gets s = 0 and all-zero codes.  The encoder is written from
+// A row of zeros gets s = 0 and all-zero codes; a row holding a NaN or an
+// infinity gets a NaN scale and zero codes.  The encoder is written from
 // the format: below the smallest normal 2^-6 the step is 2^-9 (subnormals),
 // above it 2^(E-3) with E the fp32 exponent; both round half to even, and a
 // carry out of the 3-bit mantissa moves into the exponent field.
@@ -45,15 +46,15 @@ __global__ __launch_bounds__(256) void quant_rows_e4m3_kernel(const uint16_t* __
     if (t >= T) return;  // whole waves
     const u32x4* row = reinterpret_cast<const u32x4*>(x + (size_t)t * H);
     const int nc = H / 8;
-    auto chunk_max = [](const u32x4& v, float m) {
+    // the row maximum on |x| as bf16 bits: finite magnitudes order as
+    // integers, and a NaN (above every other pattern) makes the maximum, and
+    // so the row's scale, NaN instead of being dropped as fmaxf would
+    auto chunk_max = [](const u32x4& v, uint32_t m) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            m = fmaxf(m, fabsf(__uint_as_float(v[j] << 16)));
-            m = fmaxf(m, fabsf(__uint_as_float(v[j] & 0xFFFF0000u)));
-        }
+        for (int j = 0; j < 4; ++j) m = max(m, max(v[j] & 0x7FFFu, (v[j] >> 16) & 0x7FFFu));
         return m;
     };
-    float amax = 0.0f;
+    uint32_t amax = 0u;
     u32x4 v[NCH > 0 ? NCH : 1];
     if constexpr (NCH > 0) {
 #pragma unroll
@@ -67,8 +68,10 @@ __global__ __launch_bounds__(256) void quant_rows_e4m3_kernel(const uint16_t* __
         for (int c = lane; c < nc; c += 64) amax = chunk_max(row[c], amax);
     }
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, MOE_WAVE));
-    const float s = __fdiv_rn(amax, 448.0f);
+    for (int o = 32; o > 0; o >>= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, o, MOE_WAVE));
+    // a row holding a NaN or an infinity: NaN scale (the quiet NaN 0x7FC00000)
+    // and zero codes
+    const float s = amax >= 0x7F80u ? __uint_as_float(0x7FC00000u) : __fdiv_rn(__uint_as_float(amax << 16), 448.0f);
     if (lane == 0) xs[t] = s;
     uint2* out = reinterpret_cast<uint2*>(xq + (size_t)t * H);
     auto encode_chunk = [&](const u32x4& c8) {
@@ -116,6 +119,73 @@ int launch_quant_rows_e4m3(const uint16_t* x, int T, int H, uint8_t* xq, float* 
         quant_rows_e4m3_kernel<0><<<grid, block, 0, stream>>>(x, T, H, xq, xs);
     prof_end(stream);
     return check_launch("quant_rows_e4m3_kernel");
+}
+
+// MXFP4 quantisation of activation rows for the E2M1 x E2M1 gate/up GEMM
+// ("Add gfx950 Q256 fused MXFP4 prefill pipeline": its producer quantises the
+// activations to MXFP4; the rule is the OCP Microscaling one).  One thread
+// per run of 32 elements of a row (64 bytes in, 16 code bytes and one scale
+// byte out):
+//   X = floor(log2 max|x|) - 2, clamped to [-127, 127]: with e the bf16
+//       exponent field of the largest magnitude, X = max(e - 129, -127) (an
+//       all-zero or subnormal run clamps to -127); scale byte X + 127;
+//   v = |x| * 2^-X, exact in fp32 (a power-of-two scaling of a bf16 value,
+//       at least 2^-6 and below 8);
+//   code = the number of E2M1 midpoints below v, a tie going to the even
+//       code (0.25, 1.25, 2.5 and 5 round down; 0.75, 1.75 and 3.5 up), 7
+//       for everything above 5 (saturation at 6), plus the sign bit of x.
+// A run holding a NaN or an infinity (exponent field all ones) gets the E8M0
+// NaN byte 255 and zero codes.  Element 2j of a run goes to the low nibble of
+// its byte j.
+__global__ __launch_bounds__(256) void quant_rows_mxfp4_kernel(const uint16_t* __restrict__ x, long nruns,
+                                                               uint8_t* __restrict__ codes,
+                                                               uint8_t* __restrict__ scales) {
+    const long i = (long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= nruns) return;
+    const u32x4* src = reinterpret_cast<const u32x4*>(x) + i * 4;
+    u32x4 v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = src[j];
+    uint32_t m = 0;  // largest |x| as bf16 bits (finite values order as integers)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) m = max(m, max(v[j][w] & 0x7FFFu, (v[j][w] >> 16) & 0x7FFFu));
+    const int eb = (int)(m >> 7);
+    const bool bad = m >= 0x7F80u;
+    const int X = max(eb - 129, -127);
+    const float inv = __uint_as_float((uint32_t)(127 - X) << 23);  // 2^-X, 127 - X in [2, 254]
+    u32x4 out;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t b = (v[k][e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
+            const float a = __uint_as_float((b & 0x7FFFu) << 16) * inv;
+            const uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                               (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+                               (uint32_t)(a > 5.0f);
+            word |= (c | ((b >> 12) & 8u)) << (4 * e);
+        }
+        out[k] = bad ? 0u : word;
+    }
+    *reinterpret_cast<u32x4*>(codes + i * 16) = out;
+    scales[i] = bad ? (uint8_t)255 : (uint8_t)(X + 127);
+}
+
+int launch_quant_rows_mxfp4(const uint16_t* x, int T, int H, uint8_t* codes, uint8_t* scales,
+                            hipStream_t stream) {
+    if (H % 32) {
+        set_error("MXFP4 activation quantisation needs H %% 32 == 0 (got %d)", H);
+        return MOE_EUNSUPPORTED;
+    }
+    if (T == 0) return MOE_OK;
+    const long nruns = (long)T * (H / 32);
+    prof_begin("quant_rows_mxfp4", stream);
+    quant_rows_mxfp4_kernel<<<(unsigned)((nruns + 255) / 256), 256, 0, stream>>>(x, nruns, codes, scales);
+    prof_end(stream);
+    return check_launch("quant_rows_mxfp4_kernel");
 }
 
 }  // namespace moe

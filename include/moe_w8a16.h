@@ -68,9 +68,13 @@ enum {
                                  (or per 16/32-row tile of its routes past 4096 routes), or per
                                  (expert, N tile) with few active experts */
     MOE_VARIANT_PREFILL = 2,  /* grouped bf16-MFMA GEMM over 128-row tiles of sorted routes */
-    MOE_VARIANT_PREFILL_A8 = 3  /* the prefill GEMMs with x quantised to E4M3 per token (as
+    MOE_VARIANT_PREFILL_A8 = 3, /* the prefill GEMMs with x quantised to E4M3 per token (as
                                    moe_quant_e4m3_rows) for the gate/up (or up) GEMM on the
                                    FP8 MFMA; the down GEMM as PREFILL; never chosen by AUTO */
+    MOE_VARIANT_PREFILL_A4 = 4  /* MXFP4 weights only (moe_fused_mxfp4): the prefill GEMMs with
+                                   x quantised to MXFP4 (as moe_quant_mxfp4_rows) for the
+                                   gate/up (or up) GEMM as E2M1 x E2M1 products on the scaled
+                                   MFMA; the down GEMM as PREFILL; never chosen by AUTO */
 };
 
 enum {
@@ -369,6 +373,16 @@ typedef struct {
  *              E4M3 by E2M1 codes on the scaled FP8 MFMA, each 32-element
  *              block's E8M0 byte as the MFMA's weight scale, and the down
  *              GEMM stays bf16 x MXFP4
+ *   MOE_VARIANT_PREFILL_A4  likewise, with x quantised to MXFP4 as
+ *              moe_quant_mxfp4_rows does ("Add gfx950 Q256 fused MXFP4
+ *              prefill pipeline", description: the producer quantises the
+ *              activations and the GEMMs run in MXFP4); gate/up as E2M1 x
+ *              E2M1 products with both operands' E8M0 bytes as the MFMA's
+ *              scales; every expert then computes from x_hat of
+ *              moe_quant_mxfp4_rows instead of x (the SwiGLU output stays
+ *              bf16, the down GEMM bf16 x MXFP4); the workspace also holds
+ *              the codes and scales of x.  A token whose row holds a NaN or
+ *              an infinity gets a NaN output row.
  * The E8M0 scale is applied exactly in the conversion to bf16 (every E2M1
  * value times a power of two is a bf16 value while it stays in bf16's normal
  * range; smaller products are flushed to zero), products are summed in fp32
@@ -389,7 +403,8 @@ int moe_fused_mxfp4(const void* x,
  * own.  For each row t:
  *     scales[t] = max_h |x[t][h]| / 448                    (fp32, correctly rounded)
  *     codes[t][h] = E4M3FN round-half-even of min(max(x[t][h] / scales[t], -448), 448)
- * with the quotient in fp32; a row of zeros gets scale 0 and zero codes.  The
+ * with the quotient in fp32; a row of zeros gets scale 0 and zero codes, a row
+ * holding a NaN or an infinity a NaN scale and zero codes.  The
  * value the GEMM then uses is decode(code) * scale.  Source of the format and
  * of the amax / 448 rule: NKI page, section "FP8 MoE decode kernel" (official
  * E4M3FN weights, block scale = block maximum / 448), applied per token row.
@@ -398,6 +413,28 @@ int moe_fused_mxfp4(const void* x,
  */
 int moe_quant_e4m3_rows(const void* x, int T, int H, uint8_t* codes, float* scales,
                         void* stream);
+
+/*
+ * moe_quant_mxfp4_rows -- the MXFP4 quantisation of x that
+ * MOE_VARIANT_PREFILL_A4 applies, exposed so it can be checked on its own.
+ * Source: "Add gfx950 Q256 fused MXFP4 prefill pipeline" (description: the
+ * producer quantises the activations to MXFP4); the pages give no rule, and
+ * the OCP Microscaling one is taken (as for the MXFP4 weights).  For each run
+ * of 32 consecutive elements of a row:
+ *     X = floor(log2 max |x|) - 2, clamped to [-127, 127] (an all-zero run:
+ *         -127), so the run's largest magnitude maps into [4, 8);
+ *     scales[t][r] = X + 127 (E8M0);
+ *     code = the E2M1 value nearest to |x| / 2^X (a tie to the even code,
+ *         magnitudes above 6 saturating to 6) with the sign bit of x.
+ * Every step is exact for bf16 inputs.  A run holding a NaN or an infinity
+ * gets the E8M0 NaN byte 255 and zero codes.  The value the GEMM uses is
+ * E2M1(code) * 2^(scale - 127).
+ *   x [T, H] bf16 (16-byte aligned), codes [T, H/2] uint8 (two a byte,
+ *   element 2j in the low nibble of byte j; 16-byte aligned), scales
+ *   [T, H/32] uint8; H % 32 == 0 (else MOE_EINVAL); T == 0 is a no-op.
+ */
+int moe_quant_mxfp4_rows(const void* x, int T, int H, uint8_t* codes, uint8_t* scales,
+                         void* stream);
 
 /*
  * moe_decode_e4m3fn -- decode n E4M3FN bytes to bf16 bit patterns with the

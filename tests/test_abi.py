@@ -130,6 +130,32 @@ def test_fused_activation_checks():
     assert b"H % 256" in lib.moe_last_error()
 
 
+def test_quant_mxfp4_rows_argument_checks():
+    lib = binding.load_library()
+    f = ctypes.c_void_p(0x1000)
+    assert lib.moe_quant_mxfp4_rows(f, 4, 48, f, f, None) == binding.MOE_EINVAL     # H % 32
+    assert b"multiple of 32" in lib.moe_last_error()
+    assert lib.moe_quant_mxfp4_rows(ctypes.c_void_p(0x1008), 4, 64, f, f, None) == binding.MOE_EINVAL
+    assert lib.moe_quant_mxfp4_rows(f, 4, 64, ctypes.c_void_p(0x1008), f, None) == binding.MOE_EINVAL
+    assert b"aligned" in lib.moe_last_error()
+    assert lib.moe_quant_mxfp4_rows(f, 4, 64, f, None, None) == binding.MOE_EINVAL
+    assert lib.moe_quant_mxfp4_rows(None, 0, 64, None, None, None) == binding.MOE_OK
+
+
+def test_mxfp4_activation_variant_needs_mxfp4_weights():
+    """MOE_VARIANT_PREFILL_A4 is refused for E4M3FN weights (both entry
+    points) before any launch."""
+    lib = binding.load_library()
+    f, o = ctypes.c_void_p(0x1000), ctypes.c_void_p(0x3000)
+    ws = lib.moe_fused_workspace_bytes(64, 2048, 512, 256, 8, 0, 4)
+    assert ws > lib.moe_fused_workspace_bytes(64, 2048, 512, 256, 8, 0, 2)   # + codes and scales of x
+    head = (f, f, f, f, f, f, f, 64, 2048, 512, 256, 8, None, o, None)
+    assert lib.moe_fused_w8a16_ex(*head, f, ws, 0, 4, 0, None) == binding.MOE_EUNSUPPORTED
+    assert b"MXFP4 weights" in lib.moe_last_error()
+    assert lib.moe_fused_w8a16_noalloc(*head, 0, 4, 0, None) == binding.MOE_EUNSUPPORTED
+    assert lib.moe_fused_w8a16_ex(*head, f, ws, 0, 5, 0, None) == binding.MOE_EINVAL
+
+
 def test_quant_e4m3_rows_argument_checks():
     lib = binding.load_library()
     f = ctypes.c_void_p(0x1000)

@@ -20,6 +20,21 @@ from test_gpu_parity import _xhat_rows, check_rows
 
 pytestmark = pytest.mark.gpu
 
+
+def _x4hat_rows(c, rows):
+    """The oracle's MXFP4 quantisation of the given rows of x, dequantised."""
+    xr = np_(c["x"][torch.as_tensor(rows, device=c["x"].device)].float())
+    return oracle.dequantize_mx(*oracle.quantize_rows_mxfp4(xr))
+
+
+def _xq_rows(c, rows, variant):
+    """The rows of x the variant's experts compute from (None: x itself)."""
+    if variant == "prefill_a8":
+        return _xhat_rows(c, rows)
+    if variant == "prefill_a4":
+        return _x4hat_rows(c, rows)
+    return None
+
 _cases = {}
 _oracle = {}
 
@@ -52,8 +67,8 @@ def _run(c, ids, aff, layout, activation, variant="auto", shared=True, status=No
 
 # (AUTO: the decode kernels up to 16 routes per expert, the grouped GEMMs
 # above; the large workloads also run the decode kernels' row-tile form and
-# the grouped GEMMs with x quantised to E4M3 per token)
-@pytest.mark.parametrize("variant", ["auto", "decode", "prefill_a8"])
+# the grouped GEMMs with x quantised to E4M3 per token or to MXFP4)
+@pytest.mark.parametrize("variant", ["auto", "decode", "prefill_a8", "prefill_a4"])
 @pytest.mark.parametrize("layout", ["rowmajor", "tiled"])
 @pytest.mark.parametrize("activation", ["swiglu", "relu2"])
 @pytest.mark.parametrize("name", synth.CONFIG_ORDER)
@@ -70,10 +85,9 @@ def test_mxfp4_parity(name, activation, layout, variant):
     ref_ids, ref_aff = oracle.route_softmax_topk(np_(c["logits"]), cfg.k)
     assert np.array_equal(np_(ids), ref_ids)
     rows = check_rows(name, cfg, ref_ids)
-    key = (activation, variant == "prefill_a8")
+    key = (activation, variant if variant.startswith("prefill_a") else "x")
     if key not in _oracle:
-        xr = _xhat_rows(c, rows) if variant == "prefill_a8" else None
-        _oracle[key] = oracle_rows(c, ref_ids, ref_aff, rows, xrows=xr)
+        _oracle[key] = oracle_rows(c, ref_ids, ref_aff, rows, xrows=_xq_rows(c, rows, variant))
     assert_out_close(np_(out)[rows], _oracle[key],
                      what=f"mxfp4 {name}/{activation}/{layout}/{variant} ({len(rows)} rows)")
 
@@ -98,7 +112,7 @@ def test_mxfp4_shapes(T, H, I, E, k, layout):
     assert_out_close(np_(out), ref, what=f"mxfp4 T={T} H={H} I={I} E={E} k={k}/{layout}")
 
 
-@pytest.mark.parametrize("variant", ["decode", "prefill", "prefill_a8"])
+@pytest.mark.parametrize("variant", ["decode", "prefill", "prefill_a8", "prefill_a4"])
 def test_mxfp4_scale_bytes_at_the_ends_and_zero_affinities(variant):
     """Scale bytes 1 (2^-126) and 140 (2^13) on some blocks, the rest as drawn;
     outputs stay finite and match the oracle; zero affinities give exactly 0."""
@@ -113,8 +127,7 @@ def test_mxfp4_scale_bytes_at_the_ends_and_zero_affinities(variant):
     torch.cuda.synchronize()
     ref_ids, ref_aff = oracle.route_softmax_topk(np_(c["logits"]), cfg.k)
     rows = np.arange(cfg.T)
-    xr = _xhat_rows(c, rows) if variant == "prefill_a8" else None
-    ref = oracle_rows(c, ref_ids, ref_aff, rows, xrows=xr)
+    ref = oracle_rows(c, ref_ids, ref_aff, rows, xrows=_xq_rows(c, rows, variant))
     assert np.all(np.isfinite(ref))
     assert_out_close(np_(out), ref, what=f"mxfp4 {variant} scale bytes 1 and 140")
     zero = torch.zeros_like(aff)
@@ -173,7 +186,7 @@ def test_mxfp4_unaligned_scales_take_the_decode_kernels():
     ref_ids, ref_aff = oracle.route_softmax_topk(np_(c["logits"]), cfg.k)
     assert_out_close(np_(out), oracle_rows(c, ref_ids, ref_aff, np.arange(cfg.T)),
                      what="mxfp4 unaligned scales, auto")
-    for v in ("prefill", "prefill_a8"):
+    for v in ("prefill", "prefill_a8", "prefill_a4"):
         with pytest.raises(binding.MoeError) as ei:
             binding.fused_w8a16(c["x"], c["w13"], s13, c["w2"], s2, ids, aff, variant=v,
                                 weight_format="mxfp4")
@@ -196,30 +209,52 @@ def test_pack_mx_scales_matches_reference(shape):
     assert np.array_equal(got.reshape(-1), ref)
 
 
-# x quantised to E4M3 per token, gate/up (or up) as E4M3 x E2M1 on the scaled
-# MFMA with the weights' E8M0 bytes as its B scales: against the oracle run on
-# the same quantised rows
+# x quantised to E4M3 per token (gate/up or up as E4M3 x E2M1) or to MXFP4
+# (E2M1 x E2M1) on the scaled MFMA, with the E8M0 bytes as its per-lane
+# scales: against the oracle run on the same quantised rows
+@pytest.mark.parametrize("variant", ["prefill_a8", "prefill_a4"])
 @pytest.mark.parametrize("layout", ["rowmajor", "tiled"])
 @pytest.mark.parametrize("activation", ["swiglu", "relu2"])
 @pytest.mark.parametrize("T,H,I,E,k", [(300, 512, 256, 8, 2), (257, 256, 384, 16, 4),
                                        (129, 768, 128, 4, 1)])
-def test_mxfp4_prefill_a8_shapes(T, H, I, E, k, activation, layout):
+def test_mxfp4_prefill_quantised_x_shapes(T, H, I, E, k, activation, layout, variant):
     cfg = synth.MoeConfig("mxq", T=T, H=H, I=I, E=E, k=k, shared=True)
     c = gpu_case(cfg, seed=T + I + 1, activation=activation, weight_format="mxfp4")
     g = tiled_case(c) if layout == "tiled" else c
     ids, aff = binding.route(c["logits"], k)
     out = binding.fused_w8a16(g["x"], g["w13"], g["w13_scale"], g["w2"], g["w2_scale"], ids, aff,
-                              shared=g["shared"], variant="prefill_a8", layout=layout,
+                              shared=g["shared"], variant=variant, layout=layout,
                               activation=activation, weight_format="mxfp4")
     torch.cuda.synchronize()
     ref_ids, ref_aff = oracle.route_softmax_topk(np_(c["logits"]), k)
     rows = np.arange(T)
-    ref = oracle_rows(c, ref_ids, ref_aff, rows, xrows=_xhat_rows(c, rows))
+    ref = oracle_rows(c, ref_ids, ref_aff, rows, xrows=_xq_rows(c, rows, variant))
     assert_out_close(np_(out), ref,
-                     what=f"mxfp4 prefill_a8 T={T} H={H} I={I} E={E} k={k}/{activation}/{layout}")
+                     what=f"mxfp4 {variant} T={T} H={H} I={I} E={E} k={k}/{activation}/{layout}")
 
 
-@pytest.mark.parametrize("variant", ["decode", "prefill", "prefill_a8"])
+@pytest.mark.parametrize("variant", ["prefill", "prefill_a8", "prefill_a4"])
+def test_mxfp4_nan_activation_row(variant):
+    """A NaN in one token's activations gives that token an all-NaN output
+    row (with MXFP4 activations through the E8M0 NaN byte of its run), as the
+    oracle's; every other row still matches."""
+    cfg = synth.MoeConfig("mxn", T=40, H=512, I=256, E=16, k=4, shared=True)
+    c = gpu_case(cfg, seed=23, weight_format="mxfp4")
+    t0 = 7
+    c["x"][t0, 100] = float("nan")
+    ids, aff = binding.route(c["logits"], cfg.k)
+    out = np_(_run(c, ids, aff, "rowmajor", "swiglu", variant=variant))
+    torch.cuda.synchronize()
+    ref_ids, ref_aff = oracle.route_softmax_topk(np_(c["logits"]), cfg.k)
+    ref0 = oracle_rows(c, ref_ids, ref_aff, np.array([t0]), xrows=_xq_rows(c, [t0], variant))
+    assert np.all(np.isnan(ref0))
+    assert np.all(np.isnan(out[t0])), f"{variant}: {int(np.sum(~np.isnan(out[t0])))} non-NaN values"
+    rows = np.array([t for t in range(cfg.T) if t != t0])
+    assert_out_close(out[rows], oracle_rows(c, ref_ids, ref_aff, rows, xrows=_xq_rows(c, rows, variant)),
+                     what=f"mxfp4 nan row {variant}")
+
+
+@pytest.mark.parametrize("variant", ["decode", "prefill", "prefill_a8", "prefill_a4"])
 def test_mxfp4_is_deterministic_and_graph_replays(variant):
     cfg = synth.MoeConfig("mxg", T=64, H=512, I=256, E=128, k=4, shared=True)
     c = gpu_case(cfg, seed=7, weight_format="mxfp4")

@@ -579,11 +579,12 @@ def test_fused_bad_ids_are_dropped(variant):
 
 
 @pytest.mark.parametrize("layout", LAYOUTS)
-@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("variant", VARIANTS + ["prefill_a8"])
 def test_fused_nan_activation_row(variant, layout):
     """A NaN in one token's activations makes that token's whole output row
     NaN, as the float64 oracle's does, through the fp32 decode rows and the
-    prefill's compact contributions alike; every other row still matches."""
+    prefill's compact contributions alike (with E4M3 activations through the
+    row's NaN scale); every other row still matches."""
     cfg = synth.MoeConfig("nan", T=40, H=512, I=256, E=16, k=4, shared=True)
     c = gpu_case(cfg, seed=21)
     t0 = 7
@@ -592,10 +593,12 @@ def test_fused_nan_activation_row(variant, layout):
     out = np_(_fused(c, ids, aff, variant=variant, layout=layout))
     torch.cuda.synchronize()
     ref_ids, ref_aff = oracle.route_softmax_topk(np_(c["logits"]), cfg.k)
-    assert np.all(np.isnan(oracle_rows(c, ref_ids, ref_aff, np.array([t0]))))
+    xr = (lambda r: _xhat_rows(c, r)) if variant == "prefill_a8" else (lambda r: None)
+    assert np.all(np.isnan(oracle_rows(c, ref_ids, ref_aff, np.array([t0]), xrows=xr([t0]))))
     assert np.all(np.isnan(out[t0])), f"{variant}: {int(np.sum(~np.isnan(out[t0])))} non-NaN values"
     rows = np.array([t for t in range(cfg.T) if t != t0])
-    assert_out_close(out[rows], oracle_rows(c, ref_ids, ref_aff, rows), what=f"nan row {variant}")
+    assert_out_close(out[rows], oracle_rows(c, ref_ids, ref_aff, rows, xrows=xr(rows)),
+                     what=f"nan row {variant}")
 
 
 @pytest.mark.parametrize("variant", VARIANTS)
@@ -675,11 +678,36 @@ def test_quant_e4m3_rows_bit_exact(T, H):
         x[1] = 0.0                      # a zero row: scale 0, codes 0
         x[2, :] = 0.0
         x[2, H // 2] = -1.5             # one element: it maps to -448 (0xFE)
+    if T > 4:
+        x[3, H // 3] = float("nan")     # non-finite rows: NaN scale, zero codes
+        x[4, 0] = float("inf")
     xg = x.cuda()
     codes, scales = binding.quant_e4m3_rows(xg)
     torch.cuda.synchronize()
     ref_c, ref_s = oracle.quantize_rows_e4m3(x.float().numpy())
     assert np.array_equal(np_(scales).view(np.uint32), ref_s.view(np.uint32))
+    assert np.array_equal(np_(codes), ref_c)
+
+
+@pytest.mark.parametrize("T,H", [(1, 32), (2, 96), (5, 256), (333, 2048), (7, 8192)])
+def test_quant_mxfp4_rows_bit_exact(T, H):
+    """MXFP4 quantisation of x against the oracle's, byte for byte: random
+    rows, an all-zero row, a row of E2M1 midpoints (ties) and saturating
+    values, and runs holding a NaN or an infinity."""
+    x = synth.make_activations(synth.MoeConfig("q4", T, H, 128, 8, 1), seed=T + H + 4)[0]
+    if T > 2:
+        x[1] = 0.0
+        mids = torch.tensor([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 7.0, -0.25, -1.25, -5.0, 6.0,
+                             0.375, 1.375, 2.75, 5.5])
+        x[2] = (mids.repeat(H // 16 + 1)[:H] * 2.0 ** -3).to(torch.bfloat16)
+        x[2, ::32] = 4.0 * 2.0 ** -3        # each run's exponent is -3 (7.0 and 6.0 saturate or not)
+        x[0, 5] = float("nan")
+        if H >= 64:
+            x[0, 40] = float("-inf")
+    codes, scales = binding.quant_mxfp4_rows(x.cuda())
+    torch.cuda.synchronize()
+    ref_c, ref_s = oracle.quantize_rows_mxfp4(x.float().numpy())
+    assert np.array_equal(np_(scales), ref_s)
     assert np.array_equal(np_(codes), ref_c)
 
 
