@@ -27,6 +27,7 @@ METRIC = "fused FP8 MoE tokens/s + %HBM BW (decode T=64) / %MFMA peak (prefill T
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 FP8_PEAK_TFLOPS = 5000.0       # MI355X dense fp8 MFMA, published
+FP4_PEAK_TFLOPS = 10100.0      # MI355X dense fp4 (and fp6) MFMA, published
 
 
 def log(msg):
@@ -577,6 +578,14 @@ def fused_variant_bench(cfg, dev, L, seed=0, activation="swiglu", variant="auto"
                            "frac": round(kb / (kus * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                            "traffic": profiled_traffic("decode_fused_expert_mxfp4", cfg.name),
                            "traffic_unit": "bytes per launch"}
+    a4 = [n for n in prof if n.endswith("_a4")]
+    if a4:
+        # the E2M1 x E2M1 gate/up (or up) GEMM against the FP4 MFMA peak
+        kus = prof[a4[0]][1] * 1e3
+        kfl = 2.0 * H * n13 * rows
+        out["fp4_gemm"] = {"kernel": a4[0], "avg_us": round(kus, 3), "flops": kfl,
+                           "TFLOP_per_s": round(kfl / (kus * 1e-6) / 1e12, 1),
+                           "peak": FP4_PEAK_TFLOPS, "frac": round(kfl / (kus * 1e-6) / 1e12 / FP4_PEAK_TFLOPS, 4)}
     a8 = [n for n in prof if n.endswith("_a8")]
     if a8:
         # the fp8 x fp8 gate/up (or up) GEMM against the FP8 MFMA peak
@@ -746,13 +755,15 @@ def main():
             result["mxfp4"].append(fused_variant_bench(synth.CONFIGS["prefill16k_wide"], dev, 1,
                                                        args.seed, weight_format="mxfp4"))
         if args.prefill_workload and not args.no_a8:
-            # x quantised to E4M3 per token: gate/up as E4M3 x E2M1 on the FP8 MFMA
+            # x quantised to E4M3 per token (gate/up as E4M3 x E2M1 on the FP8
+            # MFMA) or to MXFP4 (E2M1 x E2M1)
             for wname in dict.fromkeys([args.prefill_workload] +
                                        ([] if args.no_extra_workloads else ["prefill16k_wide"])):
-                result["mxfp4"].append(fused_variant_bench(synth.CONFIGS[wname], dev,
-                                                           2 if wname == "prefill8k_skew" else 1,
-                                                           args.seed, variant="prefill_a8",
-                                                           weight_format="mxfp4"))
+                for v in ("prefill_a8", "prefill_a4"):
+                    result["mxfp4"].append(fused_variant_bench(synth.CONFIGS[wname], dev,
+                                                               2 if wname == "prefill8k_skew" else 1,
+                                                               args.seed, variant=v,
+                                                               weight_format="mxfp4"))
     if args.prefill_workload and not args.no_a8:
         result["prefill_a8"] = fused_variant_bench(synth.CONFIGS[args.prefill_workload], dev, 2,
                                                    args.seed, variant="prefill_a8")
