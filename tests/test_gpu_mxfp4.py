@@ -16,7 +16,7 @@ import oracle
 from block_scaled_fp8_amd import binding, synth
 
 from _parity import assert_out_close, gpu_case, np_, oracle_rows, tiled_case
-from test_gpu_parity import _xhat_rows, check_rows
+from test_gpu_parity import SEG_SIZES, TILE_M, _xhat_rows, check_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -284,3 +284,33 @@ def test_mxfp4_is_deterministic_and_graph_replays(variant):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, a)
+
+
+@pytest.mark.parametrize("shared", [False, True])
+@pytest.mark.parametrize("layout", ["rowmajor", "tiled"])
+@pytest.mark.parametrize("activation", ["swiglu", "relu2"])
+@pytest.mark.parametrize("variant", ["decode", "prefill", "prefill_a8", "prefill_a4"])
+def test_mxfp4_segment_size_sweep(variant, activation, layout, shared):
+    """MXFP4 weights with crafted ids giving the experts exactly SEG_SIZES
+    routes each (the edges of the 32-row MFMA row groups and 128-row tiles
+    of the grouped GEMMs, and of the decode kernels' row tiles); every output
+    row against the oracle."""
+    E, k = len(SEG_SIZES), 2
+    labels = np.repeat(np.arange(E, dtype=np.int32), SEG_SIZES)
+    np.random.default_rng(33).shuffle(labels)
+    T = labels.size // k
+    ids_np = labels.reshape(T, k)
+    assert T % TILE_M == 65
+    cfg = synth.MoeConfig("mxseg", T=T, H=512, I=256, E=E, k=k, shared=shared)
+    c = gpu_case(cfg, seed=33, activation=activation, weight_format="mxfp4")
+    g = tiled_case(c) if layout == "tiled" else c
+    aff_np = synth.random_affinities(T, k, seed=33).numpy()
+    out = binding.fused_w8a16(g["x"], g["w13"], g["w13_scale"], g["w2"], g["w2_scale"],
+                              torch.from_numpy(ids_np).cuda(), torch.from_numpy(aff_np).cuda(),
+                              shared=g["shared"] if shared else None, variant=variant, layout=layout,
+                              activation=activation, weight_format="mxfp4")
+    torch.cuda.synchronize()
+    rows = np.arange(T)
+    ref = oracle_rows(c, ids_np, aff_np, rows, with_shared=shared, xrows=_xq_rows(c, rows, variant))
+    assert_out_close(np_(out), ref,
+                     what=f"mxfp4 segments {variant}/{activation}/{layout}/shared={shared}")
