@@ -123,11 +123,12 @@ int launch_quant_rows_e4m3(const uint16_t* x, int T, int H, uint8_t* xq, float* 
 
 // MXFP4 quantisation of activation rows for the E2M1 x E2M1 gate/up GEMM
 // ("Add gfx950 Q256 fused MXFP4 prefill pipeline": its producer quantises the
-// activations to MXFP4; the rule is the OCP Microscaling one).  One thread
-// per run of 32 elements of a row (64 bytes in, 16 code bytes and one scale
-// byte out):
+// activations to MXFP4; the rule is the OCP Microscaling one).  Four lanes
+// per run of 32 elements of a row, 8 elements (16 bytes) a lane, so that a
+// wave reads 1 KB and writes 256 code bytes contiguously:
 //   X = floor(log2 max|x|) - 2, clamped to [-127, 127]: with e the bf16
-//       exponent field of the largest magnitude, X = max(e - 129, -127) (an
+//       exponent field of the run's largest magnitude (the maximum of |x| as
+//       bf16 bits, shared over the lane quad), X = max(e - 129, -127) (an
 //       all-zero or subnormal run clamps to -127); scale byte X + 127;
 //   v = |x| * 2^-X, exact in fp32 (a power-of-two scaling of a bf16 value,
 //       at least 2^-6 and below 8);
@@ -140,38 +141,34 @@ int launch_quant_rows_e4m3(const uint16_t* x, int T, int H, uint8_t* xq, float* 
 __global__ __launch_bounds__(256) void quant_rows_mxfp4_kernel(const uint16_t* __restrict__ x, long nruns,
                                                                uint8_t* __restrict__ codes,
                                                                uint8_t* __restrict__ scales) {
-    const long i = (long)blockIdx.x * 256 + threadIdx.x;
-    if (i >= nruns) return;
-    const u32x4* src = reinterpret_cast<const u32x4*>(x) + i * 4;
-    u32x4 v[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) v[j] = src[j];
+    const long g = (long)blockIdx.x * 256 + threadIdx.x;  // 8-element group
+    const long run = g >> 2;
+    // (whole quads: nruns * 4 threads are rounded up to whole waves, and a
+    //  quad past the end only takes part in the shuffles)
+    const bool live = run < nruns;
+    const u32x4 v = live ? reinterpret_cast<const u32x4*>(x)[g] : u32x4{0u, 0u, 0u, 0u};
     uint32_t m = 0;  // largest |x| as bf16 bits (finite values order as integers)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) m = max(m, max(v[j][w] & 0x7FFFu, (v[j][w] >> 16) & 0x7FFFu));
+    for (int w = 0; w < 4; ++w) m = max(m, max(v[w] & 0x7FFFu, (v[w] >> 16) & 0x7FFFu));
+    m = max(m, (uint32_t)__shfl_xor((int)m, 1, MOE_WAVE));
+    m = max(m, (uint32_t)__shfl_xor((int)m, 2, MOE_WAVE));
+    if (!live) return;
     const int eb = (int)(m >> 7);
     const bool bad = m >= 0x7F80u;
     const int X = max(eb - 129, -127);
     const float inv = __uint_as_float((uint32_t)(127 - X) << 23);  // 2^-X, 127 - X in [2, 254]
-    u32x4 out;
+    uint32_t word = 0;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        uint32_t word = 0;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const uint32_t b = (v[k][e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
-            const float a = __uint_as_float((b & 0x7FFFu) << 16) * inv;
-            const uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
-                               (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
-                               (uint32_t)(a > 5.0f);
-            word |= (c | ((b >> 12) & 8u)) << (4 * e);
-        }
-        out[k] = bad ? 0u : word;
+    for (int e = 0; e < 8; ++e) {
+        const uint32_t b = (v[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
+        const float a = __uint_as_float((b & 0x7FFFu) << 16) * inv;
+        const uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                           (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+                           (uint32_t)(a > 5.0f);
+        word |= (c | ((b >> 12) & 8u)) << (4 * e);
     }
-    *reinterpret_cast<u32x4*>(codes + i * 16) = out;
-    scales[i] = bad ? (uint8_t)255 : (uint8_t)(X + 127);
+    reinterpret_cast<uint32_t*>(codes)[g] = bad ? 0u : word;
+    if ((g & 3) == 0) scales[run] = bad ? (uint8_t)255 : (uint8_t)(X + 127);
 }
 
 int launch_quant_rows_mxfp4(const uint16_t* x, int T, int H, uint8_t* codes, uint8_t* scales,
@@ -183,7 +180,7 @@ int launch_quant_rows_mxfp4(const uint16_t* x, int T, int H, uint8_t* codes, uin
     if (T == 0) return MOE_OK;
     const long nruns = (long)T * (H / 32);
     prof_begin("quant_rows_mxfp4", stream);
-    quant_rows_mxfp4_kernel<<<(unsigned)((nruns + 255) / 256), 256, 0, stream>>>(x, nruns, codes, scales);
+    quant_rows_mxfp4_kernel<<<(unsigned)((4 * nruns + 255) / 256), 256, 0, stream>>>(x, nruns, codes, scales);
     prof_end(stream);
     return check_launch("quant_rows_mxfp4_kernel");
 }
