@@ -212,11 +212,15 @@ def test_pack_mx_scales_matches_reference(shape):
 # x quantised to E4M3 per token (gate/up or up as E4M3 x E2M1) or to MXFP4
 # (E2M1 x E2M1) on the scaled MFMA, with the E8M0 bytes as its per-lane
 # scales: against the oracle run on the same quantised rows
+# (MXFP4 x stages its scales from a per-tile table for H = 512 * 2^j <= 8192,
+#  H = 512 and 8192 below and the large workloads; per step otherwise: H = 256,
+#  768 and 8448)
 @pytest.mark.parametrize("variant", ["prefill_a8", "prefill_a4"])
 @pytest.mark.parametrize("layout", ["rowmajor", "tiled"])
 @pytest.mark.parametrize("activation", ["swiglu", "relu2"])
 @pytest.mark.parametrize("T,H,I,E,k", [(300, 512, 256, 8, 2), (257, 256, 384, 16, 4),
-                                       (129, 768, 128, 4, 1)])
+                                       (129, 768, 128, 4, 1), (41, 8192, 128, 4, 2),
+                                       (37, 8448, 128, 4, 2)])
 def test_mxfp4_prefill_quantised_x_shapes(T, H, I, E, k, activation, layout, variant):
     cfg = synth.MoeConfig("mxq", T=T, H=H, I=I, E=E, k=k, shared=True)
     c = gpu_case(cfg, seed=T + I + 1, activation=activation, weight_format="mxfp4")
