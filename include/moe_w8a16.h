@@ -223,7 +223,9 @@ typedef struct {
  *              output); applies to w13, w2 and the shared expert alike
  *   variant    MOE_VARIANT_*
  * H and I must be multiples of 128 (else MOE_EUNSUPPORTED); T >= 0; T == 0
- * is a no-op.  MOE_VARIANT_PREFILL also needs H and 2I to be multiples of
+ * is a no-op.  MOE_VARIANT_PREFILL_A4 takes MXFP4 weights only and gives
+ * MOE_EUNSUPPORTED here (and in the _ex and _noalloc forms).
+ * MOE_VARIANT_PREFILL also needs H and 2I to be multiples of
  * 256 (else MOE_EUNSUPPORTED); MOE_VARIANT_AUTO picks the decode variant for
  * such shapes and for batches of at most 16 routes per expert and 4096 routes
  * in all, the prefill variant otherwise.  The expert FFN computes in bf16 x
