@@ -28,6 +28,10 @@ from .moe_ref import (  # noqa: F401
     e4m3fn_encode_rne,
     quantize_rows_e4m3,
     quantize_rows_mxfp4,
+    round_bf16,
+    quantize_hidden_mxfp4,
+    hidden_mxfp4_deviation,
+    hidden_delta,
     dequantize_rows,
     route_softmax_topk,
     route_sigmoid_topk,

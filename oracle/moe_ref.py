@@ -226,6 +226,102 @@ def quantize_rows_mxfp4(x):
     return packed, np.where(bad, 255, X + 127).astype(np.uint8)
 
 
+def round_bf16(v) -> np.ndarray:
+    """Each float64 value rounded once to the nearest bfloat16 value (8
+    significant bits, exponent range of fp32, subnormals spaced 2^-133), ties
+    to the even significand; NaN and infinities pass through, magnitudes that
+    round past the largest bf16 value become infinities."""
+    v = np.asarray(v, dtype=np.float64)
+    m, e = np.frexp(v)  # v = m * 2^e, |m| in [0.5, 1)
+    e = np.maximum(e, -125)  # below 2^-126 the grid is the subnormal spacing 2^-133
+    with np.errstate(over="ignore", invalid="ignore"):
+        r = np.ldexp(np.rint(np.ldexp(v, 8 - e)), e - 8)
+        r = np.where(np.abs(r) > 3.3895313892515355e38, np.copysign(np.inf, v), r)
+    return np.where(np.isfinite(v), r, v)
+
+
+def quantize_hidden_mxfp4(a):
+    """The hidden activation before the down GEMM when it runs on MXFP4
+    activations: rows of float64 values (the SwiGLU or relu^2 output, [M, I])
+    rounded to bf16 as every variant does before the down GEMM, then
+    quantised by the MXFP4 activation rule of quantize_rows_mxfp4 (runs of 32
+    along I).  Returns the dequantised float64 rows."""
+    q, s = quantize_rows_mxfp4(round_bf16(a))
+    return dequantize_mx(q, s)
+
+
+def _e2m1_dequant_at(b, X):
+    """b (float64) quantised to E2M1 at the E8M0 exponent X by the grid rule
+    of quantize_rows_mxfp4 (nearest grid value of |b| / 2^X, ties to the even
+    code, saturating at 6, sign kept), then dequantised."""
+    sc = np.ldexp(1.0, X)
+    v = np.abs(b) / sc
+    mag = ((v > 0.25).astype(np.int64) + (v >= 0.75) + (v > 1.25) + (v >= 1.75) +
+           (v > 2.5) + (v >= 3.5) + (v > 5.0))
+    return np.copysign(_E2M1[mag] * sc, b)
+
+
+def _mx_exponent(amax):
+    """The run exponent of quantize_rows_mxfp4 for a largest magnitude amax."""
+    _, e = np.frexp(amax)
+    return np.clip(np.where(amax > 0, e - 1 - 2, -127), -127, 127)
+
+
+def hidden_mxfp4_deviation(a, delta):
+    """How far the quantised hidden activation can move when the value it is
+    taken from is only known to within +-delta: an upper bound, per element,
+    on |dq(b)_i - dq(bf16(a))_i| over bf16 vectors b whose element i lies in
+    [bf16(a_i - delta_i), bf16(a_i + delta_i)] (bf16 rounding is monotone,
+    so these are all the values the rounding can give), dq being
+    quantize_rows_mxfp4 then dequantize_mx.  A run's exponent can then take
+    any value between those of its smallest and largest possible maximum
+    magnitude; at a fixed exponent the E2M1 value of an element is monotone
+    in it, so the extremes sit at the ends of its interval.  The bound is the
+    largest distance over those exponents and ends; it is exact when the
+    exponent cannot move.  a, delta: float64 [M, I], finite, delta >= 0;
+    returns float64 [M, I]."""
+    a = np.asarray(a, dtype=np.float64)
+    delta = np.asarray(delta, dtype=np.float64)
+    M, I = a.shape
+    assert I % MX_BLOCK == 0 and np.all(delta >= 0), (I,)
+    nb = I // MX_BLOCK
+    ref = quantize_hidden_mxfp4(a).reshape(M, nb, MX_BLOCK)
+    lo = round_bf16(a - delta).reshape(M, nb, MX_BLOCK)
+    hi = round_bf16(a + delta).reshape(M, nb, MX_BLOCK)
+    least = np.where((lo <= 0) & (hi >= 0), 0.0, np.minimum(np.abs(lo), np.abs(hi)))
+    most = np.maximum(np.abs(lo), np.abs(hi))
+    X_lo = _mx_exponent(least.max(axis=2))[..., None]
+    X_hi = _mx_exponent(most.max(axis=2))[..., None]
+    moving = (X_hi > X_lo) | (hi > lo)
+    dev = np.zeros_like(ref)
+    for dx in range(int((X_hi - X_lo).max()) + 1 if M * nb else 0):
+        X = np.minimum(X_lo + dx, X_hi)
+        for b in (lo, hi):
+            d = np.abs(_e2m1_dequant_at(b, X) - ref)
+            dev = np.maximum(dev, np.where(moving, d, 0.0))
+    return dev.reshape(M, I)
+
+
+def hidden_delta(g, u, sg, su, K: int, activation: str = "swiglu"):
+    """An upper bound on how far a kernel's fp32 hidden value can be from the
+    exact one, used with hidden_mxfp4_deviation.  g, u: the exact gate and up
+    sums (float64), sg, su: the sums of the magnitudes of their K products,
+    all [M, I].  The kernel sums exact products in fp32, each addition rounded
+    (error at most K * 2^-24 * sum |products|); it evaluates
+    g / (1 + exp(-g)) * u in fp32 with an exponential whose argument error
+    grows with |g|, within (8 + |g|) * 2^-22 of the value (and flushes it to
+    zero below g = -80); relu^2 squares the rounded u.  The result is twice
+    the first-order propagation, plus the evaluation error and 2^-140."""
+    g, u, sg, su = (np.asarray(v, dtype=np.float64) for v in (g, u, sg, su))
+    dg, du = K * 2.0 ** -24 * sg, K * 2.0 ** -24 * su
+    if activation == "relu2":
+        h = relu2(u)
+        return 2.0 * (2.0 * np.maximum(u, 0.0) * du + du * du) + 2.0 ** -20 * h + 2.0 ** -140
+    h = np.abs(swiglu(g, u))
+    rel = np.where(g > -80.0, (8.0 + np.abs(g)) * 2.0 ** -22, 1.0)
+    return 2.0 * (1.1 * np.abs(u) * dg + np.abs(g) * du + dg * du) + rel * h + 2.0 ** -140
+
+
 def dequantize_weights(codes, scales, weight_format: str = "e4m3_128") -> np.ndarray:
     """Dequantised float64 weights of either stored format: "e4m3_128"
     (E4M3FN codes, fp32 128x128 block scales) or "mxfp4" (E2M1 codes two a
@@ -341,46 +437,83 @@ def relu2(u):
 
 
 def expert_mlp(xrows, w13, w13_scale, w2, w2_scale, activation="swiglu",
-               weight_format="e4m3_128"):
+               weight_format="e4m3_128", hidden="exact", bound=False):
     """One expert on rows of x (float64 [M, H]) -> float64 [M, H].
 
     SwiGLU: w13 [2I, H] (gate rows first, then up rows); relu2 ([SPARK] module
     documentation: up projection, then relu^2 and the down projection): w13
     [I, H] is the up projection alone.  w2 [H, I]; all block-scaled (see
-    dequantize_weights for the two formats)."""
+    dequantize_weights for the two formats).
+
+    hidden="mxfp4": the down GEMM takes the hidden activation quantised by
+    quantize_hidden_mxfp4 ([AITER] description: the producer quantises the
+    hidden activation to MXFP4 and runs the down projection in MXFP4).  With
+    bound=True also returns, per output element, an upper bound on how far a
+    kernel that takes the same quantisation decision from fp32 sums can be
+    from this result on that account: |W2| times hidden_mxfp4_deviation
+    under hidden_delta."""
     W13 = dequantize_weights(w13, w13_scale, weight_format)
+    K = W13.shape[1]
     if activation == "relu2":
-        a = relu2(xrows @ W13.T)
+        g = None
+        u = xrows @ W13.T
+        a = relu2(u)
     else:
         I = W13.shape[0] // 2
         g = xrows @ W13[:I].T
         u = xrows @ W13[I:].T
         a = swiglu(g, u)
     W2 = dequantize_weights(w2, w2_scale, weight_format)
-    return a @ W2.T
+    if hidden == "exact":
+        assert not bound
+        return a @ W2.T
+    assert hidden == "mxfp4", hidden
+    y = quantize_hidden_mxfp4(a) @ W2.T
+    if not bound:
+        return y
+    ax = np.abs(xrows)
+    if activation == "relu2":
+        su = ax @ np.abs(W13).T
+        delta = hidden_delta(None, u, None, su, K, "relu2")
+    else:
+        sg = ax @ np.abs(W13[:I]).T
+        su = ax @ np.abs(W13[I:]).T
+        delta = hidden_delta(g, u, sg, su, K)
+    return y, hidden_mxfp4_deviation(a, delta) @ np.abs(W2).T
 
 
 def moe_ffn(x, w13, w13_scale, w2, w2_scale, ids, aff, shared=None, activation="swiglu",
-            weight_format="e4m3_128"):
+            weight_format="e4m3_128", hidden="exact", bound=False):
     """out[t] = sum_j aff[t, j] * MLP_{ids[t, j]}(x[t]) (+ shared MLP(x[t])).
 
     x is [T, H] (bf16 values given as float32/float64), ids [T, k], aff [T, k].
     The routed terms are added expert by expert in ascending expert index, then
-    the shared expert with affinity exactly 1."""
+    the shared expert with affinity exactly 1.  hidden and bound as in
+    expert_mlp; with bound=True returns (out, bound) where bound[t] sums
+    |aff[t, j]| times each route's bound."""
     x = np.asarray(x, dtype=np.float64)
     ids = np.asarray(ids, dtype=np.int64)
     aff = np.asarray(aff, dtype=np.float64)
     T, H = x.shape
     out = np.zeros((T, H), dtype=np.float64)
+    bnd = np.zeros((T, H), dtype=np.float64)
+
+    def mlp(rows, w):
+        r = expert_mlp(rows, *w, activation, weight_format, hidden, bound)
+        return r if bound else (r, None)
+
     for e in np.unique(ids):
         t_idx, j_idx = np.nonzero(ids == e)
-        y = expert_mlp(x[t_idx], w13[e], w13_scale[e], w2[e], w2_scale[e], activation,
-                       weight_format)
+        y, b = mlp(x[t_idx], (w13[e], w13_scale[e], w2[e], w2_scale[e]))
         np.add.at(out, t_idx, aff[t_idx, j_idx][:, None] * y)
+        if bound:
+            np.add.at(bnd, t_idx, np.abs(aff[t_idx, j_idx])[:, None] * b)
     if shared is not None:
-        out += expert_mlp(x, shared["w13"], shared["w13_scale"],
-                          shared["w2"], shared["w2_scale"], activation, weight_format)
-    return out
+        y, b = mlp(x, (shared["w13"], shared["w13_scale"], shared["w2"], shared["w2_scale"]))
+        out += y
+        if bound:
+            bnd += b
+    return (out, bnd) if bound else out
 
 
 def moe_forward(x, logits, k, w13, w13_scale, w2, w2_scale, shared=None):

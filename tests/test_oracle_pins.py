@@ -252,6 +252,154 @@ def test_ffn_mxfp4_single_expert_and_mixture_are_dense_mlps():
     np.testing.assert_allclose(got, ref, rtol=1e-11, atol=1e-12 * np.abs(ref).max())
 
 
+# ------------------------------------------------- MXFP4 hidden activation
+def test_round_bf16_matches_torch_cast():
+    """fp32 values (sweeps, exact ties between bf16 neighbours, subnormals,
+    the largest finite values): one rounding to bf16 equals torch's
+    float32 -> bfloat16 conversion."""
+    g = torch.Generator().manual_seed(5)
+    v = torch.cat([torch.randn(4000, generator=g) * 10.0 ** torch.randint(-30, 30, (4000,), generator=g),
+                   torch.randn(500, generator=g) * 2.0 ** -130])
+    bits = v.view(torch.int32)
+    ties = ((bits & ~0xFFFF) | 0x8000).view(torch.float32)  # halfway between bf16 neighbours
+    v = torch.cat([v, ties, torch.tensor([3.3895e38, -3.3895e38, 0.0, -0.0, 2.0 ** -133])])
+    got = oracle.round_bf16(v.double().numpy())
+    ref = v.to(torch.bfloat16).double().numpy()
+    np.testing.assert_array_equal(got, ref)
+    np.testing.assert_array_equal(np.signbit(got), np.signbit(ref))
+
+
+def test_hidden_quantiser_rounds_to_bf16_first():
+    """1.25 + 2^-9 is bf16 1.25, an E2M1 tie at exponent 0 that goes to the
+    even code (1.0); quantised directly it would be 1.5.  Worked by hand."""
+    a = np.zeros((1, 32))
+    a[0, 0] = 6.0
+    a[0, 1] = 1.25 + 2.0 ** -9
+    a[0, 2] = 2.25
+    a[0, 3] = -0.3
+    got = oracle.quantize_hidden_mxfp4(a)
+    assert got[0, 0] == 6.0 and got[0, 1] == 1.0 and got[0, 2] == 2.0 and got[0, 3] == -0.5
+    assert np.all(got[0, 4:] == 0.0)
+
+
+def test_hidden_deviation_hand_cases():
+    """Worked by hand.  (1) The tie above: within 2^-8 the bf16 value can
+    also be 1.2578125, which rounds to 1.5, so only that element can move,
+    by 0.5; within 2^-12 nothing can.  (2) A run whose largest element can be
+    bf16 3.984375 (exponent -1: it saturates to 3.0, 1.0 stays 1.0, 0.30078125
+    gives 0.25) or 4.0 (exponent 0: 4.0, 1.0 and 0.5): deviations 1, 0, 0.25."""
+    a = np.zeros((1, 32))
+    a[0, 0], a[0, 1] = 6.0, 1.25 + 2.0 ** -9
+    d = np.zeros_like(a)
+    d[0, 1] = 2.0 ** -8
+    dev = oracle.hidden_mxfp4_deviation(a, d)
+    assert dev[0, 1] == 0.5 and np.count_nonzero(dev) == 1
+    d[0, 1] = 2.0 ** -12
+    assert not np.any(oracle.hidden_mxfp4_deviation(a, d))
+    a = np.zeros((1, 32))
+    a[0, :3] = [3.99, 1.0, 0.3]
+    d = np.zeros_like(a)
+    d[0, 0] = 0.01
+    dev = oracle.hidden_mxfp4_deviation(a, d)
+    np.testing.assert_array_equal(dev[0, :3], [1.0, 0.0, 0.25])
+    assert not np.any(dev[0, 3:])
+
+
+def test_hidden_deviation_bounds_brute_force():
+    """Random runs with a few elements near bf16 rounding points: enumerate
+    every bf16 vector the intervals allow, quantise each with
+    quantize_rows_mxfp4, and take the largest distance from the reference.
+    The oracle's bound covers it, and equals it wherever the run's exponent
+    was the same for every vector."""
+    rng = np.random.default_rng(8)
+    tab = oracle.e2m1_table()
+    for trial in range(60):
+        a = rng.standard_normal((1, 32)) * 2.0 ** rng.integers(-6, 6)
+        a[0, rng.integers(0, 32)] *= 3.0
+        if trial % 3 == 0:  # push some elements onto E2M1 ties of their run
+            X = int(np.frexp(np.abs(a).max())[1]) - 3
+            for i in rng.choice(32, 4, replace=False):
+                a[0, i] = np.sign(a[0, i]) * rng.choice([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]) * 2.0 ** X
+        d = np.zeros_like(a)
+        idx = rng.choice(32, 3, replace=False)
+        d[0, idx] = np.abs(a[0, idx]) * 2.0 ** -8.5
+        dev = oracle.hidden_mxfp4_deviation(a, d)[0]
+        ref = oracle.quantize_hidden_mxfp4(a)[0]
+        cands = []
+        for i in range(32):
+            lo = float(torch.tensor(a[0, i] - d[0, i]).float().to(torch.bfloat16).float())
+            hi = float(torch.tensor(a[0, i] + d[0, i]).float().to(torch.bfloat16).float())
+            vals = [lo]
+            while vals[-1] < hi:  # the next bf16 value up, from its bit pattern
+                bits = int(torch.tensor([vals[-1]]).to(torch.bfloat16).view(torch.int16)) & 0xFFFF
+                bits = bits + 1 if vals[-1] > 0 or bits == 0 else (1 if bits == 0x8000 else bits - 1)
+                nxt = torch.tensor([bits if bits < 0x8000 else bits - 0x10000],
+                                   dtype=torch.int16).view(torch.bfloat16).float()
+                vals.append(float(nxt))
+            cands.append(vals)
+        brute = np.zeros(32)
+        exps = set()
+        for vec in itertools.product(*cands):
+            q, sc = oracle.quantize_rows_mxfp4(np.array([vec]))
+            exps.add(int(sc[0, 0]))
+            codes = oracle.unpack_fp4(q)[0]
+            dq = tab[codes] * 2.0 ** (int(sc[0, 0]) - 127)
+            brute = np.maximum(brute, np.abs(dq - ref))
+        assert np.all(brute <= dev), trial
+        if len(exps) == 1:
+            np.testing.assert_array_equal(brute, dev)
+
+
+def test_hidden_delta_covers_fp32_recursive_sums():
+    """The summation part of hidden_delta: sequential fp32 sums of exact
+    products (random order, random signs, heavy cancellation) stay within
+    K * 2^-24 * sum|products| of the float64 sum."""
+    rng = np.random.default_rng(3)
+    for K in (64, 512, 2048):
+        for _ in range(20):
+            p = (rng.standard_normal(K) * 2.0 ** rng.integers(-8, 8, K)).astype(np.float32)
+            p[: K // 2] = -p[K // 2:] * (1 + 2.0 ** -20)  # near-total cancellation
+            rng.shuffle(p)
+            acc = np.float32(0.0)
+            for v in p:
+                acc = np.float32(acc + v)
+            exact = float(np.sum(p.astype(np.float64)))
+            assert abs(float(acc) - exact) <= K * 2.0 ** -24 * float(np.abs(p.astype(np.float64)).sum())
+
+
+def test_ffn_hidden_mxfp4_one_hot_closed_form():
+    """relu^2 expert with one-hot x rows and E2M1 weights of 1.0 and 1.5
+    (scale byte 127): the up sums u are the weight values, relu(u)^2 is
+    1 or 2.25, and a run holding 2.25 with largest value 2.25 takes exponent
+    -1 (2.25 / 0.5 = 4.5 -> 4, i.e. 2.0) -- the down weights (identity)
+    return the quantised hidden values themselves.  Worked by hand."""
+    I = H = 64
+    # up rows: row i reads x column i with weight 1.5 (i even) or 1.0 (i odd)
+    codes = np.zeros((I, H), np.uint8)
+    for i in range(I):
+        codes[i, i] = 3 if i % 2 == 0 else 2   # E2M1 1.5 and 1.0
+    w13 = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)[None]
+    eye = np.zeros((H, I), np.uint8)
+    eye[np.arange(H), np.arange(H)] = 2
+    w2 = (eye[:, 0::2] | (eye[:, 1::2] << 4)).astype(np.uint8)[None]
+    s13 = np.full((1, I, H // 32), 127, np.uint8)
+    s2 = np.full((1, H, I // 32), 127, np.uint8)
+    x = np.ones((1, H))
+    y = oracle.moe_ffn(x, w13, s13, w2, s2, np.zeros((1, 1), np.int64), np.ones((1, 1)),
+                       activation="relu2", weight_format="mxfp4", hidden="mxfp4")
+    # relu(u)^2 = 2.25 (even i), 1.0 (odd i); run amax 2.25 -> X = -1: 2.25/0.5 = 4.5 -> 4
+    # (midpoint 5 above), 1.0/0.5 = 2 -> 2
+    want = np.where(np.arange(H) % 2 == 0, 2.0, 1.0)
+    np.testing.assert_array_equal(y[0], want)
+    y_exact = oracle.moe_ffn(x, w13, s13, w2, s2, np.zeros((1, 1), np.int64), np.ones((1, 1)),
+                             activation="relu2", weight_format="mxfp4")
+    np.testing.assert_array_equal(y_exact[0], np.where(np.arange(H) % 2 == 0, 2.25, 1.0))
+    y2, b = oracle.moe_ffn(x, w13, s13, w2, s2, np.zeros((1, 1), np.int64), np.ones((1, 1)),
+                           activation="relu2", weight_format="mxfp4", hidden="mxfp4", bound=True)
+    np.testing.assert_array_equal(y2, y)
+    assert not np.any(b)  # exact sums of one product: no element near a rounding point
+
+
 # ----------------------------------------------------------------- E4M3FN
 def test_e4m3fn_all_codes_match_torch_cast():
     codes = torch.arange(256, dtype=torch.int64).to(torch.uint8)
