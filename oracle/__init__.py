@@ -32,6 +32,7 @@ from .moe_ref import (  # noqa: F401
     quantize_hidden_mxfp4,
     hidden_mxfp4_deviation,
     hidden_delta,
+    mx_gemm_error_bound,
     dequantize_rows,
     route_softmax_topk,
     route_sigmoid_topk,

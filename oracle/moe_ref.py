@@ -278,11 +278,13 @@ def hidden_mxfp4_deviation(a, delta):
     magnitude; at a fixed exponent the E2M1 value of an element is monotone
     in it, so the extremes sit at the ends of its interval.  The bound is the
     largest distance over those exponents and ends; it is exact when the
-    exponent cannot move.  a, delta: float64 [M, I], finite, delta >= 0;
-    returns float64 [M, I]."""
+    exponent cannot move.  a, delta: float64 [M, I], delta >= 0; returns
+    float64 [M, I].  A run holding a non-finite value quantises to NaN
+    whatever its neighbours do (quantize_rows_mxfp4), so it gets no bound."""
     a = np.asarray(a, dtype=np.float64)
     delta = np.asarray(delta, dtype=np.float64)
     M, I = a.shape
+    delta = np.where(np.isnan(delta), 0.0, delta)
     assert I % MX_BLOCK == 0 and np.all(delta >= 0), (I,)
     nb = I // MX_BLOCK
     ref = quantize_hidden_mxfp4(a).reshape(M, nb, MX_BLOCK)
@@ -299,27 +301,57 @@ def hidden_mxfp4_deviation(a, delta):
         for b in (lo, hi):
             d = np.abs(_e2m1_dequant_at(b, X) - ref)
             dev = np.maximum(dev, np.where(moving, d, 0.0))
-    return dev.reshape(M, I)
+    return np.where(np.isfinite(ref), dev, 0.0).reshape(M, I)
 
 
-def hidden_delta(g, u, sg, su, K: int, activation: str = "swiglu"):
+def mx_gemm_error_bound(xrows, W, step: int = 64):
+    """An upper bound on |fl32(xrows @ W.T) - xrows @ W.T| for a product of
+    MXFP4 values (E2M1 codes times powers of two, on both sides) taken the
+    way the scaled FP4 MFMA takes it: K in steps of 64, each step adding its
+    two 32-element blocks to an fp32 accumulator.  A block's 32 products are
+    multiples of one power of two (a quarter of the product of its two
+    scales) of magnitude at most 32 * 36, so their sum is exact in fp32; a
+    step then rounds at most twice in whatever order it adds its two block
+    sums B0, B1 to the accumulator, each time by at most 2^-24 of the result.
+    With S_j the exact running sum after step j, the error is at most
+    2 * 2^-24 * sum_j (|S_j| + |S_{j-1}| + |B0_j| + |B1_j|) (the factor 2
+    covering the second-order terms).  xrows [M, K], W [N, K] float64,
+    K % 64 == 0; returns [M, N]."""
+    xrows = np.asarray(xrows, dtype=np.float64)
+    W = np.asarray(W, dtype=np.float64)
+    M, K = xrows.shape
+    assert K % step == 0 and W.shape[1] == K
+    h = step // 2
+    S = np.zeros((M, W.shape[0]))
+    tot = np.zeros_like(S)
+    for j in range(K // step):
+        k0 = j * step
+        B0 = xrows[:, k0:k0 + h] @ W[:, k0:k0 + h].T
+        B1 = xrows[:, k0 + h:k0 + step] @ W[:, k0 + h:k0 + step].T
+        Sn = S + B0 + B1
+        tot += np.abs(Sn) + np.abs(S) + np.abs(B0) + np.abs(B1)
+        S = Sn
+    return 2.0 * 2.0 ** -24 * tot
+
+
+def hidden_delta(g, u, eg, eu, activation: str = "swiglu"):
     """An upper bound on how far a kernel's fp32 hidden value can be from the
     exact one, used with hidden_mxfp4_deviation.  g, u: the exact gate and up
-    sums (float64), sg, su: the sums of the magnitudes of their K products,
-    all [M, I].  The kernel sums exact products in fp32, each addition rounded
-    (error at most K * 2^-24 * sum |products|); it evaluates
+    sums (float64; g unused for relu^2), eg, eu: bounds on the fp32 error of
+    those sums (mx_gemm_error_bound), all [M, I].  The kernel evaluates
     g / (1 + exp(-g)) * u in fp32 with an exponential whose argument error
     grows with |g|, within (8 + |g|) * 2^-22 of the value (and flushes it to
     zero below g = -80); relu^2 squares the rounded u.  The result is twice
-    the first-order propagation, plus the evaluation error and 2^-140."""
-    g, u, sg, su = (np.asarray(v, dtype=np.float64) for v in (g, u, sg, su))
-    dg, du = K * 2.0 ** -24 * sg, K * 2.0 ** -24 * su
+    the first-order propagation of eg and eu, plus that evaluation error and
+    2^-140."""
+    u, eu = np.asarray(u, dtype=np.float64), np.asarray(eu, dtype=np.float64)
     if activation == "relu2":
         h = relu2(u)
-        return 2.0 * (2.0 * np.maximum(u, 0.0) * du + du * du) + 2.0 ** -20 * h + 2.0 ** -140
+        return 2.0 * (2.0 * np.maximum(u, 0.0) * eu + eu * eu) + 2.0 ** -20 * h + 2.0 ** -140
+    g, eg = np.asarray(g, dtype=np.float64), np.asarray(eg, dtype=np.float64)
     h = np.abs(swiglu(g, u))
     rel = np.where(g > -80.0, (8.0 + np.abs(g)) * 2.0 ** -22, 1.0)
-    return 2.0 * (1.1 * np.abs(u) * dg + np.abs(g) * du + dg * du) + rel * h + 2.0 ** -140
+    return 2.0 * (1.1 * np.abs(u) * eg + np.abs(g) * eu + eg * eu) + rel * h + 2.0 ** -140
 
 
 def dequantize_weights(codes, scales, weight_format: str = "e4m3_128") -> np.ndarray:
@@ -448,12 +480,12 @@ def expert_mlp(xrows, w13, w13_scale, w2, w2_scale, activation="swiglu",
     hidden="mxfp4": the down GEMM takes the hidden activation quantised by
     quantize_hidden_mxfp4 ([AITER] description: the producer quantises the
     hidden activation to MXFP4 and runs the down projection in MXFP4).  With
-    bound=True also returns, per output element, an upper bound on how far a
-    kernel that takes the same quantisation decision from fp32 sums can be
-    from this result on that account: |W2| times hidden_mxfp4_deviation
-    under hidden_delta."""
+    bound=True (x rows of MXFP4 values and MXFP4 weights, as on that path)
+    also returns, per output element, an upper bound on how far a kernel that
+    takes the same quantisation decision from fp32 sums can be from this
+    result on that account: |W2| times hidden_mxfp4_deviation under
+    hidden_delta of the gate/up sums' mx_gemm_error_bound."""
     W13 = dequantize_weights(w13, w13_scale, weight_format)
-    K = W13.shape[1]
     if activation == "relu2":
         g = None
         u = xrows @ W13.T
@@ -471,14 +503,10 @@ def expert_mlp(xrows, w13, w13_scale, w2, w2_scale, activation="swiglu",
     y = quantize_hidden_mxfp4(a) @ W2.T
     if not bound:
         return y
-    ax = np.abs(xrows)
     if activation == "relu2":
-        su = ax @ np.abs(W13).T
-        delta = hidden_delta(None, u, None, su, K, "relu2")
+        delta = hidden_delta(None, u, None, mx_gemm_error_bound(xrows, W13), "relu2")
     else:
-        sg = ax @ np.abs(W13[:I]).T
-        su = ax @ np.abs(W13[I:]).T
-        delta = hidden_delta(g, u, sg, su, K)
+        delta = hidden_delta(g, u, mx_gemm_error_bound(xrows, W13[:I]), mx_gemm_error_bound(xrows, W13[I:]))
     return y, hidden_mxfp4_deviation(a, delta) @ np.abs(W2).T
 
 

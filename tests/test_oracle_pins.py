@@ -350,21 +350,29 @@ def test_hidden_deviation_bounds_brute_force():
             np.testing.assert_array_equal(brute, dev)
 
 
-def test_hidden_delta_covers_fp32_recursive_sums():
-    """The summation part of hidden_delta: sequential fp32 sums of exact
-    products (random order, random signs, heavy cancellation) stay within
-    K * 2^-24 * sum|products| of the float64 sum."""
+def test_mx_gemm_error_bound_covers_simulated_fp32_steps():
+    """mx_gemm_error_bound against a float32 simulation of the K loop it
+    describes (each 32-element block summed exactly, then the two blocks of
+    a 64-K step added to the accumulator in either order, every addition
+    rounded to fp32): random MXFP4 operands with wide exponent spreads and
+    near-cancelling rows stay within the bound."""
     rng = np.random.default_rng(3)
+    tab = oracle.e2m1_table()
     for K in (64, 512, 2048):
-        for _ in range(20):
-            p = (rng.standard_normal(K) * 2.0 ** rng.integers(-8, 8, K)).astype(np.float32)
-            p[: K // 2] = -p[K // 2:] * (1 + 2.0 ** -20)  # near-total cancellation
-            rng.shuffle(p)
-            acc = np.float32(0.0)
-            for v in p:
-                acc = np.float32(acc + v)
-            exact = float(np.sum(p.astype(np.float64)))
-            assert abs(float(acc) - exact) <= K * 2.0 ** -24 * float(np.abs(p.astype(np.float64)).sum())
+        x = tab[rng.integers(0, 16, (6, K))] * 2.0 ** rng.integers(-20, 20, (6, K // 32)).repeat(32, 1)
+        w = tab[rng.integers(0, 16, (5, K))] * 2.0 ** rng.integers(-20, 20, (5, K // 32)).repeat(32, 1)
+        x[0] = -x[1]  # a row whose sums cancel against the next one's
+        bound = oracle.mx_gemm_error_bound(x, w)
+        exact = x @ w.T
+        for order in (0, 1):
+            acc = np.zeros((6, 5), np.float32)
+            for j in range(K // 64):
+                b0 = (x[:, 64 * j:64 * j + 32] @ w[:, 64 * j:64 * j + 32].T).astype(np.float32)
+                b1 = (x[:, 64 * j + 32:64 * j + 64] @ w[:, 64 * j + 32:64 * j + 64].T).astype(np.float32)
+                # the block sums are exact in fp32 (checked), the step rounds its additions
+                assert np.array_equal(b0.astype(np.float64), x[:, 64 * j:64 * j + 32] @ w[:, 64 * j:64 * j + 32].T)
+                acc = (acc + b0) + b1 if order == 0 else acc + (b0 + b1)
+            assert np.all(np.abs(acc.astype(np.float64) - exact) <= bound), (K, order)
 
 
 def test_ffn_hidden_mxfp4_one_hot_closed_form():
