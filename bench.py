@@ -578,7 +578,7 @@ def fused_variant_bench(cfg, dev, L, seed=0, activation="swiglu", variant="auto"
                            "frac": round(kb / (kus * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                            "traffic": profiled_traffic("decode_fused_expert_mxfp4", cfg.name),
                            "traffic_unit": "bytes per launch"}
-    a4 = [n for n in prof if n.endswith("_a4")]
+    a4 = [n for n in prof if n.endswith(("_a4", "_a4h4")) and not n.startswith("prefill_down")]
     if a4:
         # the E2M1 x E2M1 gate/up (or up) GEMM against the FP4 MFMA peak
         kus = prof[a4[0]][1] * 1e3
@@ -586,6 +586,14 @@ def fused_variant_bench(cfg, dev, L, seed=0, activation="swiglu", variant="auto"
         out["fp4_gemm"] = {"kernel": a4[0], "avg_us": round(kus, 3), "flops": kfl,
                            "TFLOP_per_s": round(kfl / (kus * 1e-6) / 1e12, 1),
                            "peak": FP4_PEAK_TFLOPS, "frac": round(kfl / (kus * 1e-6) / 1e12 / FP4_PEAK_TFLOPS, 4)}
+    if "prefill_down_mxfp4_a4" in prof:
+        # the E2M1 x E2M1 down GEMM (MXFP4 hidden activation) against the FP4 peak
+        dus = prof["prefill_down_mxfp4_a4"][1] * 1e3
+        dfl = 2.0 * H * I * rows
+        out["fp4_down_gemm"] = {"kernel": "prefill_down_mxfp4_a4", "avg_us": round(dus, 3), "flops": dfl,
+                                "TFLOP_per_s": round(dfl / (dus * 1e-6) / 1e12, 1),
+                                "peak": FP4_PEAK_TFLOPS,
+                                "frac": round(dfl / (dus * 1e-6) / 1e12 / FP4_PEAK_TFLOPS, 4)}
     a8 = [n for n in prof if n.endswith("_a8")]
     if a8:
         # the fp8 x fp8 gate/up (or up) GEMM against the FP8 MFMA peak
@@ -756,10 +764,11 @@ def main():
                                                        args.seed, weight_format="mxfp4"))
         if args.prefill_workload and not args.no_a8:
             # x quantised to E4M3 per token (gate/up as E4M3 x E2M1 on the FP8
-            # MFMA) or to MXFP4 (E2M1 x E2M1)
+            # MFMA) or to MXFP4 (E2M1 x E2M1), and both GEMMs on MXFP4
+            # operands (the hidden activation quantised too)
             for wname in dict.fromkeys([args.prefill_workload] +
                                        ([] if args.no_extra_workloads else ["prefill16k_wide"])):
-                for v in ("prefill_a8", "prefill_a4"):
+                for v in ("prefill_a8", "prefill_a4", "prefill_fp4"):
                     result["mxfp4"].append(fused_variant_bench(synth.CONFIGS[wname], dev,
                                                                2 if wname == "prefill8k_skew" else 1,
                                                                args.seed, variant=v,

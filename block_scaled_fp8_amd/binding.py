@@ -21,7 +21,7 @@ MOE_STATUS_NONFINITE_LOGIT = 2
 MOE_MAX_EXPERTS = 1024
 MOE_MAX_TOPK = 16
 MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
-VARIANTS = {"auto": 0, "decode": 1, "prefill": 2, "prefill_a8": 3, "prefill_a4": 4}
+VARIANTS = {"auto": 0, "decode": 1, "prefill": 2, "prefill_a8": 3, "prefill_a4": 4, "prefill_fp4": 5}
 ACTIVATIONS = {"swiglu": 0, "relu2": 1}
 LAYOUTS = {"rowmajor": 0, "tiled": 1}
 

@@ -44,10 +44,12 @@ struct FusedLayout {
 // contribution row per route (+ shared rows + a trash row): fp32 for the
 // decode variant, block floating point (2 bytes a value + one exponent byte
 // per 8) for the prefill ones; AUTO is sized for either.  The fp8-activation
-// variant appends the E4M3 codes and per-token scales of x.
+// variant appends the E4M3 codes and per-token scales of x, the MXFP4 ones
+// its E2M1 codes and E8M0 bytes (MOE_VARIANT_PREFILL_FP4 keeps the MXFP4
+// hidden activation inside abuf).
 static FusedLayout fused_layout(int T, int H, int I, int E, int k, int has_shared, int variant) {
     const bool fp8_x = variant == MOE_VARIANT_PREFILL_A8;
-    const bool fp4_x = variant == MOE_VARIANT_PREFILL_A4;
+    const bool fp4_x = variant == MOE_VARIANT_PREFILL_A4 || variant == MOE_VARIANT_PREFILL_FP4;
     const bool compact = variant == MOE_VARIANT_PREFILL || fp8_x || fp4_x;
     FusedLayout L;
     const size_t R = (size_t)T * k;
@@ -229,7 +231,7 @@ int moe_sort(const int32_t* ids, int T, int k, int E, int32_t* counts, int32_t* 
 size_t moe_fused_workspace_bytes(int T, int H, int I, int E, int k, int has_shared,
                                  int variant) {
     if (T < 0 || H < 1 || I < 1 || E < 1 || k < 1) return 0;
-    if (variant < MOE_VARIANT_AUTO || variant > MOE_VARIANT_PREFILL_A4) return 0;
+    if (variant < MOE_VARIANT_AUTO || variant > MOE_VARIANT_PREFILL_FP4) return 0;
     return fused_layout(T, H, I, E, k, has_shared ? 1 : 0, variant).total;
 }
 
@@ -263,12 +265,13 @@ static int fused_impl(const char* who, const void* x, const uint8_t* w13, const 
         set_error("unknown weight layout %d", weight_layout);
         return MOE_EINVAL;
     }
-    if (variant < MOE_VARIANT_AUTO || variant > MOE_VARIANT_PREFILL_A4) {
+    if (variant < MOE_VARIANT_AUTO || variant > MOE_VARIANT_PREFILL_FP4) {
         set_error("unknown variant %d", variant);
         return MOE_EINVAL;
     }
-    if (variant == MOE_VARIANT_PREFILL_A4 && !mx4) {
-        set_error("%s: MXFP4 activations (MOE_VARIANT_PREFILL_A4) need MXFP4 weights", who);
+    if ((variant == MOE_VARIANT_PREFILL_A4 || variant == MOE_VARIANT_PREFILL_FP4) && !mx4) {
+        set_error("%s: MXFP4 activations (MOE_VARIANT_PREFILL_A4, MOE_VARIANT_PREFILL_FP4) need MXFP4 weights",
+                  who);
         return MOE_EUNSUPPORTED;
     }
     if (T == 0) return MOE_OK;
@@ -304,7 +307,8 @@ static int fused_impl(const char* who, const void* x, const uint8_t* w13, const 
     }
     const int has_shared = shared ? 1 : 0;
     const bool fp8_x = variant == MOE_VARIANT_PREFILL_A8;
-    const bool fp4_x = variant == MOE_VARIANT_PREFILL_A4;
+    const bool fp4_h = variant == MOE_VARIANT_PREFILL_FP4;
+    const bool fp4_x = variant == MOE_VARIANT_PREFILL_A4 || fp4_h;
     // the prefill GEMMs stage MXFP4 scales with 4-byte loads
     const bool mx_sc4 = !mx4 || ((((uintptr_t)w13_scale | (uintptr_t)w2_scale |
                                   (shared ? (uintptr_t)shared->w13_scale | (uintptr_t)shared->w2_scale : 0)) &
@@ -383,7 +387,8 @@ static int fused_impl(const char* who, const void* x, const uint8_t* w13, const 
                 return rc;
             rc = launch_prefill_ffn(weight_layout, xb, w13, w13_scale, w2, w2_scale, sh, p, T, H, I,
                                     E, k, abuf, ybuf, act, xq, xsc,
-                                    fp4_x ? AFMT_MXFP4 : fp8_x ? AFMT_E4M3 : AFMT_BF16, wfmt, s);
+                                    fp4_h ? AFMT_MXFP4_H4 : fp4_x ? AFMT_MXFP4 : fp8_x ? AFMT_E4M3 : AFMT_BF16,
+                                    wfmt, s);
         }
     }
     if (rc) return rc;
@@ -491,11 +496,11 @@ int moe_fused_w8a16_noalloc(const void* x, const uint8_t* w13, const float* w13_
         set_error("H and I must be positive multiples of 128 (got H=%d, I=%d)", H, I);
         return MOE_EUNSUPPORTED;
     }
-    if (variant < MOE_VARIANT_AUTO || variant > MOE_VARIANT_PREFILL_A4) {
+    if (variant < MOE_VARIANT_AUTO || variant > MOE_VARIANT_PREFILL_FP4) {
         set_error("unknown variant %d", variant);
         return MOE_EINVAL;
     }
-    if (variant == MOE_VARIANT_PREFILL_A4) {
+    if (variant == MOE_VARIANT_PREFILL_A4 || variant == MOE_VARIANT_PREFILL_FP4) {
         set_error("moe_fused_w8a16_noalloc: MXFP4 activations need MXFP4 weights");
         return MOE_EUNSUPPORTED;
     }

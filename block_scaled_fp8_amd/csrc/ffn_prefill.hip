@@ -64,6 +64,7 @@
 
 #include "common.hpp"
 #include "plan.hpp"
+#include "mxfp4_act.hpp"
 
 namespace moe {
 
@@ -74,7 +75,7 @@ constexpr int PF_XCD_RUN = 8;  // consecutive row tiles an XCD takes at a time
 // MFMA tiles of 32 x 32), STAGES LDS stages of 64-wide K, OCC workgroups per
 // CU (the register budget follows from it).
 template <int BM_, int BN_, int WM_, int WN_, int STAGES_, int OCC_, int M16_ = 0, int A8_ = 0,
-          int MX4_ = 0, int A4_ = 0>
+          int MX4_ = 0, int A4_ = 0, int H4_ = 0>
 struct PfCfg {
     static constexpr int OCC = OCC_;
     // MFMA shape: v_mfma_f32_16x16x32_bf16 (M16) or v_mfma_f32_32x32x16_bf16;
@@ -98,6 +99,11 @@ struct PfCfg {
     static constexpr bool A4 = A4_ != 0;
     static constexpr bool XT = A4_ == 2;
     static_assert(!A4 || (A8 && MX4), "MXFP4 activations pair with MXFP4 weights");
+    // H4 (gate/up and up, with A4): the hidden activation leaves as MXFP4,
+    // E2M1 codes [rows][I/2] and E8M0 bytes [rows][I/32], for a down GEMM
+    // that takes MXFP4 activations (A4 with MODE PF_DOWN)
+    static constexpr bool H4 = H4_ != 0;
+    static_assert(!H4 || A4, "the MXFP4 hidden activation belongs to the MXFP4 pipeline");
     static constexpr int MS = M16 ? 16 : 32;  // rows = columns of one MFMA tile
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
     static constexpr int THREADS = WM * WN * MOE_WAVE;
@@ -154,6 +160,13 @@ using PfGateUpMxA4 = PfCfg<128, 256, 2, 2, 3, 2, 0, 1, 1, 1>;
 using PfUpNarrowMxA4 = PfCfg<128, 128, 2, 1, 3, 2, 0, 1, 1, 1>;
 using PfGateUpMxA4T = PfCfg<128, 256, 2, 2, 3, 2, 0, 1, 1, 2>;
 using PfUpNarrowMxA4T = PfCfg<128, 128, 2, 1, 3, 2, 0, 1, 1, 2>;
+// ... and the hidden activation quantised to MXFP4 in the epilogue, for the
+// down GEMM on MXFP4 activations (per-step scales of the hidden rows)
+using PfGateUpMxA4H = PfCfg<128, 256, 2, 2, 3, 2, 0, 1, 1, 1, 1>;
+using PfUpNarrowMxA4H = PfCfg<128, 128, 2, 1, 3, 2, 0, 1, 1, 1, 1>;
+using PfGateUpMxA4TH = PfCfg<128, 256, 2, 2, 3, 2, 0, 1, 1, 2, 1>;
+using PfUpNarrowMxA4TH = PfCfg<128, 128, 2, 1, 3, 2, 0, 1, 1, 2, 1>;
+using PfDownMxA4 = PfCfg<128, 256, 2, 2, 3, 2, 0, 1, 1, 1>;
 // the x-scale table (XT): 128 rows of H/32 bytes, at most 32 KB; a row is a
 // power-of-two number of 16-byte pieces (the slot swizzle XORs piece indices)
 constexpr int PF_XT_MAX_H = 8192;
@@ -239,7 +252,8 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
     const uint8_t* __restrict__ wexp, const void* __restrict__ sexp,
     const uint8_t* __restrict__ wsh, const void* __restrict__ ssh, Plan plan,
     int T, int H, int I, int k, int nblk, int max_tiles,
-    uint16_t* __restrict__ abuf_out, float* __restrict__ ybuf, const void* __restrict__ xscale) {
+    uint16_t* __restrict__ abuf_out, float* __restrict__ ybuf, const void* __restrict__ xscale,
+    uint8_t* __restrict__ hscale_out) {
     constexpr int BM = C::BM, BN = C::BN;
     extern __shared__ __attribute__((aligned(16))) char smem[];
     __shared__ int row_tok[BM];  // gate/up: token row of x
@@ -367,11 +381,17 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
     }
     constexpr uint32_t SCS = LAYOUT == LAYOUT_TILED ? 64 : 4;  // per 128-K chunk
     // A4: lane l of wave w stages the 4 E8M0 bytes of activation row
-    // (64 w + l) % BM (row-major [T][H/32]) for the step's 128-K chunk, at
-    // byte 4 row of the stage's activation-scale area (with four waves the
-    // rows are staged twice, the second copy unused)
+    // (64 w + l) % BM (row-major [T][H/32]; down: the hidden rows
+    // [rows][I/32] at the sorted rows, padding rows reading the tile's first)
+    // for the step's 128-K chunk, at byte 4 row of the stage's
+    // activation-scale area (with four waves the rows are staged twice, the
+    // second copy unused)
     uint32_t xsrc = 0;
-    if constexpr (C::A4 && !C::XT) xsrc = (uint32_t)row_tok[(64 * wave + lane) % BM] * (uint32_t)(H / 32);
+    if constexpr (C::A4 && !C::XT) {
+        const int r = (64 * wave + lane) % BM;
+        xsrc = GATHER ? (uint32_t)row_tok[r] * (uint32_t)(H / 32)
+                      : (uint32_t)(p0 + (r < rows_here ? r : 0)) * (uint32_t)(I / 32);
+    }
 
     auto issue_stage = [&](int st, int kc) {
         const uint32_t sbase = st * C::STAGE;
@@ -999,8 +1019,27 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
         const int c = 8 * (lane % LPR);
         const int m = wm * C::WROWS + r;  // row of the tile
         const u32x4 v = *reinterpret_cast<const u32x4*>(slab + r * OUTC + c);
-        if (m < rows_here)
+        if constexpr (C::H4) {
+            // MXFP4: a lane quad holds one 32-column run of a row (OUTC is a
+            // multiple of 32 and colbase of 32), its largest magnitude shared
+            // by shuffles; a lane writes its 8 codes (4 bytes), the quad's
+            // first lane the E8M0 byte
+            uint32_t mx = bf16x8_absmax_bits(v);
+            mx = max(mx, (uint32_t)__shfl_xor((int)mx, 1, MOE_WAVE));
+            mx = max(mx, (uint32_t)__shfl_xor((int)mx, 2, MOE_WAVE));
+            const bool bad = mx >= 0x7F80u;
+            const int X = mxfp4_run_exponent(mx);
+            const uint32_t word = bad ? 0u : mxfp4_encode8(v, X);
+            if (m < rows_here) {
+                const int col = colbase + c;
+                uint8_t* hq = reinterpret_cast<uint8_t*>(abuf_out);
+                *reinterpret_cast<uint32_t*>(hq + (size_t)(p0 + m) * (I / 2) + col / 2) = word;
+                if ((lane & 3) == 0)
+                    hscale_out[(size_t)(p0 + m) * (I / 32) + col / 32] = bad ? (uint8_t)255 : (uint8_t)(X + 127);
+            }
+        } else if (m < rows_here) {
             *reinterpret_cast<u32x4*>(abuf_out + (size_t)(p0 + m) * I + colbase + c) = v;
+        }
     }
 }
 
@@ -1011,7 +1050,8 @@ template <int MODE, int LAYOUT, class C>
 static int launch_pf(const uint16_t* x, const uint16_t* abuf_in, const uint8_t* wexp,
                      const void* sexp, const uint8_t* wsh, const void* ssh, const Plan& plan,
                      int T, int H, int I, int E, int k, int has_shared, uint16_t* abuf_out,
-                     float* ybuf, hipStream_t stream, const void* xscale = nullptr) {
+                     float* ybuf, hipStream_t stream, const void* xscale = nullptr,
+                     uint8_t* hscale_out = nullptr) {
     const int nblk = MODE == PF_GATEUP ? 2 * I / C::BN : (MODE == PF_UP ? I : H) / C::BN;
     const long R = (long)T * k;
     const long max_tiles = (R + C::BM - 1) / C::BM + E + (has_shared ? (T + C::BM - 1) / C::BM : 0);
@@ -1038,22 +1078,53 @@ static int launch_pf(const uint16_t* x, const uint16_t* abuf_in, const uint8_t* 
         set_error("prefill: x-scale table needs H = 512 * 2^j <= %d", PF_XT_MAX_H);
         return MOE_EINVAL;
     }
+    static_assert(!C::H4 || MODE != PF_DOWN, "H4 is an epilogue of the first GEMM");
+    static_assert(!C::H4 || (MODE == PF_GATEUP ? C::WCOLS / 2 : C::WCOLS) % 32 == 0, "whole MXFP4 runs a wave");
+    if (C::H4 && !hscale_out) {
+        set_error("prefill: the MXFP4 hidden activation needs its scale array");
+        return MOE_EINVAL;
+    }
+    if (C::A4 && !xscale) {
+        set_error("prefill: MXFP4 activations need their scale array");
+        return MOE_EINVAL;
+    }
     const char* pname =
-        MODE == PF_DOWN ? (C::MX4 ? "prefill_down_mxfp4" : "prefill_down")
+        MODE == PF_DOWN ? (C::A4 ? "prefill_down_mxfp4_a4" : C::MX4 ? "prefill_down_mxfp4" : "prefill_down")
         : MODE == PF_UP
-            ? (C::A4 ? "prefill_up_relu2_mxfp4_a4"
+            ? (C::H4 ? "prefill_up_relu2_mxfp4_a4h4"
+               : C::A4 ? "prefill_up_relu2_mxfp4_a4"
                : C::A8 ? (C::MX4 ? "prefill_up_relu2_mxfp4_a8" : "prefill_up_relu2_a8")
                        : (C::MX4 ? "prefill_up_relu2_mxfp4" : "prefill_up_relu2"))
-            : (C::A4 ? "prefill_gateup_swiglu_mxfp4_a4"
+            : (C::H4 ? "prefill_gateup_swiglu_mxfp4_a4h4"
+               : C::A4 ? "prefill_gateup_swiglu_mxfp4_a4"
                : C::A8 ? (C::MX4 ? "prefill_gateup_swiglu_mxfp4_a8" : "prefill_gateup_swiglu_a8")
                        : (C::MX4 ? "prefill_gateup_swiglu_mxfp4" : "prefill_gateup_swiglu"));
     prof_begin(pname, stream);
     prefill_gemm_kernel<MODE, LAYOUT, C><<<(unsigned)grid, C::THREADS, lds, stream>>>(
         x, abuf_in, wexp, sexp, wsh, ssh, plan, T, H, I, k, nblk, (int)max_tiles, abuf_out, ybuf,
-        xscale);
+        xscale, hscale_out);
     prof_end(stream);
     return check_launch(MODE == PF_GATEUP ? "prefill_gemm_kernel<gateup>"
                                           : (MODE == PF_UP ? "prefill_gemm_kernel<up>" : "prefill_gemm_kernel<down>"));
+}
+
+// The first GEMM on MXFP4 activations: gate/up (SwiGLU), or the up
+// projection (relu^2) on the wide tile CW or, where I % 256 != 0, the
+// narrow tile CN.
+template <int LAYOUT, class CW, class CN>
+static int launch_first_a4(const uint16_t* xa, const uint8_t* w13, const void* w13s, const SharedW& sh,
+                           const Plan& plan, int T, int H, int I, int E, int k, int hs, uint16_t* abuf,
+                           float* ybuf, int act, bool narrow, const void* xs, uint8_t* hsc,
+                           hipStream_t stream) {
+    const void* ss = sh.w13_scale;
+    if (act != ACT_RELU2)
+        return launch_pf<PF_GATEUP, LAYOUT, CW>(xa, nullptr, w13, w13s, sh.w13, ss, plan, T, H, I, E, k, hs,
+                                                abuf, ybuf, stream, xs, hsc);
+    if (narrow)
+        return launch_pf<PF_UP, LAYOUT, CN>(xa, nullptr, w13, w13s, sh.w13, ss, plan, T, H, I, E, k, hs, abuf,
+                                            ybuf, stream, xs, hsc);
+    return launch_pf<PF_UP, LAYOUT, CW>(xa, nullptr, w13, w13s, sh.w13, ss, plan, T, H, I, E, k, hs, abuf,
+                                        ybuf, stream, xs, hsc);
 }
 
 template <int LAYOUT>
@@ -1066,33 +1137,31 @@ static int launch_prefill_c(const uint16_t* x, const uint8_t* w13, const void* w
     int rc;
     const void* ss = sh.w13_scale;
     const bool narrow = act == ACT_RELU2 && I % 256 != 0;  // (I % 128 == 0)
-    if (mx4 && afmt == AFMT_MXFP4 && prefill_xscale_table(H)) {  // ... x scales from a per-tile table
+    if (mx4 && (afmt == AFMT_MXFP4 || afmt == AFMT_MXFP4_H4)) {
+        // MXFP4 weights and activations: E2M1 x E2M1 gate/up, the x scales
+        // from a per-tile table where H allows it
         const uint16_t* xa = reinterpret_cast<const uint16_t*>(xq);
-        if (act != ACT_RELU2)
-            rc = launch_pf<PF_GATEUP, LAYOUT, PfGateUpMxA4T>(xa, nullptr, w13, w13s, sh.w13, ss, plan, T, H, I,
-                                                             E, k, hs, abuf, ybuf, stream, xs);
-        else if (narrow)
-            rc = launch_pf<PF_UP, LAYOUT, PfUpNarrowMxA4T>(xa, nullptr, w13, w13s, sh.w13, ss, plan, T, H, I, E,
-                                                           k, hs, abuf, ybuf, stream, xs);
-        else
-            rc = launch_pf<PF_UP, LAYOUT, PfGateUpMxA4T>(xa, nullptr, w13, w13s, sh.w13, ss, plan, T, H, I, E, k,
-                                                         hs, abuf, ybuf, stream, xs);
-        if (rc == MOE_OK)
-            rc = launch_pf<PF_DOWN, LAYOUT, PfDownMx>(x, abuf, w2, w2s, sh.w2, sh.w2_scale, plan, T, H, I, E, k,
-                                                      hs, abuf, ybuf, stream);
-        return rc;
-    }
-    if (mx4 && afmt == AFMT_MXFP4) {  // MXFP4 weights and activations: E2M1 x E2M1 gate/up
-        const uint16_t* xa = reinterpret_cast<const uint16_t*>(xq);
-        if (act != ACT_RELU2)
-            rc = launch_pf<PF_GATEUP, LAYOUT, PfGateUpMxA4>(xa, nullptr, w13, w13s, sh.w13, ss, plan, T, H, I,
-                                                            E, k, hs, abuf, ybuf, stream, xs);
-        else if (narrow)
-            rc = launch_pf<PF_UP, LAYOUT, PfUpNarrowMxA4>(xa, nullptr, w13, w13s, sh.w13, ss, plan, T, H, I, E,
-                                                          k, hs, abuf, ybuf, stream, xs);
-        else
-            rc = launch_pf<PF_UP, LAYOUT, PfGateUpMxA4>(xa, nullptr, w13, w13s, sh.w13, ss, plan, T, H, I, E, k,
-                                                        hs, abuf, ybuf, stream, xs);
+        const bool xt = prefill_xscale_table(H);
+        if (afmt == AFMT_MXFP4_H4) {
+            // ... and the hidden activation to MXFP4 for an E2M1 x E2M1 down:
+            // its codes [rows][I/2] from the start of abuf, its E8M0 bytes
+            // [rows][I/32] after them (256-byte aligned; within abuf's
+            // rows * I * 2 bytes)
+            const size_t rows = (size_t)T * k + (hs ? (size_t)T : 0);
+            uint8_t* hsc = reinterpret_cast<uint8_t*>(abuf) + ((rows * (I / 2) + 255) & ~(size_t)255);
+            rc = xt ? launch_first_a4<LAYOUT, PfGateUpMxA4TH, PfUpNarrowMxA4TH>(
+                          xa, w13, w13s, sh, plan, T, H, I, E, k, hs, abuf, ybuf, act, narrow, xs, hsc, stream)
+                    : launch_first_a4<LAYOUT, PfGateUpMxA4H, PfUpNarrowMxA4H>(
+                          xa, w13, w13s, sh, plan, T, H, I, E, k, hs, abuf, ybuf, act, narrow, xs, hsc, stream);
+            if (rc == MOE_OK)
+                rc = launch_pf<PF_DOWN, LAYOUT, PfDownMxA4>(x, abuf, w2, w2s, sh.w2, sh.w2_scale, plan, T, H, I,
+                                                            E, k, hs, abuf, ybuf, stream, hsc);
+            return rc;
+        }
+        rc = xt ? launch_first_a4<LAYOUT, PfGateUpMxA4T, PfUpNarrowMxA4T>(
+                      xa, w13, w13s, sh, plan, T, H, I, E, k, hs, abuf, ybuf, act, narrow, xs, nullptr, stream)
+                : launch_first_a4<LAYOUT, PfGateUpMxA4, PfUpNarrowMxA4>(
+                      xa, w13, w13s, sh, plan, T, H, I, E, k, hs, abuf, ybuf, act, narrow, xs, nullptr, stream);
         if (rc == MOE_OK)
             rc = launch_pf<PF_DOWN, LAYOUT, PfDownMx>(x, abuf, w2, w2s, sh.w2, sh.w2_scale, plan, T, H, I, E, k,
                                                       hs, abuf, ybuf, stream);
@@ -1182,7 +1251,7 @@ int launch_prefill_ffn(int layout, const uint16_t* x, const uint8_t* w13, const 
                        const uint8_t* w2, const void* w2s, const SharedW& sh, const Plan& plan,
                        int T, int H, int I, int E, int k, uint16_t* abuf, float* ybuf,
                        int act, const uint8_t* xq, const void* xs, int afmt, int wfmt, hipStream_t stream) {
-    if (afmt == AFMT_MXFP4 && wfmt != WFMT_MXFP4) {
+    if ((afmt == AFMT_MXFP4 || afmt == AFMT_MXFP4_H4) && wfmt != WFMT_MXFP4) {
         set_error("prefill variant: MXFP4 activations need MXFP4 weights");
         return MOE_EUNSUPPORTED;
     }

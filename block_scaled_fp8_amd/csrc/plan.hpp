@@ -32,7 +32,7 @@ struct Plan {
 enum { WFMT_E4M3_128 = 0, WFMT_MXFP4 = 1 };
 // activation operand of the prefill gate/up GEMM: bf16 x, x quantised to
 // E4M3 per token (fp32 scale a row), or x quantised to MXFP4 (E8M0 a run of 32)
-enum { AFMT_BF16 = 0, AFMT_E4M3 = 1, AFMT_MXFP4 = 2 };
+enum { AFMT_BF16 = 0, AFMT_E4M3 = 1, AFMT_MXFP4 = 2, AFMT_MXFP4_H4 = 3 };
 
 // One expert's weights outside the routed arrays (the shared expert); the
 // scales are fp32 (WFMT_E4M3_128) or E8M0 bytes (WFMT_MXFP4).
@@ -82,7 +82,9 @@ int launch_decode_ffn(int layout, const uint16_t* x, const uint8_t* w13, const f
 // 2*H + H/8 bytes (common.hpp, bfp16x8_encode).  Weight scales are fp32
 // 128x128 blocks, or (wfmt WFMT_MXFP4) E8M0 bytes, 4-byte aligned.  afmt
 // AFMT_E4M3: xq [T, H] codes, xs fp32 [T]; AFMT_MXFP4 (MXFP4 weights only):
-// xq [T, H/2], xs E8M0 bytes [T, H/32]; AFMT_BF16: both unused.
+// xq [T, H/2], xs E8M0 bytes [T, H/32]; AFMT_MXFP4_H4: the same x, and the
+// hidden activation quantised to MXFP4 too (codes and E8M0 bytes in abuf)
+// for an E2M1 x E2M1 down GEMM; AFMT_BF16: both unused.
 int launch_prefill_ffn(int layout, const uint16_t* x, const uint8_t* w13, const void* w13s,
                        const uint8_t* w2, const void* w2s, const SharedW& sh, const Plan& plan,
                        int T, int H, int I, int E, int k, uint16_t* abuf, float* ybuf, int act,

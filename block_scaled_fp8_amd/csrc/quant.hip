@@ -14,6 +14,7 @@
 // carry out of the 3-bit mantissa moves into the exponent field.
 #include "common.hpp"
 #include "plan.hpp"
+#include "mxfp4_act.hpp"
 
 namespace moe {
 
@@ -147,26 +148,13 @@ __global__ __launch_bounds__(256) void quant_rows_mxfp4_kernel(const uint16_t* _
     //  quad past the end only takes part in the shuffles)
     const bool live = run < nruns;
     const u32x4 v = live ? reinterpret_cast<const u32x4*>(x)[g] : u32x4{0u, 0u, 0u, 0u};
-    uint32_t m = 0;  // largest |x| as bf16 bits (finite values order as integers)
-#pragma unroll
-    for (int w = 0; w < 4; ++w) m = max(m, max(v[w] & 0x7FFFu, (v[w] >> 16) & 0x7FFFu));
+    uint32_t m = bf16x8_absmax_bits(v);
     m = max(m, (uint32_t)__shfl_xor((int)m, 1, MOE_WAVE));
     m = max(m, (uint32_t)__shfl_xor((int)m, 2, MOE_WAVE));
     if (!live) return;
-    const int eb = (int)(m >> 7);
     const bool bad = m >= 0x7F80u;
-    const int X = max(eb - 129, -127);
-    const float inv = __uint_as_float((uint32_t)(127 - X) << 23);  // 2^-X, 127 - X in [2, 254]
-    uint32_t word = 0;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const uint32_t b = (v[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
-        const float a = __uint_as_float((b & 0x7FFFu) << 16) * inv;
-        const uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
-                           (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
-                           (uint32_t)(a > 5.0f);
-        word |= (c | ((b >> 12) & 8u)) << (4 * e);
-    }
+    const int X = mxfp4_run_exponent(m);
+    const uint32_t word = mxfp4_encode8(v, X);
     reinterpret_cast<uint32_t*>(codes)[g] = bad ? 0u : word;
     if ((g & 3) == 0) scales[run] = bad ? (uint8_t)255 : (uint8_t)(X + 127);
 }

@@ -71,10 +71,14 @@ enum {
     MOE_VARIANT_PREFILL_A8 = 3, /* the prefill GEMMs with x quantised to E4M3 per token (as
                                    moe_quant_e4m3_rows) for the gate/up (or up) GEMM on the
                                    FP8 MFMA; the down GEMM as PREFILL; never chosen by AUTO */
-    MOE_VARIANT_PREFILL_A4 = 4  /* MXFP4 weights only (moe_fused_mxfp4): the prefill GEMMs with
+    MOE_VARIANT_PREFILL_A4 = 4, /* MXFP4 weights only (moe_fused_mxfp4): the prefill GEMMs with
                                    x quantised to MXFP4 (as moe_quant_mxfp4_rows) for the
                                    gate/up (or up) GEMM as E2M1 x E2M1 products on the scaled
                                    MFMA; the down GEMM as PREFILL; never chosen by AUTO */
+    MOE_VARIANT_PREFILL_FP4 = 5 /* MXFP4 weights only: PREFILL_A4, and the hidden activation
+                                   (rounded to bf16) quantised to MXFP4 by the same rule in the
+                                   gate/up epilogue, so that the down GEMM also runs E2M1 x
+                                   E2M1; never chosen by AUTO */
 };
 
 enum {
@@ -223,8 +227,9 @@ typedef struct {
  *              output); applies to w13, w2 and the shared expert alike
  *   variant    MOE_VARIANT_*
  * H and I must be multiples of 128 (else MOE_EUNSUPPORTED); T >= 0; T == 0
- * is a no-op.  MOE_VARIANT_PREFILL_A4 takes MXFP4 weights only and gives
- * MOE_EUNSUPPORTED here (and in the _ex and _noalloc forms).
+ * is a no-op.  MOE_VARIANT_PREFILL_A4 and MOE_VARIANT_PREFILL_FP4 take MXFP4
+ * weights only and give MOE_EUNSUPPORTED here (and in the _ex and _noalloc
+ * forms).
  * MOE_VARIANT_PREFILL also needs H and 2I to be multiples of
  * 256 (else MOE_EUNSUPPORTED); MOE_VARIANT_AUTO picks the decode variant for
  * such shapes and for batches of at most 16 routes per expert and 4096 routes
@@ -385,6 +390,17 @@ typedef struct {
  *              bf16, the down GEMM bf16 x MXFP4); the workspace also holds
  *              the codes and scales of x.  A token whose row holds a NaN or
  *              an infinity gets a NaN output row.
+ *   MOE_VARIANT_PREFILL_FP4  PREFILL_A4, and the hidden activation (the
+ *              SwiGLU or relu^2 output, rounded to bf16) quantised to MXFP4
+ *              by the same rule in the gate/up (up) epilogue (same page:
+ *              the producer quantises the hidden activation in registers and
+ *              runs the down projection in MXFP4), so the down GEMM also
+ *              multiplies E2M1 by E2M1 with both E8M0 bytes as the MFMA's
+ *              scales.  The quantisation decision is taken from the fp32
+ *              sums, so a hidden element within a rounding error of an E2M1
+ *              midpoint (or of a power of two that sets its run's exponent)
+ *              may land on either neighbour.  A run of 32 hidden values
+ *              holding a NaN or an infinity gives NaN outputs for its token.
  * The E8M0 scale is applied exactly in the conversion to bf16 (every E2M1
  * value times a power of two is a bf16 value while it stays in bf16's normal
  * range; smaller products are flushed to zero), products are summed in fp32

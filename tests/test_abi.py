@@ -143,17 +143,21 @@ def test_quant_mxfp4_rows_argument_checks():
 
 
 def test_mxfp4_activation_variant_needs_mxfp4_weights():
-    """MOE_VARIANT_PREFILL_A4 is refused for E4M3FN weights (both entry
-    points) before any launch."""
+    """MOE_VARIANT_PREFILL_A4 and MOE_VARIANT_PREFILL_FP4 are refused for
+    E4M3FN weights (both entry points) before any launch; 6 is no variant."""
     lib = binding.load_library()
     f, o = ctypes.c_void_p(0x1000), ctypes.c_void_p(0x3000)
     ws = lib.moe_fused_workspace_bytes(64, 2048, 512, 256, 8, 0, 4)
     assert ws > lib.moe_fused_workspace_bytes(64, 2048, 512, 256, 8, 0, 2)   # + codes and scales of x
+    # the MXFP4 hidden activation lives inside the bf16 hidden buffer
+    assert lib.moe_fused_workspace_bytes(64, 2048, 512, 256, 8, 0, 5) == ws
+    assert lib.moe_fused_workspace_bytes(64, 2048, 512, 256, 8, 0, 6) == 0
     head = (f, f, f, f, f, f, f, 64, 2048, 512, 256, 8, None, o, None)
-    assert lib.moe_fused_w8a16_ex(*head, f, ws, 0, 4, 0, None) == binding.MOE_EUNSUPPORTED
-    assert b"MXFP4 weights" in lib.moe_last_error()
-    assert lib.moe_fused_w8a16_noalloc(*head, 0, 4, 0, None) == binding.MOE_EUNSUPPORTED
-    assert lib.moe_fused_w8a16_ex(*head, f, ws, 0, 5, 0, None) == binding.MOE_EINVAL
+    for v in (4, 5):
+        assert lib.moe_fused_w8a16_ex(*head, f, ws, 0, v, 0, None) == binding.MOE_EUNSUPPORTED
+        assert b"MXFP4 weights" in lib.moe_last_error()
+        assert lib.moe_fused_w8a16_noalloc(*head, 0, v, 0, None) == binding.MOE_EUNSUPPORTED
+    assert lib.moe_fused_w8a16_ex(*head, f, ws, 0, 6, 0, None) == binding.MOE_EINVAL
 
 
 def test_quant_e4m3_rows_argument_checks():
