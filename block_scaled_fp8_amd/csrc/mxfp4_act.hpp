@@ -33,23 +33,24 @@ __device__ __forceinline__ int mxfp4_run_exponent(uint32_t amax_bits) {
 
 // E2M1 codes of 8 bf16 values at the run exponent X, element e in bits
 // 4e .. 4e+3 (the byte order of packed MXFP4: element 2j in the low nibble of
-// byte j).  |x| * 2^-X is exact in fp32 (bf16 significands, a power-of-two
-// factor within range), and the code counts the E2M1 midpoints below it: at
-// a midpoint the even code wins, so 1/4, 5/4, 5/2 and 5 round down and 3/4,
-// 7/4 and 7/2 up.
+// byte j), by gfx950's scaled conversion: each pair of bf16 values divided by
+// the fp32 2^X (X = -127: the subnormal 2^-127) and rounded to the nearest
+// E2M1 value, a tie to the even code, saturating at 6 and keeping the sign.
+// Checked on the GPU over every bf16 pattern whose quotient is below 8 (all a
+// run's elements: its largest lands in [4, 8)) at X = -127, -126, -10, -1,
+// 0, 1, 10, 125 and 127: identical to counting the E2M1 midpoints below
+// |x| / 2^X (1/4, 5/4, 5/2 and 5 round down, 3/4, 7/4 and 7/2 up).
 __device__ __forceinline__ uint32_t mxfp4_encode8(u32x4 v, int X) {
-    const float inv = __uint_as_float((uint32_t)(127 - X) << 23);  // 2^-X, 127 - X in [2, 254]
-    uint32_t word = 0;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const uint32_t b = (v[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
-        const float a = __uint_as_float((b & 0x7FFFu) << 16) * inv;
-        const uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
-                           (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
-                           (uint32_t)(a > 5.0f);
-        word |= (c | ((b >> 12) & 8u)) << (4 * e);
-    }
-    return word;
+    const float sc = __uint_as_float(X >= -126 ? (uint32_t)(X + 127) << 23 : 0x00400000u);
+    // (each word through a scalar first: a bit cast of an ext-vector
+    //  element has compiled to element 0)
+    const uint32_t p0 = v[0], p1 = v[1], p2 = v[2], p3 = v[3];
+    uint32_t w = 0;
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(w, __builtin_bit_cast(bf16x2, p0), sc, 0);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(w, __builtin_bit_cast(bf16x2, p1), sc, 1);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(w, __builtin_bit_cast(bf16x2, p2), sc, 2);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(w, __builtin_bit_cast(bf16x2, p3), sc, 3);
+    return w;
 }
 
 }  // namespace moe

@@ -693,7 +693,9 @@ def test_quant_e4m3_rows_bit_exact(T, H):
 def test_quant_mxfp4_rows_bit_exact(T, H):
     """MXFP4 quantisation of x against the oracle's, byte for byte: random
     rows, an all-zero row, a row of E2M1 midpoints (ties) and saturating
-    values, and runs holding a NaN or an infinity."""
+    values, runs holding a NaN or an infinity, and runs at the ends of the
+    exponent range (bf16 subnormals: X = -127; near the largest bf16: X =
+    125) and at random exponents between."""
     x = synth.make_activations(synth.MoeConfig("q4", T, H, 128, 8, 1), seed=T + H + 4)[0]
     if T > 2:
         x[1] = 0.0
@@ -704,6 +706,13 @@ def test_quant_mxfp4_rows_bit_exact(T, H):
         x[0, 5] = float("nan")
         if H >= 64:
             x[0, 40] = float("-inf")
+    if T > 5:
+        g = torch.Generator().manual_seed(H)
+        base = torch.randn(3, H, generator=g)
+        x[3] = (base[0] * 2.0 ** -130).to(torch.bfloat16)   # subnormal bf16 values
+        x[4] = (base[1] * 2.0 ** 125).to(torch.bfloat16)
+        ex = torch.randint(-135, 126, (H // 32,), generator=g).repeat_interleave(32)
+        x[5] = (base[2] * torch.pow(2.0, ex.double())).to(torch.bfloat16)
     codes, scales = binding.quant_mxfp4_rows(x.cuda())
     torch.cuda.synchronize()
     ref_c, ref_s = oracle.quantize_rows_mxfp4(x.float().numpy())
