@@ -955,14 +955,13 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
                     slab[(8 * (i >> 2) + 4 * lg + (i & 3)) * 128 + nt * 32 + ln] = acc[mt][nt][i];
             __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the slab is written
             __builtin_amdgcn_wave_barrier();
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
+            auto run = [&](int q, bool guarded) {
                 const int r = 4 * q + (lane >> 4);   // row of the slab
                 const int c = 8 * (lane & 15);       // the lane's first column
                 const int m = wm * C::WROWS + mt * 32 + r;  // row of the tile
                 const f32x4 v0 = *reinterpret_cast<const f32x4*>(slab + r * 128 + c);
                 const f32x4 v1 = *reinterpret_cast<const f32x4*>(slab + r * 128 + c + 4);
-                if (m < rows_here) {
+                if (!guarded || m < rows_here) {
                     u32x4 mant;
                     uint32_t ex;
                     bfp16x8_encode_scaled(v0, v1, sm, se, mant, ex);
@@ -970,6 +969,16 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
                     __builtin_nontemporal_store(mant, reinterpret_cast<u32x4*>(rowp + 2 * (size_t)(col0 + c)));
                     __builtin_nontemporal_store((uint8_t)ex, rowp + 2 * (size_t)H + (col0 + c) / 8);
                 }
+            };
+            // a slab whose 32 rows are all real stores with no per-row branch,
+            // so that the eight runs' LDS reads, encodes and stores can
+            // interleave; a partial slab checks each row
+            if (wm * C::WROWS + mt * 32 + 32 <= rows_here) {
+#pragma unroll
+                for (int q = 0; q < 8; ++q) run(q, false);
+            } else {
+#pragma unroll
+                for (int q = 0; q < 8; ++q) run(q, true);
             }
             __builtin_amdgcn_s_waitcnt(0xC07F);  // the slab is read before it is rewritten
             __builtin_amdgcn_wave_barrier();
@@ -1013,8 +1022,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the slab is written
     __builtin_amdgcn_wave_barrier();
     const int colbase = MODE == PF_GATEUP ? nb * (BN / 2) + wn * (C::WCOLS / 2) : nb * BN + wn * C::WCOLS;
-#pragma unroll
-    for (int q = 0; q < C::WROWS / RPS; ++q) {
+    auto put = [&](int q, bool guarded) {
         const int r = q * RPS + lane / LPR;
         const int c = 8 * (lane % LPR);
         const int m = wm * C::WROWS + r;  // row of the tile
@@ -1030,16 +1038,26 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
             const bool bad = mx >= 0x7F80u;
             const int X = mxfp4_run_exponent(mx);
             const uint32_t word = bad ? 0u : mxfp4_encode8(v, X);
-            if (m < rows_here) {
+            if (!guarded || m < rows_here) {
                 const int col = colbase + c;
                 uint8_t* hq = reinterpret_cast<uint8_t*>(abuf_out);
                 *reinterpret_cast<uint32_t*>(hq + (size_t)(p0 + m) * (I / 2) + col / 2) = word;
                 if ((lane & 3) == 0)
                     hscale_out[(size_t)(p0 + m) * (I / 32) + col / 32] = bad ? (uint8_t)255 : (uint8_t)(X + 127);
             }
-        } else if (m < rows_here) {
+        } else if (!guarded || m < rows_here) {
             *reinterpret_cast<u32x4*>(abuf_out + (size_t)(p0 + m) * I + colbase + c) = v;
         }
+    };
+    // a wave tile whose rows are all real stores with no per-row branch, so
+    // that its row pieces' LDS reads and stores can interleave; a partial one
+    // checks each row
+    if (wm * C::WROWS + C::WROWS <= rows_here) {
+#pragma unroll
+        for (int q = 0; q < C::WROWS / RPS; ++q) put(q, false);
+    } else {
+#pragma unroll
+        for (int q = 0; q < C::WROWS / RPS; ++q) put(q, true);
     }
 }
 
