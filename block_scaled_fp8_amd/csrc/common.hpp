@@ -145,27 +145,33 @@ __device__ __forceinline__ void bfp16x8_encode(f32x4 a, f32x4 b, u32x4& mant, ui
 // hold exactly -- a non-finite or zero largest magnitude, f < 14 (c not a
 // normal float) or an exponent byte outside 1..254 -- take bfp16x8_encode of
 // ldexp(a_j * sm, se).
-__device__ __forceinline__ void bfp16x8_encode_scaled(f32x4 a, f32x4 b, float sm, int se, u32x4& mant,
-                                                      uint32_t& ex) {
+// The common case alone, with no branch: returns whether it holds the run
+// exactly (when it does not, mant and ex are meaningless and the run must be
+// encoded by bfp16x8_encode_scaled).
+__device__ __forceinline__ bool bfp16x8_encode_scaled_fast(f32x4 a, f32x4 b, float sm, int se,
+                                                           u32x4& mant, uint32_t& ex) {
     uint32_t mx = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
         mx = max(mx, max(__float_as_uint(a[j]) & 0x7FFFFFFFu, __float_as_uint(b[j]) & 0x7FFFFFFFu));
     const int f = (int)((__float_as_uint(__uint_as_float(mx) * sm) >> 23) & 0xFFu);
     const int e = f + se;
-    if (mx < 0x7F800000u && f >= 14 && f <= 254 && e >= 1 && e <= 254) {
-        constexpr float MAGIC = 12582912.0f;  // 1.5 * 2^23
-        const float c = sm * __uint_as_float((uint32_t)(268 - f) << 23);  // sm * 2^(141 - f)
-        uint32_t m[8];
+    constexpr float MAGIC = 12582912.0f;  // 1.5 * 2^23
+    const float c = sm * __uint_as_float((uint32_t)(268 - f) << 23);  // sm * 2^(141 - f)
+    uint32_t m[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const float y = __builtin_fmaf(j < 4 ? a[j] : b[j - 4], c, MAGIC);
-            m[j] = __float_as_uint(__builtin_amdgcn_fmed3f(y, MAGIC - 32767.0f, MAGIC + 32767.0f));
-        }
+    for (int j = 0; j < 8; ++j) {
+        const float y = __builtin_fmaf(j < 4 ? a[j] : b[j - 4], c, MAGIC);
+        m[j] = __float_as_uint(__builtin_amdgcn_fmed3f(y, MAGIC - 32767.0f, MAGIC + 32767.0f));
+    }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) mant[j] = __builtin_amdgcn_perm(m[2 * j + 1], m[2 * j], 0x05040100u);
-        ex = (uint32_t)e;
-    } else {
+    for (int j = 0; j < 4; ++j) mant[j] = __builtin_amdgcn_perm(m[2 * j + 1], m[2 * j], 0x05040100u);
+    ex = (uint32_t)e;
+    return (mx < 0x7F800000u) & (f >= 14) & (f <= 254) & (e >= 1) & (e <= 254);
+}
+__device__ __forceinline__ void bfp16x8_encode_scaled(f32x4 a, f32x4 b, float sm, int se, u32x4& mant,
+                                                      uint32_t& ex) {
+    if (!bfp16x8_encode_scaled_fast(a, b, sm, se, mant, ex)) {
         f32x4 va, vb;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {

@@ -955,30 +955,62 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
                     slab[(8 * (i >> 2) + 4 * lg + (i & 3)) * 128 + nt * 32 + ln] = acc[mt][nt][i];
             __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the slab is written
             __builtin_amdgcn_wave_barrier();
-            auto run = [&](int q, bool guarded) {
-                const int r = 4 * q + (lane >> 4);   // row of the slab
-                const int c = 8 * (lane & 15);       // the lane's first column
-                const int m = wm * C::WROWS + mt * 32 + r;  // row of the tile
-                const f32x4 v0 = *reinterpret_cast<const f32x4*>(slab + r * 128 + c);
-                const f32x4 v1 = *reinterpret_cast<const f32x4*>(slab + r * 128 + c + 4);
+            // Each run is first encoded by the branch-free common case and
+            // stored; a run that case cannot hold (a largest value that is
+            // not finite, zero or near the ends of the exponent range: rare)
+            // is encoded again by the full encoder and stored over it, after
+            // all eight, so the eight runs' LDS reads, encodes and stores
+            // carry no branch and can interleave.
+            uint32_t redo = 0;  // runs to encode again (bit q)
+            const int c = 8 * (lane & 15);  // the lane's first column
+            auto ld = [&](int q, f32x4& v0, f32x4& v1) {
+                const int r = 4 * q + (lane >> 4);  // row of the slab
+                v0 = *reinterpret_cast<const f32x4*>(slab + r * 128 + c);
+                v1 = *reinterpret_cast<const f32x4*>(slab + r * 128 + c + 4);
+            };
+            auto put = [&](int q, f32x4 v0, f32x4 v1, bool guarded, bool full) {
+                const int m = wm * C::WROWS + mt * 32 + 4 * q + (lane >> 4);  // row of the tile
                 if (!guarded || m < rows_here) {
                     u32x4 mant;
                     uint32_t ex;
-                    bfp16x8_encode_scaled(v0, v1, sm, se, mant, ex);
+                    if (full)
+                        bfp16x8_encode_scaled(v0, v1, sm, se, mant, ex);
+                    else if (!bfp16x8_encode_scaled_fast(v0, v1, sm, se, mant, ex))
+                        redo |= 1u << q;
                     uint8_t* rowp = ybytes + (size_t)(p0 + m) * rowb;
                     __builtin_nontemporal_store(mant, reinterpret_cast<u32x4*>(rowp + 2 * (size_t)(col0 + c)));
                     __builtin_nontemporal_store((uint8_t)ex, rowp + 2 * (size_t)H + (col0 + c) / 8);
                 }
             };
             // a slab whose 32 rows are all real stores with no per-row branch,
-            // so that the eight runs' LDS reads, encodes and stores can
-            // interleave; a partial slab checks each row
+            // each run's LDS reads issued one run ahead; a partial slab checks
+            // each row
             if (wm * C::WROWS + mt * 32 + 32 <= rows_here) {
+                f32x4 a0, a1, b0, b1;
+                ld(0, a0, a1);
 #pragma unroll
-                for (int q = 0; q < 8; ++q) run(q, false);
+                for (int q = 0; q < 8; q += 2) {
+                    ld(q + 1, b0, b1);
+                    put(q, a0, a1, false, false);
+                    if (q + 2 < 8) ld(q + 2, a0, a1);
+                    put(q + 1, b0, b1, false, false);
+                }
             } else {
 #pragma unroll
-                for (int q = 0; q < 8; ++q) run(q, true);
+                for (int q = 0; q < 8; ++q) {
+                    f32x4 v0, v1;
+                    ld(q, v0, v1);
+                    put(q, v0, v1, true, false);
+                }
+            }
+            if (__ballot(redo != 0) != 0ull) {
+#pragma unroll
+                for (int q = 0; q < 8; ++q)
+                    if (redo & (1u << q)) {
+                        f32x4 v0, v1;
+                        ld(q, v0, v1);
+                        put(q, v0, v1, true, true);
+                    }
             }
             __builtin_amdgcn_s_waitcnt(0xC07F);  // the slab is read before it is rewritten
             __builtin_amdgcn_wave_barrier();
