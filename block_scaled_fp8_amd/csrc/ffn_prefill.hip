@@ -209,6 +209,15 @@ __device__ __forceinline__ float swiglu_fast(float g, float u) {
     return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
 }
 
+// Two floats to two bf16 bit patterns (low half: a) by gfx950's packed
+// conversion: round to nearest even, as f32_to_bf16_bits, and a NaN stays a
+// NaN.
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2_bits(float a, float b) {
+    typedef float pf_f32x2 __attribute__((ext_vector_type(2)));
+    const pf_f32x2 v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
 __device__ __forceinline__ float uniform_f32(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
 }
@@ -1038,17 +1047,28 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void prefill_gemm_kernel(
             // value = acc * mcur * x scale * 2^eref, the power of two last (an
             // exact exponent shift unless the result is subnormal)
             const float s0 = mcur[0] * xsv, s1 = mcur[1] * xsv;
+            // two values at a time through the packed bf16 conversion
             if constexpr (MODE == PF_GATEUP) {
+                static_assert(C::NT % 4 == 0, "pairs of gate tiles");
+                auto g = [&](int nt) {
+                    return swiglu_fast(ldexpf(acc[mt][nt][i] * s0, eref[0]),
+                                       ldexpf(acc[mt][nt + C::NT / 2][i] * s1, eref[1]));
+                };
 #pragma unroll
-                for (int nt = 0; nt < C::NT / 2; ++nt)
-                    slab[r * OUTC + nt * C::MS + ocol] = f32_to_bf16_bits(
-                        swiglu_fast(ldexpf(acc[mt][nt][i] * s0, eref[0]),
-                                    ldexpf(acc[mt][nt + C::NT / 2][i] * s1, eref[1])));
+                for (int nt = 0; nt < C::NT / 2; nt += 2) {
+                    const uint32_t w = f32x2_to_bf16x2_bits(g(nt), g(nt + 1));
+                    slab[r * OUTC + nt * C::MS + ocol] = (uint16_t)w;
+                    slab[r * OUTC + (nt + 1) * C::MS + ocol] = (uint16_t)(w >> 16);
+                }
             } else {
+                static_assert(C::NT % 2 == 0, "pairs of tiles");
 #pragma unroll
-                for (int nt = 0; nt < C::NT; ++nt)
-                    slab[r * OUTC + nt * C::MS + ocol] =
-                        f32_to_bf16_bits(relu2(ldexpf(acc[mt][nt][i] * s0, eref[0])));
+                for (int nt = 0; nt < C::NT; nt += 2) {
+                    const uint32_t w = f32x2_to_bf16x2_bits(relu2(ldexpf(acc[mt][nt][i] * s0, eref[0])),
+                                                            relu2(ldexpf(acc[mt][nt + 1][i] * s0, eref[0])));
+                    slab[r * OUTC + nt * C::MS + ocol] = (uint16_t)w;
+                    slab[r * OUTC + (nt + 1) * C::MS + ocol] = (uint16_t)(w >> 16);
+                }
             }
         }
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the slab is written
